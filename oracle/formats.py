@@ -1,0 +1,94 @@
+"""Decoding of the stored number formats to fp64 (test infrastructure only).
+
+[架构详解 §4]: main KV is stored as MXFP4 (E2M1 elements with block scales)
+and is dequantised before attention; SWA KV is FP8.  [架构详解 §1 config
+table]: indexer K is 128-dim.  The scale format used here is E8M0 with one
+scale per 32 elements (OCP MX v1.0); the page's own variant (one E4M3 scale
+per 16 channels) is a different entry layout and is not decoded here.
+
+Closed forms (OCP):
+  bf16     : the upper 16 bits of an IEEE binary32.
+  E4M3FN   : s=b>>7, e=(b>>3)&15, m=b&7; e==0 -> (-1)^s (m/8) 2^-6,
+             else (-1)^s (1+m/8) 2^(e-7); S.1111.111 is NaN; no infinity.
+  E2M1     : s=n>>3, e=(n>>1)&3, m=n&1; e==0 -> (-1)^s 0.5 m,
+             else (-1)^s (1+m/2) 2^(e-1).
+  E8M0     : 2^(x-127); x == 255 is NaN.
+  MXFP4    : v[i] = E2M1(nib_i) * E8M0(scale[i // 32]); byte j holds
+             element 2j in its low nibble and element 2j+1 in its high nibble.
+"""
+import numpy as np
+
+
+class FormatError(ValueError):
+    """A NaN code appeared where the method stores only finite values."""
+
+
+def bf16_to_f64(u16):
+    """bf16 bit patterns (uint16 array) -> fp64, exactly."""
+    u = np.asarray(u16, dtype=np.uint16).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):
+        return u.view(np.float32).astype(np.float64)
+
+
+def _e4m3_value(b):
+    s, e, m = b >> 7, (b >> 3) & 15, b & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    if e == 0:
+        v = (m / 8.0) * 2.0 ** -6
+    else:
+        v = (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return -v if s else v
+
+
+def _e2m1_value(n):
+    s, e, m = n >> 3, (n >> 1) & 3, n & 1
+    if e == 0:
+        v = 0.5 * m
+    else:
+        v = (1.0 + m / 2.0) * 2.0 ** (e - 1)
+    return -v if s else v
+
+
+# Per-code values computed once from the closed forms above.
+E4M3_VALUES = np.array([_e4m3_value(b) for b in range(256)], dtype=np.float64)
+E2M1_VALUES = np.array([_e2m1_value(n) for n in range(16)], dtype=np.float64)
+
+
+def e4m3_to_f64(u8):
+    """FP8 E4M3FN codes -> fp64; a NaN code raises FormatError."""
+    u8 = np.asarray(u8, dtype=np.uint8)
+    if np.any((u8 & 0x7F) == 0x7F):
+        raise FormatError("FP8 E4M3FN NaN code in input")
+    return E4M3_VALUES[u8]
+
+
+def e2m1_to_f64(nib):
+    """E2M1 nibbles (0..15) -> fp64."""
+    return E2M1_VALUES[np.asarray(nib, dtype=np.uint8) & 0xF]
+
+
+def e8m0_to_f64(u8):
+    """E8M0 scale codes -> 2^(x-127); code 255 (NaN) raises FormatError."""
+    u8 = np.asarray(u8, dtype=np.uint8)
+    if np.any(u8 == 255):
+        raise FormatError("E8M0 NaN code in input")
+    return np.ldexp(1.0, u8.astype(np.int64) - 127)
+
+
+def mxfp4_to_f64(fp4_bytes, scales):
+    """MXFP4 entries -> fp64 vectors.
+
+    fp4_bytes: uint8 [..., D/2]; scales: uint8 [..., D/32].  Returns [..., D].
+    """
+    b = np.asarray(fp4_bytes, dtype=np.uint8)
+    sc = np.asarray(scales, dtype=np.uint8)
+    d = b.shape[-1] * 2
+    if sc.shape[-1] * 32 != d:
+        raise ValueError("MXFP4: need one scale per 32 elements")
+    nib = np.empty(b.shape[:-1] + (d,), dtype=np.uint8)
+    nib[..., 0::2] = b & 0xF
+    nib[..., 1::2] = b >> 4
+    vals = e2m1_to_f64(nib)
+    scale = np.repeat(e8m0_to_f64(sc), 32, axis=-1)
+    return vals * scale

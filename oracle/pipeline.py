@@ -1,0 +1,87 @@
+"""One query's CSA2 step from raw stored bytes, fp64 (test infrastructure only).
+
+[架构详解 §3 mode table]: every mode computes its own query and SWA KV.
+  Full    -- computes indexer Q/K and its own Top-K; also builds the pool.
+  Reindex -- computes its own indexer Q and a new Top-K, re-scoring only the
+             pool, against the most recent Full layer's indexer K.
+  Reuse   -- no indexer; reuses the most recent Top-K indices.
+[架构详解 §3.2]: the Full layer scans all visible entries, takes its own
+Top-512 and builds the pool of at most 2048 blocks of 8 positions.
+[架构详解 §3.1]: the encoder compresses m=2 tokens per entry (prefill
+chunks), the decoder m=1.
+
+Raw layouts (one query): q_idx uint16 [32, 128] (bf16 bits); w float [32];
+k_idx uint16 [N, 128] (bf16 bits) or uint8 [N, 128] (FP8 E4M3FN);
+q uint16 [64, 512] (bf16 bits); kv_fp4 uint8 [N, 256]; kv_scale uint8
+[N, 16] (E8M0); swa uint8 [S, 512] (FP8 E4M3FN), slot i holding token
+swa_pos0 + i.
+"""
+import numpy as np
+
+from . import formats, indexer, topk, attention as attn
+
+CHUNK = 1 << 16
+
+
+def decode_index_keys(k_raw, kdtype):
+    if kdtype == "bf16":
+        return formats.bf16_to_f64(k_raw)
+    if kdtype == "fp8":
+        return formats.e4m3_to_f64(k_raw)
+    raise ValueError(f"unknown indexer K dtype {kdtype!r}")
+
+
+def _query(q_raw, w):
+    return formats.bf16_to_f64(q_raw), np.asarray(w, dtype=np.float64)
+
+
+def scores_prefix(q_raw, w, k_raw, kdtype, vis, chunk=CHUNK):
+    """Scores of positions [0, vis), decoded and scored chunk by chunk."""
+    q, wf = _query(q_raw, w)
+    out = np.empty(int(vis), dtype=np.float64)
+    for lo in range(0, int(vis), chunk):
+        hi = min(int(vis), lo + chunk)
+        out[lo:hi] = indexer.index_scores(q, wf, decode_index_keys(k_raw[lo:hi], kdtype))
+    return out
+
+
+def scores_at(q_raw, w, k_raw, kdtype, positions):
+    """Scores of the given positions only."""
+    q, wf = _query(q_raw, w)
+    positions = np.asarray(positions, dtype=np.int64)
+    return indexer.index_scores(q, wf, decode_index_keys(k_raw[positions], kdtype))
+
+
+def full_layer(q_raw, w, k_raw, kdtype, vis, k_blocks=topk.MAX_POOL_BLOCKS, top_k=topk.TOP_K):
+    """Full layer: scan, block maxima, pool, Top-k inside the pool."""
+    s = scores_prefix(q_raw, w, k_raw, kdtype, vis)
+    bm = indexer.block_max(s, vis)
+    pool = topk.block_topk(bm, k_blocks)
+    pos = topk.pool_positions(pool, vis)
+    idx = topk.pool_topk(s[pos], pos, top_k)
+    return {"scores": s, "block_max": bm, "pool": pool, "idx": idx}
+
+
+def reindex_layer(q_raw, w, k_raw, kdtype, pool, vis, top_k=topk.TOP_K):
+    """Reindex layer: re-score only the Full layer's pool with this layer's query."""
+    pos = topk.pool_positions(pool, vis)
+    s = scores_at(q_raw, w, k_raw, kdtype, pos)
+    return {"positions": pos, "scores": s, "idx": topk.pool_topk(s, pos, top_k)}
+
+
+def prefill_topk(q_raw, w, k_raw, kdtype, vis, top_k=topk.TOP_K):
+    """Encoder prefill (m=2): flat Top-k over every visible entry, no pool."""
+    s = scores_prefix(q_raw, w, k_raw, kdtype, vis)
+    return {"scores": s, "idx": topk.flat_topk(s, vis, top_k)}
+
+
+def attention(q_raw, kv_fp4, kv_scale, idx, swa_raw, swa_pos0, q_pos, sm_scale,
+              window=attn.WINDOW, replay_start=-1):
+    """Selected main entries (idx != -1) plus the SWA window, one softmax."""
+    idx = np.asarray(idx, dtype=np.int64)
+    sel = idx[idx >= 0]
+    main = formats.mxfp4_to_f64(kv_fp4[sel], kv_scale[sel])
+    wpos = attn.window_positions(q_pos, swa_pos0, swa_raw.shape[0], window, replay_start)
+    swa = formats.e4m3_to_f64(swa_raw[wpos - int(swa_pos0)])
+    entries = np.concatenate([main, swa], axis=0)
+    return attn.sparse_attention(formats.bf16_to_f64(q_raw), entries, sm_scale)
