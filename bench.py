@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA2 decode hot path on one MI355X (gfx950).
+
+One step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM.  Default workload (full_reindex_1m): 8 sequences at
+1,048,576 positions of context decode one token each through a decoder Full
+layer (indexer scan with fused block maximum -> Top-2048 blocks -> Top-512 in
+the 16,384-position pool -> sparse attention over 512 MXFP4 entries plus the
+128-token FP8 window) and then a Reindex layer (re-score the pool with the
+layer's own indexer query -> Top-512 -> attention with its own query and
+window).  Throughput is decode query-tokens per second: B per step.
+
+Prints ONE JSON line on stdout; diagnostics go to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA2 decode query-tokens/s at 128K and 1M ctx; % of HBM GB/s roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+SCAN_SOURCES = ["index_score.hip", "index_core.h", "csa2_device.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="full_reindex_1m",
+                   choices=["tiny_2k", "full_64k", "reuse_128k", "full_reindex_1m", "prefill_128k"])
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="CPU time budget of the oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true", help="skip the graph-replay measurement")
+    return p.parse_args()
+
+
+def scan_source_hash():
+    h = hashlib.sha256()
+    for f in SCAN_SOURCES:
+        with open(os.path.join(ROOT, "compressed_sparse_attention_index_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class Step:
+    """Buffers and the launch sequence of one hot-path step (all on one stream)."""
+
+    def __init__(self, name, d, csa, torch):
+        self.name, self.d, self.csa, self.torch = name, d, csa, torch
+        dev = "cuda"
+        B, n_q = d["B"], d["n_q"]
+        self.B, self.n_q = B, n_q
+        self.rows = B * n_q
+        self.N = d["kv_fp4"].shape[1]
+        z = lambda *s, dt=torch.int32: torch.empty(*s, dtype=dt, device=dev)
+        self.out = z(B, n_q, 64, 512, dt=torch.int16)
+        self.lse = z(B, n_q, 64, dt=torch.float32)
+        self.idx = z(B, n_q, 512)
+        self.ws_attn = self._ws(csa.OP_SPARSE_ATTN, 512, 0)
+        self.scan_ev = []
+        if name == "reuse_128k":
+            return
+        self.bm = z(B, n_q, (self.N + 7) // 8, dt=torch.float32)
+        if name == "prefill_128k":
+            self.scores = z(B, n_q, self.N, dt=torch.float32)
+            return
+        self.pool = z(B, n_q, 2048)
+        self.ws_re = self._ws(csa.OP_REINDEX_TOPK, 512, 2048)
+        if "q_idx2" in d:
+            self.idx2 = z(B, n_q, 512)
+            self.out2 = z(B, n_q, 64, 512, dt=torch.int16)
+            self.lse2 = z(B, n_q, 64, dt=torch.float32)
+
+    def _ws(self, op, top_k, kb):
+        n = self.csa.workspace_size(op, self.B, self.n_q, self.N, top_k, kb)
+        return self.torch.empty(max(n, 16), dtype=self.torch.uint8, device="cuda")
+
+    def _scan(self, timed):
+        d, csa = self.d, self.csa
+        if timed:
+            e0 = self.torch.cuda.Event(enable_timing=True)
+            e1 = self.torch.cuda.Event(enable_timing=True)
+            e0.record()
+        csa.index_score(d["q_idx"], d["w_idx"], d["k_idx"], d["vis_len"], block_max=self.bm,
+                        scores=getattr(self, "scores", None))
+        if timed:
+            e1.record()
+            self.scan_ev.append((e0, e1))
+
+    def _attn(self, fn, q, swa, idx, out, lse):
+        d = self.d
+        fn(q, d["kv_fp4"], d["kv_scale"], idx, swa, d["swa_pos0"], d["q_pos"], d["sm_scale"], out,
+           lse=lse, ws=self.ws_attn)
+
+    def run(self, timed=False):
+        d, csa = self.d, self.csa
+        if self.name == "reuse_128k":
+            if timed:
+                e0 = self.torch.cuda.Event(enable_timing=True)
+                e1 = self.torch.cuda.Event(enable_timing=True)
+                e0.record()
+            self._attn(csa.reuse_attn, d["q"], d["swa"], d["idx"], self.out, self.lse)
+            if timed:
+                e1.record()
+                self.scan_ev.append((e0, e1))
+            return
+        self._scan(timed)
+        if self.name == "prefill_128k":
+            csa.reindex_topk(csa.MODE_FULL, d["vis_len"], self.N, 512, self.idx, scores=self.scores)
+            self._attn(csa.sparse_attn_decode, d["q"], d["swa"], self.idx, self.out, self.lse)
+            return
+        csa.block_topk(self.bm, d["vis_len"], self.N, 2048, self.pool)
+        csa.reindex_topk(csa.MODE_FULL, d["vis_len"], self.N, 512, self.idx, q_idx=d["q_idx"],
+                         w_idx=d["w_idx"], k_idx=d["k_idx"], pool_blocks=self.pool, ws=self.ws_re)
+        self._attn(csa.sparse_attn_decode, d["q"], d["swa"], self.idx, self.out, self.lse)
+        if hasattr(self, "idx2"):
+            csa.reindex_topk(csa.MODE_REINDEX, d["vis_len"], self.N, 512, self.idx2,
+                             q_idx=d["q_idx2"], w_idx=d["w_idx2"], k_idx=d["k_idx"],
+                             pool_blocks=self.pool, ws=self.ws_re)
+            self._attn(csa.sparse_attn_decode, d["q2"], d["swa2"], self.idx2, self.out2, self.lse2)
+
+
+def algorithmic(name, d):
+    """(dominant kernel, its bytes or flops per launch, bound, step bytes) by definition."""
+    B, n_q = d["B"], d["n_q"]
+    attn_bytes = 512 * 272 + 128 * 512 + 64 * 512 * 2 * 2 + 512 * 4 + 64 * 4   # per query row
+    if name == "reuse_128k":
+        per = B * attn_bytes
+        return "sparse_attn", per, "hbm", per
+    T = d["k_idx"].shape[1]
+    krow = 128 if d["kdtype"] == "fp8" else 256
+    nb = (T + 7) // 8
+    if name == "prefill_128k":
+        vis = d["vis_len"].double().sum().item()
+        flops = 2.0 * 32 * 128 * vis
+        return "index_gemm", flops, "mfma", None
+    scan = B * (T * krow + 32 * 128 * 2 + 32 * 4 + nb * 4)
+    step = B * (T * krow + 32 * 128 * 2 + 32 * 4) + B * attn_bytes
+    if "q_idx2" in d:
+        step += B * (16384 * krow + 32 * 128 * 2 + 32 * 4) + B * attn_bytes
+    return "index_scan", scan, "hbm", step
+
+
+def cpu_baseline(name, d, budget_s):
+    """The fp64 oracle as it stands, on a bounded sample of the same workload's rows."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+    from oracle import pipeline
+
+    def npy(t):
+        return t.detach().cpu().numpy()
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    B, n_q = d["B"], d["n_q"]
+    rows = [(b, j) for b in range(B) for j in range(n_q)]
+    done, t_total = 0, 0.0
+    for b, j in rows:
+        kr = None
+        if "k_idx" in d:
+            kr = npy(d["k_idx"][b])
+            kd = d["kdtype"]
+            if kd == "bf16":
+                kr = kr.view(np.uint16)
+        swa = npy(d["swa"][b])
+        t0 = time.perf_counter()
+        if name == "reuse_128k":
+            idx = npy(d["idx"][b, j])
+            fp4, sc = npy(d["kv_fp4"][b][d["idx"][b, j].long()]), npy(d["kv_scale"][b][d["idx"][b, j].long()])
+            pipeline.attention(npy(d["q"][b, j]).view(np.uint16), fp4, sc, np.arange(len(idx)), swa,
+                               int(d["swa_pos0"][b]), int(d["q_pos"][b, j]), d["sm_scale"])
+        else:
+            vis = int(d["vis_len"][b, j])
+            qi, w = npy(d["q_idx"][b, j]).view(np.uint16), npy(d["w_idx"][b, j])
+            if name == "prefill_128k":
+                idx = pipeline.prefill_topk(qi, w, kr, kd, vis)["idx"]
+            else:
+                full = pipeline.full_layer(qi, w, kr, kd, vis)
+                idx = full["idx"]
+            sel = torch.from_numpy(idx[idx >= 0])
+            kvd = d["kv_fp4"].device
+            fp4 = npy(d["kv_fp4"][b][sel.to(kvd)])
+            sc = npy(d["kv_scale"][b][sel.to(kvd)])
+            pipeline.attention(npy(d["q"][b, j]).view(np.uint16), fp4, sc, np.arange(len(sel)), swa,
+                               int(d["swa_pos0"][b]), int(d["q_pos"][b, j]), d["sm_scale"])
+            if "q_idx2" in d:
+                re = pipeline.reindex_layer(npy(d["q_idx2"][b, j]).view(np.uint16),
+                                            npy(d["w_idx2"][b, j]), kr, kd, full["pool"], vis)
+                i2 = re["idx"]
+                s2 = torch.from_numpy(i2[i2 >= 0]).to(kvd)
+                pipeline.attention(npy(d["q2"][b, j]).view(np.uint16), npy(d["kv_fp4"][b][s2]),
+                                   npy(d["kv_scale"][b][s2]), np.arange(len(s2)), npy(d["swa2"][b]),
+                                   int(d["swa_pos0"][b]), int(d["q_pos"][b, j]), d["sm_scale"])
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    return {"value": done / t_total, "unit": "query-tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {len(rows)} query rows of the same workload, all of each row's "
+                      f"steps (fp64 numpy, {t_total:.1f} s)"}
+
+
+def traffic_from_profile(dominant, src_hash):
+    path = os.path.join(ROOT, "profiles", f"{dominant}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path has no "
+              "multi-GPU mode in this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import compressed_sparse_attention_index_amd as csa
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    csa.lib()
+    torch.cuda.set_device(0)
+
+    t0 = time.time()
+    d = synth.make(args.workload, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] generated {args.workload} on the GPU in {time.time() - t0:.1f} s")
+    step = Step(args.workload, d, csa, torch)
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    step.scan_ev.clear()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        step.run(timed=True)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    dom_ms = sum(a.elapsed_time(b) for a, b in step.scan_ev) / len(step.scan_ev)
+    log(f"[bench] eager: {ms * 1e3:.1f} us/step, dominant kernel {dom_ms * 1e3:.1f} us/launch")
+
+    graph_ms = None
+    if not args.no_graph:
+        try:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                step.run()
+            torch.cuda.current_stream().wait_stream(s)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step.run()
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            ev0.record()
+            for _ in range(args.steps):
+                g.replay()
+            ev1.record()
+            torch.cuda.synchronize()
+            graph_ms = ev0.elapsed_time(ev1) / args.steps
+            log(f"[bench] graph replay: {graph_ms * 1e3:.1f} us/step")
+        except Exception as exc:  # graph capture is an extra measurement only
+            log(f"[bench] graph replay skipped: {exc!r}")
+
+    dominant, per_launch, bound, step_bytes = algorithmic(args.workload, d)
+    rows = d["B"] * d["n_q"]
+    value = rows / (ms / 1e3)
+    if bound == "hbm":
+        achieved = per_launch / (dom_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = per_launch / (dom_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+    roof["kernel"] = dominant
+    roof["per_launch"] = per_launch
+    roof["launch_us"] = round(dom_ms * 1e3, 2)
+    roof["traffic"] = traffic_from_profile(dominant, scan_source_hash())
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        cpu = cpu_baseline(args.workload, d, args.cpu_seconds)
+        log(f"[bench] oracle baseline: {cpu['value']:.4f} query-tokens/s ({time.time() - t0:.1f} s)")
+
+    T = d["kv_fp4"].shape[1]
+    cfg = {"workload": args.workload, "batch": d["B"], "query_rows": rows, "context": T,
+           "indexer_k": d.get("kdtype"), "top_k": 512, "pool_blocks": 2048, "window": 128,
+           "layers": {"full_64k": "Full", "tiny_2k": "Full", "reuse_128k": "Reuse",
+                      "full_reindex_1m": "Full+Reindex", "prefill_128k": "prefill (m=2)"}[args.workload]}
+    if step_bytes:
+        cfg["step_algorithmic_bytes"] = step_bytes
+        cfg["step_hbm_frac"] = round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
+    rec = {"metric": METRIC, "value": round(value, 2), "unit": "query-tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu}
+    if graph_ms is not None:
+        rec["graph_ms_per_step"] = round(graph_ms, 5)
+        rec["graph_value"] = round(rows / (graph_ms / 1e3), 2)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

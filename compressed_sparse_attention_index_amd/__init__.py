@@ -1,0 +1,181 @@
+"""Python binding of libcsa2.so, the CSA2 decode hot path for MI355X (gfx950).
+
+Argument marshalling only: every step of the path runs in the HIP kernels
+behind the C ABI declared in include/csa2.h.  Tensors are torch tensors on
+the GPU (torch supplies device memory and the current stream); bf16 arrays
+are passed as int16/uint16/bfloat16 tensors of their bit patterns.  If the
+library is not built this module raises instead of computing anything.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "KDTYPE_BF16", "KDTYPE_FP8", "MODE_FULL", "MODE_REINDEX", "MODE_REUSE",
+    "OP_INDEX_SCORE", "OP_BLOCK_TOPK", "OP_REINDEX_TOPK", "OP_SPARSE_ATTN",
+    "Csa2Error", "lib", "abi_version", "workspace_size", "index_score", "block_topk",
+    "reindex_topk", "sparse_attn_decode", "reuse_attn",
+]
+
+KDTYPE_BF16, KDTYPE_FP8 = 0, 1
+MODE_FULL, MODE_REINDEX, MODE_REUSE = 0, 1, 2
+OP_INDEX_SCORE, OP_BLOCK_TOPK, OP_REINDEX_TOPK, OP_SPARSE_ATTN = 0, 1, 2, 3
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_S = ctypes.c_size_t
+_F = ctypes.c_float
+
+_SIGNATURES = {
+    "csa2_index_score": [_P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _P, _S, _P],
+    "csa2_block_topk": [_P, _P, _I, _I, _I, _I, _P, _P, _S, _P],
+    "csa2_reindex_topk": [_I, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _S, _P],
+    "csa2_sparse_attn_decode": [_P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _F, _P, _I, _I, _P, _P,
+                                _P, _S, _P],
+    "csa2_reuse_attn": [_P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _F, _P, _I, _I, _P, _P, _P, _S, _P],
+    "csa2_workspace_size": [_I, _I, _I, _I, _I, _I],
+    "csa2_status_string": [_I],
+    "csa2_abi_version": [],
+}
+_RESTYPES = {"csa2_workspace_size": _S, "csa2_status_string": ctypes.c_char_p,
+             "csa2_abi_version": _I}
+
+
+class AttnOpts(ctypes.Structure):
+    _fields_ = [("window", _I), ("replay_start", _I), ("kv_fmt", _I), ("reserved", _I)]
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, fn, status, text):
+        super().__init__(f"{fn} failed with status {status}: {text}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libcsa2.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m compressed_sparse_attention_index_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.argtypes = args
+            fn.restype = _RESTYPES.get(name, _I)
+        _lib = l
+    return _lib
+
+
+def _call(name, *args):
+    st = getattr(lib(), name)(*args)
+    if st != 0:
+        raise Csa2Error(name, st, lib().csa2_status_string(st).decode())
+
+
+def abi_version():
+    return lib().csa2_abi_version()
+
+
+def workspace_size(op, B, n_q, N_cap, top_k=512, k_blocks=2048):
+    return lib().csa2_workspace_size(op, B, n_q, N_cap, top_k, k_blocks)
+
+
+def _ptr(t, dtypes, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return t.data_ptr()
+
+
+_BITS16 = (torch.int16, torch.uint16, torch.bfloat16)
+_U8 = (torch.uint8, torch.float8_e4m3fn)
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _workspace(ws, nbytes, device):
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def index_score(q_idx, w_idx, k_idx, vis_len, scores=None, block_max=None, stream=None):
+    """Indexer scan: scores [B, n_q, N_cap] and/or block_max [B, n_q, ceil(N_cap/8)]."""
+    B, n_q = q_idx.shape[0], q_idx.shape[1]
+    N_cap = k_idx.shape[1]
+    kd = KDTYPE_BF16 if k_idx.dtype in _BITS16 else KDTYPE_FP8
+    _call("csa2_index_score", _ptr(q_idx, _BITS16, "q_idx"), _ptr(w_idx, _F32, "w_idx"),
+          _ptr(k_idx, _BITS16 + _U8, "k_idx"), kd, _ptr(vis_len, _I32, "vis_len"), B, n_q, N_cap,
+          _ptr(scores, _F32, "scores"), _ptr(block_max, _F32, "block_max"), None, 0,
+          _stream(stream))
+
+
+def block_topk(block_max, vis_len, N_cap, k_blocks, pool_blocks, stream=None):
+    """Pool of the top min(k_blocks, nb) blocks per query row, ascending, -1 padded."""
+    B, n_q = block_max.shape[0], block_max.shape[1]
+    _call("csa2_block_topk", _ptr(block_max, _F32, "block_max"), _ptr(vis_len, _I32, "vis_len"),
+          B, n_q, N_cap, k_blocks, _ptr(pool_blocks, _I32, "pool_blocks"), None, 0,
+          _stream(stream))
+
+
+def reindex_topk(mode, vis_len, N_cap, top_k, idx_out, scores=None, q_idx=None, w_idx=None,
+                 k_idx=None, pool_blocks=None, idx_score=None, ws=None, stream=None):
+    """Top-k inside the pool (Full / Reindex) or over [0, vis) without a pool."""
+    B, n_q = vis_len.shape[0], vis_len.shape[1]
+    k_blocks = pool_blocks.shape[-1] if pool_blocks is not None else 0
+    kd = KDTYPE_BF16 if (k_idx is None or k_idx.dtype in _BITS16) else KDTYPE_FP8
+    need = workspace_size(OP_REINDEX_TOPK, B, n_q, N_cap, top_k, k_blocks)
+    rescoring = pool_blocks is not None and not (mode == MODE_FULL and scores is not None)
+    ws, nbytes = _workspace(ws, need if rescoring else 0, vis_len.device)
+    _call("csa2_reindex_topk", mode, _ptr(scores, _F32, "scores"), _ptr(q_idx, _BITS16, "q_idx"),
+          _ptr(w_idx, _F32, "w_idx"), _ptr(k_idx, _BITS16 + _U8, "k_idx"), kd,
+          _ptr(pool_blocks, _I32, "pool_blocks"), k_blocks, _ptr(vis_len, _I32, "vis_len"),
+          B, n_q, N_cap, top_k, _ptr(idx_out, _I32, "idx_out"),
+          _ptr(idx_score, _F32, "idx_score"), _ptr(ws, (torch.uint8,), "ws"), nbytes,
+          _stream(stream))
+
+
+def _attn(name, q, kv_fp4, kv_scale, idx, swa_kv, swa_pos0, q_pos, sm_scale, out, lse=None,
+          window=128, replay_start=-1, ws=None, stream=None):
+    B, n_q = q.shape[0], q.shape[1]
+    N_cap = kv_fp4.shape[1]
+    top_k = idx.shape[-1] if idx is not None else 0
+    S_cap = swa_kv.shape[1] if swa_kv is not None else 0
+    need = workspace_size(OP_SPARSE_ATTN, B, n_q, N_cap, top_k, 0)
+    ws, nbytes = _workspace(ws, need, q.device)
+    opts = AttnOpts(window, replay_start, 0, 0)
+    _call(name, _ptr(q, _BITS16, "q"), _ptr(kv_fp4, _U8, "kv_fp4"),
+          _ptr(kv_scale, _U8, "kv_scale"), N_cap, _ptr(idx, _I32, "idx"), top_k,
+          _ptr(swa_kv, _U8, "swa_kv"), S_cap, _ptr(swa_pos0, _I32, "swa_pos0"),
+          _ptr(q_pos, _I32, "q_pos"), float(sm_scale), ctypes.byref(opts), B, n_q,
+          _ptr(out, _BITS16, "out"), _ptr(lse, _F32, "lse"), _ptr(ws, (torch.uint8,), "ws"),
+          nbytes, _stream(stream))
+
+
+def sparse_attn_decode(*args, **kw):
+    """Attention of a Full / Reindex layer over idx plus the SWA window."""
+    _attn("csa2_sparse_attn_decode", *args, **kw)
+
+
+def reuse_attn(*args, **kw):
+    """Attention of a Reuse layer (indices from an earlier layer, no indexer)."""
+    _attn("csa2_reuse_attn", *args, **kw)

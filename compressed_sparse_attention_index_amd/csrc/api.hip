@@ -1,0 +1,191 @@
+// C ABI of the CSA2 decode hot path: host-side validation and dispatch.
+// Every check runs before anything is enqueued; see include/csa2.h for the
+// contract of each entry point.
+#include "../../include/csa2.h"
+#include "csa2_launch.h"
+
+#include <stdint.h>
+
+namespace {
+
+constexpr int32_t kMaxNcap = 1 << 24;       // positions must fit the 24-bit id passes
+constexpr int32_t kMaxGridY = 65535;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+csa2_status from_hip(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
+
+int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
+
+csa2_status check_rows(int32_t B, int32_t n_q) {
+  if (B < 1 || n_q < 1) return CSA2_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * n_q > (1LL << 30)) return CSA2_ERR_SHAPE;
+  return CSA2_OK;
+}
+
+csa2_status attn_common(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
+                        int32_t N_cap, const int32_t* idx, int32_t top_k, const uint8_t* swa_kv,
+                        int32_t S_cap, const int32_t* swa_pos0, const int32_t* q_pos,
+                        float sm_scale, const csa2_attn_opts* opts, int32_t B, int32_t n_q,
+                        uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  if (!q || !kv_fp4 || !kv_scale || !swa_pos0 || !q_pos || !out) return CSA2_ERR_NULL;
+  if (top_k > 0 && !idx) return CSA2_ERR_NULL;
+  if (S_cap > 0 && !swa_kv) return CSA2_ERR_NULL;
+  csa2_status st = check_rows(B, n_q);
+  if (st != CSA2_OK) return st;
+  if (N_cap < 1 || N_cap > kMaxNcap || top_k < 0 || top_k > 512 || S_cap < 0) return CSA2_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * n_q > kMaxGridY) return CSA2_ERR_SHAPE;
+  if (!(sm_scale == sm_scale)) return CSA2_ERR_SHAPE;
+  int32_t window = 128, replay_start = -1;
+  if (opts) {
+    if (opts->kv_fmt != CSA2_KV_MXFP4_E8M0_32 || opts->reserved != 0) return CSA2_ERR_UNSUPPORTED;
+    if (opts->window < 0 || opts->window > 128 || opts->replay_start < -1) return CSA2_ERR_SHAPE;
+    window = opts->window;
+    replay_start = opts->replay_start;
+  }
+  const void* ptrs[] = {q, kv_fp4, kv_scale, idx, swa_kv, swa_pos0, q_pos, out, lse};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return CSA2_ERR_ALIGN;
+  const size_t need = csa2::attn_workspace_bytes(B * n_q, top_k);
+  if (need > 0 && (!ws || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return CSA2_ERR_ALIGN;
+  return from_hip(csa2::launch_sparse_attn(q, kv_fp4, kv_scale, N_cap, idx, top_k, swa_kv, S_cap,
+                                           swa_pos0, q_pos, sm_scale, window, replay_start, B,
+                                           n_q, out, lse, ws, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+csa2_status csa2_index_score(const uint16_t* q_idx, const float* w_idx, const void* k_idx,
+                             csa2_kdtype k_dtype, const int32_t* vis_len, int32_t B, int32_t n_q,
+                             int32_t N_cap, float* scores, float* block_max, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!q_idx || !w_idx || !k_idx || !vis_len) return CSA2_ERR_NULL;
+  if (!scores && !block_max) return CSA2_ERR_NULL;
+  if (k_dtype != CSA2_KDTYPE_BF16 && k_dtype != CSA2_KDTYPE_FP8_E4M3) return CSA2_ERR_UNSUPPORTED;
+  csa2_status st = check_rows(B, n_q);
+  if (st != CSA2_OK) return st;
+  if (N_cap < 1 || N_cap > kMaxNcap) return CSA2_ERR_SHAPE;
+  if (n_q < 16 && static_cast<int64_t>(B) * n_q > kMaxGridY) return CSA2_ERR_SHAPE;
+  if (n_q >= 16 && (B > kMaxGridY || ceil_div(n_q, 16) > kMaxGridY)) return CSA2_ERR_SHAPE;
+  const void* ptrs[] = {q_idx, w_idx, k_idx, vis_len, scores, block_max};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return CSA2_ERR_ALIGN;
+  return from_hip(csa2::launch_index_score(q_idx, w_idx, k_idx, k_dtype == CSA2_KDTYPE_FP8_E4M3,
+                                           vis_len, B, n_q, N_cap, scores, block_max, stream));
+}
+
+csa2_status csa2_block_topk(const float* block_max, const int32_t* vis_len, int32_t B,
+                            int32_t n_q, int32_t N_cap, int32_t k_blocks, int32_t* pool_blocks,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!block_max || !vis_len || !pool_blocks) return CSA2_ERR_NULL;
+  csa2_status st = check_rows(B, n_q);
+  if (st != CSA2_OK) return st;
+  if (N_cap < 1 || N_cap > kMaxNcap || k_blocks < 1 || k_blocks > 2048) return CSA2_ERR_SHAPE;
+  const void* ptrs[] = {block_max, vis_len, pool_blocks};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return CSA2_ERR_ALIGN;
+  return from_hip(csa2::launch_select(csa2::kSrcBlocks, block_max, nullptr, 0, vis_len, B * n_q,
+                                      N_cap, k_blocks, pool_blocks, nullptr, stream));
+}
+
+csa2_status csa2_reindex_topk(csa2_mode mode, const float* scores, const uint16_t* q_idx,
+                              const float* w_idx, const void* k_idx, csa2_kdtype k_dtype,
+                              const int32_t* pool_blocks, int32_t k_blocks,
+                              const int32_t* vis_len, int32_t B, int32_t n_q, int32_t N_cap,
+                              int32_t top_k, int32_t* idx_out, float* idx_score, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  if (mode != CSA2_MODE_FULL && mode != CSA2_MODE_REINDEX) return CSA2_ERR_UNSUPPORTED;
+  if (!vis_len || !idx_out) return CSA2_ERR_NULL;
+  csa2_status st = check_rows(B, n_q);
+  if (st != CSA2_OK) return st;
+  if (N_cap < 1 || N_cap > kMaxNcap || top_k < 1 || top_k > 512) return CSA2_ERR_SHAPE;
+  const int32_t rows = B * n_q;
+  const void* ptrs[] = {scores, q_idx, w_idx, k_idx, pool_blocks, vis_len, idx_out, idx_score, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return CSA2_ERR_ALIGN;
+  if (!pool_blocks) {
+    if (!scores) return CSA2_ERR_NULL;
+    return from_hip(csa2::launch_select(csa2::kSrcFlat, scores, nullptr, 0, vis_len, rows, N_cap,
+                                        top_k, idx_out, idx_score, stream));
+  }
+  if (k_blocks < 1 || k_blocks > 2048) return CSA2_ERR_SHAPE;
+  if (mode == CSA2_MODE_FULL && scores)
+    return from_hip(csa2::launch_select(csa2::kSrcPoolStored, scores, pool_blocks, k_blocks,
+                                        vis_len, rows, N_cap, top_k, idx_out, idx_score, stream));
+  if (!q_idx || !w_idx || !k_idx) return CSA2_ERR_NULL;
+  if (k_dtype != CSA2_KDTYPE_BF16 && k_dtype != CSA2_KDTYPE_FP8_E4M3) return CSA2_ERR_UNSUPPORTED;
+  if (rows > kMaxGridY) return CSA2_ERR_SHAPE;
+  const size_t need = static_cast<size_t>(rows) * k_blocks * 8 * sizeof(float);
+  if (!ws || ws_bytes < need) return CSA2_ERR_WORKSPACE;
+  float* pool_scores = static_cast<float*>(ws);
+  hipError_t e = csa2::launch_pool_rescore(q_idx, w_idx, k_idx, k_dtype == CSA2_KDTYPE_FP8_E4M3,
+                                           pool_blocks, k_blocks, vis_len, B, n_q, N_cap,
+                                           pool_scores, stream);
+  if (e != hipSuccess) return CSA2_ERR_HIP;
+  return from_hip(csa2::launch_select(csa2::kSrcPoolScored, pool_scores, pool_blocks, k_blocks,
+                                      vis_len, rows, N_cap, top_k, idx_out, idx_score, stream));
+}
+
+csa2_status csa2_sparse_attn_decode(const uint16_t* q, const uint8_t* kv_fp4,
+                                    const uint8_t* kv_scale, int32_t N_cap, const int32_t* idx,
+                                    int32_t top_k, const uint8_t* swa_kv, int32_t S_cap,
+                                    const int32_t* swa_pos0, const int32_t* q_pos, float sm_scale,
+                                    const csa2_attn_opts* opts, int32_t B, int32_t n_q,
+                                    uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  return attn_common(q, kv_fp4, kv_scale, N_cap, idx, top_k, swa_kv, S_cap, swa_pos0, q_pos,
+                     sm_scale, opts, B, n_q, out, lse, ws, ws_bytes, stream);
+}
+
+csa2_status csa2_reuse_attn(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
+                            int32_t N_cap, const int32_t* idx, int32_t top_k,
+                            const uint8_t* swa_kv, int32_t S_cap, const int32_t* swa_pos0,
+                            const int32_t* q_pos, float sm_scale, const csa2_attn_opts* opts,
+                            int32_t B, int32_t n_q, uint16_t* out, float* lse, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  return attn_common(q, kv_fp4, kv_scale, N_cap, idx, top_k, swa_kv, S_cap, swa_pos0, q_pos,
+                     sm_scale, opts, B, n_q, out, lse, ws, ws_bytes, stream);
+}
+
+size_t csa2_workspace_size(csa2_op op, int32_t B, int32_t n_q, int32_t N_cap, int32_t top_k,
+                           int32_t k_blocks) {
+  if (B < 1 || n_q < 1 || N_cap < 1) return static_cast<size_t>(-1);
+  const size_t rows = static_cast<size_t>(B) * n_q;
+  switch (op) {
+    case CSA2_OP_INDEX_SCORE:
+    case CSA2_OP_BLOCK_TOPK:
+      return 0;
+    case CSA2_OP_REINDEX_TOPK:
+      if (k_blocks < 0 || k_blocks > 2048) return static_cast<size_t>(-1);
+      return rows * static_cast<size_t>(k_blocks) * 8 * sizeof(float);
+    case CSA2_OP_SPARSE_ATTN:
+      if (top_k < 0 || top_k > 512) return static_cast<size_t>(-1);
+      return csa2::attn_workspace_bytes(static_cast<int>(rows), top_k);
+  }
+  return static_cast<size_t>(-1);
+}
+
+const char* csa2_status_string(csa2_status status) {
+  switch (status) {
+    case CSA2_OK: return "ok";
+    case CSA2_ERR_NULL: return "a required pointer is NULL";
+    case CSA2_ERR_SHAPE: return "invalid size or shape";
+    case CSA2_ERR_UNSUPPORTED: return "unsupported dtype, format, mode or option";
+    case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSA2_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case CSA2_ERR_HIP: return "HIP runtime or kernel launch error";
+  }
+  return "unknown status";
+}
+
+int32_t csa2_abi_version(void) { return CSA2_ABI_VERSION; }
+
+}  // extern "C"

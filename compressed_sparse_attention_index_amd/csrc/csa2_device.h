@@ -1,0 +1,97 @@
+// Device-side helpers shared by the CSA2 kernels (gfx950 / CDNA4 only).
+//
+// Number formats (OCP definitions; the method stores main KV as MXFP4 and SWA
+// KV as FP8 -- "DeepSeek-V4.1-Flash 架构详解", §4):
+//   FP8 E4M3FN -> bf16 and E2M1 (with an E8M0 block scale) -> bf16 use the
+//   gfx950 scaled-conversion instructions; both conversions are exact because
+//   every E4M3FN value and every E2M1 x 2^k value with k in the E8M0 range is
+//   a bf16 value.
+// Matrix cores: v_mfma_f32_32x32x16_bf16, wave64.  Operand layout (lane l):
+//   A[m][k]: m = l % 32, k = 8 * (l / 32) + i, i = 0..7
+//   B[k][n]: n = l % 32, k = 8 * (l / 32) + i
+//   D[m][n]: n = l % 32, m = 8 * (r / 4) + 4 * (l / 32) + (r % 4), r = 0..15
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kIdxHeads = 32;     // indexer heads
+constexpr int kIdxDim = 128;      // indexer dim
+constexpr int kHeads = 64;        // attention query heads
+constexpr int kDim = 512;         // attention head dim = entry dim
+constexpr int kBlock = 8;         // positions per pool block
+constexpr int kMaxTopK = 512;
+constexpr int kMaxPoolBlocks = 2048;
+constexpr int kMaxWindow = 128;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Four FP8 E4M3FN bytes -> four bf16 (two packed words).
+__device__ __forceinline__ u32x2 fp8x4_to_bf16(uint32_t w) {
+  u32x2 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+  return r;
+}
+
+// Eight FP8 bytes (two words) -> eight bf16 as an MFMA operand.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  u32x2 a = fp8x4_to_bf16(w0), b = fp8x4_to_bf16(w1);
+  u32x4 v = {a.x, a.y, b.x, b.y};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Eight E2M1 nibbles (one word, element 2j in the low nibble of byte j) with
+// one block scale -> eight bf16.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float scale) {
+  u32x4 v;
+  v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// E8M0 code -> 2^(code-127) as a float (code 0 gives the subnormal 2^-127,
+// code 255 gives NaN).
+__device__ __forceinline__ float e8m0_to_float(uint32_t code) {
+  if (code == 0) return __uint_as_float(0x00400000u);
+  if (code == 255) return __uint_as_float(0x7fc00000u);
+  return __uint_as_float(code << 23);
+}
+
+// Order-preserving map of fp32 to uint32: larger score -> larger key; -0 and
+// +0 map to the same key.
+__device__ __forceinline__ uint32_t float_to_key(float f) {
+  uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Value held by lane l ^ 32 (the other half of the wave).
+__device__ __forceinline__ float other_half(float v) {
+  uint32_t u = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ float wave_xor(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+}  // namespace csa2

@@ -1,0 +1,263 @@
+/*
+ * csa2.h -- C ABI of the CSA2 decode hot path on MI355X (gfx950).
+ *
+ * CSA2 (Compressed Sparse Attention 2) as described for DeepSeek-V4.1-Flash:
+ *   1. the hierarchical sparse indexer scores every visible main-KV entry with
+ *      a 32-head x 128-dim indexer query against one shared 128-dim indexer
+ *      key per entry, and takes the maximum score of each block of 8
+ *      positions;
+ *   2. a two-level Top-K keeps at most 2,048 blocks (a pool of at most 16,384
+ *      candidate positions) and then the Top-512 positions inside the pool;
+ *   3. sparse multi-query attention of 64 query heads of 512 dims over the
+ *      512 selected MXFP4 main-KV entries plus the 128-token FP8 sliding
+ *      window, with one softmax across both.
+ * Sources: "DeepSeek-V4.1-Flash 架构详解：CED、CSA2 与 890 字节 KV Cache"
+ * (gentlecold.top) -- §1 configuration table (64 x 512 query heads, 32 x 128
+ * indexer, top-k 512, pool <= 2048 blocks x 8, window 128), §3 mode table
+ * (Full / Reindex / Reuse), §3.2 Hierarchical Sparse Indexer, §4 MXFP4 main
+ * KV dequantised before attention and FP8 SWA KV; the DeepSeek-V4 essay at
+ * mlqm.cn (news 871487) §3.2 (indexer), §3.3 (window of the most recent 128
+ * uncompressed tokens), §4.3 (a compressed entry is both key and value).
+ * The indexer score formula is not printed on those pages; this library
+ * computes s_t = sum_h w_h * max(0, qI_h . KI_t).
+ *
+ * Conventions for every entry point
+ *   - All tensor arguments are DEVICE pointers to contiguous, row-major,
+ *     batch-major arrays with the shapes given below; the caller owns them.
+ *     bf16 values are passed as their uint16 bit patterns.
+ *   - Pointers must be 16-byte aligned (256 bytes recommended).
+ *   - Every call is asynchronous: it validates its host-side arguments,
+ *     enqueues kernels on `stream` and returns.  It never synchronises,
+ *     never allocates and never frees device memory.  Calls are ordered only
+ *     by their stream.
+ *   - On an argument error the call returns a status other than CSA2_OK and
+ *     enqueues nothing.  A failed kernel launch returns CSA2_ERR_HIP.  Faults
+ *     inside kernels surface at the caller's next synchronisation.
+ *   - Device-side index and length arguments are sanitised in the kernels,
+ *     never trusted for addressing: vis_len is clamped to [0, N_cap]; an index
+ *     outside [0, N_cap) is an empty slot; window positions outside the stored
+ *     window slots are skipped.
+ *   - Scratch memory comes only from the caller's workspace `ws` of
+ *     `ws_bytes` bytes, sized with csa2_workspace_size().  Calls that may run
+ *     at the same time must not share a workspace.  The workspace needs no
+ *     initialisation.
+ *   - The library keeps no state; it is thread-safe.
+ *   - Query rows: B sequences x n_q query tokens per sequence.  Decode uses
+ *     n_q = 1; an encoder prefill chunk uses n_q > 1 with per-query visible
+ *     lengths.
+ *   - Index lists are reported in ascending order and padded with -1.  Ties
+ *     in a selection are broken by the lower index, so results are
+ *     deterministic.
+ */
+#ifndef CSA2_H_
+#define CSA2_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_ABI_VERSION 1
+
+/* Symbols of the C ABI; everything else in the library is hidden. */
+#define CSA2_API __attribute__((visibility("default")))
+
+typedef enum {
+  CSA2_OK = 0,
+  CSA2_ERR_NULL = 1,         /* a required pointer is NULL */
+  CSA2_ERR_SHAPE = 2,        /* a size is negative, zero where it must not be, or too large */
+  CSA2_ERR_UNSUPPORTED = 3,  /* dtype, format, mode or option this build does not implement */
+  CSA2_ERR_WORKSPACE = 4,    /* workspace missing or smaller than csa2_workspace_size() */
+  CSA2_ERR_ALIGN = 5,        /* a pointer is not 16-byte aligned */
+  CSA2_ERR_HIP = 6           /* a HIP runtime call or kernel launch failed */
+} csa2_status;
+
+/* Storage type of the indexer keys. */
+typedef enum {
+  CSA2_KDTYPE_BF16 = 0,      /* 128 x bf16 = 256 bytes per entry */
+  CSA2_KDTYPE_FP8_E4M3 = 1   /* 128 x FP8 E4M3FN (OCP) = 128 bytes per entry */
+} csa2_kdtype;
+
+/* Storage format of main-KV entries (512 dims each). */
+typedef enum {
+  /* OCP MXFP4: E2M1 elements, two per byte (element 2j in the low nibble of
+     byte j), 256 bytes per entry, plus one E8M0 scale per 32 elements,
+     16 bytes per entry, stored in a separate array. */
+  CSA2_KV_MXFP4_E8M0_32 = 0
+} csa2_kvfmt;
+
+/* CSA2 layer modes ("DeepSeek-V4.1-Flash 架构详解", §3 mode table). */
+typedef enum {
+  CSA2_MODE_FULL = 0,     /* own indexer Q/K and Top-K; builds the pool */
+  CSA2_MODE_REINDEX = 1,  /* own indexer Q; re-scores only the pool against the Full layer's indexer K */
+  CSA2_MODE_REUSE = 2     /* no indexer; reuses the most recent Top-K indices */
+} csa2_mode;
+
+/* Operation ids for csa2_workspace_size(). */
+typedef enum {
+  CSA2_OP_INDEX_SCORE = 0,
+  CSA2_OP_BLOCK_TOPK = 1,
+  CSA2_OP_REINDEX_TOPK = 2,
+  CSA2_OP_SPARSE_ATTN = 3
+} csa2_op;
+
+/* Options of the attention entry points; NULL means the defaults. */
+typedef struct {
+  int32_t window;        /* SWA window in tokens, 0..128; default 128 */
+  int32_t replay_start;  /* first token a replayed window may see (window
+                            [max(s, i-W+1), i]); -1 = no truncation (default) */
+  int32_t kv_fmt;        /* csa2_kvfmt; default CSA2_KV_MXFP4_E8M0_32 */
+  int32_t reserved;      /* must be 0 */
+} csa2_attn_opts;
+
+/*
+ * csa2_index_score -- indexer scan (score every visible entry) with the block
+ * maximum over 8 positions fused in.
+ *   Computes, for query row r = b * n_q + j and every visible entry
+ *   t < vis_len[r]:
+ *     s[r][t] = sum_{h<32} w_idx[r][h] * max(0, sum_{d<128} q_idx[r][h][d] * k_idx[b][t][d])
+ *     block_max[r][i] = max_{t in [8i, min(8i+8, vis_len[r]))} s[r][t]
+ *   ("DeepSeek-V4.1-Flash 架构详解", §3.2: the Full layer scans every visible
+ *   entry and aggregates scores per block of 8 positions.)  Products are exact
+ *   in fp32 and accumulated in fp32.
+ * Arguments
+ *   q_idx     [B, n_q, 32, 128] bf16 indexer queries
+ *   w_idx     [B, n_q, 32] fp32 per-head weights
+ *   k_idx     [B, N_cap, 128] indexer keys of dtype k_dtype
+ *   vis_len   [B, n_q] int32 visible entries per query row
+ *   scores    [B, n_q, N_cap] fp32 output or NULL; entries t >= vis_len are not written
+ *   block_max [B, n_q, ceil(N_cap/8)] fp32 output or NULL; blocks past the
+ *             visible ones are not written.  At least one output must be given.
+ *   ws        unused (may be NULL; csa2_workspace_size returns 0)
+ */
+CSA2_API csa2_status csa2_index_score(const uint16_t* q_idx, const float* w_idx, const void* k_idx,
+                             csa2_kdtype k_dtype, const int32_t* vis_len, int32_t B, int32_t n_q,
+                             int32_t N_cap, float* scores, float* block_max, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/*
+ * csa2_block_topk -- first level of the Top-K: the pool of blocks.
+ *   Orders the nb = ceil(vis_len/8) visible blocks of each query row by
+ *   (block_max descending, block id ascending) and keeps the first
+ *   min(k_blocks, nb) ("DeepSeek-V4.1-Flash 架构详解", §3.2: at most 2,048
+ *   blocks of 8 positions, at most 16,384 candidates).
+ * Arguments
+ *   block_max   [B, n_q, ceil(N_cap/8)] fp32 (as written by csa2_index_score)
+ *   vis_len     [B, n_q] int32
+ *   k_blocks    1..2048
+ *   pool_blocks [B, n_q, k_blocks] int32 output: ascending block ids, -1 padded
+ */
+CSA2_API csa2_status csa2_block_topk(const float* block_max, const int32_t* vis_len, int32_t B,
+                            int32_t n_q, int32_t N_cap, int32_t k_blocks, int32_t* pool_blocks,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * csa2_reindex_topk -- second level of the Top-K.
+ *   With a pool (pool_blocks != NULL) the candidates are the visible
+ *   positions of the pool's blocks:
+ *     CSA2_MODE_FULL    keys are scores[r][t] when scores != NULL; with
+ *                       scores == NULL the pool positions are re-scored with
+ *                       q_idx / w_idx (the Full layer's own query) on k_idx.
+ *                       By construction this equals the Top-k over all
+ *                       visible positions when k_blocks * 8 >= top_k.
+ *     CSA2_MODE_REINDEX keys are the pool positions re-scored with this
+ *                       layer's q_idx / w_idx against the Full layer's k_idx
+ *                       ("DeepSeek-V4.1-Flash 架构详解", §3.2: a Reindex
+ *                       layer re-scores only the pool).
+ *   Without a pool (pool_blocks == NULL, FULL or REINDEX) the candidates are
+ *   all positions [0, vis_len) keyed by scores (flat Top-k of an encoder
+ *   prefill chunk; scores required).
+ *   The first min(top_k, #candidates) candidates in (key descending,
+ *   position ascending) order are kept.  CSA2_MODE_REUSE runs no indexer and
+ *   returns CSA2_ERR_UNSUPPORTED.
+ * Arguments
+ *   scores      [B, n_q, N_cap] fp32 or NULL (see above)
+ *   q_idx, w_idx, k_idx, k_dtype  as for csa2_index_score (may be NULL when
+ *               the keys come from scores)
+ *   pool_blocks [B, n_q, k_blocks] int32 ascending block ids, -1 padded, or NULL
+ *   vis_len     [B, n_q] int32
+ *   top_k       1..512
+ *   idx_out     [B, n_q, top_k] int32 output: ascending positions, -1 padded
+ *   idx_score   [B, n_q, top_k] fp32 output of the selected keys (-inf for
+ *               padding) or NULL
+ *   ws          csa2_workspace_size(CSA2_OP_REINDEX_TOPK, ...) bytes
+ */
+CSA2_API csa2_status csa2_reindex_topk(csa2_mode mode, const float* scores, const uint16_t* q_idx,
+                              const float* w_idx, const void* k_idx, csa2_kdtype k_dtype,
+                              const int32_t* pool_blocks, int32_t k_blocks,
+                              const int32_t* vis_len, int32_t B, int32_t n_q, int32_t N_cap,
+                              int32_t top_k, int32_t* idx_out, float* idx_score, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+
+/*
+ * csa2_sparse_attn_decode -- sparse multi-query attention of a Full or
+ * Reindex layer.
+ *   For query row r = b * n_q + j and head h < 64, the entry set is
+ *     E = { main entry idx[r][i] : 0 <= idx[r][i] < N_cap }
+ *         + { window token p : max(q_pos[r]-W+1, swa_pos0[b], replay_start, 0) <= p <= q_pos[r],
+ *                               p - swa_pos0[b] < S_cap }
+ *   (no de-duplication between the two parts).  Each entry v is used as key
+ *   and value.  Main entries are MXFP4, v[i] = E2M1(nibble i) *
+ *   2^(kv_scale[i/32] - 127); window entries are FP8 E4M3FN, slot
+ *   p - swa_pos0[b] of swa_kv.  Then
+ *     l_e = sm_scale * q[r][h] . v_e,  out[r][h] = sum_e softmax(l)_e v_e,
+ *     lse[r][h] = log sum_e exp(l_e)   (natural log; -inf for an empty set,
+ *                                       whose output is 0)
+ *   ("DeepSeek-V4.1-Flash 架构详解", §1 (64 x 512 heads, window 128), §4
+ *   (dequantised before attention), §9 step 5 (selected global KV plus this
+ *   layer's SWA KV); V4 essay §4.3 (an entry is both key and value).)
+ *   Dequantisation is exact in bf16; q.k and p.v run on bf16 matrix cores
+ *   with fp32 accumulation and an fp32 online softmax; out is rounded to bf16.
+ * Arguments
+ *   q         [B, n_q, 64, 512] bf16
+ *   kv_fp4    [B, N_cap, 256] uint8 packed E2M1
+ *   kv_scale  [B, N_cap, 16] uint8 E8M0
+ *   idx       [B, n_q, top_k] int32 entry indices, -1 = empty slot; top_k 0..512
+ *   swa_kv    [B, S_cap, 512] uint8 FP8 E4M3FN; slot i holds token swa_pos0[b] + i
+ *   swa_pos0  [B] int32
+ *   q_pos     [B, n_q] int32 token position of each query
+ *   opts      NULL or options (window, replay_start, kv_fmt)
+ *   out       [B, n_q, 64, 512] bf16 output
+ *   lse       [B, n_q, 64] fp32 output or NULL
+ *   ws        csa2_workspace_size(CSA2_OP_SPARSE_ATTN, ...) bytes
+ */
+CSA2_API csa2_status csa2_sparse_attn_decode(const uint16_t* q, const uint8_t* kv_fp4,
+                                    const uint8_t* kv_scale, int32_t N_cap, const int32_t* idx,
+                                    int32_t top_k, const uint8_t* swa_kv, int32_t S_cap,
+                                    const int32_t* swa_pos0, const int32_t* q_pos, float sm_scale,
+                                    const csa2_attn_opts* opts, int32_t B, int32_t n_q,
+                                    uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
+
+/*
+ * csa2_reuse_attn -- attention of a Reuse layer: the same computation and
+ * arguments as csa2_sparse_attn_decode, with idx taken from the most recent
+ * Full or Reindex layer and this layer's own q and swa_kv; no indexer runs
+ * ("DeepSeek-V4.1-Flash 架构详解", §3 mode table and §3.2).
+ */
+CSA2_API csa2_status csa2_reuse_attn(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
+                            int32_t N_cap, const int32_t* idx, int32_t top_k,
+                            const uint8_t* swa_kv, int32_t S_cap, const int32_t* swa_pos0,
+                            const int32_t* q_pos, float sm_scale, const csa2_attn_opts* opts,
+                            int32_t B, int32_t n_q, uint16_t* out, float* lse, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes an operation needs for the given sizes (0 if none);
+   returns (size_t)-1 for an unknown op or invalid sizes. */
+CSA2_API size_t csa2_workspace_size(csa2_op op, int32_t B, int32_t n_q, int32_t N_cap, int32_t top_k,
+                           int32_t k_blocks);
+
+/* Static description of a status code. */
+CSA2_API const char* csa2_status_string(csa2_status status);
+
+/* CSA2_ABI_VERSION of the built library. */
+CSA2_API int32_t csa2_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H_ */

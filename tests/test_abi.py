@@ -1,0 +1,128 @@
+"""The C-ABI library loads, exports what include/csa2.h declares, and rejects
+bad arguments on the host before touching a GPU (CPU only: no compute call
+here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from _helpers import ROOT, ensure_built
+
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    ensure_built()
+    import compressed_sparse_attention_index_amd as csa
+    return csa.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    decls = re.findall(r"CSA2_API\s+[\w\s\*]+?\b(csa2_\w+)\s*\(", open(HEADER).read())
+    assert len(decls) == 8
+    for name in decls:
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings(L):
+    assert L.csa2_abi_version() == 1
+    for st in range(7):
+        assert len(L.csa2_status_string(st)) > 0
+    assert L.csa2_status_string(0) == b"ok"
+
+
+def test_workspace_sizes(L):
+    import compressed_sparse_attention_index_amd as csa
+    assert csa.workspace_size(csa.OP_INDEX_SCORE, 8, 1, 1 << 20) == 0
+    assert csa.workspace_size(csa.OP_BLOCK_TOPK, 8, 1, 1 << 20) == 0
+    assert csa.workspace_size(csa.OP_REINDEX_TOPK, 8, 1, 1 << 20, 512, 2048) == 8 * 2048 * 8 * 4
+    assert csa.workspace_size(csa.OP_SPARSE_ATTN, 4096, 1, 1 << 16, 512, 0) == 0
+    assert csa.workspace_size(csa.OP_SPARSE_ATTN, 8, 1, 1 << 20, 512, 0) > 0
+    assert csa.workspace_size(7, 1, 1, 1) == ctypes.c_size_t(-1).value
+    assert csa.workspace_size(csa.OP_INDEX_SCORE, 0, 1, 1) == ctypes.c_size_t(-1).value
+
+
+A = 1 << 20      # a fake, 16-byte aligned "device" address: never dereferenced
+MIS = A + 4      # misaligned
+
+
+def _score(L, q=A, w=A, k=A, kd=1, vis=A, B=1, n_q=1, N=64, sc=A, bm=A):
+    return L.csa2_index_score(q, w, k, kd, vis, B, n_q, N, sc, bm, None, 0, None)
+
+
+def test_index_score_validation(L):
+    assert _score(L, q=None) == 1
+    assert _score(L, sc=None, bm=None) == 1
+    assert _score(L, kd=5) == 3
+    assert _score(L, B=0) == 2
+    assert _score(L, N=0) == 2
+    assert _score(L, N=(1 << 24) + 1) == 2
+    assert _score(L, B=70000) == 2
+    assert _score(L, k=MIS) == 5
+
+
+def test_block_topk_validation(L):
+    f = L.csa2_block_topk
+    assert f(None, A, 1, 1, 64, 16, A, None, 0, None) == 1
+    assert f(A, A, 1, 1, 64, 0, A, None, 0, None) == 2
+    assert f(A, A, 1, 1, 64, 2049, A, None, 0, None) == 2
+    assert f(A, A, 1, 1, 0, 16, A, None, 0, None) == 2
+    assert f(A, A, 1, 1, 64, 16, MIS, None, 0, None) == 5
+
+
+def _reindex(L, mode=1, sc=None, q=A, w=A, k=A, kd=1, pool=A, kb=2048, vis=A, B=1, n_q=1, N=1 << 20,
+             top_k=512, out=A, ws=None, ws_bytes=0):
+    return L.csa2_reindex_topk(mode, sc, q, w, k, kd, pool, kb, vis, B, n_q, N, top_k, out, None,
+                               ws, ws_bytes, None)
+
+
+def test_reindex_topk_validation(L):
+    assert _reindex(L, mode=2) == 3                 # Reuse runs no indexer
+    assert _reindex(L, mode=9) == 3
+    assert _reindex(L, out=None) == 1
+    assert _reindex(L, top_k=0) == 2
+    assert _reindex(L, top_k=513) == 2
+    assert _reindex(L, kb=0) == 2
+    assert _reindex(L, pool=None) == 1              # flat selection needs scores
+    assert _reindex(L, q=None) == 1                 # re-scoring needs the query
+    assert _reindex(L, kd=4) == 3
+    assert _reindex(L) == 4                         # no workspace for the re-scored pool
+    assert _reindex(L, ws=A, ws_bytes=2048 * 8 * 4 - 1) == 4
+    assert _reindex(L, vis=MIS) == 5
+
+
+def _attn(L, fn="csa2_sparse_attn_decode", q=A, fp4=A, sc=A, N=1 << 17, idx=A, top_k=512, swa=A,
+          S=128, p0=A, qp=A, scale=0.044, opts=None, B=64, n_q=1, out=A, lse=A, ws=None, wsb=0):
+    return getattr(L, fn)(q, fp4, sc, N, idx, top_k, swa, S, p0, qp, scale, opts, B, n_q, out, lse,
+                          ws, wsb, None)
+
+
+def test_attention_validation(L):
+    import compressed_sparse_attention_index_amd as csa
+    for fn in ("csa2_sparse_attn_decode", "csa2_reuse_attn"):
+        assert _attn(L, fn, q=None) == 1
+        assert _attn(L, fn, idx=None) == 1
+        assert _attn(L, fn, swa=None) == 1
+        assert _attn(L, fn, top_k=513) == 2
+        assert _attn(L, fn, top_k=-1) == 2
+        assert _attn(L, fn, S=-1) == 2
+        assert _attn(L, fn, N=0) == 2
+        assert _attn(L, fn, B=70000) == 2
+        assert _attn(L, fn, scale=float("nan")) == 2
+        bad_fmt = csa.AttnOpts(128, -1, 1, 0)
+        assert _attn(L, fn, opts=ctypes.byref(bad_fmt)) == 3
+        bad_win = csa.AttnOpts(129, -1, 0, 0)
+        assert _attn(L, fn, opts=ctypes.byref(bad_win)) == 2
+        assert _attn(L, fn, B=8) == 4                 # 8 rows split the entries: needs workspace
+        assert _attn(L, fn, out=MIS) == 5
+
+
+def test_binding_refuses_cpu_tensors(L):
+    import torch
+    import compressed_sparse_attention_index_amd as csa
+    x = torch.zeros(1, 1, 32, 128, dtype=torch.int16)
+    with pytest.raises(ValueError):
+        csa.index_score(x, torch.zeros(1, 1, 32), torch.zeros(1, 64, 128, dtype=torch.uint8),
+                        torch.zeros(1, 1, dtype=torch.int32), block_max=torch.zeros(1, 1, 8))

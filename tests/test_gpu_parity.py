@@ -1,0 +1,334 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Selections must agree exactly except for ties within 1e-6 of the k-th key;
+attention outputs within |g - o| <= 2e-3 + 1e-2 |o|.  Steps downstream of a
+selection are fed the GPU's selection (after it passed its own check), so a
+legal tie swap upstream cannot cascade.
+"""
+import numpy as np
+import pytest
+import torch
+
+from _helpers import check_attention, check_selection, u16
+from oracle import attention as oattn
+from oracle import formats, indexer, pipeline
+from oracle import topk as otopk
+import synth
+
+pytestmark = pytest.mark.gpu
+
+csa = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_lib():
+    global csa
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import compressed_sparse_attention_index_amd as m
+    m.lib()   # raises if the HIP library is missing
+    csa = m
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _kraw(d, b):
+    k = _np(d["k_idx"][b])
+    return (k.view(np.uint16), "bf16") if d["kdtype"] == "bf16" else (k, "fp8")
+
+
+def _scan(d, vis=None, want_scores=True):
+    B, n_q, N = d["B"], d["n_q"], d["k_idx"].shape[1]
+    vis_t = (d["vis_len"] if vis is None else torch.as_tensor(vis, dtype=torch.int32).reshape(B, n_q)).cuda()
+    sc = torch.full((B, n_q, N), float("nan"), device="cuda") if want_scores else None
+    bm = torch.full((B, n_q, (N + 7) // 8), float("nan"), device="cuda")
+    csa.index_score(d["q_idx"].cuda(), d["w_idx"].cuda(), d["k_idx"].cuda(), vis_t, scores=sc,
+                    block_max=bm)
+    torch.cuda.synchronize()
+    return vis_t, sc, bm
+
+
+# --------------------------------------------------------------------------- scan
+@pytest.mark.parametrize("kdtype,T", [("bf16", 2048), ("fp8", 2048), ("fp8", 4133)])
+def test_index_score_ragged(kdtype, T):
+    vis = [0, 1, 7, 8, 9, 33, 511, 512, 513, T - 1, T]
+    B = len(vis)
+    d = synth.decode_workload(B=B, T=T, kdtype=kdtype, seed=11, heavy_frac=0.01)
+    print(f"index_score kdtype={kdtype} T={T} vis={vis}", flush=True)
+    _, sc, bm = _scan(d, vis)
+    sc, bm = _np(sc), _np(bm)
+    for b, v in enumerate(vis):
+        kr, kd = _kraw(d, b)
+        ref = pipeline.scores_prefix(u16(d["q_idx"][b, 0]), _np(d["w_idx"][b, 0]), kr, kd, v)
+        g = sc[b, 0, :v].astype(np.float64)
+        tol = 1e-5 * np.abs(ref) + 1e-6 * (np.abs(ref).max() if v else 0)
+        assert np.all(np.abs(g - ref) <= tol), f"row {b}: max err {np.abs(g - ref).max()}"
+        assert np.all(np.isnan(sc[b, 0, v:])), "scores past vis_len must stay unwritten"
+        nb = (v + 7) // 8
+        bref = indexer.block_max(ref, v)
+        assert np.all(np.abs(bm[b, 0, :nb] - bref) <= 1e-5 * np.abs(bref) + 1e-6 * (np.abs(ref).max() if v else 0))
+        assert np.all(np.isnan(bm[b, 0, nb:]))
+
+
+def test_index_score_prefill_rows():
+    # Prefill-shaped call (n_q >= 16): per-row visible lengths, shared keys.
+    d = synth.prefill_workload(n_q=40, prefix_tokens=1000, seed=12)
+    print("index_score prefill n_q=40", flush=True)
+    vis_t, sc, bm = _scan(d)
+    sc, vis = _np(sc), _np(vis_t)[0]
+    kr, kd = _kraw(d, 0)
+    for j in range(40):
+        ref = pipeline.scores_prefix(u16(d["q_idx"][0, j]), _np(d["w_idx"][0, j]), kr, kd, vis[j])
+        g = sc[0, j, :vis[j]].astype(np.float64)
+        assert np.all(np.abs(g - ref) <= 1e-5 * np.abs(ref) + 1e-6 * np.abs(ref).max()), j
+        assert np.all(np.isnan(sc[0, j, vis[j]:]))
+
+
+# --------------------------------------------------------------------------- selection
+def _select_case(keys_rows, vis_rows, k, kind):
+    """GPU block/flat selection on given fp32 keys vs the oracle on the same fp32 keys."""
+    rows = len(keys_rows)
+    n = max(len(x) for x in keys_rows)
+    if kind == "blocks":
+        N = 8 * n
+        arr = torch.zeros(rows, 1, n, dtype=torch.float32)
+    else:
+        N = n
+        arr = torch.zeros(rows, 1, n, dtype=torch.float32)
+    for i, x in enumerate(keys_rows):
+        arr[i, 0, :len(x)] = torch.from_numpy(np.asarray(x, dtype=np.float32))
+    vis = torch.tensor(vis_rows, dtype=torch.int32).reshape(rows, 1).cuda()
+    out = torch.full((rows, 1, k), -7, dtype=torch.int32, device="cuda")
+    if kind == "blocks":
+        csa.block_topk(arr.cuda(), vis, N, k, out)
+    else:
+        ks = torch.zeros(rows, 1, k, device="cuda")
+        csa.reindex_topk(csa.MODE_FULL, vis, N, k, out, scores=arr.cuda(), idx_score=ks)
+    torch.cuda.synchronize()
+    out = _np(out)
+    for i in range(rows):
+        x32 = arr[i, 0].numpy().astype(np.float64)
+        if kind == "blocks":
+            nb = (vis_rows[i] + 7) // 8
+            ref = otopk.block_topk(x32[:nb], k)
+        else:
+            ref = otopk.flat_topk(x32, vis_rows[i], k)
+        assert np.array_equal(out[i, 0], ref), f"{kind} row {i}: exact selection differs"
+
+
+@pytest.mark.parametrize("kind", ["blocks", "flat"])
+def test_select_exact_on_fp32_keys(kind):
+    rng = np.random.default_rng(21)
+    rows, vis = [], []
+    n = 9000
+    cases = [
+        rng.standard_normal(n),                         # distinct
+        np.round(rng.standard_normal(n) * 4) / 4,       # heavy ties
+        np.full(n, 3.25),                               # all equal
+        -np.abs(rng.standard_normal(n)),                # negative
+        np.where(rng.uniform(size=n) < 0.5, 0.0, rng.standard_normal(n)),  # many zeros
+        rng.standard_normal(n) * 1e-30,                 # tiny range
+        np.concatenate([rng.standard_normal(5000) + 1e6, rng.standard_normal(4000)]),  # two clusters
+    ]
+    vis_sizes = [n, n, n, n, 4001, 17, 0]
+    for c, v in zip(cases, vis_sizes):
+        rows.append(c)
+        vis.append(8 * v if kind == "blocks" else v)
+    if kind == "blocks":
+        vis = [min(x, 8 * n) for x in vis]
+    print(f"select {kind}", flush=True)
+    for k in ((1, 16, 512, 2048) if kind == "blocks" else (1, 16, 100, 512)):
+        _select_case(rows, vis, k, kind)
+
+
+def test_pool_topk_stored_scores_exact():
+    # FULL mode from stored scores at the pool positions (fp32 keys, exact).
+    rng = np.random.default_rng(22)
+    rows, N, kb = 5, 20000, 2048
+    sc = rng.standard_normal((rows, 1, N)).astype(np.float32)
+    sc[1] = np.round(sc[1] * 2) / 2
+    sc[2] = 1.0
+    vis = np.array([N, N, N, 9999, 5], dtype=np.int32)
+    pools = np.full((rows, 1, kb), -1, np.int32)
+    for i in range(rows):
+        nb = (vis[i] + 7) // 8
+        sel = np.sort(rng.choice(nb, size=min(nb, 1500), replace=False))
+        pools[i, 0, :len(sel)] = sel
+    out = torch.zeros(rows, 1, 512, dtype=torch.int32, device="cuda")
+    ks = torch.zeros(rows, 1, 512, device="cuda")
+    csa.reindex_topk(csa.MODE_FULL, torch.from_numpy(vis).reshape(rows, 1).cuda(), N, 512, out,
+                     scores=torch.from_numpy(sc).cuda(), pool_blocks=torch.from_numpy(pools).cuda(),
+                     idx_score=ks)
+    torch.cuda.synchronize()
+    out, ks = _np(out), _np(ks)
+    for i in range(rows):
+        pos = otopk.pool_positions(pools[i, 0], vis[i])
+        ref = otopk.pool_topk(sc[i, 0, pos].astype(np.float64), pos, 512)
+        assert np.array_equal(out[i, 0], ref), i
+        m = ref >= 0
+        assert np.array_equal(ks[i, 0, m], sc[i, 0, ref[m]])
+        assert np.all(np.isneginf(ks[i, 0, ~m]))
+
+
+# --------------------------------------------------------------------------- Full / Reindex layers
+def _full_layer_gpu(d, rescore_full):
+    B, N = d["B"], d["k_idx"].shape[1]
+    vis_t, sc, bm = _scan(d, want_scores=not rescore_full)
+    pool = torch.zeros(B, 1, 2048, dtype=torch.int32, device="cuda")
+    csa.block_topk(bm, vis_t, N, 2048, pool)
+    idx = torch.zeros(B, 1, 512, dtype=torch.int32, device="cuda")
+    if rescore_full:
+        csa.reindex_topk(csa.MODE_FULL, vis_t, N, 512, idx, q_idx=d["q_idx"].cuda(),
+                         w_idx=d["w_idx"].cuda(), k_idx=d["k_idx"].cuda(), pool_blocks=pool)
+    else:
+        csa.reindex_topk(csa.MODE_FULL, vis_t, N, 512, idx, scores=sc, pool_blocks=pool)
+    torch.cuda.synchronize()
+    return vis_t, bm, pool, idx
+
+
+def _check_full_row(d, b, bm, pool, idx, vis):
+    kr, kd = _kraw(d, b)
+    ref = pipeline.full_layer(u16(d["q_idx"][b, 0]), _np(d["w_idx"][b, 0]), kr, kd, vis)
+    check_selection(_np(pool[b, 0]), ref["pool"], lambda j: ref["block_max"][j], what=f"pool row {b}")
+    # Pool Top-512 against the oracle run on the GPU's pool (hierarchy invariant:
+    # also the global Top-512 whenever the pools agree).
+    pos = otopk.pool_positions(_np(pool[b, 0]), vis)
+    ref_idx = otopk.pool_topk(ref["scores"][pos], pos, 512)
+    check_selection(_np(idx[b, 0]), ref_idx, lambda t: ref["scores"][t], what=f"idx row {b}")
+    return ref
+
+
+@pytest.mark.parametrize("rescore_full", [False, True])
+@pytest.mark.parametrize("T,kdtype", [(2048, "bf16"), (20011, "fp8"), (16384, "fp8"), (200, "fp8")])
+def test_full_layer(T, kdtype, rescore_full):
+    d = synth.decode_workload(B=3, T=T, kdtype=kdtype, seed=31, heavy_frac=0.01)
+    print(f"full layer T={T} {kdtype} rescore={rescore_full}", flush=True)
+    vis_t, bm, pool, idx = _full_layer_gpu(d, rescore_full)
+    for b in range(3):
+        _check_full_row(d, b, bm, pool, idx, T)
+
+
+def test_reindex_layer():
+    T = 40000
+    d = synth.decode_workload(B=2, T=T, kdtype="fp8", seed=32, lognormal_sigma=0.5, reindex=True)
+    print("reindex layer", flush=True)
+    vis_t, bm, pool, _ = _full_layer_gpu(d, True)
+    idx2 = torch.zeros(2, 1, 512, dtype=torch.int32, device="cuda")
+    csa.reindex_topk(csa.MODE_REINDEX, vis_t, T, 512, idx2, q_idx=d["q_idx2"].cuda(),
+                     w_idx=d["w_idx2"].cuda(), k_idx=d["k_idx"].cuda(), pool_blocks=pool)
+    torch.cuda.synchronize()
+    for b in range(2):
+        kr, kd = _kraw(d, b)
+        re = pipeline.reindex_layer(u16(d["q_idx2"][b, 0]), _np(d["w_idx2"][b, 0]), kr, kd,
+                                    _np(pool[b, 0]), T)
+        key = dict(zip(re["positions"].tolist(), re["scores"].tolist()))
+        check_selection(_np(idx2[b, 0]), re["idx"], lambda t: np.array([key[int(x)] for x in t]),
+                        what=f"reindex row {b}")
+
+
+# --------------------------------------------------------------------------- attention
+def _attn_gpu(d, idx, q=None, swa=None, window=128, replay_start=-1, reuse=False):
+    q = d["q"] if q is None else q
+    swa = d["swa"] if swa is None else swa
+    B, n_q = q.shape[0], q.shape[1]
+    out = torch.zeros(B, n_q, 64, 512, dtype=torch.int16, device="cuda")
+    lse = torch.zeros(B, n_q, 64, device="cuda")
+    fn = csa.reuse_attn if reuse else csa.sparse_attn_decode
+    fn(q.cuda(), d["kv_fp4"].cuda(), d["kv_scale"].cuda(), idx.cuda(), swa.cuda(),
+       d["swa_pos0"].cuda(), d["q_pos"].cuda(), d["sm_scale"], out, lse=lse, window=window,
+       replay_start=replay_start)
+    torch.cuda.synchronize()
+    return u16(out), _np(lse)
+
+
+def _attn_ref(d, b, j, idx_row, q=None, swa=None, window=128, replay_start=-1):
+    q = d["q"] if q is None else q
+    swa = d["swa"] if swa is None else swa
+    idx_row = np.asarray(idx_row, dtype=np.int64)
+    sel = idx_row[idx_row >= 0]
+    fp4 = _np(d["kv_fp4"][b][torch.as_tensor(sel, dtype=torch.long, device=d["kv_fp4"].device)])
+    sc = _np(d["kv_scale"][b][torch.as_tensor(sel, dtype=torch.long, device=d["kv_scale"].device)])
+    return pipeline.attention(u16(q[b, j]), fp4, sc, np.arange(len(sel)), _np(swa[b]),
+                              int(d["swa_pos0"][b]), int(d["q_pos"][b, j]), d["sm_scale"],
+                              window, replay_start)
+
+
+@pytest.mark.parametrize("case", ["topk512", "ragged", "invalid", "dense", "window16", "replay",
+                                  "seq_start", "no_main"])
+def test_attention_cases(case):
+    T, B = 2048, 3
+    d = synth.decode_workload(B=B, T=T, kdtype="bf16", seed=41)
+    rng = np.random.default_rng(41)
+    window, replay = 128, -1
+    top_k = 512
+    if case == "ragged":
+        top_k = 100
+    if case == "dense":
+        top_k = 300
+    if case == "no_main":
+        top_k = 0
+    idx = np.stack([np.sort(rng.choice(T, size=max(top_k, 1), replace=False))[:top_k] for _ in range(B)])
+    if case == "dense":
+        idx = np.tile(np.arange(300), (B, 1))
+    if case == "invalid":
+        idx[:, ::3] = -1
+        idx[0, :] = -1
+    if case == "window16":
+        window = 16
+    if case == "replay":
+        replay = T - 50
+    if case == "seq_start":
+        # queries near the sequence start: the window holds positions 0..q_pos
+        d["swa_pos0"][:] = 0
+        d["q_pos"][:, 0] = torch.tensor([0, 5, 127], dtype=torch.int32)
+    idx_t = torch.from_numpy(idx.astype(np.int32)).reshape(B, 1, top_k)
+    print(f"attention case={case}", flush=True)
+    out, lse = _attn_gpu(d, idx_t, window=window, replay_start=replay)
+    for b in range(B):
+        o, l = _attn_ref(d, b, 0, idx[b], window=window, replay_start=replay)
+        check_attention(out[b, 0], lse[b, 0], o, l, what=f"{case} row {b}")
+
+
+def test_attention_dense_equals_sdpa_through_gpu():
+    # Every entry selected: the GPU result matches dense attention over all entries.
+    T = 256
+    d = synth.decode_workload(B=1, T=T, kdtype="bf16", seed=42)
+    idx = torch.arange(T, dtype=torch.int32).reshape(1, 1, T)
+    out, lse = _attn_gpu(d, idx)
+    kv = np.concatenate([formats.mxfp4_to_f64(_np(d["kv_fp4"][0]), _np(d["kv_scale"][0])),
+                         formats.e4m3_to_f64(_np(d["swa"][0]))])
+    qf = formats.bf16_to_f64(u16(d["q"][0, 0]))
+    qt = torch.from_numpy(qf)[None, :, None, :]
+    kt = torch.from_numpy(kv)[None, None].expand(1, 64, -1, -1)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, kt, scale=d["sm_scale"])
+    check_attention(out[0, 0], None, ref[0, :, 0].numpy(), None, what="dense")
+
+
+def test_attention_single_split_and_reuse_identical():
+    # 512 query rows: each workgroup covers a whole row (no split partials).
+    d = synth.prefill_workload(n_q=512, prefix_tokens=4000, seed=43)
+    N = d["kv_fp4"].shape[1]
+    rng = np.random.default_rng(43)
+    vis = _np(d["vis_len"])[0]
+    idx = np.stack([np.sort(rng.choice(v, size=512, replace=False)) for v in vis]).astype(np.int32)
+    idx_t = torch.from_numpy(idx).reshape(1, 512, 512)
+    print("attention 512 rows", flush=True)
+    out, lse = _attn_gpu(d, idx_t)
+    out2, lse2 = _attn_gpu(d, idx_t, reuse=True)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+    for j in (0, 1, 255, 511):
+        o, l = _attn_ref(d, 0, j, idx[j])
+        check_attention(out[0, j], lse[0, j], o, l, what=f"prefill row {j}")
+    assert N == 2000 + 256
+
+
+def test_deterministic_reruns():
+    d = synth.decode_workload(B=2, T=30000, kdtype="fp8", seed=44)
+    a = _full_layer_gpu(d, True)
+    b = _full_layer_gpu(d, True)
+    for x, y in zip(a[1:], b[1:]):
+        assert torch.equal(x, y)
+    o1 = _attn_gpu(d, a[3].cpu())
+    o2 = _attn_gpu(d, a[3].cpu())
+    assert np.array_equal(o1[0], o2[0]) and np.array_equal(o1[1], o2[1])
