@@ -161,7 +161,7 @@ def decode_workload(B, T, kdtype="fp8", seed=0, device="cpu", heavy_frac=0.0,
     if supplied_idx:
         k = min(TOP_K, T)
         idx = torch.stack([torch.sort(gen.perm(T)[:k]).values for _ in range(B)])
-        d["idx"] = idx.to(torch.int32)
+        d["idx"] = idx.to(torch.int32).reshape(B, 1, k)
     d["vis_len"] = torch.full((B, 1), T, dtype=torch.int32, device=gen.device)
     d["swa_pos0"] = torch.full((B,), T - s, dtype=torch.int32, device=gen.device)
     d["q_pos"] = torch.full((B, 1), T - 1, dtype=torch.int32, device=gen.device)
