@@ -129,12 +129,14 @@ def index_score(q_idx, w_idx, k_idx, vis_len, scores=None, block_max=None, strea
           _stream(stream))
 
 
-def block_topk(block_max, vis_len, N_cap, k_blocks, pool_blocks, stream=None):
+def block_topk(block_max, vis_len, N_cap, k_blocks, pool_blocks, ws=None, stream=None):
     """Pool of the top min(k_blocks, nb) blocks per query row, ascending, -1 padded."""
     B, n_q = block_max.shape[0], block_max.shape[1]
+    ws, nbytes = _workspace(ws, workspace_size(OP_BLOCK_TOPK, B, n_q, N_cap, 0, k_blocks),
+                            block_max.device)
     _call("csa2_block_topk", _ptr(block_max, _F32, "block_max"), _ptr(vis_len, _I32, "vis_len"),
-          B, n_q, N_cap, k_blocks, _ptr(pool_blocks, _I32, "pool_blocks"), None, 0,
-          _stream(stream))
+          B, n_q, N_cap, k_blocks, _ptr(pool_blocks, _I32, "pool_blocks"),
+          _ptr(ws, (torch.uint8,), "ws"), nbytes, _stream(stream))
 
 
 def reindex_topk(mode, vis_len, N_cap, top_k, idx_out, scores=None, q_idx=None, w_idx=None,
@@ -144,8 +146,7 @@ def reindex_topk(mode, vis_len, N_cap, top_k, idx_out, scores=None, q_idx=None, 
     k_blocks = pool_blocks.shape[-1] if pool_blocks is not None else 0
     kd = KDTYPE_BF16 if (k_idx is None or k_idx.dtype in _BITS16) else KDTYPE_FP8
     need = workspace_size(OP_REINDEX_TOPK, B, n_q, N_cap, top_k, k_blocks)
-    rescoring = pool_blocks is not None and not (mode == MODE_FULL and scores is not None)
-    ws, nbytes = _workspace(ws, need if rescoring else 0, vis_len.device)
+    ws, nbytes = _workspace(ws, need if pool_blocks is not None else 0, vis_len.device)
     _call("csa2_reindex_topk", mode, _ptr(scores, _F32, "scores"), _ptr(q_idx, _BITS16, "q_idx"),
           _ptr(w_idx, _F32, "w_idx"), _ptr(k_idx, _BITS16 + _U8, "k_idx"), kd,
           _ptr(pool_blocks, _I32, "pool_blocks"), k_blocks, _ptr(vis_len, _I32, "vis_len"),

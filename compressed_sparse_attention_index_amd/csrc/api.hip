@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int32_t kMaxNcap = 1 << 24;       // positions must fit the 24-bit id passes
+constexpr int32_t kMaxNcap = 1 << 22;       // block ids fit the selection bitmap in LDS
 constexpr int32_t kMaxGridY = 65535;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -83,17 +83,18 @@ csa2_status csa2_index_score(const uint16_t* q_idx, const float* w_idx, const vo
 csa2_status csa2_block_topk(const float* block_max, const int32_t* vis_len, int32_t B,
                             int32_t n_q, int32_t N_cap, int32_t k_blocks, int32_t* pool_blocks,
                             void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (!block_max || !vis_len || !pool_blocks) return CSA2_ERR_NULL;
   csa2_status st = check_rows(B, n_q);
   if (st != CSA2_OK) return st;
   if (N_cap < 1 || N_cap > kMaxNcap || k_blocks < 1 || k_blocks > 2048) return CSA2_ERR_SHAPE;
-  const void* ptrs[] = {block_max, vis_len, pool_blocks};
+  if (static_cast<int64_t>(B) * n_q > kMaxGridY) return CSA2_ERR_SHAPE;
+  const void* ptrs[] = {block_max, vis_len, pool_blocks, ws};
   for (const void* p : ptrs)
-    if (!aligned16(p)) return CSA2_ERR_ALIGN;
-  return from_hip(csa2::launch_select(csa2::kSrcBlocks, block_max, nullptr, 0, vis_len, B * n_q,
-                                      N_cap, k_blocks, pool_blocks, nullptr, stream));
+    if (p && !aligned16(p)) return CSA2_ERR_ALIGN;
+  const size_t need = csa2::block_topk_workspace_bytes(B * n_q, N_cap);
+  if (!ws || ws_bytes < need) return CSA2_ERR_WORKSPACE;
+  return from_hip(csa2::launch_block_topk(block_max, vis_len, B * n_q, N_cap, k_blocks,
+                                          pool_blocks, ws, stream));
 }
 
 csa2_status csa2_reindex_topk(csa2_mode mode, const float* scores, const uint16_t* q_idx,
@@ -113,25 +114,23 @@ csa2_status csa2_reindex_topk(csa2_mode mode, const float* scores, const uint16_
     if (p && !aligned16(p)) return CSA2_ERR_ALIGN;
   if (!pool_blocks) {
     if (!scores) return CSA2_ERR_NULL;
-    return from_hip(csa2::launch_select(csa2::kSrcFlat, scores, nullptr, 0, vis_len, rows, N_cap,
-                                        top_k, idx_out, idx_score, stream));
+    return from_hip(csa2::launch_flat_topk(scores, vis_len, rows, N_cap, top_k, idx_out,
+                                           idx_score, stream));
   }
   if (k_blocks < 1 || k_blocks > 2048) return CSA2_ERR_SHAPE;
-  if (mode == CSA2_MODE_FULL && scores)
-    return from_hip(csa2::launch_select(csa2::kSrcPoolStored, scores, pool_blocks, k_blocks,
-                                        vis_len, rows, N_cap, top_k, idx_out, idx_score, stream));
-  if (!q_idx || !w_idx || !k_idx) return CSA2_ERR_NULL;
-  if (k_dtype != CSA2_KDTYPE_BF16 && k_dtype != CSA2_KDTYPE_FP8_E4M3) return CSA2_ERR_UNSUPPORTED;
   if (rows > kMaxGridY) return CSA2_ERR_SHAPE;
-  const size_t need = static_cast<size_t>(rows) * k_blocks * 8 * sizeof(float);
+  const bool stored = mode == CSA2_MODE_FULL && scores;
+  if (!stored) {
+    if (!q_idx || !w_idx || !k_idx) return CSA2_ERR_NULL;
+    if (k_dtype != CSA2_KDTYPE_BF16 && k_dtype != CSA2_KDTYPE_FP8_E4M3)
+      return CSA2_ERR_UNSUPPORTED;
+  }
+  const size_t need = csa2::pool_topk_workspace_bytes(rows, k_blocks);
   if (!ws || ws_bytes < need) return CSA2_ERR_WORKSPACE;
-  float* pool_scores = static_cast<float*>(ws);
-  hipError_t e = csa2::launch_pool_rescore(q_idx, w_idx, k_idx, k_dtype == CSA2_KDTYPE_FP8_E4M3,
-                                           pool_blocks, k_blocks, vis_len, B, n_q, N_cap,
-                                           pool_scores, stream);
-  if (e != hipSuccess) return CSA2_ERR_HIP;
-  return from_hip(csa2::launch_select(csa2::kSrcPoolScored, pool_scores, pool_blocks, k_blocks,
-                                      vis_len, rows, N_cap, top_k, idx_out, idx_score, stream));
+  const int kmode = stored ? 0 : (k_dtype == CSA2_KDTYPE_FP8_E4M3 ? 1 : 2);
+  return from_hip(csa2::launch_pool_topk(kmode, scores, q_idx, w_idx, k_idx, pool_blocks, k_blocks,
+                                         vis_len, rows, n_q, N_cap, top_k, idx_out, idx_score, ws,
+                                         stream));
 }
 
 csa2_status csa2_sparse_attn_decode(const uint16_t* q, const uint8_t* kv_fp4,
@@ -161,11 +160,12 @@ size_t csa2_workspace_size(csa2_op op, int32_t B, int32_t n_q, int32_t N_cap, in
   const size_t rows = static_cast<size_t>(B) * n_q;
   switch (op) {
     case CSA2_OP_INDEX_SCORE:
-    case CSA2_OP_BLOCK_TOPK:
       return 0;
+    case CSA2_OP_BLOCK_TOPK:
+      return csa2::block_topk_workspace_bytes(static_cast<int>(rows), N_cap);
     case CSA2_OP_REINDEX_TOPK:
       if (k_blocks < 0 || k_blocks > 2048) return static_cast<size_t>(-1);
-      return rows * static_cast<size_t>(k_blocks) * 8 * sizeof(float);
+      return csa2::pool_topk_workspace_bytes(static_cast<int>(rows), k_blocks);
     case CSA2_OP_SPARSE_ATTN:
       if (top_k < 0 || top_k > 512) return static_cast<size_t>(-1);
       return csa2::attn_workspace_bytes(static_cast<int>(rows), top_k);

@@ -11,19 +11,24 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w_idx, const v
                               bool fp8, const int32_t* vis_len, int B, int n_q, int N_cap,
                               float* scores, float* block_max, hipStream_t stream);
 
-// Re-scores the pool positions of every query row into pool_scores
-// [B * n_q, k_blocks * 8] (-inf for empty or invisible slots).
-hipError_t launch_pool_rescore(const uint16_t* q_idx, const float* w_idx, const void* k_idx,
-                               bool fp8, const int32_t* pool_blocks, int k_blocks,
-                               const int32_t* vis_len, int B, int n_q, int N_cap,
-                               float* pool_scores, hipStream_t stream);
+// Block Top-K (pool of blocks); see topk.hip.
+size_t block_topk_workspace_bytes(int rows, int N_cap);
+int block_topk_max_blocks();
+hipError_t launch_block_topk(const float* block_max, const int32_t* vis_len, int rows, int N_cap,
+                             int k, int32_t* out, void* ws, hipStream_t stream);
 
-enum SelectSource { kSrcBlocks = 0, kSrcPoolStored = 1, kSrcPoolScored = 2, kSrcFlat = 3 };
+// Pool Top-K.  mode 0: keys are stored scores; 1 / 2: the pool positions are
+// re-scored with q_idx / w_idx on FP8 / bf16 keys.
+size_t pool_topk_workspace_bytes(int rows, int k_blocks);
+hipError_t launch_pool_topk(int mode, const float* scores, const uint16_t* q_idx,
+                            const float* w_idx, const void* k_idx, const int32_t* pool_blocks,
+                            int k_blocks, const int32_t* vis_len, int rows, int n_q, int N_cap,
+                            int top_k, int32_t* out, float* out_key, void* ws,
+                            hipStream_t stream);
 
-// Exact Top-k selection, one workgroup per query row.  See topk.hip.
-hipError_t launch_select(SelectSource src, const float* keys, const int32_t* pool_blocks,
-                         int k_blocks, const int32_t* vis_len, int rows, int N_cap, int k,
-                         int32_t* out_ids, float* out_keys, hipStream_t stream);
+// Flat Top-K over [0, vis) of every row (prefill rows).
+hipError_t launch_flat_topk(const float* scores, const int32_t* vis_len, int rows, int N_cap,
+                            int k, int32_t* out, float* out_key, hipStream_t stream);
 
 size_t attn_workspace_bytes(int rows, int top_k);
 

@@ -1,0 +1,179 @@
+// Workgroup primitives of the exact Top-K selection (NT threads, wave64).
+//
+// Keys are order-preserving uint32 images of fp32 scores; a selection takes
+// the first k items in (key descending, id ascending) order.  Radix selection
+// finds the k-th key K* and, among items whose key equals K*, the largest id
+// I* still taken; an item is selected iff
+//     key > K*  or  (key == K* and id <= I*).
+#pragma once
+#include "csa2_device.h"
+
+namespace csa2 {
+
+constexpr int kHistBits = 12;                 // first-level bins: key bits [31:20]
+constexpr int kHistBins = 1 << kHistBits;
+constexpr int kHistShift = 32 - kHistBits;
+
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Appends `pred` lanes of the wave to a list through one atomic per wave;
+// returns each predicated lane's slot.  Call with the whole wave.
+__device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter) {
+  const uint64_t m = __ballot(pred);
+  if (m == 0) return 0;
+  const int lane = lane_id();
+  const int leader = __ffsll(static_cast<long long>(m)) - 1;
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(counter, static_cast<uint32_t>(__popcll(m)));
+  base = __shfl(base, leader, 64);
+  return base + static_cast<uint32_t>(__popcll(m & ((1ull << lane) - 1ull)));
+}
+
+template <int NT>
+struct Wg {
+  static constexpr int kWaves = NT / 64;
+  static constexpr int kScratch = 2 * kWaves + 4;   // uint32 words of scratch
+
+  // Exclusive prefix sum in thread order; *total receives the sum.
+  __device__ static uint32_t excl_scan(uint32_t v, uint32_t* wb, uint32_t* total) {
+    const int wave = threadIdx.x >> 6, lane = lane_id();
+    const uint32_t inc = wave_incl_scan_u32(v);
+    if (lane == 63) wb[wave] = inc;
+    __syncthreads();
+    if (wave == 0) {
+      const uint32_t t = lane < kWaves ? wb[lane] : 0u;
+      const uint32_t ti = wave_incl_scan_u32(t);
+      if (lane < kWaves) wb[kWaves + lane] = ti - t;
+      if (lane == kWaves - 1) wb[2 * kWaves] = ti;
+    }
+    __syncthreads();
+    const uint32_t r = wb[kWaves + wave] + inc - v;
+    *total = wb[2 * kWaves];
+    __syncthreads();
+    return r;
+  }
+
+  __device__ static uint32_t sum(uint32_t v, uint32_t* wb) {
+    uint32_t t;
+    excl_scan(v, wb, &t);
+    return t;
+  }
+
+  // Bin holding the item of 1-based rank `rank`, counting from the top bin
+  // down (descending) or from bin 0 up; *before = items in bins passed first.
+  // `hist` may be in LDS or global memory.  Needs 1 <= rank <= total.
+  __device__ static int find_rank_bin(const uint32_t* hist, int nbins, uint32_t rank,
+                                      bool descending, uint32_t* wb, uint32_t* before) {
+    const int per = (nbins + NT - 1) / NT;
+    const int t = threadIdx.x;
+    uint32_t s = 0;
+    for (int i = 0; i < per; ++i) {
+      const int idx = t * per + i;
+      if (idx < nbins) s += hist[descending ? nbins - 1 - idx : idx];
+    }
+    uint32_t tot;
+    uint32_t p = excl_scan(s, wb, &tot);
+    if (p < rank && rank <= p + s) {
+      for (int i = 0; i < per; ++i) {
+        const int idx = t * per + i;
+        const int bin = descending ? nbins - 1 - idx : idx;
+        const uint32_t c = hist[bin];
+        if (rank <= p + c) {
+          wb[2 * kWaves + 1] = static_cast<uint32_t>(bin);
+          wb[2 * kWaves + 2] = p;
+          break;
+        }
+        p += c;
+      }
+    }
+    __syncthreads();
+    const int bin = static_cast<int>(wb[2 * kWaves + 1]);
+    *before = wb[2 * kWaves + 2];
+    __syncthreads();
+    return bin;
+  }
+
+  // Resolves the selection threshold among the items whose key bits above
+  // `shift` equal `prefix` (prefix has zeros below `shift`): `rem` (>= 1) of
+  // them are taken.  `cand` exposes n, key(i) and id(i) for i < n; other
+  // items may be present and are ignored.  hist256 is 256 words of LDS.
+  // Returns K* and I*.
+  template <class Cand>
+  __device__ static void resolve(const Cand& cand, uint32_t prefix, int shift, uint32_t rem,
+                                 uint32_t* hist256, uint32_t* wb, uint32_t* kstar, int32_t* istar) {
+    const uint32_t n = cand.n;
+    uint32_t pmask = shift >= 32 ? 0u : (0xffffffffu << shift);
+    uint32_t eq_count = 0xffffffffu;
+    int lo = shift;
+    while (lo > 0) {
+      const int bits = lo >= 8 ? 8 : lo;
+      lo -= bits;
+      const uint32_t dmask = (1u << bits) - 1u;
+      for (int i = threadIdx.x; i < 256; i += NT) hist256[i] = 0;
+      __syncthreads();
+      for (uint32_t c = threadIdx.x; c < n; c += NT) {
+        const uint32_t k = cand.key(c);
+        if ((k & pmask) == prefix) atomicAdd(&hist256[(k >> lo) & dmask], 1u);
+      }
+      __syncthreads();
+      uint32_t before;
+      const int d = find_rank_bin(hist256, 1 << bits, rem, true, wb, &before);
+      eq_count = hist256[d];
+      rem -= before;
+      prefix |= static_cast<uint32_t>(d) << lo;
+      pmask |= dmask << lo;
+      __syncthreads();
+    }
+    *kstar = prefix;
+    *istar = 0x7fffffff;
+    if (eq_count == 0xffffffffu) {   // shift == 0: count the items equal to prefix
+      uint32_t c = 0;
+      for (uint32_t i = threadIdx.x; i < n; i += NT) c += cand.key(i) == prefix ? 1u : 0u;
+      eq_count = sum(c, wb);
+    }
+    if (rem < eq_count) {
+      uint32_t iprefix = 0, imask = 0;
+      for (int lo2 = 24; lo2 > 0;) {
+        lo2 -= 8;
+        for (int i = threadIdx.x; i < 256; i += NT) hist256[i] = 0;
+        __syncthreads();
+        for (uint32_t c = threadIdx.x; c < n; c += NT) {
+          const uint32_t id = static_cast<uint32_t>(cand.id(c));
+          if (cand.key(c) == prefix && (id & imask) == iprefix)
+            atomicAdd(&hist256[(id >> lo2) & 255u], 1u);
+        }
+        __syncthreads();
+        uint32_t below;
+        const int d = find_rank_bin(hist256, 256, rem, false, wb, &below);
+        rem -= below;
+        iprefix |= static_cast<uint32_t>(d) << lo2;
+        imask |= 255u << lo2;
+        __syncthreads();
+      }
+      *istar = static_cast<int32_t>(iprefix);
+    }
+  }
+};
+
+// Candidate lists held as two arrays (LDS or global memory).
+struct ArrayCand {
+  const uint32_t* keys;
+  const int32_t* ids;
+  uint32_t n;
+  __device__ uint32_t key(uint32_t i) const { return keys[i]; }
+  __device__ int32_t id(uint32_t i) const { return ids[i]; }
+};
+
+__device__ __forceinline__ bool selected(uint32_t key, int32_t id, uint32_t kstar, int32_t istar) {
+  return key > kstar || (key == kstar && id <= istar);
+}
+
+}  // namespace csa2

@@ -1,421 +1,647 @@
-// Two-level Top-K of the hierarchical sparse indexer, and the pool re-scoring
-// of Reindex layers.
+// Two-level Top-K of the hierarchical sparse indexer.
 //
 // "DeepSeek-V4.1-Flash 架构详解", §3.2: the Full layer keeps at most 2,048
-// blocks of 8 positions (a pool of at most 16,384 candidates) and its own
-// Top-512; a Reindex layer re-scores only the pool with its own indexer
-// query and takes a new Top-512.
+// blocks of 8 positions (a pool of at most 16,384 candidate positions) and
+// its own Top-512; a Reindex layer re-scores only the pool with its own
+// indexer query and takes a new Top-512.
 //
-// Selection is exact: the k-th key K* and, among items equal to K*, the
-// largest id I* still taken are found by radix selection over
-// order-preserving uint32 keys; an item is selected iff
-//   key > K*  or  (key == K* and id <= I*),
-// which is the first k items in (score descending, id ascending) order.  A
-// last pass over the items in id order compacts the selected ids with a
-// workgroup prefix sum, so the output list is ascending and independent of
-// thread timing.
+// Every selection is exact (see select_common.h) and reports ascending ids.
+// The selections of a decode step touch few query rows but many items per
+// row, so they are spread over many workgroups:
+//   block Top-K  (k_bt_hist, k_bt_filter, k_bt_final): a histogram of key
+//     bits [31:20] built by all workgroups of a row; each workgroup then
+//     writes the items above the threshold bin ("sure") and inside it
+//     (candidates) to its own segment and adds the candidates to a second
+//     histogram of bits [19:8]; one workgroup per row resolves the exact
+//     threshold, marks the selection in an LDS bitmap over block ids and
+//     compacts it in id order.
+//   pool Top-K   (k_pool_score, k_pool_final): the pool positions are
+//     re-scored on matrix cores (or stored scores are read); one workgroup
+//     per row holds every slot's key in LDS, selects, and compacts in slot
+//     order (= position order).
+//   flat Top-K   (k_flat_select, prefill rows): one workgroup per row.
+// Workgroups never wait on each other inside a kernel: kernel boundaries
+// order the phases (a device-wide fence per workgroup would write back a
+// whole L2).  The histograms are cleared by a fill kernel at the start of
+// each call, so a workspace needs no initialisation.
 #include "csa2_launch.h"
 #include "index_core.h"
+#include "select_common.h"
 
 namespace csa2 {
 namespace {
 
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kBins = 4096;
-constexpr int kCandCap = 4096;
+__global__ void k_fill_zero(uint32_t* __restrict__ p, size_t n) {
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
+
+hipError_t fill_zero(uint32_t* p, size_t n, hipStream_t stream) {
+  const size_t want = (n + 255) / 256;
+  const int blocks = static_cast<int>(want < 1024 ? want : 1024);
+  hipLaunchKernelGGL(k_fill_zero, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
 
 // ---------------------------------------------------------------------------
-// Item sources: item i of a query row -> (valid, key, id).  Ids increase with
-// i for every source (pool blocks are ascending), so a pass in item order is a
-// pass in id order.
-struct Item {
-  bool valid;
-  uint32_t key;
-  int32_t id;
+// Block Top-K: k_bt_hist -> k_bt_filter -> k_bt_final.  Workgroups never
+// wait on each other inside a kernel; the kernel boundaries order the phases.
+constexpr int kBtThreads = 1024;
+constexpr int kBtItems = 4096;          // block maxima per filter workgroup
+constexpr int kBtMaxWgs = 128;          // filter workgroups per row (kBtMaxBlocks / kBtItems)
+constexpr int kBtFinalCap = 8192;       // final-bucket candidates held in LDS
+constexpr int kBtMaxBlocks = 1 << 19;   // LDS bitmap capacity (block ids)
+
+struct BtWs {
+  uint32_t* hist;    // [rows][kHistBins] bins of key bits [31:20]
+  uint32_t* hist2;   // [rows][kHistBins] bins of key bits [19:8] inside the threshold bin
+  uint32_t* wgcnt;   // [rows][kBtMaxWgs][2]: sure and candidate counts per filter workgroup
+  int32_t* sure;     // [rows][nb_cap]: segment of workgroup w at [w * kBtItems, ...)
+  uint32_t* ckey;    // [rows][nb_cap]
+  int32_t* cid;      // [rows][nb_cap]
 };
 
-struct SrcArgs {
-  const float* keys;         // row-major [rows, stride]
-  const int32_t* pool;       // [rows, k_blocks] or null
-  const int32_t* vis_len;    // [rows]
-  int k_blocks;
-  int N_cap;
-  int stride;                // elements per row of `keys`
-};
+__device__ __forceinline__ uint32_t mid_bits(uint32_t key) { return (key >> 8) & 0xfffu; }
 
-template <int SRC>
-struct Source {
-  const float* keys;
-  const int32_t* pool;
-  int vis;
-  int nb_cap;
-  int n;
-
-  __device__ Source(const SrcArgs& a, int r) {
-    vis = min(max(a.vis_len[r], 0), a.N_cap);
-    nb_cap = (a.N_cap + 7) >> 3;
-    keys = a.keys + static_cast<size_t>(r) * a.stride;
-    pool = a.pool ? a.pool + static_cast<size_t>(r) * a.k_blocks : nullptr;
-    if (SRC == kSrcBlocks) n = (vis + 7) >> 3;
-    else if (SRC == kSrcFlat) n = vis;
-    else n = a.k_blocks * 8;
-  }
-
-  __device__ __forceinline__ Item get(int i) const {
-    Item it;
-    if (SRC == kSrcBlocks || SRC == kSrcFlat) {
-      it.valid = true;
-      it.id = i;
-      it.key = float_to_key(keys[i]);
-    } else {
-      const int blk = pool[i >> 3];
-      const int pos = blk * 8 + (i & 7);
-      it.valid = blk >= 0 && blk < nb_cap && pos < vis;
-      it.id = pos;
-      const float s = SRC == kSrcPoolStored ? (it.valid ? keys[pos] : 0.0f) : keys[i];
-      it.key = float_to_key(s);
-    }
-    return it;
-  }
-};
-
-// ---------------------------------------------------------------------------
-// Workgroup primitives (1024 threads).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = lane_id();
+__global__ __launch_bounds__(kBtThreads) void k_bt_hist(const float* __restrict__ bm,
+                                                        const int32_t* __restrict__ vis_len,
+                                                        int N_cap, int k, BtWs ws) {
+  __shared__ uint32_t h[kHistBins];
+  const int r = blockIdx.y;
+  const int nb_cap = (N_cap + 7) >> 3;
+  const int n = (min(max(vis_len[r], 0), N_cap) + 7) >> 3;
+  const int i0 = blockIdx.x * kBtItems;
+  if (n <= k || i0 >= n) return;
+  for (int i = threadIdx.x; i < kHistBins; i += kBtThreads) h[i] = 0;
+  __syncthreads();
+  const float* row = bm + static_cast<size_t>(r) * nb_cap;
+  float v[kBtItems / kBtThreads];
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
+  for (int j = 0; j < kBtItems / kBtThreads; ++j) {
+    const int i = i0 + threadIdx.x + j * kBtThreads;
+    v[j] = i < n ? row[i] : 0.0f;
   }
-  return v;
-}
-
-// Exclusive prefix sum over the workgroup in thread order; *total gets the sum.
-__device__ uint32_t wg_excl_scan(uint32_t v, uint32_t* wave_buf, uint32_t* total) {
-  const int wave = threadIdx.x >> 6, lane = lane_id();
-  const uint32_t inc = wave_incl_scan(v);
-  if (lane == 63) wave_buf[wave] = inc;
-  __syncthreads();
-  if (wave == 0) {
-    uint32_t t = lane < kSelWaves ? wave_buf[lane] : 0;
-    const uint32_t ti = wave_incl_scan(t);
-    if (lane < kSelWaves) wave_buf[kSelWaves + lane] = ti - t;
-    if (lane == kSelWaves - 1) wave_buf[2 * kSelWaves] = ti;
-  }
-  __syncthreads();
-  const uint32_t r = wave_buf[kSelWaves + wave] + inc - v;
-  *total = wave_buf[2 * kSelWaves];
-  __syncthreads();
-  return r;
-}
-
-__device__ uint32_t wg_reduce(uint32_t v, uint32_t* wave_buf, bool is_max) {
-  uint32_t t;
-  const uint32_t ex = wg_excl_scan(is_max ? 0u : v, wave_buf, &t);
-  (void)ex;
-  if (!is_max) return t;
-  // max via shuffles
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(v, d, 64)));
-  if (lane_id() == 0) wave_buf[threadIdx.x >> 6] = v;
-  __syncthreads();
-  uint32_t m = 0;
-  for (int w = 0; w < kSelWaves; ++w) m = max(m, wave_buf[w]);
-  __syncthreads();
-  return m;
-}
-
-// Given per-bin counts in hist[0..nbins), finds the bin holding the item of
-// rank `rank` (1-based) counting from the top bin down (descending) or from
-// bin 0 up (ascending).  Returns the bin; *before gets the count of items in
-// bins passed before it.  nbins <= 4 * kSelThreads.
-__device__ int find_rank_bin(const uint32_t* hist, int nbins, uint32_t rank, bool descending,
-                             uint32_t* wave_buf, uint32_t* result, uint32_t* before) {
-  const int per = (nbins + kSelThreads - 1) / kSelThreads;  // bins per thread, <= 4
-  const int t = threadIdx.x;
-  uint32_t c[4] = {0, 0, 0, 0};
-  uint32_t s = 0;
-  for (int i = 0; i < per; ++i) {
-    const int idx = t * per + i;
-    int bin = descending ? nbins - 1 - idx : idx;
-    c[i] = (idx < nbins) ? hist[bin] : 0;
-    s += c[i];
-  }
-  uint32_t tot;
-  uint32_t p = wg_excl_scan(s, wave_buf, &tot);
-  if (p < rank && rank <= p + s) {
-    for (int i = 0; i < per; ++i) {
-      if (rank <= p + c[i]) {
-        const int idx = t * per + i;
-        result[0] = static_cast<uint32_t>(descending ? nbins - 1 - idx : idx);
-        result[1] = p;
-        break;
-      }
-      p += c[i];
-    }
+  for (int j = 0; j < kBtItems / kBtThreads; ++j) {
+    const int i = i0 + threadIdx.x + j * kBtThreads;
+    if (i < n) atomicAdd(&h[float_to_key(v[j]) >> kHistShift], 1u);
   }
   __syncthreads();
-  const int bin = static_cast<int>(result[0]);
-  *before = result[1];
-  __syncthreads();
-  return bin;
+  uint32_t* gh = ws.hist + static_cast<size_t>(r) * kHistBins;
+  for (int b = threadIdx.x; b < kHistBins; b += kBtThreads)
+    if (h[b]) atomicAdd(&gh[b], h[b]);
 }
 
-// ---------------------------------------------------------------------------
-template <int SRC>
-__global__ __launch_bounds__(kSelThreads) void k_select(SrcArgs args, int k,
-                                                        int32_t* __restrict__ out_ids,
-                                                        float* __restrict__ out_keys) {
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t cand_key[kCandCap];
-  __shared__ int32_t cand_id[kCandCap];
-  __shared__ uint32_t wave_buf[2 * kSelWaves + 4];
-  __shared__ uint32_t res[4];
-  __shared__ uint32_t cand_count;
-
-  const int r = blockIdx.x;
-  const Source<SRC> src(args, r);
-  const int n = src.n;
+__global__ __launch_bounds__(kBtThreads) void k_bt_filter(const float* __restrict__ bm,
+                                                          const int32_t* __restrict__ vis_len,
+                                                          int N_cap, int k, BtWs ws) {
+  __shared__ uint32_t h2[kHistBins];
+  __shared__ uint32_t wb[Wg<kBtThreads>::kScratch];
+  __shared__ uint32_t cnt[2];
+  using W = Wg<kBtThreads>;
+  const int r = blockIdx.y;
   const int tid = threadIdx.x;
-
-  // Pass 0: valid count and key range.
-  uint32_t cnt = 0, kmin = 0xffffffffu, kmax = 0;
-  for (int i = tid; i < n; i += kSelThreads) {
-    const Item it = src.get(i);
-    if (it.valid) {
-      ++cnt;
-      kmin = min(kmin, it.key);
-      kmax = max(kmax, it.key);
+  const int nb_cap = (N_cap + 7) >> 3;
+  const int n = (min(max(vis_len[r], 0), N_cap) + 7) >> 3;
+  const int i0 = blockIdx.x * kBtItems;
+  if (n <= k || i0 >= n) return;
+  const uint32_t* gh = ws.hist + static_cast<size_t>(r) * kHistBins;
+  uint32_t above;
+  const int b1 = W::find_rank_bin(gh, kHistBins, static_cast<uint32_t>(k), true, wb, &above);
+  for (int i = tid; i < kHistBins; i += kBtThreads) h2[i] = 0;
+  if (tid < 2) cnt[tid] = 0;
+  __syncthreads();
+  const float* row = bm + static_cast<size_t>(r) * nb_cap;
+  const size_t seg = static_cast<size_t>(r) * nb_cap + i0;
+  float v[kBtItems / kBtThreads];
+#pragma unroll
+  for (int j = 0; j < kBtItems / kBtThreads; ++j) {
+    const int i = i0 + tid + j * kBtThreads;
+    v[j] = i < n ? row[i] : 0.0f;
+  }
+#pragma unroll
+  for (int j = 0; j < kBtItems / kBtThreads; ++j) {
+    const int i = i0 + tid + j * kBtThreads;
+    const uint32_t key = float_to_key(v[j]);
+    const int bin = static_cast<int>(key >> kHistShift);
+    const bool is_sure = i < n && bin > b1;
+    const bool is_cand = i < n && bin == b1;
+    const uint32_t s = wave_append(is_sure, &cnt[0]);
+    if (is_sure) ws.sure[seg + s] = i;
+    const uint32_t c = wave_append(is_cand, &cnt[1]);
+    if (is_cand) {
+      ws.ckey[seg + c] = key;
+      ws.cid[seg + c] = i;
+      atomicAdd(&h2[mid_bits(key)], 1u);
     }
   }
-  const uint32_t n_valid = wg_reduce(cnt, wave_buf, false);
-  kmax = wg_reduce(kmax, wave_buf, true);
-  kmin = ~wg_reduce(~kmin, wave_buf, true);
-  const uint32_t need = min(static_cast<uint32_t>(k), n_valid);
+  __syncthreads();
+  uint32_t* gh2 = ws.hist2 + static_cast<size_t>(r) * kHistBins;
+  for (int b = tid; b < kHistBins; b += kBtThreads)
+    if (h2[b]) atomicAdd(&gh2[b], h2[b]);
+  if (tid < 2) ws.wgcnt[(static_cast<size_t>(r) * kBtMaxWgs + blockIdx.x) * 2 + tid] = cnt[tid];
+}
 
-  // Threshold: select iff key > k_star || (key == k_star && id <= i_star).
-  uint32_t k_star = 0;
-  int32_t i_star = 0x7fffffff;
-  if (need < n_valid && need > 0) {
-    // Pass 1: histogram of (key - kmin) >> sh over at most kBins bins.
-    const uint32_t range = kmax - kmin;
-    int sh = 0;
-    while (sh < 32 && (static_cast<uint64_t>(range) >> sh) >= kBins) ++sh;
-    for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += kSelThreads) {
-      const Item it = src.get(i);
-      if (it.valid) atomicAdd(&hist[(it.key - kmin) >> sh], 1u);
+// One workgroup per row: second-level bin b2 of bits [19:8] inside b1, the
+// exact threshold inside bucket (b1, b2), an LDS bitmap of the selection and
+// its compaction in block-id order.
+__global__ __launch_bounds__(kBtThreads) void k_bt_final(const int32_t* __restrict__ vis_len,
+                                                         int N_cap, int k, BtWs ws,
+                                                         int32_t* __restrict__ out) {
+  __shared__ uint32_t fkey[kBtFinalCap];
+  __shared__ int32_t fid[kBtFinalCap];
+  __shared__ uint32_t bitmap[kBtMaxBlocks / 32];
+  __shared__ uint32_t off_s[kBtMaxWgs + 1], off_c[kBtMaxWgs + 1];
+  __shared__ uint32_t hist256[256];
+  __shared__ uint32_t wb[Wg<kBtThreads>::kScratch];
+  __shared__ uint32_t fcount;
+  using W = Wg<kBtThreads>;
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nb_cap = (N_cap + 7) >> 3;
+  const int n = (min(max(vis_len[r], 0), N_cap) + 7) >> 3;
+  int32_t* orow = out + static_cast<size_t>(r) * k;
+  if (n <= k) {  // every visible block is kept
+    for (int i = tid; i < k; i += kBtThreads) orow[i] = i < n ? i : -1;
+    return;
+  }
+  const uint32_t need = static_cast<uint32_t>(k);
+  const uint32_t* gh = ws.hist + static_cast<size_t>(r) * kHistBins;
+  const uint32_t* gh2 = ws.hist2 + static_cast<size_t>(r) * kHistBins;
+  uint32_t above;
+  const int b1 = W::find_rank_bin(gh, kHistBins, need, true, wb, &above);
+  const uint32_t rem1 = need - above;
+  uint32_t above2;
+  const int b2 = W::find_rank_bin(gh2, kHistBins, rem1, true, wb, &above2);
+  const uint32_t rem2 = rem1 - above2;
+  const uint32_t n2 = gh2[b2];
+
+  // Prefix offsets of the filter workgroups' segments.
+  const int nwg = (n + kBtItems - 1) / kBtItems;
+  if (tid < 64) {
+    const uint32_t* wc = ws.wgcnt + static_cast<size_t>(r) * kBtMaxWgs * 2;
+    uint32_t ps = 0, pc = 0;
+    for (int base = 0; base < nwg; base += 64) {
+      const int w = base + tid;
+      const uint32_t cs = w < nwg ? wc[2 * w] : 0u, cc = w < nwg ? wc[2 * w + 1] : 0u;
+      const uint32_t is = wave_incl_scan_u32(cs), ic = wave_incl_scan_u32(cc);
+      if (w < nwg) {
+        off_s[w + 1] = ps + is;
+        off_c[w + 1] = pc + ic;
+      }
+      ps += __shfl(is, 63, 64);
+      pc += __shfl(ic, 63, 64);
     }
-    __syncthreads();
-    const int nbins = static_cast<int>((static_cast<uint64_t>(range) >> sh) + 1);
+    if (tid == 0) {
+      off_s[0] = 0;
+      off_c[0] = 0;
+      fcount = 0;
+    }
+  }
+  const int nwords = (n + 31) >> 5;
+  for (int w = tid; w < nwords; w += kBtThreads) bitmap[w] = 0u;
+  __syncthreads();
+  const uint32_t n_sure = off_s[nwg], n_cand = off_c[nwg];
+  // Flattened item g -> (segment w, slot g - off[w]) by binary search.
+  auto locate = [&](const uint32_t* off, uint32_t g) {
+    int lo = 0, hi = nwg;   // off[lo] <= g < off[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (off[mid] <= g) lo = mid; else hi = mid;
+    }
+    return static_cast<size_t>(r) * nb_cap + static_cast<size_t>(lo) * kBtItems + (g - off[lo]);
+  };
+  for (uint32_t g = tid; g < n_sure; g += kBtThreads) {
+    const int id = ws.sure[locate(off_s, g)];
+    atomicOr(&bitmap[id >> 5], 1u << (id & 31));
+  }
+  for (uint32_t base = 0; base < n_cand; base += kBtThreads) {
+    const uint32_t g = base + tid;
+    const bool in = g < n_cand;
+    const size_t at = in ? locate(off_c, g) : 0;
+    const uint32_t key = in ? ws.ckey[at] : 0u;
+    const int id = in ? ws.cid[at] : 0;
+    const int mb = static_cast<int>(mid_bits(key));
+    if (in && mb > b2) atomicOr(&bitmap[id >> 5], 1u << (id & 31));
+    const bool fin = in && mb == b2;
+    const uint32_t slot = wave_append(fin, &fcount);
+    if (fin && slot < static_cast<uint32_t>(kBtFinalCap)) {
+      fkey[slot] = key;
+      fid[slot] = id;
+    }
+  }
+  __syncthreads();
+  const uint32_t prefix = (static_cast<uint32_t>(b1) << kHistShift) | (static_cast<uint32_t>(b2) << 8);
+  uint32_t kstar;
+  int32_t istar;
+  if (n2 <= static_cast<uint32_t>(kBtFinalCap)) {
+    W::resolve(ArrayCand{fkey, fid, n2}, prefix, 8, rem2, hist256, wb, &kstar, &istar);
+    for (uint32_t c = tid; c < n2; c += kBtThreads)
+      if (selected(fkey[c], fid[c], kstar, istar)) atomicOr(&bitmap[fid[c] >> 5], 1u << (fid[c] & 31));
+  } else {
+    // Degenerate input (a huge bucket of equal high bits): resolve by
+    // re-reading the candidate segments.
+    struct SegCand {
+      const uint32_t* ckey;
+      const int32_t* cid;
+      const uint32_t* off;
+      int nwg;
+      size_t base;
+      uint32_t n;
+      __device__ size_t at(uint32_t g) const {
+        int lo = 0, hi = nwg;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (off[mid] <= g) lo = mid; else hi = mid;
+        }
+        return base + static_cast<size_t>(lo) * kBtItems + (g - off[lo]);
+      }
+      __device__ uint32_t key(uint32_t g) const { return ckey[at(g)]; }
+      __device__ int32_t id(uint32_t g) const { return cid[at(g)]; }
+    } sc{ws.ckey, ws.cid, off_c, nwg, static_cast<size_t>(r) * nb_cap, n_cand};
+    W::resolve(sc, prefix, 8, rem2, hist256, wb, &kstar, &istar);
+    for (uint32_t g = tid; g < n_cand; g += kBtThreads) {
+      const uint32_t key = sc.key(g);
+      const int id = sc.id(g);
+      if ((key & 0xffffff00u) == prefix && selected(key, id, kstar, istar))
+        atomicOr(&bitmap[id >> 5], 1u << (id & 31));
+    }
+  }
+  __syncthreads();
+  const int wpt = (nwords + kBtThreads - 1) / kBtThreads;
+  const int w0 = tid * wpt;
+  uint32_t c = 0;
+  for (int w = w0; w < min(w0 + wpt, nwords); ++w) c += __popc(bitmap[w]);
+  uint32_t total;
+  uint32_t off = W::excl_scan(c, wb, &total);
+  for (int w = w0; w < min(w0 + wpt, nwords); ++w) {
+    uint32_t bits = bitmap[w];
+    while (bits) {
+      const int b = __ffs(static_cast<int>(bits)) - 1;
+      bits &= bits - 1u;
+      if (off < need) orow[off] = w * 32 + b;
+      ++off;
+    }
+  }
+  for (int i = static_cast<int>(min(total, need)) + tid; i < k; i += kBtThreads) orow[i] = -1;
+}
+
+// ---------------------------------------------------------------------------
+// Pool Top-K: k_pool_score re-scores the pool positions (Reindex, or Full
+// without stored scores) into a pool-score array; k_pool_final (one
+// workgroup per row) loads every slot's key into LDS and selects there.
+constexpr int kPsThreads = 1024;
+constexpr int kPsWaves = kPsThreads / 64;
+constexpr int kPsSlots = 1024;                 // slots per scoring workgroup
+constexpr int kPsBlocks = kPsSlots / kBlock;
+constexpr int kPsMaxSlots = kMaxPoolBlocks * kBlock;
+
+struct PoolArgs {
+  const float* scores;       // stored scores [rows, N_cap], or null when re-scored
+  const uint16_t* q_idx;
+  const float* w_idx;
+  const uint8_t* k_idx;
+  const int32_t* pool;       // [rows, kb]
+  const int32_t* vis_len;
+  int kb, n_q, N_cap, top_k;
+  float* ps;                 // [rows][kb * 8] re-scored pool scores
+  int32_t* out;              // [rows, top_k]
+  float* out_key;            // [rows, top_k] or null
+};
+
+__device__ __forceinline__ bool pool_slot_valid(const int32_t* prow, int i, int nb_cap, int vis) {
+  const int blk = prow[i >> 3];
+  return blk >= 0 && blk < nb_cap && blk * kBlock + (i & 7) < vis;
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(kPsThreads) void k_pool_score(PoolArgs a) {
+  const int r = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int vis = min(max(a.vis_len[r], 0), a.N_cap);
+  const int nb_cap = (a.N_cap + 7) >> 3;
+  const int nslots = a.kb * kBlock;
+  const int32_t* prow = a.pool + static_cast<size_t>(r) * a.kb;
+  float* ps = a.ps + static_cast<size_t>(r) * nslots;
+  bf16x8 qa[8];
+  float wr[16];
+  load_query(qa, a.q_idx + static_cast<size_t>(r) * kIdxHeads * kIdxDim, col, half);
+  load_weights(wr, a.w_idx + static_cast<size_t>(r) * kIdxHeads, half);
+  const int b = r / a.n_q;
+  const uint8_t* kbase = a.k_idx + static_cast<size_t>(b) * a.N_cap * (FP8 ? 128 : 256);
+  // 32 tiles of 32 slots (4 pool blocks each); wave w takes tiles w and w + 16.
+  const int slot0 = blockIdx.x * kPsSlots;
+  KeyTile<FP8> kt[2];
+  bool valid[2];
+  int slot[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    slot[u] = slot0 + 32 * (wave + kPsWaves * u) + col;
+    valid[u] = slot[u] < nslots && pool_slot_valid(prow, slot[u], nb_cap, vis);
+    const int pos = valid[u] ? prow[slot[u] >> 3] * kBlock + (col & 7) : 0;
+    load_key_half<FP8>(kt[u], kbase + static_cast<size_t>(pos) * (FP8 ? 128 : 256), half);
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const float s = head_sum(key_tile_dot<FP8>(qa, kt[u]), wr);
+    if (half == 0 && slot[u] < nslots) ps[slot[u]] = s;
+  }
+}
+
+struct LdsKeys {   // all slots of a row in LDS; empty slots hold key 0
+  const uint32_t* k;
+  uint32_t n;
+  __device__ uint32_t key(uint32_t i) const { return k[i]; }
+  __device__ int32_t id(uint32_t i) const { return static_cast<int32_t>(i); }
+};
+
+__global__ __launch_bounds__(kPsThreads) void k_pool_final(PoolArgs a) {
+  __shared__ uint32_t keys[kPsMaxSlots];
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t hist256[256];
+  __shared__ uint32_t wb[Wg<kPsThreads>::kScratch];
+  using W = Wg<kPsThreads>;
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int vis = min(max(a.vis_len[r], 0), a.N_cap);
+  const int nb_cap = (a.N_cap + 7) >> 3;
+  const int nslots = a.kb * kBlock;
+  const int32_t* prow = a.pool + static_cast<size_t>(r) * a.kb;
+  const float* ps = a.ps + static_cast<size_t>(r) * nslots;
+  const float* srow = a.scores ? a.scores + static_cast<size_t>(r) * a.N_cap : nullptr;
+  // Empty slots get key 0, which no finite score has.
+  for (int i = tid; i < kHistBins; i += kPsThreads) h[i] = 0;
+  __syncthreads();
+  uint32_t nv = 0;
+  for (int i = tid; i < nslots; i += kPsThreads) {
+    const bool valid = pool_slot_valid(prow, i, nb_cap, vis);
+    const float s = !valid ? 0.0f : (srow ? srow[prow[i >> 3] * kBlock + (i & 7)] : ps[i]);
+    const uint32_t key = valid ? float_to_key(s) : 0u;
+    keys[i] = key;
+    if (valid) {
+      atomicAdd(&h[key >> kHistShift], 1u);
+      ++nv;
+    }
+  }
+  const uint32_t n_valid = W::sum(nv, wb);   // includes a barrier
+  const uint32_t need = min(static_cast<uint32_t>(a.top_k), n_valid);
+  uint32_t kstar = 1u;              // need == n_valid: every valid (nonzero) key
+  int32_t istar = 0x7fffffff;
+  if (need > 0 && need < n_valid) {
     uint32_t above;
-    const int bstar = find_rank_bin(hist, nbins, need, true, wave_buf, res, &above);
-    uint32_t rem = need - above;                     // items to take at or below the bin
-    const uint32_t in_bin = hist[bstar];
-    // Candidates: items whose offset from kmin has the prefix bstar << sh.
-    uint32_t prefix = static_cast<uint32_t>(bstar) << sh;   // offset prefix
-    uint32_t pmask = sh >= 32 ? 0u : (0xffffffffu << sh);
-    const bool in_lds = in_bin <= static_cast<uint32_t>(kCandCap);
-    if (in_lds) {
-      if (tid == 0) cand_count = 0;
-      __syncthreads();
-      for (int i = tid; i < n; i += kSelThreads) {
-        const Item it = src.get(i);
-        if (it.valid && ((it.key - kmin) & pmask) == prefix) {
-          const uint32_t slot = atomicAdd(&cand_count, 1u);
-          cand_key[slot] = it.key - kmin;
-          cand_id[slot] = it.id;
-        }
+    const int b1 = W::find_rank_bin(h, kHistBins, need, true, wb, &above);
+    W::resolve(LdsKeys{keys, static_cast<uint32_t>(nslots)}, static_cast<uint32_t>(b1) << kHistShift,
+               kHistShift, need - above, hist256, wb, &kstar, &istar);
+  }
+  const int spt = (nslots + kPsThreads - 1) / kPsThreads;
+  const int s0 = tid * spt;
+  uint32_t cnt = 0;
+  for (int i = s0; i < min(s0 + spt, nslots); ++i)
+    cnt += (need > 0 && keys[i] != 0u && selected(keys[i], i, kstar, istar)) ? 1u : 0u;
+  uint32_t total;
+  uint32_t off = W::excl_scan(cnt, wb, &total);
+  int32_t* orow = a.out + static_cast<size_t>(r) * a.top_k;
+  float* krow = a.out_key ? a.out_key + static_cast<size_t>(r) * a.top_k : nullptr;
+  for (int i = s0; i < min(s0 + spt, nslots); ++i) {
+    const uint32_t key = keys[i];
+    if (need > 0 && key != 0u && selected(key, i, kstar, istar)) {
+      if (off < need) {
+        orow[off] = prow[i >> 3] * kBlock + (i & 7);
+        if (krow) krow[off] = key_to_float(key);
       }
-      __syncthreads();
-    }
-    // Radix passes over the low sh bits of the offset, 8 bits at a time.
-    uint32_t eq_count = in_bin;
-    int lo = sh;
-    while (lo > 0) {
-      const int bits = lo >= 8 ? 8 : lo;
-      lo -= bits;
-      const uint32_t dmask = (1u << bits) - 1u;
-      for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
-      __syncthreads();
-      if (in_lds) {
-        for (uint32_t c = tid; c < in_bin; c += kSelThreads) {
-          const uint32_t off = cand_key[c];
-          if ((off & pmask) == prefix) atomicAdd(&hist[(off >> lo) & dmask], 1u);
-        }
-      } else {
-        for (int i = tid; i < n; i += kSelThreads) {
-          const Item it = src.get(i);
-          const uint32_t off = it.key - kmin;
-          if (it.valid && (off & pmask) == prefix) atomicAdd(&hist[(off >> lo) & dmask], 1u);
-        }
-      }
-      __syncthreads();
-      uint32_t before;
-      const int d = find_rank_bin(hist, 1 << bits, rem, true, wave_buf, res, &before);
-      eq_count = hist[d];
-      rem -= before;
-      prefix |= static_cast<uint32_t>(d) << lo;
-      pmask |= dmask << lo;
-      __syncthreads();
-    }
-    k_star = prefix + kmin;
-    // Among items equal to k_star take the `rem` lowest ids.
-    if (rem < eq_count) {
-      uint32_t iprefix = 0, imask = 0;
-      for (int lo2 = 24; lo2 > 0;) {
-        lo2 -= 8;
-        for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
-        __syncthreads();
-        if (in_lds) {
-          for (uint32_t c = tid; c < in_bin; c += kSelThreads) {
-            const uint32_t id = static_cast<uint32_t>(cand_id[c]);
-            if (cand_key[c] + kmin == k_star && (id & imask) == iprefix)
-              atomicAdd(&hist[(id >> lo2) & 255u], 1u);
-          }
-        } else {
-          for (int i = tid; i < n; i += kSelThreads) {
-            const Item it = src.get(i);
-            const uint32_t id = static_cast<uint32_t>(it.id);
-            if (it.valid && it.key == k_star && (id & imask) == iprefix)
-              atomicAdd(&hist[(id >> lo2) & 255u], 1u);
-          }
-        }
-        __syncthreads();
-        uint32_t below;
-        const int d = find_rank_bin(hist, 256, rem, false, wave_buf, res, &below);
-        rem -= below;
-        iprefix |= static_cast<uint32_t>(d) << lo2;
-        imask |= 255u << lo2;
-        __syncthreads();
-      }
-      i_star = static_cast<int32_t>(iprefix);
+      ++off;
     }
   }
-
-  // Final pass: ordered compaction of the selected items.
-  int32_t* orow = out_ids + static_cast<size_t>(r) * k;
-  float* krow = out_keys ? out_keys + static_cast<size_t>(r) * k : nullptr;
-  constexpr int kPer = 4;
-  uint32_t written = 0;
-  for (int base = 0; base < n; base += kSelThreads * kPer) {
-    Item it[kPer];
-    bool sel[kPer];
-    uint32_t c = 0;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int i = base + tid * kPer + e;
-      it[e] = (i < n) ? src.get(i) : Item{false, 0u, 0};
-      sel[e] = it[e].valid && need > 0 &&
-               (it[e].key > k_star || (it[e].key == k_star && it[e].id <= i_star));
-      c += sel[e] ? 1u : 0u;
-    }
-    uint32_t round_total;
-    uint32_t off = written + wg_excl_scan(c, wave_buf, &round_total);
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      if (sel[e] && off < static_cast<uint32_t>(k)) {
-        orow[off] = it[e].id;
-        if (krow) krow[off] = key_to_float(it[e].key);
-        ++off;
-      }
-    }
-    written += round_total;
-  }
-  for (int i = static_cast<int>(min(written, static_cast<uint32_t>(k))) + tid; i < k; i += kSelThreads) {
+  for (int i = static_cast<int>(min(total, need)) + tid; i < a.top_k; i += kPsThreads) {
     orow[i] = -1;
     if (krow) krow[i] = -__builtin_inff();
   }
 }
 
 // ---------------------------------------------------------------------------
-// Pool re-scoring: each workgroup scores 32 pool blocks (8 tiles of 32
-// positions, 4 blocks per tile); lane col takes position 8*block + col%8 of
-// block 4*tile + col/8.  Rows of one block are 8 consecutive key rows.
-constexpr int kRescoreBlocksPerWg = 32;
+// Flat Top-K of prefill rows: one workgroup per row over [0, vis).
+constexpr int kFsThreads = 1024;
+constexpr int kFsCandCap = 8192;
+constexpr int kFsPer = 8;
 
-template <bool FP8>
-__global__ __launch_bounds__(256) void k_pool_rescore(
-    const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
-    const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ pool_blocks, int k_blocks,
-    const int32_t* __restrict__ vis_len, int n_q, int N_cap, float* __restrict__ pool_scores) {
-  const int r = blockIdx.y;
-  const int b = r / n_q;
-  const int vis = min(max(vis_len[r], 0), N_cap);
-  const int nb_cap = (N_cap + 7) >> 3;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int half = lane >> 5, col = lane & 31;
-  bf16x8 qa[8];
-  float wr[16];
-  load_query(qa, q_idx + static_cast<size_t>(r) * kIdxHeads * kIdxDim, col, half);
-  load_weights(wr, w_idx + static_cast<size_t>(r) * kIdxHeads, half);
-  const int32_t* prow = pool_blocks + static_cast<size_t>(r) * k_blocks;
-  const uint8_t* kb = k_idx + static_cast<size_t>(b) * N_cap * (FP8 ? 128 : 256);
-  float* orow = pool_scores + static_cast<size_t>(r) * k_blocks * 8;
-  const int tiles = (k_blocks + 3) / 4;
-  const int t0 = blockIdx.x * (kRescoreBlocksPerWg / 4);
-  const int t1 = min(t0 + kRescoreBlocksPerWg / 4, tiles);
-  for (int t = t0 + wave; t < t1; t += 4) {
-    const int slot = 4 * t + (col >> 3);
-    const int blk = slot < k_blocks ? prow[slot] : -1;
-    const int pos = blk * 8 + (col & 7);
-    const bool valid = blk >= 0 && blk < nb_cap && pos < vis;
-    KeyTile<FP8> kt;
-    load_key_half<FP8>(kt, kb + static_cast<size_t>(valid ? pos : 0) * (FP8 ? 128 : 256), half);
-    const float s = head_sum(key_tile_dot<FP8>(qa, kt), wr);
-    if (half == 0 && slot < k_blocks) orow[slot * 8 + (col & 7)] = valid ? s : -__builtin_inff();
+struct FlatCand {
+  const float* s;
+  uint32_t n;
+  __device__ uint32_t key(uint32_t i) const { return float_to_key(s[i]); }
+  __device__ int32_t id(uint32_t i) const { return static_cast<int32_t>(i); }
+};
+
+// Gathers the items of the row whose key has `prefix` above `shift` into LDS.
+__device__ void flat_gather(const float* row, int n, uint32_t prefix, int shift, uint32_t* ckey,
+                            int32_t* cid, uint32_t* counter) {
+  const uint32_t pmask = 0xffffffffu << shift;
+  for (int base = 0; base < n; base += kFsThreads * kFsPer) {
+    float v[kFsPer];
+#pragma unroll
+    for (int e = 0; e < kFsPer; ++e) {
+      const int i = base + e * kFsThreads + threadIdx.x;
+      v[e] = i < n ? row[i] : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < kFsPer; ++e) {
+      const int i = base + e * kFsThreads + threadIdx.x;
+      const uint32_t key = float_to_key(v[e]);
+      const bool c = i < n && (key & pmask) == prefix;
+      const uint32_t s = wave_append(c, counter);
+      if (c && s < static_cast<uint32_t>(kFsCandCap)) {
+        ckey[s] = key;
+        cid[s] = i;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kFsThreads) void k_flat_select(const float* __restrict__ scores,
+                                                            const int32_t* __restrict__ vis_len,
+                                                            int N_cap, int k,
+                                                            int32_t* __restrict__ out,
+                                                            float* __restrict__ out_key) {
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t ckey_l[kFsCandCap];
+  __shared__ int32_t cid_l[kFsCandCap];
+  __shared__ uint32_t hist256[256];
+  __shared__ uint32_t wb[Wg<kFsThreads>::kScratch];
+  __shared__ uint32_t ccount;
+  using W = Wg<kFsThreads>;
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = min(max(vis_len[r], 0), N_cap);
+  const float* row = scores + static_cast<size_t>(r) * N_cap;
+  const uint32_t need = min(static_cast<uint32_t>(k), static_cast<uint32_t>(n));
+  uint32_t kstar = 0;
+  int32_t istar = 0x7fffffff;
+  if (need > 0 && need < static_cast<uint32_t>(n)) {
+    // Level 1: bins of key bits [31:20].
+    for (int i = tid; i < kHistBins; i += kFsThreads) h[i] = 0;
+    __syncthreads();
+    for (int base = 0; base < n; base += kFsThreads * kFsPer) {
+      float v[kFsPer];
+#pragma unroll
+      for (int e = 0; e < kFsPer; ++e) {
+        const int i = base + e * kFsThreads + tid;
+        v[e] = i < n ? row[i] : 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < kFsPer; ++e)
+        if (base + e * kFsThreads + tid < n) atomicAdd(&h[float_to_key(v[e]) >> kHistShift], 1u);
+    }
+    __syncthreads();
+    uint32_t above;
+    const int b1 = W::find_rank_bin(h, kHistBins, need, true, wb, &above);
+    uint32_t rem = need - above;
+    uint32_t prefix = static_cast<uint32_t>(b1) << kHistShift;
+    int shift = kHistShift;
+    uint32_t ncand = h[b1];
+    if (ncand > static_cast<uint32_t>(kFsCandCap)) {
+      // Level 2: bins of key bits [19:8] inside b1.
+      __syncthreads();
+      for (int i = tid; i < kHistBins; i += kFsThreads) h[i] = 0;
+      __syncthreads();
+      for (int base = 0; base < n; base += kFsThreads * kFsPer) {
+        float v[kFsPer];
+#pragma unroll
+        for (int e = 0; e < kFsPer; ++e) {
+          const int i = base + e * kFsThreads + tid;
+          v[e] = i < n ? row[i] : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < kFsPer; ++e) {
+          const uint32_t key = float_to_key(v[e]);
+          if (base + e * kFsThreads + tid < n && (key >> kHistShift) == static_cast<uint32_t>(b1))
+            atomicAdd(&h[mid_bits(key)], 1u);
+        }
+      }
+      __syncthreads();
+      uint32_t above2;
+      const int b2 = W::find_rank_bin(h, kHistBins, rem, true, wb, &above2);
+      rem -= above2;
+      prefix |= static_cast<uint32_t>(b2) << 8;
+      shift = 8;
+      ncand = h[b2];
+    }
+    if (tid == 0) ccount = 0;
+    __syncthreads();
+    if (ncand <= static_cast<uint32_t>(kFsCandCap)) {
+      flat_gather(row, n, prefix, shift, ckey_l, cid_l, &ccount);
+      __syncthreads();
+      W::resolve(ArrayCand{ckey_l, cid_l, ncand}, prefix, shift, rem, hist256, wb, &kstar, &istar);
+    } else {
+      W::resolve(FlatCand{row, static_cast<uint32_t>(n)}, prefix, shift, rem, hist256, wb, &kstar,
+                 &istar);
+    }
+  }
+  // Ordered compaction: rounds of kFsThreads * kFsPer items, thread-contiguous.
+  int32_t* orow = out + static_cast<size_t>(r) * k;
+  float* krow = out_key ? out_key + static_cast<size_t>(r) * k : nullptr;
+  uint32_t written = 0;
+  for (int base = 0; base < n && need > 0; base += kFsThreads * kFsPer) {
+    float v[kFsPer];
+    uint32_t c = 0;
+#pragma unroll
+    for (int e = 0; e < kFsPer; ++e) {
+      const int i = base + tid * kFsPer + e;
+      v[e] = i < n ? row[i] : -__builtin_inff();
+      c += (i < n && selected(float_to_key(v[e]), i, kstar, istar)) ? 1u : 0u;
+    }
+    uint32_t round_total;
+    uint32_t off = written + W::excl_scan(c, wb, &round_total);
+#pragma unroll
+    for (int e = 0; e < kFsPer; ++e) {
+      const int i = base + tid * kFsPer + e;
+      if (i < n && selected(float_to_key(v[e]), i, kstar, istar)) {
+        if (off < need) {
+          orow[off] = i;
+          if (krow) krow[off] = v[e];
+        }
+        ++off;
+      }
+    }
+    written += round_total;
+  }
+  for (int i = static_cast<int>(min(written, need)) + tid; i < k; i += kFsThreads) {
+    orow[i] = -1;
+    if (krow) krow[i] = -__builtin_inff();
   }
 }
 
 }  // namespace
 
-hipError_t launch_pool_rescore(const uint16_t* q_idx, const float* w_idx, const void* k_idx,
-                               bool fp8, const int32_t* pool_blocks, int k_blocks,
-                               const int32_t* vis_len, int B, int n_q, int N_cap,
-                               float* pool_scores, hipStream_t stream) {
-  dim3 grid((k_blocks + kRescoreBlocksPerWg - 1) / kRescoreBlocksPerWg, B * n_q);
-  const uint8_t* kb = static_cast<const uint8_t*>(k_idx);
-  if (fp8)
-    hipLaunchKernelGGL(k_pool_rescore<true>, grid, dim3(256), 0, stream, q_idx, w_idx, kb,
-                       pool_blocks, k_blocks, vis_len, n_q, N_cap, pool_scores);
-  else
-    hipLaunchKernelGGL(k_pool_rescore<false>, grid, dim3(256), 0, stream, q_idx, w_idx, kb,
-                       pool_blocks, k_blocks, vis_len, n_q, N_cap, pool_scores);
+size_t block_topk_workspace_bytes(int rows, int N_cap) {
+  const size_t nb_cap = (static_cast<size_t>(N_cap) + 7) / 8;
+  return static_cast<size_t>(rows) * (2 * kHistBins + 2 * kBtMaxWgs + 3 * nb_cap) * 4;
+}
+
+size_t pool_topk_workspace_bytes(int rows, int k_blocks) {
+  return static_cast<size_t>(rows) * static_cast<size_t>(k_blocks) * kBlock * 4;
+}
+
+int block_topk_max_blocks() { return kBtMaxBlocks; }
+
+hipError_t launch_block_topk(const float* block_max, const int32_t* vis_len, int rows, int N_cap,
+                             int k, int32_t* out, void* ws, hipStream_t stream) {
+  const size_t nb_cap = (static_cast<size_t>(N_cap) + 7) / 8;
+  BtWs w;
+  w.hist = static_cast<uint32_t*>(ws);
+  w.hist2 = w.hist + static_cast<size_t>(rows) * kHistBins;
+  w.wgcnt = w.hist2 + static_cast<size_t>(rows) * kHistBins;
+  w.sure = reinterpret_cast<int32_t*>(w.wgcnt + static_cast<size_t>(rows) * kBtMaxWgs * 2);
+  w.ckey = reinterpret_cast<uint32_t*>(w.sure + static_cast<size_t>(rows) * nb_cap);
+  w.cid = reinterpret_cast<int32_t*>(w.ckey + static_cast<size_t>(rows) * nb_cap);
+  hipError_t e = fill_zero(w.hist, static_cast<size_t>(rows) * 2 * kHistBins, stream);
+  if (e != hipSuccess) return e;
+  dim3 grid(static_cast<unsigned>((nb_cap + kBtItems - 1) / kBtItems), rows);
+  hipLaunchKernelGGL(k_bt_hist, grid, dim3(kBtThreads), 0, stream, block_max, vis_len, N_cap, k, w);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_bt_filter, grid, dim3(kBtThreads), 0, stream, block_max, vis_len, N_cap, k,
+                     w);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_bt_final, dim3(rows), dim3(kBtThreads), 0, stream, vis_len, N_cap, k, w, out);
   return hipGetLastError();
 }
 
-hipError_t launch_select(SelectSource src, const float* keys, const int32_t* pool_blocks,
-                         int k_blocks, const int32_t* vis_len, int rows, int N_cap, int k,
-                         int32_t* out_ids, float* out_keys, hipStream_t stream) {
-  SrcArgs a;
-  a.keys = keys;
+hipError_t launch_pool_topk(int mode, const float* scores, const uint16_t* q_idx,
+                            const float* w_idx, const void* k_idx, const int32_t* pool_blocks,
+                            int k_blocks, const int32_t* vis_len, int rows, int n_q, int N_cap,
+                            int top_k, int32_t* out, float* out_key, void* ws,
+                            hipStream_t stream) {
+  PoolArgs a;
+  a.scores = mode == 0 ? scores : nullptr;
+  a.q_idx = q_idx;
+  a.w_idx = w_idx;
+  a.k_idx = static_cast<const uint8_t*>(k_idx);
   a.pool = pool_blocks;
   a.vis_len = vis_len;
-  a.k_blocks = k_blocks;
+  a.kb = k_blocks;
+  a.n_q = n_q;
   a.N_cap = N_cap;
-  switch (src) {
-    case kSrcBlocks: a.stride = (N_cap + 7) / 8; break;
-    case kSrcPoolScored: a.stride = k_blocks * 8; break;
-    default: a.stride = N_cap; break;
+  a.top_k = top_k;
+  a.ps = static_cast<float*>(ws);
+  a.out = out;
+  a.out_key = out_key;
+  hipError_t e;
+  if (mode != 0) {
+    dim3 grid((k_blocks + kPsBlocks - 1) / kPsBlocks, rows);
+    if (mode == 1)
+      hipLaunchKernelGGL(k_pool_score<true>, grid, dim3(kPsThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(k_pool_score<false>, grid, dim3(kPsThreads), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  dim3 grid(rows), block(kSelThreads);
-  switch (src) {
-    case kSrcBlocks:
-      hipLaunchKernelGGL(k_select<kSrcBlocks>, grid, block, 0, stream, a, k, out_ids, out_keys);
-      break;
-    case kSrcPoolStored:
-      hipLaunchKernelGGL(k_select<kSrcPoolStored>, grid, block, 0, stream, a, k, out_ids, out_keys);
-      break;
-    case kSrcPoolScored:
-      hipLaunchKernelGGL(k_select<kSrcPoolScored>, grid, block, 0, stream, a, k, out_ids, out_keys);
-      break;
-    default:
-      hipLaunchKernelGGL(k_select<kSrcFlat>, grid, block, 0, stream, a, k, out_ids, out_keys);
-      break;
-  }
+  hipLaunchKernelGGL(k_pool_final, dim3(rows), dim3(kPsThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_flat_topk(const float* scores, const int32_t* vis_len, int rows, int N_cap,
+                            int k, int32_t* out, float* out_key, hipStream_t stream) {
+  hipLaunchKernelGGL(k_flat_select, dim3(rows), dim3(kFsThreads), 0, stream, scores, vis_len,
+                     N_cap, k, out, out_key);
   return hipGetLastError();
 }
 

@@ -40,7 +40,9 @@
  *   - Scratch memory comes only from the caller's workspace `ws` of
  *     `ws_bytes` bytes, sized with csa2_workspace_size().  Calls that may run
  *     at the same time must not share a workspace.  The workspace needs no
- *     initialisation.
+ *     initialisation: every call clears what it counts in before use.
+ *   - Sizes: N_cap <= 4,194,304 entries (4x the pages' maximum context of
+ *     1,048,576 tokens), B * n_q <= 65,535 for the decode-shaped calls.
  *   - The library keeps no state; it is thread-safe.
  *   - Query rows: B sequences x n_q query tokens per sequence.  Decode uses
  *     n_q = 1; an encoder prefill chunk uses n_q > 1 with per-query visible
@@ -149,6 +151,7 @@ CSA2_API csa2_status csa2_index_score(const uint16_t* q_idx, const float* w_idx,
  *   vis_len     [B, n_q] int32
  *   k_blocks    1..2048
  *   pool_blocks [B, n_q, k_blocks] int32 output: ascending block ids, -1 padded
+ *   ws          csa2_workspace_size(CSA2_OP_BLOCK_TOPK, ...) bytes (required)
  */
 CSA2_API csa2_status csa2_block_topk(const float* block_max, const int32_t* vis_len, int32_t B,
                             int32_t n_q, int32_t N_cap, int32_t k_blocks, int32_t* pool_blocks,
@@ -183,7 +186,8 @@ CSA2_API csa2_status csa2_block_topk(const float* block_max, const int32_t* vis_
  *   idx_out     [B, n_q, top_k] int32 output: ascending positions, -1 padded
  *   idx_score   [B, n_q, top_k] fp32 output of the selected keys (-inf for
  *               padding) or NULL
- *   ws          csa2_workspace_size(CSA2_OP_REINDEX_TOPK, ...) bytes
+ *   ws          csa2_workspace_size(CSA2_OP_REINDEX_TOPK, ...) bytes, required
+ *               with a pool (unused without one)
  */
 CSA2_API csa2_status csa2_reindex_topk(csa2_mode mode, const float* scores, const uint16_t* q_idx,
                               const float* w_idx, const void* k_idx, csa2_kdtype k_dtype,

@@ -36,7 +36,7 @@ def test_version_and_status_strings(L):
 def test_workspace_sizes(L):
     import compressed_sparse_attention_index_amd as csa
     assert csa.workspace_size(csa.OP_INDEX_SCORE, 8, 1, 1 << 20) == 0
-    assert csa.workspace_size(csa.OP_BLOCK_TOPK, 8, 1, 1 << 20) == 0
+    assert csa.workspace_size(csa.OP_BLOCK_TOPK, 8, 1, 1 << 20) == 8 * (2 * 4096 + 2 * 128 + 3 * 131072) * 4
     assert csa.workspace_size(csa.OP_REINDEX_TOPK, 8, 1, 1 << 20, 512, 2048) == 8 * 2048 * 8 * 4
     assert csa.workspace_size(csa.OP_SPARSE_ATTN, 4096, 1, 1 << 16, 512, 0) == 0
     assert csa.workspace_size(csa.OP_SPARSE_ATTN, 8, 1, 1 << 20, 512, 0) > 0
@@ -58,7 +58,7 @@ def test_index_score_validation(L):
     assert _score(L, kd=5) == 3
     assert _score(L, B=0) == 2
     assert _score(L, N=0) == 2
-    assert _score(L, N=(1 << 24) + 1) == 2
+    assert _score(L, N=(1 << 22) + 1) == 2
     assert _score(L, B=70000) == 2
     assert _score(L, k=MIS) == 5
 
@@ -70,6 +70,9 @@ def test_block_topk_validation(L):
     assert f(A, A, 1, 1, 64, 2049, A, None, 0, None) == 2
     assert f(A, A, 1, 1, 0, 16, A, None, 0, None) == 2
     assert f(A, A, 1, 1, 64, 16, MIS, None, 0, None) == 5
+    assert f(A, A, 1, 1, 64, 16, A, None, 0, None) == 4          # workspace required
+    assert f(A, A, 1, 1, 64, 16, A, A, 4 * (2 * 4096 + 2 * 128 + 3 * 8) - 1, None) == 4
+    assert f(A, A, 1, 1, (1 << 22) + 1, 16, A, A, 1 << 30, None) == 2
 
 
 def _reindex(L, mode=1, sc=None, q=A, w=A, k=A, kd=1, pool=A, kb=2048, vis=A, B=1, n_q=1, N=1 << 20,
@@ -90,6 +93,7 @@ def test_reindex_topk_validation(L):
     assert _reindex(L, kd=4) == 3
     assert _reindex(L) == 4                         # no workspace for the re-scored pool
     assert _reindex(L, ws=A, ws_bytes=2048 * 8 * 4 - 1) == 4
+    assert _reindex(L, mode=0, sc=A, q=None) == 4    # stored scores: no query needed, workspace is
     assert _reindex(L, vis=MIS) == 5
 
 
