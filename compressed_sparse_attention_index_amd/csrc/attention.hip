@@ -16,8 +16,9 @@
 //      (lane: entry lane%32, dims [256*half, +256)), dequantises them exactly
 //      to bf16 with the gfx950 conversion instructions, and writes its share
 //      of them to an LDS tile [64 entries][512 dims];
-//   2. S^T[entry][head] = K . q^T on 32x32x16 bf16 MFMA with q held in
-//      registers, so each lane ends up with 16 logits of one head;
+//   2. S^T[entry][head] = K . q^T on 32x32x16 bf16 MFMA; q of the row is
+//      staged once in LDS (rows padded so the operand reads are conflict-free)
+//      and each lane ends up with 16 logits of one head;
 //   3. online softmax in fp32 (log2 domain); the two waves sharing a head tile
 //      exchange per-head maxima and sums through LDS;
 //   4. O^T[dim][head] += V^T . P^T: P^T is the softmax output still in
@@ -37,6 +38,7 @@ constexpr int kThreads = 256;
 constexpr int kChunk = 64;
 constexpr int kTile = 32;
 constexpr int kVPitch = 544;   // bf16 per LDS row: 1088 B, rows 64 B apart mod 256
+constexpr int kQPitch = 520;   // bf16 per q row in LDS: 1040 B, rows 16 B apart mod 256
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kTargetWgs = 512;
@@ -114,6 +116,7 @@ __device__ __forceinline__ bf16x8 tr_read_pair(const uint16_t* vbuf, int row, in
 
 __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t vbuf[kChunk * kVPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t qbuf[kHeads * kQPitch];
   __shared__ __attribute__((aligned(16))) uint32_t pbuf[4][64][8];
   __shared__ float xbuf[4][32];
   __shared__ float lbuf[4][32];
@@ -132,14 +135,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
   int lo = max(max(qpos - a.window + 1, a.swa_pos0[b]), 0);
   if (a.replay_start >= 0) lo = max(lo, a.replay_start);
 
-  // q^T operand of this head tile: lane = head 32h + c, dims [256*half, +256).
-  bf16x8 qb[32];
+  // q of all 64 heads staged in LDS (coalesced 16-B loads); the q^T operand
+  // of a step is read from there: lane = head 32h + c, dims 256*half + 8*s.
   {
-    const u32x4* p = reinterpret_cast<const u32x4*>(
-        a.q + (static_cast<size_t>(r) * kHeads + 32 * h + c) * kDim + 256 * half);
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.q + static_cast<size_t>(r) * kHeads * kDim);
 #pragma unroll
-    for (int s = 0; s < 32; ++s) qb[s] = __builtin_bit_cast(bf16x8, p[s]);
+    for (int i = 0; i < kHeads * kDim / 8 / kThreads; ++i) {
+      const int g = i * kThreads + threadIdx.x;         // 16-B chunk: head g/64, dims 8*(g%64)
+      *reinterpret_cast<u32x4*>(qbuf + (g >> 6) * kQPitch + 8 * (g & 63)) = src[g];
+    }
   }
+  const uint16_t* qrow = qbuf + (32 * h + c) * kQPitch + 256 * half;
 
   f32x16 o[8];
 #pragma unroll
@@ -161,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
       const bf16x8 kb = dequant_step(raw, is_main, s);
       if ((s & 1) == h)
         *reinterpret_cast<bf16x8*>(vbuf + (kTile * e + c) * kVPitch + 256 * half + 8 * s) = kb;
-      sacc = mfma32(kb, qb[s], sacc);
+      sacc = mfma32(kb, *reinterpret_cast<const bf16x8*>(qrow + 8 * s), sacc);
     }
     if (ch + 1 < c1)
       valid = load_entry(a, raw, r, b, base + kChunk + c, tkp, half, qpos, lo);
@@ -270,26 +276,48 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
 }
 
 // Merge of split partials in split order: one workgroup per (row, head),
-// 64 threads x 8 dims.
+// 64 threads x 8 dims.  Lane s < nsplit fetches split s's (m, l); the merge
+// weights are formed in registers and the partial outputs are read with all
+// loads of a group of splits issued together.
+constexpr int kMaxSplits = 64;
+
 __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
   const int r = blockIdx.x / kHeads;
   const int head = blockIdx.x % kHeads;
   const int t = threadIdx.x;
-  float mx = -__builtin_inff();
-  for (int s = 0; s < a.nsplit; ++s)
-    mx = fmaxf(mx, a.part_ml[((static_cast<size_t>(r) * a.nsplit + s) * kHeads + head) * 2]);
+  const size_t ps0 = static_cast<size_t>(r) * a.nsplit;
+  float ms = -__builtin_inff(), ls = 0.0f;
+  if (t < a.nsplit) {
+    ms = a.part_ml[((ps0 + t) * kHeads + head) * 2];
+    ls = a.part_ml[((ps0 + t) * kHeads + head) * 2 + 1];
+  }
+  float mx = ms;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
+  const float wgt_mine = (ms == -__builtin_inff()) ? 0.0f : exp2f(ms - mx);
   float L = 0.0f;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int s = 0; s < a.nsplit; ++s) {
-    const size_t ps = static_cast<size_t>(r) * a.nsplit + s;
-    const float ms = a.part_ml[(ps * kHeads + head) * 2];
-    const float ls = a.part_ml[(ps * kHeads + head) * 2 + 1];
-    const float wgt = (ms == -__builtin_inff()) ? 0.0f : exp2f(ms - mx);
-    L += wgt * ls;
-    const f32x4_t* po = reinterpret_cast<const f32x4_t*>(a.part_o + (ps * kHeads + head) * kDim + 8 * t);
-    const f32x4_t u = po[0], v = po[1];
-    acc[0] += wgt * u[0]; acc[1] += wgt * u[1]; acc[2] += wgt * u[2]; acc[3] += wgt * u[3];
-    acc[4] += wgt * v[0]; acc[5] += wgt * v[1]; acc[6] += wgt * v[2]; acc[7] += wgt * v[3];
+  constexpr int kGroup = 4;
+  for (int s0 = 0; s0 < a.nsplit; s0 += kGroup) {
+    f32x4_t u[kGroup], v[kGroup];
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) {
+      const int s = min(s0 + g, a.nsplit - 1);
+      const f32x4_t* po = reinterpret_cast<const f32x4_t*>(
+          a.part_o + ((ps0 + s) * kHeads + head) * kDim + 8 * t);
+      u[g] = po[0];
+      v[g] = po[1];
+    }
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) {
+      const float wgt = __shfl(wgt_mine, s0 + g, 64);
+      const float lsg = __shfl(ls, s0 + g, 64);
+      if (s0 + g < a.nsplit) {
+        L += wgt * lsg;
+        acc[0] += wgt * u[g][0]; acc[1] += wgt * u[g][1]; acc[2] += wgt * u[g][2]; acc[3] += wgt * u[g][3];
+        acc[4] += wgt * v[g][0]; acc[5] += wgt * v[g][1]; acc[6] += wgt * v[g][2]; acc[7] += wgt * v[g][3];
+      }
+    }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   uint32_t w[4];
@@ -314,6 +342,7 @@ void plan(int rows, int top_k, int* n_chunks, int* cps, int* nsplit) {
   long long c = (total + kTargetWgs - 1) / kTargetWgs;
   if (c < 1) c = 1;
   if (c > *n_chunks) c = *n_chunks;
+  if ((*n_chunks + c - 1) / c > kMaxSplits) c = (*n_chunks + kMaxSplits - 1) / kMaxSplits;
   *cps = static_cast<int>(c);
   *nsplit = (*n_chunks + *cps - 1) / *cps;
 }

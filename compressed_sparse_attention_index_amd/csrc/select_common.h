@@ -14,14 +14,29 @@ constexpr int kHistBits = 12;                 // first-level bins: key bits [31:
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kHistShift = 32 - kHistBits;
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts
+// (within rows of 16 lanes) and row broadcasts (across rows).
 __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
   return v;
+}
+
+// Maximum over the 64 lanes of a wave with DPP (quad swaps, mirrors, row
+// broadcasts); lane 63 ends with the result, which is then read out.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  v = mx(v, __builtin_amdgcn_update_dpp(v, v, 0xb1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+  v = mx(v, __builtin_amdgcn_update_dpp(v, v, 0x4e, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+  v = mx(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+  v = mx(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xf, 0xf, false));  // row_mirror
+  v = mx(v, __builtin_amdgcn_update_dpp(v, v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = mx(v, __builtin_amdgcn_update_dpp(v, v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
 // Appends `pred` lanes of the wave to a list through one atomic per wave;
@@ -65,6 +80,17 @@ struct Wg {
     uint32_t t;
     excl_scan(v, wb, &t);
     return t;
+  }
+
+  __device__ static uint32_t reduce_max(uint32_t v, uint32_t* wb) {
+    const int wave = threadIdx.x >> 6;
+    v = wave_max_u32(v);
+    if (lane_id() == 0) wb[wave] = v;
+    __syncthreads();
+    uint32_t m = 0;
+    for (int w = 0; w < kWaves; ++w) m = m > wb[w] ? m : wb[w];
+    __syncthreads();
+    return m;
   }
 
   // Bin holding the item of 1-based rank `rank`, counting from the top bin

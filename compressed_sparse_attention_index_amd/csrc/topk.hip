@@ -350,12 +350,20 @@ __global__ __launch_bounds__(kPsThreads) void k_pool_score(PoolArgs a) {
   }
 }
 
-struct LdsKeys {   // all slots of a row in LDS; empty slots hold key 0
+// All slots of a row in LDS (empty slots hold key 0).  Thread t owns slots
+// [16 t, 16 t + 16); slot 16 t + e is stored at LDS index e * 1024 + t so that
+// the accesses of a wave fall in distinct banks.  The accessor walks LDS
+// indices and reports keys as offsets from the smallest valid key; empty slots
+// read as all-ones, which matches no bin prefix of at most 2048 bins.
+__device__ __forceinline__ int pf_lds(int slot) { return (slot & 15) * 1024 + (slot >> 4); }
+struct LdsOffsets {
   const uint32_t* k;
-  uint32_t n;
-  __device__ uint32_t key(uint32_t i) const { return k[i]; }
-  __device__ int32_t id(uint32_t i) const { return static_cast<int32_t>(i); }
+  uint32_t kmin;
+  uint32_t n;   // LDS entries to walk (multiple of 1024 covering every slot)
+  __device__ uint32_t key(uint32_t c) const { return k[c] ? k[c] - kmin : 0xffffffffu; }
+  __device__ int32_t id(uint32_t c) const { return static_cast<int32_t>((c & 1023) * 16 + (c >> 10)); }
 };
+constexpr int kPfBins = 2048;
 
 __global__ __launch_bounds__(kPsThreads) void k_pool_final(PoolArgs a) {
   __shared__ uint32_t keys[kPsMaxSlots];
@@ -371,44 +379,91 @@ __global__ __launch_bounds__(kPsThreads) void k_pool_final(PoolArgs a) {
   const int32_t* prow = a.pool + static_cast<size_t>(r) * a.kb;
   const float* ps = a.ps + static_cast<size_t>(r) * nslots;
   const float* srow = a.scores ? a.scores + static_cast<size_t>(r) * a.N_cap : nullptr;
-  // Empty slots get key 0, which no finite score has.
-  for (int i = tid; i < kHistBins; i += kPsThreads) h[i] = 0;
+  // Empty slots get key 0, which no finite score has.  Thread t takes the
+  // contiguous slots [16 t, 16 t + 16) (two pool blocks) and issues all of
+  // its loads before using any of them.
+  constexpr int kPer = kPsMaxSlots / kPsThreads;
+  static_assert(kPer == 2 * kBlock, "two pool blocks per thread");
+  const int s0 = tid * kPer;
+  const bool mine = s0 < nslots;
+  int blk[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) blk[u] = (mine && (s0 >> 3) + u < a.kb) ? prow[(s0 >> 3) + u] : -1;
+  float sv[kPer];
+  if (srow) {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int bk = blk[e >> 3];
+      const int pos = bk * kBlock + (e & 7);
+      sv[e] = (bk >= 0 && bk < nb_cap && pos < vis) ? srow[pos] : 0.0f;
+    }
+  } else if (s0 + kPer <= nslots) {
+    const f32x4_t* p4 = reinterpret_cast<const f32x4_t*>(ps + s0);
+#pragma unroll
+    for (int e4 = 0; e4 < kPer / 4; ++e4) {
+      const f32x4_t v = p4[e4];
+      sv[4 * e4] = v[0]; sv[4 * e4 + 1] = v[1]; sv[4 * e4 + 2] = v[2]; sv[4 * e4 + 3] = v[3];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) sv[e] = s0 + e < nslots ? ps[s0 + e] : 0.0f;
+  }
   __syncthreads();
-  uint32_t nv = 0;
-  for (int i = tid; i < nslots; i += kPsThreads) {
-    const bool valid = pool_slot_valid(prow, i, nb_cap, vis);
-    const float s = !valid ? 0.0f : (srow ? srow[prow[i >> 3] * kBlock + (i & 7)] : ps[i]);
-    const uint32_t key = valid ? float_to_key(s) : 0u;
-    keys[i] = key;
+  uint32_t nv = 0, kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int bk = blk[e >> 3];
+    const bool valid = mine && bk >= 0 && bk < nb_cap && bk * kBlock + (e & 7) < vis;
+    const uint32_t key = valid ? float_to_key(sv[e]) : 0u;
+    keys[e * kPsThreads + tid] = key;
     if (valid) {
-      atomicAdd(&h[key >> kHistShift], 1u);
       ++nv;
+      kmin = min(kmin, key);
+      kmax = max(kmax, key);
     }
   }
   const uint32_t n_valid = W::sum(nv, wb);   // includes a barrier
+  kmax = W::reduce_max(kmax, wb);
+  kmin = ~W::reduce_max(~kmin, wb);
   const uint32_t need = min(static_cast<uint32_t>(a.top_k), n_valid);
   uint32_t kstar = 1u;              // need == n_valid: every valid (nonzero) key
   int32_t istar = 0x7fffffff;
   if (need > 0 && need < n_valid) {
+    // First level: kPfBins bins spanning [kmin, kmax].
+    const uint32_t range = kmax - kmin;
+    int sh = 0;
+    while ((static_cast<uint64_t>(range) >> sh) >= static_cast<uint64_t>(kPfBins)) ++sh;
+    const int nbins = static_cast<int>(range >> sh) + 1;
+    for (int i = tid; i < nbins; i += kPsThreads) h[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const uint32_t key = keys[e * kPsThreads + tid];
+      if (key) atomicAdd(&h[(key - kmin) >> sh], 1u);
+    }
+    __syncthreads();
     uint32_t above;
-    const int b1 = W::find_rank_bin(h, kHistBins, need, true, wb, &above);
-    W::resolve(LdsKeys{keys, static_cast<uint32_t>(nslots)}, static_cast<uint32_t>(b1) << kHistShift,
-               kHistShift, need - above, hist256, wb, &kstar, &istar);
+    const int b1 = W::find_rank_bin(h, nbins, need, true, wb, &above);
+    uint32_t koff;
+    W::resolve(LdsOffsets{keys, kmin, static_cast<uint32_t>(kPsMaxSlots)}, static_cast<uint32_t>(b1) << sh,
+               sh, need - above, hist256, wb, &koff, &istar);
+    kstar = koff + kmin;
   }
-  const int spt = (nslots + kPsThreads - 1) / kPsThreads;
-  const int s0 = tid * spt;
+  const int spt = kPer;
   uint32_t cnt = 0;
-  for (int i = s0; i < min(s0 + spt, nslots); ++i)
-    cnt += (need > 0 && keys[i] != 0u && selected(keys[i], i, kstar, istar)) ? 1u : 0u;
+  for (int i = s0; i < min(s0 + spt, nslots); ++i) {
+    const uint32_t key = keys[pf_lds(i)];
+    cnt += (need > 0 && key != 0u && selected(key, i, kstar, istar)) ? 1u : 0u;
+  }
   uint32_t total;
   uint32_t off = W::excl_scan(cnt, wb, &total);
   int32_t* orow = a.out + static_cast<size_t>(r) * a.top_k;
   float* krow = a.out_key ? a.out_key + static_cast<size_t>(r) * a.top_k : nullptr;
   for (int i = s0; i < min(s0 + spt, nslots); ++i) {
-    const uint32_t key = keys[i];
+    const uint32_t key = keys[pf_lds(i)];
     if (need > 0 && key != 0u && selected(key, i, kstar, istar)) {
       if (off < need) {
-        orow[off] = prow[i >> 3] * kBlock + (i & 7);
+        orow[off] = blk[(i - s0) >> 3] * kBlock + (i & 7);
         if (krow) krow[off] = key_to_float(key);
       }
       ++off;
