@@ -43,6 +43,8 @@ def parse():
                    help="CPU time budget of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="skip the graph-replay measurement")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run a 1 GiB device copy (reference for the traffic counters)")
     return p.parse_args()
 
 
@@ -69,7 +71,6 @@ class Step:
         self.lse = z(B, n_q, 64, dt=torch.float32)
         self.idx = z(B, n_q, 512)
         self.ws_attn = self._ws(csa.OP_SPARSE_ATTN, 512, 0)
-        self.scan_ev = []
         if name == "reuse_128k":
             return
         self.bm = z(B, n_q, (self.N + 7) // 8, dt=torch.float32)
@@ -77,6 +78,7 @@ class Step:
             self.scores = z(B, n_q, self.N, dt=torch.float32)
             return
         self.pool = z(B, n_q, 2048)
+        self.ws_bt = self._ws(csa.OP_BLOCK_TOPK, 512, 2048)
         self.ws_re = self._ws(csa.OP_REINDEX_TOPK, 512, 2048)
         if "q_idx2" in d:
             self.idx2 = z(B, n_q, 512)
@@ -87,41 +89,35 @@ class Step:
         n = self.csa.workspace_size(op, self.B, self.n_q, self.N, top_k, kb)
         return self.torch.empty(max(n, 16), dtype=self.torch.uint8, device="cuda")
 
-    def _scan(self, timed):
+    def _scan(self):
         d, csa = self.d, self.csa
-        if timed:
-            e0 = self.torch.cuda.Event(enable_timing=True)
-            e1 = self.torch.cuda.Event(enable_timing=True)
-            e0.record()
         csa.index_score(d["q_idx"], d["w_idx"], d["k_idx"], d["vis_len"], block_max=self.bm,
                         scores=getattr(self, "scores", None))
-        if timed:
-            e1.record()
-            self.scan_ev.append((e0, e1))
+
+    def dominant(self):
+        """Launch only the kernel the roofline figure is about."""
+        if self.name == "reuse_128k":
+            d = self.d
+            self._attn(self.csa.reuse_attn, d["q"], d["swa"], d["idx"], self.out, self.lse)
+        else:
+            self._scan()
 
     def _attn(self, fn, q, swa, idx, out, lse):
         d = self.d
         fn(q, d["kv_fp4"], d["kv_scale"], idx, swa, d["swa_pos0"], d["q_pos"], d["sm_scale"], out,
            lse=lse, ws=self.ws_attn)
 
-    def run(self, timed=False):
+    def run(self):
         d, csa = self.d, self.csa
         if self.name == "reuse_128k":
-            if timed:
-                e0 = self.torch.cuda.Event(enable_timing=True)
-                e1 = self.torch.cuda.Event(enable_timing=True)
-                e0.record()
             self._attn(csa.reuse_attn, d["q"], d["swa"], d["idx"], self.out, self.lse)
-            if timed:
-                e1.record()
-                self.scan_ev.append((e0, e1))
             return
-        self._scan(timed)
+        self._scan()
         if self.name == "prefill_128k":
             csa.reindex_topk(csa.MODE_FULL, d["vis_len"], self.N, 512, self.idx, scores=self.scores)
             self._attn(csa.sparse_attn_decode, d["q"], d["swa"], self.idx, self.out, self.lse)
             return
-        csa.block_topk(self.bm, d["vis_len"], self.N, 2048, self.pool)
+        csa.block_topk(self.bm, d["vis_len"], self.N, 2048, self.pool, ws=self.ws_bt)
         csa.reindex_topk(csa.MODE_FULL, d["vis_len"], self.N, 512, self.idx, q_idx=d["q_idx"],
                          w_idx=d["w_idx"], k_idx=d["k_idx"], pool_blocks=self.pool, ws=self.ws_re)
         self._attn(csa.sparse_attn_decode, d["q"], d["swa"], self.idx, self.out, self.lse)
@@ -246,17 +242,26 @@ def main():
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
-    step.scan_ev.clear()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
     for _ in range(args.steps):
-        step.run(timed=True)
+        step.run()
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
-    dom_ms = sum(a.elapsed_time(b) for a, b in step.scan_ev) / len(step.scan_ev)
+    # The dominant kernel alone: `steps` back-to-back launches on the same
+    # stream between two events (the launches see the same inputs as a step).
+    for _ in range(args.warmup):
+        step.dominant()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        step.dominant()
+    ev1.record()
+    torch.cuda.synchronize()
+    dom_ms = ev0.elapsed_time(ev1) / args.steps
     log(f"[bench] eager: {ms * 1e3:.1f} us/step, dominant kernel {dom_ms * 1e3:.1f} us/launch")
 
     graph_ms = None
@@ -282,6 +287,16 @@ def main():
             log(f"[bench] graph replay: {graph_ms * 1e3:.1f} us/step")
         except Exception as exc:  # graph capture is an extra measurement only
             log(f"[bench] graph replay skipped: {exc!r}")
+
+    if args.calibrate_copy:
+        # A plain 1 GiB device-to-device copy: rocprofv3's FETCH_SIZE / WRITE_SIZE
+        # for it scale the counters of the dominant kernel to bytes.
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     dominant, per_launch, bound, step_bytes = algorithmic(args.workload, d)
     rows = d["B"] * d["n_q"]
