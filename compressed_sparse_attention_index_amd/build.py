@@ -19,6 +19,10 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
+# Per-source extra flags.  The attention kernel rescales and merges its MFMA
+# accumulators with vector ALU code; keeping MFMA results in ordinary VGPRs
+# (not accumulation registers) avoids copying all of them every iteration.
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd):
@@ -33,7 +37,8 @@ def build(verbose=False):
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
-    cmds = [[HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    cmds = [[HIPCC, *FLAGS, *EXTRA.get(s, []), "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         for msg in ex.map(_run, cmds):
             if verbose and msg.strip():

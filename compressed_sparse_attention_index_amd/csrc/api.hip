@@ -36,7 +36,9 @@ csa2_status attn_common(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t*
   if (st != CSA2_OK) return st;
   if (N_cap < 1 || N_cap > kMaxNcap || top_k < 0 || top_k > 512 || S_cap < 0) return CSA2_ERR_SHAPE;
   if (static_cast<int64_t>(B) * n_q > kMaxGridY) return CSA2_ERR_SHAPE;
-  if (!(sm_scale == sm_scale)) return CSA2_ERR_SHAPE;
+  // A softmax scale is positive and finite (1 / sqrt(512) on these layers);
+  // the kernel relies on it to keep empty slots at -inf.
+  if (!(sm_scale > 0.0f) || !(sm_scale < __builtin_inff())) return CSA2_ERR_SHAPE;
   int32_t window = 128, replay_start = -1;
   if (opts) {
     if (opts->kv_fmt != CSA2_KV_MXFP4_E8M0_32 || opts->reserved != 0) return CSA2_ERR_UNSUPPORTED;

@@ -65,9 +65,8 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float scale) {
 // E8M0 code -> 2^(code-127) as a float (code 0 gives the subnormal 2^-127,
 // code 255 gives NaN).
 __device__ __forceinline__ float e8m0_to_float(uint32_t code) {
-  if (code == 0) return __uint_as_float(0x00400000u);
-  if (code == 255) return __uint_as_float(0x7fc00000u);
-  return __uint_as_float(code << 23);
+  const uint32_t bits = code == 0 ? 0x00400000u : (code == 255 ? 0x7fc00000u : code << 23);
+  return __uint_as_float(bits);
 }
 
 // Order-preserving map of fp32 to uint32: larger score -> larger key; -0 and
@@ -93,5 +92,14 @@ __device__ __forceinline__ float wave_xor(float v, int mask) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Waits until at most N vector-memory instructions of this wave are still
+// outstanding (they complete in issue order).  Direct-to-LDS loads are not
+// tracked by the compiler's own waits, so their consumers call this.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 }  // namespace csa2

@@ -47,12 +47,6 @@ __device__ __forceinline__ void emit(float s, int pos, int vis, int half, int co
 // (16 B per lane, one row per lane) free of LDS bank conflicts.  DEPTH tiles
 // are in flight per wave; loads complete in issue order, so waiting until at
 // most DEPTH tiles' loads are outstanding guarantees the oldest has landed.
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 template <bool FP8>
 struct ScanTile {
   static constexpr int kRowBytes = FP8 ? 128 : 256;

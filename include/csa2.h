@@ -223,6 +223,7 @@ CSA2_API csa2_status csa2_reindex_topk(csa2_mode mode, const float* scores, cons
  *   swa_kv    [B, S_cap, 512] uint8 FP8 E4M3FN; slot i holds token swa_pos0[b] + i
  *   swa_pos0  [B] int32
  *   q_pos     [B, n_q] int32 token position of each query
+ *   sm_scale  softmax scale, finite and > 0 (else CSA2_ERR_SHAPE)
  *   opts      NULL or options (window, replay_start, kv_fmt)
  *   out       [B, n_q, 64, 512] bf16 output
  *   lse       [B, n_q, 64] fp32 output or NULL

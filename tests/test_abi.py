@@ -115,6 +115,9 @@ def test_attention_validation(L):
         assert _attn(L, fn, N=0) == 2
         assert _attn(L, fn, B=70000) == 2
         assert _attn(L, fn, scale=float("nan")) == 2
+        assert _attn(L, fn, scale=0.0) == 2
+        assert _attn(L, fn, scale=-0.04) == 2
+        assert _attn(L, fn, scale=float("inf")) == 2
         bad_fmt = csa.AttnOpts(128, -1, 1, 0)
         assert _attn(L, fn, opts=ctypes.byref(bad_fmt)) == 3
         bad_win = csa.AttnOpts(129, -1, 0, 0)
