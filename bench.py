@@ -73,10 +73,12 @@ class Step:
         self.ws_attn = self._ws(csa.OP_SPARSE_ATTN, 512, 0)
         if name == "reuse_128k":
             return
-        self.bm = z(B, n_q, (self.N + 7) // 8, dt=torch.float32)
         if name == "prefill_128k":
+            # The flat Top-512 reads the scores; no block maxima are needed.
+            self.bm = None
             self.scores = z(B, n_q, self.N, dt=torch.float32)
             return
+        self.bm = z(B, n_q, (self.N + 7) // 8, dt=torch.float32)
         self.pool = z(B, n_q, 2048)
         self.ws_bt = self._ws(csa.OP_BLOCK_TOPK, 512, 2048)
         self.ws_re = self._ws(csa.OP_REINDEX_TOPK, 512, 2048)

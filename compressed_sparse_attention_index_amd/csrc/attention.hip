@@ -100,40 +100,6 @@ struct State {
 
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)p));
-}
-
-// Direct-to-LDS loads (lane l's 16 or 4 bytes land at lds + 16 l or + 4 l;
-// lds must be wave-uniform).  They are issued as assembly on purpose: the
-// compiler then does not track them, so it never drains them before unrelated
-// LDS accesses or barriers; their consumers wait with wait_vmem, and the
-// kernel issues no other vector-memory loads while any of them is in flight.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(lds), "v"(src)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
-               :
-               : "s"(lds), "v"(src)
-               : "memory", "m0");
-}
-
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS
-// operations, not for its direct-to-LDS loads in flight.  Every wave reads
-// only its own staging slot, after wait_vmem, so the staged bytes need no
-// barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Whether the wave's tile of chunk ch holds selected entries (else window).
 __device__ __forceinline__ bool tile_is_main(const RowCtx& x, int ch) {
   return kChunk * ch + kTile * x.e < x.tkp;
@@ -464,14 +430,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) v[k] = p[k];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      u32x4 w;
-      asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(w.x) : "v"(v[k].x));
-      asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(w.y) : "v"(v[k].y));
-      asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(w.z) : "v"(v[k].z));
-      asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(w.w) : "v"(v[k].w));
-      st.qb[k] = __builtin_bit_cast(bf16x8, w);
-    }
+    for (int k = 0; k < 16; ++k) st.qb[k] = __builtin_bit_cast(bf16x8, to_agpr(v[k]));
   }
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {

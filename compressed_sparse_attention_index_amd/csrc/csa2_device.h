@@ -102,4 +102,51 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Byte offset of an LDS object within the workgroup's LDS.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)p));
+}
+
+// Direct-to-LDS loads (lane l's 16 or 4 bytes land at lds + 16 l or + 4 l;
+// lds must be wave-uniform).  They are issued as assembly on purpose: the
+// compiler then does not track them, so it never drains them before
+// unrelated LDS accesses or barriers.  Their consumers wait with wait_vmem,
+// and a kernel that uses them issues no other vector-memory loads while any
+// of them is in flight (the compiler's own waits would miscount).
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds), "v"(src)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(lds), "v"(src)
+               : "memory", "m0");
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its direct-to-LDS loads in flight (which the caller
+// waits for with wait_vmem before the barrier when other waves read them).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Moves a value into accumulation registers.  Used for MFMA operands that
+// are loop-invariant (an MFMA may read A and B from there), which leaves the
+// VGPRs to the accumulators and to loads in flight.
+__device__ __forceinline__ u32x4 to_agpr(u32x4 v) {
+  u32x4 w;
+  asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(w.x) : "v"(v.x));
+  asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(w.y) : "v"(v.y));
+  asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(w.z) : "v"(v.z));
+  asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(w.w) : "v"(v.w));
+  return w;
+}
+
 }  // namespace csa2

@@ -11,6 +11,12 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w_idx, const v
                               bool fp8, const int32_t* vis_len, int B, int n_q, int N_cap,
                               float* scores, float* block_max, hipStream_t stream);
 
+// Prefill-chunk scoring on matrix cores (n_q >= 16 rows per sequence); see
+// index_gemm.hip.
+hipError_t launch_index_gemm(const uint16_t* q_idx, const float* w_idx, const uint8_t* k_idx,
+                             bool fp8, const int32_t* vis_len, int B, int n_q, int N_cap,
+                             float* scores, float* block_max, hipStream_t stream);
+
 // Block Top-K (pool of blocks); see topk.hip.
 size_t block_topk_workspace_bytes(int rows, int N_cap);
 int block_topk_max_blocks();

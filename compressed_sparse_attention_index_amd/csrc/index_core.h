@@ -61,12 +61,19 @@ __device__ __forceinline__ f32x16 key_tile_dot(const bf16x8 qa[8], const KeyTile
   return acc;
 }
 
+// max(0, x) as one integer max on the bit pattern: IEEE floats of either
+// sign order like their bits read as signed integers, so every negative
+// value (and -0) maps to +0 and every other value is kept.
+__device__ __forceinline__ float relu(float x) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+
 // ReLU-weighted head sum; every lane returns the full 32-head score of its
 // position (lanes l and l^32 hold the same value).
 __device__ __forceinline__ float head_sum(const f32x16& acc, const float wr[16]) {
   float p = 0.0f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) p = __builtin_fmaf(wr[r], fmaxf(acc[r], 0.0f), p);
+  for (int r = 0; r < 16; ++r) p = __builtin_fmaf(wr[r], relu(acc[r]), p);
   return p + other_half(p);
 }
 

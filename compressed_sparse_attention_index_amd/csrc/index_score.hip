@@ -145,70 +145,6 @@ __global__ __launch_bounds__(kThreads) void k_index_scan(
   }
 }
 
-// Prefill chunk: a workgroup takes 16 query rows of one sequence (4 per wave)
-// and a range of key tiles; each wave reuses every key tile it loads for its
-// 4 rows.  Query rows only see their own visible prefix.
-constexpr int kRowsPerWave = 4;
-constexpr int kRowsPerWg = kRowsPerWave * kWaves;
-
-template <bool FP8>
-__global__ __launch_bounds__(kThreads) void k_index_gemm(
-    const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
-    const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ vis_len, int n_q, int N_cap,
-    int tiles_per_wg, float* __restrict__ scores, float* __restrict__ block_max) {
-  __shared__ float w_lds[kRowsPerWg][kIdxHeads];
-  const int b = blockIdx.z;
-  const int j_wg = blockIdx.y * kRowsPerWg;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int half = lane >> 5, col = lane & 31;
-  const size_t row0 = static_cast<size_t>(b) * n_q;
-
-  for (int i = threadIdx.x; i < kRowsPerWg * kIdxHeads; i += kThreads) {
-    const int j = j_wg + i / kIdxHeads;
-    w_lds[i / kIdxHeads][i % kIdxHeads] = j < n_q ? w_idx[(row0 + j) * kIdxHeads + i % kIdxHeads] : 0.0f;
-  }
-  __syncthreads();
-
-  const int j0 = j_wg + wave * kRowsPerWave;
-  int vis[kRowsPerWave];
-  int vis_max = 0;
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    vis[i] = (j0 + i < n_q) ? min(max(vis_len[row0 + j0 + i], 0), N_cap) : 0;
-    vis_max = max(vis_max, vis[i]);
-  }
-  const int t_begin = blockIdx.x * tiles_per_wg;
-  const int t_end = min(t_begin + tiles_per_wg, (vis_max + 31) >> 5);
-  if (t_begin >= t_end) return;
-
-  bf16x8 qa[kRowsPerWave][8];
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    const int j = min(j0 + i, n_q - 1);
-    load_query(qa[i], q_idx + (row0 + j) * kIdxHeads * kIdxDim, col, half);
-  }
-  const uint8_t* kb = k_idx + static_cast<size_t>(b) * N_cap * (FP8 ? 128 : 256);
-  const size_t nb_cap = (N_cap + 7) >> 3;
-
-  KeyTile<FP8> cur, nxt;
-  load_key_half<FP8>(cur, key_row<FP8>(kb, 32 * t_begin + col, N_cap), half);
-  for (int t = t_begin; t < t_end; ++t) {
-    if (t + 1 < t_end) load_key_half<FP8>(nxt, key_row<FP8>(kb, 32 * (t + 1) + col, N_cap), half);
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-      if (32 * t >= vis[i]) continue;  // wave-uniform
-      float wr[16];
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) wr[rr] = w_lds[wave * kRowsPerWave + i][8 * (rr / 4) + 4 * half + (rr % 4)];
-      const float s = head_sum(key_tile_dot<FP8>(qa[i], cur), wr);
-      const size_t row = row0 + j0 + i;
-      emit(s, 32 * t + col, vis[i], half, col, scores ? scores + row * N_cap : nullptr,
-           block_max ? block_max + row * nb_cap : nullptr);
-    }
-    cur = nxt;
-  }
-}
-
 int pick_tiles_per_wg(long long total_tiles, int min_tiles, int target_wgs, int max_tiles) {
   long long t = (total_tiles + target_wgs - 1) / target_wgs;
   if (t < min_tiles) t = min_tiles;
@@ -224,7 +160,7 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w_idx, const v
                               float* scores, float* block_max, hipStream_t stream) {
   const int tiles = (N_cap + 31) / 32;
   const uint8_t* kb = static_cast<const uint8_t*>(k_idx);
-  if (n_q < kRowsPerWg) {
+  if (n_q < 16) {
     const int rows = B * n_q;
     const int tpw = pick_tiles_per_wg(static_cast<long long>(tiles) * rows, 8, 4096, 64);
     dim3 grid((tiles + tpw - 1) / tpw, rows);
@@ -235,15 +171,8 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w_idx, const v
       hipLaunchKernelGGL((k_index_scan<false, 1>), grid, dim3(kThreads), 0, stream, q_idx, w_idx,
                          kb, vis_len, n_q, N_cap, tpw, scores, block_max);
   } else {
-    const int groups = (n_q + kRowsPerWg - 1) / kRowsPerWg;
-    const int tpw = 64;
-    dim3 grid((tiles + tpw - 1) / tpw, groups, B);
-    if (fp8)
-      hipLaunchKernelGGL(k_index_gemm<true>, grid, dim3(kThreads), 0, stream, q_idx, w_idx, kb,
-                         vis_len, n_q, N_cap, tpw, scores, block_max);
-    else
-      hipLaunchKernelGGL(k_index_gemm<false>, grid, dim3(kThreads), 0, stream, q_idx, w_idx, kb,
-                         vis_len, n_q, N_cap, tpw, scores, block_max);
+    return launch_index_gemm(q_idx, w_idx, kb, fp8, vis_len, B, n_q, N_cap, scores, block_max,
+                             stream);
   }
   return hipGetLastError();
 }

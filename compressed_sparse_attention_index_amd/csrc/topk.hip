@@ -19,7 +19,8 @@
 //     re-scored on matrix cores (or stored scores are read); one workgroup
 //     per row holds every slot's key in LDS, selects, and compacts in slot
 //     order (= position order).
-//   flat Top-K   (k_flat_select, prefill rows): one workgroup per row.
+//   flat Top-K   (k_flat_select_reg, k_flat_select; prefill rows): one
+//     workgroup per row; rows of up to 73,728 items are held in registers.
 // Workgroups never wait on each other inside a kernel: kernel boundaries
 // order the phases (a device-wide fence per workgroup would write back a
 // whole L2).  The histograms are cleared by a fill kernel at the start of
@@ -64,6 +65,10 @@ struct BtWs {
 
 __device__ __forceinline__ uint32_t mid_bits(uint32_t key) { return (key >> 8) & 0xfffu; }
 
+// Loads of row items i < n are written as row[min(i, n - 1)] followed by a
+// select, not as a conditional load: a conditional load becomes a branch
+// with its own wait, and a thread's loads would then run one at a time.
+
 __global__ __launch_bounds__(kBtThreads) void k_bt_hist(const float* __restrict__ bm,
                                                         const int32_t* __restrict__ vis_len,
                                                         int N_cap, int k, BtWs ws) {
@@ -80,7 +85,8 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_hist(const float* __restrict_
 #pragma unroll
   for (int j = 0; j < kBtItems / kBtThreads; ++j) {
     const int i = i0 + threadIdx.x + j * kBtThreads;
-    v[j] = i < n ? row[i] : 0.0f;
+    v[j] = row[min(i, n - 1)];
+    if (i >= n) v[j] = 0.0f;
   }
 #pragma unroll
   for (int j = 0; j < kBtItems / kBtThreads; ++j) {
@@ -118,7 +124,8 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_filter(const float* __restric
 #pragma unroll
   for (int j = 0; j < kBtItems / kBtThreads; ++j) {
     const int i = i0 + tid + j * kBtThreads;
-    v[j] = i < n ? row[i] : 0.0f;
+    v[j] = row[min(i, n - 1)];
+    if (i >= n) v[j] = 0.0f;
   }
 #pragma unroll
   for (int j = 0; j < kBtItems / kBtThreads; ++j) {
@@ -497,7 +504,8 @@ __device__ void flat_gather(const float* row, int n, uint32_t prefix, int shift,
 #pragma unroll
     for (int e = 0; e < kFsPer; ++e) {
       const int i = base + e * kFsThreads + threadIdx.x;
-      v[e] = i < n ? row[i] : 0.0f;
+      v[e] = row[min(i, n - 1)];
+      if (i >= n) v[e] = 0.0f;
     }
 #pragma unroll
     for (int e = 0; e < kFsPer; ++e) {
@@ -541,7 +549,8 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select(const float* __restr
 #pragma unroll
       for (int e = 0; e < kFsPer; ++e) {
         const int i = base + e * kFsThreads + tid;
-        v[e] = i < n ? row[i] : 0.0f;
+        v[e] = row[min(i, n - 1)];
+        if (i >= n) v[e] = 0.0f;
       }
 #pragma unroll
       for (int e = 0; e < kFsPer; ++e)
@@ -564,7 +573,8 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select(const float* __restr
 #pragma unroll
         for (int e = 0; e < kFsPer; ++e) {
           const int i = base + e * kFsThreads + tid;
-          v[e] = i < n ? row[i] : 0.0f;
+          v[e] = row[min(i, n - 1)];
+          if (i >= n) v[e] = 0.0f;
         }
 #pragma unroll
         for (int e = 0; e < kFsPer; ++e) {
@@ -602,7 +612,8 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select(const float* __restr
 #pragma unroll
     for (int e = 0; e < kFsPer; ++e) {
       const int i = base + tid * kFsPer + e;
-      v[e] = i < n ? row[i] : -__builtin_inff();
+      v[e] = row[min(i, n - 1)];
+      if (i >= n) v[e] = -__builtin_inff();
       c += (i < n && selected(float_to_key(v[e]), i, kstar, istar)) ? 1u : 0u;
     }
     uint32_t round_total;
@@ -621,6 +632,161 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select(const float* __restr
     written += round_total;
   }
   for (int i = static_cast<int>(min(written, need)) + tid; i < k; i += kFsThreads) {
+    orow[i] = -1;
+    if (krow) krow[i] = -__builtin_inff();
+  }
+}
+
+// Flat Top-K of rows that fit in registers (n <= kFrPer * 1024): the row is
+// read from memory once into registers (item i = e * 1024 + tid), then
+//   1. the row's value range [vmin, vmax] is found and the items are
+//      counted into 2048 bins spread evenly over it (bin order is key order,
+//      and the bins spread the scores, so the LDS atomics rarely collide);
+//   2. the bin holding the k-th item is located; its items (usually a
+//      handful) are copied to LDS and resolved exactly (key radix, then id);
+//   3. the selected items are marked in an LDS bitmap over ids and written
+//      in id order after one prefix sum over the bitmap words.
+// A threshold bin too large for LDS is resolved over the whole row instead.
+constexpr int kFrPer = 72;
+constexpr int kRawBufferFlags = 0x00020000;   // dword 3 of a raw (untyped) buffer descriptor
+constexpr int kFrBins = 2048;
+constexpr int kFrCap = 4096;
+constexpr int kFrWords = kFrPer * kFsThreads / 32;
+
+__global__ __launch_bounds__(kFsThreads) void k_flat_select_reg(
+    const float* __restrict__ scores, const int32_t* __restrict__ vis_len, int N_cap, int k,
+    int32_t* __restrict__ out, float* __restrict__ out_key) {
+  __shared__ uint32_t hist[kFrBins];
+  __shared__ uint32_t ckey_l[kFrCap];
+  __shared__ int32_t cid_l[kFrCap];
+  __shared__ uint32_t bitmap[kFrWords];
+  __shared__ uint32_t hist256[256];
+  __shared__ uint32_t wb[Wg<kFsThreads>::kScratch];
+  __shared__ uint32_t ccount;
+  using W = Wg<kFsThreads>;
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = min(max(vis_len[r], 0), N_cap);
+  const float* row = scores + static_cast<size_t>(r) * N_cap;
+  const uint32_t need = min(static_cast<uint32_t>(k), static_cast<uint32_t>(n));
+
+  // Raw buffer loads: block e of 1024 items gets a descriptor sized to the
+  // items left in the row, so lanes past the end read 0 without a branch,
+  // every lane shares one offset register and all loads are in flight
+  // together.
+  uint32_t key[kFrPer];
+#pragma unroll
+  for (int e = 0; e < kFrPer; ++e) {
+    const int left = min(max(n - e * kFsThreads, 0), kFsThreads);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(row) + e * kFsThreads, static_cast<short>(0), left * 4, kRawBufferFlags);
+    key[e] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * tid, 0, 0);
+  }
+#pragma unroll
+  for (int e = 0; e < kFrPer; ++e)
+    key[e] = e * kFsThreads + tid < n ? float_to_key(__builtin_bit_cast(float, key[e])) : 0u;
+
+  // Every item is taken when need == n: K* = 0, I* = max.
+  uint32_t kstar = 0;
+  int32_t istar = 0x7fffffff;
+  if (need > 0 && need < static_cast<uint32_t>(n)) {
+    uint32_t mx = 0, mn_inv = 0;
+    const int full = n / kFsThreads;   // blocks with every item inside the row
+#pragma unroll
+    for (int e = 0; e < kFrPer; ++e) {
+      if (e < full || e * kFsThreads + tid < n) {
+        mx = max(mx, key[e]);
+        mn_inv = max(mn_inv, ~key[e]);
+      }
+    }
+    for (int i = tid; i < kFrBins; i += kFsThreads) hist[i] = 0;
+    const float vmax = key_to_float(W::reduce_max(mx, wb));
+    const float vmin = key_to_float(~W::reduce_max(mn_inv, wb));
+    // Bins linear in the score value between the row's min and max (scores
+    // cluster in a few binades, so bins linear in the key bits would not
+    // spread them).  Subtraction, scaling and truncation never reverse an
+    // order, so bin order is key order; a row whose range is not finite
+    // puts everything in bin 0 and is resolved over the whole row.
+    const float range = vmax - vmin;
+    const float scale = (range > 0.0f && range < __builtin_inff())
+                            ? static_cast<float>(kFrBins) * 0.99999f / range : 0.0f;
+    auto bin_of = [&](uint32_t kk) {
+      const float x = (key_to_float(kk) - vmin) * scale;
+      return min(kFrBins - 1, max(0, static_cast<int>(x)));
+    };
+#pragma unroll
+    for (int e = 0; e < kFrPer; ++e)
+      if (e * kFsThreads + tid < n) atomicAdd(&hist[bin_of(key[e])], 1u);
+    __syncthreads();
+    uint32_t above;
+    const int b1 = W::find_rank_bin(hist, kFrBins, need, true, wb, &above);
+    const uint32_t ncand = hist[b1];
+    if (ncand <= static_cast<uint32_t>(kFrCap)) {
+      if (tid == 0) ccount = 0;
+      __syncthreads();
+      // Items of bin b1 have keys >= klo, the key of the value one bin width
+      // below the bin's lower edge (a margin against rounding); only waves
+      // holding such keys evaluate the exact bin.
+      const uint32_t klo = scale > 0.0f
+                               ? float_to_key(vmin + (static_cast<float>(b1) - 1.0f) / scale)
+                               : 0u;
+#pragma unroll
+      for (int e = 0; e < kFrPer; ++e) {
+        if (__ballot(key[e] >= klo) == 0) continue;   // wave-uniform
+        const int i = e * kFsThreads + tid;
+        const bool c = i < n && bin_of(key[e]) == b1;
+        const uint32_t slot = wave_append(c, &ccount);
+        if (c) {
+          ckey_l[slot] = key[e];
+          cid_l[slot] = i;
+        }
+      }
+      __syncthreads();
+      W::resolve(ArrayCand{ckey_l, cid_l, ncand}, 0u, 32, need - above, hist256, wb, &kstar,
+                 &istar);
+    } else {
+      W::resolve(FlatCand{row, static_cast<uint32_t>(n)}, 0u, 32, need, hist256, wb, &kstar,
+                 &istar);
+    }
+  }
+
+  // Ordered output through a bitmap over ids: thread t owns words 3t .. 3t+2.
+  for (int w = tid; w < kFrWords; w += kFsThreads) bitmap[w] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kFrPer; ++e) {
+    if (__ballot(key[e] >= kstar) == 0) continue;   // selected items have key >= K*
+    const int i = e * kFsThreads + tid;
+    if (i < n && selected(key[e], i, kstar, istar)) atomicOr(&bitmap[i >> 5], 1u << (i & 31));
+  }
+  __syncthreads();
+  uint32_t words[3] = {0, 0, 0};
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    const int w = 3 * tid + u;
+    words[u] = w < kFrWords ? bitmap[w] : 0u;
+    cnt += __popc(words[u]);
+  }
+  uint32_t total;
+  uint32_t off = W::excl_scan(cnt, wb, &total);
+  int32_t* orow = out + static_cast<size_t>(r) * k;
+  float* krow = out_key ? out_key + static_cast<size_t>(r) * k : nullptr;
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    uint32_t m = words[u];
+    while (m != 0) {
+      const int bit = __ffs(m) - 1;
+      m &= m - 1;
+      const int id = 32 * (3 * tid + u) + bit;
+      if (off < need) {
+        orow[off] = id;
+        if (krow) krow[off] = row[id];
+      }
+      ++off;
+    }
+  }
+  for (int i = static_cast<int>(min(total, need)) + tid; i < k; i += kFsThreads) {
     orow[i] = -1;
     if (krow) krow[i] = -__builtin_inff();
   }
@@ -695,8 +861,12 @@ hipError_t launch_pool_topk(int mode, const float* scores, const uint16_t* q_idx
 
 hipError_t launch_flat_topk(const float* scores, const int32_t* vis_len, int rows, int N_cap,
                             int k, int32_t* out, float* out_key, hipStream_t stream) {
-  hipLaunchKernelGGL(k_flat_select, dim3(rows), dim3(kFsThreads), 0, stream, scores, vis_len,
-                     N_cap, k, out, out_key);
+  if (N_cap <= kFrPer * kFsThreads)
+    hipLaunchKernelGGL(k_flat_select_reg, dim3(rows), dim3(kFsThreads), 0, stream, scores,
+                       vis_len, N_cap, k, out, out_key);
+  else
+    hipLaunchKernelGGL(k_flat_select, dim3(rows), dim3(kFsThreads), 0, stream, scores, vis_len,
+                       N_cap, k, out, out_key);
   return hipGetLastError();
 }
 

@@ -71,18 +71,26 @@ def test_index_score_ragged(kdtype, T):
         assert np.all(np.isnan(bm[b, 0, nb:]))
 
 
-def test_index_score_prefill_rows():
-    # Prefill-shaped call (n_q >= 16): per-row visible lengths, shared keys.
-    d = synth.prefill_workload(n_q=40, prefix_tokens=1000, seed=12)
-    print("index_score prefill n_q=40", flush=True)
+@pytest.mark.parametrize("kdtype,n_q,prefix", [("bf16", 40, 1000), ("bf16", 70, 5000),
+                                               ("fp8", 70, 5000)])
+def test_index_score_prefill_rows(kdtype, n_q, prefix):
+    # Prefill-shaped call (n_q >= 16): per-row visible lengths, shared keys;
+    # 70 rows span several row groups plus a ragged one, and 2,500+ entries
+    # span every key chunk of a group.
+    d = synth.prefill_workload(n_q=n_q, prefix_tokens=prefix, seed=12, kdtype=kdtype)
+    print(f"index_score prefill {kdtype} n_q={n_q} prefix={prefix}", flush=True)
     vis_t, sc, bm = _scan(d)
-    sc, vis = _np(sc), _np(vis_t)[0]
+    sc, bm, vis = _np(sc), _np(bm), _np(vis_t)[0]
     kr, kd = _kraw(d, 0)
-    for j in range(40):
+    for j in range(n_q):
         ref = pipeline.scores_prefix(u16(d["q_idx"][0, j]), _np(d["w_idx"][0, j]), kr, kd, vis[j])
         g = sc[0, j, :vis[j]].astype(np.float64)
         assert np.all(np.abs(g - ref) <= 1e-5 * np.abs(ref) + 1e-6 * np.abs(ref).max()), j
         assert np.all(np.isnan(sc[0, j, vis[j]:]))
+        nb = (vis[j] + 7) // 8
+        bref = indexer.block_max(ref, vis[j])
+        assert np.all(np.abs(bm[0, j, :nb] - bref) <= 1e-5 * np.abs(bref) + 1e-6 * np.abs(ref).max()), j
+        assert np.all(np.isnan(bm[0, j, nb:])), j
 
 
 # --------------------------------------------------------------------------- selection
@@ -140,6 +148,19 @@ def test_select_exact_on_fp32_keys(kind):
     print(f"select {kind}", flush=True)
     for k in ((1, 16, 512, 2048) if kind == "blocks" else (1, 16, 100, 512)):
         _select_case(rows, vis, k, kind)
+
+
+@pytest.mark.parametrize("n", [73728, 80000])
+def test_flat_select_long_rows(n):
+    # 73,728 items is the largest row held in registers; 80,000 takes the
+    # streaming selection.
+    rng = np.random.default_rng(23)
+    rows = [rng.standard_normal(n), np.round(rng.standard_normal(n) * 8) / 8,
+            rng.standard_normal(n) * 1e-3 + 5.0]
+    vis = [n, n - 1, 40000]
+    print(f"flat select long rows n={n}", flush=True)
+    for k in (1, 512):
+        _select_case(rows, vis, k, "flat")
 
 
 def test_pool_topk_stored_scores_exact():
