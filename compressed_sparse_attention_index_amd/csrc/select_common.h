@@ -55,7 +55,7 @@ __device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter) {
 template <int NT>
 struct Wg {
   static constexpr int kWaves = NT / 64;
-  static constexpr int kScratch = 2 * kWaves + 4;   // uint32 words of scratch
+  static constexpr int kScratch = 3 * kWaves + 4;   // uint32 words of scratch
 
   // Exclusive prefix sum in thread order; *total receives the sum.
   __device__ static uint32_t excl_scan(uint32_t v, uint32_t* wb, uint32_t* total) {
@@ -80,6 +80,31 @@ struct Wg {
     uint32_t t;
     excl_scan(v, wb, &t);
     return t;
+  }
+
+  // Sum of a and maxima of b and c over the workgroup in one barrier
+  // (wb needs 3 * kWaves words).
+  __device__ static void reduce_sum_max_max(uint32_t& a, uint32_t& b, uint32_t& c,
+                                            uint32_t* wb) {
+    const int wave = threadIdx.x >> 6;
+    const uint32_t sa = static_cast<uint32_t>(__builtin_amdgcn_readlane(
+        static_cast<int>(wave_incl_scan_u32(a)), 63));
+    const uint32_t mb = wave_max_u32(b), mc = wave_max_u32(c);
+    if (lane_id() == 0) {
+      wb[wave] = sa;
+      wb[kWaves + wave] = mb;
+      wb[2 * kWaves + wave] = mc;
+    }
+    __syncthreads();
+    a = 0;
+    b = 0;
+    c = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      a += wb[w];
+      b = b > wb[kWaves + w] ? b : wb[kWaves + w];
+      c = c > wb[2 * kWaves + w] ? c : wb[2 * kWaves + w];
+    }
+    __syncthreads();
   }
 
   __device__ static uint32_t reduce_max(uint32_t v, uint32_t* wb) {
@@ -188,6 +213,34 @@ struct Wg {
     }
   }
 };
+
+// Threshold among n <= NT candidates (LDS arrays) of which the first `rem`
+// (>= 1) in (key descending, id ascending) order are taken: every candidate
+// counts the candidates ordered before it; the one with rank rem - 1 gives
+// K* and I*.  One pass and one barrier instead of radix passes.
+template <int NT>
+__device__ __forceinline__ void resolve_by_rank(const uint32_t* ckey, const int32_t* cid,
+                                                uint32_t n, uint32_t rem, uint32_t* wb,
+                                                uint32_t* kstar, int32_t* istar) {
+  const int t = threadIdx.x;
+  if (t < static_cast<int>(n)) {
+    const uint32_t kc = ckey[t];
+    const int32_t ic = cid[t];
+    uint32_t rank = 0;
+    for (uint32_t d = 0; d < n; ++d) {
+      const uint32_t kd = ckey[d];
+      rank += (kd > kc || (kd == kc && cid[d] < ic)) ? 1u : 0u;
+    }
+    if (rank == rem - 1) {
+      wb[0] = kc;
+      wb[1] = static_cast<uint32_t>(ic);
+    }
+  }
+  __syncthreads();
+  *kstar = wb[0];
+  *istar = static_cast<int32_t>(wb[1]);
+  __syncthreads();
+}
 
 // Candidate lists held as two arrays (LDS or global memory).
 struct ArrayCand {

@@ -298,9 +298,10 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const int32_t* __restri
 // Pool Top-K: k_pool_score re-scores the pool positions (Reindex, or Full
 // without stored scores) into a pool-score array; k_pool_final (one
 // workgroup per row) loads every slot's key into LDS and selects there.
-constexpr int kPsThreads = 1024;
-constexpr int kPsWaves = kPsThreads / 64;
-constexpr int kPsSlots = 1024;                 // slots per scoring workgroup
+constexpr int kPsThreads = 1024;                // selection workgroup
+constexpr int kPscThreads = 256;                // scoring workgroup: 4 waves x 2 tiles
+constexpr int kPscWaves = kPscThreads / 64;
+constexpr int kPsSlots = 2 * 32 * kPscWaves;    // slots per scoring workgroup
 constexpr int kPsBlocks = kPsSlots / kBlock;
 constexpr int kPsMaxSlots = kMaxPoolBlocks * kBlock;
 
@@ -323,7 +324,7 @@ __device__ __forceinline__ bool pool_slot_valid(const int32_t* prow, int i, int 
 }
 
 template <bool FP8>
-__global__ __launch_bounds__(kPsThreads) void k_pool_score(PoolArgs a) {
+__global__ __launch_bounds__(kPscThreads) void k_pool_score(PoolArgs a) {
   const int r = blockIdx.y;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
@@ -338,14 +339,14 @@ __global__ __launch_bounds__(kPsThreads) void k_pool_score(PoolArgs a) {
   load_weights(wr, a.w_idx + static_cast<size_t>(r) * kIdxHeads, half);
   const int b = r / a.n_q;
   const uint8_t* kbase = a.k_idx + static_cast<size_t>(b) * a.N_cap * (FP8 ? 128 : 256);
-  // 32 tiles of 32 slots (4 pool blocks each); wave w takes tiles w and w + 16.
+  // Tiles of 32 slots (4 pool blocks each); wave w takes tiles w and w + 4.
   const int slot0 = blockIdx.x * kPsSlots;
   KeyTile<FP8> kt[2];
   bool valid[2];
   int slot[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    slot[u] = slot0 + 32 * (wave + kPsWaves * u) + col;
+    slot[u] = slot0 + 32 * (wave + kPscWaves * u) + col;
     valid[u] = slot[u] < nslots && pool_slot_valid(prow, slot[u], nb_cap, vis);
     const int pos = valid[u] ? prow[slot[u] >> 3] * kBlock + (col & 7) : 0;
     load_key_half<FP8>(kt[u], kbase + static_cast<size_t>(pos) * (FP8 ? 128 : 256), half);
@@ -357,26 +358,33 @@ __global__ __launch_bounds__(kPsThreads) void k_pool_score(PoolArgs a) {
   }
 }
 
-// All slots of a row in LDS (empty slots hold key 0).  Thread t owns slots
-// [16 t, 16 t + 16); slot 16 t + e is stored at LDS index e * 1024 + t so that
-// the accesses of a wave fall in distinct banks.  The accessor walks LDS
-// indices and reports keys as offsets from the smallest valid key; empty slots
-// read as all-ones, which matches no bin prefix of at most 2048 bins.
+// Slot 16 t + e of thread t is kept at LDS index e * 1024 + t (the accesses
+// of a wave fall in distinct banks); empty slots hold key 0, which no finite
+// score has.
 __device__ __forceinline__ int pf_lds(int slot) { return (slot & 15) * 1024 + (slot >> 4); }
-struct LdsOffsets {
+struct LdsKeys {
   const uint32_t* k;
-  uint32_t kmin;
   uint32_t n;   // LDS entries to walk (multiple of 1024 covering every slot)
-  __device__ uint32_t key(uint32_t c) const { return k[c] ? k[c] - kmin : 0xffffffffu; }
+  __device__ uint32_t key(uint32_t c) const { return k[c]; }
   __device__ int32_t id(uint32_t c) const { return static_cast<int32_t>((c & 1023) * 16 + (c >> 10)); }
 };
 constexpr int kPfBins = 2048;
+constexpr int kPfCap = 2048;
+constexpr int kRankMax = 256;   // threshold bins up to this size are resolved by counting ranks
 
+// One workgroup per row.  Thread t holds the keys of slots [16 t, 16 t + 16)
+// (two pool blocks) in registers.  The threshold is found as in the flat
+// selection: 2048 bins linear in the score value between the row's min and
+// max, exact resolution of the threshold bin's items only (from LDS copies),
+// or of every slot when that bin is too large.
 __global__ __launch_bounds__(kPsThreads) void k_pool_final(PoolArgs a) {
   __shared__ uint32_t keys[kPsMaxSlots];
-  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t hist[kPfBins];
+  __shared__ uint32_t ckey_l[kPfCap];
+  __shared__ int32_t cid_l[kPfCap];
   __shared__ uint32_t hist256[256];
   __shared__ uint32_t wb[Wg<kPsThreads>::kScratch];
+  __shared__ uint32_t ccount;
   using W = Wg<kPsThreads>;
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
@@ -386,9 +394,6 @@ __global__ __launch_bounds__(kPsThreads) void k_pool_final(PoolArgs a) {
   const int32_t* prow = a.pool + static_cast<size_t>(r) * a.kb;
   const float* ps = a.ps + static_cast<size_t>(r) * nslots;
   const float* srow = a.scores ? a.scores + static_cast<size_t>(r) * a.N_cap : nullptr;
-  // Empty slots get key 0, which no finite score has.  Thread t takes the
-  // contiguous slots [16 t, 16 t + 16) (two pool blocks) and issues all of
-  // its loads before using any of them.
   constexpr int kPer = kPsMaxSlots / kPsThreads;
   static_assert(kPer == 2 * kBlock, "two pool blocks per thread");
   const int s0 = tid * kPer;
@@ -396,13 +401,13 @@ __global__ __launch_bounds__(kPsThreads) void k_pool_final(PoolArgs a) {
   int blk[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) blk[u] = (mine && (s0 >> 3) + u < a.kb) ? prow[(s0 >> 3) + u] : -1;
+  // All of a thread's score loads are issued before any is used.
   float sv[kPer];
   if (srow) {
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
-      const int bk = blk[e >> 3];
-      const int pos = bk * kBlock + (e & 7);
-      sv[e] = (bk >= 0 && bk < nb_cap && pos < vis) ? srow[pos] : 0.0f;
+      const int pos = blk[e >> 3] * kBlock + (e & 7);
+      sv[e] = srow[min(max(pos, 0), vis > 0 ? vis - 1 : 0)];
     }
   } else if (s0 + kPer <= nslots) {
     const f32x4_t* p4 = reinterpret_cast<const f32x4_t*>(ps + s0);
@@ -413,65 +418,91 @@ __global__ __launch_bounds__(kPsThreads) void k_pool_final(PoolArgs a) {
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) sv[e] = s0 + e < nslots ? ps[s0 + e] : 0.0f;
+    for (int e = 0; e < kPer; ++e) sv[e] = ps[min(s0 + e, nslots - 1)];
   }
-  __syncthreads();
-  uint32_t nv = 0, kmin = 0xffffffffu, kmax = 0u;
+  uint32_t key[kPer];
+  uint32_t nv = 0, mx = 0, mn_inv = 0;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
     const int bk = blk[e >> 3];
     const bool valid = mine && bk >= 0 && bk < nb_cap && bk * kBlock + (e & 7) < vis;
-    const uint32_t key = valid ? float_to_key(sv[e]) : 0u;
-    keys[e * kPsThreads + tid] = key;
+    key[e] = valid ? float_to_key(sv[e]) : 0u;
+    nv += valid ? 1u : 0u;
     if (valid) {
-      ++nv;
-      kmin = min(kmin, key);
-      kmax = max(kmax, key);
+      mx = max(mx, key[e]);
+      mn_inv = max(mn_inv, ~key[e]);
     }
   }
-  const uint32_t n_valid = W::sum(nv, wb);   // includes a barrier
-  kmax = W::reduce_max(kmax, wb);
-  kmin = ~W::reduce_max(~kmin, wb);
+  for (int i = tid; i < kPfBins; i += kPsThreads) hist[i] = 0;
+  W::reduce_sum_max_max(nv, mx, mn_inv, wb);   // includes the barrier after the clear
+  const uint32_t n_valid = nv;
   const uint32_t need = min(static_cast<uint32_t>(a.top_k), n_valid);
   uint32_t kstar = 1u;              // need == n_valid: every valid (nonzero) key
   int32_t istar = 0x7fffffff;
   if (need > 0 && need < n_valid) {
-    // First level: kPfBins bins spanning [kmin, kmax].
-    const uint32_t range = kmax - kmin;
-    int sh = 0;
-    while ((static_cast<uint64_t>(range) >> sh) >= static_cast<uint64_t>(kPfBins)) ++sh;
-    const int nbins = static_cast<int>(range >> sh) + 1;
-    for (int i = tid; i < nbins; i += kPsThreads) h[i] = 0;
-    __syncthreads();
+    const float vmax = key_to_float(mx);
+    const float vmin = key_to_float(~mn_inv);
+    // Bins linear in the value; subtraction, scaling and truncation never
+    // reverse an order, so bin order is key order.
+    const float range = vmax - vmin;
+    const float scale = (range > 0.0f && range < __builtin_inff())
+                            ? static_cast<float>(kPfBins) * 0.99999f / range : 0.0f;
+    auto bin_of = [&](uint32_t kk) {
+      const float x = (key_to_float(kk) - vmin) * scale;
+      return min(kPfBins - 1, max(0, static_cast<int>(x)));
+    };
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const uint32_t key = keys[e * kPsThreads + tid];
-      if (key) atomicAdd(&h[(key - kmin) >> sh], 1u);
-    }
+    for (int e = 0; e < kPer; ++e)
+      if (key[e] != 0u) atomicAdd(&hist[bin_of(key[e])], 1u);
     __syncthreads();
     uint32_t above;
-    const int b1 = W::find_rank_bin(h, nbins, need, true, wb, &above);
-    uint32_t koff;
-    W::resolve(LdsOffsets{keys, kmin, static_cast<uint32_t>(kPsMaxSlots)}, static_cast<uint32_t>(b1) << sh,
-               sh, need - above, hist256, wb, &koff, &istar);
-    kstar = koff + kmin;
+    const int b1 = W::find_rank_bin(hist, kPfBins, need, true, wb, &above);
+    const uint32_t ncand = hist[b1];
+    if (ncand <= static_cast<uint32_t>(kPfCap)) {
+      if (tid == 0) ccount = 0;
+      __syncthreads();
+      // Items of bin b1 have keys >= klo (one bin width of margin).
+      const uint32_t klo = scale > 0.0f
+                               ? float_to_key(vmin + (static_cast<float>(b1) - 1.0f) / scale)
+                               : 1u;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        if (__ballot(key[e] >= klo && key[e] != 0u) == 0) continue;   // wave-uniform
+        const bool c = key[e] != 0u && bin_of(key[e]) == b1;
+        const uint32_t slot = wave_append(c, &ccount);
+        if (c) {
+          ckey_l[slot] = key[e];
+          cid_l[slot] = s0 + e;
+        }
+      }
+      __syncthreads();
+      if (ncand <= static_cast<uint32_t>(kRankMax))
+        resolve_by_rank<kPsThreads>(ckey_l, cid_l, ncand, need - above, wb, &kstar, &istar);
+      else
+        W::resolve(ArrayCand{ckey_l, cid_l, ncand}, 0u, 32, need - above, hist256, wb, &kstar,
+                   &istar);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) keys[e * kPsThreads + tid] = key[e];
+      __syncthreads();
+      W::resolve(LdsKeys{keys, static_cast<uint32_t>(kPsMaxSlots)}, 0u, 32, need, hist256, wb,
+                 &kstar, &istar);
+    }
   }
-  const int spt = kPer;
   uint32_t cnt = 0;
-  for (int i = s0; i < min(s0 + spt, nslots); ++i) {
-    const uint32_t key = keys[pf_lds(i)];
-    cnt += (need > 0 && key != 0u && selected(key, i, kstar, istar)) ? 1u : 0u;
-  }
+#pragma unroll
+  for (int e = 0; e < kPer; ++e)
+    cnt += (need > 0 && key[e] != 0u && selected(key[e], s0 + e, kstar, istar)) ? 1u : 0u;
   uint32_t total;
   uint32_t off = W::excl_scan(cnt, wb, &total);
   int32_t* orow = a.out + static_cast<size_t>(r) * a.top_k;
   float* krow = a.out_key ? a.out_key + static_cast<size_t>(r) * a.top_k : nullptr;
-  for (int i = s0; i < min(s0 + spt, nslots); ++i) {
-    const uint32_t key = keys[pf_lds(i)];
-    if (need > 0 && key != 0u && selected(key, i, kstar, istar)) {
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    if (need > 0 && key[e] != 0u && selected(key[e], s0 + e, kstar, istar)) {
       if (off < need) {
-        orow[off] = blk[(i - s0) >> 3] * kBlock + (i & 7);
-        if (krow) krow[off] = key_to_float(key);
+        orow[off] = blk[e >> 3] * kBlock + (e & 7);
+        if (krow) krow[off] = key_to_float(key[e]);
       }
       ++off;
     }
@@ -690,7 +721,7 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select_reg(
   uint32_t kstar = 0;
   int32_t istar = 0x7fffffff;
   if (need > 0 && need < static_cast<uint32_t>(n)) {
-    uint32_t mx = 0, mn_inv = 0;
+    uint32_t mx = 0, mn_inv = 0, unused = 0;
     const int full = n / kFsThreads;   // blocks with every item inside the row
 #pragma unroll
     for (int e = 0; e < kFrPer; ++e) {
@@ -700,8 +731,9 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select_reg(
       }
     }
     for (int i = tid; i < kFrBins; i += kFsThreads) hist[i] = 0;
-    const float vmax = key_to_float(W::reduce_max(mx, wb));
-    const float vmin = key_to_float(~W::reduce_max(mn_inv, wb));
+    W::reduce_sum_max_max(unused, mx, mn_inv, wb);
+    const float vmax = key_to_float(mx);
+    const float vmin = key_to_float(~mn_inv);
     // Bins linear in the score value between the row's min and max (scores
     // cluster in a few binades, so bins linear in the key bits would not
     // spread them).  Subtraction, scaling and truncation never reverse an
@@ -742,8 +774,11 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select_reg(
         }
       }
       __syncthreads();
-      W::resolve(ArrayCand{ckey_l, cid_l, ncand}, 0u, 32, need - above, hist256, wb, &kstar,
-                 &istar);
+      if (ncand <= static_cast<uint32_t>(kRankMax))
+        resolve_by_rank<kFsThreads>(ckey_l, cid_l, ncand, need - above, wb, &kstar, &istar);
+      else
+        W::resolve(ArrayCand{ckey_l, cid_l, ncand}, 0u, 32, need - above, hist256, wb, &kstar,
+                   &istar);
     } else {
       W::resolve(FlatCand{row, static_cast<uint32_t>(n)}, 0u, 32, need, hist256, wb, &kstar,
                  &istar);
@@ -850,9 +885,9 @@ hipError_t launch_pool_topk(int mode, const float* scores, const uint16_t* q_idx
   if (mode != 0) {
     dim3 grid((k_blocks + kPsBlocks - 1) / kPsBlocks, rows);
     if (mode == 1)
-      hipLaunchKernelGGL(k_pool_score<true>, grid, dim3(kPsThreads), 0, stream, a);
+      hipLaunchKernelGGL(k_pool_score<true>, grid, dim3(kPscThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL(k_pool_score<false>, grid, dim3(kPsThreads), 0, stream, a);
+      hipLaunchKernelGGL(k_pool_score<false>, grid, dim3(kPscThreads), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k_pool_final, dim3(rows), dim3(kPsThreads), 0, stream, a);
