@@ -25,7 +25,13 @@ sys.path.insert(0, ROOT)
 METRIC = "CSA2 decode query-tokens/s at 128K and 1M ctx; % of HBM GB/s roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
-SCAN_SOURCES = ["index_score.hip", "index_core.h", "csa2_device.h"]
+# Sources of each dominant kernel: a stored traffic measurement is used only
+# while their hash is unchanged.
+KERNEL_SOURCES = {
+    "index_scan": ["index_score.hip", "index_core.h", "csa2_device.h"],
+    "sparse_attn": ["attention.hip", "csa2_device.h"],
+    "index_gemm": ["index_gemm.hip", "index_core.h", "csa2_device.h"],
+}
 
 
 def log(*a):
@@ -48,9 +54,9 @@ def parse():
     return p.parse_args()
 
 
-def scan_source_hash():
+def source_hash(kernel):
     h = hashlib.sha256()
-    for f in SCAN_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "compressed_sparse_attention_index_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -314,7 +320,7 @@ def main():
     roof["kernel"] = dominant
     roof["per_launch"] = per_launch
     roof["launch_us"] = round(dom_ms * 1e3, 2)
-    roof["traffic"] = traffic_from_profile(dominant, scan_source_hash())
+    roof["traffic"] = traffic_from_profile(dominant, source_hash(dominant))
 
     cpu = None
     if not args.no_cpu_baseline:
