@@ -35,8 +35,9 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
+constexpr int kWgPerCu = 2;   // two workgroups (two waves per SIMD) share a compute unit
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerWave = 8;
+constexpr int kRowsPerWave = 4;
 constexpr int kRowsPerWg = kRowsPerWave * kWaves;
 constexpr int kPairs = (kRowsPerWave + 1) / 2;   // store instructions per tile and output
 constexpr int kStages = 4;
@@ -120,7 +121,7 @@ struct Acc {
 };
 
 template <bool FP8, int OUT>
-__global__ __launch_bounds__(kThreads, 1) void k_index_gemm(
+__global__ __launch_bounds__(kThreads, kWgPerCu) void k_index_gemm(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ vis_len, int n_q, int N_cap,
     int tiles_per_wg, float* __restrict__ scores, float* __restrict__ block_max) {
@@ -160,12 +161,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_index_gemm(
   // l of load u fills chunk position p = 64 (w LPW + u) + l (row p /
   // kChunks), which holds chunk (p % kChunks) ^ (row & 7) of that row.
   const uint8_t* kbase = k_idx + static_cast<size_t>(b) * N_cap * KT::kRowBytes;
-  int goff[KT::kLoadsPerWave], grow[KT::kLoadsPerWave];
+  // Rows of load u: grow0 + u * (64 / kChunks).
+  int goff[KT::kLoadsPerWave];
+  const int grow0 = (64 * KT::kLoadsPerWave * wave + lane) / KT::kChunks;
 #pragma unroll
   for (int u = 0; u < KT::kLoadsPerWave; ++u) {
     const int p = 64 * (KT::kLoadsPerWave * wave + u) + lane;
     const int row = p / KT::kChunks;
-    grow[u] = row;
     goff[u] = row * KT::kRowBytes + (((p % KT::kChunks) ^ (row & 7)) << 4);
   }
   auto issue = [&](int t) {
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_index_gemm(
     const uint32_t dst = lds_offset(&ring[static_cast<unsigned>(t - t_begin) % kStages][0]);
 #pragma unroll
     for (int u = 0; u < KT::kLoadsPerWave; ++u)
-      dma16(base + (grow[u] < rows_left ? goff[u] : 0),
+      dma16(base + (grow0 + u * (64 / KT::kChunks) < rows_left ? goff[u] : 0),
             dst + 1024 * (KT::kLoadsPerWave * wave + u));
   };
 #pragma unroll
@@ -219,75 +221,72 @@ __global__ __launch_bounds__(kThreads, 1) void k_index_gemm(
   const size_t nb_cap = (N_cap + 7) >> 3;
   constexpr int per_row = ((OUT & kOutScores) ? 1 : 0) + ((OUT & kOutBlockMax) ? 1 : 0);
 
-  // B operands of half h of tile t: lane (c, g) of key block kb and step ks
-  // holds key 64 t + 32 h + 16 kb + c, dims dim_base(ks, g) .. + 7.
-  auto read_kop = [&](int t, int h, bf16x8 (&kop)[2][4]) {
-    const uint8_t* tile = ring[static_cast<unsigned>(t - t_begin) % kStages] + 32 * h * KT::kRowBytes;
+  // Keys are worked on in quarters of 16 (quarter qq: keys 16 qq .. + 15,
+  // rows 16 (qq % 4) .. + 15 of tile qq / 4).  B operands of a quarter: lane
+  // (c, g) of step ks holds key 16 qq + c, dims dim_base(ks, g) .. + 7.  They
+  // are read from LDS as raw bytes one quarter ahead and converted at use.
+  constexpr int kRaw = FP8 ? 2 : 4;
+  struct Raw {
+    u32x4 v[kRaw];
+  };
+  auto read_raw = [&](int qq) {
+    const uint8_t* tile = ring[static_cast<unsigned>((qq >> 2) - t_begin) % kStages];
+    const int row = 16 * (qq & 3) + c;
+    Raw r;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int u = 0; u < kRaw; ++u)
+      r.v[u] = *reinterpret_cast<const u32x4*>(tile + KT::pos(row, 4 * u + g));
+    return r;
+  };
+  auto operands = [&](const Raw& r, bf16x8 (&kq)[4]) {
+#pragma unroll
+    for (int u = 0; u < kRaw; ++u) {
       if constexpr (FP8) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const u32x4 w =
-              *reinterpret_cast<const u32x4*>(tile + KT::pos(16 * kb + c, 4 * u + g));
-          kop[kb][2 * u] = fp8x8_to_bf16x8(w.x, w.y);
-          kop[kb][2 * u + 1] = fp8x8_to_bf16x8(w.z, w.w);
-        }
+        kq[2 * u] = fp8x8_to_bf16x8(r.v[u].x, r.v[u].y);
+        kq[2 * u + 1] = fp8x8_to_bf16x8(r.v[u].z, r.v[u].w);
       } else {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          kop[kb][ks] = *reinterpret_cast<const bf16x8*>(tile + KT::pos(16 * kb + c, 4 * ks + g));
+        kq[u] = __builtin_bit_cast(bf16x8, r.v[u]);
       }
     }
   };
 
-  // One row's 16 MFMAs: four independent accumulator chains.
-  auto mma_row = [&](int i, const bf16x8 (&kop)[2][4]) {
-    Acc a;
+  // Per row, the lane partial sum over its 8 heads (16 hb + 4 g + r) for its
+  // key of the quarter: 8 MFMAs (two head blocks x four steps).
+  auto quarter = [&](const Raw& raw, float (&part)[kRowsPerWave]) {
+    bf16x8 kq[4];
+    operands(raw, kq);
+    static_for<kRowsPerWave>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      f32x4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) a.d[hb][kb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          a.d[hb][kb] = mfma16(qa[i][hb][ks], kop[kb][ks], a.d[hb][kb]);
-    return a;
-  };
-
-  // Lane partial sums over the lane's 8 heads, for keys c (key block 0) and
-  // 16 + c (key block 1), summed over lane groups g and g ^ 2: lanes 0..31
-  // then hold key c, lanes 32..63 key 16 + c.
-  auto row_part = [&](int i, const Acc& a) {
-    float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p0 = __builtin_fmaf(w8[i][4 * hb + r], relu(a.d[hb][0][r]), p0);
-        p1 = __builtin_fmaf(w8[i][4 * hb + r], relu(a.d[hb][1][r]), p1);
+      for (int ks = 0; ks < 4; ++ks) {
+        d0 = mfma16(qa[i][0][ks], kq[ks], d0);
+        d1 = mfma16(qa[i][1][ks], kq[ks], d1);
       }
-    return swap32_sum(p0, p1);
+      float p = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p = __builtin_fmaf(w8[i][r], relu(d0[r]), p);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p = __builtin_fmaf(w8[i][4 + r], relu(d1[r]), p);
+      part[i] = p;
+    });
   };
 
-  // Scores of half-tile th (keys 32 th .. + 31).  After the second swap,
-  // lane l holds the score of row i - 1 + ((l / 16) & 1) for a pair (rows
-  // i - 1, i), or of row i alone, at key 32 th + (l & 15) + 16 (l / 32).
-  // FULL: every row sees the whole half, so no lane is masked.
-  auto compute = [&](int th, const bf16x8 (&kop)[2][4], auto full_tag) {
+  // Scores of half-tile th (keys 32 th .. + 31) from the partial sums of its
+  // two quarters.  The first swap adds lane groups g and g ^ 2 and puts key
+  // 32 th + c in lanes 0..31, key 32 th + 16 + c in lanes 32..63; the second
+  // adds groups g and g ^ 1 and leaves in lane l the score of row
+  // i - 1 + ((l / 16) & 1) of a pair (rows i - 1, i), or of row i alone, at
+  // key 32 th + (l & 15) + 16 (l / 32).  FULL: every row sees the whole
+  // half, so no lane is masked.
+  auto finish = [&](int th, const float (&p0)[kRowsPerWave], const float (&p1)[kRowsPerWave],
+                    auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int key = 32 * th + c + 16 * (lane >> 5);
-    Acc acc = mma_row(0, kop);
     float first = 0.0f;
     static_for<kRowsPerWave>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      Acc next;
-      if constexpr (i + 1 < kRowsPerWave) next = mma_row(i + 1, kop);
-      const float a = row_part(i, acc);
-      if constexpr (i + 1 < kRowsPerWave) acc = next;
+      const float a = swap32_sum(p0[i], p1[i]);
       constexpr bool single = (i == kRowsPerWave - 1) && (i % 2 == 0);
       if constexpr (i % 2 == 0 && !single) {
         first = a;
@@ -312,17 +311,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_index_gemm(
       }
     });
   };
+  auto finish_half = [&](int th, const float (&p0)[kRowsPerWave],
+                         const float (&p1)[kRowsPerWave]) {
+    if (32 * th + 32 <= vis_min)
+      finish(th, p0, p1, std::true_type{});
+    else
+      finish(th, p0, p1, std::false_type{});
+  };
 
   // Vector-memory instructions complete in issue order, and the score stores
-  // count as well.  Iteration t works on half 0 of tile t, waits for tile
-  // t + 1, issues the loads of tile t + 4 and works on half 1; per half and
-  // output it makes one store per pair of rows with a visible key there
-  // (lane 0 or 16 then stores, so none is skipped).  When tile t + 1 is
-  // waited for, the instructions issued after its loads are the stores of
-  // halves 2t - 5 .. 2t and the loads of tiles t + 2 and t + 3 issued in
-  // iterations t - 2 and t - 1 (the loads issued before the loop have all
-  // completed there).  Counting fewer than were issued would only wait
-  // longer.
+  // count as well.  Iteration t works on quarters 4t .. 4t + 2, waits for
+  // tile t + 1, issues the loads of tile t + 4 and works on quarter 4t + 3;
+  // after each odd quarter it makes per output one store per pair of rows
+  // with a visible key in that half (lane 0 or 16 then stores, so none is
+  // skipped).  When tile t + 1 is waited for, the instructions issued after
+  // its loads are the stores of halves 2t - 5 .. 2t and the loads of tiles
+  // t + 2 and t + 3 issued in iterations t - 2 and t - 1 (the loads issued
+  // before the loop have all completed there).  Counting fewer than were
+  // issued would only wait longer.
   auto stores_of = [&](int th) {   // th: half-tile index
     if (th < 2 * t_begin) return 0;
     if (32 * th + 32 <= vis_min) return kPairs * per_row;
@@ -340,19 +346,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_index_gemm(
   constexpr int kSteady = 6 * kPairs * per_row + 2 * KT::kLoadsPerWave;
   static_assert(kSteady <= 63, "vmcnt range");
 
-  auto half = [&](int th, const bf16x8 (&kop)[2][4]) {
-    if (32 * th + 32 <= vis_min)
-      compute(th, kop, std::true_type{});
-    else
-      compute(th, kop, std::false_type{});
-  };
-
   lds_barrier();   // the first tiles (waited for above) are visible to all waves
-  bf16x8 kop_a[2][4], kop_b[2][4];
-  read_kop(t_begin, 0, kop_a);
+  float p0[kRowsPerWave], p1[kRowsPerWave];
+  Raw ra = read_raw(4 * t_begin), rb;
   for (int t = t_begin; t < t_end; ++t) {
-    half(2 * t, kop_a);
-    read_kop(t, 1, kop_b);
+    const int q = 4 * t;
+    rb = read_raw(q + 1);
+    quarter(ra, p0);
+    ra = read_raw(q + 2);
+    quarter(rb, p1);
+    finish_half(2 * t, p0, p1);
+    rb = read_raw(q + 3);
+    quarter(ra, p0);
     if (t + 1 < t_end) {
       int after = loads_in(t - 2, t + 2) + loads_in(t - 1, t + 3);
 #pragma unroll
@@ -363,9 +368,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_index_gemm(
         wait_le<63>(min(after, 63));
       lds_barrier();   // tile t + 1 has landed; every wave has read tile t
       if (t + kStages < t_end) issue(t + kStages);
-      read_kop(t + 1, 0, kop_a);
+      ra = read_raw(q + 4);
     }
-    half(2 * t + 1, kop_b);
+    quarter(rb, p1);
+    finish_half(2 * t + 1, p0, p1);
   }
 }
 
