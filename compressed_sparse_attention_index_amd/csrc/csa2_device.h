@@ -102,6 +102,22 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Waits until at most n (0 .. N) vector-memory instructions of this wave are
+// outstanding, for a wave-uniform n known only at run time: the immediate is
+// chosen by a chain of compares (callers test their common count first).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le(int n) {
+  if constexpr (N > 0) {
+    if (n >= N) {
+      wait_vmem<N>();
+      return;
+    }
+    wait_vmem_le<N - 1>(n);
+  } else {
+    wait_vmem<0>();
+  }
+}
+
 // Byte offset of an LDS object within the workgroup's LDS.
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return static_cast<uint32_t>(

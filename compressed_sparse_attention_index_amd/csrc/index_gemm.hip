@@ -88,21 +88,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Waits until at most n (0 .. 63) vector-memory instructions of this wave
-// are outstanding; n is wave-uniform, the immediate is chosen by a switch.
-template <int N>
-__device__ __forceinline__ void wait_le(int n) {
-  if constexpr (N > 0) {
-    if (n >= N) {
-      wait_vmem<N>();
-      return;
-    }
-    wait_le<N - 1>(n);
-  } else {
-    wait_vmem<0>();
-  }
-}
-
 // Sum of the values of lanes l and l ^ 32: of a in lanes 0..31, of b in
 // lanes 32..63.
 __device__ __forceinline__ float swap32_sum(float a, float b) {
@@ -365,7 +350,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_index_gemm(
       if (after == kSteady)
         wait_vmem<kSteady>();
       else
-        wait_le<63>(min(after, 63));
+        wait_vmem_le<63>(min(after, 63));
       lds_barrier();   // tile t + 1 has landed; every wave has read tile t
       if (t + kStages < t_end) issue(t + kStages);
       ra = read_raw(q + 4);

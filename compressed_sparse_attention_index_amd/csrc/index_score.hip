@@ -23,11 +23,19 @@ __device__ __forceinline__ const uint8_t* key_row(const uint8_t* kb, int pos, in
   return kb + static_cast<size_t>(p) * (FP8 ? 128 : 256);
 }
 
+constexpr int kOutScores = 1;
+constexpr int kOutBlockMax = 2;
+
+// Stores of one position's score and of its block's maximum.  Lane 0 always
+// holds a visible position of a tile that is worked on, so each requested
+// output is written by exactly one store instruction per tile.
+template <int OUT>
 __device__ __forceinline__ void emit(float s, int pos, int vis, int half, int col, float* scores,
                                      float* block_max) {
   const bool valid = pos < vis;
-  if (scores != nullptr && half == 0 && valid) scores[pos] = s;
-  if (block_max != nullptr) {
+  if constexpr (OUT & kOutScores)
+    if (half == 0 && valid) scores[pos] = s;
+  if constexpr (OUT & kOutBlockMax) {
     float m = valid ? s : -__builtin_inff();
     m = fmaxf(m, wave_xor(m, 1));
     m = fmaxf(m, wave_xor(m, 2));
@@ -45,8 +53,12 @@ __device__ __forceinline__ void emit(float s, int pos, int vis, int half, int co
 // is permuted so that the slot holds a swizzled layout: 16-byte chunk c of row
 // r sits at chunk position c ^ f(r), which makes the MFMA-layout reads below
 // (16 B per lane, one row per lane) free of LDS bank conflicts.  DEPTH tiles
-// are in flight per wave; loads complete in issue order, so waiting until at
-// most DEPTH tiles' loads are outstanding guarantees the oldest has landed.
+// are in flight per wave while it works on one.  One tile ahead with small
+// LDS slots (more resident workgroups) streams faster than two or more ahead
+// with fewer workgroups.  Vector-memory instructions complete in issue order
+// and the output stores count as well, so a tile has landed once no more are
+// outstanding than the loads of the tiles issued after it and the stores
+// made since.
 template <bool FP8>
 struct ScanTile {
   static constexpr int kRowBytes = FP8 ? 128 : 256;
@@ -59,28 +71,15 @@ struct ScanTile {
   }
 };
 
-template <int N>
-__device__ __forceinline__ void wait_tiles(int pending, int per_tile) {
-  // pending in [0, N]; per_tile loads per tile.  The immediate must be a
-  // constant, so branch on the (wave-uniform) count.
-  if (per_tile == 4) {
-    if (pending >= 2 && N >= 2) wait_vmem<8>();
-    else if (pending == 1) wait_vmem<4>();
-    else wait_vmem<0>();
-  } else {
-    if (pending >= 2 && N >= 2) wait_vmem<16>();
-    else if (pending == 1) wait_vmem<8>();
-    else wait_vmem<0>();
-  }
-}
-
-template <bool FP8, int DEPTH>
+template <bool FP8, int DEPTH, int OUT>
 __global__ __launch_bounds__(kThreads) void k_index_scan(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ vis_len, int n_q, int N_cap,
     int tiles_per_wg, float* __restrict__ scores, float* __restrict__ block_max) {
   using TT = ScanTile<FP8>;
-  static_assert(DEPTH <= 2, "wait_tiles handles up to two tiles in flight");
+  constexpr int kStores = ((OUT & kOutScores) ? 1 : 0) + ((OUT & kOutBlockMax) ? 1 : 0);
+  constexpr int kSteady = DEPTH * (TT::kLoads + kStores);
+  static_assert(kSteady <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][DEPTH + 1][TT::kBytes];
   const int r = blockIdx.y;
   const int b = r / n_q;
@@ -88,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void k_index_scan(
   const int ntiles = (vis + 31) >> 5;
   const int t_begin = blockIdx.x * tiles_per_wg;
   const int t_end = min(t_begin + tiles_per_wg, ntiles);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int half = lane >> 5, col = lane & 31;
   int t = t_begin + wave;
   if (t >= t_end) return;
@@ -129,22 +128,32 @@ __global__ __launch_bounds__(kThreads) void k_index_scan(
   for (int d = 0; d < DEPTH; ++d)
     if (t + d * kWaves < t_end) issue(d, t + d * kWaves);
   int slot = 0;
-  for (; t < t_end; t += kWaves) {
+  for (int k = 0; t < t_end; t += kWaves, ++k) {
     const int tp = t + DEPTH * kWaves;
     if (tp < t_end) issue((slot + DEPTH) % (DEPTH + 1), tp);
-    const int ahead = (t_end - 1 - t) / kWaves;   // tiles after t for this wave
-    wait_tiles<DEPTH>(ahead < DEPTH ? ahead : DEPTH, TT::kLoads);
+    // Issued after tile t's loads: the loads of this wave's next (up to
+    // DEPTH) tiles and the stores of its previous min(k, DEPTH) tiles.
+    const int ahead = min((t_end - 1 - t) / kWaves, DEPTH);
+    const int after = TT::kLoads * ahead + kStores * min(k, DEPTH);
+    if (after == kSteady)
+      wait_vmem<kSteady>();
+    else
+      wait_vmem_le<kSteady>(after);
     const uint8_t* st = stage[wave][slot];
     KeyTile<FP8> kt;
 #pragma unroll
     for (int j = 0; j < KeyTile<FP8>::kWords; ++j)
       kt.v[j] = *reinterpret_cast<const u32x4*>(st + TT::pos(col, (TT::kChunks / 2) * half + j));
     const float s = head_sum(key_tile_dot<FP8>(qa, kt), wr);
-    emit(s, 32 * t + col, vis, half, col, srow, brow);
+    emit<OUT>(s, 32 * t + col, vis, half, col, srow, brow);
     slot = slot == DEPTH ? 0 : slot + 1;
   }
 }
 
+// Tiles per workgroup for about `target_wgs` workgroups over all rows (at
+// least min_tiles, at most max_tiles, a multiple of the waves per workgroup).
+// Many short workgroups balance better than one resident wave of long ones:
+// units that finish early take more work.
 int pick_tiles_per_wg(long long total_tiles, int min_tiles, int target_wgs, int max_tiles) {
   long long t = (total_tiles + target_wgs - 1) / target_wgs;
   if (t < min_tiles) t = min_tiles;
@@ -162,14 +171,24 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w_idx, const v
   const uint8_t* kb = static_cast<const uint8_t*>(k_idx);
   if (n_q < 16) {
     const int rows = B * n_q;
+    const int out = (scores != nullptr ? kOutScores : 0) | (block_max != nullptr ? kOutBlockMax : 0);
     const int tpw = pick_tiles_per_wg(static_cast<long long>(tiles) * rows, 8, 4096, 64);
-    dim3 grid((tiles + tpw - 1) / tpw, rows);
-    if (fp8)
-      hipLaunchKernelGGL((k_index_scan<true, 2>), grid, dim3(kThreads), 0, stream, q_idx, w_idx,
-                         kb, vis_len, n_q, N_cap, tpw, scores, block_max);
-    else
-      hipLaunchKernelGGL((k_index_scan<false, 1>), grid, dim3(kThreads), 0, stream, q_idx, w_idx,
-                         kb, vis_len, n_q, N_cap, tpw, scores, block_max);
+#define CSA2_SCAN_LAUNCH(F, D, O)                                                              \
+  do {                                                                                         \
+    dim3 grid((tiles + tpw - 1) / tpw, rows);                                                  \
+    hipLaunchKernelGGL((k_index_scan<F, D, O>), grid, dim3(kThreads), 0, stream, q_idx, w_idx, \
+                       kb, vis_len, n_q, N_cap, tpw, scores, block_max);                       \
+  } while (0)
+    switch ((fp8 ? 4 : 0) | out) {
+      case 1: CSA2_SCAN_LAUNCH(false, 1, 1); break;
+      case 2: CSA2_SCAN_LAUNCH(false, 1, 2); break;
+      case 3: CSA2_SCAN_LAUNCH(false, 1, 3); break;
+      case 5: CSA2_SCAN_LAUNCH(true, 1, 1); break;
+      case 6: CSA2_SCAN_LAUNCH(true, 1, 2); break;
+      case 7: CSA2_SCAN_LAUNCH(true, 1, 3); break;
+      default: return hipErrorInvalidValue;   // no output requested
+    }
+#undef CSA2_SCAN_LAUNCH
   } else {
     return launch_index_gemm(q_idx, w_idx, kb, fp8, vis_len, B, n_q, N_cap, scores, block_max,
                              stream);
