@@ -152,6 +152,40 @@ struct Wg {
     return bin;
   }
 
+  // As find_rank_bin, with each thread's PER bins already in registers: v[i]
+  // holds bin nbins - 1 - (t PER + i) (descending) or t PER + i.  Also
+  // returns the found bin's count, so no bin is read from memory again.
+  template <int PER>
+  __device__ static int find_rank_bin_regs(const uint32_t (&v)[PER], int nbins, uint32_t rank,
+                                           bool descending, uint32_t* wb, uint32_t* before,
+                                           uint32_t* count) {
+    const int t = threadIdx.x;
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) s += v[i];
+    uint32_t tot;
+    uint32_t p = excl_scan(s, wb, &tot);
+    if (p < rank && rank <= p + s) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int idx = t * PER + i;
+        if (rank <= p + v[i]) {
+          wb[2 * kWaves + 1] = static_cast<uint32_t>(descending ? nbins - 1 - idx : idx);
+          wb[2 * kWaves + 2] = p;
+          wb[2 * kWaves + 3] = v[i];
+          break;
+        }
+        p += v[i];
+      }
+    }
+    __syncthreads();
+    const int bin = static_cast<int>(wb[2 * kWaves + 1]);
+    *before = wb[2 * kWaves + 2];
+    *count = wb[2 * kWaves + 3];
+    __syncthreads();
+    return bin;
+  }
+
   // Resolves the selection threshold among the items whose key bits above
   // `shift` equal `prefix` (prefix has zeros below `shift`): `rem` (>= 1) of
   // them are taken.  `cand` exposes n, key(i) and id(i) for i < n; other

@@ -113,8 +113,13 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_filter(const float* __restric
   const int i0 = blockIdx.x * kBtItems;
   if (n <= k || i0 >= n) return;
   const uint32_t* gh = ws.hist + static_cast<size_t>(r) * kHistBins;
-  uint32_t above;
-  const int b1 = W::find_rank_bin(gh, kHistBins, static_cast<uint32_t>(k), true, wb, &above);
+  constexpr int kPerBin = kHistBins / kBtThreads;
+  uint32_t h1[kPerBin];
+#pragma unroll
+  for (int i = 0; i < kPerBin; ++i) h1[i] = gh[kHistBins - 1 - (tid * kPerBin + i)];
+  uint32_t above, n1;
+  const int b1 =
+      W::find_rank_bin_regs(h1, kHistBins, static_cast<uint32_t>(k), true, wb, &above, &n1);
   for (int i = tid; i < kHistBins; i += kBtThreads) h2[i] = 0;
   if (tid < 2) cnt[tid] = 0;
   __syncthreads();
@@ -176,13 +181,22 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const int32_t* __restri
   const uint32_t need = static_cast<uint32_t>(k);
   const uint32_t* gh = ws.hist + static_cast<size_t>(r) * kHistBins;
   const uint32_t* gh2 = ws.hist2 + static_cast<size_t>(r) * kHistBins;
-  uint32_t above;
-  const int b1 = W::find_rank_bin(gh, kHistBins, need, true, wb, &above);
+  // Both histograms are loaded into registers in one batch (one memory
+  // latency) and searched there.
+  constexpr int kPerBin = kHistBins / kBtThreads;
+  static_assert(kHistBins % kBtThreads == 0, "whole bins per thread");
+  uint32_t h1[kPerBin], h2[kPerBin];
+#pragma unroll
+  for (int i = 0; i < kPerBin; ++i) {
+    h1[i] = gh[kHistBins - 1 - (tid * kPerBin + i)];
+    h2[i] = gh2[kHistBins - 1 - (tid * kPerBin + i)];
+  }
+  uint32_t above, n1;
+  const int b1 = W::find_rank_bin_regs(h1, kHistBins, need, true, wb, &above, &n1);
   const uint32_t rem1 = need - above;
-  uint32_t above2;
-  const int b2 = W::find_rank_bin(gh2, kHistBins, rem1, true, wb, &above2);
+  uint32_t above2, n2;
+  const int b2 = W::find_rank_bin_regs(h2, kHistBins, rem1, true, wb, &above2, &n2);
   const uint32_t rem2 = rem1 - above2;
-  const uint32_t n2 = gh2[b2];
 
   // Prefix offsets of the filter workgroups' segments.
   const int nwg = (n + kBtItems - 1) / kBtItems;
