@@ -37,7 +37,10 @@
 // a lane differ only by immediate offsets.
 // Rows split over several workgroups write (m, l, O) partials that a second
 // kernel merges in split order; when there are enough rows every workgroup
-// covers whole rows and no partials are written.
+// covers whole rows and no partials are written.  The partial O (relative to
+// its split's own max) is rounded to bf16, like the output itself: half the
+// bytes of fp32 partials for a rounding error of the same size as the
+// output's; m and l stay fp32.
 #include "csa2_launch.h"
 #include "csa2_device.h"
 
@@ -73,7 +76,7 @@ struct AttnArgs {
   const int32_t* q_pos;
   uint16_t* out;
   float* lse;
-  float* part_o;     // [rows, nsplit, 64, 512] or null
+  uint16_t* part_o;  // [rows, nsplit, 64, 512] bf16, or null
   float* part_ml;    // [rows, nsplit, 64, 2] or null
   int N_cap, top_k, S_cap, n_q, window, replay_start;
   int rows, n_chunks, cps, nsplit;
@@ -356,8 +359,8 @@ __device__ __forceinline__ void finish(const AttnArgs& a, const RowCtx& x, const
         *reinterpret_cast<u32x2*>(a.out + (static_cast<size_t>(x.r) * kHeads + head) * kDim + d) =
             u32x2{pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
       } else {
-        *reinterpret_cast<f32x4_t*>(a.part_o + (ps * kHeads + head) * kDim + d) =
-            f32x4_t{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<u32x2*>(a.part_o + (ps * kHeads + head) * kDim + d) =
+            u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
     }
   }
@@ -488,14 +491,11 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   constexpr int kGroup = 4;
   for (int s0 = 0; s0 < a.nsplit; s0 += kGroup) {
-    f32x4_t u[kGroup], v[kGroup];
+    u32x4 u[kGroup];
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
       const int sp = min(s0 + g, a.nsplit - 1);
-      const f32x4_t* po = reinterpret_cast<const f32x4_t*>(
-          a.part_o + ((ps0 + sp) * kHeads + head) * kDim + 8 * t);
-      u[g] = po[0];
-      v[g] = po[1];
+      u[g] = *reinterpret_cast<const u32x4*>(a.part_o + ((ps0 + sp) * kHeads + head) * kDim + 8 * t);
     }
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
@@ -503,8 +503,12 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
       const float lsg = __shfl(lsv, s0 + g, 64);
       if (s0 + g < a.nsplit) {
         L += wgt * lsg;
-        acc[0] += wgt * u[g][0]; acc[1] += wgt * u[g][1]; acc[2] += wgt * u[g][2]; acc[3] += wgt * u[g][3];
-        acc[4] += wgt * v[g][0]; acc[5] += wgt * v[g][1]; acc[6] += wgt * v[g][2]; acc[7] += wgt * v[g][3];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w = word_of(u[g], j);
+          acc[2 * j] += wgt * __uint_as_float(w << 16);
+          acc[2 * j + 1] += wgt * __uint_as_float(w & 0xffff0000u);
+        }
       }
     }
   }
@@ -537,7 +541,7 @@ size_t attn_workspace_bytes(int rows, int top_k) {
   int n_chunks, cps, nsplit;
   plan(rows, top_k, &n_chunks, &cps, &nsplit);
   if (nsplit == 1) return 0;
-  return static_cast<size_t>(rows) * nsplit * kHeads * (kDim + 2) * sizeof(float);
+  return static_cast<size_t>(rows) * nsplit * kHeads * (kDim * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
 hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
@@ -557,8 +561,8 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* kv_fp4, const ui
   a.part_o = nullptr;
   a.part_ml = nullptr;
   if (a.nsplit > 1) {
-    a.part_o = static_cast<float*>(ws);
-    a.part_ml = a.part_o + static_cast<size_t>(rows) * a.nsplit * kHeads * kDim;
+    a.part_o = static_cast<uint16_t*>(ws);
+    a.part_ml = reinterpret_cast<float*>(a.part_o + static_cast<size_t>(rows) * a.nsplit * kHeads * kDim);
   }
   const long long pairs = static_cast<long long>(rows) * a.nsplit;
   const long long wgs = (pairs + 7) / 8 * 16;
