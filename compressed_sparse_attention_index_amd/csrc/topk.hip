@@ -386,14 +386,18 @@ constexpr int kPfBins = 2048;
 constexpr int kPfCap = 2048;
 constexpr int kRankMax = 256;   // threshold bins up to this size are resolved by counting ranks
 
-// One workgroup per row.  Thread t holds the keys of slots [16 t, 16 t + 16)
-// (two pool blocks) in registers.  The threshold is found as in the flat
-// selection: 2048 bins linear in the score value between the row's min and
-// max, exact resolution of the threshold bin's items only (from LDS copies),
-// or of every slot when that bin is too large.
+// One workgroup per row.  Thread t holds the scores of slots [16 t, 16 t +
+// 16) (two pool blocks) in registers, with a validity mask.  The threshold is
+// found as in the flat selection: 2048 bins linear in the score value between
+// the row's min and max, exact resolution of the threshold bin's items only
+// (from LDS copies), or of every slot when that bin is too large.  The
+// selection is VALU-bound on one compute unit, so each slot costs as few
+// instructions as possible: the bins are computed once from the float scores
+// and kept in registers, invalid slots go to a spare bin (no branch around
+// the LDS atomic), and exact keys are formed only for the threshold bin.
 __global__ __launch_bounds__(kPsThreads) void k_pool_final(PoolArgs a) {
   __shared__ uint32_t keys[kPsMaxSlots];
-  __shared__ uint32_t hist[kPfBins];
+  __shared__ uint32_t hist[kPfBins + 1];   // + a spare bin for invalid slots
   __shared__ uint32_t ckey_l[kPfCap];
   __shared__ int32_t cid_l[kPfCap];
   __shared__ uint32_t hist256[256];
@@ -412,9 +416,14 @@ __global__ __launch_bounds__(kPsThreads) void k_pool_final(PoolArgs a) {
   static_assert(kPer == 2 * kBlock, "two pool blocks per thread");
   const int s0 = tid * kPer;
   const bool mine = s0 < nslots;
+  // Clamped loads (no branch per load), then a select.
   int blk[2];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) blk[u] = (mine && (s0 >> 3) + u < a.kb) ? prow[(s0 >> 3) + u] : -1;
+  for (int u = 0; u < 2; ++u) {
+    const int bi = min((s0 >> 3) + u, a.kb - 1);
+    const int v = prow[bi];
+    blk[u] = (mine && (s0 >> 3) + u < a.kb) ? v : -1;
+  }
   // All of a thread's score loads are issued before any is used.
   float sv[kPer];
   if (srow) {
@@ -434,58 +443,65 @@ __global__ __launch_bounds__(kPsThreads) void k_pool_final(PoolArgs a) {
 #pragma unroll
     for (int e = 0; e < kPer; ++e) sv[e] = ps[min(s0 + e, nslots - 1)];
   }
-  uint32_t key[kPer];
-  uint32_t nv = 0, mx = 0, mn_inv = 0;
+  uint32_t vm = 0;   // bit e: slot s0 + e holds a visible position
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int bk = blk[e >> 3];
-    const bool valid = mine && bk >= 0 && bk < nb_cap && bk * kBlock + (e & 7) < vis;
-    key[e] = valid ? float_to_key(sv[e]) : 0u;
-    nv += valid ? 1u : 0u;
-    if (valid) {
-      mx = max(mx, key[e]);
-      mn_inv = max(mn_inv, ~key[e]);
+  for (int u = 0; u < 2; ++u) {
+    const int bk = blk[u];
+    if (bk >= 0 && bk < nb_cap) {
+      const int m = min(max(vis - bk * kBlock, 0), kBlock);   // visible positions of the block
+      vm |= ((1u << m) - 1u) << (kBlock * u);
     }
   }
-  for (int i = tid; i < kPfBins; i += kPsThreads) hist[i] = 0;
+  float vmax = -__builtin_inff(), vmin = __builtin_inff();
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const bool v = (vm >> e) & 1u;
+    vmax = fmaxf(vmax, v ? sv[e] : -__builtin_inff());
+    vmin = fminf(vmin, v ? sv[e] : __builtin_inff());
+  }
+  uint32_t nv = static_cast<uint32_t>(__popc(vm));
+  uint32_t mx = vm ? float_to_key(vmax) : 0u, mn_inv = vm ? ~float_to_key(vmin) : 0u;
+  for (int i = tid; i <= kPfBins; i += kPsThreads) hist[i] = 0;
   W::reduce_sum_max_max(nv, mx, mn_inv, wb);   // includes the barrier after the clear
   const uint32_t n_valid = nv;
   const uint32_t need = min(static_cast<uint32_t>(a.top_k), n_valid);
-  uint32_t kstar = 1u;              // need == n_valid: every valid (nonzero) key
+  // Selection among the valid slots, by mode: 0 every one (need == n_valid);
+  // 1 bin > b1, or bin == b1 and (key, id) selected by K*, I*; 2 (threshold
+  // bin too large) (key, id) selected by K*, I*.  Bin order is key order, so
+  // every key of a higher bin exceeds every key of bin b1.
+  int mode = 0, b1 = 0;
+  uint32_t kstar = 0;
   int32_t istar = 0x7fffffff;
+  int bin[kPer];
   if (need > 0 && need < n_valid) {
-    const float vmax = key_to_float(mx);
-    const float vmin = key_to_float(~mn_inv);
+    mode = 1;
+    const float vhi = key_to_float(mx);
+    const float vlo = key_to_float(~mn_inv);
     // Bins linear in the value; subtraction, scaling and truncation never
     // reverse an order, so bin order is key order.
-    const float range = vmax - vmin;
+    const float range = vhi - vlo;
     const float scale = (range > 0.0f && range < __builtin_inff())
                             ? static_cast<float>(kPfBins) * 0.99999f / range : 0.0f;
-    auto bin_of = [&](uint32_t kk) {
-      const float x = (key_to_float(kk) - vmin) * scale;
-      return min(kPfBins - 1, max(0, static_cast<int>(x)));
-    };
 #pragma unroll
-    for (int e = 0; e < kPer; ++e)
-      if (key[e] != 0u) atomicAdd(&hist[bin_of(key[e])], 1u);
+    for (int e = 0; e < kPer; ++e) {
+      const int bv = min(kPfBins - 1, max(0, static_cast<int>((sv[e] - vlo) * scale)));
+      bin[e] = ((vm >> e) & 1u) ? bv : kPfBins;
+      atomicAdd(&hist[bin[e]], 1u);
+    }
     __syncthreads();
     uint32_t above;
-    const int b1 = W::find_rank_bin(hist, kPfBins, need, true, wb, &above);
+    b1 = W::find_rank_bin(hist, kPfBins, need, true, wb, &above);
     const uint32_t ncand = hist[b1];
     if (ncand <= static_cast<uint32_t>(kPfCap)) {
       if (tid == 0) ccount = 0;
       __syncthreads();
-      // Items of bin b1 have keys >= klo (one bin width of margin).
-      const uint32_t klo = scale > 0.0f
-                               ? float_to_key(vmin + (static_cast<float>(b1) - 1.0f) / scale)
-                               : 1u;
 #pragma unroll
       for (int e = 0; e < kPer; ++e) {
-        if (__ballot(key[e] >= klo && key[e] != 0u) == 0) continue;   // wave-uniform
-        const bool c = key[e] != 0u && bin_of(key[e]) == b1;
+        const bool c = bin[e] == b1;
+        if (__ballot(c) == 0) continue;   // wave-uniform
         const uint32_t slot = wave_append(c, &ccount);
         if (c) {
-          ckey_l[slot] = key[e];
+          ckey_l[slot] = float_to_key(sv[e]);
           cid_l[slot] = s0 + e;
         }
       }
@@ -496,27 +512,39 @@ __global__ __launch_bounds__(kPsThreads) void k_pool_final(PoolArgs a) {
         W::resolve(ArrayCand{ckey_l, cid_l, ncand}, 0u, 32, need - above, hist256, wb, &kstar,
                    &istar);
     } else {
+      // A huge threshold bin (scores barely spread): resolve over every slot.
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) keys[e * kPsThreads + tid] = key[e];
+      for (int e = 0; e < kPer; ++e)
+        keys[e * kPsThreads + tid] = ((vm >> e) & 1u) ? float_to_key(sv[e]) : 0u;
       __syncthreads();
       W::resolve(LdsKeys{keys, static_cast<uint32_t>(kPsMaxSlots)}, 0u, 32, need, hist256, wb,
                  &kstar, &istar);
+      mode = 2;
     }
   }
-  uint32_t cnt = 0;
+  auto is_sel = [&](int e) {
+    if (need == 0 || !((vm >> e) & 1u)) return false;
+    if (mode == 0) return true;
+    if (mode == 1 && bin[e] != b1) return bin[e] > b1;
+    return selected(float_to_key(sv[e]), s0 + e, kstar, istar);
+  };
+  uint32_t cnt = 0, selmask = 0;
 #pragma unroll
-  for (int e = 0; e < kPer; ++e)
-    cnt += (need > 0 && key[e] != 0u && selected(key[e], s0 + e, kstar, istar)) ? 1u : 0u;
+  for (int e = 0; e < kPer; ++e) {
+    const bool sel = is_sel(e);
+    selmask |= sel ? (1u << e) : 0u;
+    cnt += sel ? 1u : 0u;
+  }
   uint32_t total;
   uint32_t off = W::excl_scan(cnt, wb, &total);
   int32_t* orow = a.out + static_cast<size_t>(r) * a.top_k;
   float* krow = a.out_key ? a.out_key + static_cast<size_t>(r) * a.top_k : nullptr;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    if (need > 0 && key[e] != 0u && selected(key[e], s0 + e, kstar, istar)) {
+    if ((selmask >> e) & 1u) {
       if (off < need) {
         orow[off] = blk[e >> 3] * kBlock + (e & 7);
-        if (krow) krow[off] = key_to_float(key[e]);
+        if (krow) krow[off] = sv[e];
       }
       ++off;
     }
