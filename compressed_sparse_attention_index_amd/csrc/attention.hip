@@ -7,39 +7,45 @@
 // global KV plus this layer's SWA KV).  DeepSeek-V4 essay (mlqm.cn) §4.3: a
 // compressed entry serves as both key and value.
 //
-// Work decomposition.  A workgroup (4 waves) takes one query row, one tile of
-// 32 heads and a range of 64-entry chunks of the row's entry list
+// Work decomposition.  A workgroup (4 waves) takes one query row, all 64
+// heads, and a range of 64-entry chunks of the row's entry list
 //   [ top_k selected slots, padded to a multiple of 32 | 128 window slots ].
-// The two head-tile workgroups of a (row, split) get ids 8 apart, so they run
-// on the same XCD and the second one finds the gathered entries in its L2.
-// Wave w = (e, dh) owns entry tile e (32 entries) and dims half dh of every
-// chunk, and keeps its own online-softmax state for the entries of tile e:
-//   1. it gathers the raw bytes of its 32 entries x 256 dims with
-//      direct-to-LDS loads, two tiles ahead, into a private staging slot
+// Every entry of a chunk is gathered, dequantised and written to LDS once,
+// and serves all 64 heads.  Per chunk, wave w = (e, dh) with e = w / 2,
+// dh = w % 2:
+//   1. stages the raw bytes of entry tile e (32 entries) x dims half dh with
+//      direct-to-LDS loads, two chunks ahead, into a private staging slot
 //      (no registers held; waits counted by hand);
-//   2. it dequantises them exactly to bf16 with the gfx950 conversion
-//      instructions (lane: entry lane % 32, 128 dims per lane half), keeps
-//      them in its own region of an LDS tile and forms the partial
-//      S^T[entry][head] over its 256 dims on 32x32x16 bf16 MFMA with q^T in
-//      registers; the partner wave (e, 1 - dh) supplies the other 256 dims
-//      through LDS (the only exchange inside the loop);
-//   3. online softmax in fp32 (log2 domain) over tile e, identical in both
-//      waves of the pair; P stays in registers, in the accumulator's own lane
-//      order, which is the B-operand order of the next step once the entry
-//      order inside an MFMA step is permuted to match;
-//   4. O^T[dim][head] += V^T . P^T for its 256 dims, V^T read back from its
-//      own LDS region with transposing reads (ds_read_b64_tr_b16), so K and V
-//      share one copy and no other wave waits for it.
-// At the end the two entry-tile states of each dims half are merged through
-// LDS.  LDS tile rows are 1088 bytes apart and 16-byte chunk k of row r sits
-// at k ^ ((r / 4) % 4); together these keep both the row-wise stores and the
-// transposing reads free of bank conflicts, and let the transposing reads of
-// a lane differ only by immediate offsets.
+//   2. dequantises them exactly to bf16 with the gfx950 conversion
+//      instructions and forms the partial S^T[entry][head] over its 256 dims
+//      for all 64 heads on 32x32x16 bf16 MFMA (q^T for 64 heads x 256 dims
+//      sits in accumulation registers); in the same pass it accumulates the
+//      previous chunk's O^T[dims][head] += V^T . P^T for dims quarter w and
+//      all 64 heads, over both entry tiles, with V^T read from the shared LDS
+//      buffer through transposing reads (ds_read_b64_tr_b16), each read
+//      feeding the MFMAs of both head tiles;
+//   3. hands the partial of head tile 1 - dh to its partner (e, 1 - dh) and
+//      receives the partner's partial of head tile dh (one LDS exchange);
+//      once every wave is past the exchange barrier (so done reading the
+//      buffer), dequantises its tile again into the shared buffer;
+//   4. runs the online softmax (fp32, log2 domain) for entry tile e x head
+//      tile dh and publishes P (bf16, in the accumulator's lane order) with
+//      the tile's reference max and sum.
+// Two barriers per chunk order the exchange and the publication.  Every wave
+// keeps the running max and sum of all 64 heads, updated identically in all
+// four waves from the published per-tile values.  The reference max moves
+// only when a tile's max exceeds it by more than kLazyRescale, so the
+// accumulators are rarely rescaled.
+// LDS rows are 1024 bytes (one entry); 16-byte chunk k of row r sits at
+// k ^ kswz(r), which keeps the row-wise stores and the transposing reads free
+// of bank conflicts.  Before the first chunk and after the last one the same
+// buffer stages the query row and the output rows, so that both move to and
+// from HBM as whole 1 KB rows.
 // Rows split over several workgroups write (m, l, O) partials that a second
 // kernel merges in split order; when there are enough rows every workgroup
-// covers whole rows and no partials are written.  The partial O (relative to
-// its split's own max) is rounded to bf16, like the output itself: half the
-// bytes of fp32 partials for a rounding error of the same size as the
+// covers a whole row and no partials are written.  The partial O (relative
+// to its split's own max) is rounded to bf16, like the output itself: half
+// the bytes of fp32 partials for a rounding error of the same size as the
 // output's; m and l stay fp32.
 #include "csa2_launch.h"
 #include "csa2_device.h"
@@ -48,11 +54,11 @@ namespace csa2 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 64;
+constexpr int kChunk = 64;         // entries per chunk: two 32-entry tiles
 constexpr int kTile = 32;
-constexpr int kHeadTile = 32;
-constexpr int kRowBytes = 1088;    // pitch of the dequantised entries in the LDS tile
-constexpr int kStage = 8192;       // staging bytes per wave and tile
+constexpr int kRow = 1024;         // LDS bytes of one dequantised entry (512 bf16)
+constexpr int kBuf = kChunk * kRow;
+constexpr int kStage = 8192;       // staging bytes per wave and chunk
 constexpr int kMainLoads = 5;      // direct-to-LDS loads per wave: selected tile
 constexpr int kWindowLoads = 8;    //                                 window tile
 constexpr float kLog2e = 1.4426950408889634f;
@@ -60,10 +66,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kFillWgs = 256;      // rows are split until about this many workgroups exist
 constexpr int kMaxSplits = 64;
 constexpr int kMaxChunks = (kMaxTopK + kMaxWindow + kChunk - 1) / kChunk;
-// The softmax reference max of a wave moves only when a tile's max exceeds it
-// by more than this (log2 units): P then stays below 2^kLazyRescale, well
-// inside bf16 and fp32 range at unchanged relative precision, and the
-// accumulators are rescaled rarely instead of on every new max.
 constexpr float kLazyRescale = 8.0f;
 
 struct AttnArgs {
@@ -83,45 +85,68 @@ struct AttnArgs {
   float scale2;      // sm_scale * log2(e)
 };
 
-// Pointers to the kernel's LDS arrays.
-struct Lds {
-  uint8_t* v;                       // dequantised chunk, [entry][dim], swizzled
-  uint8_t (*stage)[4][kStage];      // raw bytes per stage and wave
-  f32x4_t (*sx)[4][64];             // partial S^T per wave, [wave][i / 4][lane]
-  int* ids;                         // selected ids of the workgroup's chunks (-1: none)
+struct Smem {
+  uint8_t kv[kBuf];              // dequantised entries of a chunk [entry][dims], swizzled
+  uint8_t stage[2][4][kStage];   // raw bytes [chunk parity][wave]
+  f32x4_t sx[4][4][64];          // partial S^T handed to the partner, [wave][i / 4][lane]
+  u32x4 pb[2][2][2][64];         // P^T (bf16) [entry tile][head tile][16-entry step][lane]
+  float pml[2][2][32][2];        // (reference max, sum) [entry tile][head tile][head]
+  int ids[kMaxChunks * kChunk];  // selected ids of the workgroup's chunks (-1: none)
 };
 
-struct RowCtx {
-  int r, b, tkp, qpos, lo, p0, dh, e, half, slot0, wave, lane;
+struct Ctx {
+  int r, b, tkp, qpos, lo, p0, slot0, wave, lane, c, half, e, dh;
 };
 
 struct State {
-  bf16x8 qb[16];
-  f32x16 o[8];
-  float m_run, l_run;
+  u32x4 qb[2][16];   // q^T: head 32 h + c, dims 256 dh + 128 half + 8 k + [0, 8)
+  f32x16 o[4][2];    // O^T: dims 128 w + 32 m + 8 (i / 4) + 4 half + i % 4, head 32 h + c
+  float m_run[2], l_run[2];   // heads c and 32 + c
 };
 
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+// Swizzle of the 16-byte chunks of LDS row r (a bijection of r's low four
+// bits): a row-wise store by 16 lanes, and each 16- or 32-lane group of a
+// transposing read, touches every bank at most once.
+__device__ __forceinline__ int kswz(int r) {
+  return ((r >> 2) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2) | (((r ^ (r >> 3)) & 1) << 3);
+}
 
-// Whether the wave's tile of chunk ch holds selected entries (else window).
-__device__ __forceinline__ bool tile_is_main(const RowCtx& x, int ch) {
+__device__ __forceinline__ bool tile_is_main(const Ctx& x, int ch) {
   return kChunk * ch + kTile * x.e < x.tkp;
 }
 
-// Issues the wave's direct-to-LDS loads of its tile of chunk ch into staging
-// slot `stg` and returns whether the lane's slot holds an entry.  Slot
-// layout: load i of lane l lands at 1024 i + 16 l (selected tiles: 4 x 16 B
-// of E2M1 and, at 4096 + 4 l, the 4 E8M0 scales; window tiles: 8 x 16 B of
-// FP8).  An empty slot reads a row that always exists (entry 0 of the
-// sequence, or the query row), so every tile of a kind issues a fixed number
-// of loads; it is zeroed when dequantised.
-__device__ __forceinline__ bool issue_tile(const AttnArgs& a, const RowCtx& x, const Lds& s,
-                                           int ch, int stg) {
-  const int c = x.lane & 31;
-  const int slot = kChunk * ch + kTile * x.e + c;
-  const uint32_t dst = lds_offset(s.stage[stg][x.wave]);
+__device__ __forceinline__ uint32_t word_of(const u32x4& w4, int k) {
+  return k == 0 ? w4.x : k == 1 ? w4.y : k == 2 ? w4.z : w4.w;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const __bf16 l = static_cast<__bf16>(lo), h = static_cast<__bf16>(hi);
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h)) << 16);
+}
+
+__device__ __forceinline__ bf16x8 tr_read_pair(const uint8_t* v, int off0, int off1) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v + off0));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v + off1));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Issues the wave's direct-to-LDS loads of its tile of chunk ch (entry tile
+// e, dims half dh) into staging slot `stg` and returns whether the lane's
+// slot holds an entry.  Slot layout: load i of lane l lands at 1024 i + 16 l
+// (selected tiles: 4 x 16 B of E2M1 and, at 4096 + 4 l, the 4 E8M0 scales;
+// window tiles: 8 x 16 B of FP8).  An empty slot reads a row that always
+// exists (entry 0 of the sequence, or the query row), so every tile of a kind
+// issues a fixed number of loads; it is zeroed when dequantised.
+__device__ __forceinline__ bool issue_tile(const AttnArgs& a, const Ctx& x, Smem& sm, int ch,
+                                           int stg) {
+  const int slot = kChunk * ch + kTile * x.e + x.c;
+  const uint32_t dst = lds_offset(sm.stage[stg][x.wave]);
   if (tile_is_main(x, ch)) {
-    const int id = s.ids[slot - x.slot0];
+    const int id = sm.ids[slot - x.slot0];
     const bool valid = id >= 0;
     const size_t er = static_cast<size_t>(x.b) * a.N_cap + (valid ? id : 0);
     const uint8_t* src = a.kv_fp4 + er * 256 + 128 * x.dh + 64 * x.half;
@@ -142,37 +167,210 @@ __device__ __forceinline__ bool issue_tile(const AttnArgs& a, const RowCtx& x, c
   return valid;
 }
 
-__device__ __forceinline__ uint32_t word_of(const u32x4& w4, int k) {
-  return k == 0 ? w4.x : k == 1 ? w4.y : k == 2 ? w4.z : w4.w;
+// Dequantisation of the lane's entry from its staging slot, 16 bytes of raw
+// data (a unit) at a time: a unit holds 8-dim groups k = 4 u .. 4 u + 3 of
+// E2M1 (selected entries) or k = 2 u, 2 u + 1 of FP8 (window); group k is
+// dims 256 dh + 128 half + 8 k.  Empty slots give zeros: scale 0 for E2M1,
+// which has no NaN; zeroed bytes for FP8.
+template <bool kMain>
+struct Dequant {
+  static constexpr int kPerUnit = kMain ? 4 : 2;
+  static constexpr int kUnits = 16 / kPerUnit;
+  float scale[4];
+  const uint8_t* sp;
+  bool valid;
+  __device__ __forceinline__ Dequant(const uint8_t* slot, int lane, bool lane_valid)
+      : sp(slot + 16 * lane), valid(lane_valid) {
+    if (kMain) {
+      const uint32_t sc = *reinterpret_cast<const uint32_t*>(slot + 4096 + 4 * lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t code = (sc >> (8 * i)) & 0xffu;
+        uint32_t bits = code == 0 ? 0x00400000u : (code == 255 ? 0x7fc00000u : code << 23);
+        scale[i] = __uint_as_float(lane_valid ? bits : 0u);
+      }
+    }
+  }
+  __device__ __forceinline__ u32x4 unit(int u) const {
+    return *reinterpret_cast<const u32x4*>(sp + 1024 * u);
+  }
+  __device__ __forceinline__ bf16x8 convert(const u32x4& w, int k) const {
+    if (kMain) return fp4x8_to_bf16x8(word_of(w, k & 3), scale[k >> 2]);
+    const uint32_t lo = (k & 1) ? w.z : w.x, hi = (k & 1) ? w.w : w.y;
+    return fp8x8_to_bf16x8(valid ? lo : 0u, valid ? hi : 0u);
+  }
+};
+
+// Moves the running max and sum past the chunk just finished (from the
+// per-tile reference maxima and sums its waves published) and rescales the
+// accumulators when the max moves.  Where a tile's reference differs from the
+// new max, the wave that published that tile's P rescales it in LDS before
+// anyone reads it.  All waves run this on the same values, so they take the
+// same branches (and barrier) and keep identical (m, l).
+__device__ __forceinline__ void pv_prep(const Ctx& x, Smem& sm, State& st) {
+  float b[2][2];   // [head tile][entry tile]
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float c0 = sm.pml[0][h][x.c][0], s0 = sm.pml[0][h][x.c][1];
+    const float c1 = sm.pml[1][h][x.c][0], s1 = sm.pml[1][h][x.c][1];
+    const float mn = fmaxf(c0, c1);   // never below m_run
+    const float mr = st.m_run[h];
+    const float alpha =
+        mn == mr ? 1.0f : (mr == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mr - mn));
+    b[h][0] = c0 == mn ? 1.0f : (c0 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(c0 - mn));
+    b[h][1] = c1 == mn ? 1.0f : (c1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(c1 - mn));
+    st.l_run[h] = st.l_run[h] * alpha + (s0 * b[h][0] + s1 * b[h][1]);
+    st.m_run[h] = mn;
+    if (__ballot(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) st.o[m][h] *= alpha;
+    }
+  }
+  const bool fix = b[0][0] != 1.0f || b[0][1] != 1.0f || b[1][0] != 1.0f || b[1][1] != 1.0f;
+  if (__ballot(fix) != 0) {
+    const float be = x.dh ? (x.e ? b[1][1] : b[1][0]) : (x.e ? b[0][1] : b[0][0]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const u32x4 w = sm.pb[x.e][x.dh][t][x.lane];
+      u32x4 r;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t u = word_of(w, k);
+        const uint32_t v = pack_bf16x2(__uint_as_float(u << 16) * be,
+                                       __uint_as_float(u & 0xffff0000u) * be);
+        if (k == 0) r.x = v;
+        else if (k == 1) r.y = v;
+        else if (k == 2) r.z = v;
+        else r.w = v;
+      }
+      sm.pb[x.e][x.dh][t][x.lane] = r;
+    }
+    lds_barrier();
+  }
 }
 
-__device__ __forceinline__ bf16x8 tr_read_pair(const uint8_t* v, int off0, int off1) {
-  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v + off0));
-  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v + off1));
-  typedef short i16x8 __attribute__((ext_vector_type(8)));
-  const i16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return __builtin_bit_cast(bf16x8, r);
+// Transposing-read offsets of the wave's V^T operands for 32-dim block m of
+// dims quarter w, 16-entry step j: lane (i16 = lane % 16) reads 8 bytes at
+// entry 16 j + 4 half + i16 / 4 (a) and 16 j + 8 + 4 half + i16 / 4 (b), dims
+// 128 w + 32 m + 16 ((lane / 16) % 2) + 4 (i16 % 4).  The 8 values a lane
+// receives are entries 16 j + 8 (i / 4) + 4 half + i % 4, the order of the
+// accumulator elements 8 t + i of P (j = 2 e + t).  Bits 6-7 of an offset
+// are the block m XORed with the row's swizzle, so block m is base ^ (64 m),
+// and step j adds 16 rows.
+struct TrOffs {
+  int a, b;
+  __device__ __forceinline__ int off_a(int m, int j) const { return (a ^ (64 * m)) + 16 * kRow * j; }
+  __device__ __forceinline__ int off_b(int m, int j) const { return (b ^ (64 * m)) + 16 * kRow * j; }
+};
+
+__device__ __forceinline__ TrOffs tr_offsets(const Ctx& x) {
+  const int i16 = x.lane & 15;
+  const int cl = 2 * ((x.lane >> 4) & 1) + ((i16 & 3) >> 1);
+  const int byte = 8 * (i16 & 1);
+  const int ra = 4 * x.half + (i16 >> 2), rb = ra + 8;
+  TrOffs t;
+  t.a = ra * kRow + 16 * (16 * x.wave + (cl ^ kswz(ra))) + byte;
+  t.b = rb * kRow + 16 * (16 * x.wave + (cl ^ kswz(rb))) + byte;
+  return t;
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 l = static_cast<__bf16>(lo), h = static_cast<__bf16>(hi);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h)) << 16);
+// The loops below are software-pipelined by hand (the next raw unit and the
+// next V^T operand are read one step ahead) and fenced per step, so that the
+// scheduler does not hoist every LDS read of the chunk and run out of
+// registers.
+
+// First pass over chunk ch: partial S^T of the wave's tile for both head
+// tiles, interleaved (kPV) with O^T += V^T . P^T of the previous chunk (P^T of
+// 16-entry step j = 2 e + t is pb[e][h][t]).
+template <bool kMain, bool kPV>
+__device__ __forceinline__ void qk_pv(const Ctx& x, const Smem& sm, State& st, const uint8_t* slot,
+                                      bool valid, f32x16 (&acc)[2], const TrOffs& tr) {
+  using D = Dequant<kMain>;
+  const D dq(slot, x.lane, valid);
+  u32x4 raw[2], pbv[2][2];
+  bf16x8 va[2];
+  raw[0] = dq.unit(0);
+  if (kPV) {
+    va[0] = tr_read_pair(sm.kv, tr.off_a(0, 0), tr.off_b(0, 0));
+    pbv[0][0] = sm.pb[0][0][0][x.lane];
+    pbv[0][1] = sm.pb[0][1][0][x.lane];
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int u = k / D::kPerUnit;
+    if (k % D::kPerUnit == 0 && u + 1 < D::kUnits) raw[(u + 1) & 1] = dq.unit(u + 1);
+    const int j = k >> 2, m = k & 3;
+    if (kPV && k + 1 < 16) {
+      const int j1 = (k + 1) >> 2, m1 = (k + 1) & 3;
+      va[(k + 1) & 1] = tr_read_pair(sm.kv, tr.off_a(m1, j1), tr.off_b(m1, j1));
+      if (m == 0 && j + 1 < 4) {
+        pbv[(j + 1) & 1][0] = sm.pb[(j + 1) >> 1][0][(j + 1) & 1][x.lane];
+        pbv[(j + 1) & 1][1] = sm.pb[(j + 1) >> 1][1][(j + 1) & 1][x.lane];
+      }
+    }
+    const bf16x8 kb = dq.convert(raw[u & 1], k);
+    acc[0] = mfma32(kb, __builtin_bit_cast(bf16x8, st.qb[0][k]), acc[0]);
+    acc[1] = mfma32(kb, __builtin_bit_cast(bf16x8, st.qb[1][k]), acc[1]);
+    if (kPV) {
+      st.o[m][0] = mfma32(va[k & 1], __builtin_bit_cast(bf16x8, pbv[j & 1][0]), st.o[m][0]);
+      st.o[m][1] = mfma32(va[k & 1], __builtin_bit_cast(bf16x8, pbv[j & 1][1]), st.o[m][1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
-// The wave's tile of chunk ch, staged in slot `stg`; `valid` is the lane's
-// slot validity and is replaced by that of chunk ch + 2, whose loads go to
-// the same slot once this tile is dequantised.
-__device__ __forceinline__ void attend_tile(const AttnArgs& a, const RowCtx& x, const Lds& s,
-                                            State& st, bool& valid, int ch, int c1, int stg) {
-  const int wave = x.wave, lane = x.lane;
-  const int c = lane & 31;
-  const uint32_t vmask = static_cast<uint32_t>(__ballot(valid));
-  const bool lane_valid = valid;
-  const int rho0 = 4 * x.half;   // entry of sacc[i]: 8 (i / 4) + 4 half + i % 4
+// Second pass over chunk ch: the dequantised tile goes to the LDS buffer
+// (16-byte chunk k of the lane's row at st_off ^ (k << 4)).
+template <bool kMain>
+__device__ __forceinline__ void store_tile(const Ctx& x, Smem& sm, const uint8_t* slot, bool valid,
+                                           int st_off) {
+  using D = Dequant<kMain>;
+  const D dq(slot, x.lane, valid);
+  u32x4 raw[2];
+  raw[0] = dq.unit(0);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int u = k / D::kPerUnit;
+    if (k % D::kPerUnit == 0 && u + 1 < D::kUnits) raw[(u + 1) & 1] = dq.unit(u + 1);
+    *reinterpret_cast<bf16x8*>(sm.kv + (st_off ^ (k << 4))) = dq.convert(raw[u & 1], k);
+    if (k % D::kPerUnit == D::kPerUnit - 1) __builtin_amdgcn_sched_barrier(0);
+  }
+}
 
-  // This tile's loads have landed once only chunk ch + 1's are outstanding.
+// PV of the last chunk alone.
+__device__ __forceinline__ void pv_only(const Ctx& x, const Smem& sm, State& st,
+                                        const TrOffs& tr) {
+  bf16x8 va[2];
+  u32x4 pbv[2][2];
+  va[0] = tr_read_pair(sm.kv, tr.off_a(0, 0), tr.off_b(0, 0));
+  pbv[0][0] = sm.pb[0][0][0][x.lane];
+  pbv[0][1] = sm.pb[0][1][0][x.lane];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int j = k >> 2, m = k & 3;
+    if (k + 1 < 16) {
+      const int j1 = (k + 1) >> 2, m1 = (k + 1) & 3;
+      va[(k + 1) & 1] = tr_read_pair(sm.kv, tr.off_a(m1, j1), tr.off_b(m1, j1));
+      if (m == 0 && j + 1 < 4) {
+        pbv[(j + 1) & 1][0] = sm.pb[(j + 1) >> 1][0][(j + 1) & 1][x.lane];
+        pbv[(j + 1) & 1][1] = sm.pb[(j + 1) >> 1][1][(j + 1) & 1][x.lane];
+      }
+    }
+    st.o[m][0] = mfma32(va[k & 1], __builtin_bit_cast(bf16x8, pbv[j & 1][0]), st.o[m][0]);
+    st.o[m][1] = mfma32(va[k & 1], __builtin_bit_cast(bf16x8, pbv[j & 1][1]), st.o[m][1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Chunk ch, staged in slot S; kPV: the previous chunk's PV runs in the same
+// pass.  `valid` (the lane's slot validity) is replaced by that of chunk
+// ch + 2, whose loads go to the same slot at the end.
+template <bool kMain, bool kPV>
+__device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Ctx& x, Smem& sm, State& st,
+                                             bool& valid, int ch, int c1, int S, int st_off,
+                                             const TrOffs& tr) {
+  if (kPV) pv_prep(x, sm, st);
+  // This chunk's loads have landed once only chunk ch + 1's are outstanding.
   if (ch + 1 < c1) {
     if (tile_is_main(x, ch + 1)) wait_vmem<kMainLoads>();
     else wait_vmem<kWindowLoads>();
@@ -180,224 +378,93 @@ __device__ __forceinline__ void attend_tile(const AttnArgs& a, const RowCtx& x, 
     wait_vmem<0>();
   }
   asm volatile("" ::: "memory");
+  const uint8_t* slot = sm.stage[S][x.wave];
+  const uint32_t vmask = static_cast<uint32_t>(__ballot(valid));
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  qk_pv<kMain, kPV>(x, sm, st, slot, valid, acc, tr);
 
-  // Dequantise (empty slots give zeros: scale 0 for E2M1, which has no NaN;
-  // zeroed bytes for FP8), keep in the wave's LDS region, partial S^T.  The
-  // dims-half-0 wave starts the sums of empty slots at -inf, so that S is
-  // -inf exactly there and no per-element mask is needed afterwards.
-  f32x16 sacc = {}, sacc2 = {};
-  if (x.dh == 0 && vmask != 0xffffffffu) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int rho = 8 * (i >> 2) + rho0 + (i & 3);
-      if (!((vmask >> rho) & 1u)) sacc[i] = -__builtin_inff();
-    }
-  }
-  const uint8_t* sp = s.stage[stg][wave] + 16 * lane;
-  const int row = kTile * x.e + c;
-  uint8_t* vrow = s.v + row * kRowBytes + 16 * (32 * x.dh + 16 * x.half);
-  const int g = swz(row);
-  if (tile_is_main(x, ch)) {
-    u32x4 w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = *reinterpret_cast<const u32x4*>(sp + 1024 * i);
-    const uint32_t sc = *reinterpret_cast<const uint32_t*>(s.stage[stg][wave] + 4096 + 4 * lane);
-    float scale[4];
+  // Exchange with the partner wave (e, 1 - dh): it gets this wave's partial
+  // of head tile 1 - dh, this wave gets its partial of head tile dh
+  // (a + b == b + a exactly, so the order of the two halves is immaterial).
+  auto give = [&](const f32x16& g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      scale[i] = lane_valid ? e8m0_to_float((sc >> (8 * i)) & 0xffu) : 0.0f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const bf16x8 kb = fp4x8_to_bf16x8(word_of(w[k >> 2], k & 3), scale[k >> 2]);
-      *reinterpret_cast<bf16x8*>(vrow + 16 * (k ^ g)) = kb;
-      if (k & 1) sacc2 = mfma32(kb, st.qb[k], sacc2);
-      else sacc = mfma32(kb, st.qb[k], sacc);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const u32x2 w2 = *reinterpret_cast<const u32x2*>(sp + 1024 * (k >> 1) + 8 * (k & 1));
-      const bf16x8 kb = fp8x8_to_bf16x8(lane_valid ? w2.x : 0u, lane_valid ? w2.y : 0u);
-      *reinterpret_cast<bf16x8*>(vrow + 16 * (k ^ g)) = kb;
-      if (k & 1) sacc2 = mfma32(kb, st.qb[k], sacc2);
-      else sacc = mfma32(kb, st.qb[k], sacc);
-    }
-  }
-  // Two accumulation chains (even and odd steps) keep two MFMAs in flight;
-  // they are added in a fixed order.
-  sacc += sacc2;
-  if (ch + 2 < c1) valid = issue_tile(a, x, s, ch + 2, stg);
-
-  // Exchange of the partial sums with the partner wave (e, 1 - dh): the
-  // first barrier makes sure it has read the previous tile's values.
+      sm.sx[x.wave][i][x.lane] = f32x4_t{g[4 * i], g[4 * i + 1], g[4 * i + 2], g[4 * i + 3]};
+  };
+  if (x.dh) give(acc[0]);
+  else give(acc[1]);
+  // Past this barrier every wave has finished its transposing reads of the
+  // previous chunk, so the LDS buffer takes this chunk.
   lds_barrier();
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    s.sx[wave][i][lane] = f32x4_t{sacc[4 * i], sacc[4 * i + 1], sacc[4 * i + 2], sacc[4 * i + 3]};
-  lds_barrier();
+  store_tile<kMain>(x, sm, slot, valid, st_off);
 
-  // Sums S of head c for entries rho = 8 (i / 4) + 4 half + i % 4 of the tile
-  // (a + b == b + a exactly, so both waves of the pair get the same S).
+  // Sums S of head 32 dh + c for entries rho = 8 (i / 4) + 4 half + i % 4 of
+  // the tile; empty slots get S = -inf.
   float xv[16];
-  float smax = -__builtin_inff();
+  auto sum_halves = [&](const f32x16& keep) {
 #pragma unroll
-  for (int gi = 0; gi < 4; ++gi) {
-    const f32x4_t other = s.sx[wave ^ 1][gi][lane];
+    for (int i = 0; i < 4; ++i) {
+      const f32x4_t other = sm.sx[x.wave ^ 1][i][x.lane];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      xv[4 * gi + j] = sacc[4 * gi + j] + other[j];
-      smax = fmaxf(smax, xv[4 * gi + j]);
+      for (int j = 0; j < 4; ++j) xv[4 * i + j] = keep[4 * i + j] + other[j];
+    }
+  };
+  if (x.dh) sum_halves(acc[1]);
+  else sum_halves(acc[0]);
+  if (vmask != 0xffffffffu) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rho = 8 * (i >> 2) + 4 * x.half + (i & 3);
+      if (!((vmask >> rho) & 1u)) xv[i] = -__builtin_inff();
     }
   }
+  float smax = xv[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) smax = fmaxf(smax, xv[i]);
   smax = fmaxf(smax, other_half(smax));
-  // Logits are S * scale2 (log2 units, scale2 > 0, so the max of the logits
-  // is smax * scale2).  Reference max: set by the first tile with an entry
-  // (O and l are still zero then), moved later only past kLazyRescale, with
-  // O and l rescaled.
+  // Logits are S * scale2 (log2 units, scale2 > 0, so the tile's max logit
+  // is smax * scale2).  The tile's reference: the running max, unless that
+  // is still -inf or the tile exceeds it by more than kLazyRescale.
   const float tmax = smax * a.scale2;
-  if (st.m_run == -__builtin_inff()) {
-    st.m_run = tmax;
-  } else if (__ballot(tmax > st.m_run + kLazyRescale) != 0) {
-    const float m_new = fmaxf(st.m_run, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
-    st.l_run *= alpha;
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) st.o[m][i] *= alpha;
-    st.m_run = m_new;
-  }
-  // p = 2^(S scale2 - m): empty slots have S = -inf and give exactly 0.  The
-  // max is still -inf only if no tile so far had an entry, this one included;
-  // its p are then all 0 with any finite reference.
-  const float m_ref = st.m_run == -__builtin_inff() ? 0.0f : st.m_run;
+  const float mr = x.dh ? st.m_run[1] : st.m_run[0];
+  const float cand = (mr == -__builtin_inff() || tmax > mr + kLazyRescale) ? tmax : mr;
+  const float mref = cand == -__builtin_inff() ? 0.0f : cand;
   float tsum = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    xv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(xv[i], a.scale2, -m_ref));
+    xv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(xv[i], a.scale2, -mref));
     tsum += xv[i];
   }
   tsum += other_half(tsum);
-  st.l_run += tsum;
-
-  // O^T[dims 256 dh + 32 m + .., head] += V^T . P^T over the tile's entries.
-  // Lane (i16 = lane % 16) reads 8 bytes at row r = 32 e + 16 t + 4 half +
-  // i16 / 4 (and r + 8), dims 256 dh + 32 m + 16 ((lane / 16) % 2) + 4 (i16 %
-  // 4), i.e. 16-byte chunk 32 dh + 4 m + cl; swz(r) = half and swz(r + 8) =
-  // half + 2 for every t, so m and t only move the address by constants.
-  const int i16 = lane & 15;
-  const int rq = i16 >> 2;
-  const int cl = 2 * ((lane >> 4) & 1) + ((i16 & 3) >> 1);
-  const int byte = 8 * (i16 & 1);
-  const int r0 = kTile * x.e + 4 * x.half + rq;
-  const int base_a = r0 * kRowBytes + 16 * (32 * x.dh + (cl ^ x.half)) + byte;
-  const int base_b = (r0 + 8) * kRowBytes + 16 * (32 * x.dh + (cl ^ (x.half + 2))) + byte;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    bf16x8 va[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int off = 16 * kRowBytes * t + 64 * m;
-      va[m] = tr_read_pair(s.v, base_a + off, base_b + off);
-    }
-    const bf16x8 pbv = __builtin_bit_cast(
-        bf16x8, u32x4{pack_bf16x2(xv[8 * t], xv[8 * t + 1]), pack_bf16x2(xv[8 * t + 2], xv[8 * t + 3]),
-                      pack_bf16x2(xv[8 * t + 4], xv[8 * t + 5]),
-                      pack_bf16x2(xv[8 * t + 6], xv[8 * t + 7])});
-#pragma unroll
-    for (int m = 0; m < 8; ++m) st.o[m] = mfma32(va[m], pbv, st.o[m]);
-  }
-}
-
-// Merge of the two entry-tile states of each dims half, then the output (or
-// the split partial): wave (E, dh) keeps the 32-dim blocks m with m / 4 == E
-// and hands the others to wave (1 - E, dh) through the no longer needed LDS
-// tile.  Both waves of a pair hold the same (m, l).
-template <int E>
-__device__ __forceinline__ void finish(const AttnArgs& a, const RowCtx& x, const State& st,
-                                       uint8_t* lds_tile, float (*ml)[2][32], int split,
-                                       int head) {
-  const int c = x.lane & 31;
-  f32x4_t* xo = reinterpret_cast<f32x4_t*>(lds_tile);   // [wave][4 blocks][4][64 lanes]
-#pragma unroll
-  for (int mm = 0; mm < 4; ++mm)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4)
-      xo[((x.wave * 4 + mm) * 4 + i4) * 64 + x.lane] =
-          f32x4_t{st.o[4 * (1 - E) + mm][4 * i4], st.o[4 * (1 - E) + mm][4 * i4 + 1],
-                  st.o[4 * (1 - E) + mm][4 * i4 + 2], st.o[4 * (1 - E) + mm][4 * i4 + 3]};
+  for (int t2 = 0; t2 < 2; ++t2)
+    sm.pb[x.e][x.dh][t2][x.lane] =
+        u32x4{pack_bf16x2(xv[8 * t2], xv[8 * t2 + 1]), pack_bf16x2(xv[8 * t2 + 2], xv[8 * t2 + 3]),
+              pack_bf16x2(xv[8 * t2 + 4], xv[8 * t2 + 5]),
+              pack_bf16x2(xv[8 * t2 + 6], xv[8 * t2 + 7])};
   if (x.half == 0) {
-    ml[x.wave][0][c] = st.m_run;
-    ml[x.wave][1][c] = st.l_run;
+    sm.pml[x.e][x.dh][x.c][0] = cand;
+    sm.pml[x.e][x.dh][x.c][1] = tsum;
   }
+  // The staging slot has been read twice; chunk ch + 2 goes there.
+  if (ch + 2 < c1) valid = issue_tile(a, x, sm, ch + 2, S);
   lds_barrier();
-  const int pw = x.wave ^ 2;   // partner: same dims half, other entry tile
-  const float m_o = ml[pw][0][c], l_o = ml[pw][1][c];
-  const float m_all = fmaxf(st.m_run, m_o);
-  const float w_me = st.m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(st.m_run - m_all);
-  const float w_o = m_o == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_o - m_all);
-  // Sums are formed in entry-tile order (tile 0 first) in both waves.
-  const float l_all = E == 0 ? st.l_run * w_me + l_o * w_o : l_o * w_o + st.l_run * w_me;
-
-  // This wave's dims: 256 dh + 128 E + 32 mm + 8 (i / 4) + 4 half + i % 4.
-  const int dim0 = 256 * x.dh + 128 * E;
-  const float inv = l_all > 0.0f ? 1.0f / l_all : 0.0f;
-  const size_t ps = static_cast<size_t>(x.r) * a.nsplit + split;
-#pragma unroll
-  for (int mm = 0; mm < 4; ++mm) {
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4_t other = xo[((pw * 4 + mm) * 4 + i4) * 64 + x.lane];
-      float v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float mine = st.o[4 * E + mm][4 * i4 + j] * w_me, theirs = other[j] * w_o;
-        v[j] = E == 0 ? mine + theirs : theirs + mine;
-      }
-      const int d = dim0 + 32 * mm + 8 * i4 + 4 * x.half;
-      if (a.nsplit == 1) {
-        *reinterpret_cast<u32x2*>(a.out + (static_cast<size_t>(x.r) * kHeads + head) * kDim + d) =
-            u32x2{pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
-      } else {
-        *reinterpret_cast<u32x2*>(a.part_o + (ps * kHeads + head) * kDim + d) =
-            u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      }
-    }
-  }
-  if (x.dh == 0 && E == 0 && x.half == 0) {
-    if (a.nsplit == 1) {
-      if (a.lse != nullptr)
-        a.lse[static_cast<size_t>(x.r) * kHeads + head] =
-            l_all > 0.0f ? (m_all + log2f(l_all)) * kLn2 : -__builtin_inff();
-    } else {
-      a.part_ml[(ps * kHeads + head) * 2 + 0] = m_all;
-      a.part_ml[(ps * kHeads + head) * 2 + 1] = l_all;
-    }
-  }
 }
 
 __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t l_v[kChunk * kRowBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t l_stage[2][4][kStage];
-  __shared__ __attribute__((aligned(16))) f32x4_t l_sx[4][4][64];
-  __shared__ int l_ids[kMaxChunks * kChunk];
-  __shared__ float l_ml[4][2][32];
-  const Lds s{l_v, l_stage, l_sx, l_ids};
+  __shared__ __attribute__((aligned(16))) Smem sm;
 
-  // Work id: the two head tiles of a (row, split) are 8 ids apart (same XCD).
-  const int id = blockIdx.x;
-  const int ht = (id >> 3) & 1;
-  const int pair = (id >> 4) * 8 + (id & 7);
-  if (pair >= a.rows * a.nsplit) return;
-  RowCtx x;
+  const int pair = blockIdx.x;
+  Ctx x;
   x.r = pair / a.nsplit;
   const int split = pair - x.r * a.nsplit;
   x.b = x.r / a.n_q;
   x.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   x.lane = threadIdx.x & 63;
-  x.dh = x.wave & 1;
-  x.e = x.wave >> 1;
+  x.c = x.lane & 31;
   x.half = x.lane >> 5;
+  x.e = x.wave >> 1;
+  x.dh = x.wave & 1;
   x.tkp = (a.top_k + kTile - 1) / kTile * kTile;
   x.qpos = a.q_pos[x.r];
   x.p0 = a.swa_pos0[x.b];
@@ -405,13 +472,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
   if (a.replay_start >= 0) x.lo = max(x.lo, a.replay_start);
   const int c0 = split * a.cps;
   const int c1 = min(c0 + a.cps, a.n_chunks);
-  const int c = x.lane & 31;
-  const int head = kHeadTile * ht + c;
+  x.slot0 = kChunk * c0;
 
   // The selected ids of chunks [c0, c1) go to LDS first, so that no gather
   // waits on a global id load; out-of-range ids become -1 (no entry).  The
-  // id loads and the q loads below are all issued before any is used.
-  x.slot0 = kChunk * c0;
+  // id loads and the q loads are all issued before any is used.
   constexpr int kPer = (kMaxChunks * kChunk + kThreads - 1) / kThreads;
   int sid[kPer];
 #pragma unroll
@@ -421,52 +486,127 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
     if (slot < kChunk * c1 && slot < a.top_k)
       sid[u] = a.idx[static_cast<size_t>(x.r) * a.top_k + slot];
   }
-  // q^T operand (lane = head, dims 256 dh + 128 half + 8 k).
-  State st;
+  // The query row (64 heads x 1 KB) goes to the K/V buffer, which is free
+  // until the first chunk is stored: wave w fetches head rows 16 w .. 16 w +
+  // 15 with one coalesced 1 KB load per row, lane l taking 16-byte chunk
+  // l ^ kswz(row) so that chunk C of a row lands at slot C ^ kswz(row).
   {
-    const u32x4* p = reinterpret_cast<const u32x4*>(
-        a.q + (static_cast<size_t>(x.r) * kHeads + head) * kDim + 256 * x.dh + 128 * x.half);
-    // q is only ever an MFMA operand, which may come from accumulation
-    // registers: defining it there leaves the VGPRs to the accumulators and
-    // to the LDS reads in flight.  All 16 loads are issued first.
-    u32x4 v[16];
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q + static_cast<size_t>(x.r) * kHeads * kDim);
+    const uint32_t kv0 = lds_offset(sm.kv);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = p[k];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) st.qb[k] = __builtin_bit_cast(bf16x8, to_agpr(v[k]));
+    for (int i = 0; i < 16; ++i) {
+      const int row = 16 * x.wave + i;
+      dma16(qrow + row * kRow + 16 * (x.lane ^ kswz(row)), kv0 + row * kRow);
+    }
   }
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int i = threadIdx.x + kThreads * u;
-    if (i < kChunk * (c1 - c0)) s.ids[i] = sid[u] < a.N_cap ? sid[u] : -1;
+    if (i < kChunk * (c1 - c0)) sm.ids[i] = (sid[u] >= 0 && sid[u] < a.N_cap) ? sid[u] : -1;
   }
-  // q and the ids have landed before the first gather is issued: no other
-  // vector-memory load is in flight inside the loop.
+  // The ids and the query row have landed (every wave's) before the first
+  // gather is issued: no other vector-memory load is in flight inside the
+  // loop.
   wait_vmem<0>();
   __syncthreads();
 
-  bool valid0 = issue_tile(a, x, s, c0, 0);
+  bool valid0 = issue_tile(a, x, sm, c0, 0);
   bool valid1 = false;
-  if (c0 + 1 < c1) valid1 = issue_tile(a, x, s, c0 + 1, 1);
+  if (c0 + 1 < c1) valid1 = issue_tile(a, x, sm, c0 + 1, 1);
+  // q^T operands (head 32 h + c, dims 256 dh + 128 half + 8 k).  q is only
+  // ever an MFMA operand, which may come from accumulation registers:
+  // keeping it there leaves the VGPRs to the accumulators and the operands
+  // in flight.
+  State st;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) st.o[m] = f32x16{};
-  st.m_run = -__builtin_inff();
-  st.l_run = 0.0f;
+  for (int h = 0; h < 2; ++h) {
+    const int row = 32 * h + x.c;
+    u32x4 v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      v[k] = *reinterpret_cast<const u32x4*>(
+          sm.kv + row * kRow + 16 * ((32 * x.dh + 16 * x.half + k) ^ kswz(row)));
+#pragma unroll
+    for (int k = 0; k < 16; ++k) st.qb[h][k] = to_agpr(v[k]);
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    st.o[m][0] = f32x16{};
+    st.o[m][1] = f32x16{};
+  }
+  st.m_run[0] = st.m_run[1] = -__builtin_inff();
+  st.l_run[0] = st.l_run[1] = 0.0f;
 
-  // One loop body for both staging slots (slot = chunk parity): with the
-  // body duplicated per slot the compiler no longer proves the staging slots
-  // apart from the other LDS arrays and drains the loads in flight.
-  for (int ch = c0; ch < c1; ++ch) {
-    const int stg = (ch - c0) & 1;
-    bool v = stg ? valid1 : valid0;
-    attend_tile(a, x, s, st, v, ch, c1, stg);
-    if (stg) valid1 = v;
+  const TrOffs tr = tr_offsets(x);
+  // Row-wise store offset of the lane's entry 32 e + c, dims 256 dh + 128 half.
+  const int srow = kTile * x.e + x.c;
+  const int st_off = srow * kRow + 512 * x.dh + 256 * x.half + 16 * kswz(srow);
+
+  // Chunks [c0, cm) hold selected entries in this wave's tile, [cm, c1) window
+  // entries.
+  const int cm = min(max((x.tkp - kTile * x.e + kChunk - 1) / kChunk, c0), c1);
+  if (c0 < cm) attend_chunk<true, false>(a, x, sm, st, valid0, c0, c1, 0, st_off, tr);
+  else attend_chunk<false, false>(a, x, sm, st, valid0, c0, c1, 0, st_off, tr);
+  int ch = c0 + 1;
+  for (; ch < cm; ++ch) {
+    const int S = (ch - c0) & 1;
+    bool v = S ? valid1 : valid0;
+    attend_chunk<true, true>(a, x, sm, st, v, ch, c1, S, st_off, tr);
+    if (S) valid1 = v;
     else valid0 = v;
   }
+  for (; ch < c1; ++ch) {
+    const int S = (ch - c0) & 1;
+    bool v = S ? valid1 : valid0;
+    attend_chunk<false, true>(a, x, sm, st, v, ch, c1, S, st_off, tr);
+    if (S) valid1 = v;
+    else valid0 = v;
+  }
+  pv_prep(x, sm, st);
+  pv_only(x, sm, st, tr);
 
-  lds_barrier();   // all transposing reads of the tile are done
-  if (x.e == 0) finish<0>(a, x, st, s.v, l_ml, split, head);
-  else finish<1>(a, x, st, s.v, l_ml, split, head);
+  // Output (or the split partial), through the K/V buffer once every wave
+  // is done with it: lane (c, half) holds head 32 h + c, dims 128 w + 32 m +
+  // 8 i4 + 4 half + [0, 4), i.e. half of 16-byte chunk 16 w + 4 m + i4 of
+  // the head's row; rows are then stored whole, one coalesced 1 KB store per
+  // head row.
+  const size_t ps = static_cast<size_t>(x.r) * a.nsplit + split;
+  lds_barrier();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 32 * h + x.c;
+    const float l = st.l_run[h];
+    const float f = a.nsplit == 1 ? (l > 0.0f ? 1.0f / l : 0.0f) : 1.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x16& o = st.o[m][h];
+        *reinterpret_cast<u32x2*>(sm.kv + row * kRow +
+                                  16 * ((16 * x.wave + 4 * m + i4) ^ kswz(row)) + 8 * x.half) =
+            u32x2{pack_bf16x2(o[4 * i4] * f, o[4 * i4 + 1] * f),
+                  pack_bf16x2(o[4 * i4 + 2] * f, o[4 * i4 + 3] * f)};
+      }
+    if (x.wave == 0 && x.half == 0) {
+      if (a.nsplit == 1) {
+        if (a.lse != nullptr)
+          a.lse[static_cast<size_t>(x.r) * kHeads + row] =
+              l > 0.0f ? (st.m_run[h] + log2f(l)) * kLn2 : -__builtin_inff();
+      } else {
+        a.part_ml[(ps * kHeads + row) * 2 + 0] = st.m_run[h];
+        a.part_ml[(ps * kHeads + row) * 2 + 1] = l;
+      }
+    }
+  }
+  lds_barrier();
+  uint16_t* dst = a.nsplit == 1 ? a.out + static_cast<size_t>(x.r) * kHeads * kDim
+                                : a.part_o + ps * kHeads * kDim;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = 16 * x.wave + i;
+    *reinterpret_cast<u32x4*>(dst + row * kDim + 8 * x.lane) =
+        *reinterpret_cast<const u32x4*>(sm.kv + row * kRow + 16 * (x.lane ^ kswz(row)));
+  }
 }
 
 // Merge of split partials in split order: one workgroup per (row, head),
@@ -521,13 +661,12 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
         L > 0.0f ? (mx + log2f(L)) * kLn2 : -__builtin_inff();
 }
 
-// Splits per row: none once the (row, head tile) workgroups alone reach about
-// kFillWgs, otherwise enough to get there (at most one chunk per split).
+// Splits per row: none once the row workgroups alone reach about kFillWgs,
+// otherwise enough to get there (at most one chunk per split).
 void plan(int rows, int top_k, int* n_chunks, int* cps, int* nsplit) {
   const int tkp = (top_k + kTile - 1) / kTile * kTile;
   *n_chunks = (tkp + kMaxWindow + kChunk - 1) / kChunk;
-  const long long per_split = 2LL * rows;
-  long long want = (kFillWgs + per_split - 1) / per_split;
+  long long want = (kFillWgs + rows - 1) / (rows > 0 ? rows : 1);
   if (want < 1) want = 1;
   if (want > *n_chunks) want = *n_chunks;
   if (want > kMaxSplits) want = kMaxSplits;
@@ -564,8 +703,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* kv_fp4, const ui
     a.part_o = static_cast<uint16_t*>(ws);
     a.part_ml = reinterpret_cast<float*>(a.part_o + static_cast<size_t>(rows) * a.nsplit * kHeads * kDim);
   }
-  const long long pairs = static_cast<long long>(rows) * a.nsplit;
-  const long long wgs = (pairs + 7) / 8 * 16;
+  const long long wgs = static_cast<long long>(rows) * a.nsplit;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(k_sparse_attn, dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, stream,
                      a);
