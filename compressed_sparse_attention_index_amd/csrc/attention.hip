@@ -279,51 +279,13 @@ __device__ __forceinline__ TrOffs tr_offsets(const Ctx& x) {
 // scheduler does not hoist every LDS read of the chunk and run out of
 // registers.
 
-// First pass over chunk ch: partial S^T of the wave's tile for both head
-// tiles, interleaved (kPV) with O^T += V^T . P^T of the previous chunk (P^T of
-// 16-entry step j = 2 e + t is pb[e][h][t]).
-template <bool kMain, bool kPV>
-__device__ __forceinline__ void qk_pv(const Ctx& x, const Smem& sm, State& st, const uint8_t* slot,
-                                      bool valid, f32x16 (&acc)[2], const TrOffs& tr) {
-  using D = Dequant<kMain>;
-  const D dq(slot, x.lane, valid);
-  u32x4 raw[2], pbv[2][2];
-  bf16x8 va[2];
-  raw[0] = dq.unit(0);
-  if (kPV) {
-    va[0] = tr_read_pair(sm.kv, tr.off_a(0, 0), tr.off_b(0, 0));
-    pbv[0][0] = sm.pb[0][0][0][x.lane];
-    pbv[0][1] = sm.pb[0][1][0][x.lane];
-  }
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int u = k / D::kPerUnit;
-    if (k % D::kPerUnit == 0 && u + 1 < D::kUnits) raw[(u + 1) & 1] = dq.unit(u + 1);
-    const int j = k >> 2, m = k & 3;
-    if (kPV && k + 1 < 16) {
-      const int j1 = (k + 1) >> 2, m1 = (k + 1) & 3;
-      va[(k + 1) & 1] = tr_read_pair(sm.kv, tr.off_a(m1, j1), tr.off_b(m1, j1));
-      if (m == 0 && j + 1 < 4) {
-        pbv[(j + 1) & 1][0] = sm.pb[(j + 1) >> 1][0][(j + 1) & 1][x.lane];
-        pbv[(j + 1) & 1][1] = sm.pb[(j + 1) >> 1][1][(j + 1) & 1][x.lane];
-      }
-    }
-    const bf16x8 kb = dq.convert(raw[u & 1], k);
-    acc[0] = mfma32(kb, __builtin_bit_cast(bf16x8, st.qb[0][k]), acc[0]);
-    acc[1] = mfma32(kb, __builtin_bit_cast(bf16x8, st.qb[1][k]), acc[1]);
-    if (kPV) {
-      st.o[m][0] = mfma32(va[k & 1], __builtin_bit_cast(bf16x8, pbv[j & 1][0]), st.o[m][0]);
-      st.o[m][1] = mfma32(va[k & 1], __builtin_bit_cast(bf16x8, pbv[j & 1][1]), st.o[m][1]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// Second pass over chunk ch: the dequantised tile goes to the LDS buffer
-// (16-byte chunk k of the lane's row at st_off ^ (k << 4)).
+// Chunk ch's tile: dequantised once, written to the LDS buffer (16-byte chunk
+// k of the lane's row at st_off ^ (k << 4)) and multiplied into the partial
+// S^T of both head tiles.
 template <bool kMain>
-__device__ __forceinline__ void store_tile(const Ctx& x, Smem& sm, const uint8_t* slot, bool valid,
-                                           int st_off) {
+__device__ __forceinline__ void qk_store(const Ctx& x, Smem& sm, const State& st,
+                                         const uint8_t* slot, bool valid, int st_off,
+                                         f32x16 (&acc)[2]) {
   using D = Dequant<kMain>;
   const D dq(slot, x.lane, valid);
   u32x4 raw[2];
@@ -332,14 +294,17 @@ __device__ __forceinline__ void store_tile(const Ctx& x, Smem& sm, const uint8_t
   for (int k = 0; k < 16; ++k) {
     const int u = k / D::kPerUnit;
     if (k % D::kPerUnit == 0 && u + 1 < D::kUnits) raw[(u + 1) & 1] = dq.unit(u + 1);
-    *reinterpret_cast<bf16x8*>(sm.kv + (st_off ^ (k << 4))) = dq.convert(raw[u & 1], k);
-    if (k % D::kPerUnit == D::kPerUnit - 1) __builtin_amdgcn_sched_barrier(0);
+    const bf16x8 kb = dq.convert(raw[u & 1], k);
+    *reinterpret_cast<bf16x8*>(sm.kv + (st_off ^ (k << 4))) = kb;
+    acc[0] = mfma32(kb, __builtin_bit_cast(bf16x8, st.qb[0][k]), acc[0]);
+    acc[1] = mfma32(kb, __builtin_bit_cast(bf16x8, st.qb[1][k]), acc[1]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// PV of the last chunk alone.
-__device__ __forceinline__ void pv_only(const Ctx& x, const Smem& sm, State& st,
-                                        const TrOffs& tr) {
+// O^T += V^T . P^T for the chunk in the LDS buffer (P^T of 16-entry step
+// j = 2 e + t is pb[e][h][t]).
+__device__ __forceinline__ void pv(const Ctx& x, const Smem& sm, State& st, const TrOffs& tr) {
   bf16x8 va[2];
   u32x4 pbv[2][2];
   va[0] = tr_read_pair(sm.kv, tr.off_a(0, 0), tr.off_b(0, 0));
@@ -362,14 +327,19 @@ __device__ __forceinline__ void pv_only(const Ctx& x, const Smem& sm, State& st,
   }
 }
 
-// Chunk ch, staged in slot S; kPV: the previous chunk's PV runs in the same
-// pass.  `valid` (the lane's slot validity) is replaced by that of chunk
-// ch + 2, whose loads go to the same slot at the end.
+// Chunk ch, staged in slot S; kPV: the previous chunk's PV comes first.
+// `valid` (the lane's slot validity) is replaced by that of chunk ch + 2,
+// whose loads go to the same slot once it has been read.
 template <bool kMain, bool kPV>
 __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Ctx& x, Smem& sm, State& st,
                                              bool& valid, int ch, int c1, int S, int st_off,
                                              const TrOffs& tr) {
-  if (kPV) pv_prep(x, sm, st);
+  if (kPV) {
+    pv_prep(x, sm, st);
+    pv(x, sm, st, tr);
+    // Every wave is done reading the buffer: it takes this chunk.
+    lds_barrier();
+  }
   // This chunk's loads have landed once only chunk ch + 1's are outstanding.
   if (ch + 1 < c1) {
     if (tile_is_main(x, ch + 1)) wait_vmem<kMainLoads>();
@@ -381,7 +351,9 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Ctx& x, Sm
   const uint8_t* slot = sm.stage[S][x.wave];
   const uint32_t vmask = static_cast<uint32_t>(__ballot(valid));
   f32x16 acc[2] = {f32x16{}, f32x16{}};
-  qk_pv<kMain, kPV>(x, sm, st, slot, valid, acc, tr);
+  qk_store<kMain>(x, sm, st, slot, valid, st_off, acc);
+  // The staging slot has been read; chunk ch + 2 goes there.
+  if (ch + 2 < c1) valid = issue_tile(a, x, sm, ch + 2, S);
 
   // Exchange with the partner wave (e, 1 - dh): it gets this wave's partial
   // of head tile 1 - dh, this wave gets its partial of head tile dh
@@ -393,10 +365,7 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Ctx& x, Sm
   };
   if (x.dh) give(acc[0]);
   else give(acc[1]);
-  // Past this barrier every wave has finished its transposing reads of the
-  // previous chunk, so the LDS buffer takes this chunk.
   lds_barrier();
-  store_tile<kMain>(x, sm, slot, valid, st_off);
 
   // Sums S of head 32 dh + c for entries rho = 8 (i / 4) + 4 half + i % 4 of
   // the tile; empty slots get S = -inf.
@@ -446,8 +415,6 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Ctx& x, Sm
     sm.pml[x.e][x.dh][x.c][0] = cand;
     sm.pml[x.e][x.dh][x.c][1] = tsum;
   }
-  // The staging slot has been read twice; chunk ch + 2 goes there.
-  if (ch + 2 < c1) valid = issue_tile(a, x, sm, ch + 2, S);
   lds_barrier();
 }
 
@@ -529,6 +496,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) st.qb[h][k] = to_agpr(v[k]);
   }
+  // Every wave has its q before the first chunk goes to the buffer.
+  lds_barrier();
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     st.o[m][0] = f32x16{};
@@ -563,7 +532,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
     else valid0 = v;
   }
   pv_prep(x, sm, st);
-  pv_only(x, sm, st, tr);
+  pv(x, sm, st, tr);
 
   // Output (or the split partial), through the K/V buffer once every wave
   // is done with it: lane (c, half) holds head 32 h + c, dims 128 w + 32 m +
