@@ -276,7 +276,7 @@ def _attn_ref(d, b, j, idx_row, q=None, swa=None, window=128, replay_start=-1):
 
 
 @pytest.mark.parametrize("case", ["topk512", "ragged", "invalid", "dense", "window16", "replay",
-                                  "seq_start", "no_main"])
+                                  "seq_start", "no_main", "mixed_chunk"])
 def test_attention_cases(case):
     T, B = 2048, 3
     d = synth.decode_workload(B=B, T=T, kdtype="bf16", seed=41)
@@ -289,6 +289,10 @@ def test_attention_cases(case):
         top_k = 300
     if case == "no_main":
         top_k = 0
+    if case == "mixed_chunk":
+        # 160 selected slots: one 64-entry chunk holds 32 selected and 32 window
+        # entries, and the last chunk is half past the window.
+        top_k = 160
     idx = np.stack([np.sort(rng.choice(T, size=max(top_k, 1), replace=False))[:top_k] for _ in range(B)])
     if case == "dense":
         idx = np.tile(np.arange(300), (B, 1))
@@ -342,6 +346,31 @@ def test_attention_single_split_and_reuse_identical():
         o, l = _attn_ref(d, 0, j, idx[j])
         check_attention(out[0, j], lse[0, j], o, l, what=f"prefill row {j}")
     assert N == 2000 + 256
+
+
+def test_attention_running_max_moves_mid_row():
+    # 256 rows: each workgroup walks a whole row (10 chunks).  The window
+    # entries, which come last, lie along head 0's query of row 0 (0.5 q plus
+    # a little noise), so for that head their logits (about 11) exceed the
+    # selected entries' by far more than the lazy-rescale margin: the running
+    # max jumps partway through the row and the output and sums are rescaled.
+    # The values stay O(1), so the bf16 rounding of P stays inside the
+    # tolerance.
+    d = synth.prefill_workload(n_q=256, prefix_tokens=4000, seed=46)
+    q0 = d["q"][0, 0, 0].view(torch.bfloat16).float()
+    g = synth.Gen(47)
+    d["swa"] = synth.to_fp8_bytes(0.5 * q0 + 0.1 * g.normal(*d["swa"].shape))
+    rng = np.random.default_rng(46)
+    vis = _np(d["vis_len"])[0]
+    idx = np.stack([np.sort(rng.choice(v, size=512, replace=False)) for v in vis]).astype(np.int32)
+    print("attention 256 rows, window along one query", flush=True)
+    out, lse = _attn_gpu(d, torch.from_numpy(idx).reshape(1, 256, 512))
+    for j in (0, 97, 255):
+        o, l = _attn_ref(d, 0, j, idx[j])
+        check_attention(out[0, j], lse[0, j], o, l, what=f"row {j}")
+    # Head 0 of row 0 is dominated by the window: its lse is far above the
+    # others'.
+    assert lse[0, 0, 0] > 8.0 and np.median(lse[0, 0]) < 8.0
 
 
 def test_deterministic_reruns():
