@@ -67,6 +67,7 @@ constexpr int kFillWgs = 256;      // rows are split until about this many workg
 constexpr int kMaxSplits = 64;
 constexpr int kMaxChunks = (kMaxTopK + kMaxWindow + kChunk - 1) / kChunk;
 constexpr float kLazyRescale = 8.0f;
+static_assert(kMaxChunks <= kMaxSplits, "a row splits at most once per chunk");
 
 struct AttnArgs {
   const uint16_t* q;
@@ -579,45 +580,44 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
 }
 
 // Merge of split partials in split order: one workgroup per (row, head),
-// 64 threads x 8 dims.  Lane s < nsplit fetches split s's (m, l); the merge
-// weights are formed in registers and the partial outputs are read with all
-// loads of a group of splits issued together.
+// 64 threads x 8 dims.  A row has at most S splits (S = 4, or kMaxChunks:
+// one chunk at least per split), so every split's partial output and (m, l)
+// are loaded at once (lane s < nsplit fetches split s's (m, l)); the merge
+// weights are formed in registers.
+template <int S>
 __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
   const int r = blockIdx.x / kHeads;
   const int head = blockIdx.x % kHeads;
   const int t = threadIdx.x;
   const size_t ps0 = static_cast<size_t>(r) * a.nsplit;
-  float ms = -__builtin_inff(), lsv = 0.0f;
-  if (t < a.nsplit) {
-    ms = a.part_ml[((ps0 + t) * kHeads + head) * 2];
-    lsv = a.part_ml[((ps0 + t) * kHeads + head) * 2 + 1];
+  u32x4 u[S];
+#pragma unroll
+  for (int g = 0; g < S; ++g) {
+    const int sp = min(g, a.nsplit - 1);
+    u[g] = *reinterpret_cast<const u32x4*>(a.part_o + ((ps0 + sp) * kHeads + head) * kDim + 8 * t);
   }
+  const int ts = min(t, a.nsplit - 1);
+  const float ms0 = a.part_ml[((ps0 + ts) * kHeads + head) * 2];
+  const float ls0 = a.part_ml[((ps0 + ts) * kHeads + head) * 2 + 1];
+  const float ms = t < a.nsplit ? ms0 : -__builtin_inff();
+  const float lsv = t < a.nsplit ? ls0 : 0.0f;
   float mx = ms;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
   const float wgt_mine = (ms == -__builtin_inff()) ? 0.0f : exp2f(ms - mx);
   float L = 0.0f;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  constexpr int kGroup = 4;
-  for (int s0 = 0; s0 < a.nsplit; s0 += kGroup) {
-    u32x4 u[kGroup];
 #pragma unroll
-    for (int g = 0; g < kGroup; ++g) {
-      const int sp = min(s0 + g, a.nsplit - 1);
-      u[g] = *reinterpret_cast<const u32x4*>(a.part_o + ((ps0 + sp) * kHeads + head) * kDim + 8 * t);
-    }
+  for (int g = 0; g < S; ++g) {
+    const float wgt = __shfl(wgt_mine, g, 64);
+    const float lsg = __shfl(lsv, g, 64);
+    if (g < a.nsplit) {
+      L += wgt * lsg;
 #pragma unroll
-    for (int g = 0; g < kGroup; ++g) {
-      const float wgt = __shfl(wgt_mine, s0 + g, 64);
-      const float lsg = __shfl(lsv, s0 + g, 64);
-      if (s0 + g < a.nsplit) {
-        L += wgt * lsg;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t w = word_of(u[g], j);
-          acc[2 * j] += wgt * __uint_as_float(w << 16);
-          acc[2 * j + 1] += wgt * __uint_as_float(w & 0xffff0000u);
-        }
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = word_of(u[g], j);
+        acc[2 * j] += wgt * __uint_as_float(w << 16);
+        acc[2 * j + 1] += wgt * __uint_as_float(w & 0xffff0000u);
       }
     }
   }
@@ -638,7 +638,7 @@ void plan(int rows, int top_k, int* n_chunks, int* cps, int* nsplit) {
   long long want = (kFillWgs + rows - 1) / (rows > 0 ? rows : 1);
   if (want < 1) want = 1;
   if (want > *n_chunks) want = *n_chunks;
-  if (want > kMaxSplits) want = kMaxSplits;
+  if (want > kMaxSplits) want = kMaxSplits;   // (n_chunks <= kMaxChunks <= kMaxSplits)
   *cps = (*n_chunks + static_cast<int>(want) - 1) / static_cast<int>(want);
   *nsplit = (*n_chunks + *cps - 1) / *cps;
 }
@@ -672,13 +672,18 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* kv_fp4, const ui
     a.part_o = static_cast<uint16_t*>(ws);
     a.part_ml = reinterpret_cast<float*>(a.part_o + static_cast<size_t>(rows) * a.nsplit * kHeads * kDim);
   }
+  // The merge holds every split of a row in registers.
+  if (a.nsplit > kMaxChunks) return hipErrorInvalidValue;
   const long long wgs = static_cast<long long>(rows) * a.nsplit;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(k_sparse_attn, dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, stream,
                      a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.nsplit == 1) return err;
-  hipLaunchKernelGGL(k_attn_combine, dim3(rows * kHeads), dim3(64), 0, stream, a);
+  if (a.nsplit <= 4)
+    hipLaunchKernelGGL(k_attn_combine<4>, dim3(rows * kHeads), dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_attn_combine<kMaxChunks>, dim3(rows * kHeads), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
