@@ -75,19 +75,18 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_hist(const float* __restrict_
   __shared__ uint32_t h[kHistBins];
   const int r = blockIdx.y;
   const int nb_cap = (N_cap + 7) >> 3;
-  const int n = (min(max(vis_len[r], 0), N_cap) + 7) >> 3;
   const int i0 = blockIdx.x * kBtItems;
-  if (n <= k || i0 >= n) return;
-  for (int i = threadIdx.x; i < kHistBins; i += kBtThreads) h[i] = 0;
-  __syncthreads();
+  // The row items are loaded (clamped to the row's capacity) together with
+  // the visible length, not after it.
   const float* row = bm + static_cast<size_t>(r) * nb_cap;
   float v[kBtItems / kBtThreads];
 #pragma unroll
-  for (int j = 0; j < kBtItems / kBtThreads; ++j) {
-    const int i = i0 + threadIdx.x + j * kBtThreads;
-    v[j] = row[min(i, n - 1)];
-    if (i >= n) v[j] = 0.0f;
-  }
+  for (int j = 0; j < kBtItems / kBtThreads; ++j)
+    v[j] = row[min(i0 + static_cast<int>(threadIdx.x) + j * kBtThreads, nb_cap - 1)];
+  const int n = (min(max(vis_len[r], 0), N_cap) + 7) >> 3;
+  if (n <= k || i0 >= n) return;
+  for (int i = threadIdx.x; i < kHistBins; i += kBtThreads) h[i] = 0;
+  __syncthreads();
 #pragma unroll
   for (int j = 0; j < kBtItems / kBtThreads; ++j) {
     const int i = i0 + threadIdx.x + j * kBtThreads;
@@ -109,29 +108,28 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_filter(const float* __restric
   const int r = blockIdx.y;
   const int tid = threadIdx.x;
   const int nb_cap = (N_cap + 7) >> 3;
-  const int n = (min(max(vis_len[r], 0), N_cap) + 7) >> 3;
   const int i0 = blockIdx.x * kBtItems;
-  if (n <= k || i0 >= n) return;
+  // The row items (clamped to the row's capacity), the histogram and the
+  // visible length are loaded in one batch.
+  const float* row = bm + static_cast<size_t>(r) * nb_cap;
+  float v[kBtItems / kBtThreads];
+#pragma unroll
+  for (int j = 0; j < kBtItems / kBtThreads; ++j)
+    v[j] = row[min(i0 + tid + j * kBtThreads, nb_cap - 1)];
   const uint32_t* gh = ws.hist + static_cast<size_t>(r) * kHistBins;
   constexpr int kPerBin = kHistBins / kBtThreads;
   uint32_t h1[kPerBin];
 #pragma unroll
   for (int i = 0; i < kPerBin; ++i) h1[i] = gh[kHistBins - 1 - (tid * kPerBin + i)];
+  const int n = (min(max(vis_len[r], 0), N_cap) + 7) >> 3;
+  if (n <= k || i0 >= n) return;
   uint32_t above, n1;
   const int b1 =
       W::find_rank_bin_regs(h1, kHistBins, static_cast<uint32_t>(k), true, wb, &above, &n1);
   for (int i = tid; i < kHistBins; i += kBtThreads) h2[i] = 0;
   if (tid < 2) cnt[tid] = 0;
   __syncthreads();
-  const float* row = bm + static_cast<size_t>(r) * nb_cap;
   const size_t seg = static_cast<size_t>(r) * nb_cap + i0;
-  float v[kBtItems / kBtThreads];
-#pragma unroll
-  for (int j = 0; j < kBtItems / kBtThreads; ++j) {
-    const int i = i0 + tid + j * kBtThreads;
-    v[j] = row[min(i, n - 1)];
-    if (i >= n) v[j] = 0.0f;
-  }
 #pragma unroll
   for (int j = 0; j < kBtItems / kBtThreads; ++j) {
     const int i = i0 + tid + j * kBtThreads;
@@ -172,6 +170,24 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const int32_t* __restri
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int nb_cap = (N_cap + 7) >> 3;
+  // Both histograms, the filter workgroups' counts and the visible length
+  // are loaded in one batch (one memory latency); the histograms are
+  // searched in registers.
+  const uint32_t* gh = ws.hist + static_cast<size_t>(r) * kHistBins;
+  const uint32_t* gh2 = ws.hist2 + static_cast<size_t>(r) * kHistBins;
+  constexpr int kPerBin = kHistBins / kBtThreads;
+  static_assert(kHistBins % kBtThreads == 0, "whole bins per thread");
+  static_assert(kBtMaxWgs == 128, "two filter workgroups per lane of the first wave");
+  uint32_t h1[kPerBin], h2[kPerBin];
+#pragma unroll
+  for (int i = 0; i < kPerBin; ++i) {
+    h1[i] = gh[kHistBins - 1 - (tid * kPerBin + i)];
+    h2[i] = gh2[kHistBins - 1 - (tid * kPerBin + i)];
+  }
+  const uint32_t* wc = ws.wgcnt + static_cast<size_t>(r) * kBtMaxWgs * 2;
+  const int wl = tid & 63;
+  const u32x2 wca = *reinterpret_cast<const u32x2*>(wc + 2 * wl);
+  const u32x2 wcb = *reinterpret_cast<const u32x2*>(wc + 2 * (wl + 64));
   const int n = (min(max(vis_len[r], 0), N_cap) + 7) >> 3;
   int32_t* orow = out + static_cast<size_t>(r) * k;
   if (n <= k) {  // every visible block is kept
@@ -179,18 +195,6 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const int32_t* __restri
     return;
   }
   const uint32_t need = static_cast<uint32_t>(k);
-  const uint32_t* gh = ws.hist + static_cast<size_t>(r) * kHistBins;
-  const uint32_t* gh2 = ws.hist2 + static_cast<size_t>(r) * kHistBins;
-  // Both histograms are loaded into registers in one batch (one memory
-  // latency) and searched there.
-  constexpr int kPerBin = kHistBins / kBtThreads;
-  static_assert(kHistBins % kBtThreads == 0, "whole bins per thread");
-  uint32_t h1[kPerBin], h2[kPerBin];
-#pragma unroll
-  for (int i = 0; i < kPerBin; ++i) {
-    h1[i] = gh[kHistBins - 1 - (tid * kPerBin + i)];
-    h2[i] = gh2[kHistBins - 1 - (tid * kPerBin + i)];
-  }
   uint32_t above, n1;
   const int b1 = W::find_rank_bin_regs(h1, kHistBins, need, true, wb, &above, &n1);
   const uint32_t rem1 = need - above;
@@ -198,14 +202,15 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const int32_t* __restri
   const int b2 = W::find_rank_bin_regs(h2, kHistBins, rem1, true, wb, &above2, &n2);
   const uint32_t rem2 = rem1 - above2;
 
-  // Prefix offsets of the filter workgroups' segments.
+  // Prefix offsets of the filter workgroups' segments (nwg <= kBtMaxWgs).
   const int nwg = (n + kBtItems - 1) / kBtItems;
   if (tid < 64) {
-    const uint32_t* wc = ws.wgcnt + static_cast<size_t>(r) * kBtMaxWgs * 2;
     uint32_t ps = 0, pc = 0;
-    for (int base = 0; base < nwg; base += 64) {
-      const int w = base + tid;
-      const uint32_t cs = w < nwg ? wc[2 * w] : 0u, cc = w < nwg ? wc[2 * w + 1] : 0u;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int w = 64 * half + tid;
+      const u32x2 c2 = half ? wcb : wca;
+      const uint32_t cs = w < nwg ? c2.x : 0u, cc = w < nwg ? c2.y : 0u;
       const uint32_t is = wave_incl_scan_u32(cs), ic = wave_incl_scan_u32(cc);
       if (w < nwg) {
         off_s[w + 1] = ps + is;
@@ -224,25 +229,29 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const int32_t* __restri
   for (int w = tid; w < nwords; w += kBtThreads) bitmap[w] = 0u;
   __syncthreads();
   const uint32_t n_sure = off_s[nwg], n_cand = off_c[nwg];
-  // Flattened item g -> (segment w, slot g - off[w]) by binary search.
+  // Flattened item g -> (segment w, slot g - off[w]): the last w < nwg with
+  // off[w] <= g, by a fixed-step binary search (independent searches
+  // interleave).
   auto locate = [&](const uint32_t* off, uint32_t g) {
-    int lo = 0, hi = nwg;   // off[lo] <= g < off[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (off[mid] <= g) lo = mid; else hi = mid;
-    }
+    int lo = 0;
+#pragma unroll
+    for (int step = kBtMaxWgs / 2; step > 0; step >>= 1)
+      if (lo + step < nwg && off[lo + step] <= g) lo += step;
     return static_cast<size_t>(r) * nb_cap + static_cast<size_t>(lo) * kBtItems + (g - off[lo]);
   };
-  for (uint32_t g = tid; g < n_sure; g += kBtThreads) {
-    const int id = ws.sure[locate(off_s, g)];
-    atomicOr(&bitmap[id >> 5], 1u << (id & 31));
+  // The sure items (fewer than need <= 2048, i.e. at most two per thread) and
+  // the first batch of candidates are loaded together; items past the end
+  // read slot 0 of their row's first segment and are ignored.
+  static_assert(kMaxPoolBlocks <= 2 * kBtThreads, "two sure items per thread");
+  int sid_v[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint32_t g = tid + u * kBtThreads;
+    sid_v[u] = ws.sure[locate(off_s, g < n_sure ? g : 0u)];
   }
-  for (uint32_t base = 0; base < n_cand; base += kBtThreads) {
+  auto cand_batch = [&](uint32_t base, uint32_t key, int id) {
     const uint32_t g = base + tid;
     const bool in = g < n_cand;
-    const size_t at = in ? locate(off_c, g) : 0;
-    const uint32_t key = in ? ws.ckey[at] : 0u;
-    const int id = in ? ws.cid[at] : 0;
     const int mb = static_cast<int>(mid_bits(key));
     if (in && mb > b2) atomicOr(&bitmap[id >> 5], 1u << (id & 31));
     const bool fin = in && mb == b2;
@@ -251,6 +260,20 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const int32_t* __restri
       fkey[slot] = key;
       fid[slot] = id;
     }
+  };
+  {
+    const size_t at = locate(off_c, tid < n_cand ? tid : 0u);
+    const uint32_t key0 = ws.ckey[at];
+    const int id0 = ws.cid[at];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (tid + u * kBtThreads < n_sure) atomicOr(&bitmap[sid_v[u] >> 5], 1u << (sid_v[u] & 31));
+    cand_batch(0, key0, id0);
+  }
+  for (uint32_t base = kBtThreads; base < n_cand; base += kBtThreads) {
+    const uint32_t g = base + tid;
+    const size_t at = locate(off_c, g < n_cand ? g : 0u);
+    cand_batch(base, ws.ckey[at], ws.cid[at]);
   }
   __syncthreads();
   const uint32_t prefix = (static_cast<uint32_t>(b1) << kHistShift) | (static_cast<uint32_t>(b2) << 8);
