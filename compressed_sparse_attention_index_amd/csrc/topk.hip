@@ -545,31 +545,57 @@ __global__ __launch_bounds__(kPsThreads) void k_pool_final(PoolArgs a) {
       mode = 2;
     }
   }
-  auto is_sel = [&](int e) {
-    if (need == 0 || !((vm >> e) & 1u)) return false;
-    if (mode == 0) return true;
-    if (mode == 1 && bin[e] != b1) return bin[e] > b1;
-    return selected(float_to_key(sv[e]), s0 + e, kstar, istar);
-  };
-  uint32_t cnt = 0, selmask = 0;
+  // Selected slots: every valid one (mode 0); bin above b1, or the exact
+  // (key, id) test inside bin b1 (mode 1); the exact test (mode 2).  The exact
+  // test runs only where a wave holds a slot of bin b1.
+  uint32_t selmask = 0;
+  if (need > 0) {
+    if (mode == 0) {
+      selmask = vm;
+    } else if (mode == 1) {
+      uint32_t eq = 0;
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const bool sel = is_sel(e);
-    selmask |= sel ? (1u << e) : 0u;
-    cnt += sel ? 1u : 0u;
+      for (int e = 0; e < kPer; ++e) {
+        selmask |= bin[e] > b1 && bin[e] < kPfBins ? (1u << e) : 0u;
+        eq |= bin[e] == b1 ? (1u << e) : 0u;
+      }
+      if (__ballot(eq != 0) != 0) {
+#pragma unroll
+        for (int e = 0; e < kPer; ++e)
+          if (((eq >> e) & 1u) && selected(float_to_key(sv[e]), s0 + e, kstar, istar))
+            selmask |= 1u << e;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e)
+        if (((vm >> e) & 1u) && selected(float_to_key(sv[e]), s0 + e, kstar, istar))
+          selmask |= 1u << e;
+    }
   }
+  const uint32_t cnt = static_cast<uint32_t>(__popc(selmask));
   uint32_t total;
   uint32_t off = W::excl_scan(cnt, wb, &total);
   int32_t* orow = a.out + static_cast<size_t>(r) * a.top_k;
   float* krow = a.out_key ? a.out_key + static_cast<size_t>(r) * a.top_k : nullptr;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    if ((selmask >> e) & 1u) {
-      if (off < need) {
-        orow[off] = blk[e >> 3] * kBlock + (e & 7);
-        if (krow) krow[off] = sv[e];
-      }
+  if (krow == nullptr) {
+    // Positions only: walk the set bits (slot e of block blk[e / 8]).
+    uint32_t m = selmask;
+    while (m != 0u) {
+      const int e = __builtin_ctz(m);
+      m &= m - 1u;
+      if (off < need) orow[off] = (e < kBlock ? blk[0] : blk[1]) * kBlock + (e & 7);
       ++off;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      if ((selmask >> e) & 1u) {
+        if (off < need) {
+          orow[off] = blk[e >> 3] * kBlock + (e & 7);
+          krow[off] = sv[e];
+        }
+        ++off;
+      }
     }
   }
   for (int i = static_cast<int>(min(total, need)) + tid; i < a.top_k; i += kPsThreads) {
