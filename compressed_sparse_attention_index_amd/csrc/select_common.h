@@ -76,6 +76,25 @@ struct Wg {
     return r;
   }
 
+  // As excl_scan with one barrier: every wave reads all wave totals and
+  // forms its own prefix.  wb must not be written again before another
+  // barrier (use it for the last scan of a kernel).
+  __device__ static uint32_t excl_scan_last(uint32_t v, uint32_t* wb, uint32_t* total) {
+    const int wave = threadIdx.x >> 6, lane = lane_id();
+    const uint32_t inc = wave_incl_scan_u32(v);
+    if (lane == 63) wb[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t t = wb[w];
+      before += w < wave ? t : 0u;
+      tot += t;
+    }
+    *total = tot;
+    return before + inc - v;
+  }
+
   __device__ static uint32_t sum(uint32_t v, uint32_t* wb) {
     uint32_t t;
     excl_scan(v, wb, &t);

@@ -318,7 +318,7 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const int32_t* __restri
   uint32_t c = 0;
   for (int w = w0; w < min(w0 + wpt, nwords); ++w) c += __popc(bitmap[w]);
   uint32_t total;
-  uint32_t off = W::excl_scan(c, wb, &total);
+  uint32_t off = W::excl_scan_last(c, wb, &total);
   for (int w = w0; w < min(w0 + wpt, nwords); ++w) {
     uint32_t bits = bitmap[w];
     while (bits) {
@@ -574,7 +574,7 @@ __global__ __launch_bounds__(kPsThreads) void k_pool_final(PoolArgs a) {
   }
   const uint32_t cnt = static_cast<uint32_t>(__popc(selmask));
   uint32_t total;
-  uint32_t off = W::excl_scan(cnt, wb, &total);
+  uint32_t off = W::excl_scan_last(cnt, wb, &total);
   int32_t* orow = a.out + static_cast<size_t>(r) * a.top_k;
   float* krow = a.out_key ? a.out_key + static_cast<size_t>(r) * a.top_k : nullptr;
   if (krow == nullptr) {
@@ -895,7 +895,7 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select_reg(
     cnt += __popc(words[u]);
   }
   uint32_t total;
-  uint32_t off = W::excl_scan(cnt, wb, &total);
+  uint32_t off = W::excl_scan_last(cnt, wb, &total);
   int32_t* orow = out + static_cast<size_t>(r) * k;
   float* krow = out_key ? out_key + static_cast<size_t>(r) * k : nullptr;
 #pragma unroll
