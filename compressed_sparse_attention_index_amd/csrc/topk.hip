@@ -212,10 +212,10 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const int32_t* __restri
       const u32x2 c2 = half ? wcb : wca;
       const uint32_t cs = w < nwg ? c2.x : 0u, cc = w < nwg ? c2.y : 0u;
       const uint32_t is = wave_incl_scan_u32(cs), ic = wave_incl_scan_u32(cc);
-      if (w < nwg) {
-        off_s[w + 1] = ps + is;
-        off_c[w + 1] = pc + ic;
-      }
+      // Past the last segment the offsets read as "infinite", so the segment
+      // search needs no bound test.
+      off_s[w + 1] = w < nwg ? ps + is : 0xffffffffu;
+      off_c[w + 1] = w < nwg ? pc + ic : 0xffffffffu;
       ps += __shfl(is, 63, 64);
       pc += __shfl(ic, 63, 64);
     }
@@ -229,14 +229,14 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const int32_t* __restri
   for (int w = tid; w < nwords; w += kBtThreads) bitmap[w] = 0u;
   __syncthreads();
   const uint32_t n_sure = off_s[nwg], n_cand = off_c[nwg];
-  // Flattened item g -> (segment w, slot g - off[w]): the last w < nwg with
-  // off[w] <= g, by a fixed-step binary search (independent searches
-  // interleave).
+  // Flattened item g (< off[nwg]) -> (segment w, slot g - off[w]): the last
+  // w with off[w] <= g, by a fixed-step binary search without branches
+  // (independent searches interleave).
   auto locate = [&](const uint32_t* off, uint32_t g) {
     int lo = 0;
 #pragma unroll
     for (int step = kBtMaxWgs / 2; step > 0; step >>= 1)
-      if (lo + step < nwg && off[lo + step] <= g) lo += step;
+      lo = off[lo + step] <= g ? lo + step : lo;
     return static_cast<size_t>(r) * nb_cap + static_cast<size_t>(lo) * kBtItems + (g - off[lo]);
   };
   // The sure items (fewer than need <= 2048, i.e. at most two per thread) and
@@ -262,15 +262,25 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const int32_t* __restri
     }
   };
   {
-    const size_t at = locate(off_c, tid < n_cand ? tid : 0u);
-    const uint32_t key0 = ws.ckey[at];
-    const int id0 = ws.cid[at];
+    // The first kCandBatches batches of candidates are loaded in one go too.
+    constexpr int kCandBatches = 4;
+    uint32_t ck[kCandBatches];
+    int ci[kCandBatches];
+#pragma unroll
+    for (int u = 0; u < kCandBatches; ++u) {
+      const uint32_t g = u * kBtThreads + tid;
+      const size_t at = locate(off_c, g < n_cand ? g : 0u);
+      ck[u] = ws.ckey[at];
+      ci[u] = ws.cid[at];
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u)
       if (tid + u * kBtThreads < n_sure) atomicOr(&bitmap[sid_v[u] >> 5], 1u << (sid_v[u] & 31));
-    cand_batch(0, key0, id0);
+#pragma unroll
+    for (int u = 0; u < kCandBatches; ++u)
+      if (u * kBtThreads < static_cast<int>(n_cand)) cand_batch(u * kBtThreads, ck[u], ci[u]);
   }
-  for (uint32_t base = kBtThreads; base < n_cand; base += kBtThreads) {
+  for (uint32_t base = 4 * kBtThreads; base < n_cand; base += kBtThreads) {
     const uint32_t g = base + tid;
     const size_t at = locate(off_c, g < n_cand ? g : 0u);
     cand_batch(base, ws.ckey[at], ws.cid[at]);
