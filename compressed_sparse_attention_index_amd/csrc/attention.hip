@@ -47,6 +47,8 @@
 // to its split's own max) is rounded to bf16, like the output itself: half
 // the bytes of fp32 partials for a rounding error of the same size as the
 // output's; m and l stay fp32.
+#include <type_traits>
+
 #include "csa2_launch.h"
 #include "csa2_device.h"
 
@@ -120,10 +122,12 @@ __device__ __forceinline__ uint32_t word_of(const u32x4& w4, int k) {
   return k == 0 ? w4.x : k == 1 ? w4.y : k == 2 ? w4.z : w4.w;
 }
 
+// Two floats -> two bf16 (round to nearest even), lo in the low half: one
+// v_cvt_pk_bf16_f32 (converting the halves one by one takes four).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 l = static_cast<__bf16>(lo), h = static_cast<__bf16>(hi);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ bf16x8 tr_read_pair(const uint8_t* v, int off0, int off1) {
@@ -222,7 +226,8 @@ __device__ __forceinline__ void pv_prep(const Ctx& x, Smem& sm, State& st) {
     b[h][1] = c1 == mn ? 1.0f : (c1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(c1 - mn));
     st.l_run[h] = st.l_run[h] * alpha + (s0 * b[h][0] + s1 * b[h][1]);
     st.m_run[h] = mn;
-    if (__ballot(alpha != 1.0f) != 0) {
+    // (While the max is still -inf nothing has been accumulated: O is zero.)
+    if (__ballot(alpha != 1.0f && mr != -__builtin_inff()) != 0) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) st.o[m][h] *= alpha;
     }
@@ -542,21 +547,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
   // head row.
   const size_t ps = static_cast<size_t>(x.r) * a.nsplit + split;
   lds_barrier();
+  // Split partials are written unnormalised, whole rows normalised by 1 / l.
+  auto write_rows = [&](auto normalise) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 32 * h + x.c;
+      const float l = st.l_run[h];
+      const float f = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x16& o = st.o[m][h];
+          float v[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = decltype(normalise)::value ? o[4 * i4 + j] * f : o[4 * i4 + j];
+          *reinterpret_cast<u32x2*>(sm.kv + row * kRow +
+                                    16 * ((16 * x.wave + 4 * m + i4) ^ kswz(row)) + 8 * x.half) =
+              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+    }
+  };
+  if (a.nsplit == 1) write_rows(std::true_type{});
+  else write_rows(std::false_type{});
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int row = 32 * h + x.c;
     const float l = st.l_run[h];
-    const float f = a.nsplit == 1 ? (l > 0.0f ? 1.0f / l : 0.0f) : 1.0f;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x16& o = st.o[m][h];
-        *reinterpret_cast<u32x2*>(sm.kv + row * kRow +
-                                  16 * ((16 * x.wave + 4 * m + i4) ^ kswz(row)) + 8 * x.half) =
-            u32x2{pack_bf16x2(o[4 * i4] * f, o[4 * i4 + 1] * f),
-                  pack_bf16x2(o[4 * i4 + 2] * f, o[4 * i4 + 3] * f)};
-      }
     if (x.wave == 0 && x.half == 0) {
       if (a.nsplit == 1) {
         if (a.lse != nullptr)
