@@ -95,7 +95,8 @@ class Step:
 
     def _ws(self, op, top_k, kb):
         n = self.csa.workspace_size(op, self.B, self.n_q, self.N, top_k, kb)
-        return self.torch.empty(max(n, 16), dtype=self.torch.uint8, device="cuda")
+        # Zero-filled once, as the block Top-K workspace expects.
+        return self.torch.zeros(max(n, 16), dtype=self.torch.uint8, device="cuda")
 
     def _scan(self):
         d, csa = self.d, self.csa

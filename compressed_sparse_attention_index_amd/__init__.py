@@ -111,10 +111,12 @@ def _stream(stream):
 
 
 def _workspace(ws, nbytes, device):
+    # Zero-filled: the block Top-K histograms must start at zero to take the
+    # fast path (every call leaves them zeroed again).
     if nbytes == 0:
         return None, 0
     if ws is None:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
     return ws, ws.numel() * ws.element_size()
 
 

@@ -16,26 +16,25 @@
 //   1. stages the raw bytes of entry tile e (32 entries) x dims half dh with
 //      direct-to-LDS loads, two chunks ahead, into a private staging slot
 //      (no registers held; waits counted by hand);
-//   2. dequantises them exactly to bf16 with the gfx950 conversion
-//      instructions and forms the partial S^T[entry][head] over its 256 dims
-//      for all 64 heads on 32x32x16 bf16 MFMA (q^T for 64 heads x 256 dims
-//      sits in accumulation registers); in the same pass it accumulates the
-//      previous chunk's O^T[dims][head] += V^T . P^T for dims quarter w and
-//      all 64 heads, over both entry tiles, with V^T read from the shared LDS
-//      buffer through transposing reads (ds_read_b64_tr_b16), each read
-//      feeding the MFMAs of both head tiles;
-//   3. hands the partial of head tile 1 - dh to its partner (e, 1 - dh) and
-//      receives the partner's partial of head tile dh (one LDS exchange);
-//      once every wave is past the exchange barrier (so done reading the
-//      buffer), dequantises its tile again into the shared buffer;
-//   4. runs the online softmax (fp32, log2 domain) for entry tile e x head
+//   2. finishes the previous chunk's O^T[dims][head] += V^T . P^T for dims
+//      quarter w and all 64 heads, with V^T read from the shared LDS buffer
+//      through transposing reads (ds_read_b64_tr_b16), each read feeding the
+//      MFMAs of both head tiles; a barrier follows (the buffer is free);
+//   3. dequantises its tile exactly to bf16 with the gfx950 conversion
+//      instructions, in one pass that writes the shared buffer and forms the
+//      partial S^T[entry][head] over its 256 dims for all 64 heads on
+//      32x32x16 bf16 MFMA (q^T for 64 heads x 256 dims sits in accumulation
+//      registers for the whole row);
+//   4. hands the partial of head tile 1 - dh to its partner (e, 1 - dh) and
+//      receives the partner's partial of head tile dh (one LDS exchange,
+//      one barrier);
+//   5. runs the online softmax (fp32, log2 domain) for entry tile e x head
 //      tile dh and publishes P (bf16, in the accumulator's lane order) with
-//      the tile's reference max and sum.
-// Two barriers per chunk order the exchange and the publication.  Every wave
-// keeps the running max and sum of all 64 heads, updated identically in all
-// four waves from the published per-tile values.  The reference max moves
-// only when a tile's max exceeds it by more than kLazyRescale, so the
-// accumulators are rarely rescaled.
+//      the tile's reference max and sum (a third barrier).
+// Every wave keeps the running max and sum of all 64 heads, updated
+// identically in all four waves from the published per-tile values.  The
+// reference max moves only when a tile's max exceeds it by more than
+// kLazyRescale, so the accumulators are rarely rescaled.
 // LDS rows are 1024 bytes (one entry); 16-byte chunk k of row r sits at
 // k ^ kswz(r), which keeps the row-wise stores and the transposing reads free
 // of bank conflicts.  Before the first chunk and after the last one the same

@@ -173,17 +173,20 @@ struct Wg {
 
   // As find_rank_bin, with each thread's PER bins already in registers: v[i]
   // holds bin nbins - 1 - (t PER + i) (descending) or t PER + i.  Also
-  // returns the found bin's count, so no bin is read from memory again.
+  // returns the found bin's count, so no bin is read from memory again, and
+  // (if `total` is given) the sum of all bins modulo 2^32.  When rank exceeds
+  // that sum the returned bin and counts are meaningless.
   template <int PER>
   __device__ static int find_rank_bin_regs(const uint32_t (&v)[PER], int nbins, uint32_t rank,
                                            bool descending, uint32_t* wb, uint32_t* before,
-                                           uint32_t* count) {
+                                           uint32_t* count, uint32_t* total = nullptr) {
     const int t = threadIdx.x;
     uint32_t s = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) s += v[i];
     uint32_t tot;
     uint32_t p = excl_scan(s, wb, &tot);
+    if (total != nullptr) *total = tot;
     if (p < rank && rank <= p + s) {
 #pragma unroll
       for (int i = 0; i < PER; ++i) {

@@ -23,27 +23,18 @@
 //     workgroup per row; rows of up to 73,728 items are held in registers.
 // Workgroups never wait on each other inside a kernel: kernel boundaries
 // order the phases (a device-wide fence per workgroup would write back a
-// whole L2).  The histograms are cleared by a fill kernel at the start of
-// each call, so a workspace needs no initialisation.
+// whole L2).  The block Top-K histograms are accumulated with atomics, so
+// they must start at zero: the final kernel clears them after reading, which
+// leaves a workspace ready for the next call without a clearing kernel.  It
+// also checks their totals (the visible block count, the candidate count);
+// a workspace that did not start at zero fails that check, and the row is
+// then selected exactly by radix passes over all its blocks.
 #include "csa2_launch.h"
 #include "index_core.h"
 #include "select_common.h"
 
 namespace csa2 {
 namespace {
-
-__global__ void k_fill_zero(uint32_t* __restrict__ p, size_t n) {
-  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
-       i += static_cast<size_t>(gridDim.x) * blockDim.x)
-    p[i] = 0u;
-}
-
-hipError_t fill_zero(uint32_t* p, size_t n, hipStream_t stream) {
-  const size_t want = (n + 255) / 256;
-  const int blocks = static_cast<int>(want < 1024 ? want : 1024);
-  hipLaunchKernelGGL(k_fill_zero, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, stream, p, n);
-  return hipGetLastError();
-}
 
 // ---------------------------------------------------------------------------
 // Block Top-K: k_bt_hist -> k_bt_filter -> k_bt_final.  Workgroups never
@@ -156,7 +147,8 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_filter(const float* __restric
 // One workgroup per row: second-level bin b2 of bits [19:8] inside b1, the
 // exact threshold inside bucket (b1, b2), an LDS bitmap of the selection and
 // its compaction in block-id order.
-__global__ __launch_bounds__(kBtThreads) void k_bt_final(const int32_t* __restrict__ vis_len,
+__global__ __launch_bounds__(kBtThreads) void k_bt_final(const float* __restrict__ bm,
+                                                         const int32_t* __restrict__ vis_len,
                                                          int N_cap, int k, BtWs ws,
                                                          int32_t* __restrict__ out) {
   __shared__ uint32_t fkey[kBtFinalCap];
@@ -173,8 +165,8 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const int32_t* __restri
   // Both histograms, the filter workgroups' counts and the visible length
   // are loaded in one batch (one memory latency); the histograms are
   // searched in registers.
-  const uint32_t* gh = ws.hist + static_cast<size_t>(r) * kHistBins;
-  const uint32_t* gh2 = ws.hist2 + static_cast<size_t>(r) * kHistBins;
+  uint32_t* gh = ws.hist + static_cast<size_t>(r) * kHistBins;
+  uint32_t* gh2 = ws.hist2 + static_cast<size_t>(r) * kHistBins;
   constexpr int kPerBin = kHistBins / kBtThreads;
   static_assert(kHistBins % kBtThreads == 0, "whole bins per thread");
   static_assert(kBtMaxWgs == 128, "two filter workgroups per lane of the first wave");
@@ -195,12 +187,19 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const int32_t* __restri
     return;
   }
   const uint32_t need = static_cast<uint32_t>(k);
-  uint32_t above, n1;
-  const int b1 = W::find_rank_bin_regs(h1, kHistBins, need, true, wb, &above, &n1);
+  uint32_t above, n1, tot1;
+  const int b1 = W::find_rank_bin_regs(h1, kHistBins, need, true, wb, &above, &n1, &tot1);
   const uint32_t rem1 = need - above;
-  uint32_t above2, n2;
-  const int b2 = W::find_rank_bin_regs(h2, kHistBins, rem1, true, wb, &above2, &n2);
+  uint32_t above2, n2, tot2;
+  const int b2 = W::find_rank_bin_regs(h2, kHistBins, rem1, true, wb, &above2, &n2, &tot2);
   const uint32_t rem2 = rem1 - above2;
+  // Both histograms are left zeroed for the next call: each thread clears
+  // the bins it read.
+#pragma unroll
+  for (int i = 0; i < kPerBin; ++i) {
+    gh[kHistBins - 1 - (tid * kPerBin + i)] = 0u;
+    gh2[kHistBins - 1 - (tid * kPerBin + i)] = 0u;
+  }
 
   // Prefix offsets of the filter workgroups' segments (nwg <= kBtMaxWgs).
   const int nwg = (n + kBtItems - 1) / kBtItems;
@@ -229,98 +228,120 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const int32_t* __restri
   for (int w = tid; w < nwords; w += kBtThreads) bitmap[w] = 0u;
   __syncthreads();
   const uint32_t n_sure = off_s[nwg], n_cand = off_c[nwg];
-  // Flattened item g (< off[nwg]) -> (segment w, slot g - off[w]): the last
-  // w with off[w] <= g, by a fixed-step binary search without branches
-  // (independent searches interleave).
-  auto locate = [&](const uint32_t* off, uint32_t g) {
-    int lo = 0;
+  // The histograms were complete and started from zero exactly when their
+  // totals are the visible block count and the candidate count.  Otherwise
+  // (a workspace not left zeroed by a previous call) the threshold is
+  // resolved exactly over the whole row instead.
+  const bool clean = tot1 == static_cast<uint32_t>(n) && tot2 == n_cand;
+  if (clean) {
+    // Flattened item g (< off[nwg]) -> (segment w, slot g - off[w]): the last
+    // w with off[w] <= g, by a fixed-step binary search without branches
+    // (independent searches interleave).
+    auto locate = [&](const uint32_t* off, uint32_t g) {
+      int lo = 0;
 #pragma unroll
-    for (int step = kBtMaxWgs / 2; step > 0; step >>= 1)
-      lo = off[lo + step] <= g ? lo + step : lo;
-    return static_cast<size_t>(r) * nb_cap + static_cast<size_t>(lo) * kBtItems + (g - off[lo]);
-  };
-  // The sure items (fewer than need <= 2048, i.e. at most two per thread) and
-  // the first batch of candidates are loaded together; items past the end
-  // read slot 0 of their row's first segment and are ignored.
-  static_assert(kMaxPoolBlocks <= 2 * kBtThreads, "two sure items per thread");
-  int sid_v[2];
+      for (int step = kBtMaxWgs / 2; step > 0; step >>= 1)
+        lo = off[lo + step] <= g ? lo + step : lo;
+      return static_cast<size_t>(r) * nb_cap + static_cast<size_t>(lo) * kBtItems + (g - off[lo]);
+    };
+    // The sure items (fewer than need <= 2048, i.e. at most two per thread) and
+    // the first batch of candidates are loaded together; items past the end
+    // read slot 0 of their row's first segment and are ignored.
+    static_assert(kMaxPoolBlocks <= 2 * kBtThreads, "two sure items per thread");
+    int sid_v[2];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const uint32_t g = tid + u * kBtThreads;
-    sid_v[u] = ws.sure[locate(off_s, g < n_sure ? g : 0u)];
-  }
-  auto cand_batch = [&](uint32_t base, uint32_t key, int id) {
-    const uint32_t g = base + tid;
-    const bool in = g < n_cand;
-    const int mb = static_cast<int>(mid_bits(key));
-    if (in && mb > b2) atomicOr(&bitmap[id >> 5], 1u << (id & 31));
-    const bool fin = in && mb == b2;
-    const uint32_t slot = wave_append(fin, &fcount);
-    if (fin && slot < static_cast<uint32_t>(kBtFinalCap)) {
-      fkey[slot] = key;
-      fid[slot] = id;
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t g = tid + u * kBtThreads;
+      sid_v[u] = ws.sure[locate(off_s, g < n_sure ? g : 0u)];
     }
-  };
-  {
-    // The first kCandBatches batches of candidates are loaded in one go too.
-    constexpr int kCandBatches = 4;
-    uint32_t ck[kCandBatches];
-    int ci[kCandBatches];
-#pragma unroll
-    for (int u = 0; u < kCandBatches; ++u) {
-      const uint32_t g = u * kBtThreads + tid;
-      const size_t at = locate(off_c, g < n_cand ? g : 0u);
-      ck[u] = ws.ckey[at];
-      ci[u] = ws.cid[at];
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      if (tid + u * kBtThreads < n_sure) atomicOr(&bitmap[sid_v[u] >> 5], 1u << (sid_v[u] & 31));
-#pragma unroll
-    for (int u = 0; u < kCandBatches; ++u)
-      if (u * kBtThreads < static_cast<int>(n_cand)) cand_batch(u * kBtThreads, ck[u], ci[u]);
-  }
-  for (uint32_t base = 4 * kBtThreads; base < n_cand; base += kBtThreads) {
-    const uint32_t g = base + tid;
-    const size_t at = locate(off_c, g < n_cand ? g : 0u);
-    cand_batch(base, ws.ckey[at], ws.cid[at]);
-  }
-  __syncthreads();
-  const uint32_t prefix = (static_cast<uint32_t>(b1) << kHistShift) | (static_cast<uint32_t>(b2) << 8);
-  uint32_t kstar;
-  int32_t istar;
-  if (n2 <= static_cast<uint32_t>(kBtFinalCap)) {
-    W::resolve(ArrayCand{fkey, fid, n2}, prefix, 8, rem2, hist256, wb, &kstar, &istar);
-    for (uint32_t c = tid; c < n2; c += kBtThreads)
-      if (selected(fkey[c], fid[c], kstar, istar)) atomicOr(&bitmap[fid[c] >> 5], 1u << (fid[c] & 31));
-  } else {
-    // Degenerate input (a huge bucket of equal high bits): resolve by
-    // re-reading the candidate segments.
-    struct SegCand {
-      const uint32_t* ckey;
-      const int32_t* cid;
-      const uint32_t* off;
-      int nwg;
-      size_t base;
-      uint32_t n;
-      __device__ size_t at(uint32_t g) const {
-        int lo = 0, hi = nwg;
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (off[mid] <= g) lo = mid; else hi = mid;
-        }
-        return base + static_cast<size_t>(lo) * kBtItems + (g - off[lo]);
+    auto cand_batch = [&](uint32_t base, uint32_t key, int id) {
+      const uint32_t g = base + tid;
+      const bool in = g < n_cand;
+      const int mb = static_cast<int>(mid_bits(key));
+      if (in && mb > b2) atomicOr(&bitmap[id >> 5], 1u << (id & 31));
+      const bool fin = in && mb == b2;
+      const uint32_t slot = wave_append(fin, &fcount);
+      if (fin && slot < static_cast<uint32_t>(kBtFinalCap)) {
+        fkey[slot] = key;
+        fid[slot] = id;
       }
-      __device__ uint32_t key(uint32_t g) const { return ckey[at(g)]; }
-      __device__ int32_t id(uint32_t g) const { return cid[at(g)]; }
-    } sc{ws.ckey, ws.cid, off_c, nwg, static_cast<size_t>(r) * nb_cap, n_cand};
-    W::resolve(sc, prefix, 8, rem2, hist256, wb, &kstar, &istar);
-    for (uint32_t g = tid; g < n_cand; g += kBtThreads) {
-      const uint32_t key = sc.key(g);
-      const int id = sc.id(g);
-      if ((key & 0xffffff00u) == prefix && selected(key, id, kstar, istar))
-        atomicOr(&bitmap[id >> 5], 1u << (id & 31));
+    };
+    {
+      // The first kCandBatches batches of candidates are loaded in one go too.
+      constexpr int kCandBatches = 4;
+      uint32_t ck[kCandBatches];
+      int ci[kCandBatches];
+#pragma unroll
+      for (int u = 0; u < kCandBatches; ++u) {
+        const uint32_t g = u * kBtThreads + tid;
+        const size_t at = locate(off_c, g < n_cand ? g : 0u);
+        ck[u] = ws.ckey[at];
+        ci[u] = ws.cid[at];
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (tid + u * kBtThreads < n_sure) atomicOr(&bitmap[sid_v[u] >> 5], 1u << (sid_v[u] & 31));
+#pragma unroll
+      for (int u = 0; u < kCandBatches; ++u)
+        if (u * kBtThreads < static_cast<int>(n_cand)) cand_batch(u * kBtThreads, ck[u], ci[u]);
     }
+    for (uint32_t base = 4 * kBtThreads; base < n_cand; base += kBtThreads) {
+      const uint32_t g = base + tid;
+      const size_t at = locate(off_c, g < n_cand ? g : 0u);
+      cand_batch(base, ws.ckey[at], ws.cid[at]);
+    }
+    __syncthreads();
+    const uint32_t prefix =
+        (static_cast<uint32_t>(b1) << kHistShift) | (static_cast<uint32_t>(b2) << 8);
+    uint32_t kstar;
+    int32_t istar;
+    if (n2 <= static_cast<uint32_t>(kBtFinalCap)) {
+      W::resolve(ArrayCand{fkey, fid, n2}, prefix, 8, rem2, hist256, wb, &kstar, &istar);
+      for (uint32_t c = tid; c < n2; c += kBtThreads)
+        if (selected(fkey[c], fid[c], kstar, istar))
+          atomicOr(&bitmap[fid[c] >> 5], 1u << (fid[c] & 31));
+    } else {
+      // Degenerate input (a huge bucket of equal high bits): resolve by
+      // re-reading the candidate segments.
+      struct SegCand {
+        const uint32_t* ckey;
+        const int32_t* cid;
+        const uint32_t* off;
+        int nwg;
+        size_t base;
+        uint32_t n;
+        __device__ size_t at(uint32_t g) const {
+          int lo = 0, hi = nwg;
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (off[mid] <= g) lo = mid; else hi = mid;
+          }
+          return base + static_cast<size_t>(lo) * kBtItems + (g - off[lo]);
+        }
+        __device__ uint32_t key(uint32_t g) const { return ckey[at(g)]; }
+        __device__ int32_t id(uint32_t g) const { return cid[at(g)]; }
+      } sc{ws.ckey, ws.cid, off_c, nwg, static_cast<size_t>(r) * nb_cap, n_cand};
+      W::resolve(sc, prefix, 8, rem2, hist256, wb, &kstar, &istar);
+      for (uint32_t g = tid; g < n_cand; g += kBtThreads) {
+        const uint32_t key = sc.key(g);
+        const int id = sc.id(g);
+        if ((key & 0xffffff00u) == prefix && selected(key, id, kstar, istar))
+          atomicOr(&bitmap[id >> 5], 1u << (id & 31));
+      }
+    }
+  } else {
+    struct RowCand {
+      const float* row;
+      uint32_t n;
+      __device__ uint32_t key(uint32_t i) const { return float_to_key(row[i]); }
+      __device__ int32_t id(uint32_t i) const { return static_cast<int32_t>(i); }
+    } rc{bm + static_cast<size_t>(r) * nb_cap, static_cast<uint32_t>(n)};
+    uint32_t kstar;
+    int32_t istar;
+    W::resolve(rc, 0u, 32, need, hist256, wb, &kstar, &istar);
+    for (uint32_t i = tid; i < rc.n; i += kBtThreads)
+      if (selected(rc.key(i), static_cast<int32_t>(i), kstar, istar))
+        atomicOr(&bitmap[i >> 5], 1u << (i & 31));
   }
   __syncthreads();
   const int wpt = (nwords + kBtThreads - 1) / kBtThreads;
@@ -951,15 +972,15 @@ hipError_t launch_block_topk(const float* block_max, const int32_t* vis_len, int
   w.sure = reinterpret_cast<int32_t*>(w.wgcnt + static_cast<size_t>(rows) * kBtMaxWgs * 2);
   w.ckey = reinterpret_cast<uint32_t*>(w.sure + static_cast<size_t>(rows) * nb_cap);
   w.cid = reinterpret_cast<int32_t*>(w.ckey + static_cast<size_t>(rows) * nb_cap);
-  hipError_t e = fill_zero(w.hist, static_cast<size_t>(rows) * 2 * kHistBins, stream);
-  if (e != hipSuccess) return e;
+  hipError_t e;
   dim3 grid(static_cast<unsigned>((nb_cap + kBtItems - 1) / kBtItems), rows);
   hipLaunchKernelGGL(k_bt_hist, grid, dim3(kBtThreads), 0, stream, block_max, vis_len, N_cap, k, w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_bt_filter, grid, dim3(kBtThreads), 0, stream, block_max, vis_len, N_cap, k,
                      w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_bt_final, dim3(rows), dim3(kBtThreads), 0, stream, vis_len, N_cap, k, w, out);
+  hipLaunchKernelGGL(k_bt_final, dim3(rows), dim3(kBtThreads), 0, stream, block_max, vis_len, N_cap,
+                     k, w, out);
   return hipGetLastError();
 }
 

@@ -39,8 +39,10 @@
  *     window slots are skipped.
  *   - Scratch memory comes only from the caller's workspace `ws` of
  *     `ws_bytes` bytes, sized with csa2_workspace_size().  Calls that may run
- *     at the same time must not share a workspace.  The workspace needs no
- *     initialisation: every call clears what it counts in before use.
+ *     at the same time must not share a workspace.  Results never depend on
+ *     its contents on entry.  csa2_block_topk runs fastest on a workspace
+ *     that was zero-filled once when allocated or last used by a
+ *     csa2_block_topk call with the same B * n_q (see there).
  *   - Sizes: N_cap <= 4,194,304 entries (4x the pages' maximum context of
  *     1,048,576 tokens), B * n_q <= 65,535 for the decode-shaped calls.
  *   - The library keeps no state; it is thread-safe.
@@ -151,7 +153,13 @@ CSA2_API csa2_status csa2_index_score(const uint16_t* q_idx, const float* w_idx,
  *   vis_len     [B, n_q] int32
  *   k_blocks    1..2048
  *   pool_blocks [B, n_q, k_blocks] int32 output: ascending block ids, -1 padded
- *   ws          csa2_workspace_size(CSA2_OP_BLOCK_TOPK, ...) bytes (required)
+ *   ws          csa2_workspace_size(CSA2_OP_BLOCK_TOPK, ...) bytes (required).
+ *               Its first 2 * B * n_q * 4096 words are histograms that must
+ *               start at zero; every call leaves them zeroed.  A call that
+ *               finds them not zeroed (their totals do not match the counts
+ *               they must hold) still returns the exact result, by a slower
+ *               exact pass over every visible block of the row.  Zero-fill
+ *               a new workspace once (hipMemset) to avoid that pass.
  */
 CSA2_API csa2_status csa2_block_topk(const float* block_max, const int32_t* vis_len, int32_t B,
                             int32_t n_q, int32_t N_cap, int32_t k_blocks, int32_t* pool_blocks,

@@ -163,6 +163,48 @@ def test_flat_select_long_rows(n):
         _select_case(rows, vis, k, "flat")
 
 
+def test_block_topk_workspace_contents():
+    # The block Top-K histograms live in the workspace and must start at
+    # zero; every call leaves them zeroed.  A workspace that did not start at
+    # zero (garbage, or another row count's layout) must still give the exact
+    # pool, by the slow exact pass, and be left zeroed for the next call.
+    rng = np.random.default_rng(24)
+    n, k = 20000, 2048
+    keys = [rng.standard_normal(n), np.round(rng.standard_normal(n) * 4) / 4,
+            np.full(n, -1.5), rng.standard_normal(n), rng.standard_normal(1000)]
+    vis_rows = [8 * n, 8 * n - 3, 8 * n, 8 * 7001, 8 * 1000]    # the last has n <= k
+    rows = len(keys)
+    arr = torch.zeros(rows, 1, n, dtype=torch.float32)
+    for i, x in enumerate(keys):
+        arr[i, 0, :len(x)] = torch.from_numpy(x.astype(np.float32))
+    bm = arr.cuda()
+    N = 8 * n
+    nbytes = csa.workspace_size(csa.OP_BLOCK_TOPK, rows, 1, N, 0, k)
+    refs = [otopk.block_topk(arr[i, 0].numpy().astype(np.float64)[:(vis_rows[i] + 7) // 8], k)
+            for i in range(rows)]
+
+    def run(r, ws, label):
+        vis = torch.tensor(vis_rows[:r], dtype=torch.int32).reshape(r, 1).cuda()
+        out = torch.full((r, 1, k), -7, dtype=torch.int32, device="cuda")
+        print(f"block_topk workspace case: {label}, rows={r}", flush=True)
+        csa.block_topk(bm[:r], vis, N, k, out, ws=ws)
+        torch.cuda.synchronize()
+        out = _np(out)
+        for i in range(r):
+            assert np.array_equal(out[i, 0], refs[i]), f"{label}: row {i} differs"
+        h = _np(ws[:2 * r * 4096 * 4].view(torch.int32)).reshape(2, r, 4096)
+        for i in range(r):
+            if (vis_rows[i] + 7) // 8 > k:
+                assert not h[:, i].any(), f"{label}: row {i} histograms not left zeroed"
+
+    for fill in (0xA7, 0xFF):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device="cuda")
+        run(rows, ws, f"garbage 0x{fill:02X}")
+        run(rows, ws, "after a call")
+        run(2, ws, "fewer rows")
+        run(rows, ws, "more rows again")
+
+
 def test_pool_topk_stored_scores_exact():
     # FULL mode from stored scores at the pool positions (fp32 keys, exact).
     rng = np.random.default_rng(22)
