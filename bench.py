@@ -218,13 +218,15 @@ def cpu_baseline(name, d, budget_s):
                       f"steps (fp64 numpy, {t_total:.1f} s)"}
 
 
-def traffic_from_profile(dominant, src_hash):
+def traffic_from_profile(dominant, src_hash, workload):
+    # Counters are per launch of one workload's dominant call: they apply only
+    # to that workload and only while the kernel's sources are unchanged.
     path = os.path.join(ROOT, "profiles", f"{dominant}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != src_hash:
+    if rec.get("source_hash") != src_hash or rec.get("workload") != workload:
         return None
     return rec.get("bytes_per_launch")
 
@@ -321,7 +323,7 @@ def main():
     roof["kernel"] = dominant
     roof["per_launch"] = per_launch
     roof["launch_us"] = round(dom_ms * 1e3, 2)
-    roof["traffic"] = traffic_from_profile(dominant, source_hash(dominant))
+    roof["traffic"] = traffic_from_profile(dominant, source_hash(dominant), args.workload)
 
     cpu = None
     if not args.no_cpu_baseline:
