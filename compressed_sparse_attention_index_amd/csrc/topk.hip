@@ -540,7 +540,13 @@ __global__ __launch_bounds__(kPsThreads) void k_pool_final(PoolArgs a) {
     for (int e = 0; e < kPer; ++e) {
       const int bv = min(kPfBins - 1, max(0, static_cast<int>((sv[e] - vlo) * scale)));
       bin[e] = ((vm >> e) & 1u) ? bv : kPfBins;
-      atomicAdd(&hist[bin[e]], 1u);
+    }
+    // A wave without a valid slot (a pool of fewer than 2,048 blocks leaves
+    // whole waves empty) adds nothing: its 1,024 atomics would all hit the
+    // spare bin one after another.
+    if (__ballot(vm != 0u) != 0) {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) atomicAdd(&hist[bin[e]], 1u);
     }
     __syncthreads();
     uint32_t above;
