@@ -69,6 +69,8 @@ constexpr int kMaxSplits = 64;
 constexpr int kMaxChunks = (kMaxTopK + kMaxWindow + kChunk - 1) / kChunk;
 constexpr float kLazyRescale = 8.0f;
 static_assert(kMaxChunks <= kMaxSplits, "a row splits at most once per chunk");
+constexpr int kCombineHeads = 4;   // heads (one wave each) per split-merge workgroup
+static_assert(kHeads % kCombineHeads == 0, "whole head groups");
 
 struct AttnArgs {
   const uint16_t* q;
@@ -595,16 +597,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
   }
 }
 
-// Merge of split partials in split order: one workgroup per (row, head),
-// 64 threads x 8 dims.  A row has at most S splits (S = 4, or kMaxChunks:
-// one chunk at least per split), so every split's partial output and (m, l)
-// are loaded at once (lane s < nsplit fetches split s's (m, l)); the merge
-// weights are formed in registers.
+// Merge of split partials in split order: one wave per (row, head), 64
+// lanes x 8 dims, kCombineHeads heads of a row per workgroup.  A row has at
+// most S splits (S = 4, or kMaxChunks: one chunk at least per split), so
+// every split's partial output and (m, l) are loaded at once (lane s <
+// nsplit fetches split s's (m, l)); the merge weights are formed in
+// registers.
 template <int S>
-__global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
-  const int r = blockIdx.x / kHeads;
-  const int head = blockIdx.x % kHeads;
-  const int t = threadIdx.x;
+__global__ __launch_bounds__(64 * kCombineHeads) void k_attn_combine(AttnArgs a) {
+  const int r = blockIdx.x / (kHeads / kCombineHeads);
+  const int head = blockIdx.x % (kHeads / kCombineHeads) * kCombineHeads +
+                   __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t = threadIdx.x & 63;
   const size_t ps0 = static_cast<size_t>(r) * a.nsplit;
   u32x4 u[S];
 #pragma unroll
@@ -696,10 +700,11 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* kv_fp4, const ui
                      a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.nsplit == 1) return err;
+  const dim3 cgrid(rows * (kHeads / kCombineHeads)), cblock(64 * kCombineHeads);
   if (a.nsplit <= 4)
-    hipLaunchKernelGGL(k_attn_combine<4>, dim3(rows * kHeads), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(k_attn_combine<4>, cgrid, cblock, 0, stream, a);
   else
-    hipLaunchKernelGGL(k_attn_combine<kMaxChunks>, dim3(rows * kHeads), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(k_attn_combine<kMaxChunks>, cgrid, cblock, 0, stream, a);
   return hipGetLastError();
 }
 
