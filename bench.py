@@ -14,6 +14,7 @@ Prints ONE JSON line on stdout; diagnostics go to stderr.
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -55,10 +56,15 @@ def parse():
 
 
 def source_hash(kernel):
+    """Hash of the code of a kernel's sources: comments and layout are left out,
+    since they do not change what the counters measured."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "compressed_sparse_attention_index_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "compressed_sparse_attention_index_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(l.strip() for l in text.splitlines() if l.strip()).encode())
     return h.hexdigest()[:16]
 
 

@@ -6,24 +6,25 @@
 // over 32 heads of 128 dims; a prefill query sees only its own visible prefix
 // (vis_len[j] entries).
 //
-// Work decomposition.  A workgroup (4 waves) takes 32 query rows of one
-// sequence (8 per wave) and a range of 64-key tiles.  Every key tile is
-// copied once from memory into a 4-slot LDS ring with direct-to-LDS loads
-// (each wave issues its share; waits counted by hand; one LDS barrier per
-// tile) and read by all four waves, so each key is fetched once per 32 query
-// rows.  A tile is worked on in two 32-key halves.  A wave keeps the A operands of its 8 query rows (32 heads x 128
-// dims each) in accumulation registers for the whole range.  Per tile and
-// row and half it runs 16 steps of v_mfma_f32_16x16x32_bf16 (two 16-head blocks x two
-// 16-key blocks x four 32-dim steps).  In that shape a lane holds 8 heads of
-// 2 keys, so a row needs only 8 head weights in registers, which leaves room
-// for a second accumulator set and for the next tile's B operands: the
-// ReLU-weighted head sum of one row runs on the vector ALU while the matrix
-// core works on the next row, and the LDS reads of the next half are in
-// flight while the current half is worked on.  Lane partial sums are combined across the four
-// 16-lane groups with two lane-swap steps that also pack two rows into one
-// 64-lane store.  Workgroup ids are ordered so that the key chunk varies
-// fastest: with a multiple of 8 chunks each XCD always works on the same key
-// chunk, which stays in its L2.
+// Work decomposition.  A workgroup (4 waves) takes 16 query rows of one
+// sequence (4 per wave) and a range of 64-key tiles; two workgroups share a
+// compute unit (two waves per SIMD).  Every key tile is copied once from
+// memory into a 4-slot LDS ring with direct-to-LDS loads (each wave issues
+// its share; waits counted by hand; one LDS barrier per tile) and read by all
+// four waves, so each key is fetched once per 16 query rows.  A wave keeps
+// the A operands of its 4 query rows (32 heads x 128 dims each) in
+// accumulation registers for the whole range.  Keys are worked on in
+// quarters of 16: per row and quarter, 8 steps of v_mfma_f32_16x16x32_bf16
+// (two 16-head blocks x four 32-dim steps).  In that shape a lane holds 8
+// heads of one key, so a row needs only 8 head weights in registers, which
+// is what lets two waves share a SIMD: the ReLU-weighted head sums of one
+// wave run on the vector ALU while the matrix core works for the other.
+// The B operands of the next quarter are read from LDS while the current
+// one is worked on.  Per 32-key half tile, lane partial sums are combined
+// across the four 16-lane groups with two lane-swap steps that also pack two
+// rows into one 64-lane store.  Workgroup ids are ordered so that the key
+// chunk varies fastest: with a multiple of 8 chunks each XCD always works on
+// the same key chunk, which stays in its L2.
 #include "csa2_launch.h"
 #include "index_core.h"
 
