@@ -17,8 +17,9 @@
 //     compacts it in id order.
 //   pool Top-K   (k_pool_score, k_pool_final): the pool positions are
 //     re-scored on matrix cores (or stored scores are read); one workgroup
-//     per row holds every slot's key in LDS, selects, and compacts in slot
-//     order (= position order).
+//     per row holds every slot's score in registers (16 per thread), finds
+//     the threshold bin of a value-linear histogram, resolves it exactly,
+//     and compacts the selection in slot order (= position order).
 //   flat Top-K   (k_flat_select_reg, k_flat_select; prefill rows): one
 //     workgroup per row; rows of up to 73,728 items are held in registers.
 // Workgroups never wait on each other inside a kernel: kernel boundaries
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const float* __restrict
 // ---------------------------------------------------------------------------
 // Pool Top-K: k_pool_score re-scores the pool positions (Reindex, or Full
 // without stored scores) into a pool-score array; k_pool_final (one
-// workgroup per row) loads every slot's key into LDS and selects there.
+// workgroup per row) holds every slot's score in registers and selects.
 constexpr int kPsThreads = 1024;                // selection workgroup
 constexpr int kPscThreads = 256;                // scoring workgroup: 4 waves x 2 tiles
 constexpr int kPscWaves = kPscThreads / 64;
