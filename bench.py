@@ -23,6 +23,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+APPEND_METRIC = "KV append tokens/s (MXFP4 main KV + FP8 window); % of HBM GB/s roofline"
 METRIC = "CSA2 decode query-tokens/s at 128K and 1M ctx; % of HBM GB/s roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
@@ -32,6 +33,7 @@ KERNEL_SOURCES = {
     "index_scan": ["index_score.hip", "index_core.h", "csa2_device.h"],
     "sparse_attn": ["attention.hip", "csa2_device.h"],
     "index_gemm": ["index_gemm.hip", "index_core.h", "csa2_device.h"],
+    "kv_append": ["kv_append.hip", "csa2_device.h"],
 }
 
 
@@ -45,7 +47,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="full_reindex_1m",
-                   choices=["tiny_2k", "full_64k", "reuse_128k", "full_reindex_1m", "prefill_128k"])
+                   choices=["tiny_2k", "full_64k", "reuse_128k", "full_reindex_1m", "prefill_128k",
+                            "kv_append_64k"])
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU time budget of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -78,6 +81,9 @@ class Step:
         self.B, self.n_q = B, n_q
         self.rows = B * n_q
         self.N = d["kv_fp4"].shape[1]
+        if name == "kv_append_64k":
+            self.rows = B * d["n_new"]   # tokens appended per step
+            return
         z = lambda *s, dt=torch.int32: torch.empty(*s, dtype=dt, device=dev)
         self.out = z(B, n_q, 64, 512, dt=torch.int16)
         self.lse = z(B, n_q, 64, dt=torch.float32)
@@ -111,7 +117,9 @@ class Step:
 
     def dominant(self):
         """Launch only the kernel the roofline figure is about."""
-        if self.name == "reuse_128k":
+        if self.name == "kv_append_64k":
+            self.run()
+        elif self.name == "reuse_128k":
             d = self.d
             self._attn(self.csa.reuse_attn, d["q"], d["swa"], d["idx"], self.out, self.lse)
         else:
@@ -124,6 +132,10 @@ class Step:
 
     def run(self):
         d, csa = self.d, self.csa
+        if self.name == "kv_append_64k":
+            csa.kv_append(d["kv_new"], d["pos"], d["kv_fp4"], d["kv_scale"], swa_new=d["swa_new"],
+                          swa_kv=d["swa"], swa_pos0=d["swa_pos0"])
+            return
         if self.name == "reuse_128k":
             self._attn(csa.reuse_attn, d["q"], d["swa"], d["idx"], self.out, self.lse)
             return
@@ -146,6 +158,11 @@ class Step:
 def algorithmic(name, d):
     """(dominant kernel, its bytes or flops per launch, bound, step bytes) by definition."""
     B, n_q = d["B"], d["n_q"]
+    if name == "kv_append_64k":
+        # Per token: the bf16 main entry read, its MXFP4 row written; per
+        # window row: the bf16 entry read, its FP8 row written; pos, swa_pos0.
+        per = B * (d["n_new"] * (1024 + 256 + 16) + d["swa"].shape[1] * (1024 + 512) + 8)
+        return "kv_append", per, "hbm", per
     attn_bytes = 512 * 272 + 128 * 512 + 64 * 512 * 2 * 2 + 512 * 4 + 64 * 4   # per query row
     if name == "reuse_128k":
         per = B * attn_bytes
@@ -176,6 +193,25 @@ def cpu_baseline(name, d, budget_s):
 
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     B, n_q = d["B"], d["n_q"]
+    if name == "kv_append_64k":
+        # Chunks of the first sequence's tokens through the oracle's append.
+        kv, sw = npy(d["kv_new"][0]).view(np.uint16), npy(d["swa_new"][0]).view(np.uint16)
+        n_new, s_cap, chunk = d["n_new"], d["swa"].shape[1], 1024
+        done, t_total = 0, 0.0
+        while done < n_new and t_total < budget_s:
+            m = min(chunk, n_new - done)
+            fp4 = np.zeros((1, n_new, 256), np.uint8)
+            sc = np.zeros((1, n_new, 16), np.uint8)
+            swa = np.zeros((1, s_cap, 512), np.uint8)
+            t0 = time.perf_counter()
+            pipeline.kv_append(fp4, sc, swa, kv[None, done:done + m], sw[None, done:done + m],
+                               np.array([done]), np.array([n_new - s_cap]))
+            t_total += time.perf_counter() - t0
+            done += m
+        return {"value": done / t_total, "unit": "tokens/s", "cores": int(threads),
+                "kind": "oracle",
+                "sample": f"the first {done} of {B * n_new} appended tokens (sequence 0), "
+                          f"{chunk} per call (fp64 numpy, {t_total:.1f} s)"}
     rows = [(b, j) for b in range(B) for j in range(n_q)]
     done, t_total = 0, 0.0
     for b, j in rows:
@@ -316,7 +352,9 @@ def main():
         del src, dst
 
     dominant, per_launch, bound, step_bytes = algorithmic(args.workload, d)
-    rows = d["B"] * d["n_q"]
+    append = args.workload == "kv_append_64k"
+    rows = step.rows
+    unit = "tokens/s" if append else "query-tokens/s"
     value = rows / (ms / 1e3)
     if bound == "hbm":
         achieved = per_launch / (dom_ms / 1e3) / 1e9
@@ -335,19 +373,25 @@ def main():
     if not args.no_cpu_baseline:
         t0 = time.time()
         cpu = cpu_baseline(args.workload, d, args.cpu_seconds)
-        log(f"[bench] oracle baseline: {cpu['value']:.4f} query-tokens/s ({time.time() - t0:.1f} s)")
+        log(f"[bench] oracle baseline: {cpu['value']:.4f} {cpu['unit']} ({time.time() - t0:.1f} s)")
 
     T = d["kv_fp4"].shape[1]
-    cfg = {"workload": args.workload, "batch": d["B"], "query_rows": rows, "context": T,
-           "indexer_k": d.get("kdtype"), "top_k": 512, "pool_blocks": 2048, "window": 128,
-           "layers": {"full_64k": "Full", "tiny_2k": "Full", "reuse_128k": "Reuse",
-                      "full_reindex_1m": "Full+Reindex", "prefill_128k": "prefill (m=2)"}[args.workload]}
+    if append:
+        cfg = {"workload": args.workload, "batch": d["B"], "tokens_per_sequence": d["n_new"],
+               "window": d["swa"].shape[1], "main_kv": "MXFP4 (E2M1 + E8M0/32)", "swa_kv": "FP8 E4M3FN"}
+    else:
+        cfg = {"workload": args.workload, "batch": d["B"], "query_rows": rows, "context": T,
+               "indexer_k": d.get("kdtype"), "top_k": 512, "pool_blocks": 2048, "window": 128,
+               "layers": {"full_64k": "Full", "tiny_2k": "Full", "reuse_128k": "Reuse",
+                          "full_reindex_1m": "Full+Reindex",
+                          "prefill_128k": "prefill (m=2)"}[args.workload]}
     if step_bytes:
         cfg["step_algorithmic_bytes"] = step_bytes
         cfg["step_hbm_frac"] = round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
-    rec = {"metric": METRIC, "value": round(value, 2), "unit": "query-tokens/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+    rec = {"metric": APPEND_METRIC if append else METRIC, "value": round(value, 2), "unit": unit,
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "fp32" if append else "bf16",
            "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu}
     if graph_ms is not None:
         rec["graph_ms_per_step"] = round(graph_ms, 5)

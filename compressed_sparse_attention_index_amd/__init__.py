@@ -15,7 +15,7 @@ __all__ = [
     "KDTYPE_BF16", "KDTYPE_FP8", "MODE_FULL", "MODE_REINDEX", "MODE_REUSE",
     "OP_INDEX_SCORE", "OP_BLOCK_TOPK", "OP_REINDEX_TOPK", "OP_SPARSE_ATTN",
     "Csa2Error", "lib", "abi_version", "workspace_size", "index_score", "block_topk",
-    "reindex_topk", "sparse_attn_decode", "reuse_attn",
+    "reindex_topk", "sparse_attn_decode", "reuse_attn", "kv_append",
 ]
 
 KDTYPE_BF16, KDTYPE_FP8 = 0, 1
@@ -36,6 +36,7 @@ _SIGNATURES = {
     "csa2_sparse_attn_decode": [_P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _F, _P, _I, _I, _P, _P,
                                 _P, _S, _P],
     "csa2_reuse_attn": [_P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _F, _P, _I, _I, _P, _P, _P, _S, _P],
+    "csa2_kv_append": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _I, _P, _P],
     "csa2_workspace_size": [_I, _I, _I, _I, _I, _I],
     "csa2_status_string": [_I],
     "csa2_abi_version": [],
@@ -182,3 +183,16 @@ def sparse_attn_decode(*args, **kw):
 def reuse_attn(*args, **kw):
     """Attention of a Reuse layer (indices from an earlier layer, no indexer)."""
     _attn("csa2_reuse_attn", *args, **kw)
+
+
+def kv_append(kv_new, pos, kv_fp4, kv_scale, swa_new=None, swa_kv=None, swa_pos0=None,
+              stream=None):
+    """Encodes new tokens' entries (kv_new [B, n_new, 512] bf16 -> MXFP4 rows
+    pos[b] + i of kv_fp4 / kv_scale; swa_new -> FP8 rows of swa_kv)."""
+    B, n_new = kv_new.shape[0], kv_new.shape[1]
+    N_cap = kv_fp4.shape[1]
+    S_cap = swa_kv.shape[1] if swa_kv is not None else 0
+    _call("csa2_kv_append", _ptr(kv_new, _BITS16, "kv_new"), _ptr(swa_new, _BITS16, "swa_new"),
+          _ptr(pos, _I32, "pos"), B, n_new, N_cap, _ptr(kv_fp4, _U8, "kv_fp4"),
+          _ptr(kv_scale, _U8, "kv_scale"), _ptr(swa_kv, _U8, "swa_kv"), S_cap,
+          _ptr(swa_pos0, _I32, "swa_pos0"), _stream(stream))

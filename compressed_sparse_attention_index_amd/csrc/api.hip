@@ -156,6 +156,22 @@ csa2_status csa2_reuse_attn(const uint16_t* q, const uint8_t* kv_fp4, const uint
                      sm_scale, opts, B, n_q, out, lse, ws, ws_bytes, stream);
 }
 
+csa2_status csa2_kv_append(const uint16_t* kv_new, const uint16_t* swa_new, const int32_t* pos,
+                           int32_t B, int32_t n_new, int32_t N_cap, uint8_t* kv_fp4,
+                           uint8_t* kv_scale, uint8_t* swa_kv, int32_t S_cap,
+                           const int32_t* swa_pos0, hipStream_t stream) {
+  if (!kv_new || !pos || !kv_fp4 || !kv_scale) return CSA2_ERR_NULL;
+  if (swa_new && (!swa_kv || !swa_pos0)) return CSA2_ERR_NULL;
+  csa2_status st = check_rows(B, n_new);
+  if (st != CSA2_OK) return st;
+  if (N_cap < 1 || N_cap > kMaxNcap || S_cap < 0) return CSA2_ERR_SHAPE;
+  const void* ptrs[] = {kv_new, swa_new, pos, kv_fp4, kv_scale, swa_kv, swa_pos0};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return CSA2_ERR_ALIGN;
+  return from_hip(csa2::launch_kv_append(kv_new, swa_new, pos, B, n_new, N_cap, kv_fp4, kv_scale,
+                                         swa_new ? swa_kv : nullptr, S_cap, swa_pos0, stream));
+}
+
 size_t csa2_workspace_size(csa2_op op, int32_t B, int32_t n_q, int32_t N_cap, int32_t top_k,
                            int32_t k_blocks) {
   if (B < 1 || n_q < 1 || N_cap < 1) return static_cast<size_t>(-1);

@@ -44,4 +44,11 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* kv_fp4, const ui
                               float sm_scale, int window, int replay_start, int B, int n_q,
                               uint16_t* out, float* lse, void* ws, hipStream_t stream);
 
+// KV append: MXFP4 main entries and FP8 window entries of new tokens; see
+// kv_append.hip.
+hipError_t launch_kv_append(const uint16_t* kv_new, const uint16_t* swa_new, const int32_t* pos,
+                            int B, int n_new, int N_cap, uint8_t* kv_fp4, uint8_t* kv_scale,
+                            uint8_t* swa, int S_cap, const int32_t* swa_pos0,
+                            hipStream_t stream);
+
 }  // namespace csa2

@@ -258,6 +258,37 @@ CSA2_API csa2_status csa2_reuse_attn(const uint16_t* q, const uint8_t* kv_fp4, c
                             int32_t B, int32_t n_q, uint16_t* out, float* lse, void* ws,
                             size_t ws_bytes, hipStream_t stream);
 
+/*
+ * csa2_kv_append -- encode and store the KV entries of new tokens.
+ *   For sequence b and new token i < n_new at position p = pos[b] + i:
+ *     main KV    if 0 <= p < N_cap:  kv_fp4[b][p], kv_scale[b][p] <- MXFP4 of kv_new[b][i]
+ *     window KV  if swa_new != NULL and 0 <= p - swa_pos0[b] < S_cap:
+ *                swa_kv[b][p - swa_pos0[b]] <- FP8 E4M3FN of swa_new[b][i]
+ *   Positions outside a cache are skipped.  ("DeepSeek-V4.1-Flash 架构详解",
+ *   §4: main KV is stored as MXFP4, SWA KV as FP8.)  Encoding (OCP MX v1.0,
+ *   OCP FP8):
+ *     MXFP4: per 32 elements X = floor(log2(max |v|)) - 2 clamped to
+ *       [-127, 127] (-127 for an all-zero block), E8M0 code X + 127; each
+ *       v / 2^X rounds to the nearest E2M1 value, ties to the even code,
+ *       saturating at 6; a value that rounds to zero is stored as +0.
+ *     FP8: saturate to +-448, round to nearest, ties to even; the sign is
+ *       kept for values that round to zero.
+ *   Inputs must be finite (a non-finite value leaves its block's or
+ *   element's codes unspecified).  The caches' layouts are those the
+ *   attention entry points read.
+ * Arguments
+ *   kv_new    [B, n_new, 512] bf16 main-KV entries
+ *   swa_new   [B, n_new, 512] bf16 window entries, or NULL (no window writes)
+ *   pos       [B] int32 position of each sequence's first new token
+ *   kv_fp4    [B, N_cap, 256] uint8, kv_scale [B, N_cap, 16] uint8 (written)
+ *   swa_kv    [B, S_cap, 512] uint8 (written; may be NULL when swa_new is)
+ *   swa_pos0  [B] int32 (may be NULL when swa_new is)
+ */
+CSA2_API csa2_status csa2_kv_append(const uint16_t* kv_new, const uint16_t* swa_new,
+                           const int32_t* pos, int32_t B, int32_t n_new, int32_t N_cap,
+                           uint8_t* kv_fp4, uint8_t* kv_scale, uint8_t* swa_kv, int32_t S_cap,
+                           const int32_t* swa_pos0, hipStream_t stream);
+
 /* Workspace bytes an operation needs for the given sizes (0 if none);
    returns (size_t)-1 for an unknown op or invalid sizes. */
 CSA2_API size_t csa2_workspace_size(csa2_op op, int32_t B, int32_t n_q, int32_t N_cap, int32_t top_k,

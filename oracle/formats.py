@@ -92,3 +92,66 @@ def mxfp4_to_f64(fp4_bytes, scales):
     vals = e2m1_to_f64(nib)
     scale = np.repeat(e8m0_to_f64(sc), 32, axis=-1)
     return vals * scale
+
+
+# ---------------------------------------------------------------------------
+# Encoding (the KV append step: [架构详解 §4] stores each new main-KV entry as
+# MXFP4 and each SWA entry as FP8).  Plain nearest-value rounding on the code
+# tables above, written from the OCP definitions:
+#   E4M3FN : saturate to +-448 (the largest finite value), then the nearest
+#            finite value, a tie going to the even code; the sign bit is kept
+#            for values that round to zero (as an IEEE conversion does).
+#   MXFP4  : per 32 elements the shared exponent X = floor(log2(amax)) - 2
+#            (2 = the largest E2M1 exponent), clamped to [-127, 127], with
+#            X = -127 for an all-zero block; the E8M0 code is X + 127.  Each
+#            element v / 2^X goes to the nearest E2M1 magnitude, a tie going
+#            to the even code, saturating at 6; a value that rounds to zero
+#            is stored as +0.  Element 2j goes to the low nibble of byte j.
+# Inputs must be finite.
+
+def _nearest_code(mag, table):
+    """Index of the nearest entry of an ascending table; ties to the even index."""
+    mag = np.asarray(mag, dtype=np.float64)
+    hi = np.clip(np.searchsorted(table, mag, side="left"), 1, len(table) - 1)
+    lo = hi - 1
+    d_lo = mag - table[lo]
+    d_hi = table[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    return np.where(pick_hi, hi, lo)
+
+
+# Non-negative finite E4M3FN values (codes 0x00 .. 0x7E) ascend with the code.
+_E4M3_POS = E4M3_VALUES[:0x7F]
+_E2M1_POS = E2M1_VALUES[:8]
+
+
+def f64_to_e4m3(x):
+    """fp64 -> FP8 E4M3FN codes (saturating, round to nearest even)."""
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise FormatError("non-finite value to encode")
+    mag = np.minimum(np.abs(x), _E4M3_POS[-1])
+    code = _nearest_code(mag, _E4M3_POS).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+
+
+def f64_to_mxfp4(x):
+    """fp64 [..., D] (D a multiple of 32) -> (uint8 [..., D/2] packed E2M1,
+    uint8 [..., D/32] E8M0 codes)."""
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise FormatError("non-finite value to encode")
+    d = x.shape[-1]
+    if d % 32:
+        raise ValueError("MXFP4: the last dimension must be a multiple of 32")
+    blocks = x.reshape(x.shape[:-1] + (d // 32, 32))
+    amax = np.abs(blocks).max(axis=-1)
+    _, e = np.frexp(amax)                    # amax = m 2^e with m in [0.5, 1)
+    xexp = np.clip(e - 1 - 2, -127, 127)
+    xexp = np.where(amax > 0, xexp, -127)
+    scaled = np.abs(blocks) / np.ldexp(1.0, xexp)[..., None]
+    mag = _nearest_code(np.minimum(scaled, 6.0), _E2M1_POS).astype(np.uint8)
+    nib = np.where((blocks < 0) & (mag > 0), mag | 8, mag).astype(np.uint8)
+    nib = nib.reshape(x.shape)
+    packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+    return packed, (xexp + 127).astype(np.uint8)

@@ -85,3 +85,26 @@ def attention(q_raw, kv_fp4, kv_scale, idx, swa_raw, swa_pos0, q_pos, sm_scale,
     swa = formats.e4m3_to_f64(swa_raw[wpos - int(swa_pos0)])
     entries = np.concatenate([main, swa], axis=0)
     return attn.sparse_attention(formats.bf16_to_f64(q_raw), entries, sm_scale)
+
+
+def kv_append(kv_fp4, kv_scale, swa, kv_new_bits, swa_new_bits, pos, swa_pos0):
+    """The KV append step ([架构详解 §4]: main KV stored as MXFP4, SWA KV as
+    FP8): token i of sequence b sits at position p = pos[b] + i; its main
+    entry is encoded into row p of (kv_fp4, kv_scale) when 0 <= p < N_cap,
+    and its window entry into row p - swa_pos0[b] of swa when that row
+    exists.  Returns updated copies of the three caches (numpy uint8)."""
+    kv_fp4, kv_scale = np.array(kv_fp4, np.uint8), np.array(kv_scale, np.uint8)
+    swa = None if swa is None else np.array(swa, np.uint8)
+    B, n_new = kv_new_bits.shape[0], kv_new_bits.shape[1]
+    n_cap = kv_fp4.shape[1]
+    for b in range(B):
+        for i in range(n_new):
+            p = int(pos[b]) + i
+            if 0 <= p < n_cap:
+                kv_fp4[b, p], kv_scale[b, p] = formats.f64_to_mxfp4(
+                    formats.bf16_to_f64(kv_new_bits[b, i]))
+            if swa_new_bits is not None:
+                j = p - int(swa_pos0[b])
+                if 0 <= j < swa.shape[1]:
+                    swa[b, j] = formats.f64_to_e4m3(formats.bf16_to_f64(swa_new_bits[b, i]))
+    return kv_fp4, kv_scale, swa

@@ -193,6 +193,23 @@ def prefill_workload(n_q=4096, prefix_tokens=131072, seed=4, device="cpu", kdtyp
 
 
 # The five workloads, by name: (builder, kwargs).
+def kv_append_workload(B, n_new, seed=0, device="cpu"):
+    """KV append inputs: n_new new tokens per sequence at positions 0 ..
+    n_new - 1 (bf16 entries ~N(0,1)), empty caches of n_new main entries and
+    a window of the last 128 tokens."""
+    gen = Gen(seed, device)
+    s = min(WINDOW, n_new)
+    d = {"B": B, "n_q": 1, "n_new": n_new}
+    d["kv_new"] = to_bf16_bits(gen.normal(B, n_new, DIM))
+    d["swa_new"] = to_bf16_bits(gen.normal(B, n_new, DIM))
+    d["pos"] = torch.zeros(B, dtype=torch.int32, device=gen.device)
+    d["swa_pos0"] = torch.full((B,), n_new - s, dtype=torch.int32, device=gen.device)
+    d["kv_fp4"] = torch.zeros(B, n_new, DIM // 2, dtype=torch.uint8, device=gen.device)
+    d["kv_scale"] = torch.zeros(B, n_new, DIM // 32, dtype=torch.uint8, device=gen.device)
+    d["swa"] = torch.zeros(B, s, DIM, dtype=torch.uint8, device=gen.device)
+    return d
+
+
 WORKLOADS = {
     "tiny_2k": (decode_workload, dict(B=1, T=2048, kdtype="bf16", seed=0)),
     "full_64k": (decode_workload, dict(B=4, T=65536, kdtype="fp8", seed=1, heavy_frac=0.01)),
@@ -200,6 +217,7 @@ WORKLOADS = {
     "full_reindex_1m": (decode_workload, dict(B=8, T=1048576, kdtype="fp8", seed=3,
                                               lognormal_sigma=0.5, reindex=True)),
     "prefill_128k": (prefill_workload, dict(n_q=4096, prefix_tokens=131072, seed=4)),
+    "kv_append_64k": (kv_append_workload, dict(B=4, n_new=65536, seed=5)),
 }
 
 

@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     decls = re.findall(r"CSA2_API\s+[\w\s\*]+?\b(csa2_\w+)\s*\(", open(HEADER).read())
-    assert len(decls) == 8
+    assert len(decls) == 9
     for name in decls:
         assert hasattr(L, name), name
 
@@ -133,3 +133,19 @@ def test_binding_refuses_cpu_tensors(L):
     with pytest.raises(ValueError):
         csa.index_score(x, torch.zeros(1, 1, 32), torch.zeros(1, 64, 128, dtype=torch.uint8),
                         torch.zeros(1, 1, dtype=torch.int32), block_max=torch.zeros(1, 1, 8))
+
+
+def test_kv_append_validation(L):
+    f = L.csa2_kv_append
+    def call(kv=A, swn=None, pos=A, B=1, n=1, N=64, fp4=A, sc=A, swa=None, S=0, p0=None):
+        return f(kv, swn, pos, B, n, N, fp4, sc, swa, S, p0, None)
+    assert call(kv=None) == 1
+    assert call(sc=None) == 1
+    assert call(swn=A) == 1                     # window entries without a window cache
+    assert call(swn=A, swa=A) == 1              # ... or without swa_pos0
+    assert call(B=0) == 2
+    assert call(n=0) == 2
+    assert call(N=0) == 2
+    assert call(S=-1) == 2
+    assert call(kv=MIS) == 5
+    assert call(swn=A, swa=MIS, S=128, p0=A) == 5

@@ -424,3 +424,63 @@ def test_deterministic_reruns():
     o1 = _attn_gpu(d, a[3].cpu())
     o2 = _attn_gpu(d, a[3].cpu())
     assert np.array_equal(o1[0], o2[0]) and np.array_equal(o1[1], o2[1])
+
+
+# --------------------------------------------------------------------------- KV append
+def _append_inputs(rng, B, n_new):
+    """bf16 entries with per-block magnitudes from 2^-30 to 2^30 and planted
+    edge cases: E2M1 and E4M3 ties, an all-zero block, subnormal-range and
+    huge values, negative zeros, values past the FP8 range."""
+    scale = np.exp2(rng.integers(-30, 30, size=(B, n_new, 16, 1)))
+    kv = (rng.standard_normal((B, n_new, 16, 32)) * scale).reshape(B, n_new, 512)
+    sw = rng.standard_normal((B, n_new, 512)) * np.exp2(rng.integers(-12, 9, size=(B, n_new, 1)))
+    kv[0, 0, 0:32] = 0.0
+    kv[0, 0, 32:64] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 4) * 2.0 ** -3
+    kv[0, 0, 64:96] = rng.standard_normal(32) * 1e-39
+    kv[0, 0, 96:128] = rng.standard_normal(32) * 1e30
+    kv[0, 0, 128:136] = -0.0
+    vals = formats.e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    sw[0, 0, :126] = mids
+    sw[0, 1, :126] = -mids
+    sw[0, 2, :8] = [500.0, -1e4, 448.0, 2.0 ** -10, -(2.0 ** -10), -0.0, 1e-30, 464.0]
+    kv_bits = torch.from_numpy(kv.astype(np.float32)).to(torch.bfloat16).view(torch.int16)
+    sw_bits = torch.from_numpy(sw.astype(np.float32)).to(torch.bfloat16).view(torch.int16)
+    return kv_bits, sw_bits
+
+
+def test_kv_append_exact():
+    rng = np.random.default_rng(51)
+    B, n_new, N_cap, S_cap = 5, 3, 40, 16
+    kv_bits, sw_bits = _append_inputs(rng, B, n_new)
+    # Rows past either end of a cache are skipped: pos 38 writes rows 38, 39;
+    # pos -1 writes rows 0, 1; window rows follow p - swa_pos0.
+    pos = np.array([0, 10, 38, -1, 39], np.int32)
+    swa_pos0 = np.array([0, 5, 30, 0, 39], np.int32)
+    fp4 = np.full((B, N_cap, 256), 0xA5, np.uint8)
+    sc = np.full((B, N_cap, 16), 0xA5, np.uint8)
+    swa = np.full((B, S_cap, 512), 0xA5, np.uint8)
+    g = [torch.from_numpy(a.copy()).cuda() for a in (fp4, sc, swa)]
+    print("kv_append edge cases", flush=True)
+    csa.kv_append(kv_bits.cuda(), torch.from_numpy(pos).cuda(), g[0], g[1],
+                  swa_new=sw_bits.cuda(), swa_kv=g[2], swa_pos0=torch.from_numpy(swa_pos0).cuda())
+    torch.cuda.synchronize()
+    want = pipeline.kv_append(fp4, sc, swa, kv_bits.numpy().view(np.uint16),
+                              sw_bits.numpy().view(np.uint16), pos, swa_pos0)
+    for name, got, ref in zip(("kv_fp4", "kv_scale", "swa"), g, want):
+        assert np.array_equal(_np(got), ref), f"{name} differs from the oracle"
+
+
+def test_kv_append_without_window():
+    rng = np.random.default_rng(52)
+    B, n_new, N_cap = 2, 5, 8
+    kv_bits, _ = _append_inputs(rng, B, n_new)
+    pos = np.array([3, 0], np.int32)
+    fp4 = np.zeros((B, N_cap, 256), np.uint8)
+    sc = np.zeros((B, N_cap, 16), np.uint8)
+    g = [torch.from_numpy(a.copy()).cuda() for a in (fp4, sc)]
+    print("kv_append main only", flush=True)
+    csa.kv_append(kv_bits.cuda(), torch.from_numpy(pos).cuda(), g[0], g[1])
+    torch.cuda.synchronize()
+    want = pipeline.kv_append(fp4, sc, None, kv_bits.numpy().view(np.uint16), None, pos, None)
+    assert np.array_equal(_np(g[0]), want[0]) and np.array_equal(_np(g[1]), want[1])

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from _helpers import check_attention, check_selection, u16
-from oracle import pipeline
+from oracle import formats, pipeline
 from oracle import topk as otopk
 import synth
 
@@ -155,3 +155,25 @@ def test_prefill_128k():
         check_selection(gi, ref["idx"], lambda t: s[t], what=f"prefill idx row {j}")
         o, l = _attn_ref(d, 0, j, gi, d["q"], d["swa"])
         check_attention(u16(out[0, j]), _np(lse[0, j]), o, l, what=f"prefill attention row {j}")
+
+
+def test_kv_append_64k():
+    # The benchmark's append (4 x 65,536 tokens, window of the last 128), run
+    # once on the device; sampled main rows and every window row are checked
+    # against the oracle's encoding (placement is covered at small size).
+    d = synth.make("kv_append_64k", device="cuda")
+    print("kv_append_64k", flush=True)
+    csa.kv_append(d["kv_new"], d["pos"], d["kv_fp4"], d["kv_scale"], swa_new=d["swa_new"],
+                  swa_kv=d["swa"], swa_pos0=d["swa_pos0"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(53)
+    n_new, s_cap = d["n_new"], d["swa"].shape[1]
+    for b in range(d["B"]):
+        rows = torch.from_numpy(
+            np.unique(np.concatenate([rng.integers(0, n_new, 96), [0, n_new - 1]]))).cuda()
+        kv = formats.bf16_to_f64(_np(d["kv_new"][b][rows]).view(np.uint16))
+        fp4, sc = formats.f64_to_mxfp4(kv)
+        assert np.array_equal(_np(d["kv_fp4"][b][rows]), fp4)
+        assert np.array_equal(_np(d["kv_scale"][b][rows]), sc)
+        sw = formats.bf16_to_f64(_np(d["swa_new"][b, n_new - s_cap:]).view(np.uint16))
+        assert np.array_equal(_np(d["swa"][b]), formats.f64_to_e4m3(sw))

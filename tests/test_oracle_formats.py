@@ -97,3 +97,76 @@ def test_bf16_matches_torch():
     ok = ~np.isnan(lib)
     np.testing.assert_array_equal(got[ok], lib[ok])
     assert np.all(np.isnan(got[~ok]))
+
+
+# ---------------------------------------------------------------- encoding
+def test_e4m3_encode_round_trips_every_code():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    np.testing.assert_array_equal(formats.f64_to_e4m3(formats.e4m3_to_f64(codes)), codes)
+
+
+def test_e4m3_encode_matches_torch_cast():
+    # Library routine: torch's float32 -> float8_e4m3fn cast rounds to nearest
+    # even; it does not saturate, so inputs are clamped to +-448 first.  The
+    # inputs are fp32 values (the path encodes bf16), so that no double
+    # rounding through fp32 enters the library's result.
+    rng = np.random.default_rng(5)
+    vals = formats.e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)          # exact ties
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * np.exp2(rng.integers(-12, 10, 20000)),
+        mids, -mids, np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(0)),
+        np.array([0.0, -0.0, 448.0, 460.0, 1e6, -1e6]),
+    ]).astype(np.float32).astype(np.float64)
+    lib = torch.from_numpy(np.clip(x, -448.0, 448.0).astype(np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(formats.f64_to_e4m3(x), lib)
+
+
+def test_mxfp4_encode_round_trips():
+    # Codes whose block holds a magnitude 4 or 6 element encode back to
+    # themselves (that element fixes the shared exponent).  -0 is excluded:
+    # a zero is stored as +0.
+    rng = np.random.default_rng(6)
+    nib = rng.integers(0, 16, size=(40, 512)).astype(np.uint8)
+    nib[nib == 8] = 0
+    nib[:, ::32] = rng.choice(np.array([6, 7, 14, 15], np.uint8), size=(40, 16))
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    scales = rng.integers(1, 255, size=(40, 16)).astype(np.uint8)
+    p, s = formats.f64_to_mxfp4(formats.mxfp4_to_f64(packed, scales))
+    np.testing.assert_array_equal(p, packed)
+    np.testing.assert_array_equal(s, scales)
+
+
+def test_mxfp4_encode_worked_block():
+    # amax 6.5 -> shared exponent floor(log2 6.5) - 2 = 0 (code 127); every
+    # E2M1 tie goes to the even code; 6.5 saturates at 6; -0.2 -> +0.
+    x = np.zeros(32)
+    x[:12] = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.5, -0.2, -0.3, -6.0, 0.26]
+    p, s = formats.f64_to_mxfp4(x)
+    nib = np.empty(32, np.uint8)
+    nib[0::2], nib[1::2] = p & 0xF, p >> 4
+    assert s.tolist() == [127]
+    assert nib[:12].tolist() == [0, 2, 2, 4, 4, 6, 6, 7, 0, 9, 15, 1]
+    assert not nib[12:].any()
+    # All-zero block: code 0, all nibbles +0.
+    p, s = formats.f64_to_mxfp4(np.zeros(32))
+    assert s.tolist() == [0] and not p.any()
+    # Power-of-two amax: 2^k -> exponent k - 2.
+    for k in (-100, -3, 0, 5, 100):
+        _, s = formats.f64_to_mxfp4(np.full(32, np.ldexp(1.0, k)))
+        assert s.tolist() == [k - 2 + 127]
+
+
+def test_mxfp4_encode_matches_the_input_recipe():
+    # The input generator quantises with threshold comparisons in torch, a
+    # separate implementation of the same OCP rule.
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((64, 512)) * np.exp2(rng.integers(-20, 20, size=(64, 1)))
+    x[3, 64:96] = 0.0
+    x[5, :32] = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.75], 32) * 4.0
+    xb = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32)
+    p_ref, s_ref = synth.to_mxfp4(xb)
+    p, s = formats.f64_to_mxfp4(xb.numpy().astype(np.float64))
+    np.testing.assert_array_equal(p, p_ref.numpy())
+    np.testing.assert_array_equal(s, s_ref.numpy())

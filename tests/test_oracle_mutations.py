@@ -99,6 +99,43 @@ def _attention_unscaled(q, kv, scale):
     return attention.sparse_attention(q, kv, 1.0)
 
 
+def _pin_e4m3_encode(encode):
+    x = np.concatenate([formats.E4M3_VALUES[:0x7F], (formats.E4M3_VALUES[:0x7E] +
+                                                     formats.E4M3_VALUES[1:0x7F]) / 2, [500.0, -3.0]])
+    lib = torch.from_numpy(np.clip(x, -448, 448).astype(np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return np.array_equal(encode(x), lib)
+
+
+def _pin_mxfp4_encode(encode):
+    x = np.zeros(32)
+    x[:12] = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.5, -0.2, -0.3, -6.0, 0.26]
+    p, s = encode(x)
+    nib = np.empty(32, np.uint8)
+    nib[0::2], nib[1::2] = p & 0xF, p >> 4
+    return s.tolist() == [127] and nib[:12].tolist() == [0, 2, 2, 4, 4, 6, 6, 7, 0, 9, 15, 1]
+
+
+def _e4m3_ties_up(x):
+    # Ties rounded away from zero instead of to the even code.
+    x = np.asarray(x, np.float64)
+    up = formats.f64_to_e4m3(x)
+    mag = np.minimum(np.abs(x), 448.0)
+    vals = formats.E4M3_VALUES[:0x7F]
+    hi = np.clip(np.searchsorted(vals, mag), 0, 0x7E)
+    tie = (hi > 0) & (mag - vals[np.maximum(hi - 1, 0)] == vals[hi] - mag)
+    return np.where(tie, (hi | (up & 0x80)).astype(np.uint8), up)
+
+
+def _mxfp4_scale_from_ceil(x):
+    # Shared exponent from ceil(log2 amax) instead of floor.
+    x = np.asarray(x, np.float64)
+    amax = np.abs(x.reshape(-1, 32)).max(axis=-1)
+    bump = np.where((amax > 0) & (np.frexp(amax)[0] != 0.5), 1.0, 0.0)
+    return formats.f64_to_mxfp4(x / np.repeat(np.ldexp(1.0, bump.astype(int)), 32))[0], \
+        formats.f64_to_mxfp4(x)[1] + bump.astype(np.uint8)
+
+
 MUTATIONS = [
     ("fp8 exponent bias", _pin_e4m3, formats.e4m3_to_f64, _e4m3_bias8),
     ("fp4 nibble order", _pin_mxfp4, formats.mxfp4_to_f64, _mxfp4_swapped_nibbles),
@@ -108,6 +145,8 @@ MUTATIONS = [
     ("partial block dropped", _pin_block_max, indexer.block_max, _block_max_drops_partial),
     ("window off by one", _pin_window, attention.window_positions, _window_excludes_current),
     ("softmax scale ignored", _pin_attention, attention.sparse_attention, _attention_unscaled),
+    ("fp8 encode ties away", _pin_e4m3_encode, formats.f64_to_e4m3, _e4m3_ties_up),
+    ("fp4 scale from ceil", _pin_mxfp4_encode, formats.f64_to_mxfp4, _mxfp4_scale_from_ceil),
 ]
 
 
