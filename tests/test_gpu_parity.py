@@ -484,3 +484,40 @@ def test_kv_append_without_window():
     torch.cuda.synchronize()
     want = pipeline.kv_append(fp4, sc, None, kv_bits.numpy().view(np.uint16), None, pos, None)
     assert np.array_equal(_np(g[0]), want[0]) and np.array_equal(_np(g[1]), want[1])
+
+
+def test_multi_query_decode_rows():
+    # n_q = 4 query tokens per sequence below the matrix-core threshold (the
+    # decode scan, speculative-verification shape): each row scans its own
+    # visible prefix of its sequence's keys, and attends with its own
+    # position.
+    B, T, n_q = 2, 3000, 4
+    d = synth.decode_workload(B=B, T=T, kdtype="fp8", seed=61)
+    g = torch.Generator().manual_seed(62)
+    d["n_q"] = n_q
+    d["q_idx"] = synth.to_bf16_bits(torch.randn(B, n_q, 32, 128, generator=g))
+    d["w_idx"] = torch.rand(B, n_q, 32, generator=g)
+    d["q"] = synth.to_bf16_bits(torch.randn(B, n_q, 64, 512, generator=g))
+    vis = [T - 3, T - 2, T - 1, T, 1999, 2000, 2001, 2008]
+    d["q_pos"] = (torch.tensor(vis, dtype=torch.int32) - 1).reshape(B, n_q)
+    print("multi-query decode rows n_q=4", flush=True)
+    _, sc, bm = _scan(d, vis)
+    sc, bm = _np(sc), _np(bm)
+    for b in range(B):
+        kr, kd = _kraw(d, b)
+        for j in range(n_q):
+            v = vis[b * n_q + j]
+            ref = pipeline.scores_prefix(u16(d["q_idx"][b, j]), _np(d["w_idx"][b, j]), kr, kd, v)
+            tol = 1e-5 * np.abs(ref) + 1e-6 * np.abs(ref).max()
+            assert np.all(np.abs(sc[b, j, :v].astype(np.float64) - ref) <= tol), f"row ({b}, {j})"
+            assert np.all(np.isnan(sc[b, j, v:]))
+            bref = indexer.block_max(ref, v)
+            nb = (v + 7) // 8
+            assert np.all(np.abs(bm[b, j, :nb] - bref) <= 1e-5 * np.abs(bref) + 1e-6 * np.abs(ref).max())
+    rng = np.random.default_rng(63)
+    idx = np.stack([np.sort(rng.choice(vis[r], size=512, replace=False)) for r in range(B * n_q)])
+    out, lse = _attn_gpu(d, torch.from_numpy(idx.astype(np.int32)).reshape(B, n_q, 512))
+    for b in range(B):
+        for j in range(n_q):
+            o, l = _attn_ref(d, b, j, idx[b * n_q + j])
+            check_attention(out[b, j], lse[b, j], o, l, what=f"attention row ({b}, {j})")
