@@ -46,7 +46,8 @@ _RESTYPES = {"csa2_workspace_size": _S, "csa2_status_string": ctypes.c_char_p,
 
 
 class AttnOpts(ctypes.Structure):
-    _fields_ = [("window", _I), ("replay_start", _I), ("kv_fmt", _I), ("reserved", _I)]
+    _fields_ = [("window", _I), ("replay_start", _I), ("kv_fmt", _I), ("reserved", _I),
+                ("sink", ctypes.c_void_p)]
 
 
 class Csa2Error(RuntimeError):
@@ -159,14 +160,14 @@ def reindex_topk(mode, vis_len, N_cap, top_k, idx_out, scores=None, q_idx=None, 
 
 
 def _attn(name, q, kv_fp4, kv_scale, idx, swa_kv, swa_pos0, q_pos, sm_scale, out, lse=None,
-          window=128, replay_start=-1, ws=None, stream=None):
+          window=128, replay_start=-1, sink=None, ws=None, stream=None):
     B, n_q = q.shape[0], q.shape[1]
     N_cap = kv_fp4.shape[1]
     top_k = idx.shape[-1] if idx is not None else 0
     S_cap = swa_kv.shape[1] if swa_kv is not None else 0
     need = workspace_size(OP_SPARSE_ATTN, B, n_q, N_cap, top_k, 0)
     ws, nbytes = _workspace(ws, need, q.device)
-    opts = AttnOpts(window, replay_start, 0, 0)
+    opts = AttnOpts(window, replay_start, 0, 0, _ptr(sink, _F32, "sink"))
     _call(name, _ptr(q, _BITS16, "q"), _ptr(kv_fp4, _U8, "kv_fp4"),
           _ptr(kv_scale, _U8, "kv_scale"), N_cap, _ptr(idx, _I32, "idx"), top_k,
           _ptr(swa_kv, _U8, "swa_kv"), S_cap, _ptr(swa_pos0, _I32, "swa_pos0"),

@@ -40,21 +40,23 @@ csa2_status attn_common(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t*
   // the kernel relies on it to keep empty slots at -inf.
   if (!(sm_scale > 0.0f) || !(sm_scale < __builtin_inff())) return CSA2_ERR_SHAPE;
   int32_t window = 128, replay_start = -1;
+  const float* sink = nullptr;
   if (opts) {
     if (opts->kv_fmt != CSA2_KV_MXFP4_E8M0_32 || opts->reserved != 0) return CSA2_ERR_UNSUPPORTED;
     if (opts->window < 0 || opts->window > 128 || opts->replay_start < -1) return CSA2_ERR_SHAPE;
     window = opts->window;
     replay_start = opts->replay_start;
+    sink = opts->sink;
   }
-  const void* ptrs[] = {q, kv_fp4, kv_scale, idx, swa_kv, swa_pos0, q_pos, out, lse};
+  const void* ptrs[] = {q, kv_fp4, kv_scale, idx, swa_kv, swa_pos0, q_pos, out, lse, sink};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return CSA2_ERR_ALIGN;
   const size_t need = csa2::attn_workspace_bytes(B * n_q, top_k);
   if (need > 0 && (!ws || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return CSA2_ERR_ALIGN;
   return from_hip(csa2::launch_sparse_attn(q, kv_fp4, kv_scale, N_cap, idx, top_k, swa_kv, S_cap,
-                                           swa_pos0, q_pos, sm_scale, window, replay_start, B,
-                                           n_q, out, lse, ws, stream));
+                                           swa_pos0, q_pos, sm_scale, window, replay_start, sink,
+                                           B, n_q, out, lse, ws, stream));
 }
 
 }  // namespace

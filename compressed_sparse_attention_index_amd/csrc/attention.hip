@@ -84,6 +84,7 @@ struct AttnArgs {
   float* lse;
   uint16_t* part_o;  // [rows, nsplit, 64, 512] bf16, or null
   float* part_ml;    // [rows, nsplit, 64, 2] or null
+  const float* sink; // [64] per-head sink logits (natural log), or null
   int N_cap, top_k, S_cap, n_q, window, replay_start;
   int rows, n_chunks, cps, nsplit;
   float scale2;      // sm_scale * log2(e)
@@ -548,13 +549,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
   // head row.
   const size_t ps = static_cast<size_t>(x.r) * a.nsplit + split;
   lds_barrier();
-  // Split partials are written unnormalised, whole rows normalised by 1 / l.
+  // Split partials are written unnormalised (the merge adds the sink).  A
+  // whole row is normalised by its softmax sum, which a sink logit s (log2
+  // units s2) extends: with m' = max(m, s2) the sum is l 2^(m - m') +
+  // 2^(s2 - m') and O (relative to m) is scaled by 2^(m - m') / sum.
+  float fo[2], lse2[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float mr = st.m_run[h], l = st.l_run[h];
+    const float s2 = a.sink != nullptr ? a.sink[32 * h + x.c] * kLog2e : -__builtin_inff();
+    const float mn = fmaxf(mr, s2);
+    const float al = mr == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mr - mn);
+    const float sum = l * al + (s2 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(s2 - mn));
+    fo[h] = sum > 0.0f ? al / sum : 0.0f;
+    lse2[h] = sum > 0.0f ? mn + log2f(sum) : -__builtin_inff();
+  }
   auto write_rows = [&](auto normalise) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int row = 32 * h + x.c;
-      const float l = st.l_run[h];
-      const float f = l > 0.0f ? 1.0f / l : 0.0f;
+      const float f = fo[h];
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -577,9 +591,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
     const float l = st.l_run[h];
     if (x.wave == 0 && x.half == 0) {
       if (a.nsplit == 1) {
-        if (a.lse != nullptr)
-          a.lse[static_cast<size_t>(x.r) * kHeads + row] =
-              l > 0.0f ? (st.m_run[h] + log2f(l)) * kLn2 : -__builtin_inff();
+        if (a.lse != nullptr) a.lse[static_cast<size_t>(x.r) * kHeads + row] = lse2[h] * kLn2;
       } else {
         a.part_ml[(ps * kHeads + row) * 2 + 0] = st.m_run[h];
         a.part_ml[(ps * kHeads + row) * 2 + 1] = l;
@@ -624,6 +636,9 @@ __global__ __launch_bounds__(64 * kCombineHeads) void k_attn_combine(AttnArgs a)
   float mx = ms;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
+  // A sink logit (log2 units s2) joins the normaliser, with no value.
+  const float s2 = a.sink != nullptr ? a.sink[head] * kLog2e : -__builtin_inff();
+  mx = fmaxf(mx, s2);
   const float wgt_mine = (ms == -__builtin_inff()) ? 0.0f : exp2f(ms - mx);
   float L = 0.0f;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -641,6 +656,7 @@ __global__ __launch_bounds__(64 * kCombineHeads) void k_attn_combine(AttnArgs a)
       }
     }
   }
+  if (s2 != -__builtin_inff()) L += exp2f(s2 - mx);
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   *reinterpret_cast<u32x4*>(a.out + (static_cast<size_t>(r) * kHeads + head) * kDim + 8 * t) =
       u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
@@ -675,14 +691,16 @@ size_t attn_workspace_bytes(int rows, int top_k) {
 hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
                               int N_cap, const int32_t* idx, int top_k, const uint8_t* swa_kv,
                               int S_cap, const int32_t* swa_pos0, const int32_t* q_pos,
-                              float sm_scale, int window, int replay_start, int B, int n_q,
-                              uint16_t* out, float* lse, void* ws, hipStream_t stream) {
+                              float sm_scale, int window, int replay_start, const float* sink,
+                              int B, int n_q, uint16_t* out, float* lse, void* ws,
+                              hipStream_t stream) {
   const int rows = B * n_q;
   AttnArgs a;
   a.q = q; a.kv_fp4 = kv_fp4; a.kv_scale = kv_scale; a.idx = idx; a.swa = swa_kv;
   a.swa_pos0 = swa_pos0; a.q_pos = q_pos; a.out = out; a.lse = lse;
   a.N_cap = N_cap; a.top_k = top_k; a.S_cap = S_cap; a.n_q = n_q;
   a.window = window; a.replay_start = replay_start;
+  a.sink = sink;
   a.scale2 = sm_scale * kLog2e;
   a.rows = rows;
   plan(rows, top_k, &a.n_chunks, &a.cps, &a.nsplit);

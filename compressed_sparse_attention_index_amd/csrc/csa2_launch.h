@@ -41,8 +41,9 @@ size_t attn_workspace_bytes(int rows, int top_k);
 hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
                               int N_cap, const int32_t* idx, int top_k, const uint8_t* swa_kv,
                               int S_cap, const int32_t* swa_pos0, const int32_t* q_pos,
-                              float sm_scale, int window, int replay_start, int B, int n_q,
-                              uint16_t* out, float* lse, void* ws, hipStream_t stream);
+                              float sm_scale, int window, int replay_start, const float* sink,
+                              int B, int n_q, uint16_t* out, float* lse, void* ws,
+                              hipStream_t stream);
 
 // KV append: MXFP4 main entries and FP8 window entries of new tokens; see
 // kv_append.hip.

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 1
+#define CSA2_ABI_VERSION 2
 
 /* Symbols of the C ABI; everything else in the library is hidden. */
 #define CSA2_API __attribute__((visibility("default")))
@@ -115,6 +115,8 @@ typedef struct {
                             [max(s, i-W+1), i]); -1 = no truncation (default) */
   int32_t kv_fmt;        /* csa2_kvfmt; default CSA2_KV_MXFP4_E8M0_32 */
   int32_t reserved;      /* must be 0 */
+  const float* sink;     /* NULL, or [64] fp32 per-head sink logits (device memory); see
+                            csa2_sparse_attn_decode */
 } csa2_attn_opts;
 
 /*
@@ -218,6 +220,11 @@ CSA2_API csa2_status csa2_reindex_topk(csa2_mode mode, const float* scores, cons
  *     l_e = sm_scale * q[r][h] . v_e,  out[r][h] = sum_e softmax(l)_e v_e,
  *     lse[r][h] = log sum_e exp(l_e)   (natural log; -inf for an empty set,
  *                                       whose output is 0)
+ *   With opts->sink, head h also has a sink logit s_h: the normaliser gains
+ *   exp(s_h) and no value, i.e. out = sum_e exp(l_e) v_e / (sum_e exp(l_e) +
+ *   exp(s_h)) and lse = log(sum_e exp(l_e) + exp(s_h)); s_h = -inf is no
+ *   sink (DeepSeek-V4 essay (mlqm.cn) §4.3: a learnable attention sink on
+ *   which each head may put part of its probability mass).
  *   ("DeepSeek-V4.1-Flash 架构详解", §1 (64 x 512 heads, window 128), §4
  *   (dequantised before attention), §9 step 5 (selected global KV plus this
  *   layer's SWA KV); V4 essay §4.3 (an entry is both key and value).)
@@ -232,7 +239,7 @@ CSA2_API csa2_status csa2_reindex_topk(csa2_mode mode, const float* scores, cons
  *   swa_pos0  [B] int32
  *   q_pos     [B, n_q] int32 token position of each query
  *   sm_scale  softmax scale, finite and > 0 (else CSA2_ERR_SHAPE)
- *   opts      NULL or options (window, replay_start, kv_fmt)
+ *   opts      NULL or options (window, replay_start, kv_fmt, sink)
  *   out       [B, n_q, 64, 512] bf16 output
  *   lse       [B, n_q, 64] fp32 output or NULL
  *   ws        csa2_workspace_size(CSA2_OP_SPARSE_ATTN, ...) bytes

@@ -30,20 +30,29 @@ def window_positions(q_pos, swa_pos0, s_cap, window=WINDOW, replay_start=-1):
     return np.arange(lo, hi + 1, dtype=np.int64) if hi >= lo else np.zeros(0, np.int64)
 
 
-def sparse_attention(q, entries, sm_scale):
+def sparse_attention(q, entries, sm_scale, sink=None):
     """Softmax attention of q [H, D] over entries [E, D] used as K and V.
 
     Returns (out [H, D], lse [H]) with lse the natural-log normaliser
     log sum_e exp(sm_scale * q_h . k_e).  With no entries: out 0, lse -inf.
+
+    sink: None, or [H] per-head sink logits (DeepSeek-V4 essay §4.3: each
+    head may put part of its probability mass on a virtual sink instead of
+    the history).  The sink adds exp(sink_h) to head h's normaliser and
+    contributes no value; -inf is no sink.
     """
     q = np.asarray(q, dtype=np.float64)
     kv = np.asarray(entries, dtype=np.float64)
-    if kv.shape[0] == 0:
-        return np.zeros_like(q), np.full(q.shape[0], -np.inf)
     logits = float(sm_scale) * (q @ kv.T)          # [H, E]
-    mu = logits.max(axis=1, keepdims=True)
-    p = np.exp(logits - mu)
-    l = p.sum(axis=1)
-    out = (p @ kv) / l[:, None]
-    lse = mu[:, 0] + np.log(l)
+    s = (np.full(q.shape[0], -np.inf) if sink is None
+         else np.asarray(sink, dtype=np.float64).reshape(q.shape[0]))
+    mu = np.maximum(logits.max(axis=1) if kv.shape[0] else np.full(q.shape[0], -np.inf), s)
+    if kv.shape[0] == 0 and np.all(np.isneginf(mu)):
+        return np.zeros_like(q), np.full(q.shape[0], -np.inf)
+    safe = np.where(np.isneginf(mu), 0.0, mu)      # heads with nothing at all: l = 0
+    p = np.exp(logits - safe[:, None])
+    l = p.sum(axis=1) + np.exp(s - safe)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        out = np.where(l[:, None] > 0, (p @ kv) / np.where(l > 0, l, 1.0)[:, None], 0.0)
+        lse = np.where(l > 0, safe + np.log(np.where(l > 0, l, 1.0)), -np.inf)
     return out, lse

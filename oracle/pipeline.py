@@ -76,15 +76,16 @@ def prefill_topk(q_raw, w, k_raw, kdtype, vis, top_k=topk.TOP_K):
 
 
 def attention(q_raw, kv_fp4, kv_scale, idx, swa_raw, swa_pos0, q_pos, sm_scale,
-              window=attn.WINDOW, replay_start=-1):
-    """Selected main entries (idx != -1) plus the SWA window, one softmax."""
+              window=attn.WINDOW, replay_start=-1, sink=None):
+    """Selected main entries (idx != -1) plus the SWA window, one softmax
+    (with an optional per-head sink, see attention.sparse_attention)."""
     idx = np.asarray(idx, dtype=np.int64)
     sel = idx[idx >= 0]
     main = formats.mxfp4_to_f64(kv_fp4[sel], kv_scale[sel])
     wpos = attn.window_positions(q_pos, swa_pos0, swa_raw.shape[0], window, replay_start)
     swa = formats.e4m3_to_f64(swa_raw[wpos - int(swa_pos0)])
     entries = np.concatenate([main, swa], axis=0)
-    return attn.sparse_attention(formats.bf16_to_f64(q_raw), entries, sm_scale)
+    return attn.sparse_attention(formats.bf16_to_f64(q_raw), entries, sm_scale, sink)
 
 
 def kv_append(kv_fp4, kv_scale, swa, kv_new_bits, swa_new_bits, pos, swa_pos0):

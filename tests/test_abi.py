@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.csa2_abi_version() == 1
+    assert L.csa2_abi_version() == 2
     for st in range(7):
         assert len(L.csa2_status_string(st)) > 0
     assert L.csa2_status_string(0) == b"ok"
@@ -122,6 +122,8 @@ def test_attention_validation(L):
         assert _attn(L, fn, opts=ctypes.byref(bad_fmt)) == 3
         bad_win = csa.AttnOpts(129, -1, 0, 0)
         assert _attn(L, fn, opts=ctypes.byref(bad_win)) == 2
+        bad_sink = csa.AttnOpts(128, -1, 0, 0, MIS)
+        assert _attn(L, fn, opts=ctypes.byref(bad_sink)) == 5
         assert _attn(L, fn, B=8) == 4                 # 8 rows split the entries: needs workspace
         assert _attn(L, fn, out=MIS) == 5
 

@@ -291,7 +291,7 @@ def test_reindex_layer():
 
 
 # --------------------------------------------------------------------------- attention
-def _attn_gpu(d, idx, q=None, swa=None, window=128, replay_start=-1, reuse=False):
+def _attn_gpu(d, idx, q=None, swa=None, window=128, replay_start=-1, reuse=False, sink=None):
     q = d["q"] if q is None else q
     swa = d["swa"] if swa is None else swa
     B, n_q = q.shape[0], q.shape[1]
@@ -300,12 +300,12 @@ def _attn_gpu(d, idx, q=None, swa=None, window=128, replay_start=-1, reuse=False
     fn = csa.reuse_attn if reuse else csa.sparse_attn_decode
     fn(q.cuda(), d["kv_fp4"].cuda(), d["kv_scale"].cuda(), idx.cuda(), swa.cuda(),
        d["swa_pos0"].cuda(), d["q_pos"].cuda(), d["sm_scale"], out, lse=lse, window=window,
-       replay_start=replay_start)
+       replay_start=replay_start, sink=None if sink is None else sink.cuda())
     torch.cuda.synchronize()
     return u16(out), _np(lse)
 
 
-def _attn_ref(d, b, j, idx_row, q=None, swa=None, window=128, replay_start=-1):
+def _attn_ref(d, b, j, idx_row, q=None, swa=None, window=128, replay_start=-1, sink=None):
     q = d["q"] if q is None else q
     swa = d["swa"] if swa is None else swa
     idx_row = np.asarray(idx_row, dtype=np.int64)
@@ -314,7 +314,7 @@ def _attn_ref(d, b, j, idx_row, q=None, swa=None, window=128, replay_start=-1):
     sc = _np(d["kv_scale"][b][torch.as_tensor(sel, dtype=torch.long, device=d["kv_scale"].device)])
     return pipeline.attention(u16(q[b, j]), fp4, sc, np.arange(len(sel)), _np(swa[b]),
                               int(d["swa_pos0"][b]), int(d["q_pos"][b, j]), d["sm_scale"],
-                              window, replay_start)
+                              window, replay_start, sink)
 
 
 @pytest.mark.parametrize("case", ["topk512", "ragged", "invalid", "dense", "window16", "replay",
@@ -521,3 +521,29 @@ def test_multi_query_decode_rows():
         for j in range(n_q):
             o, l = _attn_ref(d, b, j, idx[b * n_q + j])
             check_attention(out[b, j], lse[b, j], o, l, what=f"attention row ({b}, {j})")
+
+
+@pytest.mark.parametrize("rows", [3, 256])
+def test_attention_sink(rows):
+    # Per-head sink logits (no sink, small, comparable to the logits, and one
+    # that takes nearly all the mass), through the split merge (3 rows) and
+    # the single-workgroup rows (256).
+    T = 4000
+    if rows == 3:
+        d = synth.decode_workload(B=3, T=T, kdtype="bf16", seed=71)
+    else:
+        d = synth.prefill_workload(n_q=256, prefix_tokens=T, seed=72)
+    B, n_q = d["q"].shape[0], d["q"].shape[1]
+    rng = np.random.default_rng(73)
+    sink = rng.uniform(-4.0, 6.0, 64)
+    sink[:8] = -np.inf
+    sink[8] = 40.0
+    sink_t = torch.from_numpy(sink.astype(np.float32))
+    nkv = d["kv_fp4"].shape[1]
+    idx = np.stack([np.sort(rng.choice(nkv, size=512, replace=False)) for _ in range(B * n_q)])
+    print(f"attention sink rows={rows}", flush=True)
+    out, lse = _attn_gpu(d, torch.from_numpy(idx.astype(np.int32)).reshape(B, n_q, 512), sink=sink_t)
+    for r in (range(B * n_q) if rows == 3 else (0, 97, 255)):
+        b, j = divmod(r, n_q)
+        o, l = _attn_ref(d, b, j, idx[r], sink=sink.astype(np.float32).astype(np.float64))
+        check_attention(out[b, j], lse[b, j], o, l, what=f"sink row {r}")

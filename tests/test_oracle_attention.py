@@ -104,3 +104,24 @@ def test_invalid_indices_are_skipped():
     a = pipeline.attention(q, fp4, sc, np.array([5, -1, 9, -1]), swa, 0, 63, 0.05)
     b = pipeline.attention(q, fp4, sc, np.array([9, 5]), swa, 0, 63, 0.05)
     np.testing.assert_allclose(a[0], b[0], rtol=1e-13)
+
+
+def test_sink_matches_softmax_with_a_zero_value_slot():
+    # Library routine: torch.softmax over the logits with the sink logit
+    # appended as one more column; the sink's column carries no value.
+    rng = np.random.default_rng(31)
+    q = rng.standard_normal((6, 16)); kv = rng.standard_normal((9, 16))
+    sink = np.array([-np.inf, -3.0, 0.0, 2.5, 40.0, -40.0])
+    scale = 0.3
+    logits = torch.from_numpy(scale * (q @ kv.T))
+    full = torch.cat([logits, torch.from_numpy(sink)[:, None]], dim=1)
+    p = torch.softmax(full, dim=1)[:, :-1].numpy()
+    out, lse = attention.sparse_attention(q, kv, scale, sink)
+    np.testing.assert_allclose(out, p @ kv, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, torch.logsumexp(full, dim=1).numpy(), rtol=1e-12)
+    # No sink equals the plain attention; no entries leaves lse = sink, out 0.
+    o0, l0 = attention.sparse_attention(q, kv, scale)
+    o1, l1 = attention.sparse_attention(q, kv, scale, np.full(6, -np.inf))
+    np.testing.assert_array_equal(o0, o1); np.testing.assert_array_equal(l0, l1)
+    o2, l2 = attention.sparse_attention(q, kv[:0], scale, sink)
+    assert not o2.any() and np.array_equal(l2, sink)
