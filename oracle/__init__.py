@@ -20,11 +20,14 @@ The bit-level number formats (OCP MX v1.0 E2M1 / E8M0, OCP FP8 E4M3FN) are
 the public OCP definitions; the pages only name the formats.
 
 Modules:
-  formats    -- decoding of bf16, FP8 E4M3FN, E2M1, E8M0 and MXFP4 entries
+  formats    -- decoding of bf16, FP8 E4M3FN, E2M1, E8M0 and MXFP4 entries, and
+                encoding into FP8 E4M3FN and MXFP4 (the KV append step)
   indexer    -- indexer score and block maximum
   topk       -- block Top-K, pool Top-K (Full / Reindex), flat Top-K
-  attention  -- sparse multi-query attention with the SWA window, one softmax
-  pipeline   -- one query's Full / Reindex / Reuse / prefill step from raw bytes
+  attention  -- sparse multi-query attention with the SWA window, one softmax,
+                optional per-head sink
+  pipeline   -- one query's Full / Reindex / Reuse / prefill step from raw bytes,
+                and the KV append of new tokens
 
 Every function here is pinned by a CPU test (closed forms, invariants, brute
 force, library routines, hand-worked examples); none is marked

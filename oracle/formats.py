@@ -1,4 +1,5 @@
-"""Decoding of the stored number formats to fp64 (test infrastructure only).
+"""Decoding of the stored number formats to fp64, and the encoding of new
+entries into them (test infrastructure only).
 
 [架构详解 §4]: main KV is stored as MXFP4 (E2M1 elements with block scales)
 and is dequantised before attention; SWA KV is FP8.  [架构详解 §1 config
