@@ -1,7 +1,7 @@
 """Graph replay of whole hot-path steps.
 
-A decode step (scan, block Top-K, Full and Reindex selections, both
-attentions) and a prefill step (matrix-core scoring, flat Top-K, attention)
+A decode step (KV append, scan, block Top-K, Full and Reindex selections,
+both attentions) and a prefill step (matrix-core scoring, flat Top-K, attention)
 are captured into a HIP graph through torch.cuda.CUDAGraph and replayed
 several times.  Before the eager reference run and before every replay the
 outputs are overwritten with a sentinel, and unrelated eager work runs on
@@ -44,8 +44,16 @@ def _decode_step(d):
     ws_bt = _ws(csa.OP_BLOCK_TOPK, B, 1, N, 512, 2048)
     ws_re = _ws(csa.OP_REINDEX_TOPK, B, 1, N, 512, 2048)
     ws_at = _ws(csa.OP_SPARSE_ATTN, B, 1, N, 512, 0)
+    # The step starts by appending the current token's entries (position
+    # N - 1, main and window caches), as a decode step of an engine would.
+    g = torch.Generator(device="cuda").manual_seed(23)
+    kv_new = synth.to_bf16_bits(torch.randn(B, 1, 512, device="cuda", generator=g))
+    swa_new = synth.to_bf16_bits(torch.randn(B, 1, 512, device="cuda", generator=g))
+    pos = torch.full((B,), N - 1, dtype=torch.int32, device="cuda")
 
     def run():
+        csa.kv_append(kv_new, pos, d["kv_fp4"], d["kv_scale"], swa_new=swa_new, swa_kv=d["swa"],
+                      swa_pos0=d["swa_pos0"])
         csa.index_score(d["q_idx"], d["w_idx"], d["k_idx"], d["vis_len"], block_max=o["bm"])
         csa.block_topk(o["bm"], d["vis_len"], N, 2048, o["pool"], ws=ws_bt)
         csa.reindex_topk(csa.MODE_FULL, d["vis_len"], N, 512, o["idx"], q_idx=d["q_idx"],
