@@ -45,9 +45,17 @@ _RESTYPES = {"csa2_workspace_size": _S, "csa2_status_string": ctypes.c_char_p,
              "csa2_abi_version": _I}
 
 
+ATTN_SINK = 1   # csa2_attn_opts.flags bit: the sink pointer is read
+
+
 class AttnOpts(ctypes.Structure):
-    _fields_ = [("window", _I), ("replay_start", _I), ("kv_fmt", _I), ("reserved", _I),
+    _fields_ = [("window", _I), ("replay_start", _I), ("kv_fmt", _I), ("flags", ctypes.c_uint32),
                 ("sink", ctypes.c_void_p)]
+
+
+class AttnOptsV1(ctypes.Structure):
+    """The 16-byte options struct of ABI 1 (no sink pointer)."""
+    _fields_ = [("window", _I), ("replay_start", _I), ("kv_fmt", _I), ("reserved", _I)]
 
 
 class Csa2Error(RuntimeError):
@@ -167,7 +175,8 @@ def _attn(name, q, kv_fp4, kv_scale, idx, swa_kv, swa_pos0, q_pos, sm_scale, out
     S_cap = swa_kv.shape[1] if swa_kv is not None else 0
     need = workspace_size(OP_SPARSE_ATTN, B, n_q, N_cap, top_k, 0)
     ws, nbytes = _workspace(ws, need, q.device)
-    opts = AttnOpts(window, replay_start, 0, 0, _ptr(sink, _F32, "sink"))
+    sp = _ptr(sink, _F32, "sink")
+    opts = AttnOpts(window, replay_start, 0, ATTN_SINK if sp else 0, sp)
     _call(name, _ptr(q, _BITS16, "q"), _ptr(kv_fp4, _U8, "kv_fp4"),
           _ptr(kv_scale, _U8, "kv_scale"), N_cap, _ptr(idx, _I32, "idx"), top_k,
           _ptr(swa_kv, _U8, "swa_kv"), S_cap, _ptr(swa_pos0, _I32, "swa_pos0"),

@@ -42,11 +42,15 @@ csa2_status attn_common(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t*
   int32_t window = 128, replay_start = -1;
   const float* sink = nullptr;
   if (opts) {
-    if (opts->kv_fmt != CSA2_KV_MXFP4_E8M0_32 || opts->reserved != 0) return CSA2_ERR_UNSUPPORTED;
+    if (opts->kv_fmt != CSA2_KV_MXFP4_E8M0_32 || (opts->flags & ~CSA2_ATTN_SINK) != 0)
+      return CSA2_ERR_UNSUPPORTED;
     if (opts->window < 0 || opts->window > 128 || opts->replay_start < -1) return CSA2_ERR_SHAPE;
     window = opts->window;
     replay_start = opts->replay_start;
-    sink = opts->sink;
+    if (opts->flags & CSA2_ATTN_SINK) {
+      sink = opts->sink;
+      if (!sink) return CSA2_ERR_NULL;
+    }
   }
   const void* ptrs[] = {q, kv_fp4, kv_scale, idx, swa_kv, swa_pos0, q_pos, out, lse, sink};
   for (const void* p : ptrs)

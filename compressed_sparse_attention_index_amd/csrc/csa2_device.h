@@ -3,9 +3,11 @@
 // Number formats (OCP definitions; the method stores main KV as MXFP4 and SWA
 // KV as FP8 -- "DeepSeek-V4.1-Flash 架构详解", §4):
 //   FP8 E4M3FN -> bf16 and E2M1 (with an E8M0 block scale) -> bf16 use the
-//   gfx950 scaled-conversion instructions; both conversions are exact because
-//   every E4M3FN value and every E2M1 x 2^k value with k in the E8M0 range is
-//   a bf16 value.
+//   gfx950 scaled-conversion instructions.  Every E4M3FN value is a bf16
+//   value, and so is every E2M1 x 2^(c - 127) for E8M0 codes c <= 252 (the
+//   largest, 6 x 2^125, is below the bf16 maximum; code 0 gives bf16
+//   subnormals): those conversions are exact.  Codes 253 and 254 overflow
+//   bf16 for E2M1 magnitudes >= 4 and >= 2 respectively.
 // Matrix cores: v_mfma_f32_32x32x16_bf16, wave64.  Operand layout (lane l):
 //   A[m][k]: m = l % 32, k = 8 * (l / 32) + i, i = 0..7
 //   B[k][n]: n = l % 32, k = 8 * (l / 32) + i

@@ -39,10 +39,10 @@
  *     window slots are skipped.
  *   - Scratch memory comes only from the caller's workspace `ws` of
  *     `ws_bytes` bytes, sized with csa2_workspace_size().  Calls that may run
- *     at the same time must not share a workspace.  Results never depend on
- *     its contents on entry.  csa2_block_topk runs fastest on a workspace
- *     that was zero-filled once when allocated or last used by a
- *     csa2_block_topk call with the same B * n_q (see there).
+ *     at the same time must not share a workspace.  Apart from
+ *     csa2_block_topk, results never depend on the workspace contents on
+ *     entry.  csa2_block_topk needs a workspace that was zero-filled once
+ *     when allocated or last used by a csa2_block_topk call (see there).
  *   - Sizes: N_cap <= 4,194,304 entries (4x the pages' maximum context of
  *     1,048,576 tokens), B * n_q <= 65,535 for the decode-shaped calls.
  *   - The library keeps no state; it is thread-safe.
@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 2
+#define CSA2_ABI_VERSION 3
 
 /* Symbols of the C ABI; everything else in the library is hidden. */
 #define CSA2_API __attribute__((visibility("default")))
@@ -108,15 +108,22 @@ typedef enum {
   CSA2_OP_SPARSE_ATTN = 3
 } csa2_op;
 
-/* Options of the attention entry points; NULL means the defaults. */
+/* Bits of csa2_attn_opts.flags. */
+#define CSA2_ATTN_SINK 1u  /* opts->sink is read (per-head sink logits) */
+
+/* Options of the attention entry points; NULL means the defaults.  The
+   first four fields have the layout of ABI 1, whose last field (then
+   `reserved`, always 0) is now `flags`: an ABI-1 caller's struct, which
+   ends there, is read correctly because `sink` is read only when
+   flags & CSA2_ATTN_SINK. */
 typedef struct {
   int32_t window;        /* SWA window in tokens, 0..128; default 128 */
   int32_t replay_start;  /* first token a replayed window may see (window
                             [max(s, i-W+1), i]); -1 = no truncation (default) */
   int32_t kv_fmt;        /* csa2_kvfmt; default CSA2_KV_MXFP4_E8M0_32 */
-  int32_t reserved;      /* must be 0 */
-  const float* sink;     /* NULL, or [64] fp32 per-head sink logits (device memory); see
-                            csa2_sparse_attn_decode */
+  uint32_t flags;        /* CSA2_ATTN_* bits; other bits must be 0 */
+  const float* sink;     /* with CSA2_ATTN_SINK: [64] fp32 per-head sink logits (device
+                            memory), see csa2_sparse_attn_decode; otherwise not read */
 } csa2_attn_opts;
 
 /*
@@ -157,11 +164,14 @@ CSA2_API csa2_status csa2_index_score(const uint16_t* q_idx, const float* w_idx,
  *   pool_blocks [B, n_q, k_blocks] int32 output: ascending block ids, -1 padded
  *   ws          csa2_workspace_size(CSA2_OP_BLOCK_TOPK, ...) bytes (required).
  *               Its first 2 * B * n_q * 4096 words are histograms that must
- *               start at zero; every call leaves them zeroed.  A call that
- *               finds them not zeroed (their totals do not match the counts
- *               they must hold) still returns the exact result, by a slower
- *               exact pass over every visible block of the row.  Zero-fill
- *               a new workspace once (hipMemset) to avoid that pass.
+ *               start at zero; every call leaves them zeroed, so a workspace
+ *               zero-filled once (hipMemset) when allocated, or last used by
+ *               csa2_block_topk, is always ready.  Other contents are caught
+ *               by the histograms' totals (they must equal the visible block
+ *               count and the candidate count of the row): such a row is
+ *               still selected exactly, by a slower pass over every visible
+ *               block.  Stale bins whose totals happen to match are not
+ *               caught and give an unspecified pool.
  */
 CSA2_API csa2_status csa2_block_topk(const float* block_max, const int32_t* vis_len, int32_t B,
                             int32_t n_q, int32_t N_cap, int32_t k_blocks, int32_t* pool_blocks,
@@ -220,7 +230,7 @@ CSA2_API csa2_status csa2_reindex_topk(csa2_mode mode, const float* scores, cons
  *     l_e = sm_scale * q[r][h] . v_e,  out[r][h] = sum_e softmax(l)_e v_e,
  *     lse[r][h] = log sum_e exp(l_e)   (natural log; -inf for an empty set,
  *                                       whose output is 0)
- *   With opts->sink, head h also has a sink logit s_h: the normaliser gains
+ *   With CSA2_ATTN_SINK, head h also has a sink logit s_h: the normaliser gains
  *   exp(s_h) and no value, i.e. out = sum_e exp(l_e) v_e / (sum_e exp(l_e) +
  *   exp(s_h)) and lse = log(sum_e exp(l_e) + exp(s_h)); s_h = -inf is no
  *   sink (DeepSeek-V4 essay (mlqm.cn) §4.3: a learnable attention sink on

@@ -10,7 +10,8 @@ uncompressed tokens.  [架构详解 §5]: a replayed window is truncated to
 Readings: one softmax over the union of selected main entries and window
 tokens (no de-duplication), each entry used as both K and V, logits scaled by
 sm_scale (1/sqrt(512) in the workloads), window [q_pos-W+1, q_pos] including
-the current token, no attention sink, no norm or rotary inside.
+the current token, no norm or rotary inside.  An attention sink is optional
+(sparse_attention's `sink`; none by default).
 """
 import numpy as np
 

@@ -53,13 +53,25 @@ def scores_at(q_raw, w, k_raw, kdtype, positions):
 
 
 def full_layer(q_raw, w, k_raw, kdtype, vis, k_blocks=topk.MAX_POOL_BLOCKS, top_k=topk.TOP_K):
-    """Full layer: scan, block maxima, pool, Top-k inside the pool."""
+    """Full layer: scan, block maxima, pool, Top-k inside the pool.
+
+    [架构详解 §3.2] defines the Full layer's Top-512 over every visible entry
+    and builds the pool beside it.  When the pool keeps at least top_k blocks
+    (or every block), the Top-k inside the pool is that global Top-k: each
+    block ranked above the block of a selected position contributes its own
+    maximum, a distinct position ranked above it, so fewer than top_k blocks
+    rank above it.  The global Top-k is computed too and the two are asserted
+    equal in that case.
+    """
     s = scores_prefix(q_raw, w, k_raw, kdtype, vis)
     bm = indexer.block_max(s, vis)
     pool = topk.block_topk(bm, k_blocks)
     pos = topk.pool_positions(pool, vis)
     idx = topk.pool_topk(s[pos], pos, top_k)
-    return {"scores": s, "block_max": bm, "pool": pool, "idx": idx}
+    glob = topk.flat_topk(s, vis, top_k)
+    if int(k_blocks) >= int(top_k) or int(k_blocks) >= bm.shape[0]:
+        assert np.array_equal(idx, glob), "pool Top-k differs from the global Top-k"
+    return {"scores": s, "block_max": bm, "pool": pool, "idx": idx, "global_idx": glob}
 
 
 def reindex_layer(q_raw, w, k_raw, kdtype, pool, vis, top_k=topk.TOP_K):

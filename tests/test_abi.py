@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.csa2_abi_version() == 2
+    assert L.csa2_abi_version() == 3
     for st in range(7):
         assert len(L.csa2_status_string(st)) > 0
     assert L.csa2_status_string(0) == b"ok"
@@ -122,8 +122,19 @@ def test_attention_validation(L):
         assert _attn(L, fn, opts=ctypes.byref(bad_fmt)) == 3
         bad_win = csa.AttnOpts(129, -1, 0, 0)
         assert _attn(L, fn, opts=ctypes.byref(bad_win)) == 2
-        bad_sink = csa.AttnOpts(128, -1, 0, 0, MIS)
+        bad_sink = csa.AttnOpts(128, -1, 0, csa.ATTN_SINK, MIS)
         assert _attn(L, fn, opts=ctypes.byref(bad_sink)) == 5
+        null_sink = csa.AttnOpts(128, -1, 0, csa.ATTN_SINK, None)
+        assert _attn(L, fn, opts=ctypes.byref(null_sink)) == 1
+        bad_flag = csa.AttnOpts(128, -1, 0, 2, None)
+        assert _attn(L, fn, opts=ctypes.byref(bad_flag)) == 3
+        # Without the sink flag the pointer is not read: an ABI-1 caller's
+        # 16-byte struct (no pointer field) passes validation up to the
+        # workspace check, like NULL options.
+        v1 = csa.AttnOptsV1(128, -1, 0, 0)
+        assert _attn(L, fn, opts=ctypes.byref(v1), B=8) == 4
+        unread = csa.AttnOpts(128, -1, 0, 0, MIS)
+        assert _attn(L, fn, opts=ctypes.byref(unread), B=8) == 4
         assert _attn(L, fn, B=8) == 4                 # 8 rows split the entries: needs workspace
         assert _attn(L, fn, out=MIS) == 5
 

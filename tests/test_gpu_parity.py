@@ -372,6 +372,33 @@ def test_attention_dense_equals_sdpa_through_gpu():
     check_attention(out[0, 0], None, ref[0, :, 0].numpy(), None, what="dense")
 
 
+def test_attention_extreme_scale_codes():
+    # Main entries with every E2M1 code (random bytes) and E8M0 codes across
+    # the range the dequantisation holds exactly in bf16: blocks 0..13 take
+    # codes 0 (the subnormal scale 2^-127), 1, 2, 64, 125, 127, 129; blocks
+    # 14 and 15 take 190 and 224 (values up to 6 x 2^97), and the query is
+    # zero on their dims, so the logits stay O(1) while those output dims are
+    # huge and are checked relatively.
+    T, B = 700, 2
+    d = synth.decode_workload(B=B, T=T, kdtype="bf16", seed=81)
+    rng = np.random.default_rng(81)
+    small = np.array([0, 1, 2, 64, 125, 127, 129], np.uint8)
+    sc = small[rng.integers(0, len(small), size=(B, T, 16))]
+    sc[:, :, 14:] = np.array([190, 224], np.uint8)[rng.integers(0, 2, size=(B, T, 2))]
+    d["kv_scale"] = torch.from_numpy(sc)
+    d["kv_fp4"] = torch.from_numpy(rng.integers(0, 256, size=(B, T, 256), dtype=np.uint8))
+    q = d["q"].view(torch.bfloat16).clone()
+    q[..., 448:] = 0
+    d["q"] = q.view(torch.int16)
+    idx = np.stack([np.sort(rng.choice(T, size=512, replace=False)) for _ in range(B)])
+    print("attention extreme E8M0 codes", flush=True)
+    out, lse = _attn_gpu(d, torch.from_numpy(idx.astype(np.int32)).reshape(B, 1, 512))
+    for b in range(B):
+        o, l = _attn_ref(d, b, 0, idx[b])
+        assert np.abs(o[:, 448:]).max() > 2.0 ** 80
+        check_attention(out[b, 0], lse[b, 0], o, l, what=f"extreme codes row {b}")
+
+
 def test_attention_single_split_and_reuse_identical():
     # 512 query rows: each workgroup covers a whole row (no split partials).
     d = synth.prefill_workload(n_q=512, prefix_tokens=4000, seed=43)

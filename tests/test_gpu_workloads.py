@@ -78,9 +78,11 @@ def _check_full(d, b, pool, idx, out, lse):
     ri = otopk.pool_topk(ref["scores"][pos], pos, 512)
     gi = _np(idx[b, 0])
     check_selection(gi, ri, lambda t: ref["scores"][t], what=f"idx row {b}")
-    # Hierarchy invariant on the real workload: the pool's Top-512 is the
-    # global Top-512 (up to ties).
-    check_selection(gi, ref["idx"], lambda t: ref["scores"][t], what=f"global idx row {b}")
+    # The Full layer's Top-512 is defined over every visible entry: the
+    # GPU's in-pool selection must equal the flat Top-512 over [0, T) (up to
+    # ties).
+    glob = otopk.flat_topk(ref["scores"], T, 512)
+    check_selection(gi, glob, lambda t: ref["scores"][t], what=f"global idx row {b}")
     o, l = _attn_ref(d, b, 0, gi, d["q"], d["swa"])
     check_attention(u16(out[b, 0]), _np(lse[b, 0]), o, l, what=f"attention row {b}")
     return gp

@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention, formats, indexer, topk
+from oracle import attention, formats, indexer, pipeline, topk
+import test_oracle_pipeline as pp
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -136,6 +137,91 @@ def _mxfp4_scale_from_ceil(x):
         formats.f64_to_mxfp4(x)[1] + bump.astype(np.uint8)
 
 
+# Planted mistakes in copies of the pipeline's composition functions.
+
+def _scores_prefix_tail_dropped(q_raw, w, k_raw, kdtype, vis, chunk=pipeline.CHUNK):
+    q, wf = formats.bf16_to_f64(q_raw), np.asarray(w, np.float64)
+    out = np.zeros(int(vis))
+    for lo in range(0, int(vis) - chunk + 1, chunk):     # the partial last chunk is never scored
+        out[lo:lo + chunk] = indexer.index_scores(
+            q, wf, pipeline.decode_index_keys(k_raw[lo:lo + chunk], kdtype))
+    return out
+
+
+def _scores_prefix_shifted(q_raw, w, k_raw, kdtype, vis, chunk=pipeline.CHUNK):
+    q, wf = formats.bf16_to_f64(q_raw), np.asarray(w, np.float64)
+    out = np.empty(int(vis))
+    for lo in range(0, int(vis), chunk):
+        hi = min(int(vis), lo + chunk)
+        src = k_raw[lo + (lo > 0):hi + (lo > 0)]           # chunks after the first read one row late
+        out[lo:hi] = indexer.index_scores(q, wf, pipeline.decode_index_keys(src, kdtype))
+    return out
+
+
+def _full_layer_global_not_pool(q_raw, w, k_raw, kdtype, vis, k_blocks=2048, top_k=512):
+    s = pipeline.scores_prefix(q_raw, w, k_raw, kdtype, vis)
+    bm = indexer.block_max(s, vis)
+    return {"scores": s, "block_max": bm, "pool": topk.block_topk(bm, k_blocks),
+            "idx": topk.flat_topk(s, vis, top_k)}       # Top-k taken outside the pool
+
+
+def _full_layer_pool_of_top_k(q_raw, w, k_raw, kdtype, vis, k_blocks=2048, top_k=512):
+    s = pipeline.scores_prefix(q_raw, w, k_raw, kdtype, vis)
+    bm = indexer.block_max(s, vis)
+    pool = topk.block_topk(bm, min(k_blocks, top_k))     # pool sized by top_k
+    pool = topk.pad(pool[pool >= 0], k_blocks)
+    pos = topk.pool_positions(pool, vis)
+    return {"scores": s, "block_max": bm, "pool": pool, "idx": topk.pool_topk(s[pos], pos, top_k)}
+
+
+def _reindex_block_ids_as_positions(q_raw, w, k_raw, kdtype, pool, vis, top_k=512):
+    blocks = np.sort(np.asarray(pool)[np.asarray(pool) >= 0])   # the x8 expansion forgotten
+    s = pipeline.scores_at(q_raw, w, k_raw, kdtype, blocks)
+    return {"positions": blocks, "scores": s, "idx": topk.pool_topk(s, blocks, top_k)}
+
+
+def _reindex_unclipped(q_raw, w, k_raw, kdtype, pool, vis, top_k=512):
+    blocks = np.sort(np.asarray(pool)[np.asarray(pool) >= 0])
+    pos = (blocks[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
+    pos = pos[pos < k_raw.shape[0]]                      # clipped to the cache, not to vis
+    s = pipeline.scores_at(q_raw, w, k_raw, kdtype, pos)
+    return {"positions": pos, "scores": s, "idx": topk.pool_topk(s, pos, top_k)}
+
+
+def _prefill_last_entry_hidden(q_raw, w, k_raw, kdtype, vis, top_k=512):
+    return pipeline.prefill_topk(q_raw, w, k_raw, kdtype, vis - 1, top_k)
+
+
+def _kv_append_variant(window_shift=0, wrap_main=False, wrap_window=False):
+    def fn(kv_fp4, kv_scale, swa, kv_new_bits, swa_new_bits, pos, swa_pos0):
+        kv_fp4, kv_scale, swa = np.array(kv_fp4), np.array(kv_scale), np.array(swa)
+        n_cap, s_cap = kv_fp4.shape[1], swa.shape[1]
+        for b in range(kv_new_bits.shape[0]):
+            for i in range(kv_new_bits.shape[1]):
+                p = int(pos[b]) + i
+                if (-n_cap <= p < n_cap) if wrap_main else (0 <= p < n_cap):
+                    kv_fp4[b, p], kv_scale[b, p] = formats.f64_to_mxfp4(
+                        formats.bf16_to_f64(kv_new_bits[b, i]))
+                j = p - int(swa_pos0[b]) + window_shift
+                if (-s_cap <= j < s_cap) if wrap_window else (0 <= j < s_cap):
+                    swa[b, j] = formats.f64_to_e4m3(formats.bf16_to_f64(swa_new_bits[b, i]))
+        return kv_fp4, kv_scale, swa
+    return fn
+
+
+def _attention_variant(slot_shift=0, keep_empty=False):
+    def fn(q_raw, kv_fp4, kv_scale, idx, swa_raw, swa_pos0, q_pos, sm_scale, window=128,
+           replay_start=-1, sink=None):
+        idx = np.asarray(idx, dtype=np.int64)
+        sel = idx if keep_empty else idx[idx >= 0]
+        main = formats.mxfp4_to_f64(kv_fp4[sel], kv_scale[sel])
+        wpos = attention.window_positions(q_pos, swa_pos0, swa_raw.shape[0], window, replay_start)
+        swa = formats.e4m3_to_f64(swa_raw[wpos - int(swa_pos0) + slot_shift])
+        return attention.sparse_attention(formats.bf16_to_f64(q_raw),
+                                          np.concatenate([main, swa]), sm_scale, sink)
+    return fn
+
+
 MUTATIONS = [
     ("fp8 exponent bias", _pin_e4m3, formats.e4m3_to_f64, _e4m3_bias8),
     ("fp4 nibble order", _pin_mxfp4, formats.mxfp4_to_f64, _mxfp4_swapped_nibbles),
@@ -147,10 +233,41 @@ MUTATIONS = [
     ("softmax scale ignored", _pin_attention, attention.sparse_attention, _attention_unscaled),
     ("fp8 encode ties away", _pin_e4m3_encode, formats.f64_to_e4m3, _e4m3_ties_up),
     ("fp4 scale from ceil", _pin_mxfp4_encode, formats.f64_to_mxfp4, _mxfp4_scale_from_ceil),
+    ("score chunk tail dropped", pp.pin_scores_prefix, pipeline.scores_prefix,
+     _scores_prefix_tail_dropped),
+    ("score chunk slice off by one", pp.pin_scores_prefix, pipeline.scores_prefix,
+     _scores_prefix_shifted),
+    ("full Top-k outside the pool", pp.pin_full_layer, pipeline.full_layer,
+     _full_layer_global_not_pool),
+    ("pool sized by top_k", pp.pin_full_layer, pipeline.full_layer, _full_layer_pool_of_top_k),
+    ("reindex block ids as positions", pp.pin_reindex_layer, pipeline.reindex_layer,
+     _reindex_block_ids_as_positions),
+    ("reindex pool not clipped to vis", pp.pin_reindex_layer, pipeline.reindex_layer,
+     _reindex_unclipped),
+    ("prefill last entry hidden", pp.pin_prefill_topk, pipeline.prefill_topk,
+     _prefill_last_entry_hidden),
+    ("append window row off by one", pp.pin_kv_append, pipeline.kv_append,
+     _kv_append_variant(window_shift=1)),
+    ("append main skip rule dropped", pp.pin_kv_append, pipeline.kv_append,
+     _kv_append_variant(wrap_main=True)),
+    ("append window skip rule dropped", pp.pin_kv_append, pipeline.kv_append,
+     _kv_append_variant(wrap_window=True)),
+    ("attention window slot off by one", pp.pin_attention, pipeline.attention,
+     _attention_variant(slot_shift=-1)),
+    ("attention empty slots kept", pp.pin_attention, pipeline.attention,
+     _attention_variant(keep_empty=True)),
 ]
+
+
+def _holds(pin, fn):
+    # A pin that raises on a wrong function has caught it as well.
+    try:
+        return bool(pin(fn))
+    except (AssertionError, IndexError, ValueError):
+        return False
 
 
 @pytest.mark.parametrize("name,pin,good,bad", MUTATIONS, ids=[m[0] for m in MUTATIONS])
 def test_pin_catches_planted_mistake(name, pin, good, bad):
     assert pin(good), f"pin for {name} fails on the real oracle"
-    assert not pin(bad), f"pin for {name} does not catch the planted mistake"
+    assert not _holds(pin, bad), f"pin for {name} does not catch the planted mistake"

@@ -1,0 +1,298 @@
+"""Pins of the oracle's composition functions (oracle/pipeline.py), CPU only.
+
+Each pin checks a pipeline function against something other than itself:
+torch's own dtype casts for the key decoding, pure-Python loops for the
+scores, Python's `sorted` for every selection, the inverse placement map for
+the KV append, and torch's scaled_dot_product_attention over an entry list
+assembled by hand for the attention step.  The pins are written as functions
+of the pipeline function under test so that test_oracle_mutations.py can
+plant mistakes in copies of it.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats, pipeline
+import synth
+
+
+# ---------------------------------------------------------------------------
+# Independent helpers (no oracle arithmetic)
+
+def _torch_keys(k_raw, kdtype):
+    t = torch.from_numpy(np.ascontiguousarray(k_raw))
+    if kdtype == "bf16":
+        return t.view(torch.int16).view(torch.bfloat16).to(torch.float64).numpy()
+    return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _loop_scores(q, w, k):
+    out = []
+    for t in range(k.shape[0]):
+        total = 0.0
+        for h in range(q.shape[0]):
+            dot = float(np.dot(q[h], k[t]))       # one head's dot product
+            total += float(w[h]) * (dot if dot > 0.0 else 0.0)
+        out.append(total)
+    return np.array(out)
+
+
+def _sorted_pick(keys, ids, k):
+    order = sorted(range(len(ids)), key=lambda i: (-keys[i], ids[i]))
+    return sorted(int(ids[i]) for i in order[:k])
+
+
+def _padded(ids, k):
+    return ids + [-1] * (k - len(ids))
+
+
+def _inputs(seed, vis, kdtype, ties=False):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((32, 128))
+    if ties:
+        # Integer-valued keys from a few distinct rows: many exactly equal
+        # scores and equal block maxima.
+        base = np.round(rng.standard_normal((5, 128)) * 2)
+        kf = base[rng.integers(0, 5, vis)]
+        q = np.round(q * 2)
+    else:
+        kf = rng.standard_normal((vis, 128))
+    w = rng.uniform(size=32)
+    q_raw = synth.to_bf16_bits(torch.from_numpy(q).float()).numpy().view(np.uint16)
+    if kdtype == "bf16":
+        k_raw = synth.to_bf16_bits(torch.from_numpy(kf).float()).numpy().view(np.uint16)
+    else:
+        k_raw = synth.to_fp8_bytes(torch.from_numpy(kf).float()).numpy()
+    return q_raw, w, k_raw
+
+
+def _qf(q_raw):
+    return torch.from_numpy(q_raw.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+# ---------------------------------------------------------------------------
+# Pins (each returns True when the function passed in is right)
+
+def pin_decode_keys(fn):
+    rng = np.random.default_rng(1)
+    ok = True
+    bf = rng.integers(0, 1 << 16, (9, 128), dtype=np.uint16)
+    bf[(bf & 0x7F80) == 0x7F80] = 0x3F80                 # no inf / NaN patterns
+    ok &= np.array_equal(fn(bf, "bf16"), _torch_keys(bf, "bf16"))
+    f8 = rng.integers(0, 256, (9, 128), dtype=np.uint8)
+    f8[(f8 & 0x7F) == 0x7F] = 0x38                       # no NaN codes
+    ok &= np.array_equal(fn(f8, "fp8"), _torch_keys(f8, "fp8"))
+    return bool(ok)
+
+
+def pin_scores_prefix(fn):
+    # Chunks of 7 over 50 positions: 7 whole chunks and a partial one.
+    for kdtype in ("bf16", "fp8"):
+        q_raw, w, k_raw = _inputs(2, 60, kdtype)
+        want = _loop_scores(_qf(q_raw), w, _torch_keys(k_raw, kdtype))
+        for vis, chunk in ((50, 7), (49, 7), (7, 7), (8, 7), (1, 3), (50, 64), (60, 1 << 16)):
+            got = fn(q_raw, w, k_raw, kdtype, vis, chunk=chunk)
+            if got.shape != (vis,) or not np.allclose(got, want[:vis], rtol=1e-12, atol=1e-12):
+                return False
+    return True
+
+
+def pin_scores_at(fn):
+    q_raw, w, k_raw = _inputs(3, 40, "fp8")
+    pos = np.array([39, 0, 17, 17, 5])
+    want = _loop_scores(_qf(q_raw), w, _torch_keys(k_raw, "fp8")[pos])
+    return np.allclose(fn(q_raw, w, k_raw, "fp8", pos), want, rtol=1e-12, atol=1e-12)
+
+
+def _brute_full(q_raw, w, k_raw, kdtype, vis, kb, k):
+    s = _loop_scores(_qf(q_raw), w, _torch_keys(k_raw[:vis], kdtype))
+    nb = (vis + 7) // 8
+    bm = [max(s[8 * j:min(8 * j + 8, vis)]) for j in range(nb)]
+    pool = _sorted_pick(bm, list(range(nb)), min(kb, nb))
+    cand = [t for j in pool for t in range(8 * j, min(8 * j + 8, vis))]
+    idx = _sorted_pick([s[t] for t in cand], cand, k)
+    glob = _sorted_pick(list(s), list(range(vis)), k)
+    return s, bm, _padded(pool, kb), _padded(idx, k), _padded(glob, k)
+
+
+FULL_CASES = [  # (seed, vis, kdtype, k_blocks, top_k, ties)
+    (10, 200, "bf16", 12, 9, False),
+    (11, 203, "fp8", 30, 16, True),
+    (12, 64, "bf16", 2048, 512, False),     # every block kept, fewer than k positions
+    (13, 97, "fp8", 6, 20, False),          # pool smaller than k: Top-k inside the pool only
+    (14, 150, "bf16", 19, 19, True),
+    (15, 1, "fp8", 4, 3, False),
+]
+
+
+def pin_full_layer(fn):
+    for seed, vis, kdtype, kb, k, ties in FULL_CASES:
+        q_raw, w, k_raw = _inputs(seed, vis + 5, kdtype, ties)
+        s, bm, pool, idx, glob = _brute_full(q_raw, w, k_raw, kdtype, vis, kb, k)
+        r = fn(q_raw, w, k_raw, kdtype, vis, k_blocks=kb, top_k=k)
+        if not np.allclose(r["scores"], s, rtol=1e-12, atol=1e-12):
+            return False
+        if not np.allclose(r["block_max"], bm, rtol=1e-12, atol=1e-12):
+            return False
+        if r["pool"].tolist() != pool or r["idx"].tolist() != idx:
+            return False
+        if kb >= k and r["idx"].tolist() != glob:
+            return False
+    return True
+
+
+def pin_reindex_layer(fn):
+    for seed, vis, kdtype, ties in ((20, 180, "fp8", False), (21, 77, "bf16", True)):
+        q_raw, w, k_raw = _inputs(seed, vis + 3, kdtype, ties)
+        rng = np.random.default_rng(seed)
+        nb = (vis + 7) // 8
+        blocks = sorted(rng.choice(nb, size=min(9, nb), replace=False).tolist())
+        pool = np.array(blocks + [-1] * 3)
+        pos = [t for j in blocks for t in range(8 * j, min(8 * j + 8, vis))]
+        s = _loop_scores(_qf(q_raw), w, _torch_keys(k_raw, kdtype)[pos])
+        want = _padded(_sorted_pick(list(s), pos, 13), 13)
+        r = fn(q_raw, w, k_raw, kdtype, pool, vis, top_k=13)
+        if r["idx"].tolist() != want or r["positions"].tolist() != pos:
+            return False
+        if not np.allclose(r["scores"], s, rtol=1e-12, atol=1e-12):
+            return False
+    return True
+
+
+def pin_prefill_topk(fn):
+    # (seed, vis, kdtype, ties, top_k); the last case keeps every visible
+    # entry, so each one, the last included, must appear.
+    for seed, vis, kdtype, ties, k in ((30, 90, "bf16", False, 16), (31, 41, "fp8", True, 16),
+                                       (32, 20, "bf16", False, 24)):
+        q_raw, w, k_raw = _inputs(seed, vis + 9, kdtype, ties)
+        s = _loop_scores(_qf(q_raw), w, _torch_keys(k_raw[:vis], kdtype))
+        want = _padded(_sorted_pick(list(s), list(range(vis)), k), k)
+        if fn(q_raw, w, k_raw, kdtype, vis, top_k=k)["idx"].tolist() != want:
+            return False
+    return True
+
+
+def pin_kv_append(fn):
+    # Tiny caches with a sentinel fill: a row is rewritten exactly when some
+    # new token maps to it (inverse map: i = p - pos[b] for cache row p,
+    # window slot j holding token swa_pos0[b] + j); every other row keeps
+    # the sentinel.  Encodings come from torch's FP8 cast and the torch MXFP4
+    # recipe of the input generator.
+    n_cap, s_cap, n_new = 6, 3, 5
+    # The last sequence's first tokens fall before its window (rows -4..-1).
+    pos = np.array([-1, 0, n_cap - 1, 3, 0])
+    swa_pos0 = np.array([0, 2, 1, 5, 4])
+    B = len(pos)
+    rng = np.random.default_rng(40)
+    kv_new = synth.to_bf16_bits(torch.from_numpy(rng.standard_normal((B, n_new, 512))).float())
+    swa_new = synth.to_bf16_bits(torch.from_numpy(rng.standard_normal((B, n_new, 512))).float())
+    fp4 = np.full((B, n_cap, 256), 0xAB, np.uint8)
+    sc = np.full((B, n_cap, 16), 0xCD, np.uint8)
+    swa = np.full((B, s_cap, 512), 0xEF, np.uint8)
+    got_fp4, got_sc, got_swa = fn(fp4, sc, swa, kv_new.numpy().view(np.uint16),
+                                  swa_new.numpy().view(np.uint16), pos, swa_pos0)
+    kv_f = kv_new.view(torch.bfloat16).float()
+    sw_f = swa_new.view(torch.bfloat16).float()
+    for b in range(B):
+        for p in range(n_cap):
+            i = p - pos[b]
+            if 0 <= i < n_new:
+                wp, ws = synth.to_mxfp4(kv_f[b, i][None])
+                want_p, want_s = wp[0].numpy(), ws[0].numpy()
+            else:
+                want_p, want_s = fp4[b, p], sc[b, p]
+            if not (np.array_equal(got_fp4[b, p], want_p) and np.array_equal(got_sc[b, p], want_s)):
+                return False
+        for j in range(s_cap):
+            i = swa_pos0[b] + j - pos[b]
+            want = synth.to_fp8_bytes(sw_f[b, i]).numpy() if 0 <= i < n_new else swa[b, j]
+            if not np.array_equal(got_swa[b, j], want):
+                return False
+    return True
+
+
+def pin_attention(fn):
+    # Stored window slots hold tokens 20 .. 27; the query sits at token 25
+    # with a window of 4 and a replay start of 23, so it sees tokens 23..25
+    # (slots 3..5).  Entries assembled by hand; SDPA in float64 is the check.
+    rng = np.random.default_rng(50)
+    n, s_cap, p0, qpos = 12, 8, 20, 25
+    kv = rng.standard_normal((n, 512))
+    fp4, sc = (t.numpy() for t in synth.to_mxfp4(torch.from_numpy(kv).float()))
+    swa = synth.to_fp8_bytes(torch.from_numpy(rng.standard_normal((s_cap, 512))).float()).numpy()
+    q_raw = synth.to_bf16_bits(torch.from_numpy(rng.standard_normal((4, 512))).float()).numpy()
+    idx = np.array([7, -1, 2, 11, -1])
+    main = torch.from_numpy(fp4[[7, 2, 11]])
+    # MXFP4 decode by table lookup of the OCP values (independent of the oracle).
+    table = torch.tensor([0, .5, 1, 1.5, 2, 3, 4, 6, 0, -.5, -1, -1.5, -2, -3, -4, -6],
+                         dtype=torch.float64)
+    nib = torch.stack([main & 15, main >> 4], dim=-1).reshape(3, 512).long()
+    scale = torch.pow(2.0, torch.from_numpy(sc[[7, 2, 11]]).double() - 127).repeat_interleave(32, -1)
+    ent = [table[nib] * scale]
+    ent.append(torch.from_numpy(swa[[3, 4, 5]]).view(torch.float8_e4m3fn).double())
+    e = torch.cat(ent)
+    qf = torch.from_numpy(q_raw.view(np.int16)).view(torch.bfloat16).double()
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qf[None, :, None, :], e[None, None].expand(1, 4, -1, -1),
+        e[None, None].expand(1, 4, -1, -1), scale=0.06)[0, :, 0].numpy()
+    out, lse = fn(q_raw.view(np.uint16), fp4, sc, idx, swa, p0, qpos, 0.06, window=4,
+                  replay_start=23)
+    lse_ref = torch.logsumexp(0.06 * (qf @ e.T), dim=1).numpy()
+    return bool(np.allclose(out, ref, rtol=1e-10, atol=1e-12)
+                and np.allclose(lse, lse_ref, rtol=1e-12))
+
+
+# ---------------------------------------------------------------------------
+
+def test_decode_index_keys_matches_torch_casts():
+    assert pin_decode_keys(pipeline.decode_index_keys)
+
+
+def test_scores_prefix_across_chunk_boundaries():
+    assert pin_scores_prefix(pipeline.scores_prefix)
+
+
+def test_scores_at_given_positions():
+    assert pin_scores_at(pipeline.scores_at)
+
+
+def test_full_layer_against_brute_force():
+    assert pin_full_layer(pipeline.full_layer)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_full_layer_pool_topk_is_global_topk(seed):
+    # With a pool of at least top_k blocks the Full layer's Top-k is the
+    # Top-k over every visible position ([架构详解 §3.2]).
+    vis = 700 + 37 * seed
+    q_raw, w, k_raw = _inputs(60 + seed, vis, "fp8", ties=seed % 2 == 1)
+    r = pipeline.full_layer(q_raw, w, k_raw, "fp8", vis, k_blocks=24, top_k=24)
+    want = _padded(_sorted_pick(list(r["scores"]), list(range(vis)), 24), 24)
+    assert r["idx"].tolist() == want and r["global_idx"].tolist() == want
+
+
+def test_reindex_layer_against_brute_force():
+    assert pin_reindex_layer(pipeline.reindex_layer)
+
+
+def test_reindex_equals_flat_when_the_pool_covers_everything():
+    # vis <= 8 k_blocks: the pool is every position, so Reindex is the flat
+    # Top-k with the Reindex query (I4).
+    q_raw, w, k_raw = _inputs(70, 100, "bf16")
+    q2, w2, _ = _inputs(71, 100, "bf16")
+    full = pipeline.full_layer(q_raw, w, k_raw, "bf16", 100)
+    re = pipeline.reindex_layer(q2, w2, k_raw, "bf16", full["pool"], 100, top_k=30)
+    flat = pipeline.prefill_topk(q2, w2, k_raw, "bf16", 100, top_k=30)
+    assert re["idx"].tolist() == flat["idx"].tolist()
+
+
+def test_prefill_topk_against_brute_force():
+    assert pin_prefill_topk(pipeline.prefill_topk)
+
+
+def test_kv_append_placement_and_skip_rules():
+    assert pin_kv_append(pipeline.kv_append)
+
+
+def test_attention_assembles_selected_and_window_entries():
+    assert pin_attention(pipeline.attention)
