@@ -53,6 +53,8 @@ def parse():
                    help="CPU time budget of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="skip the graph-replay measurement")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the 128K points (Reuse decode, prefill chunk) of the default line")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a 1 GiB device copy (reference for the traffic counters)")
     return p.parse_args()
@@ -71,11 +73,58 @@ def source_hash(kernel):
     return h.hexdigest()[:16]
 
 
+# Per-step inputs read whole by a step, by workload: extra input sets replace
+# these (large shared tensors such as the main-KV cache, of which a step
+# gathers only the selected rows, are kept).
+ROTATED = {
+    "tiny_2k": (),
+    "full_64k": ("q_idx", "w_idx", "k_idx", "q", "swa"),
+    "reuse_128k": ("q", "swa", "idx"),
+    "full_reindex_1m": (),
+    "prefill_128k": (),
+    "kv_append_64k": ("kv_new", "swa_new"),
+}
+CACHE_BYTES = 256 << 20        # MI355X last-level (Infinity) cache
+
+
+def rotation_sets(name, d, step_bytes, torch, synth, max_sets=64):
+    """Input sets cycled through by consecutive steps so that the bytes the
+    steps read between two uses of one set exceed twice the 256 MB
+    last-level cache: each timed step then reads its inputs from HBM, not
+    from the cache.  Workloads whose step alone reads more (the 1M scan reads
+    1 GiB; the prefill chunk reads 0.6 GB) use one set; so does the tiny
+    latency-bound configuration."""
+    keys = ROTATED[name]
+    n = 1 if not keys else min(max_sets, -(-2 * CACHE_BYTES // max(step_bytes, 1)) + 1)
+    sets = [d]
+    for s in range(1, n):
+        if name == "full_64k":
+            # Same recipe (heavy-tail keys included), another seed.
+            sets.append(synth.make(name, device="cuda", seed=1000 + s))
+            continue
+        g = synth.Gen(1000 + s, "cuda")
+        e = dict(d)
+        for k in keys:
+            t = d[k]
+            if k == "idx":
+                T = d["kv_fp4"].shape[1]
+                e[k] = torch.stack([torch.sort(g.perm(T)[:t.shape[-1]]).values
+                                    for _ in range(t.shape[0])]).to(torch.int32).reshape(t.shape)
+            elif t.dtype == torch.uint8:            # FP8 window entries
+                e[k] = synth.to_fp8_bytes(g.normal(*t.shape))
+            else:                                   # bf16 bits, N(0,1)
+                e[k] = synth.to_bf16_bits(g.normal(*t.shape))
+        sets.append(e)
+    return sets
+
+
 class Step:
     """Buffers and the launch sequence of one hot-path step (all on one stream)."""
 
-    def __init__(self, name, d, csa, torch):
+    def __init__(self, name, d, csa, torch, sets=None):
         self.name, self.d, self.csa, self.torch = name, d, csa, torch
+        self.sets = sets or [d]
+        self.turn = 0
         dev = "cuda"
         B, n_q = d["B"], d["n_q"]
         self.B, self.n_q = B, n_q
@@ -110,8 +159,13 @@ class Step:
         # Zero-filled once, as the block Top-K workspace expects.
         return self.torch.zeros(max(n, 16), dtype=self.torch.uint8, device="cuda")
 
-    def _scan(self):
-        d, csa = self.d, self.csa
+    def _next(self):
+        d = self.sets[self.turn % len(self.sets)]
+        self.turn += 1
+        return d
+
+    def _scan(self, d):
+        csa = self.csa
         csa.index_score(d["q_idx"], d["w_idx"], d["k_idx"], d["vis_len"], block_max=self.bm,
                         scores=getattr(self, "scores", None))
 
@@ -120,39 +174,39 @@ class Step:
         if self.name == "kv_append_64k":
             self.run()
         elif self.name == "reuse_128k":
-            d = self.d
-            self._attn(self.csa.reuse_attn, d["q"], d["swa"], d["idx"], self.out, self.lse)
+            d = self._next()
+            self._attn(d, self.csa.reuse_attn, d["q"], d["swa"], d["idx"], self.out, self.lse)
         else:
-            self._scan()
+            self._scan(self._next())
 
-    def _attn(self, fn, q, swa, idx, out, lse):
-        d = self.d
+    def _attn(self, d, fn, q, swa, idx, out, lse):
         fn(q, d["kv_fp4"], d["kv_scale"], idx, swa, d["swa_pos0"], d["q_pos"], d["sm_scale"], out,
            lse=lse, ws=self.ws_attn)
 
     def run(self):
-        d, csa = self.d, self.csa
+        d, csa = self._next(), self.csa
         if self.name == "kv_append_64k":
             csa.kv_append(d["kv_new"], d["pos"], d["kv_fp4"], d["kv_scale"], swa_new=d["swa_new"],
                           swa_kv=d["swa"], swa_pos0=d["swa_pos0"])
             return
         if self.name == "reuse_128k":
-            self._attn(csa.reuse_attn, d["q"], d["swa"], d["idx"], self.out, self.lse)
+            self._attn(d, csa.reuse_attn, d["q"], d["swa"], d["idx"], self.out, self.lse)
             return
-        self._scan()
+        self._scan(d)
         if self.name == "prefill_128k":
             csa.reindex_topk(csa.MODE_FULL, d["vis_len"], self.N, 512, self.idx, scores=self.scores)
-            self._attn(csa.sparse_attn_decode, d["q"], d["swa"], self.idx, self.out, self.lse)
+            self._attn(d, csa.sparse_attn_decode, d["q"], d["swa"], self.idx, self.out, self.lse)
             return
         csa.block_topk(self.bm, d["vis_len"], self.N, 2048, self.pool, ws=self.ws_bt)
         csa.reindex_topk(csa.MODE_FULL, d["vis_len"], self.N, 512, self.idx, q_idx=d["q_idx"],
                          w_idx=d["w_idx"], k_idx=d["k_idx"], pool_blocks=self.pool, ws=self.ws_re)
-        self._attn(csa.sparse_attn_decode, d["q"], d["swa"], self.idx, self.out, self.lse)
+        self._attn(d, csa.sparse_attn_decode, d["q"], d["swa"], self.idx, self.out, self.lse)
         if hasattr(self, "idx2"):
             csa.reindex_topk(csa.MODE_REINDEX, d["vis_len"], self.N, 512, self.idx2,
                              q_idx=d["q_idx2"], w_idx=d["w_idx2"], k_idx=d["k_idx"],
                              pool_blocks=self.pool, ws=self.ws_re)
-            self._attn(csa.sparse_attn_decode, d["q2"], d["swa2"], self.idx2, self.out2, self.lse2)
+            self._attn(d, csa.sparse_attn_decode, d["q2"], d["swa2"], self.idx2, self.out2,
+                       self.lse2)
 
 
 def algorithmic(name, d):
@@ -273,52 +327,57 @@ def traffic_from_profile(dominant, src_hash, workload):
     return rec.get("bytes_per_launch")
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path has no "
-              "multi-GPU mode in this build.", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    import synth
-    import compressed_sparse_attention_index_amd as csa
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    csa.lib()
-    torch.cuda.set_device(0)
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
+
+def timed(torch, fn, steps):
+    """`steps` back-to-back calls of fn on the current stream, an event after
+    each: (mean ms, p10 ms, p90 ms) of the per-call intervals."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(steps):
+        fn()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    q = lambda f: per[min(len(per) - 1, int(round(f * (len(per) - 1))))]
+    return evs[0].elapsed_time(evs[steps]) / steps, q(0.1), q(0.9)
+
+
+def measure(name, args, torch, synth, csa, cpu=True, graph=True):
+    """One workload: input generation, rotated input sets, eager steps, the
+    dominant kernel alone, optional graph replay and oracle baseline."""
     t0 = time.time()
-    d = synth.make(args.workload, device="cuda")
+    d = synth.make(name, device="cuda")
+    dominant, per_launch, bound, step_bytes = algorithmic(name, d)
+    sets = rotation_sets(name, d, step_bytes or per_launch, torch, synth)
     torch.cuda.synchronize()
-    log(f"[bench] generated {args.workload} on the GPU in {time.time() - t0:.1f} s")
-    step = Step(args.workload, d, csa, torch)
+    log(f"[bench] generated {name} on the GPU ({len(sets)} input set(s)) in "
+        f"{time.time() - t0:.1f} s")
+    step = Step(name, d, csa, torch, sets)
 
     for _ in range(args.warmup):
         step.run()
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(args.steps):
-        step.run()
-    ev1.record()
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
-    # The dominant kernel alone: `steps` back-to-back launches on the same
-    # stream between two events (the launches see the same inputs as a step).
+    ms, p10, p90 = timed(torch, step.run, args.steps)
+    # The dominant call alone: `steps` back-to-back launches on the same
+    # stream (rotating input sets like the steps).
     for _ in range(args.warmup):
         step.dominant()
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(args.steps):
-        step.dominant()
-    ev1.record()
-    torch.cuda.synchronize()
-    dom_ms = ev0.elapsed_time(ev1) / args.steps
-    log(f"[bench] eager: {ms * 1e3:.1f} us/step, dominant kernel {dom_ms * 1e3:.1f} us/launch")
+    dom_ms, dom_p10, dom_p90 = timed(torch, step.dominant, args.steps)
+    log(f"[bench] {name}: eager {ms * 1e3:.1f} us/step (p10 {p10 * 1e3:.1f}, p90 {p90 * 1e3:.1f}), "
+        f"dominant call {dom_ms * 1e3:.1f} us/launch")
 
     graph_ms = None
-    if not args.no_graph:
+    if graph:
         try:
             s = torch.cuda.Stream()
             s.wait_stream(torch.cuda.current_stream())
@@ -330,14 +389,8 @@ def main():
                 step.run()
             for _ in range(args.warmup):
                 g.replay()
-            torch.cuda.synchronize()
-            ev0.record()
-            for _ in range(args.steps):
-                g.replay()
-            ev1.record()
-            torch.cuda.synchronize()
-            graph_ms = ev0.elapsed_time(ev1) / args.steps
-            log(f"[bench] graph replay: {graph_ms * 1e3:.1f} us/step")
+            graph_ms = timed(torch, g.replay, args.steps)[0]
+            log(f"[bench] {name}: graph replay {graph_ms * 1e3:.1f} us/step")
         except Exception as exc:  # graph capture is an extra measurement only
             log(f"[bench] graph replay skipped: {exc!r}")
 
@@ -351,11 +404,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    dominant, per_launch, bound, step_bytes = algorithmic(args.workload, d)
-    append = args.workload == "kv_append_64k"
+    append = name == "kv_append_64k"
     rows = step.rows
     unit = "tokens/s" if append else "query-tokens/s"
-    value = rows / (ms / 1e3)
     if bound == "hbm":
         achieved = per_launch / (dom_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -364,38 +415,75 @@ def main():
         achieved = per_launch / (dom_ms / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+    roof["traffic"] = traffic_from_profile(dominant, source_hash(dominant), name)
     roof["kernel"] = dominant
     roof["per_launch"] = per_launch
     roof["launch_us"] = round(dom_ms * 1e3, 2)
-    roof["traffic"] = traffic_from_profile(dominant, source_hash(dominant), args.workload)
+    roof["launch_us_p10_p90"] = [round(dom_p10 * 1e3, 2), round(dom_p90 * 1e3, 2)]
 
-    cpu = None
-    if not args.no_cpu_baseline:
+    cpu_rec = None
+    if cpu:
         t0 = time.time()
-        cpu = cpu_baseline(args.workload, d, args.cpu_seconds)
-        log(f"[bench] oracle baseline: {cpu['value']:.4f} {cpu['unit']} ({time.time() - t0:.1f} s)")
+        cpu_rec = cpu_baseline(name, d, args.cpu_seconds)
+        cpu_rec["cpu_model"] = cpu_model()
+        log(f"[bench] oracle baseline: {cpu_rec['value']:.4f} {cpu_rec['unit']} "
+            f"({time.time() - t0:.1f} s)")
 
     T = d["kv_fp4"].shape[1]
     if append:
-        cfg = {"workload": args.workload, "batch": d["B"], "tokens_per_sequence": d["n_new"],
+        cfg = {"workload": name, "batch": d["B"], "tokens_per_sequence": d["n_new"],
                "window": d["swa"].shape[1], "main_kv": "MXFP4 (E2M1 + E8M0/32)", "swa_kv": "FP8 E4M3FN"}
     else:
-        cfg = {"workload": args.workload, "batch": d["B"], "query_rows": rows, "context": T,
-               "indexer_k": d.get("kdtype"), "top_k": 512, "pool_blocks": 2048, "window": 128,
+        reuse = name == "reuse_128k"
+        cfg = {"workload": name, "batch": d["B"], "query_rows": rows, "context": T,
+               "indexer_k": None if reuse else d.get("kdtype"), "top_k": 512,
+               "pool_blocks": None if reuse or name == "prefill_128k" else 2048, "window": 128,
                "layers": {"full_64k": "Full", "tiny_2k": "Full", "reuse_128k": "Reuse",
                           "full_reindex_1m": "Full+Reindex",
-                          "prefill_128k": "prefill (m=2)"}[args.workload]}
+                          "prefill_128k": "prefill (m=2)"}[name]}
+    cfg["input_sets"] = len(sets)
     if step_bytes:
         cfg["step_algorithmic_bytes"] = step_bytes
         cfg["step_hbm_frac"] = round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
-    rec = {"metric": APPEND_METRIC if append else METRIC, "value": round(value, 2), "unit": unit,
-           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "fp32" if append else "bf16",
-           "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu}
+    rec = {"value": round(rows / (ms / 1e3), 2), "unit": unit, "ms_per_step": round(ms, 5),
+           "ms_per_step_p10": round(p10, 5), "ms_per_step_p90": round(p90, 5),
+           "config": cfg, "roofline": roof, "cpu_baseline": cpu_rec}
     if graph_ms is not None:
         rec["graph_ms_per_step"] = round(graph_ms, 5)
         rec["graph_value"] = round(rows / (graph_ms / 1e3), 2)
+    del step, sets, d
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path has no "
+              "multi-GPU mode in this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import compressed_sparse_attention_index_amd as csa
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    csa.lib()
+    torch.cuda.set_device(0)
+
+    head = measure(args.workload, args, torch, synth, csa, cpu=not args.no_cpu_baseline,
+                   graph=not args.no_graph)
+    append = args.workload == "kv_append_64k"
+    rec = {"metric": APPEND_METRIC if append else METRIC, "value": head["value"],
+           "unit": head["unit"], "n_gpus": 1, "steps": args.steps, "warmup": args.warmup}
+    rec.update({k: v for k, v in head.items() if k not in ("value", "unit")})
+    rec.update({"higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                "dtype": "fp32" if append else "bf16", "data": "synthetic"})
+    if args.workload == "full_reindex_1m" and not args.no_extra:
+        # The 128K points of the metric: the Reuse-layer decode (B=64) and the
+        # encoder prefill chunk, each with its own dominant call's roofline.
+        rec["points_128k"] = [
+            measure(w, args, torch, synth, csa, cpu=False, graph=False)
+            for w in ("reuse_128k", "prefill_128k")]
     print(json.dumps(rec), flush=True)
 
 

@@ -373,30 +373,44 @@ def test_attention_dense_equals_sdpa_through_gpu():
 
 
 def test_attention_extreme_scale_codes():
-    # Main entries with every E2M1 code (random bytes) and E8M0 codes across
-    # the range the dequantisation holds exactly in bf16: blocks 0..13 take
-    # codes 0 (the subnormal scale 2^-127), 1, 2, 64, 125, 127, 129; blocks
-    # 14 and 15 take 190 and 224 (values up to 6 x 2^97), and the query is
-    # zero on their dims, so the logits stay O(1) while those output dims are
-    # huge and are checked relatively.
+    # E8M0 codes across the range the dequantisation holds exactly in bf16,
+    # one code per block index for every entry: 0 (the subnormal scale
+    # 2^-127), 1, 2, 64, 100, 125, 126, 127, 224 and 190.  The E2M1 nibbles
+    # come from N(0,1) values quantised as in the workloads, whose block
+    # codes sit near 126, so at code 126 a block holds N(0,1)-like values and
+    # at code c they are scaled by 2^(c - 126).  The query is zero on the
+    # dims of the two huge blocks, so the logits stay O(1), and the window
+    # (FP8, O(1)) is zero on the dims of the five tiny blocks.  Each output
+    # dim is compared in units of its block's scale (at least 1 where the
+    # window contributes): the tolerance's absolute term is meant for O(1)
+    # values, and the tiny blocks then check the subnormal scales.
     T, B = 700, 2
     d = synth.decode_workload(B=B, T=T, kdtype="bf16", seed=81)
     rng = np.random.default_rng(81)
-    small = np.array([0, 1, 2, 64, 125, 127, 129], np.uint8)
-    sc = small[rng.integers(0, len(small), size=(B, T, 16))]
-    sc[:, :, 14:] = np.array([190, 224], np.uint8)[rng.integers(0, 2, size=(B, T, 2))]
-    d["kv_scale"] = torch.from_numpy(sc)
-    d["kv_fp4"] = torch.from_numpy(rng.integers(0, 256, size=(B, T, 256), dtype=np.uint8))
+    codes = np.array([0, 1, 2, 64, 100, 125, 126, 126, 126, 127, 126, 126, 126, 126, 224, 190],
+                     np.uint8)
+    d["kv_scale"] = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(codes, (B, T, 16))))
     q = d["q"].view(torch.bfloat16).clone()
     q[..., 448:] = 0
     d["q"] = q.view(torch.int16)
+    d["swa"] = d["swa"].clone()
+    d["swa"][..., :160] = 0
     idx = np.stack([np.sort(rng.choice(T, size=512, replace=False)) for _ in range(B)])
     print("attention extreme E8M0 codes", flush=True)
     out, lse = _attn_gpu(d, torch.from_numpy(idx.astype(np.int32)).reshape(B, 1, 512))
+    unit = np.ldexp(1.0, codes.astype(int) - 126)
+    unit[5:14] = np.maximum(unit[5:14], 1.0)
+    dim_scale = np.repeat(unit, 32)
     for b in range(B):
         o, l = _attn_ref(d, b, 0, idx[b])
-        assert np.abs(o[:, 448:]).max() > 2.0 ** 80
-        check_attention(out[b, 0], lse[b, 0], o, l, what=f"extreme codes row {b}")
+        assert np.abs(o[:, 448:480]).max() > 2.0 ** 90
+        check_attention(out[b, 0], lse[b, 0], o, l, what=f"extreme codes row {b}",
+                        dim_scale=dim_scale)
+        # The subnormal scales are not flushed: where the oracle's output in
+        # the code-0 block exceeds two bf16 subnormal steps, the GPU's is not 0.
+        g0 = out[b, 0][:, :32]
+        big = np.abs(o[:, :32]) > 2 * 2.0 ** -133
+        assert big.any() and np.all(g0[big] & 0x7FFF != 0)
 
 
 def test_attention_single_split_and_reuse_identical():
