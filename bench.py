@@ -31,7 +31,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 # while their hash is unchanged.
 KERNEL_SOURCES = {
     "index_scan": ["index_score.hip", "index_core.h", "csa2_device.h"],
-    "sparse_attn": ["attention.hip", "csa2_device.h"],
+    "sparse_attn": ["attention.hip", "attention_rows.hip", "csa2_device.h"],
     "index_gemm": ["index_gemm.hip", "index_core.h", "csa2_device.h"],
     "kv_append": ["kv_append.hip", "csa2_device.h"],
 }

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["api.hip", "index_score.hip", "index_gemm.hip", "topk.hip", "attention.hip",
-           "kv_append.hip"]
+           "attention_rows.hip", "kv_append.hip"]
 LIB = os.path.join(HERE, "libcsa2.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -20,11 +20,12 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
-# Per-source extra flags.  The attention and prefill-scoring kernels work on
-# their MFMA accumulators with vector ALU code; keeping MFMA results in
-# ordinary VGPRs (not accumulation registers) avoids copying them around.
-EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "index_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags.  The prefill-scoring and whole-row attention
+# kernels work on their MFMA accumulators with vector ALU code; keeping MFMA
+# results in ordinary VGPRs (not accumulation registers) avoids copying them
+# around.
+EXTRA = {"index_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "attention_rows.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd):

@@ -5,72 +5,72 @@
 // 512 dims, window 128), §4 (main KV is MXFP4 and is dequantised before
 // attention, SWA KV is FP8), §9 step 5 (decode attends to the CSA2-selected
 // global KV plus this layer's SWA KV).  DeepSeek-V4 essay (mlqm.cn) §4.3: a
-// compressed entry serves as both key and value.
+// compressed entry serves as both key and value; §6.4: kernels are batch
+// invariant (a query gives the same bits whatever else is in the batch).
 //
-// Work decomposition.  A workgroup (4 waves) takes one query row, all 64
-// heads, and a range of 64-entry chunks of the row's entry list
-//   [ top_k selected slots, padded to a multiple of 32 | 128 window slots ].
-// Every entry of a chunk is gathered, dequantised and written to LDS once,
-// and serves all 64 heads.  Per chunk, wave w = (e, dh) with e = w / 2,
-// dh = w % 2:
-//   1. stages the raw bytes of entry tile e (32 entries) x dims half dh with
-//      direct-to-LDS loads, two chunks ahead, into a private staging slot
-//      (no registers held; waits counted by hand);
-//   2. finishes the previous chunk's O^T[dims][head] += V^T . P^T for dims
-//      quarter w and all 64 heads, with V^T read from the shared LDS buffer
-//      through transposing reads (ds_read_b64_tr_b16), each read feeding the
-//      MFMAs of both head tiles; a barrier follows (the buffer is free);
-//   3. dequantises its tile exactly to bf16 with the gfx950 conversion
-//      instructions, in one pass that writes the shared buffer and forms the
-//      partial S^T[entry][head] over its 256 dims for all 64 heads on
-//      32x32x16 bf16 MFMA (q^T for 64 heads x 256 dims sits in accumulation
-//      registers for the whole row);
-//   4. hands the partial of head tile 1 - dh to its partner (e, 1 - dh) and
-//      receives the partner's partial of head tile dh (one LDS exchange,
-//      one barrier);
-//   5. runs the online softmax (fp32, log2 domain) for entry tile e x head
-//      tile dh and publishes P (bf16, in the accumulator's lane order) with
-//      the tile's reference max and sum (a third barrier).
-// Every wave keeps the running max and sum of all 64 heads, updated
-// identically in all four waves from the published per-tile values.  The
-// reference max moves only when a tile's max exceeds it by more than
-// kLazyRescale, so the accumulators are rarely rescaled.
-// LDS rows are 1024 bytes (one entry); 16-byte chunk k of row r sits at
-// k ^ kswz(r), which keeps the row-wise stores and the transposing reads free
-// of bank conflicts.  Before the first chunk and after the last one the same
-// buffer stages the query row and the output rows, so that both move to and
-// from HBM as whole 1 KB rows.
-// Rows split over several workgroups write (m, l, O) partials that a second
-// kernel merges in split order; when there are enough rows every workgroup
-// covers a whole row and no partials are written.  The partial O (relative
-// to its split's own max) is rounded to bf16, like the output itself: half
-// the bytes of fp32 partials for a rounding error of the same size as the
-// output's; m and l stay fp32.
-#include <type_traits>
-
+// Work decomposition.  A query row's 64 heads are split into four groups of
+// 16; one workgroup takes one (row, head group) and walks the row's whole
+// entry list
+//   [ top_k selected slots, padded to a multiple of 32 | 128 window slots ]
+// in tiles of 32 entries.  The four workgroups of a row get ids that differ
+// by 8, so they run on the same XCD and its L2 serves the row's gathers to
+// all four.  No row is ever split across workgroups over its entries: there
+// are no partial results in memory, no merge kernel and no workspace, and
+// the arithmetic of a row (tile order, wave assignment, merge order) depends
+// only on top_k and the row's own data, never on the other rows of the call.
+//
+// A workgroup is 8 waves in 4 pairs; pair p takes tiles p, p + 4, ...; wave
+// (p, d) of a pair covers dims half d (256 dims).  Per tile, without waiting
+// on the other pairs except at two workgroup barriers:
+//   1. gather: lane (m, c) = (lane % 16, lane / 16) loads, for entries m and
+//      16 + m, 32 bytes of E2M1 (dims 256 d + 64 c .. + 64) and the dword
+//      holding their two E8M0 scales, or 64 FP8 bytes of the same dims for
+//      window entries, straight into registers, one tile ahead;
+//   2. exact dequantisation to bf16 (gfx950 scaled conversions) in the
+//      A-operand layout of v_mfma_f32_16x16x32_bf16 with entries on M:
+//      partial S^T[entry][head] = K . q^T over the wave's dims, contraction
+//      step s taking dims 256 d + 64 c + 8 s .. + 8 from lane group c (q^T,
+//      the B operand, holds the same dims for the whole row); each converted
+//      16-byte piece also goes to the wave's private LDS tile;
+//   3. the two waves of the pair exchange their partial sums through LDS
+//      (barrier), both form S = S_0 + S_1 and run the same softmax in log2
+//      units against a per-head reference that moves only when a tile's
+//      maximum exceeds it by more than kLazyRescale.  The accumulator layout
+//      of S^T (lane (head, c) holds entries 4 c + i and 16 + 4 c + i) is
+//      already the B-operand layout of P^T for the PV product;
+//   4. O^T[dim][head] += V^T . P^T over the tile's 32 entries for the wave's
+//      256 dims, V^T read from its own LDS tile with transposing reads
+//      (ds_read_b64_tr_b16); a second barrier frees the exchange buffer.
+// At the end the four pairs' (reference, sum, O^T) are merged in pair order
+// through LDS and each wave writes 64 dims of the 16 heads.
 #include "csa2_launch.h"
 #include "csa2_device.h"
 
 namespace csa2 {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kChunk = 64;         // entries per chunk: two 32-entry tiles
-constexpr int kTile = 32;
-constexpr int kRow = 1024;         // LDS bytes of one dequantised entry (512 bf16)
-constexpr int kBuf = kChunk * kRow;
-constexpr int kStage = 8192;       // staging bytes per wave and chunk
-constexpr int kMainLoads = 5;      // direct-to-LDS loads per wave: selected tile
-constexpr int kWindowLoads = 8;    //                                 window tile
+constexpr int kWaves = 8;
+constexpr int kPairs = kWaves / 2;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kHeadsPerWg = 16;
+constexpr int kGroupsPerRow = kHeads / kHeadsPerWg;
+constexpr int kTile = 32;                    // entries per tile
+constexpr int kHalfDims = kDim / 2;          // dims of one wave of a pair
+// LDS row of one dequantised half entry (512 bytes) plus 32 bytes of padding:
+// row r then starts 32 r bytes (mod 256) into the 64 banks, so the 16-byte
+// stores of 8 consecutive rows, and the 32-byte pieces a transposing read
+// takes from 8 consecutive rows, each fall in distinct banks with no
+// address swizzle (every per-step offset is an immediate).
+constexpr int kRowBytes = kHalfDims * 2 + 32;
+constexpr int kTileBytes = kTile * kRowBytes;
+static_assert(kMaxWindow == kTile * 4, "one window tile per pair");
+constexpr int kDimTiles = kHalfDims / 16;    // 16-dim tiles of O^T per wave
+constexpr int kSteps = kHalfDims / 32;       // contraction steps of the partial S
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kFillWgs = 256;      // rows are split until about this many workgroups exist
-constexpr int kMaxSplits = 64;
-constexpr int kMaxChunks = (kMaxTopK + kMaxWindow + kChunk - 1) / kChunk;
 constexpr float kLazyRescale = 8.0f;
-static_assert(kMaxChunks <= kMaxSplits, "a row splits at most once per chunk");
-constexpr int kCombineHeads = 4;   // heads (one wave each) per split-merge workgroup
-static_assert(kHeads % kCombineHeads == 0, "whole head groups");
+static_assert(kGroupsPerRow == 4, "row = 4 head groups");
+static_assert(kMaxWindow % kTile == 0 && kMaxTopK % kTile == 0, "whole tiles");
 
 struct AttnArgs {
   const uint16_t* q;
@@ -82,610 +82,429 @@ struct AttnArgs {
   const int32_t* q_pos;
   uint16_t* out;
   float* lse;
-  uint16_t* part_o;  // [rows, nsplit, 64, 512] bf16, or null
-  float* part_ml;    // [rows, nsplit, 64, 2] or null
-  const float* sink; // [64] per-head sink logits (natural log), or null
-  int N_cap, top_k, S_cap, n_q, window, replay_start;
-  int rows, n_chunks, cps, nsplit;
-  float scale2;      // sm_scale * log2(e)
+  const float* sink;   // [64] per-head sink logits (natural log), or null
+  int N_cap, top_k, S_cap, n_q, window, replay_start, rows;
+  float scale2;        // sm_scale * log2(e)
 };
 
 struct Smem {
-  uint8_t kv[kBuf];              // dequantised entries of a chunk [entry][dims], swizzled
-  uint8_t stage[2][4][kStage];   // raw bytes [chunk parity][wave]
-  f32x4_t sx[4][4][64];          // partial S^T handed to the partner, [wave][i / 4][lane]
-  u32x4 pb[2][2][2][64];         // P^T (bf16) [entry tile][head tile][16-entry step][lane]
-  float pml[2][2][32][2];        // (reference max, sum) [entry tile][head tile][head]
-  int ids[kMaxChunks * kChunk];  // selected ids of the workgroup's chunks (-1: none)
+  uint8_t tile[kWaves][kTileBytes];     // dequantised half entries [entry][dims]; O^T at the end
+  f32x4_t xs[kWaves][2][64];            // partial S^T handed to the partner
+  float ml[kPairs][kHeadsPerWg][2];     // per pair and head: reference max (log2), sum
+  int32_t ids[kMaxTopK];                // the row's selected ids (-1: no entry)
+  uint32_t ready[kWaves];               // last round whose partial is in xs[wave]
+  uint32_t taken[kWaves];               // last round in which the wave read its partner's partial
 };
 
 struct Ctx {
-  int r, b, tkp, qpos, lo, p0, slot0, wave, lane, c, half, e, dh;
+  int r, b, hg, wave, pair, d, lane, m, c;
+  int sel_tiles, qpos, p0, lo;
+};
+
+// A tile's raw bytes for one lane, halves h = 0, 1 (entries m and 16 + m).
+// Selected entries (MainRaw): f[h][0..1] = E2M1 bytes 128 d + 32 c .. + 32,
+// sc[h] = the dword of E8M0 scales holding blocks 8 d + 2 c and 8 d + 2 c +
+// 1.  Window entries (WinRaw): v[h][0..3] = FP8 bytes 256 d + 64 c .. + 64.
+struct MainRaw {
+  u32x4 f[2][2];
+  uint32_t sc[2];
+  bool valid[2];
+};
+struct WinRaw {
+  u32x4 v[2][4];
+  bool valid[2];
 };
 
 struct State {
-  u32x4 qb[2][16];   // q^T: head 32 h + c, dims 256 dh + 128 half + 8 k + [0, 8)
-  f32x16 o[4][2];    // O^T: dims 128 w + 32 m + 8 (i / 4) + 4 half + i % 4, head 32 h + c
-  float m_run[2], l_run[2];   // heads c and 32 + c
+  u32x4 qb[kSteps];        // q^T B operands: head m, dims 256 d + 64 c + 8 s .. + 8
+  f32x4_t o[kDimTiles];    // O^T: lane (head m, c) holds dims 256 d + 16 t + 4 c + i
+  float m_ref, l;          // per head (every lane of head m holds the same)
+  uint32_t exchanged;      // last round in which the pair exchanged partial sums
 };
 
-// Swizzle of the 16-byte chunks of LDS row r (a bijection of r's low four
-// bits): a row-wise store by 16 lanes, and each 16- or 32-lane group of a
-// transposing read, touches every bank at most once.
-__device__ __forceinline__ int kswz(int r) {
-  return ((r >> 2) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2) | (((r ^ (r >> 3)) & 1) << 3);
+__device__ __forceinline__ f32x4_t mfma16(bf16x8 a, bf16x8 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bool tile_is_main(const Ctx& x, int ch) {
-  return kChunk * ch + kTile * x.e < x.tkp;
+__device__ __forceinline__ uint32_t word_of(const u32x4& w, int k) {
+  return k == 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w;
 }
 
-__device__ __forceinline__ uint32_t word_of(const u32x4& w4, int k) {
-  return k == 0 ? w4.x : k == 1 ? w4.y : k == 2 ? w4.z : w4.w;
-}
-
-// Two floats -> two bf16 (round to nearest even), lo in the low half: one
-// v_cvt_pk_bf16_f32 (converting the halves one by one takes four).
+// Two floats -> two bf16 (round to nearest even), lo in the low half.
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-__device__ __forceinline__ bf16x8 tr_read_pair(const uint8_t* v, int off0, int off1) {
-  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v + off0));
-  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v + off1));
-  typedef short i16x8 __attribute__((ext_vector_type(8)));
-  const i16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return __builtin_bit_cast(bf16x8, r);
+// Max and sum over the four lanes of one head (lanes m + 16 c').
+__device__ __forceinline__ float head_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float head_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Issues the wave's direct-to-LDS loads of its tile of chunk ch (entry tile
-// e, dims half dh) into staging slot `stg` and returns whether the lane's
-// slot holds an entry.  Slot layout: load i of lane l lands at 1024 i + 16 l
-// (selected tiles: 4 x 16 B of E2M1 and, at 4096 + 4 l, the 4 E8M0 scales;
-// window tiles: 8 x 16 B of FP8).  An empty slot reads a row that always
-// exists (entry 0 of the sequence, or the query row), so every tile of a kind
-// issues a fixed number of loads; it is zeroed when dequantised.
-__device__ __forceinline__ bool issue_tile(const AttnArgs& a, const Ctx& x, Smem& sm, int ch,
-                                           int stg) {
-  const int slot = kChunk * ch + kTile * x.e + x.c;
-  const uint32_t dst = lds_offset(sm.stage[stg][x.wave]);
-  if (tile_is_main(x, ch)) {
-    const int id = sm.ids[slot - x.slot0];
-    const bool valid = id >= 0;
-    const size_t er = static_cast<size_t>(x.b) * a.N_cap + (valid ? id : 0);
-    const uint8_t* src = a.kv_fp4 + er * 256 + 128 * x.dh + 64 * x.half;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(src + 16 * i, dst + 1024 * i);
-    dma4(a.kv_scale + er * 16 + 8 * x.dh + 4 * x.half, dst + 4096);
-    return valid;
-  }
-  const int j = slot - x.tkp;
-  const int p = x.qpos - (kMaxWindow - 1) + j;
-  const bool valid = j < kMaxWindow && p >= x.lo && p <= x.qpos && p - x.p0 < a.S_cap;
-  const uint8_t* row =
-      valid ? a.swa + (static_cast<size_t>(x.b) * a.S_cap + (p - x.p0)) * 512
-            : reinterpret_cast<const uint8_t*>(a.q + static_cast<size_t>(x.r) * kHeads * kDim);
-  const uint8_t* src = row + 256 * x.dh + 128 * x.half;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) dma16(src + 16 * i, dst + 1024 * i);
-  return valid;
-}
-
-// Dequantisation of the lane's entry from its staging slot, 16 bytes of raw
-// data (a unit) at a time: a unit holds 8-dim groups k = 4 u .. 4 u + 3 of
-// E2M1 (selected entries) or k = 2 u, 2 u + 1 of FP8 (window); group k is
-// dims 256 dh + 128 half + 8 k.  Empty slots give zeros: scale 0 for E2M1,
-// which has no NaN; zeroed bytes for FP8.
-template <bool kMain>
-struct Dequant {
-  static constexpr int kPerUnit = kMain ? 4 : 2;
-  static constexpr int kUnits = 16 / kPerUnit;
-  float scale[4];
-  const uint8_t* sp;
-  bool valid;
-  __device__ __forceinline__ Dequant(const uint8_t* slot, int lane, bool lane_valid)
-      : sp(slot + 16 * lane), valid(lane_valid) {
-    if (kMain) {
-      const uint32_t sc = *reinterpret_cast<const uint32_t*>(slot + 4096 + 4 * lane);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t code = (sc >> (8 * i)) & 0xffu;
-        uint32_t bits = code == 0 ? 0x00400000u : (code == 255 ? 0x7fc00000u : code << 23);
-        scale[i] = __uint_as_float(lane_valid ? bits : 0u);
-      }
-    }
-  }
-  __device__ __forceinline__ u32x4 unit(int u) const {
-    return *reinterpret_cast<const u32x4*>(sp + 1024 * u);
-  }
-  __device__ __forceinline__ bf16x8 convert(const u32x4& w, int k) const {
-    if (kMain) return fp4x8_to_bf16x8(word_of(w, k & 3), scale[k >> 2]);
-    const uint32_t lo = (k & 1) ? w.z : w.x, hi = (k & 1) ? w.w : w.y;
-    return fp8x8_to_bf16x8(valid ? lo : 0u, valid ? hi : 0u);
-  }
-};
-
-// Moves the running max and sum past the chunk just finished (from the
-// per-tile reference maxima and sums its waves published) and rescales the
-// accumulators when the max moves.  Where a tile's reference differs from the
-// new max, the wave that published that tile's P rescales it in LDS before
-// anyone reads it.  All waves run this on the same values, so they take the
-// same branches (and barrier) and keep identical (m, l).
-__device__ __forceinline__ void pv_prep(const Ctx& x, Smem& sm, State& st) {
-  float b[2][2];   // [head tile][entry tile]
+// Issues the loads of selected-entry tile t (wave-uniform) into w.  Every
+// call issues the same loads (a tile past the list reads slots that hold -1
+// and so entry 0 of the sequence), so that the compiler can count the loads
+// still in flight on every path and wait only for the ones it needs.
+__device__ __forceinline__ void gather_main(const AttnArgs& a, const Ctx& x, const int32_t* ids,
+                                            int t, MainRaw& w) {
+  t = min(t, kMaxTopK / kTile - 1);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const float c0 = sm.pml[0][h][x.c][0], s0 = sm.pml[0][h][x.c][1];
-    const float c1 = sm.pml[1][h][x.c][0], s1 = sm.pml[1][h][x.c][1];
-    const float mn = fmaxf(c0, c1);   // never below m_run
-    const float mr = st.m_run[h];
-    const float alpha =
-        mn == mr ? 1.0f : (mr == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mr - mn));
-    b[h][0] = c0 == mn ? 1.0f : (c0 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(c0 - mn));
-    b[h][1] = c1 == mn ? 1.0f : (c1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(c1 - mn));
-    st.l_run[h] = st.l_run[h] * alpha + (s0 * b[h][0] + s1 * b[h][1]);
-    st.m_run[h] = mn;
-    // (While the max is still -inf nothing has been accumulated: O is zero.)
-    if (__ballot(alpha != 1.0f && mr != -__builtin_inff()) != 0) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) st.o[m][h] *= alpha;
-    }
+    const int id = ids[kTile * t + 16 * h + x.m];
+    const bool valid = id >= 0;
+    w.valid[h] = valid;
+    const size_t er = static_cast<size_t>(x.b) * a.N_cap + (valid ? id : 0);
+    const uint8_t* src = a.kv_fp4 + er * 256 + 128 * x.d + 32 * x.c;
+    w.f[h][0] = *reinterpret_cast<const u32x4*>(src);
+    w.f[h][1] = *reinterpret_cast<const u32x4*>(src + 16);
+    w.sc[h] = *reinterpret_cast<const uint32_t*>(a.kv_scale + er * 16 + 8 * x.d + 4 * (x.c >> 1));
   }
-  const bool fix = b[0][0] != 1.0f || b[0][1] != 1.0f || b[1][0] != 1.0f || b[1][1] != 1.0f;
-  if (__ballot(fix) != 0) {
-    const float be = x.dh ? (x.e ? b[1][1] : b[1][0]) : (x.e ? b[0][1] : b[0][0]);
+}
+
+// Issues the loads of window tile u (positions q_pos - 127 + 32 u ..) into w.
+__device__ __forceinline__ void gather_window(const AttnArgs& a, const Ctx& x, int u, WinRaw& w) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const u32x4 w = sm.pb[x.e][x.dh][t][x.lane];
-      u32x4 r;
+  for (int h = 0; h < 2; ++h) {
+    const int j = kTile * u + 16 * h + x.m;
+    const int p = x.qpos - (kMaxWindow - 1) + j;
+    const bool valid = p >= x.lo && p <= x.qpos && p - x.p0 < a.S_cap;
+    w.valid[h] = valid;
+    // An empty slot reads the query row, which always exists.
+    const uint8_t* row =
+        valid ? a.swa + (static_cast<size_t>(x.b) * a.S_cap + (p - x.p0)) * 512
+              : reinterpret_cast<const uint8_t*>(a.q + static_cast<size_t>(x.r) * kHeads * kDim);
+    const uint8_t* src = row + 256 * x.d + 64 * x.c;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t u = word_of(w, k);
-        const uint32_t v = pack_bf16x2(__uint_as_float(u << 16) * be,
-                                       __uint_as_float(u & 0xffff0000u) * be);
-        if (k == 0) r.x = v;
-        else if (k == 1) r.y = v;
-        else if (k == 2) r.z = v;
-        else r.w = v;
+    for (int k = 0; k < 4; ++k) w.v[h][k] = *reinterpret_cast<const u32x4*>(src + 16 * k);
+  }
+}
+
+// Dequantisation, LDS store and the partial S^T = K . q^T of one tile.
+// Step s: lane (m, c) supplies dims 256 d + 64 c + 8 s .. + 8 of entry
+// 16 h + m, which is 16-byte chunk 8 c + s of its LDS row.
+template <bool kMain, class R>
+__device__ __forceinline__ void qk_tile(const Ctx& x, const R& w, const State& st, uint8_t* tile,
+                                        f32x4_t (&acc)[2]) {
+  float scale[2][2];
+  if constexpr (kMain) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // Blocks 8 d + 2 c + k: bytes 2 (c % 2) + k of the loaded dword.
+      const uint32_t two = w.sc[h] >> (16 * (x.c & 1));
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        // E8M0 -> 2^(code - 127): code 0 is the subnormal 2^-127, code 255
+        // NaN.  An empty slot gets scale 0 (E2M1 has no NaN, so its values
+        // become 0).  Selects only, no branches.
+        const uint32_t code = (two >> (8 * k)) & 0xffu;
+        uint32_t bits = code << 23;
+        bits = code == 0 ? 0x00400000u : bits;
+        bits = code == 255 ? 0x7fc00000u : bits;
+        scale[h][k] = __uint_as_float(w.valid[h] ? bits : 0u);
       }
-      sm.pb[x.e][x.dh][t][x.lane] = r;
     }
-    lds_barrier();
   }
-}
-
-// Transposing-read offsets of the wave's V^T operands for 32-dim block m of
-// dims quarter w, 16-entry step j: lane (i16 = lane % 16) reads 8 bytes at
-// entry 16 j + 4 half + i16 / 4 (a) and 16 j + 8 + 4 half + i16 / 4 (b), dims
-// 128 w + 32 m + 16 ((lane / 16) % 2) + 4 (i16 % 4).  The 8 values a lane
-// receives are entries 16 j + 8 (i / 4) + 4 half + i % 4, the order of the
-// accumulator elements 8 t + i of P (j = 2 e + t).  Bits 6-7 of an offset
-// are the block m XORed with the row's swizzle, so block m is base ^ (64 m),
-// and step j adds 16 rows.
-struct TrOffs {
-  int a, b;
-  __device__ __forceinline__ int off_a(int m, int j) const { return (a ^ (64 * m)) + 16 * kRow * j; }
-  __device__ __forceinline__ int off_b(int m, int j) const { return (b ^ (64 * m)) + 16 * kRow * j; }
-};
-
-__device__ __forceinline__ TrOffs tr_offsets(const Ctx& x) {
-  const int i16 = x.lane & 15;
-  const int cl = 2 * ((x.lane >> 4) & 1) + ((i16 & 3) >> 1);
-  const int byte = 8 * (i16 & 1);
-  const int ra = 4 * x.half + (i16 >> 2), rb = ra + 8;
-  TrOffs t;
-  t.a = ra * kRow + 16 * (16 * x.wave + (cl ^ kswz(ra))) + byte;
-  t.b = rb * kRow + 16 * (16 * x.wave + (cl ^ kswz(rb))) + byte;
-  return t;
-}
-
-// The loops below are software-pipelined by hand (the next raw unit and the
-// next V^T operand are read one step ahead) and fenced per step, so that the
-// scheduler does not hoist every LDS read of the chunk and run out of
-// registers.
-
-// Chunk ch's tile: dequantised once, written to the LDS buffer (16-byte chunk
-// k of the lane's row at st_off ^ (k << 4)) and multiplied into the partial
-// S^T of both head tiles.
-template <bool kMain>
-__device__ __forceinline__ void qk_store(const Ctx& x, Smem& sm, const State& st,
-                                         const uint8_t* slot, bool valid, int st_off,
-                                         f32x16 (&acc)[2]) {
-  using D = Dequant<kMain>;
-  const D dq(slot, x.lane, valid);
-  u32x4 raw[2];
-  raw[0] = dq.unit(0);
+  // Two accumulators per half (even and odd steps), added at the end: four
+  // independent MFMA chains hide the result latency of each product.
+  f32x4_t part[2][2];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int u = k / D::kPerUnit;
-    if (k % D::kPerUnit == 0 && u + 1 < D::kUnits) raw[(u + 1) & 1] = dq.unit(u + 1);
-    const bf16x8 kb = dq.convert(raw[u & 1], k);
-    *reinterpret_cast<bf16x8*>(sm.kv + (st_off ^ (k << 4))) = kb;
-    acc[0] = mfma32(kb, __builtin_bit_cast(bf16x8, st.qb[0][k]), acc[0]);
-    acc[1] = mfma32(kb, __builtin_bit_cast(bf16x8, st.qb[1][k]), acc[1]);
+  for (int h = 0; h < 2; ++h) part[h][0] = part[h][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 kb;
+      if constexpr (kMain) {
+        kb = fp4x8_to_bf16x8(word_of(w.f[h][s >> 2], s & 3), scale[h][s >> 2]);
+      } else {
+        const u32x4& q4 = w.v[h][s >> 1];
+        const uint32_t lo = (s & 1) ? q4.z : q4.x, hi = (s & 1) ? q4.w : q4.y;
+        kb = fp8x8_to_bf16x8(w.valid[h] ? lo : 0u, w.valid[h] ? hi : 0u);
+      }
+      *reinterpret_cast<bf16x8*>(tile + (16 * h + x.m) * kRowBytes + 16 * (8 * x.c + s)) = kb;
+      part[h][s & 1] = mfma16(kb, __builtin_bit_cast(bf16x8, st.qb[s]), part[h][s & 1]);
+    }
+    // One step at a time: unfenced, the scheduler hoists the conversions of
+    // every step and runs out of registers.
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  acc[0] = part[0][0] + part[0][1];
+  acc[1] = part[1][0] + part[1][1];
+}
+
+// Transposing read of V^T for one A operand: lanes of group c read rows
+// (entries) 4 c + j / 4 (a) and 16 + 4 c + j / 4 (b), dims 16 t + 4 (j % 4)
+// .. + 4 (j = lane % 16); lane j then holds dim 16 t + j of entries 4 c ..
+// 4 c + 3 and 16 + 4 c .. + 3, the k order of P^T's B operand.
+__device__ __forceinline__ bf16x8 tr_read_pair(const uint8_t* tile, int off_a, int off_b) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off_a));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off_b));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Softmax of the tile (S = the pair's two partial sums) and O^T += V^T . P^T.
+__device__ __forceinline__ void softmax_pv(const AttnArgs& a, const Ctx& x, uint32_t vm0,
+                                           uint32_t vm1, const uint8_t* tile, int off_a, int off_b,
+                                           const f32x4_t (&s0)[2], const f32x4_t (&s1)[2],
+                                           State& st) {
+  // Validity of entry 16 h + e is bit e of vm_h; lane (m, c) holds entries
+  // 16 h + 4 c + i.
+  float xv[8];
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int h = i >> 2;
+    const bool v = ((h ? vm1 : vm0) >> (4 * x.c + (i & 3))) & 1u;
+    // The partner's partial is added in the same order in both waves.
+    const float s = s0[h][i & 3] + s1[h][i & 3];
+    xv[i] = v ? s * a.scale2 : -__builtin_inff();
+    mx = fmaxf(mx, xv[i]);
+  }
+  mx = head_max(mx);
+  // Reference: kept unless still -inf or exceeded by more than kLazyRescale.
+  const float mr = st.m_ref;
+  const float ref = (mr == -__builtin_inff() || mx > mr + kLazyRescale) ? mx : mr;
+  if (ref != mr) {
+    // A finite mr means O and l hold sums relative to it: rescale them.
+    const float alpha = mr == -__builtin_inff() ? 1.0f : __builtin_amdgcn_exp2f(mr - ref);
+    if (__ballot(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int t = 0; t < kDimTiles; ++t) st.o[t] *= alpha;
+      st.l *= alpha;
+    }
+    st.m_ref = ref;
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    xv[i] = xv[i] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(xv[i] - st.m_ref);
+    sum += xv[i];
+  }
+  st.l += head_sum(sum);
+  const u32x4 pw = {pack_bf16x2(xv[0], xv[1]), pack_bf16x2(xv[2], xv[3]),
+                    pack_bf16x2(xv[4], xv[5]), pack_bf16x2(xv[6], xv[7])};
+  const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+  // The wave's own LDS stores of this tile precede these reads in issue
+  // order (the LDS operations of a wave complete in order).
+  // V^T operands read kAhead dims tiles ahead of their product (LDS latency
+  // is several products long).
+  constexpr int kAhead = 4;
+  bf16x8 va[kAhead];
+#pragma unroll
+  for (int t = 0; t < kAhead; ++t) va[t] = tr_read_pair(tile, off_a + 32 * t, off_b + 32 * t);
+#pragma unroll
+  for (int t = 0; t < kDimTiles; ++t) {
+    const bf16x8 cur = va[t % kAhead];
+    if (t + kAhead < kDimTiles)
+      va[t % kAhead] = tr_read_pair(tile, off_a + 32 * (t + kAhead), off_b + 32 * (t + kAhead));
+    st.o[t] = mfma16(cur, pb, st.o[t]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// O^T += V^T . P^T for the chunk in the LDS buffer (P^T of 16-entry step
-// j = 2 e + t is pb[e][h][t]).
-__device__ __forceinline__ void pv(const Ctx& x, const Smem& sm, State& st, const TrOffs& tr) {
-  bf16x8 va[2];
-  u32x4 pbv[2][2];
-  va[0] = tr_read_pair(sm.kv, tr.off_a(0, 0), tr.off_b(0, 0));
-  pbv[0][0] = sm.pb[0][0][0][x.lane];
-  pbv[0][1] = sm.pb[0][1][0][x.lane];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int j = k >> 2, m = k & 3;
-    if (k + 1 < 16) {
-      const int j1 = (k + 1) >> 2, m1 = (k + 1) & 3;
-      va[(k + 1) & 1] = tr_read_pair(sm.kv, tr.off_a(m1, j1), tr.off_b(m1, j1));
-      if (m == 0 && j + 1 < 4) {
-        pbv[(j + 1) & 1][0] = sm.pb[(j + 1) >> 1][0][(j + 1) & 1][x.lane];
-        pbv[(j + 1) & 1][1] = sm.pb[(j + 1) >> 1][1][(j + 1) & 1][x.lane];
-      }
-    }
-    st.o[m][0] = mfma32(va[k & 1], __builtin_bit_cast(bf16x8, pbv[j & 1][0]), st.o[m][0]);
-    st.o[m][1] = mfma32(va[k & 1], __builtin_bit_cast(bf16x8, pbv[j & 1][1]), st.o[m][1]);
-    __builtin_amdgcn_sched_barrier(0);
+// Waits (bounded) until the LDS counter reaches `want`.  The two waves of a
+// pair synchronise only with each other through these counters, so the four
+// pairs of a workgroup run independently and the two waves that share a SIMD
+// overlap one's products with the other's conversions.  A pair's rounds
+// always complete (each wave signals every round it works on), so the wait
+// ends; the bound only guards against a wave that never signals.
+__device__ __forceinline__ void wait_counter(const uint32_t* ctr, uint32_t want) {
+  for (int spin = 0; spin < (1 << 22); ++spin) {
+    if (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= want) return;
+    __builtin_amdgcn_s_sleep(1);
   }
 }
+__device__ __forceinline__ void signal_counter(uint32_t* ctr, uint32_t v) {
+  __hip_atomic_store(ctr, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 
-// Chunk ch, staged in slot S; kPV: the previous chunk's PV comes first.
-// `valid` (the lane's slot validity) is replaced by that of chunk ch + 2,
-// whose loads go to the same slot once it has been read.
-template <bool kMain, bool kPV>
-__device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Ctx& x, Smem& sm, State& st,
-                                             bool& valid, int ch, int c1, int S, int st_off,
-                                             const TrOffs& tr) {
-  if (kPV) {
-    pv_prep(x, sm, st);
-    pv(x, sm, st, tr);
-    // Every wave is done reading the buffer: it takes this chunk.
-    lds_barrier();
-  }
-  // This chunk's loads have landed once only chunk ch + 1's are outstanding.
-  if (ch + 1 < c1) {
-    if (tile_is_main(x, ch + 1)) wait_vmem<kMainLoads>();
-    else wait_vmem<kWindowLoads>();
-  } else {
-    wait_vmem<0>();
-  }
-  asm volatile("" ::: "memory");
-  const uint8_t* slot = sm.stage[S][x.wave];
-  const uint32_t vmask = static_cast<uint32_t>(__ballot(valid));
-  f32x16 acc[2] = {f32x16{}, f32x16{}};
-  qk_store<kMain>(x, sm, st, slot, valid, st_off, acc);
-  // The staging slot has been read; chunk ch + 2 goes there.
-  if (ch + 2 < c1) valid = issue_tile(a, x, sm, ch + 2, S);
-
-  // Exchange with the partner wave (e, 1 - dh): it gets this wave's partial
-  // of head tile 1 - dh, this wave gets its partial of head tile dh
-  // (a + b == b + a exactly, so the order of the two halves is immaterial).
-  auto give = [&](const f32x16& g) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sm.sx[x.wave][i][x.lane] = f32x4_t{g[4 * i], g[4 * i + 1], g[4 * i + 2], g[4 * i + 3]};
-  };
-  if (x.dh) give(acc[0]);
-  else give(acc[1]);
-  lds_barrier();
-
-  // Sums S of head 32 dh + c for entries rho = 8 (i / 4) + 4 half + i % 4 of
-  // the tile; empty slots get S = -inf.
-  float xv[16];
-  auto sum_halves = [&](const f32x16& keep) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4_t other = sm.sx[x.wave ^ 1][i][x.lane];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) xv[4 * i + j] = keep[4 * i + j] + other[j];
-    }
-  };
-  if (x.dh) sum_halves(acc[1]);
-  else sum_halves(acc[0]);
-  if (vmask != 0xffffffffu) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int rho = 8 * (i >> 2) + 4 * x.half + (i & 3);
-      if (!((vmask >> rho) & 1u)) xv[i] = -__builtin_inff();
-    }
-  }
-  float smax = xv[0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) smax = fmaxf(smax, xv[i]);
-  smax = fmaxf(smax, other_half(smax));
-  // Logits are S * scale2 (log2 units, scale2 > 0, so the tile's max logit
-  // is smax * scale2).  The tile's reference: the running max, unless that
-  // is still -inf or the tile exceeds it by more than kLazyRescale.
-  const float tmax = smax * a.scale2;
-  const float mr = x.dh ? st.m_run[1] : st.m_run[0];
-  const float cand = (mr == -__builtin_inff() || tmax > mr + kLazyRescale) ? tmax : mr;
-  const float mref = cand == -__builtin_inff() ? 0.0f : cand;
-  float tsum = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    xv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(xv[i], a.scale2, -mref));
-    tsum += xv[i];
-  }
-  tsum += other_half(tsum);
-#pragma unroll
-  for (int t2 = 0; t2 < 2; ++t2)
-    sm.pb[x.e][x.dh][t2][x.lane] =
-        u32x4{pack_bf16x2(xv[8 * t2], xv[8 * t2 + 1]), pack_bf16x2(xv[8 * t2 + 2], xv[8 * t2 + 3]),
-              pack_bf16x2(xv[8 * t2 + 4], xv[8 * t2 + 5]),
-              pack_bf16x2(xv[8 * t2 + 6], xv[8 * t2 + 7])};
-  if (x.half == 0) {
-    sm.pml[x.e][x.dh][x.c][0] = cand;
-    sm.pml[x.e][x.dh][x.c][1] = tsum;
-  }
-  lds_barrier();
+// Round `round` (numbered from 1) of one pair: its tile, processed only when
+// `work` (the same in both waves of the pair).  The exchange: a wave writes
+// its partial S^T once its partner has taken the one of the pair's previous
+// exchange, signals it, and reads the partner's once that is signalled.
+template <bool kMain, class R>
+__device__ __forceinline__ void round_tile(const AttnArgs& a, const Ctx& x, Smem& sm, const R& w,
+                                           bool work, uint32_t round, uint8_t* tile, int off_a,
+                                           int off_b, State& st) {
+  if (!work) return;
+  f32x4_t acc[2];
+  qk_tile<kMain, R>(x, w, st, tile, acc);
+  const int partner = x.wave ^ 1;
+  wait_counter(&sm.taken[partner], st.exchanged);
+  st.exchanged = round;
+  sm.xs[x.wave][0][x.lane] = acc[0];
+  sm.xs[x.wave][1][x.lane] = acc[1];
+  signal_counter(&sm.ready[x.wave], round);
+  wait_counter(&sm.ready[partner], round);
+  f32x4_t other[2] = {sm.xs[partner][0][x.lane], sm.xs[partner][1][x.lane]};
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): both reads have returned
+  signal_counter(&sm.taken[x.wave], round);
+  const uint32_t vm0 = static_cast<uint32_t>(__ballot(w.valid[0])) & 0xffffu;
+  const uint32_t vm1 = static_cast<uint32_t>(__ballot(w.valid[1])) & 0xffffu;
+  if (x.d == 0) softmax_pv(a, x, vm0, vm1, tile, off_a, off_b, acc, other, st);
+  else softmax_pv(a, x, vm0, vm1, tile, off_a, off_b, other, acc, st);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) Smem sm;
-
-  const int pair = blockIdx.x;
   Ctx x;
-  x.r = pair / a.nsplit;
-  const int split = pair - x.r * a.nsplit;
+  // Workgroup id -> (row, head group): the four head groups of row r have
+  // ids 32 (r / 8) + 8 hg + r % 8, i.e. the same id modulo 8 (one XCD).
+  const int id = blockIdx.x;
+  x.r = (id >> 5) * 8 + (id & 7);
+  x.hg = (id >> 3) & 3;
+  if (x.r >= a.rows) return;
   x.b = x.r / a.n_q;
   x.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  x.pair = x.wave >> 1;
+  x.d = x.wave & 1;
   x.lane = threadIdx.x & 63;
-  x.c = x.lane & 31;
-  x.half = x.lane >> 5;
-  x.e = x.wave >> 1;
-  x.dh = x.wave & 1;
-  x.tkp = (a.top_k + kTile - 1) / kTile * kTile;
+  x.m = x.lane & 15;
+  x.c = x.lane >> 4;
+  x.sel_tiles = (a.top_k + kTile - 1) / kTile;
   x.qpos = a.q_pos[x.r];
   x.p0 = a.swa_pos0[x.b];
   x.lo = max(max(x.qpos - a.window + 1, x.p0), 0);
   if (a.replay_start >= 0) x.lo = max(x.lo, a.replay_start);
-  const int c0 = split * a.cps;
-  const int c1 = min(c0 + a.cps, a.n_chunks);
-  x.slot0 = kChunk * c0;
 
-  // The selected ids of chunks [c0, c1) go to LDS first, so that no gather
-  // waits on a global id load; out-of-range ids become -1 (no entry).  The
-  // id loads and the q loads are all issued before any is used.
-  constexpr int kPer = (kMaxChunks * kChunk + kThreads - 1) / kThreads;
-  int sid[kPer];
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int slot = x.slot0 + threadIdx.x + kThreads * u;
-    sid[u] = -1;
-    if (slot < kChunk * c1 && slot < a.top_k)
-      sid[u] = a.idx[static_cast<size_t>(x.r) * a.top_k + slot];
-  }
-  // The query row (64 heads x 1 KB) goes to the K/V buffer, which is free
-  // until the first chunk is stored: wave w fetches head rows 16 w .. 16 w +
-  // 15 with one coalesced 1 KB load per row, lane l taking 16-byte chunk
-  // l ^ kswz(row) so that chunk C of a row lands at slot C ^ kswz(row).
+  // The row's selected ids go to LDS first (out-of-range ids and the slots
+  // past top_k up to the tile boundary become -1: no entry).
   {
-    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q + static_cast<size_t>(x.r) * kHeads * kDim);
-    const uint32_t kv0 = lds_offset(sm.kv);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 16 * x.wave + i;
-      dma16(qrow + row * kRow + 16 * (x.lane ^ kswz(row)), kv0 + row * kRow);
+    const int32_t* irow = a.idx + static_cast<size_t>(x.r) * a.top_k;
+    const int slot = threadIdx.x;
+    const int v = slot < a.top_k ? irow[slot] : -1;
+    sm.ids[slot] = (v >= 0 && v < a.N_cap) ? v : -1;
+    if (slot < kWaves) {
+      sm.ready[slot] = 0;
+      sm.taken[slot] = 0;
     }
   }
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int i = threadIdx.x + kThreads * u;
-    if (i < kChunk * (c1 - c0)) sm.ids[i] = (sid[u] >= 0 && sid[u] < a.N_cap) ? sid[u] : -1;
-  }
-  // The ids and the query row have landed (every wave's) before the first
-  // gather is issued: no other vector-memory load is in flight inside the
-  // loop.
-  wait_vmem<0>();
-  __syncthreads();
-
-  bool valid0 = issue_tile(a, x, sm, c0, 0);
-  bool valid1 = false;
-  if (c0 + 1 < c1) valid1 = issue_tile(a, x, sm, c0 + 1, 1);
-  // q^T operands (head 32 h + c, dims 256 dh + 128 half + 8 k).  q is only
-  // ever an MFMA operand, which may come from accumulation registers:
-  // keeping it there leaves the VGPRs to the accumulators and the operands
-  // in flight.
+  // q^T operands of head 16 hg + m: step s takes dims 256 d + 64 c + 8 s ..
+  // + 8 (16 bytes at 512 d + 128 c + 16 s of the head's row).
   State st;
+  {
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(
+        a.q + (static_cast<size_t>(x.r) * kHeads + kHeadsPerWg * x.hg + x.m) * kDim);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = 32 * h + x.c;
-    u32x4 v[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-      v[k] = *reinterpret_cast<const u32x4*>(
-          sm.kv + row * kRow + 16 * ((32 * x.dh + 16 * x.half + k) ^ kswz(row)));
-#pragma unroll
-    for (int k = 0; k < 16; ++k) st.qb[h][k] = to_agpr(v[k]);
+    for (int s = 0; s < kSteps; ++s)
+      st.qb[s] = *reinterpret_cast<const u32x4*>(qrow + 512 * x.d + 128 * x.c + 16 * s);
   }
-  // Every wave has its q before the first chunk goes to the buffer.
-  lds_barrier();
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    st.o[m][0] = f32x16{};
-    st.o[m][1] = f32x16{};
-  }
-  st.m_run[0] = st.m_run[1] = -__builtin_inff();
-  st.l_run[0] = st.l_run[1] = 0.0f;
+  for (int t = 0; t < kDimTiles; ++t) st.o[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  st.m_ref = -__builtin_inff();
+  st.l = 0.0f;
+  st.exchanged = 0;
 
-  const TrOffs tr = tr_offsets(x);
-  // Row-wise store offset of the lane's entry 32 e + c, dims 256 dh + 128 half.
-  const int srow = kTile * x.e + x.c;
-  const int st_off = srow * kRow + 512 * x.dh + 256 * x.half + 16 * kswz(srow);
+  uint8_t* tile = sm.tile[x.wave];
+  // Transposing-read offsets for dims tile 0 (tile t: + 32 t): row 4 c + j /
+  // 4 (a) or 16 + 4 c + j / 4 (b), dims 4 (j % 4) .. + 4.
+  const int j = x.m;
+  const int off_a = (4 * x.c + (j >> 2)) * kRowBytes + 8 * (j & 3);
+  const int off_b = off_a + 16 * kRowBytes;
 
-  // Chunks [c0, cm) hold selected entries in this wave's tile, [cm, c1) window
-  // entries.
-  const int cm = min(max((x.tkp - kTile * x.e + kChunk - 1) / kChunk, c0), c1);
-  if (c0 < cm) attend_chunk<true, false>(a, x, sm, st, valid0, c0, c1, 0, st_off, tr);
-  else attend_chunk<false, false>(a, x, sm, st, valid0, c0, c1, 0, st_off, tr);
-  int ch = c0 + 1;
-  for (; ch < cm; ++ch) {
-    const int S = (ch - c0) & 1;
-    bool v = S ? valid1 : valid0;
-    attend_chunk<true, true>(a, x, sm, st, v, ch, c1, S, st_off, tr);
-    if (S) valid1 = v;
-    else valid0 = v;
-  }
-  for (; ch < c1; ++ch) {
-    const int S = (ch - c0) & 1;
-    bool v = S ? valid1 : valid0;
-    attend_chunk<false, true>(a, x, sm, st, v, ch, c1, S, st_off, tr);
-    if (S) valid1 = v;
-    else valid0 = v;
-  }
-  pv_prep(x, sm, st);
-  pv(x, sm, st, tr);
-
-  // Output (or the split partial), through the K/V buffer once every wave
-  // is done with it: lane (c, half) holds head 32 h + c, dims 128 w + 32 m +
-  // 8 i4 + 4 half + [0, 4), i.e. half of 16-byte chunk 16 w + 4 m + i4 of
-  // the head's row; rows are then stored whole, one coalesced 1 KB store per
-  // head row.
-  const size_t ps = static_cast<size_t>(x.r) * a.nsplit + split;
-  lds_barrier();
-  // Split partials are written unnormalised (the merge adds the sink).  A
-  // whole row is normalised by its softmax sum, which a sink logit s (log2
-  // units s2) extends: with m' = max(m, s2) the sum is l 2^(m - m') +
-  // 2^(s2 - m') and O (relative to m) is scaled by 2^(m - m') / sum.
-  float fo[2], lse2[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const float mr = st.m_run[h], l = st.l_run[h];
-    const float s2 = a.sink != nullptr ? a.sink[32 * h + x.c] * kLog2e : -__builtin_inff();
-    const float mn = fmaxf(mr, s2);
-    const float al = mr == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mr - mn);
-    const float sum = l * al + (s2 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(s2 - mn));
-    fo[h] = sum > 0.0f ? al / sum : 0.0f;
-    lse2[h] = sum > 0.0f ? mn + log2f(sum) : -__builtin_inff();
-  }
-  auto write_rows = [&](auto normalise) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int row = 32 * h + x.c;
-      const float f = fo[h];
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const f32x16& o = st.o[m][h];
-          float v[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = decltype(normalise)::value ? o[4 * i4 + j] * f : o[4 * i4 + j];
-          *reinterpret_cast<u32x2*>(sm.kv + row * kRow +
-                                    16 * ((16 * x.wave + 4 * m + i4) ^ kswz(row)) + 8 * x.half) =
-              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        }
-    }
-  };
-  if (a.nsplit == 1) write_rows(std::true_type{});
-  else write_rows(std::false_type{});
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = 32 * h + x.c;
-    const float l = st.l_run[h];
-    if (x.wave == 0 && x.half == 0) {
-      if (a.nsplit == 1) {
-        if (a.lse != nullptr) a.lse[static_cast<size_t>(x.r) * kHeads + row] = lse2[h] * kLn2;
-      } else {
-        a.part_ml[(ps * kHeads + row) * 2 + 0] = st.m_run[h];
-        a.part_ml[(ps * kHeads + row) * 2 + 1] = l;
-      }
+  // Round 1: pair p takes window tile p.  Then pair p takes selected tiles
+  // p, p + 4, ... (one round each); the next tile's loads are issued before
+  // the current one is processed (two register buffers).  The loads stay in
+  // issue order (window tile, then the first selected tile): the waits
+  // before each tile's use then count only later loads.  The window tile
+  // needs no ids, so its loads go out before the ids barrier.
+  {
+    WinRaw wr;
+    MainRaw m0, m1;
+    gather_window(a, x, x.pair, wr);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();   // the ids are in LDS (the window loads stay in flight)
+    gather_main(a, x, sm.ids, x.pair, m0);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool work = __ballot(wr.valid[0] || wr.valid[1]) != 0;
+    uint32_t round = 1;
+    round_tile<false>(a, x, sm, wr, work, round, tile, off_a, off_b, st);
+    const int rounds = (x.sel_tiles + kPairs - 1) / kPairs;
+    int t = x.pair;
+    auto run = [&](const MainRaw& w) {
+      ++round;
+      const bool wk = t < x.sel_tiles && __ballot(w.valid[0] || w.valid[1]) != 0;
+      round_tile<true>(a, x, sm, w, wk, round, tile, off_a, off_b, st);
+      t += kPairs;
+    };
+    for (int i = 0; i < rounds; i += 2) {
+      gather_main(a, x, sm.ids, t + kPairs, m1);
+      __builtin_amdgcn_sched_barrier(0);
+      run(m0);
+      if (i + 1 >= rounds) break;
+      gather_main(a, x, sm.ids, t + kPairs, m0);
+      __builtin_amdgcn_sched_barrier(0);
+      run(m1);
     }
   }
-  lds_barrier();
-  uint16_t* dst = a.nsplit == 1 ? a.out + static_cast<size_t>(x.r) * kHeads * kDim
-                                : a.part_o + ps * kHeads * kDim;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int row = 16 * x.wave + i;
-    *reinterpret_cast<u32x4*>(dst + row * kDim + 8 * x.lane) =
-        *reinterpret_cast<const u32x4*>(sm.kv + row * kRow + 16 * (x.lane ^ kswz(row)));
-  }
-}
 
-// Merge of split partials in split order: one wave per (row, head), 64
-// lanes x 8 dims, kCombineHeads heads of a row per workgroup.  A row has at
-// most S splits (S = 4, or kMaxChunks: one chunk at least per split), so
-// every split's partial output and (m, l) are loaded at once (lane s <
-// nsplit fetches split s's (m, l)); the merge weights are formed in
-// registers.
-template <int S>
-__global__ __launch_bounds__(64 * kCombineHeads) void k_attn_combine(AttnArgs a) {
-  const int r = blockIdx.x / (kHeads / kCombineHeads);
-  const int head = blockIdx.x % (kHeads / kCombineHeads) * kCombineHeads +
-                   __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int t = threadIdx.x & 63;
-  const size_t ps0 = static_cast<size_t>(r) * a.nsplit;
-  u32x4 u[S];
+  // Merge of the four pairs' partial results, in pair order.  Each wave
+  // leaves its O^T in its tile ([dims tile][lane], fp32) and each pair its
+  // (reference, sum) per head; wave (p, d) then finishes dims tiles 4 p ..
+  // 4 p + 3 of its half.
+  f32x4_t* mine = reinterpret_cast<f32x4_t*>(tile);
 #pragma unroll
-  for (int g = 0; g < S; ++g) {
-    const int sp = min(g, a.nsplit - 1);
-    u[g] = *reinterpret_cast<const u32x4*>(a.part_o + ((ps0 + sp) * kHeads + head) * kDim + 8 * t);
+  for (int tt = 0; tt < kDimTiles; ++tt) mine[tt * 64 + x.lane] = st.o[tt];
+  if (x.d == 0 && x.c == 0) {
+    sm.ml[x.pair][x.m][0] = st.m_ref;
+    sm.ml[x.pair][x.m][1] = st.l;
   }
-  const int ts = min(t, a.nsplit - 1);
-  const float ms0 = a.part_ml[((ps0 + ts) * kHeads + head) * 2];
-  const float ls0 = a.part_ml[((ps0 + ts) * kHeads + head) * 2 + 1];
-  const float ms = t < a.nsplit ? ms0 : -__builtin_inff();
-  const float lsv = t < a.nsplit ? ls0 : 0.0f;
-  float mx = ms;
+  __syncthreads();
+  const int head = kHeadsPerWg * x.hg + x.m;
+  float mi[kPairs], li[kPairs];
+  float M = a.sink != nullptr ? a.sink[head] * kLog2e : -__builtin_inff();
+  const float s2 = M;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
-  // A sink logit (log2 units s2) joins the normaliser, with no value.
-  const float s2 = a.sink != nullptr ? a.sink[head] * kLog2e : -__builtin_inff();
-  mx = fmaxf(mx, s2);
-  const float wgt_mine = (ms == -__builtin_inff()) ? 0.0f : exp2f(ms - mx);
+  for (int i = 0; i < kPairs; ++i) {
+    mi[i] = sm.ml[i][x.m][0];
+    li[i] = sm.ml[i][x.m][1];
+    M = fmaxf(M, mi[i]);
+  }
+  float wt[kPairs];
   float L = 0.0f;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-  for (int g = 0; g < S; ++g) {
-    const float wgt = __shfl(wgt_mine, g, 64);
-    const float lsg = __shfl(lsv, g, 64);
-    if (g < a.nsplit) {
-      L += wgt * lsg;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = word_of(u[g], j);
-        acc[2 * j] += wgt * __uint_as_float(w << 16);
-        acc[2 * j + 1] += wgt * __uint_as_float(w & 0xffff0000u);
-      }
-    }
+  for (int i = 0; i < kPairs; ++i) {
+    wt[i] = mi[i] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mi[i] - M);
+    L += wt[i] * li[i];
   }
-  if (s2 != -__builtin_inff()) L += exp2f(s2 - mx);
+  if (s2 != -__builtin_inff()) L += __builtin_amdgcn_exp2f(s2 - M);
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  *reinterpret_cast<u32x4*>(a.out + (static_cast<size_t>(r) * kHeads + head) * kDim + 8 * t) =
-      u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
-            pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
-  if (t == 0 && a.lse != nullptr)
-    a.lse[static_cast<size_t>(r) * kHeads + head] =
-        L > 0.0f ? (mx + log2f(L)) * kLn2 : -__builtin_inff();
-}
-
-// Splits per row: none once the row workgroups alone reach about kFillWgs,
-// otherwise enough to get there (at most one chunk per split).
-void plan(int rows, int top_k, int* n_chunks, int* cps, int* nsplit) {
-  const int tkp = (top_k + kTile - 1) / kTile * kTile;
-  *n_chunks = (tkp + kMaxWindow + kChunk - 1) / kChunk;
-  long long want = (kFillWgs + rows - 1) / (rows > 0 ? rows : 1);
-  if (want < 1) want = 1;
-  if (want > *n_chunks) want = *n_chunks;
-  if (want > kMaxSplits) want = kMaxSplits;   // (n_chunks <= kMaxChunks <= kMaxSplits)
-  *cps = (*n_chunks + static_cast<int>(want) - 1) / static_cast<int>(want);
-  *nsplit = (*n_chunks + *cps - 1) / *cps;
+  uint16_t* orow = a.out + (static_cast<size_t>(x.r) * kHeads + head) * kDim + kHalfDims * x.d;
+#pragma unroll
+  for (int tt = 0; tt < kDimTiles / kPairs; ++tt) {
+    const int dt = (kDimTiles / kPairs) * x.pair + tt;
+    f32x4_t v = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i)
+      v += wt[i] * reinterpret_cast<const f32x4_t*>(sm.tile[2 * i + x.d])[dt * 64 + x.lane];
+    v *= inv;
+    *reinterpret_cast<u32x2*>(orow + 16 * dt + 4 * x.c) =
+        u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  }
+  if (a.lse != nullptr && x.wave == 0 && x.c == 0)
+    a.lse[static_cast<size_t>(x.r) * kHeads + head] =
+        L > 0.0f ? (M + log2f(L)) * kLn2 : -__builtin_inff();
 }
 
 }  // namespace
 
 size_t attn_workspace_bytes(int rows, int top_k) {
-  int n_chunks, cps, nsplit;
-  plan(rows, top_k, &n_chunks, &cps, &nsplit);
-  if (nsplit == 1) return 0;
-  return static_cast<size_t>(rows) * nsplit * kHeads * (kDim * sizeof(uint16_t) + 2 * sizeof(float));
+  (void)rows;
+  (void)top_k;
+  return 0;
 }
 
 hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
@@ -694,35 +513,24 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* kv_fp4, const ui
                               float sm_scale, int window, int replay_start, const float* sink,
                               int B, int n_q, uint16_t* out, float* lse, void* ws,
                               hipStream_t stream) {
-  const int rows = B * n_q;
+  (void)ws;
+  // Prefill-shaped calls (many query rows per sequence) take the one-row-
+  // per-workgroup kernel; the choice depends on n_q only, never on B.
+  if (n_q >= kRowsKernelMinNq)
+    return launch_attn_rows(q, kv_fp4, kv_scale, N_cap, idx, top_k, swa_kv, S_cap, swa_pos0,
+                            q_pos, sm_scale, window, replay_start, sink, B, n_q, out, lse, stream);
   AttnArgs a;
   a.q = q; a.kv_fp4 = kv_fp4; a.kv_scale = kv_scale; a.idx = idx; a.swa = swa_kv;
-  a.swa_pos0 = swa_pos0; a.q_pos = q_pos; a.out = out; a.lse = lse;
+  a.swa_pos0 = swa_pos0; a.q_pos = q_pos; a.out = out; a.lse = lse; a.sink = sink;
   a.N_cap = N_cap; a.top_k = top_k; a.S_cap = S_cap; a.n_q = n_q;
   a.window = window; a.replay_start = replay_start;
-  a.sink = sink;
+  a.rows = B * n_q;
   a.scale2 = sm_scale * kLog2e;
-  a.rows = rows;
-  plan(rows, top_k, &a.n_chunks, &a.cps, &a.nsplit);
-  a.part_o = nullptr;
-  a.part_ml = nullptr;
-  if (a.nsplit > 1) {
-    a.part_o = static_cast<uint16_t*>(ws);
-    a.part_ml = reinterpret_cast<float*>(a.part_o + static_cast<size_t>(rows) * a.nsplit * kHeads * kDim);
-  }
-  // The merge holds every split of a row in registers.
-  if (a.nsplit > kMaxChunks) return hipErrorInvalidValue;
-  const long long wgs = static_cast<long long>(rows) * a.nsplit;
+  // Rows in groups of 8 (one per XCD), 4 head groups each.
+  const long long wgs = static_cast<long long>((a.rows + 7) / 8) * 8 * kGroupsPerRow;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(k_sparse_attn, dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, stream,
                      a);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || a.nsplit == 1) return err;
-  const dim3 cgrid(rows * (kHeads / kCombineHeads)), cblock(64 * kCombineHeads);
-  if (a.nsplit <= 4)
-    hipLaunchKernelGGL(k_attn_combine<4>, cgrid, cblock, 0, stream, a);
-  else
-    hipLaunchKernelGGL(k_attn_combine<kMaxChunks>, cgrid, cblock, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -38,6 +38,16 @@ hipError_t launch_flat_topk(const float* scores, const int32_t* vis_len, int row
 
 size_t attn_workspace_bytes(int rows, int top_k);
 
+// Attention of prefill-shaped calls (n_q >= kRowsKernelMinNq): one
+// workgroup per query row, all 64 heads; see attention_rows.hip.  Decode
+// rows use the head-group kernel of attention.hip.
+constexpr int kRowsKernelMinNq = 16;
+hipError_t launch_attn_rows(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
+                            int N_cap, const int32_t* idx, int top_k, const uint8_t* swa_kv,
+                            int S_cap, const int32_t* swa_pos0, const int32_t* q_pos,
+                            float sm_scale, int window, int replay_start, const float* sink,
+                            int B, int n_q, uint16_t* out, float* lse, hipStream_t stream);
+
 hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
                               int N_cap, const int32_t* idx, int top_k, const uint8_t* swa_kv,
                               int S_cap, const int32_t* swa_pos0, const int32_t* q_pos,

@@ -39,7 +39,9 @@ def test_workspace_sizes(L):
     assert csa.workspace_size(csa.OP_BLOCK_TOPK, 8, 1, 1 << 20) == 8 * (2 * 4096 + 2 * 128 + 3 * 131072) * 4
     assert csa.workspace_size(csa.OP_REINDEX_TOPK, 8, 1, 1 << 20, 512, 2048) == 8 * 2048 * 8 * 4
     assert csa.workspace_size(csa.OP_SPARSE_ATTN, 4096, 1, 1 << 16, 512, 0) == 0
-    assert csa.workspace_size(csa.OP_SPARSE_ATTN, 8, 1, 1 << 20, 512, 0) > 0
+    # Attention never splits a row over workgroups: no workspace at any size.
+    assert csa.workspace_size(csa.OP_SPARSE_ATTN, 8, 1, 1 << 20, 512, 0) == 0
+    assert csa.workspace_size(csa.OP_SPARSE_ATTN, 1, 1, 1 << 20, 512, 0) == 0
     assert csa.workspace_size(7, 1, 1, 1) == ctypes.c_size_t(-1).value
     assert csa.workspace_size(csa.OP_INDEX_SCORE, 0, 1, 1) == ctypes.c_size_t(-1).value
 
@@ -132,10 +134,9 @@ def test_attention_validation(L):
         # 16-byte struct (no pointer field) passes validation up to the
         # workspace check, like NULL options.
         v1 = csa.AttnOptsV1(128, -1, 0, 0)
-        assert _attn(L, fn, opts=ctypes.byref(v1), B=8) == 4
+        assert _attn(L, fn, opts=ctypes.byref(v1), out=MIS) == 5
         unread = csa.AttnOpts(128, -1, 0, 0, MIS)
-        assert _attn(L, fn, opts=ctypes.byref(unread), B=8) == 4
-        assert _attn(L, fn, B=8) == 4                 # 8 rows split the entries: needs workspace
+        assert _attn(L, fn, opts=ctypes.byref(unread), out=MIS) == 5
         assert _attn(L, fn, out=MIS) == 5
 
 

@@ -456,6 +456,57 @@ def test_attention_running_max_moves_mid_row():
     assert lse[0, 0, 0] > 8.0 and np.median(lse[0, 0]) < 8.0
 
 
+def test_attention_batch_invariant():
+    # The same query rows in batches of 64, 8 and 1 (and at another position
+    # in the batch) give bit-identical outputs and lse: a row's arithmetic
+    # does not depend on the other rows of the call ([V4 essay §6.4]).
+    T, B = 4000, 64
+    d = synth.decode_workload(B=B, T=T, kdtype="bf16", seed=91)
+    rng = np.random.default_rng(91)
+    idx = np.stack([np.sort(rng.choice(T, size=512, replace=False)) for _ in range(B)])
+    idx_t = torch.from_numpy(idx.astype(np.int32)).reshape(B, 1, 512)
+    print("attention batch invariance 64 / 8 / 1", flush=True)
+    full, full_lse = _attn_gpu(d, idx_t)
+
+    def sub(rows):
+        e = {k: (v[rows] if torch.is_tensor(v) and v.dim() > 0 and v.shape[0] == B else v)
+             for k, v in d.items()}
+        return _attn_gpu(e, idx_t[rows])
+
+    o8, l8 = sub(slice(8, 16))
+    assert np.array_equal(o8, full[8:16]) and np.array_equal(l8, full_lse[8:16])
+    for b in (0, 13, 63):
+        o1, l1 = sub(slice(b, b + 1))
+        assert np.array_equal(o1, full[b:b + 1]) and np.array_equal(l1, full_lse[b:b + 1]), b
+    # Row 13 placed first in a batch of 2 with row 40.
+    o2, l2 = sub(torch.tensor([13, 40]))
+    assert np.array_equal(o2[0], full[13]) and np.array_equal(o2[1], full[40])
+
+
+def test_attention_batch_invariant_prefill_rows():
+    # Prefill-shaped calls (16 query rows per sequence): the same sequences
+    # in a batch of 4 and alone give bit-identical outputs.
+    T, B, n_q = 3000, 4, 16
+    d = synth.decode_workload(B=B, T=T, kdtype="bf16", seed=92)
+    g = torch.Generator().manual_seed(93)
+    d["q"] = synth.to_bf16_bits(torch.randn(B, n_q, 64, 512, generator=g))
+    d["q_pos"] = (T - n_q + torch.arange(n_q, dtype=torch.int32)).repeat(B, 1)
+    d["swa"] = synth.to_fp8_bytes(torch.randn(B, 160, 512, generator=g))
+    d["swa_pos0"] = torch.full((B,), T - 160, dtype=torch.int32)
+    rng = np.random.default_rng(92)
+    idx = np.stack([np.sort(rng.choice(T - n_q, size=512, replace=False)) for _ in range(B * n_q)])
+    idx_t = torch.from_numpy(idx.astype(np.int32)).reshape(B, n_q, 512)
+    print("attention batch invariance, prefill rows", flush=True)
+    full, full_lse = _attn_gpu(d, idx_t)
+    for b in (0, 3):
+        e = {k: (v[b:b + 1] if torch.is_tensor(v) and v.dim() > 0 and v.shape[0] == B else v)
+             for k, v in d.items()}
+        o1, l1 = _attn_gpu(e, idx_t[b:b + 1])
+        assert np.array_equal(o1, full[b:b + 1]) and np.array_equal(l1, full_lse[b:b + 1]), b
+    o, l = _attn_ref(d, 1, 5, idx[1 * n_q + 5])
+    check_attention(full[1, 5], full_lse[1, 5], o, l, what="prefill row (1, 5)")
+
+
 def test_deterministic_reruns():
     d = synth.decode_workload(B=2, T=30000, kdtype="fp8", seed=44)
     a = _full_layer_gpu(d, True)
