@@ -15,6 +15,7 @@ __all__ = [
     "KDTYPE_BF16", "KDTYPE_FP8", "MODE_FULL", "MODE_REINDEX", "MODE_REUSE",
     "OP_INDEX_SCORE", "OP_BLOCK_TOPK", "OP_REINDEX_TOPK", "OP_SPARSE_ATTN",
     "Csa2Error", "lib", "abi_version", "workspace_size", "index_score", "block_topk",
+    "block_topk_noalloc",
     "reindex_topk", "sparse_attn_decode", "reuse_attn", "kv_append",
 ]
 
@@ -32,6 +33,7 @@ _F = ctypes.c_float
 _SIGNATURES = {
     "csa2_index_score": [_P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _P, _S, _P],
     "csa2_block_topk": [_P, _P, _I, _I, _I, _I, _P, _P, _S, _P],
+    "csa2_block_topk_noalloc": [_P, _P, _I, _I, _I, _I, _P, _P],
     "csa2_reindex_topk": [_I, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _S, _P],
     "csa2_sparse_attn_decode": [_P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _F, _P, _I, _I, _P, _P,
                                 _P, _S, _P],
@@ -149,6 +151,15 @@ def block_topk(block_max, vis_len, N_cap, k_blocks, pool_blocks, ws=None, stream
     _call("csa2_block_topk", _ptr(block_max, _F32, "block_max"), _ptr(vis_len, _I32, "vis_len"),
           B, n_q, N_cap, k_blocks, _ptr(pool_blocks, _I32, "pool_blocks"),
           _ptr(ws, (torch.uint8,), "ws"), nbytes, _stream(stream))
+
+
+def block_topk_noalloc(block_max, vis_len, N_cap, k_blocks, pool_blocks, stream=None):
+    """block_topk on the library's own fixed device scratch array (no workspace,
+    no allocation); limits and sharing rules in include/csa2.h."""
+    B, n_q = block_max.shape[0], block_max.shape[1]
+    _call("csa2_block_topk_noalloc", _ptr(block_max, _F32, "block_max"),
+          _ptr(vis_len, _I32, "vis_len"), B, n_q, N_cap, k_blocks,
+          _ptr(pool_blocks, _I32, "pool_blocks"), _stream(stream))
 
 
 def reindex_topk(mode, vis_len, N_cap, top_k, idx_out, scores=None, q_idx=None, w_idx=None,

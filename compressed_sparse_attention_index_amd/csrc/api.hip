@@ -105,6 +105,22 @@ csa2_status csa2_block_topk(const float* block_max, const int32_t* vis_len, int3
                                           pool_blocks, ws, stream));
 }
 
+csa2_status csa2_block_topk_noalloc(const float* block_max, const int32_t* vis_len, int32_t B,
+                                    int32_t n_q, int32_t N_cap, int32_t k_blocks,
+                                    int32_t* pool_blocks, hipStream_t stream) {
+  if (!block_max || !vis_len || !pool_blocks) return CSA2_ERR_NULL;
+  csa2_status st = check_rows(B, n_q);
+  if (st != CSA2_OK) return st;
+  if (N_cap < 1 || N_cap > kMaxNcap || k_blocks < 1 || k_blocks > 2048) return CSA2_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * n_q > kMaxGridY) return CSA2_ERR_SHAPE;
+  const void* ptrs[] = {block_max, vis_len, pool_blocks};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return CSA2_ERR_ALIGN;
+  if (!csa2::block_topk_noalloc_fits(B * n_q, N_cap)) return CSA2_ERR_WORKSPACE;
+  return from_hip(csa2::launch_block_topk_noalloc(block_max, vis_len, B * n_q, N_cap, k_blocks,
+                                                  pool_blocks, stream));
+}
+
 csa2_status csa2_reindex_topk(csa2_mode mode, const float* scores, const uint16_t* q_idx,
                               const float* w_idx, const void* k_idx, csa2_kdtype k_dtype,
                               const int32_t* pool_blocks, int32_t k_blocks,

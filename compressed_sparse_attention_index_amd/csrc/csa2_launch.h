@@ -22,6 +22,11 @@ size_t block_topk_workspace_bytes(int rows, int N_cap);
 int block_topk_max_blocks();
 hipError_t launch_block_topk(const float* block_max, const int32_t* vis_len, int rows, int N_cap,
                              int k, int32_t* out, void* ws, hipStream_t stream);
+// The same selection with the library's own fixed-size device scratch array
+// instead of a caller's workspace (no allocation); see topk.hip.
+bool block_topk_noalloc_fits(int rows, int N_cap);
+hipError_t launch_block_topk_noalloc(const float* block_max, const int32_t* vis_len, int rows,
+                                     int N_cap, int k, int32_t* out, hipStream_t stream);
 
 // Pool Top-K.  mode 0: keys are stored scores; 1 / 2: the pool positions are
 // re-scored with q_idx / w_idx on FP8 / bf16 keys.

@@ -30,6 +30,9 @@
 // also checks their totals (the visible block count, the candidate count);
 // a workspace that did not start at zero fails that check, and the row is
 // then selected exactly by radix passes over all its blocks.
+#include <atomic>
+#include <mutex>
+
 #include "csa2_launch.h"
 #include "index_core.h"
 #include "select_common.h"
@@ -969,16 +972,11 @@ size_t pool_topk_workspace_bytes(int rows, int k_blocks) {
 
 int block_topk_max_blocks() { return kBtMaxBlocks; }
 
-hipError_t launch_block_topk(const float* block_max, const int32_t* vis_len, int rows, int N_cap,
-                             int k, int32_t* out, void* ws, hipStream_t stream) {
+namespace {
+
+hipError_t run_block_topk(const float* block_max, const int32_t* vis_len, int rows, int N_cap,
+                          int k, int32_t* out, const BtWs& w, hipStream_t stream) {
   const size_t nb_cap = (static_cast<size_t>(N_cap) + 7) / 8;
-  BtWs w;
-  w.hist = static_cast<uint32_t*>(ws);
-  w.hist2 = w.hist + static_cast<size_t>(rows) * kHistBins;
-  w.wgcnt = w.hist2 + static_cast<size_t>(rows) * kHistBins;
-  w.sure = reinterpret_cast<int32_t*>(w.wgcnt + static_cast<size_t>(rows) * kBtMaxWgs * 2);
-  w.ckey = reinterpret_cast<uint32_t*>(w.sure + static_cast<size_t>(rows) * nb_cap);
-  w.cid = reinterpret_cast<int32_t*>(w.ckey + static_cast<size_t>(rows) * nb_cap);
   hipError_t e;
   dim3 grid(static_cast<unsigned>((nb_cap + kBtItems - 1) / kBtItems), rows);
   hipLaunchKernelGGL(k_bt_hist, grid, dim3(kBtThreads), 0, stream, block_max, vis_len, N_cap, k, w);
@@ -989,6 +987,88 @@ hipError_t launch_block_topk(const float* block_max, const int32_t* vis_len, int
   hipLaunchKernelGGL(k_bt_final, dim3(rows), dim3(kBtThreads), 0, stream, block_max, vis_len, N_cap,
                      k, w, out);
   return hipGetLastError();
+}
+
+// Workspace layout of a caller's buffer: histograms of the call's rows, then
+// the per-workgroup counts and the segments.
+BtWs caller_layout(void* ws, int rows, size_t nb_cap) {
+  BtWs w;
+  w.hist = static_cast<uint32_t*>(ws);
+  w.hist2 = w.hist + static_cast<size_t>(rows) * kHistBins;
+  w.wgcnt = w.hist2 + static_cast<size_t>(rows) * kHistBins;
+  w.sure = reinterpret_cast<int32_t*>(w.wgcnt + static_cast<size_t>(rows) * kBtMaxWgs * 2);
+  w.ckey = reinterpret_cast<uint32_t*>(w.sure + static_cast<size_t>(rows) * nb_cap);
+  w.cid = reinterpret_cast<int32_t*>(w.ckey + static_cast<size_t>(rows) * nb_cap);
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free block Top-K: the workspace is a file-scope device array of
+// fixed size, one copy per GPU, resolved once per device with
+// hipGetSymbolAddress (in host code `scratch` names a host-side stand-in,
+// never the device memory).  Its layout does not depend on the call: the
+// histograms of all kNoAllocRows rows come first, so they are zero when the
+// code object is loaded and every call leaves them zeroed again, whatever
+// its row count; the counts and segments follow.  Calls that overlap on one
+// GPU share the array and race.
+constexpr int kNoAllocRows = 64;
+constexpr size_t kNoAllocBytes = size_t{16} << 20;
+constexpr size_t kNoAllocFixed = static_cast<size_t>(kNoAllocRows) * (2 * kHistBins + 2 * kBtMaxWgs) * 4;
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_block_topk(const float* block_max, const int32_t* vis_len, int rows, int N_cap,
+                             int k, int32_t* out, void* ws, hipStream_t stream) {
+  const size_t nb_cap = (static_cast<size_t>(N_cap) + 7) / 8;
+  return run_block_topk(block_max, vis_len, rows, N_cap, k, out, caller_layout(ws, rows, nb_cap),
+                        stream);
+}
+
+bool block_topk_noalloc_fits(int rows, int N_cap) {
+  const size_t nb_cap = (static_cast<size_t>(N_cap) + 7) / 8;
+  return rows >= 1 && rows <= kNoAllocRows &&
+         static_cast<size_t>(rows) * nb_cap * 3 * 4 <= kNoAllocBytes - kNoAllocFixed;
+}
+
+hipError_t launch_block_topk_noalloc(const float* block_max, const int32_t* vis_len, int rows,
+                                     int N_cap, int k, int32_t* out, hipStream_t stream) {
+  if (!block_topk_noalloc_fits(rows, N_cap)) return hipErrorInvalidValue;
+  void* base = nullptr;
+  hipError_t e = scratch_address(&base);
+  if (e != hipSuccess) return e;
+  const size_t nb_cap = (static_cast<size_t>(N_cap) + 7) / 8;
+  BtWs w;
+  w.hist = static_cast<uint32_t*>(base);
+  w.hist2 = w.hist + static_cast<size_t>(kNoAllocRows) * kHistBins;
+  w.wgcnt = w.hist2 + static_cast<size_t>(kNoAllocRows) * kHistBins;
+  w.sure = reinterpret_cast<int32_t*>(w.wgcnt + static_cast<size_t>(kNoAllocRows) * kBtMaxWgs * 2);
+  w.ckey = reinterpret_cast<uint32_t*>(w.sure + static_cast<size_t>(rows) * nb_cap);
+  w.cid = reinterpret_cast<int32_t*>(w.ckey + static_cast<size_t>(rows) * nb_cap);
+  return run_block_topk(block_max, vis_len, rows, N_cap, k, out, w, stream);
 }
 
 hipError_t launch_pool_topk(int mode, const float* scores, const uint16_t* q_idx,

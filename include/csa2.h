@@ -178,6 +178,27 @@ CSA2_API csa2_status csa2_block_topk(const float* block_max, const int32_t* vis_
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * csa2_block_topk_noalloc -- csa2_block_topk with no workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *   Same arguments (minus ws / ws_bytes), result and errors as
+ *   csa2_block_topk.  Scratch memory is a fixed 16 MiB device array inside
+ *   the library (one per GPU, held until the process ends; its address is
+ *   resolved on the first call on each device).  The call allocates
+ *   nothing.  Limits: B * n_q <= 64 and B * n_q * ceil(N_cap / 8) * 12 <=
+ *   16 MiB - 2,162,688 bytes (e.g. 8 rows at N_cap = 1,048,576 or 64 rows at
+ *   131,072); larger calls return CSA2_ERR_WORKSPACE and enqueue nothing.
+ *   Every call on a GPU shares that GPU's array: calls that may overlap on
+ *   one GPU (other streams, other threads) race and must be serialised by
+ *   the caller.  The array's histograms are zero when the library is loaded
+ *   and every call leaves them zeroed.
+ */
+CSA2_API csa2_status csa2_block_topk_noalloc(const float* block_max, const int32_t* vis_len,
+                                             int32_t B, int32_t n_q, int32_t N_cap,
+                                             int32_t k_blocks, int32_t* pool_blocks,
+                                             hipStream_t stream);
+
+/*
  * csa2_reindex_topk -- second level of the Top-K.
  *   With a pool (pool_blocks != NULL) the candidates are the visible
  *   positions of the pool's blocks:

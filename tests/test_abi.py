@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     decls = re.findall(r"CSA2_API\s+[\w\s\*]+?\b(csa2_\w+)\s*\(", open(HEADER).read())
-    assert len(decls) == 9
+    assert len(decls) == 10
     for name in decls:
         assert hasattr(L, name), name
 
@@ -75,6 +75,18 @@ def test_block_topk_validation(L):
     assert f(A, A, 1, 1, 64, 16, A, None, 0, None) == 4          # workspace required
     assert f(A, A, 1, 1, 64, 16, A, A, 4 * (2 * 4096 + 2 * 128 + 3 * 8) - 1, None) == 4
     assert f(A, A, 1, 1, (1 << 22) + 1, 16, A, A, 1 << 30, None) == 2
+
+
+def test_block_topk_noalloc_validation(L):
+    f = L.csa2_block_topk_noalloc
+    assert f(None, A, 1, 1, 64, 16, A, None) == 1
+    assert f(A, A, 1, 1, 64, 0, A, None) == 2
+    assert f(A, A, 1, 1, 0, 16, A, None) == 2
+    assert f(A, A, 1, 1, 64, 16, MIS, None) == 5
+    # Beyond the fixed scratch array: more than 64 rows, or too many blocks.
+    assert f(A, A, 65, 1, 64, 16, A, None) == 4
+    assert f(A, A, 8, 2, 1 << 20, 16, A, None) == 4
+    assert f(A, A, 10, 1, 1 << 20, 16, A, None) == 4
 
 
 def _reindex(L, mode=1, sc=None, q=A, w=A, k=A, kd=1, pool=A, kb=2048, vis=A, B=1, n_q=1, N=1 << 20,
