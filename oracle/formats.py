@@ -3,9 +3,10 @@ entries into them (test infrastructure only).
 
 [架构详解 §4]: main KV is stored as MXFP4 (E2M1 elements with block scales)
 and is dequantised before attention; SWA KV is FP8.  [架构详解 §1 config
-table]: indexer K is 128-dim.  The scale format used here is E8M0 with one
-scale per 32 elements (OCP MX v1.0); the page's own variant (one E4M3 scale
-per 16 channels) is a different entry layout and is not decoded here.
+table]: indexer K is 128-dim.  Two scale layouts of the E2M1 elements are
+decoded: one E8M0 scale per 32 elements (OCP MX v1.0, the layout of the
+benchmark workloads), and the page's own: one E4M3 scale per 16 channels and
+no global scale ([架构详解 §4]; [4sapi, "FP4 and Bounded Replay"]).
 
 Closed forms (OCP):
   bf16     : the upper 16 bits of an IEEE binary32.
@@ -16,6 +17,7 @@ Closed forms (OCP):
   E8M0     : 2^(x-127); x == 255 is NaN.
   MXFP4    : v[i] = E2M1(nib_i) * E8M0(scale[i // 32]); byte j holds
              element 2j in its low nibble and element 2j+1 in its high nibble.
+  FP4/E4M3 : v[i] = E2M1(nib_i) * E4M3FN(scale[i // 16]), same nibble packing.
 """
 import numpy as np
 
@@ -95,6 +97,23 @@ def mxfp4_to_f64(fp4_bytes, scales):
     return vals * scale
 
 
+def fp4e4_to_f64(fp4_bytes, scales):
+    """E2M1 entries with one E4M3FN scale per 16 elements -> fp64 vectors.
+
+    fp4_bytes: uint8 [..., D/2]; scales: uint8 [..., D/16].  Returns [..., D].
+    A NaN scale code raises FormatError.
+    """
+    b = np.asarray(fp4_bytes, dtype=np.uint8)
+    sc = np.asarray(scales, dtype=np.uint8)
+    d = b.shape[-1] * 2
+    if sc.shape[-1] * 16 != d:
+        raise ValueError("FP4/E4M3: need one scale per 16 elements")
+    nib = np.empty(b.shape[:-1] + (d,), dtype=np.uint8)
+    nib[..., 0::2] = b & 0xF
+    nib[..., 1::2] = b >> 4
+    return e2m1_to_f64(nib) * np.repeat(e4m3_to_f64(sc), 16, axis=-1)
+
+
 # ---------------------------------------------------------------------------
 # Encoding (the KV append step: [架构详解 §4] stores each new main-KV entry as
 # MXFP4 and each SWA entry as FP8).  Plain nearest-value rounding on the code
@@ -156,3 +175,32 @@ def f64_to_mxfp4(x):
     nib = nib.reshape(x.shape)
     packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
     return packed, (xexp + 127).astype(np.uint8)
+
+
+def f64_to_fp4e4(x):
+    """fp64 [..., D] (D a multiple of 16) -> (uint8 [..., D/2] packed E2M1,
+    uint8 [..., D/16] E4M3FN scale codes): the page's layout.
+
+    Per 16 elements the scale is the E4M3FN value nearest to amax / 6 (6 =
+    the largest E2M1 magnitude; ties to the even code, saturating at 448), so
+    the block's largest element lands at the top of the E2M1 range.  Each
+    element v goes to the E2M1 magnitude nearest to |v| / s (ties to the even
+    code, saturating at 6), sign kept, a zero stored as +0; a block whose
+    scale is 0 stores +0 everywhere.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise FormatError("non-finite value to encode")
+    d = x.shape[-1]
+    if d % 16:
+        raise ValueError("FP4/E4M3: the last dimension must be a multiple of 16")
+    blocks = x.reshape(x.shape[:-1] + (d // 16, 16))
+    amax = np.abs(blocks).max(axis=-1)
+    code = f64_to_e4m3(amax / 6.0)
+    s = E4M3_VALUES[code]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        scaled = np.where(s[..., None] > 0, np.abs(blocks) / s[..., None], 0.0)
+    mag = _nearest_code(np.minimum(scaled, 6.0), _E2M1_POS).astype(np.uint8)
+    nib = np.where((blocks < 0) & (mag > 0), mag | 8, mag).astype(np.uint8).reshape(x.shape)
+    packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+    return packed, code.astype(np.uint8)

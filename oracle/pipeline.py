@@ -87,25 +87,39 @@ def prefill_topk(q_raw, w, k_raw, kdtype, vis, top_k=topk.TOP_K):
     return {"scores": s, "idx": topk.flat_topk(s, vis, top_k)}
 
 
+def decode_main_kv(kv_fp4, kv_scale, kv_fmt="e8m0_32"):
+    """Main-KV entries -> fp64: E2M1 with an E8M0 scale per 32 elements
+    ("e8m0_32", OCP MXFP4) or with an E4M3 scale per 16 channels ("e4m3_16",
+    the layout [架构详解 §4] describes)."""
+    if kv_fmt == "e8m0_32":
+        return formats.mxfp4_to_f64(kv_fp4, kv_scale)
+    if kv_fmt == "e4m3_16":
+        return formats.fp4e4_to_f64(kv_fp4, kv_scale)
+    raise ValueError(f"unknown main-KV format {kv_fmt!r}")
+
+
 def attention(q_raw, kv_fp4, kv_scale, idx, swa_raw, swa_pos0, q_pos, sm_scale,
-              window=attn.WINDOW, replay_start=-1, sink=None):
+              window=attn.WINDOW, replay_start=-1, sink=None, kv_fmt="e8m0_32"):
     """Selected main entries (idx != -1) plus the SWA window, one softmax
     (with an optional per-head sink, see attention.sparse_attention)."""
     idx = np.asarray(idx, dtype=np.int64)
     sel = idx[idx >= 0]
-    main = formats.mxfp4_to_f64(kv_fp4[sel], kv_scale[sel])
+    main = decode_main_kv(kv_fp4[sel], kv_scale[sel], kv_fmt)
     wpos = attn.window_positions(q_pos, swa_pos0, swa_raw.shape[0], window, replay_start)
     swa = formats.e4m3_to_f64(swa_raw[wpos - int(swa_pos0)])
     entries = np.concatenate([main, swa], axis=0)
     return attn.sparse_attention(formats.bf16_to_f64(q_raw), entries, sm_scale, sink)
 
 
-def kv_append(kv_fp4, kv_scale, swa, kv_new_bits, swa_new_bits, pos, swa_pos0):
+def kv_append(kv_fp4, kv_scale, swa, kv_new_bits, swa_new_bits, pos, swa_pos0,
+              kv_fmt="e8m0_32"):
     """The KV append step ([架构详解 §4]: main KV stored as MXFP4, SWA KV as
     FP8): token i of sequence b sits at position p = pos[b] + i; its main
-    entry is encoded into row p of (kv_fp4, kv_scale) when 0 <= p < N_cap,
-    and its window entry into row p - swa_pos0[b] of swa when that row
-    exists.  Returns updated copies of the three caches (numpy uint8)."""
+    entry is encoded into row p of (kv_fp4, kv_scale) when 0 <= p < N_cap
+    (scales E8M0 per 32 or E4M3 per 16, by kv_fmt), and its window entry
+    into row p - swa_pos0[b] of swa when that row exists.  Returns updated
+    copies of the three caches (numpy uint8)."""
+    encode = {"e8m0_32": formats.f64_to_mxfp4, "e4m3_16": formats.f64_to_fp4e4}[kv_fmt]
     kv_fp4, kv_scale = np.array(kv_fp4, np.uint8), np.array(kv_scale, np.uint8)
     swa = None if swa is None else np.array(swa, np.uint8)
     B, n_new = kv_new_bits.shape[0], kv_new_bits.shape[1]
@@ -114,8 +128,7 @@ def kv_append(kv_fp4, kv_scale, swa, kv_new_bits, swa_new_bits, pos, swa_pos0):
         for i in range(n_new):
             p = int(pos[b]) + i
             if 0 <= p < n_cap:
-                kv_fp4[b, p], kv_scale[b, p] = formats.f64_to_mxfp4(
-                    formats.bf16_to_f64(kv_new_bits[b, i]))
+                kv_fp4[b, p], kv_scale[b, p] = encode(formats.bf16_to_f64(kv_new_bits[b, i]))
             if swa_new_bits is not None:
                 j = p - int(swa_pos0[b])
                 if 0 <= j < swa.shape[1]:

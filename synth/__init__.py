@@ -70,6 +70,33 @@ def to_mxfp4(x):
     return packed.contiguous(), code.reshape(*shp[:-1], d // 32).contiguous()
 
 
+def to_fp4_e4m3(x):
+    """float tensor [..., D] -> (uint8 [..., D/2] packed E2M1, uint8 [..., D/16]
+    E4M3FN scale codes): per 16 elements the scale is amax / 6 cast to
+    float8_e4m3fn (round to nearest even, clamped to 448); each element
+    |v| / s rounded to nearest even on the E2M1 grid (threshold compares
+    against t * s, exact in float32), saturating at 6; element 2j in the low
+    nibble of byte j; a block whose scale is 0 stores +0."""
+    shp = x.shape
+    d = shp[-1]
+    xb = x.reshape(*shp[:-1], d // 16, 16).to(torch.float32)
+    amax = xb.abs().amax(dim=-1, keepdim=True)
+    code = (amax / 6.0).clamp(max=448.0).to(torch.float8_e4m3fn)
+    s = code.to(torch.float32)
+    a = xb.abs()
+    mag = torch.zeros_like(a, dtype=torch.uint8)
+    for t, up in zip(_E2M1_MID, _E2M1_TIE_UP):
+        thr = t * s
+        mag += (a > thr).to(torch.uint8)
+        if up:
+            mag += (a == thr).to(torch.uint8)
+    mag = torch.where(s > 0, mag, torch.zeros_like(mag))
+    nib = mag | ((xb < 0) & (mag > 0)).to(torch.uint8) << 3
+    nib = nib.reshape(*shp[:-1], d)
+    packed = nib[..., 0::2] | (nib[..., 1::2] << 4)
+    return packed.contiguous(), code.view(torch.uint8).reshape(*shp[:-1], d // 16).contiguous()
+
+
 class Gen:
     """A seeded generator bound to one device."""
 

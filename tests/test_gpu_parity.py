@@ -615,6 +615,56 @@ def test_multi_query_decode_rows():
             check_attention(out[b, j], lse[b, j], o, l, what=f"attention row ({b}, {j})")
 
 
+def test_multi_query_rows_through_selection():
+    # n_q = 4 query tokens per sequence (draft verification) through the whole
+    # decode path: each row scans its own visible prefix, gets its own pool,
+    # Full Top-k and Reindex Top-k (its own second indexer query), and its
+    # attention.  Pools of 128 blocks and top_k = 200 keep every stage a real
+    # selection at these sizes.
+    B, T, n_q, kb, top_k = 2, 6000, 4, 128, 200
+    d = synth.decode_workload(B=B, T=T, kdtype="fp8", seed=65, heavy_frac=0.01)
+    g = torch.Generator().manual_seed(66)
+    d["n_q"] = n_q
+    d["q_idx"] = synth.to_bf16_bits(torch.randn(B, n_q, 32, 128, generator=g))
+    d["w_idx"] = torch.rand(B, n_q, 32, generator=g)
+    q_idx2 = synth.to_bf16_bits(torch.randn(B, n_q, 32, 128, generator=g))
+    w_idx2 = torch.rand(B, n_q, 32, generator=g)
+    d["q"] = synth.to_bf16_bits(torch.randn(B, n_q, 64, 512, generator=g))
+    vis = [T - 3, T - 2, T - 1, T, 4001, 4002, 4003, 4010]
+    d["q_pos"] = (torch.tensor(vis, dtype=torch.int32) - 1).reshape(B, n_q)
+    print("multi-query rows through block / pool Top-K and attention", flush=True)
+    vis_t, _, bm = _scan(d, vis, want_scores=False)
+    pool = torch.full((B, n_q, kb), -7, dtype=torch.int32, device="cuda")
+    csa.block_topk(bm, vis_t, T, kb, pool)
+    idx = torch.full((B, n_q, top_k), -7, dtype=torch.int32, device="cuda")
+    csa.reindex_topk(csa.MODE_FULL, vis_t, T, top_k, idx, q_idx=d["q_idx"].cuda(),
+                     w_idx=d["w_idx"].cuda(), k_idx=d["k_idx"].cuda(), pool_blocks=pool)
+    idx2 = torch.full((B, n_q, top_k), -7, dtype=torch.int32, device="cuda")
+    csa.reindex_topk(csa.MODE_REINDEX, vis_t, T, top_k, idx2, q_idx=q_idx2.cuda(),
+                     w_idx=w_idx2.cuda(), k_idx=d["k_idx"].cuda(), pool_blocks=pool)
+    out, lse = _attn_gpu(d, idx2.cpu())
+    torch.cuda.synchronize()
+    for b in range(B):
+        kr, kd = _kraw(d, b)
+        for j in range(n_q):
+            v = vis[b * n_q + j]
+            ref = pipeline.full_layer(u16(d["q_idx"][b, j]), _np(d["w_idx"][b, j]), kr, kd, v,
+                                      k_blocks=kb, top_k=top_k)
+            gp = _np(pool[b, j])
+            check_selection(gp, ref["pool"], lambda t: ref["block_max"][t], what=f"pool ({b},{j})")
+            pos = otopk.pool_positions(gp, v)
+            ri = otopk.pool_topk(ref["scores"][pos], pos, top_k)
+            check_selection(_np(idx[b, j]), ri, lambda t: ref["scores"][t], what=f"idx ({b},{j})")
+            re = pipeline.reindex_layer(u16(q_idx2[b, j]), _np(w_idx2[b, j]), kr, kd, gp, v,
+                                        top_k=top_k)
+            key = dict(zip(re["positions"].tolist(), re["scores"].tolist()))
+            gi2 = _np(idx2[b, j])
+            check_selection(gi2, re["idx"], lambda t: np.array([key[int(x)] for x in t]),
+                            what=f"reindex ({b},{j})")
+            o, l = _attn_ref(d, b, j, gi2)
+            check_attention(out[b, j], lse[b, j], o, l, what=f"attention ({b},{j})")
+
+
 @pytest.mark.parametrize("rows", [3, 256])
 def test_attention_sink(rows):
     # Per-head sink logits (no sink, small, comparable to the logits, and one

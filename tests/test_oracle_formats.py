@@ -170,3 +170,68 @@ def test_mxfp4_encode_matches_the_input_recipe():
     p, s = formats.f64_to_mxfp4(xb.numpy().astype(np.float64))
     np.testing.assert_array_equal(p, p_ref.numpy())
     np.testing.assert_array_equal(s, s_ref.numpy())
+
+
+# --------------------------------------------------------------------------- FP4 / E4M3 per 16
+def test_fp4e4_golden_bytes():
+    for c in _gold("e5_fp4_e4m3.json")["decode"]:
+        b = np.zeros(8, np.uint8)
+        b[0] = c["byte"]
+        sc = np.full(1, c["scale_code"], np.uint8)
+        np.testing.assert_array_equal(formats.fp4e4_to_f64(b, sc)[:2], c["elements"])
+
+
+def test_fp4e4_decode_matches_torch_scale_cast():
+    # Every finite E4M3 scale code, decoded by torch's float8_e4m3fn cast,
+    # times the OCP E2M1 value listing, one scale per 16 elements.
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    sv = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    table = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6])
+    rng = np.random.default_rng(15)
+    nib = rng.integers(0, 16, size=(len(codes), 512)).astype(np.uint8)
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    sc = np.stack([np.roll(codes, i)[:32] for i in range(len(codes))])
+    scv = np.stack([np.roll(sv, i)[:32] for i in range(len(codes))])
+    want = table[nib] * np.repeat(scv, 16, axis=-1)
+    np.testing.assert_array_equal(formats.fp4e4_to_f64(packed, sc), want)
+    with pytest.raises(formats.FormatError):
+        formats.fp4e4_to_f64(packed[:1], np.full((1, 32), 0x7F, np.uint8))
+
+
+def test_fp4e4_encode_worked_block():
+    g = _gold("e5_fp4_e4m3.json")["encode"]
+    p, s = formats.f64_to_fp4e4(np.array(g["block"], np.float64))
+    nib = np.empty(16, np.uint8)
+    nib[0::2], nib[1::2] = p & 0xF, p >> 4
+    assert s.tolist() == [g["scale_code"]] and nib.tolist() == g["nibbles"]
+    # All-zero block and a block too small for any scale: everything +0.
+    for x in (np.zeros(16), np.full(16, 1e-6)):
+        p, s = formats.f64_to_fp4e4(x)
+        assert not p.any() and s.tolist() == [0]
+
+
+def test_fp4e4_encode_matches_the_input_recipe():
+    # The input generator quantises with torch's float8 cast and threshold
+    # comparisons, a separate implementation of the same rule.
+    rng = np.random.default_rng(16)
+    x = rng.standard_normal((64, 512)) * np.exp2(rng.integers(-14, 10, size=(64, 1)))
+    x[2, 32:48] = 0.0
+    x[4, :16] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 2) * 1.125
+    xb = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32)
+    p_ref, s_ref = synth.to_fp4_e4m3(xb)
+    p, s = formats.f64_to_fp4e4(xb.numpy().astype(np.float64))
+    np.testing.assert_array_equal(p, p_ref.numpy())
+    np.testing.assert_array_equal(s, s_ref.numpy())
+
+
+def test_fp4e4_encode_error_bound():
+    # Decoding gives each input back within half an E2M1 step of its block's
+    # grid (times the scale), or the saturation error above 6 s.
+    x = torch.randn(64, 512, generator=torch.Generator().manual_seed(17), dtype=torch.float64).numpy()
+    p, s = formats.f64_to_fp4e4(x)
+    dec = formats.fp4e4_to_f64(p, s)
+    scale = np.repeat(formats.e4m3_to_f64(s), 16, axis=-1)
+    a = np.abs(x) / scale
+    step = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
+    bound = np.where(a <= 6, step / 2, a - 6) * scale
+    assert np.all(np.abs(dec - x) <= bound + 1e-12)

@@ -137,6 +137,38 @@ def _mxfp4_scale_from_ceil(x):
         formats.f64_to_mxfp4(x)[1] + bump.astype(np.uint8)
 
 
+def _pin_fp4e4(decode):
+    with open(os.path.join(GOLD, "e5_fp4_e4m3.json")) as f:
+        cases = json.load(f)["decode"]
+    for c in cases:
+        b = np.zeros(16, np.uint8); b[0] = c["byte"]
+        if not np.array_equal(decode(b, np.full(2, c["scale_code"], np.uint8))[:2], c["elements"]):
+            return False
+    # one scale per 16 elements: element 16 takes the second scale
+    b = np.full(16, 0x22, np.uint8)
+    v = decode(b, np.array([0x38, 0x40], np.uint8))
+    return bool(np.all(v[:16] == 1.0) and np.all(v[16:] == 2.0))
+
+
+def _fp4e4_scale_per_32(b, sc):
+    sc = np.asarray(sc, np.uint8)
+    return formats.fp4e4_to_f64(b, np.repeat(sc[..., ::2], 2, axis=-1))
+
+
+def _pin_fp4e4_encode(encode):
+    with open(os.path.join(GOLD, "e5_fp4_e4m3.json")) as f:
+        g = json.load(f)["encode"]
+    p, s = encode(np.array(g["block"], np.float64))
+    nib = np.empty(16, np.uint8)
+    nib[0::2], nib[1::2] = p & 0xF, p >> 4
+    return s.tolist() == [g["scale_code"]] and nib.tolist() == g["nibbles"]
+
+
+def _fp4e4_scale_amax_over_4(x):
+    # Scale chosen for E2M1's top binade (amax / 4) instead of its maximum 6.
+    return formats.f64_to_fp4e4(np.asarray(x, np.float64) * 1.5)
+
+
 # Planted mistakes in copies of the pipeline's composition functions.
 
 def _scores_prefix_tail_dropped(q_raw, w, k_raw, kdtype, vis, chunk=pipeline.CHUNK):
@@ -233,6 +265,9 @@ MUTATIONS = [
     ("softmax scale ignored", _pin_attention, attention.sparse_attention, _attention_unscaled),
     ("fp8 encode ties away", _pin_e4m3_encode, formats.f64_to_e4m3, _e4m3_ties_up),
     ("fp4 scale from ceil", _pin_mxfp4_encode, formats.f64_to_mxfp4, _mxfp4_scale_from_ceil),
+    ("fp4/e4m3 scale per 32", _pin_fp4e4, formats.fp4e4_to_f64, _fp4e4_scale_per_32),
+    ("fp4/e4m3 scale from amax / 4", _pin_fp4e4_encode, formats.f64_to_fp4e4,
+     _fp4e4_scale_amax_over_4),
     ("score chunk tail dropped", pp.pin_scores_prefix, pipeline.scores_prefix,
      _scores_prefix_tail_dropped),
     ("score chunk slice off by one", pp.pin_scores_prefix, pipeline.scores_prefix,

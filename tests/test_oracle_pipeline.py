@@ -172,7 +172,7 @@ def pin_prefill_topk(fn):
     return True
 
 
-def pin_kv_append(fn):
+def pin_kv_append(fn, kv_fmt="e8m0_32"):
     # Tiny caches with a sentinel fill: a row is rewritten exactly when some
     # new token maps to it (inverse map: i = p - pos[b] for cache row p,
     # window slot j holding token swa_pos0[b] + j); every other row keeps
@@ -186,18 +186,21 @@ def pin_kv_append(fn):
     rng = np.random.default_rng(40)
     kv_new = synth.to_bf16_bits(torch.from_numpy(rng.standard_normal((B, n_new, 512))).float())
     swa_new = synth.to_bf16_bits(torch.from_numpy(rng.standard_normal((B, n_new, 512))).float())
+    nsc = 16 if kv_fmt == "e8m0_32" else 32
+    quant = synth.to_mxfp4 if kv_fmt == "e8m0_32" else synth.to_fp4_e4m3
     fp4 = np.full((B, n_cap, 256), 0xAB, np.uint8)
-    sc = np.full((B, n_cap, 16), 0xCD, np.uint8)
+    sc = np.full((B, n_cap, nsc), 0xCD, np.uint8)
     swa = np.full((B, s_cap, 512), 0xEF, np.uint8)
-    got_fp4, got_sc, got_swa = fn(fp4, sc, swa, kv_new.numpy().view(np.uint16),
-                                  swa_new.numpy().view(np.uint16), pos, swa_pos0)
+    args = (fp4, sc, swa, kv_new.numpy().view(np.uint16), swa_new.numpy().view(np.uint16), pos,
+            swa_pos0)
+    got_fp4, got_sc, got_swa = fn(*args) if kv_fmt == "e8m0_32" else fn(*args, kv_fmt=kv_fmt)
     kv_f = kv_new.view(torch.bfloat16).float()
     sw_f = swa_new.view(torch.bfloat16).float()
     for b in range(B):
         for p in range(n_cap):
             i = p - pos[b]
             if 0 <= i < n_new:
-                wp, ws = synth.to_mxfp4(kv_f[b, i][None])
+                wp, ws = quant(kv_f[b, i][None])
                 want_p, want_s = wp[0].numpy(), ws[0].numpy()
             else:
                 want_p, want_s = fp4[b, p], sc[b, p]
@@ -296,3 +299,22 @@ def test_kv_append_placement_and_skip_rules():
 
 def test_attention_assembles_selected_and_window_entries():
     assert pin_attention(pipeline.attention)
+
+
+def test_kv_append_e4m3_layout():
+    # The page's layout: 32 E4M3 scales per row, from the torch recipe.
+    assert pin_kv_append(pipeline.kv_append, kv_fmt="e4m3_16")
+
+
+def test_decode_main_kv_e4m3_layout():
+    # E2M1 value listing times torch's float8_e4m3fn cast of the scales.
+    rng = np.random.default_rng(51)
+    fp4 = rng.integers(0, 256, (5, 256), dtype=np.uint8)
+    sc = rng.integers(0, 0x7E, (5, 32), dtype=np.uint8)
+    table = torch.tensor([0, .5, 1, 1.5, 2, 3, 4, 6, 0, -.5, -1, -1.5, -2, -3, -4, -6],
+                         dtype=torch.float64)
+    t = torch.from_numpy(fp4)
+    nib = torch.stack([t & 15, t >> 4], dim=-1).reshape(5, 512).long()
+    s = torch.from_numpy(sc).view(torch.float8_e4m3fn).double().repeat_interleave(16, -1)
+    np.testing.assert_array_equal(pipeline.decode_main_kv(fp4, sc, "e4m3_16"),
+                                  (table[nib] * s).numpy())
