@@ -47,8 +47,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="full_reindex_1m",
-                   choices=["tiny_2k", "full_64k", "reuse_128k", "full_reindex_1m", "prefill_128k",
-                            "kv_append_64k"])
+                   choices=["tiny_2k", "full_64k", "reuse_128k", "reuse_128k_e4m3",
+                            "full_reindex_1m", "prefill_128k", "kv_append_64k"])
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU time budget of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -80,6 +80,7 @@ ROTATED = {
     "tiny_2k": (),
     "full_64k": ("q_idx", "w_idx", "k_idx", "q", "swa"),
     "reuse_128k": ("q", "swa", "idx"),
+    "reuse_128k_e4m3": ("q", "swa", "idx"),
     "full_reindex_1m": (),
     "prefill_128k": (),
     "kv_append_64k": ("kv_new", "swa_new"),
@@ -138,7 +139,7 @@ class Step:
         self.lse = z(B, n_q, 64, dt=torch.float32)
         self.idx = z(B, n_q, 512)
         self.ws_attn = self._ws(csa.OP_SPARSE_ATTN, 512, 0)
-        if name == "reuse_128k":
+        if name.startswith("reuse_128k"):
             return
         if name == "prefill_128k":
             # The flat Top-512 reads the scores; no block maxima are needed.
@@ -173,15 +174,16 @@ class Step:
         """Launch only the kernel the roofline figure is about."""
         if self.name == "kv_append_64k":
             self.run()
-        elif self.name == "reuse_128k":
+        elif self.name.startswith("reuse_128k"):
             d = self._next()
             self._attn(d, self.csa.reuse_attn, d["q"], d["swa"], d["idx"], self.out, self.lse)
         else:
             self._scan(self._next())
 
     def _attn(self, d, fn, q, swa, idx, out, lse):
+        fmt = self.csa.KV_FP4_E4M3_16 if d.get("kv_fmt") == "e4m3_16" else self.csa.KV_MXFP4_E8M0_32
         fn(q, d["kv_fp4"], d["kv_scale"], idx, swa, d["swa_pos0"], d["q_pos"], d["sm_scale"], out,
-           lse=lse, ws=self.ws_attn)
+           lse=lse, kv_fmt=fmt, ws=self.ws_attn)
 
     def run(self):
         d, csa = self._next(), self.csa
@@ -189,7 +191,7 @@ class Step:
             csa.kv_append(d["kv_new"], d["pos"], d["kv_fp4"], d["kv_scale"], swa_new=d["swa_new"],
                           swa_kv=d["swa"], swa_pos0=d["swa_pos0"])
             return
-        if self.name == "reuse_128k":
+        if self.name.startswith("reuse_128k"):
             self._attn(d, csa.reuse_attn, d["q"], d["swa"], d["idx"], self.out, self.lse)
             return
         self._scan(d)
@@ -217,8 +219,12 @@ def algorithmic(name, d):
         # window row: the bf16 entry read, its FP8 row written; pos, swa_pos0.
         per = B * (d["n_new"] * (1024 + 256 + 16) + d["swa"].shape[1] * (1024 + 512) + 8)
         return "kv_append", per, "hbm", per
-    attn_bytes = 512 * 272 + 128 * 512 + 64 * 512 * 2 * 2 + 512 * 4 + 64 * 4   # per query row
-    if name == "reuse_128k":
+    # Per query row: 512 selected entries (256 B of E2M1 plus 16 B of E8M0
+    # or 32 B of E4M3 scales), 128 FP8 window entries, q in and out (bf16),
+    # the indices and lse.
+    entry = 256 + (32 if d.get("kv_fmt") == "e4m3_16" else 16)
+    attn_bytes = 512 * entry + 128 * 512 + 64 * 512 * 2 * 2 + 512 * 4 + 64 * 4
+    if name.startswith("reuse_128k"):
         per = B * attn_bytes
         return "sparse_attn", per, "hbm", per
     T = d["k_idx"].shape[1]
@@ -277,11 +283,12 @@ def cpu_baseline(name, d, budget_s):
                 kr = kr.view(np.uint16)
         swa = npy(d["swa"][b])
         t0 = time.perf_counter()
-        if name == "reuse_128k":
+        if name.startswith("reuse_128k"):
             idx = npy(d["idx"][b, j])
             fp4, sc = npy(d["kv_fp4"][b][d["idx"][b, j].long()]), npy(d["kv_scale"][b][d["idx"][b, j].long()])
             pipeline.attention(npy(d["q"][b, j]).view(np.uint16), fp4, sc, np.arange(len(idx)), swa,
-                               int(d["swa_pos0"][b]), int(d["q_pos"][b, j]), d["sm_scale"])
+                               int(d["swa_pos0"][b]), int(d["q_pos"][b, j]), d["sm_scale"],
+                               kv_fmt=d.get("kv_fmt", "e8m0_32"))
         else:
             vis = int(d["vis_len"][b, j])
             qi, w = npy(d["q_idx"][b, j]).view(np.uint16), npy(d["w_idx"][b, j])
@@ -434,13 +441,15 @@ def measure(name, args, torch, synth, csa, cpu=True, graph=True):
         cfg = {"workload": name, "batch": d["B"], "tokens_per_sequence": d["n_new"],
                "window": d["swa"].shape[1], "main_kv": "MXFP4 (E2M1 + E8M0/32)", "swa_kv": "FP8 E4M3FN"}
     else:
-        reuse = name == "reuse_128k"
+        reuse = name.startswith("reuse_128k")
         cfg = {"workload": name, "batch": d["B"], "query_rows": rows, "context": T,
                "indexer_k": None if reuse else d.get("kdtype"), "top_k": 512,
                "pool_blocks": None if reuse or name == "prefill_128k" else 2048, "window": 128,
                "layers": {"full_64k": "Full", "tiny_2k": "Full", "reuse_128k": "Reuse",
-                          "full_reindex_1m": "Full+Reindex",
-                          "prefill_128k": "prefill (m=2)"}[name]}
+                          "reuse_128k_e4m3": "Reuse", "full_reindex_1m": "Full+Reindex",
+                          "prefill_128k": "prefill (m=2)"}[name],
+               "main_kv": ("E2M1 + E4M3/16" if d.get("kv_fmt") == "e4m3_16"
+                           else "MXFP4 (E2M1 + E8M0/32)")}
     cfg["input_sets"] = len(sets)
     if step_bytes:
         cfg["step_algorithmic_bytes"] = step_bytes
@@ -479,11 +488,12 @@ def main():
     rec.update({"higher_is_better": True, "scaling": "weak", "vs_baseline": None,
                 "dtype": "fp32" if append else "bf16", "data": "synthetic"})
     if args.workload == "full_reindex_1m" and not args.no_extra:
-        # The 128K points of the metric: the Reuse-layer decode (B=64) and the
-        # encoder prefill chunk, each with its own dominant call's roofline.
+        # The 128K points of the metric: the Reuse-layer decode (B=64) with
+        # either main-KV scale format and the encoder prefill chunk, each with
+        # its own dominant call's roofline.
         rec["points_128k"] = [
             measure(w, args, torch, synth, csa, cpu=False, graph=False)
-            for w in ("reuse_128k", "prefill_128k")]
+            for w in ("reuse_128k", "reuse_128k_e4m3", "prefill_128k")]
     print(json.dumps(rec), flush=True)
 
 

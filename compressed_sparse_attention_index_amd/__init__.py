@@ -12,7 +12,7 @@ import os
 import torch
 
 __all__ = [
-    "KDTYPE_BF16", "KDTYPE_FP8", "MODE_FULL", "MODE_REINDEX", "MODE_REUSE",
+    "KDTYPE_BF16", "KDTYPE_FP8", "KV_MXFP4_E8M0_32", "KV_FP4_E4M3_16", "MODE_FULL", "MODE_REINDEX", "MODE_REUSE",
     "OP_INDEX_SCORE", "OP_BLOCK_TOPK", "OP_REINDEX_TOPK", "OP_SPARSE_ATTN",
     "Csa2Error", "lib", "abi_version", "workspace_size", "index_score", "block_topk",
     "block_topk_noalloc",
@@ -20,6 +20,7 @@ __all__ = [
 ]
 
 KDTYPE_BF16, KDTYPE_FP8 = 0, 1
+KV_MXFP4_E8M0_32, KV_FP4_E4M3_16 = 0, 1   # main-KV scale formats (csa2_kvfmt)
 MODE_FULL, MODE_REINDEX, MODE_REUSE = 0, 1, 2
 OP_INDEX_SCORE, OP_BLOCK_TOPK, OP_REINDEX_TOPK, OP_SPARSE_ATTN = 0, 1, 2, 3
 
@@ -38,7 +39,7 @@ _SIGNATURES = {
     "csa2_sparse_attn_decode": [_P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _F, _P, _I, _I, _P, _P,
                                 _P, _S, _P],
     "csa2_reuse_attn": [_P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _F, _P, _I, _I, _P, _P, _P, _S, _P],
-    "csa2_kv_append": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _I, _P, _P],
+    "csa2_kv_append": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P],
     "csa2_workspace_size": [_I, _I, _I, _I, _I, _I],
     "csa2_status_string": [_I],
     "csa2_abi_version": [],
@@ -179,7 +180,7 @@ def reindex_topk(mode, vis_len, N_cap, top_k, idx_out, scores=None, q_idx=None, 
 
 
 def _attn(name, q, kv_fp4, kv_scale, idx, swa_kv, swa_pos0, q_pos, sm_scale, out, lse=None,
-          window=128, replay_start=-1, sink=None, ws=None, stream=None):
+          window=128, replay_start=-1, sink=None, kv_fmt=KV_MXFP4_E8M0_32, ws=None, stream=None):
     B, n_q = q.shape[0], q.shape[1]
     N_cap = kv_fp4.shape[1]
     top_k = idx.shape[-1] if idx is not None else 0
@@ -187,7 +188,7 @@ def _attn(name, q, kv_fp4, kv_scale, idx, swa_kv, swa_pos0, q_pos, sm_scale, out
     need = workspace_size(OP_SPARSE_ATTN, B, n_q, N_cap, top_k, 0)
     ws, nbytes = _workspace(ws, need, q.device)
     sp = _ptr(sink, _F32, "sink")
-    opts = AttnOpts(window, replay_start, 0, ATTN_SINK if sp else 0, sp)
+    opts = AttnOpts(window, replay_start, kv_fmt, ATTN_SINK if sp else 0, sp)
     _call(name, _ptr(q, _BITS16, "q"), _ptr(kv_fp4, _U8, "kv_fp4"),
           _ptr(kv_scale, _U8, "kv_scale"), N_cap, _ptr(idx, _I32, "idx"), top_k,
           _ptr(swa_kv, _U8, "swa_kv"), S_cap, _ptr(swa_pos0, _I32, "swa_pos0"),
@@ -207,13 +208,14 @@ def reuse_attn(*args, **kw):
 
 
 def kv_append(kv_new, pos, kv_fp4, kv_scale, swa_new=None, swa_kv=None, swa_pos0=None,
-              stream=None):
-    """Encodes new tokens' entries (kv_new [B, n_new, 512] bf16 -> MXFP4 rows
-    pos[b] + i of kv_fp4 / kv_scale; swa_new -> FP8 rows of swa_kv)."""
+              kv_fmt=KV_MXFP4_E8M0_32, stream=None):
+    """Encodes new tokens' entries (kv_new [B, n_new, 512] bf16 -> E2M1 rows
+    pos[b] + i of kv_fp4 with scales in kv_scale, format kv_fmt; swa_new ->
+    FP8 rows of swa_kv)."""
     B, n_new = kv_new.shape[0], kv_new.shape[1]
     N_cap = kv_fp4.shape[1]
     S_cap = swa_kv.shape[1] if swa_kv is not None else 0
     _call("csa2_kv_append", _ptr(kv_new, _BITS16, "kv_new"), _ptr(swa_new, _BITS16, "swa_new"),
-          _ptr(pos, _I32, "pos"), B, n_new, N_cap, _ptr(kv_fp4, _U8, "kv_fp4"),
+          _ptr(pos, _I32, "pos"), B, n_new, N_cap, kv_fmt, _ptr(kv_fp4, _U8, "kv_fp4"),
           _ptr(kv_scale, _U8, "kv_scale"), _ptr(swa_kv, _U8, "swa_kv"), S_cap,
           _ptr(swa_pos0, _I32, "swa_pos0"), _stream(stream))

@@ -3,8 +3,12 @@
 // contract of each entry point.
 #include "../../include/csa2.h"
 #include "csa2_launch.h"
+#include "csa2_device.h"
 
 #include <stdint.h>
+
+static_assert(csa2::kFmtE8M0 == CSA2_KV_MXFP4_E8M0_32 && csa2::kFmtE4M3 == CSA2_KV_FP4_E4M3_16,
+              "kernel format ids follow csa2_kvfmt");
 
 namespace {
 
@@ -39,11 +43,13 @@ csa2_status attn_common(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t*
   // A softmax scale is positive and finite (1 / sqrt(512) on these layers);
   // the kernel relies on it to keep empty slots at -inf.
   if (!(sm_scale > 0.0f) || !(sm_scale < __builtin_inff())) return CSA2_ERR_SHAPE;
-  int32_t window = 128, replay_start = -1;
+  int32_t window = 128, replay_start = -1, kv_fmt = CSA2_KV_MXFP4_E8M0_32;
   const float* sink = nullptr;
   if (opts) {
-    if (opts->kv_fmt != CSA2_KV_MXFP4_E8M0_32 || (opts->flags & ~CSA2_ATTN_SINK) != 0)
+    if ((opts->kv_fmt != CSA2_KV_MXFP4_E8M0_32 && opts->kv_fmt != CSA2_KV_FP4_E4M3_16) ||
+        (opts->flags & ~CSA2_ATTN_SINK) != 0)
       return CSA2_ERR_UNSUPPORTED;
+    kv_fmt = opts->kv_fmt;
     if (opts->window < 0 || opts->window > 128 || opts->replay_start < -1) return CSA2_ERR_SHAPE;
     window = opts->window;
     replay_start = opts->replay_start;
@@ -60,7 +66,7 @@ csa2_status attn_common(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t*
   if (ws && !aligned16(ws)) return CSA2_ERR_ALIGN;
   return from_hip(csa2::launch_sparse_attn(q, kv_fp4, kv_scale, N_cap, idx, top_k, swa_kv, S_cap,
                                            swa_pos0, q_pos, sm_scale, window, replay_start, sink,
-                                           B, n_q, out, lse, ws, stream));
+                                           kv_fmt, B, n_q, out, lse, ws, stream));
 }
 
 }  // namespace
@@ -179,18 +185,20 @@ csa2_status csa2_reuse_attn(const uint16_t* q, const uint8_t* kv_fp4, const uint
 }
 
 csa2_status csa2_kv_append(const uint16_t* kv_new, const uint16_t* swa_new, const int32_t* pos,
-                           int32_t B, int32_t n_new, int32_t N_cap, uint8_t* kv_fp4,
-                           uint8_t* kv_scale, uint8_t* swa_kv, int32_t S_cap,
+                           int32_t B, int32_t n_new, int32_t N_cap, int32_t kv_fmt,
+                           uint8_t* kv_fp4, uint8_t* kv_scale, uint8_t* swa_kv, int32_t S_cap,
                            const int32_t* swa_pos0, hipStream_t stream) {
   if (!kv_new || !pos || !kv_fp4 || !kv_scale) return CSA2_ERR_NULL;
   if (swa_new && (!swa_kv || !swa_pos0)) return CSA2_ERR_NULL;
   csa2_status st = check_rows(B, n_new);
   if (st != CSA2_OK) return st;
   if (N_cap < 1 || N_cap > kMaxNcap || S_cap < 0) return CSA2_ERR_SHAPE;
+  if (kv_fmt != CSA2_KV_MXFP4_E8M0_32 && kv_fmt != CSA2_KV_FP4_E4M3_16) return CSA2_ERR_UNSUPPORTED;
   const void* ptrs[] = {kv_new, swa_new, pos, kv_fp4, kv_scale, swa_kv, swa_pos0};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return CSA2_ERR_ALIGN;
-  return from_hip(csa2::launch_kv_append(kv_new, swa_new, pos, B, n_new, N_cap, kv_fp4, kv_scale,
+  return from_hip(csa2::launch_kv_append(kv_new, swa_new, pos, B, n_new, N_cap, kv_fmt, kv_fp4,
+                                         kv_scale,
                                          swa_new ? swa_kv : nullptr, S_cap, swa_pos0, stream));
 }
 

@@ -103,8 +103,10 @@ struct Ctx {
 
 // A tile's raw bytes for one lane, halves h = 0, 1 (entries m and 16 + m).
 // Selected entries (MainRaw): f[h][0..1] = E2M1 bytes 128 d + 32 c .. + 32,
-// sc[h] = the dword of E8M0 scales holding blocks 8 d + 2 c and 8 d + 2 c +
-// 1.  Window entries (WinRaw): v[h][0..3] = FP8 bytes 256 d + 64 c .. + 64.
+// sc[h] = the dword of scales covering those 64 dims: E8M0 blocks 8 d + 2 c
+// and + 1 (bytes 2 (c % 2) + k), or E4M3 blocks 16 d + 4 c .. + 3 (bytes
+// 0..3).  Window entries (WinRaw): v[h][0..3] = FP8 bytes 256 d + 64 c ..
+// + 64.
 struct MainRaw {
   u32x4 f[2][2];
   uint32_t sc[2];
@@ -155,8 +157,10 @@ __device__ __forceinline__ float head_sum(float v) {
 // call issues the same loads (a tile past the list reads slots that hold -1
 // and so entry 0 of the sequence), so that the compiler can count the loads
 // still in flight on every path and wait only for the ones it needs.
+template <int FMT>
 __device__ __forceinline__ void gather_main(const AttnArgs& a, const Ctx& x, const int32_t* ids,
                                             int t, MainRaw& w) {
+  constexpr int kSc = KvFmt<FMT>::kScaleBytes;
   t = min(t, kMaxTopK / kTile - 1);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -167,7 +171,8 @@ __device__ __forceinline__ void gather_main(const AttnArgs& a, const Ctx& x, con
     const uint8_t* src = a.kv_fp4 + er * 256 + 128 * x.d + 32 * x.c;
     w.f[h][0] = *reinterpret_cast<const u32x4*>(src);
     w.f[h][1] = *reinterpret_cast<const u32x4*>(src + 16);
-    w.sc[h] = *reinterpret_cast<const uint32_t*>(a.kv_scale + er * 16 + 8 * x.d + 4 * (x.c >> 1));
+    const int sc_off = FMT == kFmtE8M0 ? 8 * x.d + 4 * (x.c >> 1) : 16 * x.d + 4 * x.c;
+    w.sc[h] = *reinterpret_cast<const uint32_t*>(a.kv_scale + er * kSc + sc_off);
   }
 }
 
@@ -192,11 +197,21 @@ __device__ __forceinline__ void gather_window(const AttnArgs& a, const Ctx& x, i
 // Dequantisation, LDS store and the partial S^T = K . q^T of one tile.
 // Step s: lane (m, c) supplies dims 256 d + 64 c + 8 s .. + 8 of entry
 // 16 h + m, which is 16-byte chunk 8 c + s of its LDS row.
-template <bool kMain, class R>
+template <bool kMain, int FMT, class R>
 __device__ __forceinline__ void qk_tile(const Ctx& x, const R& w, const State& st, uint8_t* tile,
                                         f32x4_t (&acc)[2]) {
-  float scale[2][2];
-  if constexpr (kMain) {
+  // Scale of step s: E8M0 per 32 dims, scale[h][s / 4]; E4M3 per 16 dims,
+  // scale[h][s / 2].
+  float scale[2][4];
+  if constexpr (kMain && FMT == kFmtE4M3) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float f[4];
+      e4m3x4_to_f32(w.sc[h], f);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) scale[h][k] = w.valid[h] ? f[k] : 0.0f;
+    }
+  } else if constexpr (kMain) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       // Blocks 8 d + 2 c + k: bytes 2 (c % 2) + k of the loaded dword.
@@ -204,8 +219,9 @@ __device__ __forceinline__ void qk_tile(const Ctx& x, const R& w, const State& s
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         // E8M0 -> 2^(code - 127): code 0 is the subnormal 2^-127, code 255
-        // NaN.  An empty slot gets scale 0 (E2M1 has no NaN, so its values
-        // become 0).  Selects only, no branches.
+        // NaN.  An empty slot gets the bits 0, read as 2^-127 by the
+        // conversion: finite values, which the softmax masks by the slot's
+        // validity.  Selects only, no branches.
         const uint32_t code = (two >> (8 * k)) & 0xffu;
         uint32_t bits = code << 23;
         bits = code == 0 ? 0x00400000u : bits;
@@ -225,7 +241,10 @@ __device__ __forceinline__ void qk_tile(const Ctx& x, const R& w, const State& s
     for (int h = 0; h < 2; ++h) {
       bf16x8 kb;
       if constexpr (kMain) {
-        kb = fp4x8_to_bf16x8(word_of(w.f[h][s >> 2], s & 3), scale[h][s >> 2]);
+        if constexpr (FMT == kFmtE4M3)
+          kb = fp4x8_mul_to_bf16x8(word_of(w.f[h][s >> 2], s & 3), scale[h][s >> 1]);
+        else
+          kb = fp4x8_to_bf16x8(word_of(w.f[h][s >> 2], s & 3), scale[h][s >> 2]);
       } else {
         const u32x4& q4 = w.v[h][s >> 1];
         const uint32_t lo = (s & 1) ? q4.z : q4.x, hi = (s & 1) ? q4.w : q4.y;
@@ -335,13 +354,13 @@ __device__ __forceinline__ void signal_counter(uint32_t* ctr, uint32_t v) {
 // `work` (the same in both waves of the pair).  The exchange: a wave writes
 // its partial S^T once its partner has taken the one of the pair's previous
 // exchange, signals it, and reads the partner's once that is signalled.
-template <bool kMain, class R>
+template <bool kMain, int FMT, class R>
 __device__ __forceinline__ void round_tile(const AttnArgs& a, const Ctx& x, Smem& sm, const R& w,
                                            bool work, uint32_t round, uint8_t* tile, int off_a,
                                            int off_b, State& st) {
   if (!work) return;
   f32x4_t acc[2];
-  qk_tile<kMain, R>(x, w, st, tile, acc);
+  qk_tile<kMain, FMT, R>(x, w, st, tile, acc);
   const int partner = x.wave ^ 1;
   wait_counter(&sm.taken[partner], st.exchanged);
   st.exchanged = round;
@@ -358,6 +377,7 @@ __device__ __forceinline__ void round_tile(const AttnArgs& a, const Ctx& x, Smem
   else softmax_pv(a, x, vm0, vm1, tile, off_a, off_b, other, acc, st);
 }
 
+template <int FMT>
 __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) Smem sm;
   Ctx x;
@@ -427,25 +447,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
     gather_window(a, x, x.pair, wr);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();   // the ids are in LDS (the window loads stay in flight)
-    gather_main(a, x, sm.ids, x.pair, m0);
+    gather_main<FMT>(a, x, sm.ids, x.pair, m0);
     __builtin_amdgcn_sched_barrier(0);
     const bool work = __ballot(wr.valid[0] || wr.valid[1]) != 0;
     uint32_t round = 1;
-    round_tile<false>(a, x, sm, wr, work, round, tile, off_a, off_b, st);
+    round_tile<false, FMT>(a, x, sm, wr, work, round, tile, off_a, off_b, st);
     const int rounds = (x.sel_tiles + kPairs - 1) / kPairs;
     int t = x.pair;
     auto run = [&](const MainRaw& w) {
       ++round;
       const bool wk = t < x.sel_tiles && __ballot(w.valid[0] || w.valid[1]) != 0;
-      round_tile<true>(a, x, sm, w, wk, round, tile, off_a, off_b, st);
+      round_tile<true, FMT>(a, x, sm, w, wk, round, tile, off_a, off_b, st);
       t += kPairs;
     };
     for (int i = 0; i < rounds; i += 2) {
-      gather_main(a, x, sm.ids, t + kPairs, m1);
+      gather_main<FMT>(a, x, sm.ids, t + kPairs, m1);
       __builtin_amdgcn_sched_barrier(0);
       run(m0);
       if (i + 1 >= rounds) break;
-      gather_main(a, x, sm.ids, t + kPairs, m0);
+      gather_main<FMT>(a, x, sm.ids, t + kPairs, m0);
       __builtin_amdgcn_sched_barrier(0);
       run(m1);
     }
@@ -511,14 +531,15 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* kv_fp4, const ui
                               int N_cap, const int32_t* idx, int top_k, const uint8_t* swa_kv,
                               int S_cap, const int32_t* swa_pos0, const int32_t* q_pos,
                               float sm_scale, int window, int replay_start, const float* sink,
-                              int B, int n_q, uint16_t* out, float* lse, void* ws,
+                              int kv_fmt, int B, int n_q, uint16_t* out, float* lse, void* ws,
                               hipStream_t stream) {
   (void)ws;
   // Prefill-shaped calls (many query rows per sequence) take the one-row-
   // per-workgroup kernel; the choice depends on n_q only, never on B.
   if (n_q >= kRowsKernelMinNq)
     return launch_attn_rows(q, kv_fp4, kv_scale, N_cap, idx, top_k, swa_kv, S_cap, swa_pos0,
-                            q_pos, sm_scale, window, replay_start, sink, B, n_q, out, lse, stream);
+                            q_pos, sm_scale, window, replay_start, sink, kv_fmt, B, n_q, out,
+                            lse, stream);
   AttnArgs a;
   a.q = q; a.kv_fp4 = kv_fp4; a.kv_scale = kv_scale; a.idx = idx; a.swa = swa_kv;
   a.swa_pos0 = swa_pos0; a.q_pos = q_pos; a.out = out; a.lse = lse; a.sink = sink;
@@ -529,8 +550,12 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* kv_fp4, const ui
   // Rows in groups of 8 (one per XCD), 4 head groups each.
   const long long wgs = static_cast<long long>((a.rows + 7) / 8) * 8 * kGroupsPerRow;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(k_sparse_attn, dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, stream,
-                     a);
+  if (kv_fmt == kFmtE8M0)
+    hipLaunchKernelGGL(k_sparse_attn<kFmtE8M0>, dim3(static_cast<unsigned>(wgs)), dim3(kThreads),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL(k_sparse_attn<kFmtE4M3>, dim3(static_cast<unsigned>(wgs)), dim3(kThreads),
+                       0, stream, a);
   return hipGetLastError();
 }
 

@@ -54,8 +54,10 @@ constexpr int kTile = 32;
 constexpr int kRow = 1024;         // LDS bytes of one dequantised entry (512 bf16)
 constexpr int kBuf = kChunk * kRow;
 constexpr int kStage = 8192;       // staging bytes per wave and chunk
-constexpr int kMainLoads = 5;      // direct-to-LDS loads per wave: selected tile
-constexpr int kWindowLoads = 8;    //                                 window tile
+// Direct-to-LDS loads per wave and tile: selected tiles 4 x 16 B of E2M1
+// plus one (E8M0) or two (E4M3) dwords of scales; window tiles 8 x 16 B.
+template <int FMT> constexpr int kMainLoads = FMT == kFmtE8M0 ? 5 : 6;
+constexpr int kWindowLoads = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxChunks = (kMaxTopK + kMaxWindow + kChunk - 1) / kChunk;
@@ -131,10 +133,12 @@ __device__ __forceinline__ bf16x8 tr_read_pair(const uint8_t* v, int off0, int o
 // Issues the wave's direct-to-LDS loads of its tile of chunk ch (entry tile
 // e, dims half dh) into staging slot `stg` and returns whether the lane's
 // slot holds an entry.  Slot layout: load i of lane l lands at 1024 i + 16 l
-// (selected tiles: 4 x 16 B of E2M1 and, at 4096 + 4 l, the 4 E8M0 scales;
-// window tiles: 8 x 16 B of FP8).  An empty slot reads a row that always
+// (selected tiles: 4 x 16 B of E2M1 and, at 4096 + 4 l, the 4 E8M0 scales of
+// its 128 dims, or at 4096 + 4 l and 4352 + 4 l its 8 E4M3 scales; window
+// tiles: 8 x 16 B of FP8).  An empty slot reads a row that always
 // exists (entry 0 of the sequence, or the query row), so every tile of a kind
 // issues a fixed number of loads; it is zeroed when dequantised.
+template <int FMT>
 __device__ __forceinline__ bool issue_tile(const AttnArgs& a, const Ctx& x, Smem& sm, int ch,
                                            int stg) {
   const int slot = kChunk * ch + kTile * x.e + x.c;
@@ -146,7 +150,13 @@ __device__ __forceinline__ bool issue_tile(const AttnArgs& a, const Ctx& x, Smem
     const uint8_t* src = a.kv_fp4 + er * 256 + 128 * x.dh + 64 * x.half;
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(src + 16 * i, dst + 1024 * i);
-    dma4(a.kv_scale + er * 16 + 8 * x.dh + 4 * x.half, dst + 4096);
+    if (FMT == kFmtE8M0) {
+      dma4(a.kv_scale + er * 16 + 8 * x.dh + 4 * x.half, dst + 4096);
+    } else {
+      const uint8_t* sc = a.kv_scale + er * 32 + 16 * x.dh + 8 * x.half;
+      dma4(sc, dst + 4096);
+      dma4(sc + 4, dst + 4352);
+    }
     return valid;
   }
   const int j = slot - x.tkp;
@@ -164,18 +174,20 @@ __device__ __forceinline__ bool issue_tile(const AttnArgs& a, const Ctx& x, Smem
 // Dequantisation of the lane's entry from its staging slot, 16 bytes of raw
 // data (a unit) at a time: a unit holds 8-dim groups k = 4 u .. 4 u + 3 of
 // E2M1 (selected entries) or k = 2 u, 2 u + 1 of FP8 (window); group k is
-// dims 256 dh + 128 half + 8 k.  Empty slots give zeros: scale 0 for E2M1,
-// which has no NaN; zeroed bytes for FP8.
-template <bool kMain>
+// dims 256 dh + 128 half + 8 k, whose scale is E8M0 block k / 4 or E4M3
+// block k / 2 of the lane's 128 dims.  Empty slots get the scale bits 0
+// (read as 2^-127 by the E8M0 conversion, 0 by the E4M3 multiply) or zeroed
+// FP8 bytes: finite values, which the softmax masks by the slot's validity.
+template <bool kMain, int FMT>
 struct Dequant {
   static constexpr int kPerUnit = kMain ? 4 : 2;
   static constexpr int kUnits = 16 / kPerUnit;
-  float scale[4];
+  float scale[8];
   const uint8_t* sp;
   bool valid;
   __device__ __forceinline__ Dequant(const uint8_t* slot, int lane, bool lane_valid)
       : sp(slot + 16 * lane), valid(lane_valid) {
-    if (kMain) {
+    if (kMain && FMT == kFmtE8M0) {
       const uint32_t sc = *reinterpret_cast<const uint32_t*>(slot + 4096 + 4 * lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -183,12 +195,21 @@ struct Dequant {
         uint32_t bits = code == 0 ? 0x00400000u : (code == 255 ? 0x7fc00000u : code << 23);
         scale[i] = __uint_as_float(lane_valid ? bits : 0u);
       }
+    } else if (kMain) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        float f[4];
+        e4m3x4_to_f32(*reinterpret_cast<const uint32_t*>(slot + 4096 + 256 * q + 4 * lane), f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) scale[4 * q + i] = lane_valid ? f[i] : 0.0f;
+      }
     }
   }
   __device__ __forceinline__ u32x4 unit(int u) const {
     return *reinterpret_cast<const u32x4*>(sp + 1024 * u);
   }
   __device__ __forceinline__ bf16x8 convert(const u32x4& w, int k) const {
+    if (kMain && FMT == kFmtE4M3) return fp4x8_mul_to_bf16x8(word_of(w, k & 3), scale[k >> 1]);
     if (kMain) return fp4x8_to_bf16x8(word_of(w, k & 3), scale[k >> 2]);
     const uint32_t lo = (k & 1) ? w.z : w.x, hi = (k & 1) ? w.w : w.y;
     return fp8x8_to_bf16x8(valid ? lo : 0u, valid ? hi : 0u);
@@ -277,11 +298,11 @@ __device__ __forceinline__ TrOffs tr_offsets(const Ctx& x) {
 // Chunk ch's tile: dequantised once, written to the LDS buffer (16-byte chunk
 // k of the lane's row at st_off ^ (k << 4)) and multiplied into the partial
 // S^T of both head tiles.
-template <bool kMain>
+template <bool kMain, int FMT>
 __device__ __forceinline__ void qk_store(const Ctx& x, Smem& sm, const State& st,
                                          const uint8_t* slot, bool valid, int st_off,
                                          f32x16 (&acc)[2]) {
-  using D = Dequant<kMain>;
+  using D = Dequant<kMain, FMT>;
   const D dq(slot, x.lane, valid);
   u32x4 raw[2];
   raw[0] = dq.unit(0);
@@ -325,7 +346,7 @@ __device__ __forceinline__ void pv(const Ctx& x, const Smem& sm, State& st, cons
 // Chunk ch, staged in slot S; kPV: the previous chunk's PV comes first.
 // `valid` (the lane's slot validity) is replaced by that of chunk ch + 2,
 // whose loads go to the same slot once it has been read.
-template <bool kMain, bool kPV>
+template <bool kMain, bool kPV, int FMT>
 __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Ctx& x, Smem& sm, State& st,
                                              bool& valid, int ch, int c1, int S, int st_off,
                                              const TrOffs& tr) {
@@ -337,7 +358,7 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Ctx& x, Sm
   }
   // This chunk's loads have landed once only chunk ch + 1's are outstanding.
   if (ch + 1 < c1) {
-    if (tile_is_main(x, ch + 1)) wait_vmem<kMainLoads>();
+    if (tile_is_main(x, ch + 1)) wait_vmem<kMainLoads<FMT>>();
     else wait_vmem<kWindowLoads>();
   } else {
     wait_vmem<0>();
@@ -346,9 +367,9 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Ctx& x, Sm
   const uint8_t* slot = sm.stage[S][x.wave];
   const uint32_t vmask = static_cast<uint32_t>(__ballot(valid));
   f32x16 acc[2] = {f32x16{}, f32x16{}};
-  qk_store<kMain>(x, sm, st, slot, valid, st_off, acc);
+  qk_store<kMain, FMT>(x, sm, st, slot, valid, st_off, acc);
   // The staging slot has been read; chunk ch + 2 goes there.
-  if (ch + 2 < c1) valid = issue_tile(a, x, sm, ch + 2, S);
+  if (ch + 2 < c1) valid = issue_tile<FMT>(a, x, sm, ch + 2, S);
 
   // Exchange with the partner wave (e, 1 - dh): it gets this wave's partial
   // of head tile 1 - dh, this wave gets its partial of head tile dh
@@ -413,6 +434,7 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Ctx& x, Sm
   lds_barrier();
 }
 
+template <int FMT>
 __global__ __launch_bounds__(kThreads, 1) void k_attn_rows(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) Smem sm;
 
@@ -470,9 +492,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_rows(AttnArgs a) {
   wait_vmem<0>();
   __syncthreads();
 
-  bool valid0 = issue_tile(a, x, sm, c0, 0);
+  bool valid0 = issue_tile<FMT>(a, x, sm, c0, 0);
   bool valid1 = false;
-  if (c0 + 1 < c1) valid1 = issue_tile(a, x, sm, c0 + 1, 1);
+  if (c0 + 1 < c1) valid1 = issue_tile<FMT>(a, x, sm, c0 + 1, 1);
   // q^T operands (head 32 h + c, dims 256 dh + 128 half + 8 k).  q is only
   // ever an MFMA operand, which may come from accumulation registers:
   // keeping it there leaves the VGPRs to the accumulators and the operands
@@ -507,20 +529,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_rows(AttnArgs a) {
   // Chunks [c0, cm) hold selected entries in this wave's tile, [cm, c1) window
   // entries.
   const int cm = min(max((x.tkp - kTile * x.e + kChunk - 1) / kChunk, c0), c1);
-  if (c0 < cm) attend_chunk<true, false>(a, x, sm, st, valid0, c0, c1, 0, st_off, tr);
-  else attend_chunk<false, false>(a, x, sm, st, valid0, c0, c1, 0, st_off, tr);
+  if (c0 < cm) attend_chunk<true, false, FMT>(a, x, sm, st, valid0, c0, c1, 0, st_off, tr);
+  else attend_chunk<false, false, FMT>(a, x, sm, st, valid0, c0, c1, 0, st_off, tr);
   int ch = c0 + 1;
   for (; ch < cm; ++ch) {
     const int S = (ch - c0) & 1;
     bool v = S ? valid1 : valid0;
-    attend_chunk<true, true>(a, x, sm, st, v, ch, c1, S, st_off, tr);
+    attend_chunk<true, true, FMT>(a, x, sm, st, v, ch, c1, S, st_off, tr);
     if (S) valid1 = v;
     else valid0 = v;
   }
   for (; ch < c1; ++ch) {
     const int S = (ch - c0) & 1;
     bool v = S ? valid1 : valid0;
-    attend_chunk<false, true>(a, x, sm, st, v, ch, c1, S, st_off, tr);
+    attend_chunk<false, true, FMT>(a, x, sm, st, v, ch, c1, S, st_off, tr);
     if (S) valid1 = v;
     else valid0 = v;
   }
@@ -579,7 +601,8 @@ hipError_t launch_attn_rows(const uint16_t* q, const uint8_t* kv_fp4, const uint
                             int N_cap, const int32_t* idx, int top_k, const uint8_t* swa_kv,
                             int S_cap, const int32_t* swa_pos0, const int32_t* q_pos,
                             float sm_scale, int window, int replay_start, const float* sink,
-                            int B, int n_q, uint16_t* out, float* lse, hipStream_t stream) {
+                            int kv_fmt, int B, int n_q, uint16_t* out, float* lse,
+                            hipStream_t stream) {
   const int rows = B * n_q;
   AttnArgs a;
   a.q = q; a.kv_fp4 = kv_fp4; a.kv_scale = kv_scale; a.idx = idx; a.swa = swa_kv;
@@ -591,7 +614,12 @@ hipError_t launch_attn_rows(const uint16_t* q, const uint8_t* kv_fp4, const uint
   a.rows = rows;
   const int tkp = (top_k + kTile - 1) / kTile * kTile;
   a.n_chunks = (tkp + kMaxWindow + kChunk - 1) / kChunk;
-  hipLaunchKernelGGL(k_attn_rows, dim3(static_cast<unsigned>(rows)), dim3(kThreads), 0, stream, a);
+  if (kv_fmt == kFmtE8M0)
+    hipLaunchKernelGGL(k_attn_rows<kFmtE8M0>, dim3(static_cast<unsigned>(rows)), dim3(kThreads), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL(k_attn_rows<kFmtE4M3>, dim3(static_cast<unsigned>(rows)), dim3(kThreads), 0,
+                       stream, a);
   return hipGetLastError();
 }
 

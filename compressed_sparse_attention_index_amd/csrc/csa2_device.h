@@ -2,12 +2,14 @@
 //
 // Number formats (OCP definitions; the method stores main KV as MXFP4 and SWA
 // KV as FP8 -- "DeepSeek-V4.1-Flash 架构详解", §4):
-//   FP8 E4M3FN -> bf16 and E2M1 (with an E8M0 block scale) -> bf16 use the
+//   FP8 E4M3FN -> bf16 and E2M1 (with a block scale) -> bf16 use the
 //   gfx950 scaled-conversion instructions.  Every E4M3FN value is a bf16
 //   value, and so is every E2M1 x 2^(c - 127) for E8M0 codes c <= 252 (the
 //   largest, 6 x 2^125, is below the bf16 maximum; code 0 gives bf16
 //   subnormals): those conversions are exact.  Codes 253 and 254 overflow
-//   bf16 for E2M1 magnitudes >= 4 and >= 2 respectively.
+//   bf16 for E2M1 magnitudes >= 4 and >= 2 respectively.  Every E2M1 x E4M3
+//   product (at most 2 x 4 significant bits, magnitudes 2^-10 .. 2688) is a
+//   bf16 value too.
 // Matrix cores: v_mfma_f32_32x32x16_bf16, wave64.  Operand layout (lane l):
 //   A[m][k]: m = l % 32, k = 8 * (l / 32) + i, i = 0..7
 //   B[k][n]: n = l % 32, k = 8 * (l / 32) + i
@@ -54,7 +56,9 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 }
 
 // Eight E2M1 nibbles (one word, element 2j in the low nibble of byte j) with
-// one block scale -> eight bf16.
+// one power-of-two block scale -> eight bf16.  The gfx950 scaled conversion
+// reads only the exponent field of its fp32 scale operand (as an E8M0 code):
+// the mantissa and the sign are ignored and +0 reads as 2^-127.
 __device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float scale) {
   u32x4 v;
   v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
@@ -62,6 +66,47 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float scale) {
   v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
   v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
   return __builtin_bit_cast(bf16x8, v);
+}
+
+// Eight E2M1 nibbles times an arbitrary fp32 scale s -> eight bf16.  The
+// elements are converted at unit scale (exact) and multiplied by s in fp32;
+// for an E4M3 scale the product of the two has at most 6 significant bits
+// and lies within [2^-10, 2688], so the product and its bf16 rounding are
+// both exact, and s = 0 gives zeros.
+__device__ __forceinline__ bf16x8 fp4x8_mul_to_bf16x8(uint32_t w, float s) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  uint32_t r[4];
+#define CSA2_FP4_PAIR(I)                                                                \
+  {                                                                                     \
+    const f32x2_t f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, I);             \
+    r[I] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f * s, bf16x2_t));      \
+  }
+  CSA2_FP4_PAIR(0)
+  CSA2_FP4_PAIR(1)
+  CSA2_FP4_PAIR(2)
+  CSA2_FP4_PAIR(3)
+#undef CSA2_FP4_PAIR
+  u32x4 v = {r[0], r[1], r[2], r[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Main-KV scale layouts (csa2_kvfmt): E8M0 per 32 elements (16 bytes per
+// entry) or E4M3FN per 16 elements (32 bytes per entry).
+constexpr int kFmtE8M0 = 0;
+constexpr int kFmtE4M3 = 1;
+template <int FMT> struct KvFmt;
+template <> struct KvFmt<kFmtE8M0> { static constexpr int kScaleBytes = 16, kBlock = 32; };
+template <> struct KvFmt<kFmtE4M3> { static constexpr int kScaleBytes = 32, kBlock = 16; };
+
+// Four FP8 E4M3FN bytes -> four floats (exact; the gfx950 conversion).
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float (&f)[4]) {
+  const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+  const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+  f[0] = lo[0];
+  f[1] = lo[1];
+  f[2] = hi[0];
+  f[3] = hi[1];
 }
 
 // E8M0 code -> 2^(code-127) as a float (code 0 gives the subnormal 2^-127,

@@ -1,5 +1,6 @@
 // Internal launchers behind the C ABI (host side).  Arguments are validated by
-// the API layer before any of these is called.
+// the API layer before any of these is called.  A kv_fmt argument is a
+// csa2_kvfmt value (0: E8M0 per 32, 1: E4M3 per 16).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -51,20 +52,21 @@ hipError_t launch_attn_rows(const uint16_t* q, const uint8_t* kv_fp4, const uint
                             int N_cap, const int32_t* idx, int top_k, const uint8_t* swa_kv,
                             int S_cap, const int32_t* swa_pos0, const int32_t* q_pos,
                             float sm_scale, int window, int replay_start, const float* sink,
-                            int B, int n_q, uint16_t* out, float* lse, hipStream_t stream);
+                            int kv_fmt, int B, int n_q, uint16_t* out, float* lse,
+                            hipStream_t stream);
 
 hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
                               int N_cap, const int32_t* idx, int top_k, const uint8_t* swa_kv,
                               int S_cap, const int32_t* swa_pos0, const int32_t* q_pos,
                               float sm_scale, int window, int replay_start, const float* sink,
-                              int B, int n_q, uint16_t* out, float* lse, void* ws,
+                              int kv_fmt, int B, int n_q, uint16_t* out, float* lse, void* ws,
                               hipStream_t stream);
 
 // KV append: MXFP4 main entries and FP8 window entries of new tokens; see
 // kv_append.hip.
 hipError_t launch_kv_append(const uint16_t* kv_new, const uint16_t* swa_new, const int32_t* pos,
-                            int B, int n_new, int N_cap, uint8_t* kv_fp4, uint8_t* kv_scale,
-                            uint8_t* swa, int S_cap, const int32_t* swa_pos0,
+                            int B, int n_new, int N_cap, int kv_fmt, uint8_t* kv_fp4,
+                            uint8_t* kv_scale, uint8_t* swa, int S_cap, const int32_t* swa_pos0,
                             hipStream_t stream);
 
 }  // namespace csa2

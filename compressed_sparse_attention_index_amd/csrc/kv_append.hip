@@ -3,18 +3,28 @@
 // attention kernels read.
 //
 // "DeepSeek-V4.1-Flash 架构详解", §4: main KV is stored as MXFP4 (E2M1
-// elements with block scales; here one E8M0 scale per 32 elements, OCP MX
-// v1.0) and SWA KV as FP8 (E4M3FN).  Encoding rules:
+// elements with block scales) and SWA KV as FP8 (E4M3FN).  Two block-scale
+// formats: one E8M0 scale per 32 elements (OCP MX v1.0) or one E4M3FN scale
+// per 16 elements (the page's §4 layout).  Encoding rules:
 //   MXFP4: per 32 elements the shared exponent X = floor(log2(amax)) - 2
 //     (2 is the largest E2M1 exponent), clamped to [-127, 127]; an all-zero
 //     block takes X = -127.  The E8M0 code is X + 127.  Each element v / 2^X
 //     is rounded to the nearest E2M1 magnitude {0, .5, 1, 1.5, 2, 3, 4, 6},
 //     a tie going to the even code, saturating at 6; a value that rounds to
 //     zero is stored as +0.  Element 2j sits in the low nibble of byte j.
+//   E2M1 with E4M3 scales: per 16 elements the scale s is amax / 6 rounded
+//     to E4M3FN as below, so that the block's largest element lands at the
+//     top of the E2M1 range; each element goes to the E2M1 magnitude nearest
+//     to |v| / s (ties to the even code, saturating at 6), sign kept, a zero
+//     stored as +0; a block whose scale is 0 stores +0 everywhere.
 //   FP8 E4M3FN: saturate to +-448, then round to the nearest value, a tie
 //     going to the even code; the sign is kept for values that round to 0.
 // Inputs are bf16, so every step below is exact in fp32 up to the rounding
-// to the target grid (the scaling by 2^-X is a power of two).
+// to the target grid: the scaling by 2^-X is a power of two; amax / 6 is
+// the correctly rounded fp32 quotient, which never crosses an E4M3 midpoint
+// (a bf16 amax is either exactly 6 times a midpoint or at least one bf16 ulp
+// from it); and |v| is compared with t s, midpoint t times the E4M3 scale,
+// a product of at most 7 significant bits and so exact.
 //
 // A wave encodes kPer entries one after another: for each, lane l holds
 // elements 8 l .. 8 l + 7 (one 16-byte load of the bf16 row), so a
@@ -96,11 +106,55 @@ __device__ __forceinline__ void put_main(const u32x4& w, int lane, size_t row,
   if ((lane & 3) == 0) kv_scale[row * (kDim / 32) + (lane >> 2)] = static_cast<uint8_t>(X + 127);
 }
 
+// Encodes one main entry with E4M3 scales per 16 elements (lane l: elements
+// 8 l .. 8 l + 7 in w, half of block l / 2) into row `row`.
+__device__ __forceinline__ void put_main_e4m3(const u32x4& w, int lane, size_t row,
+                                              uint8_t* __restrict__ kv_fp4,
+                                              uint8_t* __restrict__ kv_scale) {
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t u = word_of4(w, k);
+    v[2 * k] = bf16_lo(u);
+    v[2 * k + 1] = bf16_hi(u);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[k]));
+  amax = fmaxf(amax, wave_xor(amax, 1));   // the block's two lanes agree
+  const uint32_t code = e4m3_code(amax / 6.0f);
+  float sv[4];
+  e4m3x4_to_f32(code, sv);
+  const float s = sv[0];
+  // E2M1 midpoints 0.25 .. 5 and whether a tie there rounds up (to the even
+  // code 2, 4 or 6) or down (to 0, 2 or 4).
+  constexpr float kMid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  constexpr bool kTieUp[7] = {false, true, false, true, false, true, false};
+  uint32_t packed = 0u;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float a = fabsf(v[k]);
+    uint32_t mag = 0u;
+#pragma unroll
+    for (int m = 0; m < 7; ++m) {
+      const float t = kMid[m] * s;
+      mag += kTieUp[m] ? (a >= t ? 1u : 0u) : (a > t ? 1u : 0u);
+    }
+    if (code == 0u) mag = 0u;
+    const uint32_t nib = mag | ((v[k] < 0.0f && mag != 0u) ? 8u : 0u);
+    packed |= nib << (4 * k);
+  }
+  __builtin_nontemporal_store(packed,
+                              reinterpret_cast<uint32_t*>(kv_fp4 + row * (kDim / 2) + 4 * lane));
+  if ((lane & 1) == 0) kv_scale[row * (kDim / 16) + (lane >> 1)] = static_cast<uint8_t>(code);
+}
+
 // Wave w of workgroup x takes entries g0 .. g0 + kPer - 1 (g = b n_new + i)
 // with g0 = kPer (kWaves x + w); the main-entry loads of all of them are
 // issued together (rows clamped to the last entry, unused past it).  New
 // entries are read once and the cache rows are not read back here, so both
 // move with non-temporal loads and stores.
+template <int FMT>
 __global__ __launch_bounds__(64 * kWaves) void k_kv_append(
     const uint16_t* __restrict__ kv_new, const uint16_t* __restrict__ swa_new,
     const int32_t* __restrict__ pos, int B, int n_new, int N_cap, uint8_t* __restrict__ kv_fp4,
@@ -137,9 +191,10 @@ __global__ __launch_bounds__(64 * kWaves) void k_kv_append(
   for (int e = 0; e < kPer; ++e) {
     if (g0 + e >= total) break;
     const long long p = static_cast<long long>(pos[bs[e]]) + is[e];
-    if (p >= 0 && p < N_cap)
-      put_main(w[e], lane, static_cast<size_t>(bs[e]) * N_cap + static_cast<size_t>(p), kv_fp4,
-               kv_scale);
+    if (p < 0 || p >= N_cap) continue;
+    const size_t row = static_cast<size_t>(bs[e]) * N_cap + static_cast<size_t>(p);
+    if (FMT == kFmtE8M0) put_main(w[e], lane, row, kv_fp4, kv_scale);
+    else put_main_e4m3(w[e], lane, row, kv_fp4, kv_scale);
   }
   if (swa_new == nullptr) return;
   // Window entries: only the rows inside the window are read.
@@ -169,16 +224,21 @@ __global__ __launch_bounds__(64 * kWaves) void k_kv_append(
 }  // namespace
 
 hipError_t launch_kv_append(const uint16_t* kv_new, const uint16_t* swa_new, const int32_t* pos,
-                            int B, int n_new, int N_cap, uint8_t* kv_fp4, uint8_t* kv_scale,
-                            uint8_t* swa, int S_cap, const int32_t* swa_pos0,
+                            int B, int n_new, int N_cap, int kv_fmt, uint8_t* kv_fp4,
+                            uint8_t* kv_scale, uint8_t* swa, int S_cap, const int32_t* swa_pos0,
                             hipStream_t stream) {
   const long long waves = (static_cast<long long>(B) * n_new + kPer - 1) / kPer;
   const long long wgs = (waves + kWaves - 1) / kWaves;
   if (wgs < 1) return hipSuccess;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(k_kv_append, dim3(static_cast<unsigned>(wgs)), dim3(64 * kWaves), 0, stream,
-                     kv_new, swa_new, pos, B, n_new, N_cap, kv_fp4, kv_scale, swa, S_cap,
-                     swa_pos0);
+  if (kv_fmt == kFmtE8M0)
+    hipLaunchKernelGGL(k_kv_append<kFmtE8M0>, dim3(static_cast<unsigned>(wgs)), dim3(64 * kWaves),
+                       0, stream, kv_new, swa_new, pos, B, n_new, N_cap, kv_fp4, kv_scale, swa,
+                       S_cap, swa_pos0);
+  else
+    hipLaunchKernelGGL(k_kv_append<kFmtE4M3>, dim3(static_cast<unsigned>(wgs)), dim3(64 * kWaves),
+                       0, stream, kv_new, swa_new, pos, B, n_new, N_cap, kv_fp4, kv_scale, swa,
+                       S_cap, swa_pos0);
   return hipGetLastError();
 }
 

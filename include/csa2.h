@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 3
+#define CSA2_ABI_VERSION 4
 
 /* Symbols of the C ABI; everything else in the library is hidden. */
 #define CSA2_API __attribute__((visibility("default")))
@@ -85,12 +85,17 @@ typedef enum {
   CSA2_KDTYPE_FP8_E4M3 = 1   /* 128 x FP8 E4M3FN (OCP) = 128 bytes per entry */
 } csa2_kdtype;
 
-/* Storage format of main-KV entries (512 dims each). */
+/* Storage format of main-KV entries (512 dims each).  Both store E2M1
+   elements two per byte (element 2j in the low nibble of byte j), 256 bytes
+   per entry, and the block scales in a separate array. */
 typedef enum {
-  /* OCP MXFP4: E2M1 elements, two per byte (element 2j in the low nibble of
-     byte j), 256 bytes per entry, plus one E8M0 scale per 32 elements,
-     16 bytes per entry, stored in a separate array. */
-  CSA2_KV_MXFP4_E8M0_32 = 0
+  /* OCP MXFP4: one E8M0 scale per 32 elements, 16 bytes per entry; element
+     i = E2M1 * 2^(scale[i/32] - 127). */
+  CSA2_KV_MXFP4_E8M0_32 = 0,
+  /* One FP8 E4M3FN scale per 16 elements and no global scale
+     ("DeepSeek-V4.1-Flash 架构详解", §4): 32 bytes of scales per entry,
+     288 bytes per entry in all; element i = E2M1 * E4M3FN(scale[i/16]). */
+  CSA2_KV_FP4_E4M3_16 = 1
 } csa2_kvfmt;
 
 /* CSA2 layer modes ("DeepSeek-V4.1-Flash 架构详解", §3 mode table). */
@@ -120,7 +125,8 @@ typedef struct {
   int32_t window;        /* SWA window in tokens, 0..128; default 128 */
   int32_t replay_start;  /* first token a replayed window may see (window
                             [max(s, i-W+1), i]); -1 = no truncation (default) */
-  int32_t kv_fmt;        /* csa2_kvfmt; default CSA2_KV_MXFP4_E8M0_32 */
+  int32_t kv_fmt;        /* csa2_kvfmt of kv_fp4 / kv_scale; default CSA2_KV_MXFP4_E8M0_32;
+                            another value gives CSA2_ERR_UNSUPPORTED */
   uint32_t flags;        /* CSA2_ATTN_* bits; other bits must be 0 */
   const float* sink;     /* with CSA2_ATTN_SINK: [64] fp32 per-head sink logits (device
                             memory), see csa2_sparse_attn_decode; otherwise not read */
@@ -245,9 +251,10 @@ CSA2_API csa2_status csa2_reindex_topk(csa2_mode mode, const float* scores, cons
  *         + { window token p : max(q_pos[r]-W+1, swa_pos0[b], replay_start, 0) <= p <= q_pos[r],
  *                               p - swa_pos0[b] < S_cap }
  *   (no de-duplication between the two parts).  Each entry v is used as key
- *   and value.  Main entries are MXFP4, v[i] = E2M1(nibble i) *
- *   2^(kv_scale[i/32] - 127); window entries are FP8 E4M3FN, slot
- *   p - swa_pos0[b] of swa_kv.  Then
+ *   and value.  Main entries are E2M1 with block scales, v[i] = E2M1(nibble i)
+ *   * 2^(kv_scale[i/32] - 127) (CSA2_KV_MXFP4_E8M0_32, the default) or
+ *   E2M1(nibble i) * E4M3FN(kv_scale[i/16]) (CSA2_KV_FP4_E4M3_16, opts->kv_fmt);
+ *   window entries are FP8 E4M3FN, slot p - swa_pos0[b] of swa_kv.  Then
  *     l_e = sm_scale * q[r][h] . v_e,  out[r][h] = sum_e softmax(l)_e v_e,
  *     lse[r][h] = log sum_e exp(l_e)   (natural log; -inf for an empty set,
  *                                       whose output is 0)
@@ -264,7 +271,7 @@ CSA2_API csa2_status csa2_reindex_topk(csa2_mode mode, const float* scores, cons
  * Arguments
  *   q         [B, n_q, 64, 512] bf16
  *   kv_fp4    [B, N_cap, 256] uint8 packed E2M1
- *   kv_scale  [B, N_cap, 16] uint8 E8M0
+ *   kv_scale  [B, N_cap, 16] uint8 E8M0, or [B, N_cap, 32] uint8 E4M3FN
  *   idx       [B, n_q, top_k] int32 entry indices, -1 = empty slot; top_k 0..512
  *   swa_kv    [B, S_cap, 512] uint8 FP8 E4M3FN; slot i holds token swa_pos0[b] + i
  *   swa_pos0  [B] int32
@@ -299,16 +306,22 @@ CSA2_API csa2_status csa2_reuse_attn(const uint16_t* q, const uint8_t* kv_fp4, c
 /*
  * csa2_kv_append -- encode and store the KV entries of new tokens.
  *   For sequence b and new token i < n_new at position p = pos[b] + i:
- *     main KV    if 0 <= p < N_cap:  kv_fp4[b][p], kv_scale[b][p] <- MXFP4 of kv_new[b][i]
+ *     main KV    if 0 <= p < N_cap:  kv_fp4[b][p], kv_scale[b][p] <- kv_new[b][i]
+ *                encoded in format kv_fmt
  *     window KV  if swa_new != NULL and 0 <= p - swa_pos0[b] < S_cap:
  *                swa_kv[b][p - swa_pos0[b]] <- FP8 E4M3FN of swa_new[b][i]
  *   Positions outside a cache are skipped.  ("DeepSeek-V4.1-Flash 架构详解",
  *   §4: main KV is stored as MXFP4, SWA KV as FP8.)  Encoding (OCP MX v1.0,
  *   OCP FP8):
- *     MXFP4: per 32 elements X = floor(log2(max |v|)) - 2 clamped to
- *       [-127, 127] (-127 for an all-zero block), E8M0 code X + 127; each
- *       v / 2^X rounds to the nearest E2M1 value, ties to the even code,
- *       saturating at 6; a value that rounds to zero is stored as +0.
+ *     MXFP4 (CSA2_KV_MXFP4_E8M0_32): per 32 elements X = floor(log2(max |v|))
+ *       - 2 clamped to [-127, 127] (-127 for an all-zero block), E8M0 code
+ *       X + 127; each v / 2^X rounds to the nearest E2M1 value, ties to the
+ *       even code, saturating at 6; a value that rounds to zero is stored
+ *       as +0.
+ *     CSA2_KV_FP4_E4M3_16: per 16 elements the scale s is max |v| / 6
+ *       rounded to FP8 E4M3FN (rule below); each |v| / s rounds to the
+ *       nearest E2M1 value, ties to the even code, saturating at 6, sign
+ *       kept, zero stored as +0; a block with s = 0 stores +0 everywhere.
  *     FP8: saturate to +-448, round to nearest, ties to even; the sign is
  *       kept for values that round to zero.
  *   Inputs must be finite (a non-finite value leaves its block's or
@@ -318,14 +331,17 @@ CSA2_API csa2_status csa2_reuse_attn(const uint16_t* q, const uint8_t* kv_fp4, c
  *   kv_new    [B, n_new, 512] bf16 main-KV entries
  *   swa_new   [B, n_new, 512] bf16 window entries, or NULL (no window writes)
  *   pos       [B] int32 position of each sequence's first new token
- *   kv_fp4    [B, N_cap, 256] uint8, kv_scale [B, N_cap, 16] uint8 (written)
+ *   kv_fmt    csa2_kvfmt of the main cache (else CSA2_ERR_UNSUPPORTED)
+ *   kv_fp4    [B, N_cap, 256] uint8, kv_scale [B, N_cap, 16] (E8M0) or
+ *             [B, N_cap, 32] (E4M3FN) uint8 (written)
  *   swa_kv    [B, S_cap, 512] uint8 (written; may be NULL when swa_new is)
  *   swa_pos0  [B] int32 (may be NULL when swa_new is)
  */
 CSA2_API csa2_status csa2_kv_append(const uint16_t* kv_new, const uint16_t* swa_new,
                            const int32_t* pos, int32_t B, int32_t n_new, int32_t N_cap,
-                           uint8_t* kv_fp4, uint8_t* kv_scale, uint8_t* swa_kv, int32_t S_cap,
-                           const int32_t* swa_pos0, hipStream_t stream);
+                           int32_t kv_fmt, uint8_t* kv_fp4, uint8_t* kv_scale,
+                           uint8_t* swa_kv, int32_t S_cap, const int32_t* swa_pos0,
+                           hipStream_t stream);
 
 /* Workspace bytes an operation needs for the given sizes (0 if none);
    returns (size_t)-1 for an unknown op or invalid sizes. */

@@ -115,14 +115,16 @@ class Gen:
         return torch.randperm(n, generator=self.g, device=self.device)
 
 
-def _normal_mxfp4(gen, b, n, chunk=1 << 18):
-    """Main KV [b, n, 512] ~ N(0,1) stored as MXFP4, drawn in row chunks."""
+def _normal_mxfp4(gen, b, n, chunk=1 << 18, kv_fmt="e8m0_32"):
+    """Main KV [b, n, 512] ~ N(0,1) stored as E2M1 with E8M0 scales per 32
+    ("e8m0_32") or E4M3 scales per 16 ("e4m3_16"), drawn in row chunks."""
+    enc, per = {"e8m0_32": (to_mxfp4, 32), "e4m3_16": (to_fp4_e4m3, 16)}[kv_fmt]
     fp4 = torch.empty(b, n, DIM // 2, dtype=torch.uint8, device=gen.device)
-    sc = torch.empty(b, n, DIM // 32, dtype=torch.uint8, device=gen.device)
+    sc = torch.empty(b, n, DIM // per, dtype=torch.uint8, device=gen.device)
     for bi in range(b):
         for lo in range(0, n, chunk):
             hi = min(n, lo + chunk)
-            p, s = to_mxfp4(gen.normal(hi - lo, DIM))
+            p, s = enc(gen.normal(hi - lo, DIM))
             fp4[bi, lo:hi] = p
             sc[bi, lo:hi] = s
     return fp4, sc
@@ -163,14 +165,15 @@ def swa_kv(gen, b, s):
 
 
 def decode_workload(B, T, kdtype="fp8", seed=0, device="cpu", heavy_frac=0.0,
-                    lognormal_sigma=None, reindex=False, supplied_idx=False):
-    """Decode step inputs: one query token per sequence at position T-1.
+                    lognormal_sigma=None, reindex=False, supplied_idx=False, kv_fmt="e8m0_32"):
+    """Decode step inputs: one query token per sequence at position T-1;
+    main KV in scale format kv_fmt ("e8m0_32" or "e4m3_16").
 
     Full (and optional Reindex) layers share indexer K and main KV; each layer
     has its own indexer query, attention query and SWA KV.
     """
     gen = Gen(seed, device)
-    d = {"B": B, "T": T, "n_q": 1, "kdtype": kdtype, "sm_scale": SM_SCALE}
+    d = {"B": B, "T": T, "n_q": 1, "kdtype": kdtype, "sm_scale": SM_SCALE, "kv_fmt": kv_fmt}
     if not supplied_idx:
         d["q_idx"], d["w_idx"] = indexer_query(gen, B)
         heavy = int(round(heavy_frac * T)) if heavy_frac else 0
@@ -179,7 +182,7 @@ def decode_workload(B, T, kdtype="fp8", seed=0, device="cpu", heavy_frac=0.0,
         if reindex:
             d["q_idx2"], d["w_idx2"] = indexer_query(gen, B)
     d["q"] = attn_query(gen, B)
-    d["kv_fp4"], d["kv_scale"] = _normal_mxfp4(gen, B, T)
+    d["kv_fp4"], d["kv_scale"] = _normal_mxfp4(gen, B, T, kv_fmt=kv_fmt)
     s = min(WINDOW, T)
     d["swa"] = swa_kv(gen, B, s)
     if reindex:
@@ -195,7 +198,8 @@ def decode_workload(B, T, kdtype="fp8", seed=0, device="cpu", heavy_frac=0.0,
     return d
 
 
-def prefill_workload(n_q=4096, prefix_tokens=131072, seed=4, device="cpu", kdtype="bf16"):
+def prefill_workload(n_q=4096, prefix_tokens=131072, seed=4, device="cpu", kdtype="bf16",
+                     kv_fmt="e8m0_32"):
     """Encoder prefill chunk (m=2): n_q new tokens after a prefix of prefix_tokens.
 
     Entries: prefix_tokens/2 prefix entries plus n_q/2 chunk entries; token p
@@ -204,11 +208,12 @@ def prefill_workload(n_q=4096, prefix_tokens=131072, seed=4, device="cpu", kdtyp
     """
     gen = Gen(seed, device)
     n_ent = prefix_tokens // 2 + n_q // 2
-    d = {"B": 1, "n_q": n_q, "T": n_ent, "kdtype": kdtype, "sm_scale": SM_SCALE}
+    d = {"B": 1, "n_q": n_q, "T": n_ent, "kdtype": kdtype, "sm_scale": SM_SCALE,
+         "kv_fmt": kv_fmt}
     d["q_idx"], d["w_idx"] = indexer_query(gen, 1, n_q)
     d["k_idx"] = _index_keys(gen, 1, n_ent, kdtype)
     d["q"] = attn_query(gen, 1, n_q)
-    d["kv_fp4"], d["kv_scale"] = _normal_mxfp4(gen, 1, n_ent)
+    d["kv_fp4"], d["kv_scale"] = _normal_mxfp4(gen, 1, n_ent, kv_fmt=kv_fmt)
     swa_lo = prefix_tokens - WINDOW + 1
     s = prefix_tokens + n_q - swa_lo
     d["swa"] = swa_kv(gen, 1, s)
@@ -219,20 +224,21 @@ def prefill_workload(n_q=4096, prefix_tokens=131072, seed=4, device="cpu", kdtyp
     return d
 
 
-# The five workloads, by name: (builder, kwargs).
-def kv_append_workload(B, n_new, seed=0, device="cpu"):
+# The workloads, by name: (builder, kwargs).
+def kv_append_workload(B, n_new, seed=0, device="cpu", kv_fmt="e8m0_32"):
     """KV append inputs: n_new new tokens per sequence at positions 0 ..
     n_new - 1 (bf16 entries ~N(0,1)), empty caches of n_new main entries and
     a window of the last 128 tokens."""
     gen = Gen(seed, device)
     s = min(WINDOW, n_new)
-    d = {"B": B, "n_q": 1, "n_new": n_new}
+    d = {"B": B, "n_q": 1, "n_new": n_new, "kv_fmt": kv_fmt}
     d["kv_new"] = to_bf16_bits(gen.normal(B, n_new, DIM))
     d["swa_new"] = to_bf16_bits(gen.normal(B, n_new, DIM))
     d["pos"] = torch.zeros(B, dtype=torch.int32, device=gen.device)
     d["swa_pos0"] = torch.full((B,), n_new - s, dtype=torch.int32, device=gen.device)
     d["kv_fp4"] = torch.zeros(B, n_new, DIM // 2, dtype=torch.uint8, device=gen.device)
-    d["kv_scale"] = torch.zeros(B, n_new, DIM // 32, dtype=torch.uint8, device=gen.device)
+    per = {"e8m0_32": 32, "e4m3_16": 16}[kv_fmt]
+    d["kv_scale"] = torch.zeros(B, n_new, DIM // per, dtype=torch.uint8, device=gen.device)
     d["swa"] = torch.zeros(B, s, DIM, dtype=torch.uint8, device=gen.device)
     return d
 
@@ -241,6 +247,8 @@ WORKLOADS = {
     "tiny_2k": (decode_workload, dict(B=1, T=2048, kdtype="bf16", seed=0)),
     "full_64k": (decode_workload, dict(B=4, T=65536, kdtype="fp8", seed=1, heavy_frac=0.01)),
     "reuse_128k": (decode_workload, dict(B=64, T=131072, seed=2, supplied_idx=True)),
+    "reuse_128k_e4m3": (decode_workload, dict(B=64, T=131072, seed=2, supplied_idx=True,
+                                              kv_fmt="e4m3_16")),
     "full_reindex_1m": (decode_workload, dict(B=8, T=1048576, kdtype="fp8", seed=3,
                                               lognormal_sigma=0.5, reindex=True)),
     "prefill_128k": (prefill_workload, dict(n_q=4096, prefix_tokens=131072, seed=4)),

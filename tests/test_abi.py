@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.csa2_abi_version() == 3
+    assert L.csa2_abi_version() == 4
     for st in range(7):
         assert len(L.csa2_status_string(st)) > 0
     assert L.csa2_status_string(0) == b"ok"
@@ -132,8 +132,10 @@ def test_attention_validation(L):
         assert _attn(L, fn, scale=0.0) == 2
         assert _attn(L, fn, scale=-0.04) == 2
         assert _attn(L, fn, scale=float("inf")) == 2
-        bad_fmt = csa.AttnOpts(128, -1, 1, 0)
+        bad_fmt = csa.AttnOpts(128, -1, 2, 0)
         assert _attn(L, fn, opts=ctypes.byref(bad_fmt)) == 3
+        e4m3 = csa.AttnOpts(128, -1, csa.KV_FP4_E4M3_16, 0)   # accepted up to the alignment check
+        assert _attn(L, fn, opts=ctypes.byref(e4m3), out=MIS) == 5
         bad_win = csa.AttnOpts(129, -1, 0, 0)
         assert _attn(L, fn, opts=ctypes.byref(bad_win)) == 2
         bad_sink = csa.AttnOpts(128, -1, 0, csa.ATTN_SINK, MIS)
@@ -163,9 +165,12 @@ def test_binding_refuses_cpu_tensors(L):
 
 def test_kv_append_validation(L):
     f = L.csa2_kv_append
-    def call(kv=A, swn=None, pos=A, B=1, n=1, N=64, fp4=A, sc=A, swa=None, S=0, p0=None):
-        return f(kv, swn, pos, B, n, N, fp4, sc, swa, S, p0, None)
+    def call(kv=A, swn=None, pos=A, B=1, n=1, N=64, fmt=0, fp4=A, sc=A, swa=None, S=0, p0=None):
+        return f(kv, swn, pos, B, n, N, fmt, fp4, sc, swa, S, p0, None)
     assert call(kv=None) == 1
+    assert call(fmt=2) == 3
+    assert call(fmt=-1) == 3
+    assert call(fmt=1, kv=MIS) == 5             # the E4M3 format passes up to the alignment check
     assert call(sc=None) == 1
     assert call(swn=A) == 1                     # window entries without a window cache
     assert call(swn=A, swa=A) == 1              # ... or without swa_pos0

@@ -292,6 +292,7 @@ def test_reindex_layer():
 
 # --------------------------------------------------------------------------- attention
 def _attn_gpu(d, idx, q=None, swa=None, window=128, replay_start=-1, reuse=False, sink=None):
+    kv_fmt = csa.KV_FP4_E4M3_16 if d.get("kv_fmt") == "e4m3_16" else csa.KV_MXFP4_E8M0_32
     q = d["q"] if q is None else q
     swa = d["swa"] if swa is None else swa
     B, n_q = q.shape[0], q.shape[1]
@@ -300,7 +301,7 @@ def _attn_gpu(d, idx, q=None, swa=None, window=128, replay_start=-1, reuse=False
     fn = csa.reuse_attn if reuse else csa.sparse_attn_decode
     fn(q.cuda(), d["kv_fp4"].cuda(), d["kv_scale"].cuda(), idx.cuda(), swa.cuda(),
        d["swa_pos0"].cuda(), d["q_pos"].cuda(), d["sm_scale"], out, lse=lse, window=window,
-       replay_start=replay_start, sink=None if sink is None else sink.cuda())
+       replay_start=replay_start, sink=None if sink is None else sink.cuda(), kv_fmt=kv_fmt)
     torch.cuda.synchronize()
     return u16(out), _np(lse)
 
@@ -314,7 +315,7 @@ def _attn_ref(d, b, j, idx_row, q=None, swa=None, window=128, replay_start=-1, s
     sc = _np(d["kv_scale"][b][torch.as_tensor(sel, dtype=torch.long, device=d["kv_scale"].device)])
     return pipeline.attention(u16(q[b, j]), fp4, sc, np.arange(len(sel)), _np(swa[b]),
                               int(d["swa_pos0"][b]), int(d["q_pos"][b, j]), d["sm_scale"],
-                              window, replay_start, sink)
+                              window, replay_start, sink, kv_fmt=d.get("kv_fmt", "e8m0_32"))
 
 
 @pytest.mark.parametrize("case", ["topk512", "ragged", "invalid", "dense", "window16", "replay",
@@ -411,6 +412,104 @@ def test_attention_extreme_scale_codes():
         g0 = out[b, 0][:, :32]
         big = np.abs(o[:, :32]) > 2 * 2.0 ** -133
         assert big.any() and np.all(g0[big] & 0x7FFF != 0)
+
+
+# E4M3FN scale codes of the per-16 format, one per block index (dims 16 i
+# .. 16 i + 15): the smallest subnormals and the subnormal/normal boundary
+# (blocks 0, 1, 2, 8), scales with every mantissa bit set or clear, the
+# largest value 448 (block 7) and 26 (block 14), negative codes (the
+# dequantised values change sign) and 0 (a block of zeros, block 11).
+_E4M3_CODES = np.array([0x01, 0x07, 0x08, 0x30, 0x38, 0x39, 0x3F, 0x7E,
+                        0x81, 0xB8, 0xB0, 0x00, 0x3A, 0x40, 0x5D, 0x3F] * 2, np.uint8)
+_E4M3_TINY = [0, 1, 2, 8]
+_E4M3_BIG = [7, 14]
+
+
+@pytest.mark.parametrize("case", ["recipe", "codes"])
+@pytest.mark.parametrize("n_q", [1, 16])
+def test_attention_e4m3_scales(case, n_q):
+    # The per-16 E4M3 scale format through both attention kernels (decode
+    # rows, n_q = 1, and prefill-shaped rows, n_q = 16).  "recipe": N(0,1)
+    # entries encoded as in the workloads.  "codes": the same nibbles with
+    # every entry's scales replaced by _E4M3_CODES.  There the query is zero
+    # on the dims of the two big blocks and scaled by 1/4 elsewhere, so the
+    # logits stay O(1) and the softmax spreads over many entries (P is
+    # rounded to bf16 before P.V, an error of up to 2^-9 of each entry's
+    # share, which a softmax peaked on a few entries of values up to 12 would
+    # show above the O(1) tolerance); the window (FP8, O(1)) is zero on the
+    # dims of the tiny blocks; each output
+    # dim is compared in units of its block's |scale| (at least 1 where the
+    # window contributes), so that the tiny blocks are checked at their own
+    # resolution and the big ones are not held to an O(1) absolute bound.
+    T, B = 1500, 2
+    d = synth.decode_workload(B=B, T=T, kdtype="bf16", seed=91, kv_fmt="e4m3_16")
+    assert d["kv_scale"].shape == (B, T, 32)
+    rng = np.random.default_rng(91)
+    g = torch.Generator().manual_seed(92)
+    q = torch.randn(B, n_q, 64, 512, generator=g)
+    dim_scale = None
+    if case == "codes":
+        d["kv_scale"] = torch.from_numpy(
+            np.ascontiguousarray(np.broadcast_to(_E4M3_CODES, (B, T, 32))))
+        unit = np.abs(formats.e4m3_to_f64(_E4M3_CODES))
+        unit[11] = unit[27] = 1.0
+        q *= 0.25
+        for blk in _E4M3_BIG:
+            for k in (blk, blk + 16):
+                q[..., 16 * k:16 * k + 16] = 0
+        d["swa"] = d["swa"].clone()
+        for blk in _E4M3_TINY:
+            for k in (blk, blk + 16):
+                d["swa"][..., 16 * k:16 * k + 16] = 0
+        tiny = np.zeros(32, bool)
+        tiny[_E4M3_TINY] = tiny[[k + 16 for k in _E4M3_TINY]] = True
+        unit = np.where(tiny, unit, np.maximum(unit, 1.0))
+        dim_scale = np.repeat(unit, 16)
+    d["q"] = synth.to_bf16_bits(q)
+    d["q_pos"] = torch.full((B, n_q), T - 1, dtype=torch.int32)
+    top_k = 300
+    idx = np.stack([np.stack([np.sort(rng.choice(T, size=top_k, replace=False))
+                              for _ in range(n_q)]) for _ in range(B)])
+    idx[0, 0, ::7] = -1
+    print(f"attention E4M3 scales case={case} n_q={n_q}", flush=True)
+    out, lse = _attn_gpu(d, torch.from_numpy(idx.astype(np.int32)))
+    for b in range(B):
+        for j in sorted({0, n_q - 1}):
+            o, l = _attn_ref(d, b, j, idx[b, j])
+            if case == "codes":
+                assert np.abs(o[:, 112:128]).max() > 100.0     # the 448 block is in the output
+            check_attention(out[b, j], lse[b, j], o, l, what=f"E4M3 {case} row {b},{j}",
+                            dim_scale=dim_scale)
+
+
+@pytest.mark.parametrize("n_q", [1, 16])
+def test_attention_single_entry_is_its_dequantisation(n_q):
+    # Zero query, one selected entry and no window: every logit is 0, the
+    # softmax weight is exactly 1, and each head's output is the entry
+    # itself, dequantised: bit-exact in bf16 for both scale formats and both
+    # kernels, over E8M0 codes whose values stay normal in fp32 and finite in
+    # bf16 (3 .. 252) and the special E4M3 codes (subnormal, negative, zero,
+    # 448).
+    T, B = 64, 4
+    for fmt, codes, dec in (("e8m0_32", np.array([3, 64, 100, 126, 127, 130, 200, 252] * 2, np.uint8),
+                             formats.mxfp4_to_f64),
+                            ("e4m3_16", _E4M3_CODES, formats.fp4e4_to_f64)):
+        d = synth.decode_workload(B=B, T=T, kdtype="bf16", seed=93, kv_fmt=fmt)
+        d["kv_scale"] = torch.from_numpy(
+            np.ascontiguousarray(np.broadcast_to(codes, d["kv_scale"].shape)))
+        d["q"] = torch.zeros(B, n_q, 64, 512, dtype=torch.int16)
+        d["q_pos"] = torch.full((B, n_q), T - 1, dtype=torch.int32)
+        idx = (np.arange(B * n_q).reshape(B, n_q, 1) * 3 % T).astype(np.int32)
+        print(f"attention single entry {fmt} n_q={n_q}", flush=True)
+        out, lse = _attn_gpu(d, torch.from_numpy(idx), window=0)
+        got = (out.astype(np.uint32) << 16).view(np.float32)
+        for b in range(B):
+            for j in range(n_q):
+                e = idx[b, j, 0]
+                want = dec(_np(d["kv_fp4"][b, e])[None], _np(d["kv_scale"][b, e])[None])[0]
+                assert np.array_equal(got[b, j], np.broadcast_to(want, (64, 512))), \
+                    f"{fmt} row {b},{j}: the output is not entry {e}"
+                assert np.all(lse[b, j] == 0.0)
 
 
 def test_attention_single_split_and_reuse_identical():
@@ -576,6 +675,59 @@ def test_kv_append_without_window():
     torch.cuda.synchronize()
     want = pipeline.kv_append(fp4, sc, None, kv_bits.numpy().view(np.uint16), None, pos, None)
     assert np.array_equal(_np(g[0]), want[0]) and np.array_equal(_np(g[1]), want[1])
+
+
+def _e4m3_append_inputs(rng, B, n_new):
+    """bf16 entries for the per-16 E4M3 encoder, per-block magnitudes 2^-14
+    .. 2^14, with its edge cases in sequence 0: blocks whose amax / 6 is an
+    E4M3 midpoint (a tie, to the even code), a block whose elements sit on
+    the E2M1 midpoints times its scale (ties, to the even code), an all-zero
+    block, a block whose scale rounds to 0, one whose scale saturates at
+    448, one with subnormal scales, and negative zeros."""
+    kv = rng.standard_normal((B, n_new, 32, 16)) * np.exp2(rng.integers(-14, 14, size=(B, n_new, 32, 1)))
+    kv = kv.reshape(B, n_new, 512)
+    e4 = formats.e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+    mids = (e4[:-1] + e4[1:]) / 2
+    # amax = 6 x midpoint, exact in bf16 (a midpoint has at most 5
+    # significant bits): block 0 of entries (0, i).
+    for i in range(min(n_new, 3)):
+        m = mids[[40, 41, 77][i]]
+        kv[0, i, 0:16] = rng.uniform(-1, 1, 16) * m * 6
+        kv[0, i, 3] = 6 * m
+    # A block with amax 6 s, s = 1.25, and elements on the E2M1 midpoints times s.
+    kv[0, 0, 16:32] = np.array([6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0,
+                                -0.25, -0.75, -1.25, -1.75, -2.5, -3.5, -5.0, -6]) * 1.25
+    kv[0, 0, 32:48] = 0.0
+    kv[0, 0, 48:64] = rng.standard_normal(16) * 2.0 ** -14     # amax / 6 below 2^-10: scale 0
+    kv[0, 0, 64:80] = rng.standard_normal(16) * 1e5             # scale saturates at 448
+    kv[0, 0, 80:96] = rng.standard_normal(16) * 2.0 ** -8       # subnormal scales
+    kv[0, 0, 96:112] = -0.0
+    return torch.from_numpy(kv.astype(np.float32)).to(torch.bfloat16).view(torch.int16)
+
+
+def test_kv_append_e4m3_exact():
+    rng = np.random.default_rng(53)
+    B, n_new, N_cap, S_cap = 4, 5, 24, 8
+    kv_bits = _e4m3_append_inputs(rng, B, n_new)
+    _, sw_bits = _append_inputs(rng, B, n_new)
+    pos = np.array([0, 19, -2, 7], np.int32)
+    swa_pos0 = np.array([0, 15, 0, 3], np.int32)
+    fp4 = np.full((B, N_cap, 256), 0x5A, np.uint8)
+    sc = np.full((B, N_cap, 32), 0x5A, np.uint8)
+    swa = np.full((B, S_cap, 512), 0x5A, np.uint8)
+    g = [torch.from_numpy(a.copy()).cuda() for a in (fp4, sc, swa)]
+    print("kv_append E4M3 scales", flush=True)
+    csa.kv_append(kv_bits.cuda(), torch.from_numpy(pos).cuda(), g[0], g[1],
+                  swa_new=sw_bits.cuda(), swa_kv=g[2], swa_pos0=torch.from_numpy(swa_pos0).cuda(),
+                  kv_fmt=csa.KV_FP4_E4M3_16)
+    torch.cuda.synchronize()
+    want = pipeline.kv_append(fp4, sc, swa, kv_bits.numpy().view(np.uint16),
+                              sw_bits.numpy().view(np.uint16), pos, swa_pos0, kv_fmt="e4m3_16")
+    # The planted cases are present: a tie of amax / 6, scale code 0, 0x7E.
+    codes = want[1][0, 0]
+    assert 0x00 in codes and 0x7E in codes
+    for name, got, ref in zip(("kv_fp4", "kv_scale", "swa"), g, want):
+        assert np.array_equal(_np(got), ref), f"{name} differs from the oracle"
 
 
 def test_multi_query_decode_rows():

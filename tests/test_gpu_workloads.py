@@ -1,4 +1,4 @@
-"""Parity at the full sizes of the five workloads, in the launch configuration
+"""Parity at the full sizes of the workloads, in the launch configuration
 the benchmark times, on query rows the oracle computes one by one.
 
 Inputs are generated on the GPU by the seeded synthetic generator; the oracle
@@ -41,7 +41,8 @@ def _attn_ref(d, b, j, idx_row, q, swa):
     sel = torch.as_tensor(idx_row[idx_row >= 0], device="cuda")
     return pipeline.attention(u16(q[b, j]), _np(d["kv_fp4"][b][sel]), _np(d["kv_scale"][b][sel]),
                               np.arange(len(sel)), _np(swa[b]), int(d["swa_pos0"][b]),
-                              int(d["q_pos"][b, j]), d["sm_scale"])
+                              int(d["q_pos"][b, j]), d["sm_scale"],
+                              kv_fmt=d.get("kv_fmt", "e8m0_32"))
 
 
 def _attention(d, q, swa, idx, reuse=False):
@@ -49,8 +50,9 @@ def _attention(d, q, swa, idx, reuse=False):
     out = torch.empty(B, n_q, 64, 512, dtype=torch.int16, device="cuda")
     lse = torch.empty(B, n_q, 64, device="cuda")
     fn = csa.reuse_attn if reuse else csa.sparse_attn_decode
+    kv_fmt = csa.KV_FP4_E4M3_16 if d.get("kv_fmt") == "e4m3_16" else csa.KV_MXFP4_E8M0_32
     fn(q, d["kv_fp4"], d["kv_scale"], idx, swa, d["swa_pos0"], d["q_pos"], d["sm_scale"], out,
-       lse=lse)
+       lse=lse, kv_fmt=kv_fmt)
     return out, lse
 
 
@@ -104,14 +106,15 @@ def test_full_64k():
         _check_full(d, b, pool, idx, out, lse)
 
 
-def test_reuse_128k():
-    d = synth.make("reuse_128k", device="cuda")
-    print("workload reuse_128k", flush=True)
+@pytest.mark.parametrize("name", ["reuse_128k", "reuse_128k_e4m3"])
+def test_reuse_128k(name):
+    d = synth.make(name, device="cuda")
+    print(f"workload {name}", flush=True)
     out, lse = _attention(d, d["q"], d["swa"], d["idx"], reuse=True)
     torch.cuda.synchronize()
     for b in (0, 21, 42, 63):
         o, l = _attn_ref(d, b, 0, _np(d["idx"][b, 0]), d["q"], d["swa"])
-        check_attention(u16(out[b, 0]), _np(lse[b, 0]), o, l, what=f"reuse row {b}")
+        check_attention(u16(out[b, 0]), _np(lse[b, 0]), o, l, what=f"{name} row {b}")
 
 
 def test_full_reindex_1m():
@@ -159,14 +162,16 @@ def test_prefill_128k():
         check_attention(u16(out[0, j]), _np(lse[0, j]), o, l, what=f"prefill attention row {j}")
 
 
-def test_kv_append_64k():
+@pytest.mark.parametrize("kv_fmt", ["e8m0_32", "e4m3_16"])
+def test_kv_append_64k(kv_fmt):
     # The benchmark's append (4 x 65,536 tokens, window of the last 128), run
     # once on the device; sampled main rows and every window row are checked
     # against the oracle's encoding (placement is covered at small size).
-    d = synth.make("kv_append_64k", device="cuda")
-    print("kv_append_64k", flush=True)
+    d = synth.make("kv_append_64k", device="cuda", kv_fmt=kv_fmt)
+    print(f"kv_append_64k {kv_fmt}", flush=True)
+    fmt = csa.KV_FP4_E4M3_16 if kv_fmt == "e4m3_16" else csa.KV_MXFP4_E8M0_32
     csa.kv_append(d["kv_new"], d["pos"], d["kv_fp4"], d["kv_scale"], swa_new=d["swa_new"],
-                  swa_kv=d["swa"], swa_pos0=d["swa_pos0"])
+                  swa_kv=d["swa"], swa_pos0=d["swa_pos0"], kv_fmt=fmt)
     torch.cuda.synchronize()
     rng = np.random.default_rng(53)
     n_new, s_cap = d["n_new"], d["swa"].shape[1]
@@ -174,7 +179,7 @@ def test_kv_append_64k():
         rows = torch.from_numpy(
             np.unique(np.concatenate([rng.integers(0, n_new, 96), [0, n_new - 1]]))).cuda()
         kv = formats.bf16_to_f64(_np(d["kv_new"][b][rows]).view(np.uint16))
-        fp4, sc = formats.f64_to_mxfp4(kv)
+        fp4, sc = (formats.f64_to_fp4e4 if kv_fmt == "e4m3_16" else formats.f64_to_mxfp4)(kv)
         assert np.array_equal(_np(d["kv_fp4"][b][rows]), fp4)
         assert np.array_equal(_np(d["kv_scale"][b][rows]), sc)
         sw = formats.bf16_to_f64(_np(d["swa_new"][b, n_new - s_cap:]).view(np.uint16))
