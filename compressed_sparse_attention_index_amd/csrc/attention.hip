@@ -65,6 +65,18 @@ constexpr int kRowBytes = kHalfDims * 2 + 32;
 constexpr int kTileBytes = kTile * kRowBytes;
 static_assert(kMaxWindow == kTile * 4, "one window tile per pair");
 constexpr int kDimTiles = kHalfDims / 16;    // 16-dim tiles of O^T per wave
+// Staging in a wave's own tile region before its first dequantised store:
+// the q rows of the workgroup's 16 heads over the wave's dims half (16 x
+// 512 bytes, row stride kQStride) and the raw FP8 bytes of its window
+// tile's 32 rows over the same half (32 x 256 bytes, stride kWStride, from
+// byte kWinStage).  Each load instruction then covers whole 128-byte lines
+// (instead of one 16-byte piece of 64 different lines), and the operands
+// are read back from LDS in the MFMA layouts; with these strides the 16
+// rows one read touches fall in distinct banks.
+constexpr int kQStride = 528;
+constexpr int kWStride = 272;
+constexpr int kWinStage = 16 * kQStride;
+static_assert(kWinStage + kTile * kWStride <= kTileBytes, "staging fits the tile");
 constexpr int kSteps = kHalfDims / 32;       // contraction steps of the partial S
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -158,16 +170,14 @@ __device__ __forceinline__ float head_sum(float v) {
 // and so entry 0 of the sequence), so that the compiler can count the loads
 // still in flight on every path and wait only for the ones it needs.
 template <int FMT>
-__device__ __forceinline__ void gather_main(const AttnArgs& a, const Ctx& x, const int32_t* ids,
-                                            int t, MainRaw& w) {
+__device__ __forceinline__ void gather_rows(const AttnArgs& a, const Ctx& x, const int (&id)[2],
+                                            MainRaw& w) {
   constexpr int kSc = KvFmt<FMT>::kScaleBytes;
-  t = min(t, kMaxTopK / kTile - 1);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int id = ids[kTile * t + 16 * h + x.m];
-    const bool valid = id >= 0;
+    const bool valid = id[h] >= 0;
     w.valid[h] = valid;
-    const size_t er = static_cast<size_t>(x.b) * a.N_cap + (valid ? id : 0);
+    const size_t er = static_cast<size_t>(x.b) * a.N_cap + (valid ? id[h] : 0);
     const uint8_t* src = a.kv_fp4 + er * 256 + 128 * x.d + 32 * x.c;
     w.f[h][0] = *reinterpret_cast<const u32x4*>(src);
     w.f[h][1] = *reinterpret_cast<const u32x4*>(src + 16);
@@ -175,23 +185,64 @@ __device__ __forceinline__ void gather_main(const AttnArgs& a, const Ctx& x, con
     w.sc[h] = *reinterpret_cast<const uint32_t*>(a.kv_scale + er * kSc + sc_off);
   }
 }
+template <int FMT>
+__device__ __forceinline__ void gather_main(const AttnArgs& a, const Ctx& x, const int32_t* ids,
+                                            int t, MainRaw& w) {
+  t = min(t, kMaxTopK / kTile - 1);
+  const int id[2] = {ids[kTile * t + x.m], ids[kTile * t + 16 + x.m]};
+  gather_rows<FMT>(a, x, id, w);
+}
 
-// Issues the loads of window tile u (positions q_pos - 127 + 32 u ..) into w.
-__device__ __forceinline__ void gather_window(const AttnArgs& a, const Ctx& x, int u, WinRaw& w) {
+// Id of selected slot `slot` of row r read from global memory (-1: no entry).
+__device__ __forceinline__ int slot_id(const AttnArgs& a, int r, int slot) {
+  const int v = slot < a.top_k ? a.idx[static_cast<size_t>(r) * a.top_k + slot] : -1;
+  return (v >= 0 && v < a.N_cap) ? v : -1;
+}
+
+// Window tile u (positions q_pos - 127 + 32 u .. + 31), dims half d: the
+// validity of the lane's two slots (entries 16 h + m), and the loads of
+// the 32 rows, lane l of load j taking row 4 j + l / 16, bytes 16 (l % 16)
+// .. + 16 of the half.  An empty row reads the query row, which always
+// exists.
+struct WinLoad {
+  u32x4 raw[8];
+};
+__device__ __forceinline__ int window_pos(const Ctx& x, int u, int j) {
+  return x.qpos - (kMaxWindow - 1) + kTile * u + j;
+}
+__device__ __forceinline__ bool window_valid(const AttnArgs& a, const Ctx& x, int p) {
+  return p >= x.lo && p <= x.qpos && p - x.p0 < a.S_cap;
+}
+__device__ __forceinline__ void load_window(const AttnArgs& a, const Ctx& x, int u, WinLoad& l,
+                                            WinRaw& w) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int j = kTile * u + 16 * h + x.m;
-    const int p = x.qpos - (kMaxWindow - 1) + j;
-    const bool valid = p >= x.lo && p <= x.qpos && p - x.p0 < a.S_cap;
-    w.valid[h] = valid;
-    // An empty slot reads the query row, which always exists.
-    const uint8_t* row =
-        valid ? a.swa + (static_cast<size_t>(x.b) * a.S_cap + (p - x.p0)) * 512
-              : reinterpret_cast<const uint8_t*>(a.q + static_cast<size_t>(x.r) * kHeads * kDim);
-    const uint8_t* src = row + 256 * x.d + 64 * x.c;
+  for (int h = 0; h < 2; ++h) w.valid[h] = window_valid(a, x, window_pos(x, u, 16 * h + x.m));
+  const uint8_t* qrow =
+      reinterpret_cast<const uint8_t*>(a.q + static_cast<size_t>(x.r) * kHeads * kDim);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) w.v[h][k] = *reinterpret_cast<const u32x4*>(src + 16 * k);
+  for (int j = 0; j < 8; ++j) {
+    const int p = window_pos(x, u, 4 * j + (x.lane >> 4));
+    const uint8_t* row = window_valid(a, x, p)
+                             ? a.swa + (static_cast<size_t>(x.b) * a.S_cap + (p - x.p0)) * 512
+                             : qrow;
+    l.raw[j] = *reinterpret_cast<const u32x4*>(row + 256 * x.d + 16 * (x.lane & 15));
   }
+}
+// Through the staging area into the operand layout: v[h][0..3] = bytes
+// 64 c .. + 64 of row 16 h + m.
+__device__ __forceinline__ void stage_window(const Ctx& x, const WinLoad& l, uint8_t* tile,
+                                             WinRaw& w) {
+  uint8_t* st = tile + kWinStage;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    *reinterpret_cast<u32x4*>(st + (4 * j + (x.lane >> 4)) * kWStride + 16 * (x.lane & 15)) =
+        l.raw[j];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w.v[h][k] = *reinterpret_cast<const u32x4*>(st + (16 * h + x.m) * kWStride + 64 * x.c +
+                                                  16 * k);
 }
 
 // Dequantisation, LDS store and the partial S^T = K . q^T of one tile.
@@ -218,15 +269,13 @@ __device__ __forceinline__ void qk_tile(const Ctx& x, const R& w, const State& s
       const uint32_t two = w.sc[h] >> (16 * (x.c & 1));
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        // E8M0 -> 2^(code - 127): code 0 is the subnormal 2^-127, code 255
-        // NaN.  An empty slot gets the bits 0, read as 2^-127 by the
-        // conversion: finite values, which the softmax masks by the slot's
-        // validity.  Selects only, no branches.
+        // The conversion reads only the exponent field of its scale
+        // operand, as an E8M0 code: the code shifted into that field is the
+        // scale 2^(code - 127) for every code (0: 2^-127, 255: NaN).  An
+        // empty slot gets the bits 0 (2^-127): finite values, which the
+        // softmax masks by the slot's validity.
         const uint32_t code = (two >> (8 * k)) & 0xffu;
-        uint32_t bits = code << 23;
-        bits = code == 0 ? 0x00400000u : bits;
-        bits = code == 255 ? 0x7fc00000u : bits;
-        scale[h][k] = __uint_as_float(w.valid[h] ? bits : 0u);
+        scale[h][k] = __uint_as_float(w.valid[h] ? code << 23 : 0u);
       }
     }
   }
@@ -280,19 +329,24 @@ __device__ __forceinline__ void softmax_pv(const AttnArgs& a, const Ctx& x, uint
                                            const f32x4_t (&s0)[2], const f32x4_t (&s1)[2],
                                            State& st) {
   // Validity of entry 16 h + e is bit e of vm_h; lane (m, c) holds entries
-  // 16 h + 4 c + i.
+  // 16 h + 4 c + i.  The partner's partial is added in the same order in
+  // both waves.  Logits are scaled into log2 units after the maximum (a
+  // positive scale commutes with it) and inside the exponent's fma.
   float xv[8];
-  float mx = -__builtin_inff();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int h = i >> 2;
-    const bool v = ((h ? vm1 : vm0) >> (4 * x.c + (i & 3))) & 1u;
-    // The partner's partial is added in the same order in both waves.
-    const float s = s0[h][i & 3] + s1[h][i & 3];
-    xv[i] = v ? s * a.scale2 : -__builtin_inff();
-    mx = fmaxf(mx, xv[i]);
+  for (int i = 0; i < 8; ++i) xv[i] = s0[i >> 2][i & 3] + s1[i >> 2][i & 3];
+  if ((vm0 & vm1) != 0xffffu) {   // wave-uniform: some slot of the tile is empty
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool v = (((i >> 2) ? vm1 : vm0) >> (4 * x.c + (i & 3))) & 1u;
+      xv[i] = v ? xv[i] : -__builtin_inff();
+    }
   }
-  mx = head_max(mx);
+  float mx = fmaxf(fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3])),
+                   fmaxf(fmaxf(xv[4], xv[5]), fmaxf(xv[6], xv[7])));
+  // A tile is processed only when one of its slots holds an entry, so the
+  // maximum (and from here on the reference) is finite.
+  mx = head_max(mx) * a.scale2;
   // Reference: kept unless still -inf or exceeded by more than kLazyRescale.
   const float mr = st.m_ref;
   const float ref = (mr == -__builtin_inff() || mx > mr + kLazyRescale) ? mx : mr;
@@ -309,7 +363,8 @@ __device__ __forceinline__ void softmax_pv(const AttnArgs& a, const Ctx& x, uint
   float sum = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    xv[i] = xv[i] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(xv[i] - st.m_ref);
+    // exp2(-inf) = 0 for an empty slot.
+    xv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(xv[i], a.scale2, -st.m_ref));
     sum += xv[i];
   }
   st.l += head_sum(sum);
@@ -395,63 +450,91 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
   x.m = x.lane & 15;
   x.c = x.lane >> 4;
   x.sel_tiles = (a.top_k + kTile - 1) / kTile;
+  // Loads issued first, in this order: the window bounds, the slot id this
+  // thread stores to LDS, the ids of the pair's first selected tile
+  // (straight from global memory, so that its gather goes out as soon as
+  // they arrive, without waiting for the workgroup's ids), and the q rows
+  // (lane l of load j: head 2 j + l / 32, bytes 16 (l % 32) .. + 16 of the
+  // wave's dims half).
   x.qpos = a.q_pos[x.r];
   x.p0 = a.swa_pos0[x.b];
+  const int my_id = slot_id(a, x.r, threadIdx.x);
+  const int first[2] = {slot_id(a, x.r, kTile * x.pair + x.m),
+                        slot_id(a, x.r, kTile * x.pair + 16 + x.m)};
+  u32x4 qraw[8];
+  {
+    const uint8_t* qbase = reinterpret_cast<const uint8_t*>(
+        a.q + (static_cast<size_t>(x.r) * kHeads + kHeadsPerWg * x.hg) * kDim) + 512 * x.d;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      qraw[j] = *reinterpret_cast<const u32x4*>(qbase + (2 * j + (x.lane >> 5)) * 1024 +
+                                                16 * (x.lane & 31));
+  }
+  __builtin_amdgcn_sched_barrier(0);
   x.lo = max(max(x.qpos - a.window + 1, x.p0), 0);
   if (a.replay_start >= 0) x.lo = max(x.lo, a.replay_start);
-
-  // The row's selected ids go to LDS first (out-of-range ids and the slots
-  // past top_k up to the tile boundary become -1: no entry).
-  {
-    const int32_t* irow = a.idx + static_cast<size_t>(x.r) * a.top_k;
-    const int slot = threadIdx.x;
-    const int v = slot < a.top_k ? irow[slot] : -1;
-    sm.ids[slot] = (v >= 0 && v < a.N_cap) ? v : -1;
-    if (slot < kWaves) {
-      sm.ready[slot] = 0;
-      sm.taken[slot] = 0;
-    }
-  }
-  // q^T operands of head 16 hg + m: step s takes dims 256 d + 64 c + 8 s ..
-  // + 8 (16 bytes at 512 d + 128 c + 16 s of the head's row).
   State st;
-  {
-    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(
-        a.q + (static_cast<size_t>(x.r) * kHeads + kHeadsPerWg * x.hg + x.m) * kDim);
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s)
-      st.qb[s] = *reinterpret_cast<const u32x4*>(qrow + 512 * x.d + 128 * x.c + 16 * s);
-  }
+  uint8_t* tile = sm.tile[x.wave];
 #pragma unroll
   for (int t = 0; t < kDimTiles; ++t) st.o[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   st.m_ref = -__builtin_inff();
   st.l = 0.0f;
   st.exchanged = 0;
 
-  uint8_t* tile = sm.tile[x.wave];
   // Transposing-read offsets for dims tile 0 (tile t: + 32 t): row 4 c + j /
   // 4 (a) or 16 + 4 c + j / 4 (b), dims 4 (j % 4) .. + 4.
   const int j = x.m;
   const int off_a = (4 * x.c + (j >> 2)) * kRowBytes + 8 * (j & 3);
   const int off_b = off_a + 16 * kRowBytes;
 
-  // Round 1: pair p takes window tile p.  Then pair p takes selected tiles
-  // p, p + 4, ... (one round each); the next tile's loads are issued before
-  // the current one is processed (two register buffers).  The loads stay in
-  // issue order (window tile, then the first selected tile): the waits
-  // before each tile's use then count only later loads.  The window tile
-  // needs no ids, so its loads go out before the ids barrier.
+  // Round 1: pair p takes window tile p, before the workgroup barrier that
+  // publishes the ids (the window needs none); its exchange goes through
+  // that barrier.  Then pair p takes selected tiles p, p + 4, ... (one
+  // round each), the next tile's loads issued before the current one is
+  // processed (two register buffers).
   {
     WinRaw wr;
+    WinLoad wl;
     MainRaw m0, m1;
-    gather_window(a, x, x.pair, wr);
+    load_window(a, x, x.pair, wl, wr);
+    gather_rows<FMT>(a, x, first, m0);
     __builtin_amdgcn_sched_barrier(0);
-    lds_barrier();   // the ids are in LDS (the window loads stay in flight)
-    gather_main<FMT>(a, x, sm.ids, x.pair, m0);
+    // q^T operands of head 16 hg + m: step s takes dims 256 d + 64 c + 8 s
+    // .. + 8, i.e. 16 bytes at 128 c + 16 s of the head's staged half row.
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<u32x4*>(tile + (2 * j + (x.lane >> 5)) * kQStride + 16 * (x.lane & 31)) =
+          qraw[j];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+      st.qb[s] = *reinterpret_cast<const u32x4*>(tile + x.m * kQStride + 128 * x.c + 16 * s);
+    stage_window(x, wl, tile, wr);
     __builtin_amdgcn_sched_barrier(0);
     const bool work = __ballot(wr.valid[0] || wr.valid[1]) != 0;
+    f32x4_t acc[2];
+    if (work) {
+      qk_tile<false, FMT, WinRaw>(x, wr, st, tile, acc);
+      sm.xs[x.wave][0][x.lane] = acc[0];
+      sm.xs[x.wave][1][x.lane] = acc[1];
+    }
+    sm.ids[threadIdx.x] = my_id;
+    if (x.lane == 0) {
+      sm.ready[x.wave] = 0;
+      sm.taken[x.wave] = 0;
+    }
+    lds_barrier();   // ids, counters and the window partials are in LDS
     uint32_t round = 1;
-    round_tile<false, FMT>(a, x, sm, wr, work, round, tile, off_a, off_b, st);
+    if (work) {
+      const int partner = x.wave ^ 1;
+      f32x4_t other[2] = {sm.xs[partner][0][x.lane], sm.xs[partner][1][x.lane]};
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): both reads have returned
+      signal_counter(&sm.taken[x.wave], round);
+      st.exchanged = round;
+      const uint32_t vm0 = static_cast<uint32_t>(__ballot(wr.valid[0])) & 0xffffu;
+      const uint32_t vm1 = static_cast<uint32_t>(__ballot(wr.valid[1])) & 0xffffu;
+      if (x.d == 0) softmax_pv(a, x, vm0, vm1, tile, off_a, off_b, acc, other, st);
+      else softmax_pv(a, x, vm0, vm1, tile, off_a, off_b, other, acc, st);
+    }
     const int rounds = (x.sel_tiles + kPairs - 1) / kPairs;
     int t = x.pair;
     auto run = [&](const MainRaw& w) {
