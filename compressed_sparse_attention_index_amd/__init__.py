@@ -14,7 +14,7 @@ import torch
 __all__ = [
     "KDTYPE_BF16", "KDTYPE_FP8", "KV_MXFP4_E8M0_32", "KV_FP4_E4M3_16", "MODE_FULL", "MODE_REINDEX", "MODE_REUSE",
     "OP_INDEX_SCORE", "OP_BLOCK_TOPK", "OP_REINDEX_TOPK", "OP_SPARSE_ATTN",
-    "Csa2Error", "lib", "abi_version", "workspace_size", "index_score", "block_topk",
+    "Csa2Error", "Paging", "lib", "abi_version", "workspace_size", "index_score", "block_topk",
     "block_topk_noalloc",
     "reindex_topk", "sparse_attn_decode", "reuse_attn", "kv_append",
 ]
@@ -32,14 +32,15 @@ _S = ctypes.c_size_t
 _F = ctypes.c_float
 
 _SIGNATURES = {
-    "csa2_index_score": [_P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _P, _S, _P],
+    "csa2_index_score": [_P, _P, _P, _I, _P, _P, _I, _I, _I, _P, _P, _P, _S, _P],
     "csa2_block_topk": [_P, _P, _I, _I, _I, _I, _P, _P, _S, _P],
     "csa2_block_topk_noalloc": [_P, _P, _I, _I, _I, _I, _P, _P],
-    "csa2_reindex_topk": [_I, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _S, _P],
+    "csa2_reindex_topk": [_I, _P, _P, _P, _P, _I, _P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _S,
+                          _P],
     "csa2_sparse_attn_decode": [_P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _F, _P, _I, _I, _P, _P,
                                 _P, _S, _P],
     "csa2_reuse_attn": [_P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _F, _P, _I, _I, _P, _P, _P, _S, _P],
-    "csa2_kv_append": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P],
+    "csa2_kv_append": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P],
     "csa2_workspace_size": [_I, _I, _I, _I, _I, _I],
     "csa2_status_string": [_I],
     "csa2_abi_version": [],
@@ -48,12 +49,41 @@ _RESTYPES = {"csa2_workspace_size": _S, "csa2_status_string": ctypes.c_char_p,
              "csa2_abi_version": _I}
 
 
-ATTN_SINK = 1   # csa2_attn_opts.flags bit: the sink pointer is read
+ATTN_SINK = 1    # csa2_attn_opts.flags bit: the sink pointer is read
+ATTN_PAGED = 2   # csa2_attn_opts.flags bit: the paging pointer is read
+
+
+class PagingStruct(ctypes.Structure):
+    """csa2_paging."""
+    _fields_ = [("block_table", ctypes.c_void_p), ("page_entries", _I), ("max_pages", _I),
+                ("num_pages", _I)]
 
 
 class AttnOpts(ctypes.Structure):
     _fields_ = [("window", _I), ("replay_start", _I), ("kv_fmt", _I), ("flags", ctypes.c_uint32),
-                ("sink", ctypes.c_void_p)]
+                ("sink", ctypes.c_void_p), ("paging", ctypes.POINTER(PagingStruct))]
+
+
+class Paging:
+    """A page table (include/csa2.h, csa2_paging): block_table [B, max_pages]
+    int32 on the GPU, page_entries entries per page, num_pages pages in the
+    pool.  The logical capacity per sequence is max_pages * page_entries."""
+
+    def __init__(self, block_table, page_entries, num_pages):
+        self.block_table = block_table
+        self.page_entries = int(page_entries)
+        self.num_pages = int(num_pages)
+        self.max_pages = int(block_table.shape[1])
+        self.n_cap = self.max_pages * self.page_entries
+        self.struct = PagingStruct(_ptr(block_table, (torch.int32,), "block_table"),
+                                   self.page_entries, self.max_pages, self.num_pages)
+
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+
+def _paging(paging):
+    return paging.ref() if paging is not None else None
 
 
 class AttnOptsV1(ctypes.Structure):
@@ -133,13 +163,16 @@ def _workspace(ws, nbytes, device):
     return ws, ws.numel() * ws.element_size()
 
 
-def index_score(q_idx, w_idx, k_idx, vis_len, scores=None, block_max=None, stream=None):
-    """Indexer scan: scores [B, n_q, N_cap] and/or block_max [B, n_q, ceil(N_cap/8)]."""
+def index_score(q_idx, w_idx, k_idx, vis_len, scores=None, block_max=None, paging=None,
+                stream=None):
+    """Indexer scan: scores [B, n_q, N_cap] and/or block_max [B, n_q, ceil(N_cap/8)].
+    With paging, k_idx is a page pool [num_pages * page_entries, 128]."""
     B, n_q = q_idx.shape[0], q_idx.shape[1]
-    N_cap = k_idx.shape[1]
+    N_cap = paging.n_cap if paging is not None else k_idx.shape[1]
     kd = KDTYPE_BF16 if k_idx.dtype in _BITS16 else KDTYPE_FP8
     _call("csa2_index_score", _ptr(q_idx, _BITS16, "q_idx"), _ptr(w_idx, _F32, "w_idx"),
-          _ptr(k_idx, _BITS16 + _U8, "k_idx"), kd, _ptr(vis_len, _I32, "vis_len"), B, n_q, N_cap,
+          _ptr(k_idx, _BITS16 + _U8, "k_idx"), kd, _paging(paging),
+          _ptr(vis_len, _I32, "vis_len"), B, n_q, N_cap,
           _ptr(scores, _F32, "scores"), _ptr(block_max, _F32, "block_max"), None, 0,
           _stream(stream))
 
@@ -164,7 +197,7 @@ def block_topk_noalloc(block_max, vis_len, N_cap, k_blocks, pool_blocks, stream=
 
 
 def reindex_topk(mode, vis_len, N_cap, top_k, idx_out, scores=None, q_idx=None, w_idx=None,
-                 k_idx=None, pool_blocks=None, idx_score=None, ws=None, stream=None):
+                 k_idx=None, pool_blocks=None, idx_score=None, paging=None, ws=None, stream=None):
     """Top-k inside the pool (Full / Reindex) or over [0, vis) without a pool."""
     B, n_q = vis_len.shape[0], vis_len.shape[1]
     k_blocks = pool_blocks.shape[-1] if pool_blocks is not None else 0
@@ -172,7 +205,7 @@ def reindex_topk(mode, vis_len, N_cap, top_k, idx_out, scores=None, q_idx=None, 
     need = workspace_size(OP_REINDEX_TOPK, B, n_q, N_cap, top_k, k_blocks)
     ws, nbytes = _workspace(ws, need if pool_blocks is not None else 0, vis_len.device)
     _call("csa2_reindex_topk", mode, _ptr(scores, _F32, "scores"), _ptr(q_idx, _BITS16, "q_idx"),
-          _ptr(w_idx, _F32, "w_idx"), _ptr(k_idx, _BITS16 + _U8, "k_idx"), kd,
+          _ptr(w_idx, _F32, "w_idx"), _ptr(k_idx, _BITS16 + _U8, "k_idx"), kd, _paging(paging),
           _ptr(pool_blocks, _I32, "pool_blocks"), k_blocks, _ptr(vis_len, _I32, "vis_len"),
           B, n_q, N_cap, top_k, _ptr(idx_out, _I32, "idx_out"),
           _ptr(idx_score, _F32, "idx_score"), _ptr(ws, (torch.uint8,), "ws"), nbytes,
@@ -180,15 +213,18 @@ def reindex_topk(mode, vis_len, N_cap, top_k, idx_out, scores=None, q_idx=None, 
 
 
 def _attn(name, q, kv_fp4, kv_scale, idx, swa_kv, swa_pos0, q_pos, sm_scale, out, lse=None,
-          window=128, replay_start=-1, sink=None, kv_fmt=KV_MXFP4_E8M0_32, ws=None, stream=None):
+          window=128, replay_start=-1, sink=None, kv_fmt=KV_MXFP4_E8M0_32, paging=None, ws=None,
+          stream=None):
     B, n_q = q.shape[0], q.shape[1]
-    N_cap = kv_fp4.shape[1]
+    N_cap = paging.n_cap if paging is not None else kv_fp4.shape[1]
     top_k = idx.shape[-1] if idx is not None else 0
     S_cap = swa_kv.shape[1] if swa_kv is not None else 0
     need = workspace_size(OP_SPARSE_ATTN, B, n_q, N_cap, top_k, 0)
     ws, nbytes = _workspace(ws, need, q.device)
     sp = _ptr(sink, _F32, "sink")
-    opts = AttnOpts(window, replay_start, kv_fmt, ATTN_SINK if sp else 0, sp)
+    flags = (ATTN_SINK if sp else 0) | (ATTN_PAGED if paging is not None else 0)
+    opts = AttnOpts(window, replay_start, kv_fmt, flags, sp,
+                    ctypes.pointer(paging.struct) if paging is not None else None)
     _call(name, _ptr(q, _BITS16, "q"), _ptr(kv_fp4, _U8, "kv_fp4"),
           _ptr(kv_scale, _U8, "kv_scale"), N_cap, _ptr(idx, _I32, "idx"), top_k,
           _ptr(swa_kv, _U8, "swa_kv"), S_cap, _ptr(swa_pos0, _I32, "swa_pos0"),
@@ -208,14 +244,15 @@ def reuse_attn(*args, **kw):
 
 
 def kv_append(kv_new, pos, kv_fp4, kv_scale, swa_new=None, swa_kv=None, swa_pos0=None,
-              kv_fmt=KV_MXFP4_E8M0_32, stream=None):
+              kv_fmt=KV_MXFP4_E8M0_32, paging=None, stream=None):
     """Encodes new tokens' entries (kv_new [B, n_new, 512] bf16 -> E2M1 rows
     pos[b] + i of kv_fp4 with scales in kv_scale, format kv_fmt; swa_new ->
     FP8 rows of swa_kv)."""
     B, n_new = kv_new.shape[0], kv_new.shape[1]
-    N_cap = kv_fp4.shape[1]
+    N_cap = paging.n_cap if paging is not None else kv_fp4.shape[1]
     S_cap = swa_kv.shape[1] if swa_kv is not None else 0
     _call("csa2_kv_append", _ptr(kv_new, _BITS16, "kv_new"), _ptr(swa_new, _BITS16, "swa_new"),
-          _ptr(pos, _I32, "pos"), B, n_new, N_cap, kv_fmt, _ptr(kv_fp4, _U8, "kv_fp4"),
+          _ptr(pos, _I32, "pos"), B, n_new, N_cap, kv_fmt, _paging(paging),
+          _ptr(kv_fp4, _U8, "kv_fp4"),
           _ptr(kv_scale, _U8, "kv_scale"), _ptr(swa_kv, _U8, "swa_kv"), S_cap,
           _ptr(swa_pos0, _I32, "swa_pos0"), _stream(stream))

@@ -21,6 +21,24 @@ csa2_status from_hip(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR
 
 int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
+// A page table: NULL (contiguous) or a valid csa2_paging whose logical
+// capacity is N_cap.  Fills `pg` (bt = nullptr for NULL).
+csa2_status check_paging(const csa2_paging* paging, int32_t N_cap, csa2::Pages* pg) {
+  *pg = csa2::Pages{nullptr, 0, 0, 0};
+  if (!paging) return CSA2_OK;
+  if (!paging->block_table) return CSA2_ERR_NULL;
+  if (!aligned16(paging->block_table)) return CSA2_ERR_ALIGN;
+  const int32_t P = paging->page_entries;
+  if (P < 64 || P > 65536 || (P & (P - 1)) != 0) return CSA2_ERR_SHAPE;
+  if (paging->max_pages < 1 || paging->num_pages < 1) return CSA2_ERR_SHAPE;
+  if (static_cast<int64_t>(paging->max_pages) * P != N_cap) return CSA2_ERR_SHAPE;
+  if (static_cast<int64_t>(paging->num_pages) * P > 0x7fffffffLL) return CSA2_ERR_SHAPE;
+  int log2p = 0;
+  while ((1 << log2p) < P) ++log2p;
+  *pg = csa2::Pages{paging->block_table, log2p, paging->max_pages, paging->num_pages};
+  return CSA2_OK;
+}
+
 csa2_status check_rows(int32_t B, int32_t n_q) {
   if (B < 1 || n_q < 1) return CSA2_ERR_SHAPE;
   if (static_cast<int64_t>(B) * n_q > (1LL << 30)) return CSA2_ERR_SHAPE;
@@ -45,10 +63,16 @@ csa2_status attn_common(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t*
   if (!(sm_scale > 0.0f) || !(sm_scale < __builtin_inff())) return CSA2_ERR_SHAPE;
   int32_t window = 128, replay_start = -1, kv_fmt = CSA2_KV_MXFP4_E8M0_32;
   const float* sink = nullptr;
+  csa2::Pages pg{nullptr, 0, 0, 0};
   if (opts) {
     if ((opts->kv_fmt != CSA2_KV_MXFP4_E8M0_32 && opts->kv_fmt != CSA2_KV_FP4_E4M3_16) ||
-        (opts->flags & ~CSA2_ATTN_SINK) != 0)
+        (opts->flags & ~(CSA2_ATTN_SINK | CSA2_ATTN_PAGED)) != 0)
       return CSA2_ERR_UNSUPPORTED;
+    if (opts->flags & CSA2_ATTN_PAGED) {
+      if (!opts->paging) return CSA2_ERR_NULL;
+      const csa2_status ps = check_paging(opts->paging, N_cap, &pg);
+      if (ps != CSA2_OK) return ps;
+    }
     kv_fmt = opts->kv_fmt;
     if (opts->window < 0 || opts->window > 128 || opts->replay_start < -1) return CSA2_ERR_SHAPE;
     window = opts->window;
@@ -66,7 +90,7 @@ csa2_status attn_common(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t*
   if (ws && !aligned16(ws)) return CSA2_ERR_ALIGN;
   return from_hip(csa2::launch_sparse_attn(q, kv_fp4, kv_scale, N_cap, idx, top_k, swa_kv, S_cap,
                                            swa_pos0, q_pos, sm_scale, window, replay_start, sink,
-                                           kv_fmt, B, n_q, out, lse, ws, stream));
+                                           kv_fmt, pg, B, n_q, out, lse, ws, stream));
 }
 
 }  // namespace
@@ -74,9 +98,10 @@ csa2_status attn_common(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t*
 extern "C" {
 
 csa2_status csa2_index_score(const uint16_t* q_idx, const float* w_idx, const void* k_idx,
-                             csa2_kdtype k_dtype, const int32_t* vis_len, int32_t B, int32_t n_q,
-                             int32_t N_cap, float* scores, float* block_max, void* ws,
-                             size_t ws_bytes, hipStream_t stream) {
+                             csa2_kdtype k_dtype, const csa2_paging* paging,
+                             const int32_t* vis_len, int32_t B, int32_t n_q, int32_t N_cap,
+                             float* scores, float* block_max, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
   (void)ws;
   (void)ws_bytes;
   if (!q_idx || !w_idx || !k_idx || !vis_len) return CSA2_ERR_NULL;
@@ -90,8 +115,11 @@ csa2_status csa2_index_score(const uint16_t* q_idx, const float* w_idx, const vo
   const void* ptrs[] = {q_idx, w_idx, k_idx, vis_len, scores, block_max};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return CSA2_ERR_ALIGN;
+  csa2::Pages pg;
+  st = check_paging(paging, N_cap, &pg);
+  if (st != CSA2_OK) return st;
   return from_hip(csa2::launch_index_score(q_idx, w_idx, k_idx, k_dtype == CSA2_KDTYPE_FP8_E4M3,
-                                           vis_len, B, n_q, N_cap, scores, block_max, stream));
+                                           pg, vis_len, B, n_q, N_cap, scores, block_max, stream));
 }
 
 csa2_status csa2_block_topk(const float* block_max, const int32_t* vis_len, int32_t B,
@@ -129,10 +157,10 @@ csa2_status csa2_block_topk_noalloc(const float* block_max, const int32_t* vis_l
 
 csa2_status csa2_reindex_topk(csa2_mode mode, const float* scores, const uint16_t* q_idx,
                               const float* w_idx, const void* k_idx, csa2_kdtype k_dtype,
-                              const int32_t* pool_blocks, int32_t k_blocks,
-                              const int32_t* vis_len, int32_t B, int32_t n_q, int32_t N_cap,
-                              int32_t top_k, int32_t* idx_out, float* idx_score, void* ws,
-                              size_t ws_bytes, hipStream_t stream) {
+                              const csa2_paging* paging, const int32_t* pool_blocks,
+                              int32_t k_blocks, const int32_t* vis_len, int32_t B, int32_t n_q,
+                              int32_t N_cap, int32_t top_k, int32_t* idx_out, float* idx_score,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
   if (mode != CSA2_MODE_FULL && mode != CSA2_MODE_REINDEX) return CSA2_ERR_UNSUPPORTED;
   if (!vis_len || !idx_out) return CSA2_ERR_NULL;
   csa2_status st = check_rows(B, n_q);
@@ -142,6 +170,9 @@ csa2_status csa2_reindex_topk(csa2_mode mode, const float* scores, const uint16_
   const void* ptrs[] = {scores, q_idx, w_idx, k_idx, pool_blocks, vis_len, idx_out, idx_score, ws};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return CSA2_ERR_ALIGN;
+  csa2::Pages pg;
+  st = check_paging(paging, N_cap, &pg);
+  if (st != CSA2_OK) return st;
   if (!pool_blocks) {
     if (!scores) return CSA2_ERR_NULL;
     return from_hip(csa2::launch_flat_topk(scores, vis_len, rows, N_cap, top_k, idx_out,
@@ -158,7 +189,8 @@ csa2_status csa2_reindex_topk(csa2_mode mode, const float* scores, const uint16_
   const size_t need = csa2::pool_topk_workspace_bytes(rows, k_blocks);
   if (!ws || ws_bytes < need) return CSA2_ERR_WORKSPACE;
   const int kmode = stored ? 0 : (k_dtype == CSA2_KDTYPE_FP8_E4M3 ? 1 : 2);
-  return from_hip(csa2::launch_pool_topk(kmode, scores, q_idx, w_idx, k_idx, pool_blocks, k_blocks,
+  return from_hip(csa2::launch_pool_topk(kmode, scores, q_idx, w_idx, k_idx, pg, pool_blocks,
+                                         k_blocks,
                                          vis_len, rows, n_q, N_cap, top_k, idx_out, idx_score, ws,
                                          stream));
 }
@@ -186,8 +218,9 @@ csa2_status csa2_reuse_attn(const uint16_t* q, const uint8_t* kv_fp4, const uint
 
 csa2_status csa2_kv_append(const uint16_t* kv_new, const uint16_t* swa_new, const int32_t* pos,
                            int32_t B, int32_t n_new, int32_t N_cap, int32_t kv_fmt,
-                           uint8_t* kv_fp4, uint8_t* kv_scale, uint8_t* swa_kv, int32_t S_cap,
-                           const int32_t* swa_pos0, hipStream_t stream) {
+                           const csa2_paging* paging, uint8_t* kv_fp4, uint8_t* kv_scale,
+                           uint8_t* swa_kv, int32_t S_cap, const int32_t* swa_pos0,
+                           hipStream_t stream) {
   if (!kv_new || !pos || !kv_fp4 || !kv_scale) return CSA2_ERR_NULL;
   if (swa_new && (!swa_kv || !swa_pos0)) return CSA2_ERR_NULL;
   csa2_status st = check_rows(B, n_new);
@@ -197,8 +230,11 @@ csa2_status csa2_kv_append(const uint16_t* kv_new, const uint16_t* swa_new, cons
   const void* ptrs[] = {kv_new, swa_new, pos, kv_fp4, kv_scale, swa_kv, swa_pos0};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return CSA2_ERR_ALIGN;
-  return from_hip(csa2::launch_kv_append(kv_new, swa_new, pos, B, n_new, N_cap, kv_fmt, kv_fp4,
-                                         kv_scale,
+  csa2::Pages pg;
+  st = check_paging(paging, N_cap, &pg);
+  if (st != CSA2_OK) return st;
+  return from_hip(csa2::launch_kv_append(kv_new, swa_new, pos, B, n_new, N_cap, kv_fmt, pg,
+                                         kv_fp4, kv_scale,
                                          swa_new ? swa_kv : nullptr, S_cap, swa_pos0, stream));
 }
 

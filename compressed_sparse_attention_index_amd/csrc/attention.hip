@@ -95,6 +95,7 @@ struct AttnArgs {
   uint16_t* out;
   float* lse;
   const float* sink;   // [64] per-head sink logits (natural log), or null
+  Pages pg;            // main-KV page table (pg.bt == nullptr: contiguous)
   int N_cap, top_k, S_cap, n_q, window, replay_start, rows;
   float scale2;        // sm_scale * log2(e)
 };
@@ -109,6 +110,7 @@ struct Smem {
 };
 
 struct Ctx {
+  size_t row0;         // main-KV row of entry 0 of the sequence (0 with paging: ids are pool rows)
   int r, b, hg, wave, pair, d, lane, m, c;
   int sel_tiles, qpos, p0, lo;
 };
@@ -177,7 +179,7 @@ __device__ __forceinline__ void gather_rows(const AttnArgs& a, const Ctx& x, con
   for (int h = 0; h < 2; ++h) {
     const bool valid = id[h] >= 0;
     w.valid[h] = valid;
-    const size_t er = static_cast<size_t>(x.b) * a.N_cap + (valid ? id[h] : 0);
+    const size_t er = x.row0 + (valid ? id[h] : 0);
     const uint8_t* src = a.kv_fp4 + er * 256 + 128 * x.d + 32 * x.c;
     w.f[h][0] = *reinterpret_cast<const u32x4*>(src);
     w.f[h][1] = *reinterpret_cast<const u32x4*>(src + 16);
@@ -193,10 +195,16 @@ __device__ __forceinline__ void gather_main(const AttnArgs& a, const Ctx& x, con
   gather_rows<FMT>(a, x, id, w);
 }
 
-// Id of selected slot `slot` of row r read from global memory (-1: no entry).
-__device__ __forceinline__ int slot_id(const AttnArgs& a, int r, int slot) {
+// Selected slot `slot` of row r (sequence b) read from global memory: the
+// entry id, or with paging its pool row; -1 for no entry (an id out of
+// range or on an unmapped page).
+__device__ __forceinline__ int slot_id(const AttnArgs& a, int r, int b, int slot) {
   const int v = slot < a.top_k ? a.idx[static_cast<size_t>(r) * a.top_k + slot] : -1;
-  return (v >= 0 && v < a.N_cap) ? v : -1;
+  if (v < 0 || v >= a.N_cap) return -1;
+  if (a.pg.bt == nullptr) return v;
+  bool mapped;
+  const size_t row = pool_row(a.pg, b, a.N_cap, v, mapped);
+  return mapped ? static_cast<int>(row) : -1;
 }
 
 // Window tile u (positions q_pos - 127 + 32 u .. + 31), dims half d: the
@@ -458,9 +466,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
   // wave's dims half).
   x.qpos = a.q_pos[x.r];
   x.p0 = a.swa_pos0[x.b];
-  const int my_id = slot_id(a, x.r, threadIdx.x);
-  const int first[2] = {slot_id(a, x.r, kTile * x.pair + x.m),
-                        slot_id(a, x.r, kTile * x.pair + 16 + x.m)};
+  x.row0 = a.pg.bt == nullptr ? static_cast<size_t>(x.b) * a.N_cap : 0;
+  const int my_id = slot_id(a, x.r, x.b, threadIdx.x);
+  const int first[2] = {slot_id(a, x.r, x.b, kTile * x.pair + x.m),
+                        slot_id(a, x.r, x.b, kTile * x.pair + 16 + x.m)};
   u32x4 qraw[8];
   {
     const uint8_t* qbase = reinterpret_cast<const uint8_t*>(
@@ -614,18 +623,19 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* kv_fp4, const ui
                               int N_cap, const int32_t* idx, int top_k, const uint8_t* swa_kv,
                               int S_cap, const int32_t* swa_pos0, const int32_t* q_pos,
                               float sm_scale, int window, int replay_start, const float* sink,
-                              int kv_fmt, int B, int n_q, uint16_t* out, float* lse, void* ws,
-                              hipStream_t stream) {
+                              int kv_fmt, const Pages& pg, int B, int n_q, uint16_t* out,
+                              float* lse, void* ws, hipStream_t stream) {
   (void)ws;
   // Prefill-shaped calls (many query rows per sequence) take the one-row-
   // per-workgroup kernel; the choice depends on n_q only, never on B.
   if (n_q >= kRowsKernelMinNq)
     return launch_attn_rows(q, kv_fp4, kv_scale, N_cap, idx, top_k, swa_kv, S_cap, swa_pos0,
-                            q_pos, sm_scale, window, replay_start, sink, kv_fmt, B, n_q, out,
+                            q_pos, sm_scale, window, replay_start, sink, kv_fmt, pg, B, n_q, out,
                             lse, stream);
   AttnArgs a;
   a.q = q; a.kv_fp4 = kv_fp4; a.kv_scale = kv_scale; a.idx = idx; a.swa = swa_kv;
   a.swa_pos0 = swa_pos0; a.q_pos = q_pos; a.out = out; a.lse = lse; a.sink = sink;
+  a.pg = pg;
   a.N_cap = N_cap; a.top_k = top_k; a.S_cap = S_cap; a.n_q = n_q;
   a.window = window; a.replay_start = replay_start;
   a.rows = B * n_q;

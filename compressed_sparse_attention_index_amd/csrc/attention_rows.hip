@@ -74,6 +74,7 @@ struct AttnArgs {
   uint16_t* out;
   float* lse;
   const float* sink; // [64] per-head sink logits (natural log), or null
+  Pages pg;          // main-KV page table (pg.bt == nullptr: contiguous)
   int N_cap, top_k, S_cap, n_q, window, replay_start;
   int rows, n_chunks;
   float scale2;      // sm_scale * log2(e)
@@ -89,6 +90,7 @@ struct Smem {
 };
 
 struct Ctx {
+  size_t row0;   // main-KV row of entry 0 of the sequence (0 with paging: ids are pool rows)
   int r, b, tkp, qpos, lo, p0, slot0, wave, lane, c, half, e, dh;
 };
 
@@ -146,7 +148,7 @@ __device__ __forceinline__ bool issue_tile(const AttnArgs& a, const Ctx& x, Smem
   if (tile_is_main(x, ch)) {
     const int id = sm.ids[slot - x.slot0];
     const bool valid = id >= 0;
-    const size_t er = static_cast<size_t>(x.b) * a.N_cap + (valid ? id : 0);
+    const size_t er = x.row0 + (valid ? id : 0);
     const uint8_t* src = a.kv_fp4 + er * 256 + 128 * x.dh + 64 * x.half;
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(src + 16 * i, dst + 1024 * i);
@@ -441,6 +443,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_rows(AttnArgs a) {
   Ctx x;
   x.r = blockIdx.x;
   x.b = x.r / a.n_q;
+  x.row0 = a.pg.bt == nullptr ? static_cast<size_t>(x.b) * a.N_cap : 0;
   x.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   x.lane = threadIdx.x & 63;
   x.c = x.lane & 31;
@@ -457,8 +460,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_rows(AttnArgs a) {
   x.slot0 = kChunk * c0;
 
   // The selected ids of chunks [c0, c1) go to LDS first, so that no gather
-  // waits on a global id load; out-of-range ids become -1 (no entry).  The
-  // id loads and the q loads are all issued before any is used.
+  // waits on a global id load; out-of-range ids (and, with paging, ids on
+  // unmapped pages) become -1 (no entry), and with paging the others become
+  // pool rows.  The id loads and the q loads are all issued before any is
+  // used.
   constexpr int kPer = (kMaxChunks * kChunk + kThreads - 1) / kThreads;
   int sid[kPer];
 #pragma unroll
@@ -484,7 +489,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_rows(AttnArgs a) {
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int i = threadIdx.x + kThreads * u;
-    if (i < kChunk * (c1 - c0)) sm.ids[i] = (sid[u] >= 0 && sid[u] < a.N_cap) ? sid[u] : -1;
+    if (i >= kChunk * (c1 - c0)) continue;
+    int v = (sid[u] >= 0 && sid[u] < a.N_cap) ? sid[u] : -1;
+    if (v >= 0 && a.pg.bt != nullptr) {
+      bool mapped;
+      const size_t row = pool_row(a.pg, x.b, a.N_cap, v, mapped);
+      v = mapped ? static_cast<int>(row) : -1;
+    }
+    sm.ids[i] = v;
   }
   // The ids and the query row have landed (every wave's) before the first
   // gather is issued: no other vector-memory load is in flight inside the
@@ -601,7 +613,7 @@ hipError_t launch_attn_rows(const uint16_t* q, const uint8_t* kv_fp4, const uint
                             int N_cap, const int32_t* idx, int top_k, const uint8_t* swa_kv,
                             int S_cap, const int32_t* swa_pos0, const int32_t* q_pos,
                             float sm_scale, int window, int replay_start, const float* sink,
-                            int kv_fmt, int B, int n_q, uint16_t* out, float* lse,
+                            int kv_fmt, const Pages& pg, int B, int n_q, uint16_t* out, float* lse,
                             hipStream_t stream) {
   const int rows = B * n_q;
   AttnArgs a;
@@ -610,6 +622,7 @@ hipError_t launch_attn_rows(const uint16_t* q, const uint8_t* kv_fp4, const uint
   a.N_cap = N_cap; a.top_k = top_k; a.S_cap = S_cap; a.n_q = n_q;
   a.window = window; a.replay_start = replay_start;
   a.sink = sink;
+  a.pg = pg;
   a.scale2 = sm_scale * kLog2e;
   a.rows = rows;
   const int tkp = (top_k + kTile - 1) / kTile * kTile;

@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "csa2_launch.h"
+
 namespace csa2 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -210,6 +212,27 @@ __device__ __forceinline__ u32x4 to_agpr(u32x4 v) {
   asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(w.z) : "v"(v.z));
   asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(w.w) : "v"(v.w));
   return w;
+}
+
+// Physical page of logical page j of sequence b.  `mapped` says whether the
+// table holds an id in [0, num_pages); an id outside is clamped into that
+// range, so that no address is ever out of bounds.
+__device__ __forceinline__ int page_id(const Pages& pg, int b, int j, bool& mapped) {
+  const int v = pg.bt[static_cast<size_t>(b) * pg.max_pages + j];
+  mapped = v >= 0 && v < pg.num_pages;
+  return min(max(v, 0), pg.num_pages - 1);
+}
+
+// Row of entry e (0 <= e < N_cap) of sequence b: in the page pool, or
+// b * N_cap + e without paging.
+__device__ __forceinline__ size_t pool_row(const Pages& pg, int b, int N_cap, int e,
+                                           bool& mapped) {
+  if (pg.bt == nullptr) {
+    mapped = true;
+    return static_cast<size_t>(b) * N_cap + e;
+  }
+  const int p = page_id(pg, b, e >> pg.log2p, mapped);
+  return (static_cast<size_t>(p) << pg.log2p) + (e & ((1 << pg.log2p) - 1));
 }
 
 }  // namespace csa2

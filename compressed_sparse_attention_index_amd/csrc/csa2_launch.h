@@ -8,15 +8,23 @@
 
 namespace csa2 {
 
+// Page table of a paged cache (csa2_paging in include/csa2.h): entry e of
+// sequence b sits in pool row bt[b * max_pages + (e >> log2p)] * 2^log2p +
+// (e & (2^log2p - 1)).  bt == nullptr: contiguous arrays, row b * N_cap + e.
+struct Pages {
+  const int32_t* bt;
+  int log2p, max_pages, num_pages;
+};
+
 hipError_t launch_index_score(const uint16_t* q_idx, const float* w_idx, const void* k_idx,
-                              bool fp8, const int32_t* vis_len, int B, int n_q, int N_cap,
-                              float* scores, float* block_max, hipStream_t stream);
+                              bool fp8, const Pages& pg, const int32_t* vis_len, int B, int n_q,
+                              int N_cap, float* scores, float* block_max, hipStream_t stream);
 
 // Prefill-chunk scoring on matrix cores (n_q >= 16 rows per sequence); see
 // index_gemm.hip.
 hipError_t launch_index_gemm(const uint16_t* q_idx, const float* w_idx, const uint8_t* k_idx,
-                             bool fp8, const int32_t* vis_len, int B, int n_q, int N_cap,
-                             float* scores, float* block_max, hipStream_t stream);
+                             bool fp8, const Pages& pg, const int32_t* vis_len, int B, int n_q,
+                             int N_cap, float* scores, float* block_max, hipStream_t stream);
 
 // Block Top-K (pool of blocks); see topk.hip.
 size_t block_topk_workspace_bytes(int rows, int N_cap);
@@ -33,7 +41,8 @@ hipError_t launch_block_topk_noalloc(const float* block_max, const int32_t* vis_
 // re-scored with q_idx / w_idx on FP8 / bf16 keys.
 size_t pool_topk_workspace_bytes(int rows, int k_blocks);
 hipError_t launch_pool_topk(int mode, const float* scores, const uint16_t* q_idx,
-                            const float* w_idx, const void* k_idx, const int32_t* pool_blocks,
+                            const float* w_idx, const void* k_idx, const Pages& pg,
+                            const int32_t* pool_blocks,
                             int k_blocks, const int32_t* vis_len, int rows, int n_q, int N_cap,
                             int top_k, int32_t* out, float* out_key, void* ws,
                             hipStream_t stream);
@@ -52,20 +61,21 @@ hipError_t launch_attn_rows(const uint16_t* q, const uint8_t* kv_fp4, const uint
                             int N_cap, const int32_t* idx, int top_k, const uint8_t* swa_kv,
                             int S_cap, const int32_t* swa_pos0, const int32_t* q_pos,
                             float sm_scale, int window, int replay_start, const float* sink,
-                            int kv_fmt, int B, int n_q, uint16_t* out, float* lse,
+                            int kv_fmt, const Pages& pg, int B, int n_q, uint16_t* out, float* lse,
                             hipStream_t stream);
 
 hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
                               int N_cap, const int32_t* idx, int top_k, const uint8_t* swa_kv,
                               int S_cap, const int32_t* swa_pos0, const int32_t* q_pos,
                               float sm_scale, int window, int replay_start, const float* sink,
-                              int kv_fmt, int B, int n_q, uint16_t* out, float* lse, void* ws,
-                              hipStream_t stream);
+                              int kv_fmt, const Pages& pg, int B, int n_q, uint16_t* out,
+                              float* lse, void* ws, hipStream_t stream);
 
 // KV append: MXFP4 main entries and FP8 window entries of new tokens; see
 // kv_append.hip.
 hipError_t launch_kv_append(const uint16_t* kv_new, const uint16_t* swa_new, const int32_t* pos,
-                            int B, int n_new, int N_cap, int kv_fmt, uint8_t* kv_fp4,
+                            int B, int n_new, int N_cap, int kv_fmt, const Pages& pg,
+                            uint8_t* kv_fp4,
                             uint8_t* kv_scale, uint8_t* swa, int S_cap, const int32_t* swa_pos0,
                             hipStream_t stream);
 

@@ -109,8 +109,8 @@ struct Acc {
 template <bool FP8, int OUT>
 __global__ __launch_bounds__(kThreads, kWgPerCu) void k_index_gemm(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
-    const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ vis_len, int n_q, int N_cap,
-    int tiles_per_wg, float* __restrict__ scores, float* __restrict__ block_max) {
+    const uint8_t* __restrict__ k_idx, Pages pg, const int32_t* __restrict__ vis_len, int n_q,
+    int N_cap, int tiles_per_wg, float* __restrict__ scores, float* __restrict__ block_max) {
   using KT = KTile<FP8>;
   static_assert(kStages == 4, "the wait accounting below assumes this ring depth");
   __shared__ __attribute__((aligned(16))) uint8_t ring[kStages][KT::kBytes];
@@ -147,6 +147,17 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_index_gemm(
   // l of load u fills chunk position p = 64 (w LPW + u) + l (row p /
   // kChunks), which holds chunk (p % kChunks) ^ (row & 7) of that row.
   const uint8_t* kbase = k_idx + static_cast<size_t>(b) * N_cap * KT::kRowBytes;
+  // With paging, lane l holds the pool page of the workgroup's l-th logical
+  // page (the launcher keeps a paged workgroup within 32 tiles of 64 entries
+  // and pages hold at least 64: at most 33 pages); a tile never straddles
+  // two pages.
+  const bool paged = pg.bt != nullptr;
+  const int page0 = paged ? (64 * t_begin) >> pg.log2p : 0;
+  int my_page = 0;
+  if (paged && page0 + lane < pg.max_pages) {
+    bool mapped;
+    my_page = page_id(pg, b, page0 + lane, mapped);
+  }
   // Rows of load u: grow0 + u * (64 / kChunks).
   int goff[KT::kLoadsPerWave];
   const int grow0 = (64 * KT::kLoadsPerWave * wave + lane) / KT::kChunks;
@@ -159,6 +170,12 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_index_gemm(
   auto issue = [&](int t) {
     const int rows_left = N_cap - 64 * t;   // rows of this tile inside the buffer
     const uint8_t* base = kbase + static_cast<size_t>(64) * t * KT::kRowBytes;
+    if (paged) {
+      const int e = 64 * t;
+      const int pid = __shfl(my_page, (e >> pg.log2p) - page0, 64);
+      base = k_idx + ((static_cast<size_t>(pid) << pg.log2p) + (e & ((1 << pg.log2p) - 1))) *
+                         KT::kRowBytes;
+    }
     const uint32_t dst = lds_offset(&ring[static_cast<unsigned>(t - t_begin) % kStages][0]);
 #pragma unroll
     for (int u = 0; u < KT::kLoadsPerWave; ++u)
@@ -364,16 +381,17 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_index_gemm(
 }  // namespace
 
 hipError_t launch_index_gemm(const uint16_t* q_idx, const float* w_idx, const uint8_t* k_idx,
-                             bool fp8, const int32_t* vis_len, int B, int n_q, int N_cap,
-                             float* scores, float* block_max, hipStream_t stream) {
+                             bool fp8, const Pages& pg, const int32_t* vis_len, int B, int n_q,
+                             int N_cap, float* scores, float* block_max, hipStream_t stream) {
   const int tiles = (N_cap + 63) / 64;
-  const int tpw = (tiles + kChunksPerRow - 1) / kChunksPerRow;
+  int tpw = (tiles + kChunksPerRow - 1) / kChunksPerRow;
+  if (pg.bt != nullptr) tpw = tpw < 32 ? tpw : 32;   // at most 33 pages per workgroup
   const int groups = (n_q + kRowsPerWg - 1) / kRowsPerWg;
   dim3 grid((tiles + tpw - 1) / tpw, groups, B);
   const int out = (scores != nullptr ? kOutScores : 0) | (block_max != nullptr ? kOutBlockMax : 0);
 #define CSA2_GEMM_LAUNCH(F, O)                                                                 \
   hipLaunchKernelGGL((k_index_gemm<F, O>), grid, dim3(kThreads), 0, stream, q_idx, w_idx, k_idx, \
-                     vis_len, n_q, N_cap, tpw, scores, block_max)
+                     pg, vis_len, n_q, N_cap, tpw, scores, block_max)
   switch ((fp8 ? 4 : 0) | out) {
     case 1: CSA2_GEMM_LAUNCH(false, 1); break;
     case 2: CSA2_GEMM_LAUNCH(false, 2); break;

@@ -74,8 +74,8 @@ struct ScanTile {
 template <bool FP8, int DEPTH, int OUT>
 __global__ __launch_bounds__(kThreads) void k_index_scan(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
-    const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ vis_len, int n_q, int N_cap,
-    int tiles_per_wg, float* __restrict__ scores, float* __restrict__ block_max) {
+    const uint8_t* __restrict__ k_idx, Pages pg, const int32_t* __restrict__ vis_len, int n_q,
+    int N_cap, int tiles_per_wg, float* __restrict__ scores, float* __restrict__ block_max) {
   using TT = ScanTile<FP8>;
   constexpr int kStores = ((OUT & kOutScores) ? 1 : 0) + ((OUT & kOutBlockMax) ? 1 : 0);
   constexpr int kSteady = DEPTH * (TT::kLoads + kStores);
@@ -97,6 +97,16 @@ __global__ __launch_bounds__(kThreads) void k_index_scan(
   load_query(qa, q_idx + static_cast<size_t>(r) * kIdxHeads * kIdxDim, col, half);
   load_weights(wr, w_idx + static_cast<size_t>(r) * kIdxHeads, half);
   const uint8_t* kb = k_idx + static_cast<size_t>(b) * N_cap * TT::kRowBytes;
+  // With paging, lane l holds the pool page of the workgroup's l-th logical
+  // page (a workgroup spans at most 64 tiles of 32 entries, pages hold at
+  // least 64 entries: at most 33 pages); a tile never straddles two pages.
+  const bool paged = pg.bt != nullptr;
+  const int page0 = paged ? (32 * t_begin) >> pg.log2p : 0;
+  int my_page = 0;
+  if (paged && page0 + lane < pg.max_pages) {
+    bool mapped;
+    my_page = page_id(pg, b, page0 + lane, mapped);
+  }
   float* srow = scores ? scores + static_cast<size_t>(r) * N_cap : nullptr;
   float* brow = block_max ? block_max + static_cast<size_t>(r) * ((N_cap + 7) >> 3) : nullptr;
 
@@ -114,6 +124,12 @@ __global__ __launch_bounds__(kThreads) void k_index_scan(
   auto issue = [&](int slot, int tile) {
     const int rows = N_cap - 32 * tile;           // rows of this tile inside the buffer
     const uint8_t* base = kb + static_cast<size_t>(32) * tile * TT::kRowBytes;
+    if (paged) {
+      const int e = 32 * tile;
+      const int pid = __shfl(my_page, (e >> pg.log2p) - page0, 64);
+      base = k_idx + ((static_cast<size_t>(pid) << pg.log2p) + (e & ((1 << pg.log2p) - 1))) *
+                         TT::kRowBytes;
+    }
 #pragma unroll
     for (int i = 0; i < TT::kLoads; ++i) {
       const uint8_t* src = base + (grow[i] < rows ? goff[i] : 0);
@@ -165,8 +181,8 @@ int pick_tiles_per_wg(long long total_tiles, int min_tiles, int target_wgs, int 
 }  // namespace
 
 hipError_t launch_index_score(const uint16_t* q_idx, const float* w_idx, const void* k_idx,
-                              bool fp8, const int32_t* vis_len, int B, int n_q, int N_cap,
-                              float* scores, float* block_max, hipStream_t stream) {
+                              bool fp8, const Pages& pg, const int32_t* vis_len, int B, int n_q,
+                              int N_cap, float* scores, float* block_max, hipStream_t stream) {
   const int tiles = (N_cap + 31) / 32;
   const uint8_t* kb = static_cast<const uint8_t*>(k_idx);
   if (n_q < 16) {
@@ -177,7 +193,7 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w_idx, const v
   do {                                                                                         \
     dim3 grid((tiles + tpw - 1) / tpw, rows);                                                  \
     hipLaunchKernelGGL((k_index_scan<F, D, O>), grid, dim3(kThreads), 0, stream, q_idx, w_idx, \
-                       kb, vis_len, n_q, N_cap, tpw, scores, block_max);                       \
+                       kb, pg, vis_len, n_q, N_cap, tpw, scores, block_max);                   \
   } while (0)
     switch ((fp8 ? 4 : 0) | out) {
       case 1: CSA2_SCAN_LAUNCH(false, 1, 1); break;
@@ -190,8 +206,8 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w_idx, const v
     }
 #undef CSA2_SCAN_LAUNCH
   } else {
-    return launch_index_gemm(q_idx, w_idx, kb, fp8, vis_len, B, n_q, N_cap, scores, block_max,
-                             stream);
+    return launch_index_gemm(q_idx, w_idx, kb, fp8, pg, vis_len, B, n_q, N_cap, scores,
+                             block_max, stream);
   }
   return hipGetLastError();
 }

@@ -157,7 +157,8 @@ __device__ __forceinline__ void put_main_e4m3(const u32x4& w, int lane, size_t r
 template <int FMT>
 __global__ __launch_bounds__(64 * kWaves) void k_kv_append(
     const uint16_t* __restrict__ kv_new, const uint16_t* __restrict__ swa_new,
-    const int32_t* __restrict__ pos, int B, int n_new, int N_cap, uint8_t* __restrict__ kv_fp4,
+    const int32_t* __restrict__ pos, int B, int n_new, int N_cap, Pages pg,
+    uint8_t* __restrict__ kv_fp4,
     uint8_t* __restrict__ kv_scale, uint8_t* __restrict__ swa, int S_cap,
     const int32_t* __restrict__ swa_pos0) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -192,7 +193,9 @@ __global__ __launch_bounds__(64 * kWaves) void k_kv_append(
     if (g0 + e >= total) break;
     const long long p = static_cast<long long>(pos[bs[e]]) + is[e];
     if (p < 0 || p >= N_cap) continue;
-    const size_t row = static_cast<size_t>(bs[e]) * N_cap + static_cast<size_t>(p);
+    bool mapped;
+    const size_t row = pool_row(pg, bs[e], N_cap, static_cast<int>(p), mapped);
+    if (!mapped) continue;   // an unmapped page: the entry is skipped
     if (FMT == kFmtE8M0) put_main(w[e], lane, row, kv_fp4, kv_scale);
     else put_main_e4m3(w[e], lane, row, kv_fp4, kv_scale);
   }
@@ -224,7 +227,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_kv_append(
 }  // namespace
 
 hipError_t launch_kv_append(const uint16_t* kv_new, const uint16_t* swa_new, const int32_t* pos,
-                            int B, int n_new, int N_cap, int kv_fmt, uint8_t* kv_fp4,
+                            int B, int n_new, int N_cap, int kv_fmt, const Pages& pg,
+                            uint8_t* kv_fp4,
                             uint8_t* kv_scale, uint8_t* swa, int S_cap, const int32_t* swa_pos0,
                             hipStream_t stream) {
   const long long waves = (static_cast<long long>(B) * n_new + kPer - 1) / kPer;
@@ -233,11 +237,11 @@ hipError_t launch_kv_append(const uint16_t* kv_new, const uint16_t* swa_new, con
   if (wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (kv_fmt == kFmtE8M0)
     hipLaunchKernelGGL(k_kv_append<kFmtE8M0>, dim3(static_cast<unsigned>(wgs)), dim3(64 * kWaves),
-                       0, stream, kv_new, swa_new, pos, B, n_new, N_cap, kv_fp4, kv_scale, swa,
+                       0, stream, kv_new, swa_new, pos, B, n_new, N_cap, pg, kv_fp4, kv_scale, swa,
                        S_cap, swa_pos0);
   else
     hipLaunchKernelGGL(k_kv_append<kFmtE4M3>, dim3(static_cast<unsigned>(wgs)), dim3(64 * kWaves),
-                       0, stream, kv_new, swa_new, pos, B, n_new, N_cap, kv_fp4, kv_scale, swa,
+                       0, stream, kv_new, swa_new, pos, B, n_new, N_cap, pg, kv_fp4, kv_scale, swa,
                        S_cap, swa_pos0);
   return hipGetLastError();
 }

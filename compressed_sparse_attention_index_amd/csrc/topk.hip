@@ -382,6 +382,7 @@ struct PoolArgs {
   const uint16_t* q_idx;
   const float* w_idx;
   const uint8_t* k_idx;
+  Pages pg;                  // indexer-K page table (pg.bt == nullptr: contiguous)
   const int32_t* pool;       // [rows, kb]
   const int32_t* vis_len;
   int kb, n_q, N_cap, top_k;
@@ -410,7 +411,6 @@ __global__ __launch_bounds__(kPscThreads) void k_pool_score(PoolArgs a) {
   load_query(qa, a.q_idx + static_cast<size_t>(r) * kIdxHeads * kIdxDim, col, half);
   load_weights(wr, a.w_idx + static_cast<size_t>(r) * kIdxHeads, half);
   const int b = r / a.n_q;
-  const uint8_t* kbase = a.k_idx + static_cast<size_t>(b) * a.N_cap * (FP8 ? 128 : 256);
   // Tiles of 32 slots (4 pool blocks each); wave w takes tiles w and w + 4.
   const int slot0 = blockIdx.x * kPsSlots;
   KeyTile<FP8> kt[2];
@@ -421,7 +421,9 @@ __global__ __launch_bounds__(kPscThreads) void k_pool_score(PoolArgs a) {
     slot[u] = slot0 + 32 * (wave + kPscWaves * u) + col;
     valid[u] = slot[u] < nslots && pool_slot_valid(prow, slot[u], nb_cap, vis);
     const int pos = valid[u] ? prow[slot[u] >> 3] * kBlock + (col & 7) : 0;
-    load_key_half<FP8>(kt[u], kbase + static_cast<size_t>(pos) * (FP8 ? 128 : 256), half);
+    bool mapped;
+    const size_t row = pool_row(a.pg, b, a.N_cap, pos, mapped);
+    load_key_half<FP8>(kt[u], a.k_idx + row * (FP8 ? 128 : 256), half);
   }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -1072,7 +1074,8 @@ hipError_t launch_block_topk_noalloc(const float* block_max, const int32_t* vis_
 }
 
 hipError_t launch_pool_topk(int mode, const float* scores, const uint16_t* q_idx,
-                            const float* w_idx, const void* k_idx, const int32_t* pool_blocks,
+                            const float* w_idx, const void* k_idx, const Pages& pg,
+                            const int32_t* pool_blocks,
                             int k_blocks, const int32_t* vis_len, int rows, int n_q, int N_cap,
                             int top_k, int32_t* out, float* out_key, void* ws,
                             hipStream_t stream) {
@@ -1081,6 +1084,7 @@ hipError_t launch_pool_topk(int mode, const float* scores, const uint16_t* q_idx
   a.q_idx = q_idx;
   a.w_idx = w_idx;
   a.k_idx = static_cast<const uint8_t*>(k_idx);
+  a.pg = pg;
   a.pool = pool_blocks;
   a.vis_len = vis_len;
   a.kb = k_blocks;

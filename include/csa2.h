@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 4
+#define CSA2_ABI_VERSION 5
 
 /* Symbols of the C ABI; everything else in the library is hidden. */
 #define CSA2_API __attribute__((visibility("default")))
@@ -113,8 +113,39 @@ typedef enum {
   CSA2_OP_SPARSE_ATTN = 3
 } csa2_op;
 
+/*
+ * Paged caches.  The DeepSeek-V4 essay (mlqm.cn, §7.1) keeps the compressed
+ * KV and the indexer K of every request in a paged cache (the sliding-window
+ * KV stays in a per-request state cache).  A main-KV or indexer-K argument
+ * with paging points to a pool of num_pages pages of page_entries
+ * consecutive entries each (pool arrays [num_pages * page_entries, ...]).
+ * Entry e of sequence b lives in pool row
+ *   block_table[b * max_pages + e / page_entries] * page_entries + e % page_entries
+ * and the sequence's logical capacity is N_cap = max_pages * page_entries
+ * (a call's N_cap must equal it).  Rows never straddle pages, so every
+ * kernel reads whole tiles from one page.
+ *   block_table  [B, max_pages] int32 device memory: physical page of each
+ *                logical page, or -1 (unmapped)
+ *   page_entries a power of two, 64 .. 65536
+ *   max_pages    >= 1
+ *   num_pages    >= 1, num_pages * page_entries <= 2^31 - 1
+ * Every page holding an entry that a call reads (a visible position of the
+ * scan or pool re-scoring) must be mapped: an id outside [0, num_pages) is
+ * clamped into it for addressing (nothing is read out of bounds) and the
+ * results that depend on it are unspecified.  Attention treats a selected
+ * id on an unmapped page as an empty slot; the KV append skips entries whose
+ * page is unmapped.  NULL paging = contiguous [B, N_cap, ...] arrays.
+ */
+typedef struct {
+  const int32_t* block_table;
+  int32_t page_entries;
+  int32_t max_pages;
+  int32_t num_pages;
+} csa2_paging;
+
 /* Bits of csa2_attn_opts.flags. */
-#define CSA2_ATTN_SINK 1u  /* opts->sink is read (per-head sink logits) */
+#define CSA2_ATTN_SINK 1u   /* opts->sink is read (per-head sink logits) */
+#define CSA2_ATTN_PAGED 2u  /* opts->paging is read: kv_fp4 / kv_scale are page pools */
 
 /* Options of the attention entry points; NULL means the defaults.  The
    first four fields have the layout of ABI 1, whose last field (then
@@ -130,6 +161,8 @@ typedef struct {
   uint32_t flags;        /* CSA2_ATTN_* bits; other bits must be 0 */
   const float* sink;     /* with CSA2_ATTN_SINK: [64] fp32 per-head sink logits (device
                             memory), see csa2_sparse_attn_decode; otherwise not read */
+  const csa2_paging* paging;  /* with CSA2_ATTN_PAGED: the main-KV page table (host
+                                 memory, read during the call); otherwise not read */
 } csa2_attn_opts;
 
 /*
@@ -145,7 +178,8 @@ typedef struct {
  * Arguments
  *   q_idx     [B, n_q, 32, 128] bf16 indexer queries
  *   w_idx     [B, n_q, 32] fp32 per-head weights
- *   k_idx     [B, N_cap, 128] indexer keys of dtype k_dtype
+ *   k_idx     [B, N_cap, 128] indexer keys of dtype k_dtype, or a page pool
+ *   paging    NULL, or the page table of k_idx (see csa2_paging)
  *   vis_len   [B, n_q] int32 visible entries per query row
  *   scores    [B, n_q, N_cap] fp32 output or NULL; entries t >= vis_len are not written
  *   block_max [B, n_q, ceil(N_cap/8)] fp32 output or NULL; blocks past the
@@ -153,7 +187,8 @@ typedef struct {
  *   ws        unused (may be NULL; csa2_workspace_size returns 0)
  */
 CSA2_API csa2_status csa2_index_score(const uint16_t* q_idx, const float* w_idx, const void* k_idx,
-                             csa2_kdtype k_dtype, const int32_t* vis_len, int32_t B, int32_t n_q,
+                             csa2_kdtype k_dtype, const csa2_paging* paging,
+                             const int32_t* vis_len, int32_t B, int32_t n_q,
                              int32_t N_cap, float* scores, float* block_max, void* ws,
                              size_t ws_bytes, hipStream_t stream);
 
@@ -225,8 +260,8 @@ CSA2_API csa2_status csa2_block_topk_noalloc(const float* block_max, const int32
  *   returns CSA2_ERR_UNSUPPORTED.
  * Arguments
  *   scores      [B, n_q, N_cap] fp32 or NULL (see above)
- *   q_idx, w_idx, k_idx, k_dtype  as for csa2_index_score (may be NULL when
- *               the keys come from scores)
+ *   q_idx, w_idx, k_idx, k_dtype, paging  as for csa2_index_score (may be
+ *               NULL when the keys come from scores)
  *   pool_blocks [B, n_q, k_blocks] int32 ascending block ids, -1 padded, or NULL
  *   vis_len     [B, n_q] int32
  *   top_k       1..512
@@ -238,7 +273,8 @@ CSA2_API csa2_status csa2_block_topk_noalloc(const float* block_max, const int32
  */
 CSA2_API csa2_status csa2_reindex_topk(csa2_mode mode, const float* scores, const uint16_t* q_idx,
                               const float* w_idx, const void* k_idx, csa2_kdtype k_dtype,
-                              const int32_t* pool_blocks, int32_t k_blocks,
+                              const csa2_paging* paging, const int32_t* pool_blocks,
+                              int32_t k_blocks,
                               const int32_t* vis_len, int32_t B, int32_t n_q, int32_t N_cap,
                               int32_t top_k, int32_t* idx_out, float* idx_score, void* ws,
                               size_t ws_bytes, hipStream_t stream);
@@ -270,14 +306,15 @@ CSA2_API csa2_status csa2_reindex_topk(csa2_mode mode, const float* scores, cons
  *   with fp32 accumulation and an fp32 online softmax; out is rounded to bf16.
  * Arguments
  *   q         [B, n_q, 64, 512] bf16
- *   kv_fp4    [B, N_cap, 256] uint8 packed E2M1
- *   kv_scale  [B, N_cap, 16] uint8 E8M0, or [B, N_cap, 32] uint8 E4M3FN
+ *   kv_fp4    [B, N_cap, 256] uint8 packed E2M1 (or a page pool, opts->paging)
+ *   kv_scale  [B, N_cap, 16] uint8 E8M0, or [B, N_cap, 32] uint8 E4M3FN (same
+ *             paging as kv_fp4)
  *   idx       [B, n_q, top_k] int32 entry indices, -1 = empty slot; top_k 0..512
  *   swa_kv    [B, S_cap, 512] uint8 FP8 E4M3FN; slot i holds token swa_pos0[b] + i
  *   swa_pos0  [B] int32
  *   q_pos     [B, n_q] int32 token position of each query
  *   sm_scale  softmax scale, finite and > 0 (else CSA2_ERR_SHAPE)
- *   opts      NULL or options (window, replay_start, kv_fmt, sink)
+ *   opts      NULL or options (window, replay_start, kv_fmt, sink, paging)
  *   out       [B, n_q, 64, 512] bf16 output
  *   lse       [B, n_q, 64] fp32 output or NULL
  *   ws        csa2_workspace_size(CSA2_OP_SPARSE_ATTN, ...) bytes
@@ -332,6 +369,8 @@ CSA2_API csa2_status csa2_reuse_attn(const uint16_t* q, const uint8_t* kv_fp4, c
  *   swa_new   [B, n_new, 512] bf16 window entries, or NULL (no window writes)
  *   pos       [B] int32 position of each sequence's first new token
  *   kv_fmt    csa2_kvfmt of the main cache (else CSA2_ERR_UNSUPPORTED)
+ *   paging    NULL, or the page table of kv_fp4 / kv_scale (see csa2_paging);
+ *             the window cache is never paged
  *   kv_fp4    [B, N_cap, 256] uint8, kv_scale [B, N_cap, 16] (E8M0) or
  *             [B, N_cap, 32] (E4M3FN) uint8 (written)
  *   swa_kv    [B, S_cap, 512] uint8 (written; may be NULL when swa_new is)
@@ -339,7 +378,8 @@ CSA2_API csa2_status csa2_reuse_attn(const uint16_t* q, const uint8_t* kv_fp4, c
  */
 CSA2_API csa2_status csa2_kv_append(const uint16_t* kv_new, const uint16_t* swa_new,
                            const int32_t* pos, int32_t B, int32_t n_new, int32_t N_cap,
-                           int32_t kv_fmt, uint8_t* kv_fp4, uint8_t* kv_scale,
+                           int32_t kv_fmt, const csa2_paging* paging, uint8_t* kv_fp4,
+                           uint8_t* kv_scale,
                            uint8_t* swa_kv, int32_t S_cap, const int32_t* swa_pos0,
                            hipStream_t stream);
 

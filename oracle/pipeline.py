@@ -134,3 +134,26 @@ def kv_append(kv_fp4, kv_scale, swa, kv_new_bits, swa_new_bits, pos, swa_pos0,
                 if 0 <= j < swa.shape[1]:
                     swa[b, j] = formats.f64_to_e4m3(formats.bf16_to_f64(swa_new_bits[b, i]))
     return kv_fp4, kv_scale, swa
+
+
+def unpage(pool, block_table, page_entries):
+    """Logical view of a paged cache: [B, max_pages * page_entries, ...] from
+    a pool [num_pages * page_entries, ...] and block_table [B, max_pages]
+    (DeepSeek-V4 essay §7.1: compressed KV and indexer K live in a paged
+    cache; entry e of sequence b is row block_table[b][e // P] * P + e % P
+    of the pool).  Entries on unmapped pages (ids < 0 or >= num_pages) are
+    marked False in `mapped` and their rows are zeros."""
+    pool = np.asarray(pool)
+    bt = np.asarray(block_table, dtype=np.int64)
+    P = int(page_entries)
+    num_pages = pool.shape[0] // P
+    B, max_pages = bt.shape
+    out = np.zeros((B, max_pages * P) + pool.shape[1:], dtype=pool.dtype)
+    mapped = np.zeros((B, max_pages * P), dtype=bool)
+    for b in range(B):
+        for j in range(max_pages):
+            page = bt[b, j]
+            if 0 <= page < num_pages:
+                out[b, j * P:(j + 1) * P] = pool[page * P:(page + 1) * P]
+                mapped[b, j * P:(j + 1) * P] = True
+    return out, mapped

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.csa2_abi_version() == 4
+    assert L.csa2_abi_version() == 5
     for st in range(7):
         assert len(L.csa2_status_string(st)) > 0
     assert L.csa2_status_string(0) == b"ok"
@@ -50,8 +50,13 @@ A = 1 << 20      # a fake, 16-byte aligned "device" address: never dereferenced
 MIS = A + 4      # misaligned
 
 
-def _score(L, q=A, w=A, k=A, kd=1, vis=A, B=1, n_q=1, N=64, sc=A, bm=A):
-    return L.csa2_index_score(q, w, k, kd, vis, B, n_q, N, sc, bm, None, 0, None)
+def _score(L, q=A, w=A, k=A, kd=1, vis=A, B=1, n_q=1, N=64, sc=A, bm=A, pg=None):
+    return L.csa2_index_score(q, w, k, kd, pg, vis, B, n_q, N, sc, bm, None, 0, None)
+
+
+def _pg(bt=A, P=64, max_pages=1, num_pages=1):
+    import compressed_sparse_attention_index_amd as csa
+    return ctypes.byref(csa.PagingStruct(bt, P, max_pages, num_pages))
 
 
 def test_index_score_validation(L):
@@ -63,6 +68,33 @@ def test_index_score_validation(L):
     assert _score(L, N=(1 << 22) + 1) == 2
     assert _score(L, B=70000) == 2
     assert _score(L, k=MIS) == 5
+
+
+def test_paging_validation(L):
+    # The page table is checked on the host before anything is enqueued:
+    # N_cap must be max_pages * page_entries, page_entries a power of two in
+    # [64, 65536], the pool addressable with 31-bit rows.
+    assert _score(L, N=128, pg=_pg(max_pages=2, num_pages=4)) != 2   # valid: fails later (no GPU)
+    assert _score(L, N=128, pg=_pg(bt=None, max_pages=2)) == 1
+    assert _score(L, N=128, pg=_pg(bt=MIS, max_pages=2)) == 5
+    assert _score(L, N=128, pg=_pg(max_pages=1)) == 2                # 64 != 128
+    assert _score(L, N=96, pg=_pg(P=48, max_pages=2)) == 2           # not a power of two
+    assert _score(L, N=64, pg=_pg(P=32, max_pages=2)) == 2           # below 64 entries
+    assert _score(L, N=128, pg=_pg(max_pages=2, num_pages=0)) == 2
+    assert _score(L, N=1 << 16, pg=_pg(P=1 << 16, num_pages=1 << 15)) == 2   # 2^31 rows
+    assert _reindex(L, N=128, kb=16, pg=_pg(max_pages=1)) == 2
+    f = L.csa2_kv_append
+    assert f(A, None, A, 1, 1, 128, 0, _pg(max_pages=1), A, A, None, 0, None, None) == 2
+    import compressed_sparse_attention_index_amd as csa
+    for fn in ("csa2_sparse_attn_decode", "csa2_reuse_attn"):
+        paged = csa.AttnOpts(128, -1, 0, csa.ATTN_PAGED, None, None)
+        assert _attn(L, fn, opts=ctypes.byref(paged)) == 1          # flag without a table
+        bad = csa.PagingStruct(A, 64, 1, 1)
+        paged = csa.AttnOpts(128, -1, 0, csa.ATTN_PAGED, None, ctypes.pointer(bad))
+        assert _attn(L, fn, opts=ctypes.byref(paged)) == 2          # 64 != N_cap
+        ok = csa.PagingStruct(A, 1024, 128, 4096)
+        paged = csa.AttnOpts(128, -1, 0, csa.ATTN_PAGED, None, ctypes.pointer(ok))
+        assert _attn(L, fn, opts=ctypes.byref(paged), out=MIS) == 5   # accepted up to alignment
 
 
 def test_block_topk_validation(L):
@@ -90,9 +122,9 @@ def test_block_topk_noalloc_validation(L):
 
 
 def _reindex(L, mode=1, sc=None, q=A, w=A, k=A, kd=1, pool=A, kb=2048, vis=A, B=1, n_q=1, N=1 << 20,
-             top_k=512, out=A, ws=None, ws_bytes=0):
-    return L.csa2_reindex_topk(mode, sc, q, w, k, kd, pool, kb, vis, B, n_q, N, top_k, out, None,
-                               ws, ws_bytes, None)
+             top_k=512, out=A, ws=None, ws_bytes=0, pg=None):
+    return L.csa2_reindex_topk(mode, sc, q, w, k, kd, pg, pool, kb, vis, B, n_q, N, top_k, out,
+                               None, ws, ws_bytes, None)
 
 
 def test_reindex_topk_validation(L):
@@ -142,7 +174,7 @@ def test_attention_validation(L):
         assert _attn(L, fn, opts=ctypes.byref(bad_sink)) == 5
         null_sink = csa.AttnOpts(128, -1, 0, csa.ATTN_SINK, None)
         assert _attn(L, fn, opts=ctypes.byref(null_sink)) == 1
-        bad_flag = csa.AttnOpts(128, -1, 0, 2, None)
+        bad_flag = csa.AttnOpts(128, -1, 0, 4, None)
         assert _attn(L, fn, opts=ctypes.byref(bad_flag)) == 3
         # Without the sink flag the pointer is not read: an ABI-1 caller's
         # 16-byte struct (no pointer field) passes validation up to the
@@ -166,7 +198,7 @@ def test_binding_refuses_cpu_tensors(L):
 def test_kv_append_validation(L):
     f = L.csa2_kv_append
     def call(kv=A, swn=None, pos=A, B=1, n=1, N=64, fmt=0, fp4=A, sc=A, swa=None, S=0, p0=None):
-        return f(kv, swn, pos, B, n, N, fmt, fp4, sc, swa, S, p0, None)
+        return f(kv, swn, pos, B, n, N, fmt, None, fp4, sc, swa, S, p0, None)
     assert call(kv=None) == 1
     assert call(fmt=2) == 3
     assert call(fmt=-1) == 3

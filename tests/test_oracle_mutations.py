@@ -241,6 +241,23 @@ def _kv_append_variant(window_shift=0, wrap_main=False, wrap_window=False):
     return fn
 
 
+def _unpage_variant():
+    # Mistake: page j of a sequence read from pool row j * P instead of its
+    # table entry's page (the table ignored).
+    def unpage(pool, block_table, page_entries):
+        pool = np.asarray(pool)
+        bt = np.asarray(block_table)
+        P = int(page_entries)
+        B, max_pages = bt.shape
+        out = np.zeros((B, max_pages * P) + pool.shape[1:], dtype=pool.dtype)
+        for b in range(B):
+            for j in range(max_pages):
+                if (j + 1) * P <= pool.shape[0]:
+                    out[b, j * P:(j + 1) * P] = pool[j * P:(j + 1) * P]
+        return out, np.ones((B, max_pages * P), bool)
+    return unpage
+
+
 def _attention_variant(slot_shift=0, keep_empty=False):
     def fn(q_raw, kv_fp4, kv_scale, idx, swa_raw, swa_pos0, q_pos, sm_scale, window=128,
            replay_start=-1, sink=None):
@@ -291,6 +308,8 @@ MUTATIONS = [
      _attention_variant(slot_shift=-1)),
     ("attention empty slots kept", pp.pin_attention, pipeline.attention,
      _attention_variant(keep_empty=True)),
+    ("unpage with the page index as the row offset", pp.pin_unpage, pipeline.unpage,
+     _unpage_variant()),
 ]
 
 

@@ -318,3 +318,34 @@ def test_decode_main_kv_e4m3_layout():
     s = torch.from_numpy(sc).view(torch.float8_e4m3fn).double().repeat_interleave(16, -1)
     np.testing.assert_array_equal(pipeline.decode_main_kv(fp4, sc, "e4m3_16"),
                                   (table[nib] * s).numpy())
+
+
+def pin_unpage(fn):
+    """The logical view of a paged cache: a hand-written two-sequence example
+    (rows named by value), and scattering a contiguous cache into shuffled
+    pages (with spare pages) then reading it back."""
+    P = 2
+    pool = np.arange(5 * P * 3, dtype=np.int32).reshape(5 * P, 3)   # 5 pages of 2 rows
+    bt = np.array([[3, 0, -1], [4, 7, 1]])      # page 7 is out of range: unmapped
+    view, mapped = fn(pool, bt, P)
+    want = np.zeros((2, 6, 3), np.int32)
+    want[0, 0:2] = pool[6:8]
+    want[0, 2:4] = pool[0:2]
+    want[1, 0:2] = pool[8:10]
+    want[1, 4:6] = pool[2:4]
+    ok = np.array_equal(view, want)
+    ok &= np.array_equal(mapped, np.array([[1, 1, 1, 1, 0, 0], [1, 1, 0, 0, 1, 1]], bool))
+    rng = np.random.default_rng(5)
+    B, max_pages, P, spare = 3, 4, 8, 5
+    x = rng.integers(0, 255, size=(B, max_pages * P, 16), dtype=np.uint8)
+    perm = rng.permutation(B * max_pages + spare)[:B * max_pages].reshape(B, max_pages)
+    pool = np.zeros(((B * max_pages + spare) * P, 16), np.uint8)
+    for b in range(B):
+        for j in range(max_pages):
+            pool[perm[b, j] * P:(perm[b, j] + 1) * P] = x[b, j * P:(j + 1) * P]
+    view, mapped = fn(pool, perm, P)
+    return bool(ok and np.array_equal(view, x) and mapped.all())
+
+
+def test_unpage_logical_view():
+    assert pin_unpage(pipeline.unpage)
