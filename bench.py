@@ -48,7 +48,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="full_reindex_1m",
                    choices=["tiny_2k", "full_64k", "reuse_128k", "reuse_128k_e4m3",
-                            "full_reindex_1m", "prefill_128k", "kv_append_64k"])
+                            "full_reindex_1m", "prefill_128k", "kv_append_64k", "decoder_1m"])
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU time budget of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -84,6 +84,7 @@ ROTATED = {
     "full_reindex_1m": (),
     "prefill_128k": (),
     "kv_append_64k": ("kv_new", "swa_new"),
+    "decoder_1m": (),
 }
 CACHE_BYTES = 256 << 20        # MI355X last-level (Infinity) cache
 
@@ -134,6 +135,13 @@ class Step:
         if name == "kv_append_64k":
             self.rows = B * d["n_new"]   # tokens appended per step
             return
+        if name == "decoder_1m":
+            # The decoder's 20 layers through the layer driver.
+            self.state = csa.LayerState(B, n_q, self.N, k_blocks=2048, top_k=512)
+            self.out = torch.empty(B, n_q, 64, 512, dtype=torch.int16, device=dev)
+            self.lse = torch.empty(B, n_q, 64, dtype=torch.float32, device=dev)
+            self.bm = torch.empty(B, n_q, (self.N + 7) // 8, dtype=torch.float32, device=dev)
+            return
         z = lambda *s, dt=torch.int32: torch.empty(*s, dtype=dt, device=dev)
         self.out = z(B, n_q, 64, 512, dt=torch.int16)
         self.lse = z(B, n_q, 64, dt=torch.float32)
@@ -172,7 +180,11 @@ class Step:
 
     def dominant(self):
         """Launch only the kernel the roofline figure is about."""
-        if self.name == "kv_append_64k":
+        if self.name == "decoder_1m":
+            d = self._next()
+            self.csa.index_score(d["layers"][0]["q_idx"], d["layers"][0]["w_idx"], d["k_idx"],
+                                 d["vis_len"], block_max=self.bm)
+        elif self.name == "kv_append_64k":
             self.run()
         elif self.name.startswith("reuse_128k"):
             d = self._next()
@@ -187,6 +199,14 @@ class Step:
 
     def run(self):
         d, csa = self._next(), self.csa
+        if self.name == "decoder_1m":
+            self.state.struct.has_pool = self.state.struct.has_idx = 0
+            for e in d["layers"]:
+                csa.run_layer(csa.layer_mode(e["layer"]), self.state, d["k_idx"], d["kv_fp4"],
+                              d["kv_scale"], d["vis_len"], e["q"], e["swa"], d["swa_pos0"],
+                              d["q_pos"], d["sm_scale"], self.out, lse=self.lse,
+                              q_idx=e.get("q_idx"), w_idx=e.get("w_idx"))
+            return
         if self.name == "kv_append_64k":
             csa.kv_append(d["kv_new"], d["pos"], d["kv_fp4"], d["kv_scale"], swa_new=d["swa_new"],
                           swa_kv=d["swa"], swa_pos0=d["swa_pos0"])
@@ -230,6 +250,13 @@ def algorithmic(name, d):
     T = d["k_idx"].shape[1]
     krow = 128 if d["kdtype"] == "fp8" else 256
     nb = (T + 7) // 8
+    if name == "decoder_1m":
+        # One scan (Full layer 20), four pool re-scores (Reindex layers), 20
+        # attention calls.
+        scan = B * (T * krow + 32 * 128 * 2 + 32 * 4 + nb * 4)
+        step = (B * (T * krow + 32 * 128 * 2 + 32 * 4) + 4 * B * (16384 * krow + 32 * 128 * 2 + 32 * 4)
+                + 20 * B * attn_bytes)
+        return "index_scan", scan, "hbm", step
     if name == "prefill_128k":
         vis = d["vis_len"].double().sum().item()
         flops = 2.0 * 32 * 128 * vis
@@ -283,7 +310,27 @@ def cpu_baseline(name, d, budget_s):
                 kr = kr.view(np.uint16)
         swa = npy(d["swa"][b])
         t0 = time.perf_counter()
-        if name.startswith("reuse_128k"):
+        if name == "decoder_1m":
+            # The 20 decoder layers of one row: Full, Reindex re-scoring its
+            # pool, and every layer's attention over the latest Top-k.
+            vis = int(d["vis_len"][b, j])
+            kvd = d["kv_fp4"].device
+            for e in d["layers"]:
+                mode = pipeline.layer_mode(e["layer"])
+                if mode == "full":
+                    full = pipeline.full_layer(npy(e["q_idx"][b, j]).view(np.uint16),
+                                               npy(e["w_idx"][b, j]), kr, kd, vis)
+                    idx = full["idx"]
+                elif mode == "reindex":
+                    idx = pipeline.reindex_layer(npy(e["q_idx"][b, j]).view(np.uint16),
+                                                 npy(e["w_idx"][b, j]), kr, kd, full["pool"],
+                                                 vis)["idx"]
+                sel = torch.from_numpy(idx[idx >= 0]).to(kvd)
+                pipeline.attention(npy(e["q"][b, j]).view(np.uint16), npy(d["kv_fp4"][b][sel]),
+                                   npy(d["kv_scale"][b][sel]), np.arange(len(sel)),
+                                   npy(e["swa"][b]), int(d["swa_pos0"][b]), int(d["q_pos"][b, j]),
+                                   d["sm_scale"])
+        elif name.startswith("reuse_128k"):
             idx = npy(d["idx"][b, j])
             fp4, sc = npy(d["kv_fp4"][b][d["idx"][b, j].long()]), npy(d["kv_scale"][b][d["idx"][b, j].long()])
             pipeline.attention(npy(d["q"][b, j]).view(np.uint16), fp4, sc, np.arange(len(idx)), swa,
@@ -447,7 +494,9 @@ def measure(name, args, torch, synth, csa, cpu=True, graph=True):
                "pool_blocks": None if reuse or name == "prefill_128k" else 2048, "window": 128,
                "layers": {"full_64k": "Full", "tiny_2k": "Full", "reuse_128k": "Reuse",
                           "reuse_128k_e4m3": "Reuse", "full_reindex_1m": "Full+Reindex",
-                          "prefill_128k": "prefill (m=2)"}[name],
+                          "prefill_128k": "prefill (m=2)",
+                          "decoder_1m": "decoder layers 20-39 (Full + 3 Reuse, "
+                                        "4 x (Reindex + 3 Reuse))"}[name],
                "main_kv": ("E2M1 + E4M3/16" if d.get("kv_fmt") == "e4m3_16"
                            else "MXFP4 (E2M1 + E8M0/32)")}
     cfg["input_sets"] = len(sets)

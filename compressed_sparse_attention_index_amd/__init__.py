@@ -17,11 +17,12 @@ __all__ = [
     "Csa2Error", "Paging", "lib", "abi_version", "workspace_size", "index_score", "block_topk",
     "block_topk_noalloc",
     "reindex_topk", "sparse_attn_decode", "reuse_attn", "kv_append",
+    "MODE_SWA", "layer_mode", "LayerState", "run_layer",
 ]
 
 KDTYPE_BF16, KDTYPE_FP8 = 0, 1
 KV_MXFP4_E8M0_32, KV_FP4_E4M3_16 = 0, 1   # main-KV scale formats (csa2_kvfmt)
-MODE_FULL, MODE_REINDEX, MODE_REUSE = 0, 1, 2
+MODE_FULL, MODE_REINDEX, MODE_REUSE, MODE_SWA = 0, 1, 2, 3
 OP_INDEX_SCORE, OP_BLOCK_TOPK, OP_REINDEX_TOPK, OP_SPARSE_ATTN = 0, 1, 2, 3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
@@ -42,11 +43,14 @@ _SIGNATURES = {
     "csa2_reuse_attn": [_P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _F, _P, _I, _I, _P, _P, _P, _S, _P],
     "csa2_kv_append": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P],
     "csa2_workspace_size": [_I, _I, _I, _I, _I, _I],
+    "csa2_layer_mode": [_I],
+    "csa2_layer_workspace_size": [_I, _I, _I, _I, _I],
+    "csa2_run_layer": [_I, _P, _P, _P, _P, _P],
     "csa2_status_string": [_I],
     "csa2_abi_version": [],
 }
 _RESTYPES = {"csa2_workspace_size": _S, "csa2_status_string": ctypes.c_char_p,
-             "csa2_abi_version": _I}
+             "csa2_abi_version": _I, "csa2_layer_workspace_size": _S}
 
 
 ATTN_SINK = 1    # csa2_attn_opts.flags bit: the sink pointer is read
@@ -256,3 +260,64 @@ def kv_append(kv_new, pos, kv_fp4, kv_scale, swa_new=None, swa_kv=None, swa_pos0
           _ptr(kv_fp4, _U8, "kv_fp4"),
           _ptr(kv_scale, _U8, "kv_scale"), _ptr(swa_kv, _U8, "swa_kv"), S_cap,
           _ptr(swa_pos0, _I32, "swa_pos0"), _stream(stream))
+
+
+class LayerArgs(ctypes.Structure):
+    """csa2_layer_args."""
+    _fields_ = [("k_idx", _P), ("k_dtype", _I), ("k_paging", ctypes.POINTER(PagingStruct)),
+                ("kv_fp4", _P), ("kv_scale", _P), ("kv_fmt", _I),
+                ("kv_paging", ctypes.POINTER(PagingStruct)), ("N_cap", _I), ("vis_len", _P),
+                ("q_idx", _P), ("w_idx", _P), ("q", _P), ("swa_kv", _P), ("S_cap", _I),
+                ("swa_pos0", _P), ("q_pos", _P), ("sm_scale", _F), ("window", _I),
+                ("replay_start", _I), ("sink", _P), ("B", _I), ("n_q", _I)]
+
+
+class LayerStateStruct(ctypes.Structure):
+    """csa2_layer_state."""
+    _fields_ = [("block_max", _P), ("scores", _P), ("pool_blocks", _P), ("k_blocks", _I),
+                ("idx", _P), ("top_k", _I), ("ws", _P), ("ws_bytes", _S), ("has_pool", _I),
+                ("has_idx", _I)]
+
+
+def layer_mode(layer):
+    """Mode of layer 0..39 in the model's schedule (-1 otherwise)."""
+    return lib().csa2_layer_mode(layer)
+
+
+class LayerState:
+    """Device buffers carried across layers (the pool and the Top-K indices)
+    for B x n_q query rows over N_cap entries."""
+
+    def __init__(self, B, n_q, N_cap, k_blocks=2048, top_k=512, device="cuda"):
+        z = lambda *shape, dt=torch.int32: torch.empty(*shape, dtype=dt, device=device)
+        self.prefill = n_q >= 16
+        self.block_max = None if self.prefill else z(B, n_q, (N_cap + 7) // 8, dt=torch.float32)
+        self.scores = z(B, n_q, N_cap, dt=torch.float32) if self.prefill else None
+        self.pool_blocks = z(B, n_q, k_blocks)
+        self.idx = z(B, n_q, top_k)
+        n = lib().csa2_layer_workspace_size(B, n_q, N_cap, k_blocks, top_k)
+        self.ws = torch.zeros(max(int(n), 16), dtype=torch.uint8, device=device)
+        self.struct = LayerStateStruct(
+            _ptr(self.block_max, _F32, "block_max"), _ptr(self.scores, _F32, "scores"),
+            _ptr(self.pool_blocks, _I32, "pool_blocks"), k_blocks, _ptr(self.idx, _I32, "idx"),
+            top_k, self.ws.data_ptr(), self.ws.numel(), 0, 0)
+
+
+def run_layer(mode, state, k_idx, kv_fp4, kv_scale, vis_len, q, swa_kv, swa_pos0, q_pos,
+              sm_scale, out, lse=None, q_idx=None, w_idx=None, kv_fmt=KV_MXFP4_E8M0_32,
+              window=128, replay_start=-1, sink=None, k_paging=None, kv_paging=None,
+              stream=None):
+    """One layer's CSA2 work by mode (include/csa2.h, csa2_run_layer)."""
+    B, n_q = q.shape[0], q.shape[1]
+    N_cap = kv_paging.n_cap if kv_paging is not None else kv_fp4.shape[1]
+    kd = KDTYPE_BF16 if k_idx.dtype in _BITS16 else KDTYPE_FP8
+    a = LayerArgs(_ptr(k_idx, _BITS16 + _U8, "k_idx"), kd,
+                  ctypes.pointer(k_paging.struct) if k_paging is not None else None,
+                  _ptr(kv_fp4, _U8, "kv_fp4"), _ptr(kv_scale, _U8, "kv_scale"), kv_fmt,
+                  ctypes.pointer(kv_paging.struct) if kv_paging is not None else None, N_cap,
+                  _ptr(vis_len, _I32, "vis_len"), _ptr(q_idx, _BITS16, "q_idx"),
+                  _ptr(w_idx, _F32, "w_idx"), _ptr(q, _BITS16, "q"), _ptr(swa_kv, _U8, "swa_kv"),
+                  swa_kv.shape[1], _ptr(swa_pos0, _I32, "swa_pos0"), _ptr(q_pos, _I32, "q_pos"),
+                  float(sm_scale), window, replay_start, _ptr(sink, _F32, "sink"), B, n_q)
+    _call("csa2_run_layer", mode, ctypes.byref(a), ctypes.byref(state.struct),
+          _ptr(out, _BITS16, "out"), _ptr(lse, _F32, "lse"), _stream(stream))

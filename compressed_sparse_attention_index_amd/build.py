@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["api.hip", "index_score.hip", "index_gemm.hip", "topk.hip", "attention.hip",
-           "attention_rows.hip", "kv_append.hip"]
+           "attention_rows.hip", "kv_append.hip", "driver.hip"]
 LIB = os.path.join(HERE, "libcsa2.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -266,6 +266,7 @@ const char* csa2_status_string(csa2_status status) {
     case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
     case CSA2_ERR_ALIGN: return "pointer not 16-byte aligned";
     case CSA2_ERR_HIP: return "HIP runtime or kernel launch error";
+    case CSA2_ERR_STATE: return "layer state lacks the pool or indices the mode reuses";
   }
   return "unknown status";
 }

@@ -76,7 +76,8 @@ typedef enum {
   CSA2_ERR_UNSUPPORTED = 3,  /* dtype, format, mode or option this build does not implement */
   CSA2_ERR_WORKSPACE = 4,    /* workspace missing or smaller than csa2_workspace_size() */
   CSA2_ERR_ALIGN = 5,        /* a pointer is not 16-byte aligned */
-  CSA2_ERR_HIP = 6           /* a HIP runtime call or kernel launch failed */
+  CSA2_ERR_HIP = 6,          /* a HIP runtime call or kernel launch failed */
+  CSA2_ERR_STATE = 7         /* csa2_run_layer: the layer state lacks what the mode reuses */
 } csa2_status;
 
 /* Storage type of the indexer keys. */
@@ -102,7 +103,8 @@ typedef enum {
 typedef enum {
   CSA2_MODE_FULL = 0,     /* own indexer Q/K and Top-K; builds the pool */
   CSA2_MODE_REINDEX = 1,  /* own indexer Q; re-scores only the pool against the Full layer's indexer K */
-  CSA2_MODE_REUSE = 2     /* no indexer; reuses the most recent Top-K indices */
+  CSA2_MODE_REUSE = 2,    /* no indexer; reuses the most recent Top-K indices */
+  CSA2_MODE_SWA = 3       /* sliding-window attention only (no global KV) */
 } csa2_mode;
 
 /* Operation ids for csa2_workspace_size(). */
@@ -382,6 +384,90 @@ CSA2_API csa2_status csa2_kv_append(const uint16_t* kv_new, const uint16_t* swa_
                            uint8_t* kv_scale,
                            uint8_t* swa_kv, int32_t S_cap, const int32_t* swa_pos0,
                            hipStream_t stream);
+
+/*
+ * Layer driver.  The model's 40 layers follow one static schedule
+ * ("DeepSeek-V4.1-Flash 架构详解", §3.1 and §1): layers 0 and 1 are pure
+ * sliding-window attention; the 18 other encoder layers (2..19, m = 2) form
+ * three groups of six, a Full layer then five Reuse layers; the 20 decoder
+ * layers (20..39, m = 1) form five groups of four, the first a Full layer
+ * and the others a Reindex layer, each followed by three Reuse layers.  A
+ * Reuse layer reuses the most recent Top-K indices, a Reindex layer the most
+ * recent pool, and every layer computes its own query and SWA KV (§3 mode
+ * table).  csa2_layer_mode gives a layer's mode; csa2_run_layer enqueues one
+ * layer's CSA2 work and carries the pool and the indices from layer to layer
+ * in a caller-owned state.
+ */
+
+/* Mode of layer `layer` (0..39) of the schedule; -1 for another index. */
+CSA2_API int32_t csa2_layer_mode(int32_t layer);
+
+/* Inputs of one layer: the shared caches (the indexer K and main KV, which
+   the Full layer's projections wrote) and this layer's own query and window. */
+typedef struct {
+  const void* k_idx;             /* indexer K, as for csa2_index_score */
+  csa2_kdtype k_dtype;
+  const csa2_paging* k_paging;   /* NULL: contiguous */
+  const uint8_t* kv_fp4;         /* main KV, as for csa2_sparse_attn_decode */
+  const uint8_t* kv_scale;
+  int32_t kv_fmt;                /* csa2_kvfmt */
+  const csa2_paging* kv_paging;  /* NULL: contiguous */
+  int32_t N_cap;
+  const int32_t* vis_len;        /* [B, n_q] visible entries per query row */
+  const uint16_t* q_idx;         /* [B, n_q, 32, 128] bf16: Full and Reindex layers */
+  const float* w_idx;            /* [B, n_q, 32] fp32: Full and Reindex layers */
+  const uint16_t* q;             /* [B, n_q, 64, 512] bf16 */
+  const uint8_t* swa_kv;         /* [B, S_cap, 512] FP8, this layer's window */
+  int32_t S_cap;
+  const int32_t* swa_pos0;       /* [B] */
+  const int32_t* q_pos;          /* [B, n_q] */
+  float sm_scale;
+  int32_t window;                /* 0..128 */
+  int32_t replay_start;          /* -1: none */
+  const float* sink;             /* [64] per-head sink logits, or NULL */
+  int32_t B, n_q;
+} csa2_layer_args;
+
+/* State carried across layers: device buffers owned by the caller, sized
+   for the largest layer.  The driver sets has_pool / has_idx (host fields)
+   when it enqueues the work that fills them; a caller starts with both 0. */
+typedef struct {
+  float* block_max;      /* [B, n_q, ceil(N_cap/8)] (decode rows: n_q < 16) */
+  float* scores;         /* [B, n_q, N_cap] (prefill-shaped rows: n_q >= 16) or NULL */
+  int32_t* pool_blocks;  /* [B, n_q, k_blocks] */
+  int32_t k_blocks;      /* 1..2048 (2048 in the model) */
+  int32_t* idx;          /* [B, n_q, top_k] */
+  int32_t top_k;         /* 1..512 (512 in the model) */
+  void* ws;              /* csa2_layer_workspace_size(...) bytes, zero-filled once */
+  size_t ws_bytes;
+  int32_t has_pool;
+  int32_t has_idx;
+} csa2_layer_state;
+
+/*
+ * csa2_run_layer -- one layer's CSA2 work, by mode:
+ *   CSA2_MODE_FULL     decode rows (n_q < 16): scan with block maxima,
+ *                      block Top-K (pool), Top-k re-scored in the pool;
+ *                      prefill-shaped rows (n_q >= 16): scan with scores,
+ *                      flat Top-k (no pool; state->scores required); then
+ *                      attention.  Sets has_idx (and has_pool for decode rows).
+ *   CSA2_MODE_REINDEX  re-scores the state's pool with this layer's q_idx /
+ *                      w_idx, Top-k, attention (needs has_pool).
+ *   CSA2_MODE_REUSE    attention over the state's indices (needs has_idx).
+ *   CSA2_MODE_SWA      attention over the window only.
+ * Returns CSA2_ERR_STATE when the state lacks what the mode reuses; other
+ * errors as for the calls it makes (nothing of a failed call is enqueued,
+ * but earlier calls of the same layer may have been).
+ *   out, lse   as for csa2_sparse_attn_decode
+ */
+CSA2_API csa2_status csa2_run_layer(csa2_mode mode, const csa2_layer_args* args,
+                                    csa2_layer_state* state, uint16_t* out, float* lse,
+                                    hipStream_t stream);
+
+/* Workspace bytes of csa2_run_layer for the given sizes (the largest of the
+   calls it makes); (size_t)-1 for invalid sizes. */
+CSA2_API size_t csa2_layer_workspace_size(int32_t B, int32_t n_q, int32_t N_cap, int32_t k_blocks,
+                                          int32_t top_k);
 
 /* Workspace bytes an operation needs for the given sizes (0 if none);
    returns (size_t)-1 for an unknown op or invalid sizes. */

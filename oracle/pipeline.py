@@ -157,3 +157,22 @@ def unpage(pool, block_table, page_entries):
                 out[b, j * P:(j + 1) * P] = pool[page * P:(page + 1) * P]
                 mapped[b, j * P:(j + 1) * P] = True
     return out, mapped
+
+
+def layer_mode(layer):
+    """Mode of layer `layer` of the 40-layer model ([架构详解 §1]): layers
+    0-19 are the causal encoder, 20-39 the decoder; only the encoder's first
+    two layers are pure sliding-window attention ("swa"); its other 18 form
+    three groups of six, each a Full layer then five Reuse layers; the
+    decoder's 20 form five groups of four, the first Full + three Reuse, the
+    other four Reindex + three Reuse.  None outside 0..39."""
+    if not 0 <= layer < 40:
+        return None
+    if layer < 2:
+        return "swa"
+    if layer < 20:
+        return "full" if (layer - 2) % 6 == 0 else "reuse"
+    group, first = divmod(layer - 20, 4)
+    if first:
+        return "reuse"
+    return "full" if group == 0 else "reindex"

@@ -198,6 +198,25 @@ def decode_workload(B, T, kdtype="fp8", seed=0, device="cpu", heavy_frac=0.0,
     return d
 
 
+def decoder_workload(B, T, kdtype="fp8", seed=6, device="cpu", lognormal_sigma=0.5):
+    """One decode step through the decoder's 20 layers (layers 20..39): the
+    shared indexer K and main KV of `decode_workload`, and per layer its own
+    attention query and SWA KV, plus its own indexer query and weights for
+    the Full and Reindex layers (layers 20, 24, 28, 32, 36)."""
+    d = decode_workload(B=B, T=T, kdtype=kdtype, seed=seed, device=device,
+                        lognormal_sigma=lognormal_sigma)
+    gen = Gen(seed + 1000, device)
+    s = d["swa"].shape[1]
+    layers = []
+    for layer in range(20, 40):
+        e = {"layer": layer, "q": attn_query(gen, B), "swa": swa_kv(gen, B, s)}
+        if (layer - 20) % 4 == 0:
+            e["q_idx"], e["w_idx"] = indexer_query(gen, B)
+        layers.append(e)
+    d["layers"] = layers
+    return d
+
+
 def prefill_workload(n_q=4096, prefix_tokens=131072, seed=4, device="cpu", kdtype="bf16",
                      kv_fmt="e8m0_32"):
     """Encoder prefill chunk (m=2): n_q new tokens after a prefix of prefix_tokens.
@@ -253,6 +272,7 @@ WORKLOADS = {
                                               lognormal_sigma=0.5, reindex=True)),
     "prefill_128k": (prefill_workload, dict(n_q=4096, prefix_tokens=131072, seed=4)),
     "kv_append_64k": (kv_append_workload, dict(B=4, n_new=65536, seed=5)),
+    "decoder_1m": (decoder_workload, dict(B=8, T=1048576, kdtype="fp8", seed=6)),
 }
 
 

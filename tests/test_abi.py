@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     decls = re.findall(r"CSA2_API\s+[\w\s\*]+?\b(csa2_\w+)\s*\(", open(HEADER).read())
-    assert len(decls) == 10
+    assert len(decls) == 13
     for name in decls:
         assert hasattr(L, name), name
 
@@ -212,3 +212,31 @@ def test_kv_append_validation(L):
     assert call(S=-1) == 2
     assert call(kv=MIS) == 5
     assert call(swn=A, swa=MIS, S=128, p0=A) == 5
+
+
+def test_layer_schedule_matches_oracle(L):
+    # The library's schedule (host code) against the oracle's reading of the page.
+    from oracle import pipeline
+    names = {0: "full", 1: "reindex", 2: "reuse", 3: "swa", -1: None}
+    for layer in range(-2, 42):
+        assert names[L.csa2_layer_mode(layer)] == pipeline.layer_mode(layer), layer
+
+
+def test_run_layer_state_validation(L):
+    # Checked on the host before anything is enqueued.
+    import compressed_sparse_attention_index_amd as csa
+    args = csa.LayerArgs()
+    st = csa.LayerStateStruct(A, None, A, 2048, A, 512, A, 1 << 20, 0, 0)
+    run = lambda mode, a=ctypes.byref(args), s=ctypes.byref(st): L.csa2_run_layer(mode, a, s, A, A,
+                                                                                  None)
+    assert run(csa.MODE_REUSE) == 7           # no indices from an earlier layer
+    assert run(csa.MODE_REINDEX) == 7         # no pool from an earlier Full layer
+    assert run(9) == 3
+    assert run(csa.MODE_REUSE, a=None) == 1
+    st.top_k = 513
+    assert run(csa.MODE_REUSE) == 2
+    st.top_k, st.idx = 512, None
+    assert run(csa.MODE_REUSE) == 1
+    assert L.csa2_layer_workspace_size(8, 1, 1 << 20, 2048, 512) == (
+        L.csa2_workspace_size(1, 8, 1, 1 << 20, 512, 2048) + 255) // 256 * 256 + \
+        L.csa2_workspace_size(2, 8, 1, 1 << 20, 512, 2048)

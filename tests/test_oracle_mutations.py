@@ -241,6 +241,22 @@ def _kv_append_variant(window_shift=0, wrap_main=False, wrap_window=False):
     return fn
 
 
+def _layer_mode_variant():
+    # Mistake: decoder groups of five layers (the encoder's grouping habit).
+    def layer_mode(layer):
+        if not 0 <= layer < 40:
+            return None
+        if layer < 2:
+            return "swa"
+        if layer < 20:
+            return "full" if (layer - 2) % 6 == 0 else "reuse"
+        group, first = divmod(layer - 20, 5)
+        if first:
+            return "reuse"
+        return "full" if group == 0 else "reindex"
+    return layer_mode
+
+
 def _unpage_variant():
     # Mistake: page j of a sequence read from pool row j * P instead of its
     # table entry's page (the table ignored).
@@ -310,6 +326,8 @@ MUTATIONS = [
      _attention_variant(keep_empty=True)),
     ("unpage with the page index as the row offset", pp.pin_unpage, pipeline.unpage,
      _unpage_variant()),
+    ("schedule with decoder groups of five", pp.pin_layer_mode, pipeline.layer_mode,
+     _layer_mode_variant()),
 ]
 
 

@@ -349,3 +349,25 @@ def pin_unpage(fn):
 
 def test_unpage_logical_view():
     assert pin_unpage(pipeline.unpage)
+
+
+def pin_layer_mode(fn):
+    """The schedule's counts and group structure as the page states them:
+    2 pure-SWA layers; encoder layers 2..19 in three groups of six, each
+    Full then five Reuse; decoder layers 20..39 in five groups of four, the
+    first starting with Full, the others with Reindex, three Reuse after
+    each; nothing outside 0..39."""
+    modes = [fn(layer) for layer in range(40)]
+    enc, dec = modes[:20], modes[20:]
+    ok = enc[:2] == ["swa", "swa"]
+    ok &= all(enc[2 + 6 * g:8 + 6 * g] == ["full"] + ["reuse"] * 5 for g in range(3))
+    ok &= dec[0:4] == ["full", "reuse", "reuse", "reuse"]
+    ok &= all(dec[4 * g:4 * g + 4] == ["reindex", "reuse", "reuse", "reuse"] for g in range(1, 5))
+    ok &= (modes.count("full"), modes.count("reindex"), modes.count("reuse"),
+           modes.count("swa")) == (4, 4, 30, 2)
+    ok &= fn(-1) is None and fn(40) is None
+    return bool(ok)
+
+
+def test_layer_schedule():
+    assert pin_layer_mode(pipeline.layer_mode)
