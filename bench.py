@@ -48,7 +48,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="full_reindex_1m",
                    choices=["tiny_2k", "full_64k", "reuse_128k", "reuse_128k_e4m3",
-                            "full_reindex_1m", "prefill_128k", "kv_append_64k", "decoder_1m"])
+                            "full_reindex_1m", "full_reindex_1m_fp4", "prefill_128k",
+                            "kv_append_64k", "decoder_1m"])
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU time budget of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -82,6 +83,7 @@ ROTATED = {
     "reuse_128k": ("q", "swa", "idx"),
     "reuse_128k_e4m3": ("q", "swa", "idx"),
     "full_reindex_1m": (),
+    "full_reindex_1m_fp4": (),
     "prefill_128k": (),
     "kv_append_64k": ("kv_new", "swa_new"),
     "decoder_1m": (),
@@ -247,8 +249,8 @@ def algorithmic(name, d):
     if name.startswith("reuse_128k"):
         per = B * attn_bytes
         return "sparse_attn", per, "hbm", per
-    T = d["k_idx"].shape[1]
-    krow = 128 if d["kdtype"] == "fp8" else 256
+    T = d["T"]
+    krow = {"fp8": 128, "bf16": 256, "mxfp4": 68}[d["kdtype"]]
     nb = (T + 7) // 8
     if name == "decoder_1m":
         # One scan (Full layer 20), four pool re-scores (Reindex layers), 20
@@ -266,6 +268,40 @@ def algorithmic(name, d):
     if "q_idx2" in d:
         step += B * (16384 * krow + 32 * 128 * 2 + 32 * 4) + B * attn_bytes
     return "index_scan", scan, "hbm", step
+
+
+def mxfp4_rows(d, b):
+    """Sequence b's MXFP4 indexer keys in the oracle's row layout [T, 68]."""
+    import numpy as np
+    T, rows = d["T"], d["B"] * d["T"]
+    buf = d["k_idx_buf"]
+    e2m1 = buf[b * T * 64:(b + 1) * T * 64].view(T, 64)
+    sc = buf[rows * 64 + b * T * 4:rows * 64 + (b + 1) * T * 4].view(T, 4)
+    return np.concatenate([e2m1.cpu().numpy(), sc.cpu().numpy()], axis=1)
+
+
+def fp4_recall(d, step):
+    """Recall of the FP4 indexer path: the GPU Full layer's Top-512 on MXFP4
+    keys against the oracle's Top-512 on the same keys unquantised (bf16),
+    per query row; the mean and the minimum over the rows."""
+    import numpy as np
+    from oracle import pipeline
+    step.run()
+    import torch
+    torch.cuda.synchronize()
+    rec = []
+    for b in range(d["B"]):
+        vis = int(d["vis_len"][b, 0])
+        ref = pipeline.full_layer(d["q_idx"][b, 0].cpu().numpy().view(np.uint16),
+                                  d["w_idx"][b, 0].cpu().numpy(),
+                                  d["k_idx_ref"][b].cpu().numpy().view(np.uint16), "bf16", vis)
+        want = ref["idx"][ref["idx"] >= 0]
+        got = step.idx[b, 0].cpu().numpy()
+        got = got[got >= 0]
+        rec.append(len(np.intersect1d(want, got)) / max(len(want), 1))
+    return {"mean": round(float(np.mean(rec)), 5), "min": round(float(np.min(rec)), 5),
+            "rows": len(rec),
+            "against": "oracle Top-512 over the same keys unquantised (bf16), fp64 scores"}
 
 
 def cpu_baseline(name, d, budget_s):
@@ -304,10 +340,13 @@ def cpu_baseline(name, d, budget_s):
     for b, j in rows:
         kr = None
         if "k_idx" in d:
-            kr = npy(d["k_idx"][b])
             kd = d["kdtype"]
-            if kd == "bf16":
-                kr = kr.view(np.uint16)
+            if kd == "mxfp4":
+                kr = mxfp4_rows(d, b)
+            else:
+                kr = npy(d["k_idx"][b])
+                if kd == "bf16":
+                    kr = kr.view(np.uint16)
         swa = npy(d["swa"][b])
         t0 = time.perf_counter()
         if name == "decoder_1m":
@@ -412,6 +451,11 @@ def measure(name, args, torch, synth, csa, cpu=True, graph=True):
     dominant kernel alone, optional graph replay and oracle baseline."""
     t0 = time.time()
     d = synth.make(name, device="cuda")
+    if d.get("kdtype") == "mxfp4":
+        # The FP4 indexer keys go to the library as one buffer (E2M1 rows,
+        # then their scales); the oracle reads them row by row.
+        d["k_idx_buf"] = d["k_idx"]
+        d["k_idx"] = csa.Mxfp4Keys(d["k_idx"], d["B"] * d["T"], d["T"])
     dominant, per_launch, bound, step_bytes = algorithmic(name, d)
     sets = rotation_sets(name, d, step_bytes or per_launch, torch, synth)
     torch.cuda.synchronize()
@@ -494,6 +538,7 @@ def measure(name, args, torch, synth, csa, cpu=True, graph=True):
                "pool_blocks": None if reuse or name == "prefill_128k" else 2048, "window": 128,
                "layers": {"full_64k": "Full", "tiny_2k": "Full", "reuse_128k": "Reuse",
                           "reuse_128k_e4m3": "Reuse", "full_reindex_1m": "Full+Reindex",
+                          "full_reindex_1m_fp4": "Full+Reindex (FP4 indexer keys)",
                           "prefill_128k": "prefill (m=2)",
                           "decoder_1m": "decoder layers 20-39 (Full + 3 Reuse, "
                                         "4 x (Reindex + 3 Reuse))"}[name],
@@ -509,6 +554,10 @@ def measure(name, args, torch, synth, csa, cpu=True, graph=True):
     if graph_ms is not None:
         rec["graph_ms_per_step"] = round(graph_ms, 5)
         rec["graph_value"] = round(rows / (graph_ms / 1e3), 2)
+    if d.get("kdtype") == "mxfp4":
+        t0 = time.time()
+        rec["recall_fp4_keys"] = fp4_recall(d, step)
+        log(f"[bench] FP4 indexer recall {rec['recall_fp4_keys']} ({time.time() - t0:.1f} s)")
     del step, sets, d
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

@@ -12,7 +12,7 @@ import os
 import torch
 
 __all__ = [
-    "KDTYPE_BF16", "KDTYPE_FP8", "KV_MXFP4_E8M0_32", "KV_FP4_E4M3_16", "MODE_FULL", "MODE_REINDEX", "MODE_REUSE",
+    "KDTYPE_BF16", "KDTYPE_FP8", "KDTYPE_MXFP4", "Mxfp4Keys", "KV_MXFP4_E8M0_32", "KV_FP4_E4M3_16", "MODE_FULL", "MODE_REINDEX", "MODE_REUSE",
     "OP_INDEX_SCORE", "OP_BLOCK_TOPK", "OP_REINDEX_TOPK", "OP_SPARSE_ATTN",
     "Csa2Error", "Paging", "lib", "abi_version", "workspace_size", "index_score", "block_topk",
     "block_topk_noalloc",
@@ -20,7 +20,7 @@ __all__ = [
     "MODE_SWA", "layer_mode", "LayerState", "run_layer",
 ]
 
-KDTYPE_BF16, KDTYPE_FP8 = 0, 1
+KDTYPE_BF16, KDTYPE_FP8, KDTYPE_MXFP4 = 0, 1, 2
 KV_MXFP4_E8M0_32, KV_FP4_E4M3_16 = 0, 1   # main-KV scale formats (csa2_kvfmt)
 MODE_FULL, MODE_REINDEX, MODE_REUSE, MODE_SWA = 0, 1, 2, 3
 OP_INDEX_SCORE, OP_BLOCK_TOPK, OP_REINDEX_TOPK, OP_SPARSE_ATTN = 0, 1, 2, 3
@@ -88,6 +88,26 @@ class Paging:
 
 def _paging(paging):
     return paging.ref() if paging is not None else None
+
+
+class Mxfp4Keys:
+    """Indexer keys in MXFP4 (CSA2_KDTYPE_MXFP4): `buf` is a uint8 GPU tensor
+    of 68 * rows bytes (rows = B * N_cap, or the page pool's rows), the rows'
+    64 bytes of E2M1 first, then their 4 E8M0 scale bytes."""
+
+    def __init__(self, buf, rows, n_cap):
+        assert buf.dtype == torch.uint8 and buf.numel() == 68 * rows
+        self.buf, self.rows, self.n_cap = buf, int(rows), int(n_cap)
+
+
+def _keys(k_idx):
+    """(pointer, csa2_kdtype, N_cap or None) of an indexer-key argument."""
+    if k_idx is None:
+        return None, KDTYPE_BF16, None
+    if isinstance(k_idx, Mxfp4Keys):
+        return _ptr(k_idx.buf, (torch.uint8,), "k_idx"), KDTYPE_MXFP4, k_idx.n_cap
+    kd = KDTYPE_BF16 if k_idx.dtype in _BITS16 else KDTYPE_FP8
+    return _ptr(k_idx, _BITS16 + _U8, "k_idx"), kd, k_idx.shape[1]
 
 
 class AttnOptsV1(ctypes.Structure):
@@ -172,10 +192,10 @@ def index_score(q_idx, w_idx, k_idx, vis_len, scores=None, block_max=None, pagin
     """Indexer scan: scores [B, n_q, N_cap] and/or block_max [B, n_q, ceil(N_cap/8)].
     With paging, k_idx is a page pool [num_pages * page_entries, 128]."""
     B, n_q = q_idx.shape[0], q_idx.shape[1]
-    N_cap = paging.n_cap if paging is not None else k_idx.shape[1]
-    kd = KDTYPE_BF16 if k_idx.dtype in _BITS16 else KDTYPE_FP8
+    kp, kd, kn = _keys(k_idx)
+    N_cap = paging.n_cap if paging is not None else kn
     _call("csa2_index_score", _ptr(q_idx, _BITS16, "q_idx"), _ptr(w_idx, _F32, "w_idx"),
-          _ptr(k_idx, _BITS16 + _U8, "k_idx"), kd, _paging(paging),
+          kp, kd, _paging(paging),
           _ptr(vis_len, _I32, "vis_len"), B, n_q, N_cap,
           _ptr(scores, _F32, "scores"), _ptr(block_max, _F32, "block_max"), None, 0,
           _stream(stream))
@@ -205,11 +225,11 @@ def reindex_topk(mode, vis_len, N_cap, top_k, idx_out, scores=None, q_idx=None, 
     """Top-k inside the pool (Full / Reindex) or over [0, vis) without a pool."""
     B, n_q = vis_len.shape[0], vis_len.shape[1]
     k_blocks = pool_blocks.shape[-1] if pool_blocks is not None else 0
-    kd = KDTYPE_BF16 if (k_idx is None or k_idx.dtype in _BITS16) else KDTYPE_FP8
+    kp, kd, _ = _keys(k_idx)
     need = workspace_size(OP_REINDEX_TOPK, B, n_q, N_cap, top_k, k_blocks)
     ws, nbytes = _workspace(ws, need if pool_blocks is not None else 0, vis_len.device)
     _call("csa2_reindex_topk", mode, _ptr(scores, _F32, "scores"), _ptr(q_idx, _BITS16, "q_idx"),
-          _ptr(w_idx, _F32, "w_idx"), _ptr(k_idx, _BITS16 + _U8, "k_idx"), kd, _paging(paging),
+          _ptr(w_idx, _F32, "w_idx"), kp, kd, _paging(paging),
           _ptr(pool_blocks, _I32, "pool_blocks"), k_blocks, _ptr(vis_len, _I32, "vis_len"),
           B, n_q, N_cap, top_k, _ptr(idx_out, _I32, "idx_out"),
           _ptr(idx_score, _F32, "idx_score"), _ptr(ws, (torch.uint8,), "ws"), nbytes,
@@ -310,8 +330,8 @@ def run_layer(mode, state, k_idx, kv_fp4, kv_scale, vis_len, q, swa_kv, swa_pos0
     """One layer's CSA2 work by mode (include/csa2.h, csa2_run_layer)."""
     B, n_q = q.shape[0], q.shape[1]
     N_cap = kv_paging.n_cap if kv_paging is not None else kv_fp4.shape[1]
-    kd = KDTYPE_BF16 if k_idx.dtype in _BITS16 else KDTYPE_FP8
-    a = LayerArgs(_ptr(k_idx, _BITS16 + _U8, "k_idx"), kd,
+    kp, kd, _ = _keys(k_idx)
+    a = LayerArgs(kp, kd,
                   ctypes.pointer(k_paging.struct) if k_paging is not None else None,
                   _ptr(kv_fp4, _U8, "kv_fp4"), _ptr(kv_scale, _U8, "kv_scale"), kv_fmt,
                   ctypes.pointer(kv_paging.struct) if kv_paging is not None else None, N_cap,

@@ -106,7 +106,11 @@ csa2_status csa2_index_score(const uint16_t* q_idx, const float* w_idx, const vo
   (void)ws_bytes;
   if (!q_idx || !w_idx || !k_idx || !vis_len) return CSA2_ERR_NULL;
   if (!scores && !block_max) return CSA2_ERR_NULL;
-  if (k_dtype != CSA2_KDTYPE_BF16 && k_dtype != CSA2_KDTYPE_FP8_E4M3) return CSA2_ERR_UNSUPPORTED;
+  if (k_dtype != CSA2_KDTYPE_BF16 && k_dtype != CSA2_KDTYPE_FP8_E4M3 &&
+      k_dtype != CSA2_KDTYPE_MXFP4)
+    return CSA2_ERR_UNSUPPORTED;
+  // MXFP4 keys: decode rows only (the prefill-shaped kernel reads bf16 / FP8).
+  if (k_dtype == CSA2_KDTYPE_MXFP4 && n_q >= 16) return CSA2_ERR_UNSUPPORTED;
   csa2_status st = check_rows(B, n_q);
   if (st != CSA2_OK) return st;
   if (N_cap < 1 || N_cap > kMaxNcap) return CSA2_ERR_SHAPE;
@@ -118,8 +122,8 @@ csa2_status csa2_index_score(const uint16_t* q_idx, const float* w_idx, const vo
   csa2::Pages pg;
   st = check_paging(paging, N_cap, &pg);
   if (st != CSA2_OK) return st;
-  return from_hip(csa2::launch_index_score(q_idx, w_idx, k_idx, k_dtype == CSA2_KDTYPE_FP8_E4M3,
-                                           pg, vis_len, B, n_q, N_cap, scores, block_max, stream));
+  return from_hip(csa2::launch_index_score(q_idx, w_idx, k_idx, static_cast<int>(k_dtype), pg,
+                                           vis_len, B, n_q, N_cap, scores, block_max, stream));
 }
 
 csa2_status csa2_block_topk(const float* block_max, const int32_t* vis_len, int32_t B,
@@ -183,12 +187,15 @@ csa2_status csa2_reindex_topk(csa2_mode mode, const float* scores, const uint16_
   const bool stored = mode == CSA2_MODE_FULL && scores;
   if (!stored) {
     if (!q_idx || !w_idx || !k_idx) return CSA2_ERR_NULL;
-    if (k_dtype != CSA2_KDTYPE_BF16 && k_dtype != CSA2_KDTYPE_FP8_E4M3)
+    if (k_dtype != CSA2_KDTYPE_BF16 && k_dtype != CSA2_KDTYPE_FP8_E4M3 &&
+        k_dtype != CSA2_KDTYPE_MXFP4)
       return CSA2_ERR_UNSUPPORTED;
   }
   const size_t need = csa2::pool_topk_workspace_bytes(rows, k_blocks);
   if (!ws || ws_bytes < need) return CSA2_ERR_WORKSPACE;
-  const int kmode = stored ? 0 : (k_dtype == CSA2_KDTYPE_FP8_E4M3 ? 1 : 2);
+  const int kmode = stored ? 0
+                          : k_dtype == CSA2_KDTYPE_FP8_E4M3 ? 1
+                          : k_dtype == CSA2_KDTYPE_BF16 ? 2 : 3;
   return from_hip(csa2::launch_pool_topk(kmode, scores, q_idx, w_idx, k_idx, pg, pool_blocks,
                                          k_blocks,
                                          vis_len, rows, n_q, N_cap, top_k, idx_out, idx_score, ws,

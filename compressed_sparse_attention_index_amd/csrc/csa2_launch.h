@@ -16,8 +16,9 @@ struct Pages {
   int log2p, max_pages, num_pages;
 };
 
+// kd: csa2_kdtype (0 bf16, 1 FP8, 2 MXFP4; MXFP4 only for n_q < 16).
 hipError_t launch_index_score(const uint16_t* q_idx, const float* w_idx, const void* k_idx,
-                              bool fp8, const Pages& pg, const int32_t* vis_len, int B, int n_q,
+                              int kd, const Pages& pg, const int32_t* vis_len, int B, int n_q,
                               int N_cap, float* scores, float* block_max, hipStream_t stream);
 
 // Prefill-chunk scoring on matrix cores (n_q >= 16 rows per sequence); see
@@ -37,8 +38,8 @@ bool block_topk_noalloc_fits(int rows, int N_cap);
 hipError_t launch_block_topk_noalloc(const float* block_max, const int32_t* vis_len, int rows,
                                      int N_cap, int k, int32_t* out, hipStream_t stream);
 
-// Pool Top-K.  mode 0: keys are stored scores; 1 / 2: the pool positions are
-// re-scored with q_idx / w_idx on FP8 / bf16 keys.
+// Pool Top-K.  mode 0: keys are stored scores; 1 / 2 / 3: the pool
+// positions are re-scored with q_idx / w_idx on FP8 / bf16 / MXFP4 keys.
 size_t pool_topk_workspace_bytes(int rows, int k_blocks);
 hipError_t launch_pool_topk(int mode, const float* scores, const uint16_t* q_idx,
                             const float* w_idx, const void* k_idx, const Pages& pg,

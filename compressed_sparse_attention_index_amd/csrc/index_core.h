@@ -16,18 +16,34 @@
 
 namespace csa2 {
 
-template <bool FP8>
-struct KeyTile {
-  static constexpr int kWords = FP8 ? 4 : 8;  // 16-byte words per lane
-  u32x4 v[kWords];
+// Indexer-key storage types (csa2_kdtype): bf16 (256 B per entry), FP8
+// E4M3FN (128 B), MXFP4 (64 B of E2M1 plus 4 E8M0 scales, one per 32 dims;
+// the scales of all R rows of a buffer follow its R rows of E2M1).
+constexpr int kKdBf16 = 0;
+constexpr int kKdFp8 = 1;
+constexpr int kKdFp4 = 2;
+template <int KD>
+struct KeyFmt {
+  static constexpr int kRowBytes = KD == kKdBf16 ? 256 : KD == kKdFp8 ? 128 : 64;
 };
 
-// Loads the lane's 64-dim half of one indexer-key row.
-template <bool FP8>
-__device__ __forceinline__ void load_key_half(KeyTile<FP8>& t, const uint8_t* row, int half) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(row + (FP8 ? 64 : 128) * half);
+template <int KD>
+struct KeyTile {
+  static constexpr int kWords = KD == kKdBf16 ? 8 : KD == kKdFp8 ? 4 : 2;  // 16-B words per lane
+  u32x4 v[kWords];
+  uint32_t sc;   // MXFP4: the two E8M0 codes of the lane's half (low byte: dims 64 half .. + 32)
+};
+
+// Loads the lane's 64-dim half of one indexer-key row (MXFP4: and its two
+// scale bytes from `scale_row`, the row's 4 scales).
+template <int KD>
+__device__ __forceinline__ void load_key_half(KeyTile<KD>& t, const uint8_t* row, int half,
+                                              const uint8_t* scale_row = nullptr) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(row + (KeyFmt<KD>::kRowBytes / 2) * half);
 #pragma unroll
-  for (int i = 0; i < KeyTile<FP8>::kWords; ++i) t.v[i] = p[i];
+  for (int i = 0; i < KeyTile<KD>::kWords; ++i) t.v[i] = p[i];
+  if constexpr (KD == kKdFp4)
+    t.sc = *reinterpret_cast<const uint16_t*>(scale_row + 2 * half);
 }
 
 // Query operand: the lane's head row (lane % 32), dims of its half.
@@ -44,15 +60,21 @@ __device__ __forceinline__ void load_weights(float wr[16], const float* w_row, i
   for (int r = 0; r < 16; ++r) wr[r] = w_row[8 * (r / 4) + 4 * half + (r % 4)];
 }
 
-template <bool FP8>
-__device__ __forceinline__ f32x16 key_tile_dot(const bf16x8 qa[8], const KeyTile<FP8>& t) {
+template <int KD>
+__device__ __forceinline__ f32x16 key_tile_dot(const bf16x8 qa[8], const KeyTile<KD>& t) {
   f32x16 acc = {};
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     bf16x8 kb;
-    if constexpr (FP8) {
+    if constexpr (KD == kKdFp8) {
       const u32x4 w = t.v[s / 2];
       kb = (s & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
+    } else if constexpr (KD == kKdFp4) {
+      // Dims 64 half + 8 s .. + 7: word s % 4 of chunk s / 4, scale s / 4
+      // (the conversion reads the E8M0 code from the exponent field).
+      const u32x4 w = t.v[s / 4];
+      const uint32_t word = (s & 3) == 0 ? w.x : (s & 3) == 1 ? w.y : (s & 3) == 2 ? w.z : w.w;
+      kb = fp4x8_to_bf16x8(word, __uint_as_float(((t.sc >> (8 * (s / 4))) & 0xffu) << 23));
     } else {
       kb = __builtin_bit_cast(bf16x8, t.v[s]);
     }

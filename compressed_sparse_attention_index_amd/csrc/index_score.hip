@@ -15,14 +15,6 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
-template <bool FP8>
-__device__ __forceinline__ const uint8_t* key_row(const uint8_t* kb, int pos, int N_cap) {
-  // Rows past the end of the buffer are never addressed: the last tile's
-  // extra lanes re-read the final row and are masked afterwards.
-  const int p = pos < N_cap ? pos : N_cap - 1;
-  return kb + static_cast<size_t>(p) * (FP8 ? 128 : 256);
-}
-
 constexpr int kOutScores = 1;
 constexpr int kOutBlockMax = 2;
 
@@ -59,24 +51,30 @@ __device__ __forceinline__ void emit(float s, int pos, int vis, int half, int co
 // and the output stores count as well, so a tile has landed once no more are
 // outstanding than the loads of the tiles issued after it and the stores
 // made since.
-template <bool FP8>
+// MXFP4 keys: the tile's 32 rows of 64 B of E2M1, then (at byte 2048) one
+// 4-byte load per lane of the rows' scales (lanes 32..63 repeat lanes
+// 0..31, landing in the next 128 bytes).
+template <int KD>
 struct ScanTile {
-  static constexpr int kRowBytes = FP8 ? 128 : 256;
+  static constexpr int kRowBytes = KeyFmt<KD>::kRowBytes;
   static constexpr int kChunks = kRowBytes / 16;            // 16-B chunks per row
-  static constexpr int kBytes = 32 * kRowBytes;              // one tile
-  static constexpr int kLoads = kBytes / 1024;               // direct-to-LDS loads per tile
+  static constexpr int kDataBytes = 32 * kRowBytes;
+  static constexpr int kBytes = kDataBytes + (KD == kKdFp4 ? 256 : 0);   // one tile slot
+  static constexpr int kLoads = kDataBytes / 1024 + (KD == kKdFp4 ? 1 : 0);  // loads per tile
+  __device__ static int swz(int row) {
+    return KD == kKdFp8 ? ((row >> 1) & 7) : KD == kKdBf16 ? (row & 15) : ((row >> 2) & 3);
+  }
   __device__ static int pos(int row, int chunk) {            // swizzled byte offset
-    const int f = FP8 ? ((row >> 1) & 7) : (row & 15);
-    return row * kRowBytes + ((chunk ^ f) << 4);
+    return row * kRowBytes + ((chunk ^ swz(row)) << 4);
   }
 };
 
-template <bool FP8, int DEPTH, int OUT>
+template <int KD, int DEPTH, int OUT>
 __global__ __launch_bounds__(kThreads) void k_index_scan(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint8_t* __restrict__ k_idx, Pages pg, const int32_t* __restrict__ vis_len, int n_q,
     int N_cap, int tiles_per_wg, float* __restrict__ scores, float* __restrict__ block_max) {
-  using TT = ScanTile<FP8>;
+  using TT = ScanTile<KD>;
   constexpr int kStores = ((OUT & kOutScores) ? 1 : 0) + ((OUT & kOutBlockMax) ? 1 : 0);
   constexpr int kSteady = DEPTH * (TT::kLoads + kStores);
   static_assert(kSteady <= 63, "vmcnt range");
@@ -96,7 +94,6 @@ __global__ __launch_bounds__(kThreads) void k_index_scan(
   float wr[16];
   load_query(qa, q_idx + static_cast<size_t>(r) * kIdxHeads * kIdxDim, col, half);
   load_weights(wr, w_idx + static_cast<size_t>(r) * kIdxHeads, half);
-  const uint8_t* kb = k_idx + static_cast<size_t>(b) * N_cap * TT::kRowBytes;
   // With paging, lane l holds the pool page of the workgroup's l-th logical
   // page (a workgroup spans at most 64 tiles of 32 entries, pages hold at
   // least 64 entries: at most 33 pages); a tile never straddles two pages.
@@ -110,32 +107,45 @@ __global__ __launch_bounds__(kThreads) void k_index_scan(
   float* srow = scores ? scores + static_cast<size_t>(r) * N_cap : nullptr;
   float* brow = block_max ? block_max + static_cast<size_t>(r) * ((N_cap + 7) >> 3) : nullptr;
 
-  // Source offset (within a tile) of this lane for each of the tile's loads.
-  int goff[TT::kLoads];
-  int grow[TT::kLoads];
+  // Source offset (within a tile) of this lane for each of the tile's
+  // 16-byte loads.
+  constexpr int kData = TT::kDataBytes / 1024;
+  int goff[kData];
+  int grow[kData];
 #pragma unroll
-  for (int i = 0; i < TT::kLoads; ++i) {
+  for (int i = 0; i < kData; ++i) {
     const int g = 64 * i + lane;                  // destination chunk index in the slot
     const int row = g / TT::kChunks, p = g % TT::kChunks;
-    const int f = FP8 ? ((row >> 1) & 7) : (row & 15);
     grow[i] = row;
-    goff[i] = row * TT::kRowBytes + ((p ^ f) << 4);
+    goff[i] = row * TT::kRowBytes + ((p ^ TT::swz(row)) << 4);
   }
+  // MXFP4: the scales of all rows follow the rows of E2M1 in the buffer.
+  const size_t total_rows = paged ? (static_cast<size_t>(pg.num_pages) << pg.log2p)
+                                  : static_cast<size_t>(gridDim.y / n_q) * N_cap;
+  const uint8_t* scales = k_idx + total_rows * TT::kRowBytes;
   auto issue = [&](int slot, int tile) {
     const int rows = N_cap - 32 * tile;           // rows of this tile inside the buffer
-    const uint8_t* base = kb + static_cast<size_t>(32) * tile * TT::kRowBytes;
+    size_t row0 = static_cast<size_t>(b) * N_cap + static_cast<size_t>(32) * tile;
     if (paged) {
       const int e = 32 * tile;
       const int pid = __shfl(my_page, (e >> pg.log2p) - page0, 64);
-      base = k_idx + ((static_cast<size_t>(pid) << pg.log2p) + (e & ((1 << pg.log2p) - 1))) *
-                         TT::kRowBytes;
+      row0 = (static_cast<size_t>(pid) << pg.log2p) + (e & ((1 << pg.log2p) - 1));
     }
+    const uint8_t* base = k_idx + row0 * TT::kRowBytes;
 #pragma unroll
-    for (int i = 0; i < TT::kLoads; ++i) {
+    for (int i = 0; i < kData; ++i) {
       const uint8_t* src = base + (grow[i] < rows ? goff[i] : 0);
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)src,
           (__attribute__((address_space(3))) void*)(&stage[wave][slot][i * 1024]), 16, 0,
+          2 /* non-temporal */);
+    }
+    if constexpr (KD == kKdFp4) {
+      const int r = lane & 31;
+      const uint8_t* src = scales + (row0 + (r < rows ? r : 0)) * 4;
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)src,
+          (__attribute__((address_space(3))) void*)(&stage[wave][slot][TT::kDataBytes]), 4, 0,
           2 /* non-temporal */);
     }
   };
@@ -156,11 +166,13 @@ __global__ __launch_bounds__(kThreads) void k_index_scan(
     else
       wait_vmem_le<kSteady>(after);
     const uint8_t* st = stage[wave][slot];
-    KeyTile<FP8> kt;
+    KeyTile<KD> kt;
 #pragma unroll
-    for (int j = 0; j < KeyTile<FP8>::kWords; ++j)
+    for (int j = 0; j < KeyTile<KD>::kWords; ++j)
       kt.v[j] = *reinterpret_cast<const u32x4*>(st + TT::pos(col, (TT::kChunks / 2) * half + j));
-    const float s = head_sum(key_tile_dot<FP8>(qa, kt), wr);
+    if constexpr (KD == kKdFp4)
+      kt.sc = *reinterpret_cast<const uint16_t*>(st + TT::kDataBytes + 4 * col + 2 * half);
+    const float s = head_sum(key_tile_dot<KD>(qa, kt), wr);
     emit<OUT>(s, 32 * t + col, vis, half, col, srow, brow);
     slot = slot == DEPTH ? 0 : slot + 1;
   }
@@ -181,7 +193,7 @@ int pick_tiles_per_wg(long long total_tiles, int min_tiles, int target_wgs, int 
 }  // namespace
 
 hipError_t launch_index_score(const uint16_t* q_idx, const float* w_idx, const void* k_idx,
-                              bool fp8, const Pages& pg, const int32_t* vis_len, int B, int n_q,
+                              int kd, const Pages& pg, const int32_t* vis_len, int B, int n_q,
                               int N_cap, float* scores, float* block_max, hipStream_t stream) {
   const int tiles = (N_cap + 31) / 32;
   const uint8_t* kb = static_cast<const uint8_t*>(k_idx);
@@ -195,18 +207,22 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w_idx, const v
     hipLaunchKernelGGL((k_index_scan<F, D, O>), grid, dim3(kThreads), 0, stream, q_idx, w_idx, \
                        kb, pg, vis_len, n_q, N_cap, tpw, scores, block_max);                   \
   } while (0)
-    switch ((fp8 ? 4 : 0) | out) {
-      case 1: CSA2_SCAN_LAUNCH(false, 1, 1); break;
-      case 2: CSA2_SCAN_LAUNCH(false, 1, 2); break;
-      case 3: CSA2_SCAN_LAUNCH(false, 1, 3); break;
-      case 5: CSA2_SCAN_LAUNCH(true, 1, 1); break;
-      case 6: CSA2_SCAN_LAUNCH(true, 1, 2); break;
-      case 7: CSA2_SCAN_LAUNCH(true, 1, 3); break;
+    switch (4 * kd + out) {
+      case 1: CSA2_SCAN_LAUNCH(kKdBf16, 1, 1); break;
+      case 2: CSA2_SCAN_LAUNCH(kKdBf16, 1, 2); break;
+      case 3: CSA2_SCAN_LAUNCH(kKdBf16, 1, 3); break;
+      case 5: CSA2_SCAN_LAUNCH(kKdFp8, 1, 1); break;
+      case 6: CSA2_SCAN_LAUNCH(kKdFp8, 1, 2); break;
+      case 7: CSA2_SCAN_LAUNCH(kKdFp8, 1, 3); break;
+      case 9: CSA2_SCAN_LAUNCH(kKdFp4, 1, 1); break;
+      case 10: CSA2_SCAN_LAUNCH(kKdFp4, 1, 2); break;
+      case 11: CSA2_SCAN_LAUNCH(kKdFp4, 1, 3); break;
       default: return hipErrorInvalidValue;   // no output requested
     }
 #undef CSA2_SCAN_LAUNCH
   } else {
-    return launch_index_gemm(q_idx, w_idx, kb, fp8, pg, vis_len, B, n_q, N_cap, scores,
+    if (kd == kKdFp4) return hipErrorInvalidValue;   // rejected by the API layer first
+    return launch_index_gemm(q_idx, w_idx, kb, kd == kKdFp8, pg, vis_len, B, n_q, N_cap, scores,
                              block_max, stream);
   }
   return hipGetLastError();

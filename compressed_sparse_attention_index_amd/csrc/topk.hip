@@ -396,7 +396,7 @@ __device__ __forceinline__ bool pool_slot_valid(const int32_t* prow, int i, int 
   return blk >= 0 && blk < nb_cap && blk * kBlock + (i & 7) < vis;
 }
 
-template <bool FP8>
+template <int KD>
 __global__ __launch_bounds__(kPscThreads) void k_pool_score(PoolArgs a) {
   const int r = blockIdx.y;
   const int tid = threadIdx.x;
@@ -413,7 +413,13 @@ __global__ __launch_bounds__(kPscThreads) void k_pool_score(PoolArgs a) {
   const int b = r / a.n_q;
   // Tiles of 32 slots (4 pool blocks each); wave w takes tiles w and w + 4.
   const int slot0 = blockIdx.x * kPsSlots;
-  KeyTile<FP8> kt[2];
+  KeyTile<KD> kt[2];
+  constexpr int kRow = KeyFmt<KD>::kRowBytes;
+  // MXFP4: the scales of all rows follow the rows of E2M1 in the buffer.
+  const size_t total_rows = a.pg.bt != nullptr
+                                ? (static_cast<size_t>(a.pg.num_pages) << a.pg.log2p)
+                                : static_cast<size_t>(gridDim.y / a.n_q) * a.N_cap;
+  const uint8_t* scales = a.k_idx + total_rows * kRow;
   bool valid[2];
   int slot[2];
 #pragma unroll
@@ -423,11 +429,11 @@ __global__ __launch_bounds__(kPscThreads) void k_pool_score(PoolArgs a) {
     const int pos = valid[u] ? prow[slot[u] >> 3] * kBlock + (col & 7) : 0;
     bool mapped;
     const size_t row = pool_row(a.pg, b, a.N_cap, pos, mapped);
-    load_key_half<FP8>(kt[u], a.k_idx + row * (FP8 ? 128 : 256), half);
+    load_key_half<KD>(kt[u], a.k_idx + row * kRow, half, scales + row * 4);
   }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const float s = head_sum(key_tile_dot<FP8>(qa, kt[u]), wr);
+    const float s = head_sum(key_tile_dot<KD>(qa, kt[u]), wr);
     if (half == 0 && slot[u] < nslots) ps[slot[u]] = s;
   }
 }
@@ -1098,9 +1104,11 @@ hipError_t launch_pool_topk(int mode, const float* scores, const uint16_t* q_idx
   if (mode != 0) {
     dim3 grid((k_blocks + kPsBlocks - 1) / kPsBlocks, rows);
     if (mode == 1)
-      hipLaunchKernelGGL(k_pool_score<true>, grid, dim3(kPscThreads), 0, stream, a);
+      hipLaunchKernelGGL(k_pool_score<kKdFp8>, grid, dim3(kPscThreads), 0, stream, a);
+    else if (mode == 2)
+      hipLaunchKernelGGL(k_pool_score<kKdBf16>, grid, dim3(kPscThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL(k_pool_score<false>, grid, dim3(kPscThreads), 0, stream, a);
+      hipLaunchKernelGGL(k_pool_score<kKdFp4>, grid, dim3(kPscThreads), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k_pool_final, dim3(rows), dim3(kPsThreads), 0, stream, a);

@@ -83,7 +83,15 @@ typedef enum {
 /* Storage type of the indexer keys. */
 typedef enum {
   CSA2_KDTYPE_BF16 = 0,      /* 128 x bf16 = 256 bytes per entry */
-  CSA2_KDTYPE_FP8_E4M3 = 1   /* 128 x FP8 E4M3FN (OCP) = 128 bytes per entry */
+  CSA2_KDTYPE_FP8_E4M3 = 1,  /* 128 x FP8 E4M3FN (OCP) = 128 bytes per entry */
+  /* FP4 indexer QK path (DeepSeek-V4 essay, mlqm.cn, §10.2: the Lightning
+     Indexer's QK path in FP4): OCP MXFP4, 64 bytes of E2M1 (element 2j in
+     the low nibble of byte j) plus 4 E8M0 scales (one per 32 dims) per
+     entry.  A buffer of R entries (R = B * N_cap, or num_pages *
+     page_entries with paging) holds the R rows of E2M1 first and then the R
+     rows of 4 scale bytes: 68 * R bytes.  Decode rows only (n_q < 16);
+     prefill-shaped calls return CSA2_ERR_UNSUPPORTED. */
+  CSA2_KDTYPE_MXFP4 = 2
 } csa2_kdtype;
 
 /* Storage format of main-KV entries (512 dims each).  Both store E2M1

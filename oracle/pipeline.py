@@ -11,7 +11,8 @@ Top-512 and builds the pool of at most 2048 blocks of 8 positions.
 chunks), the decoder m=1.
 
 Raw layouts (one query): q_idx uint16 [32, 128] (bf16 bits); w float [32];
-k_idx uint16 [N, 128] (bf16 bits) or uint8 [N, 128] (FP8 E4M3FN);
+k_idx uint16 [N, 128] (bf16 bits), uint8 [N, 128] (FP8 E4M3FN) or uint8
+[N, 68] (MXFP4: 64 bytes of E2M1, then 4 E8M0 scales);
 q uint16 [64, 512] (bf16 bits); kv_fp4 uint8 [N, 256]; kv_scale uint8
 [N, 16] (E8M0); swa uint8 [S, 512] (FP8 E4M3FN), slot i holding token
 swa_pos0 + i.
@@ -24,10 +25,17 @@ CHUNK = 1 << 16
 
 
 def decode_index_keys(k_raw, kdtype):
+    """Indexer keys -> fp64 [N, 128].  "bf16": uint16 [N, 128] bits; "fp8":
+    uint8 [N, 128] E4M3FN; "mxfp4" (the FP4 indexer QK path of [V4 essay
+    §10.2]): uint8 [N, 68] rows, 64 bytes of E2M1 (OCP MXFP4 nibble order)
+    then the 4 E8M0 scales of dims 32 q .. 32 q + 31."""
     if kdtype == "bf16":
         return formats.bf16_to_f64(k_raw)
     if kdtype == "fp8":
         return formats.e4m3_to_f64(k_raw)
+    if kdtype == "mxfp4":
+        k_raw = np.asarray(k_raw, dtype=np.uint8)
+        return formats.mxfp4_to_f64(k_raw[..., :64], k_raw[..., 64:68])
     raise ValueError(f"unknown indexer K dtype {kdtype!r}")
 
 

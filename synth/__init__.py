@@ -132,7 +132,23 @@ def _normal_mxfp4(gen, b, n, chunk=1 << 18, kv_fmt="e8m0_32"):
 
 def _index_keys(gen, b, n, kdtype, heavy_rows=0, heavy_scale=4.0, lognormal_sigma=None,
                 chunk=1 << 18):
-    """Indexer K [b, n, 128] ~ N(0,1), optionally with row scaling, stored bf16 or FP8."""
+    """Indexer K [b, n, 128] ~ N(0,1), optionally with row scaling, stored bf16
+    or FP8 ([b, n, 128]), or MXFP4: (a uint8 buffer of b * n * 68 bytes, the
+    rows' 64 bytes of E2M1 first, then their 4 E8M0 scales; and the same keys
+    as bf16 bits [b, n, 128], the unquantised reference)."""
+    if kdtype == "mxfp4":
+        ref = _index_keys(gen, b, n, "bf16", heavy_rows, heavy_scale, lognormal_sigma, chunk)
+        rows = b * n
+        buf = torch.empty(rows * 68, dtype=torch.uint8, device=gen.device)
+        e2m1 = buf[:rows * 64].view(rows, 64)
+        sc = buf[rows * 64:].view(rows, 4)
+        flat = ref.view(rows, DIM_IDX)
+        for lo in range(0, rows, chunk):
+            hi = min(rows, lo + chunk)
+            p, s = to_mxfp4(flat[lo:hi].view(torch.bfloat16).float())
+            e2m1[lo:hi] = p
+            sc[lo:hi] = s
+        return buf, ref
     out_dtype = torch.int16 if kdtype == "bf16" else torch.uint8
     k = torch.empty(b, n, DIM_IDX, dtype=out_dtype, device=gen.device)
     for bi in range(b):
@@ -179,6 +195,10 @@ def decode_workload(B, T, kdtype="fp8", seed=0, device="cpu", heavy_frac=0.0,
         heavy = int(round(heavy_frac * T)) if heavy_frac else 0
         d["k_idx"] = _index_keys(gen, B, T, kdtype, heavy_rows=heavy,
                                  lognormal_sigma=lognormal_sigma)
+        if kdtype == "mxfp4":
+            # The MXFP4 buffer, and the unquantised keys the recall of the
+            # FP4 path is measured against.
+            d["k_idx"], d["k_idx_ref"] = d["k_idx"]
         if reindex:
             d["q_idx2"], d["w_idx2"] = indexer_query(gen, B)
     d["q"] = attn_query(gen, B)
@@ -272,6 +292,8 @@ WORKLOADS = {
                                               lognormal_sigma=0.5, reindex=True)),
     "prefill_128k": (prefill_workload, dict(n_q=4096, prefix_tokens=131072, seed=4)),
     "kv_append_64k": (kv_append_workload, dict(B=4, n_new=65536, seed=5)),
+    "full_reindex_1m_fp4": (decode_workload, dict(B=8, T=1048576, kdtype="mxfp4", seed=3,
+                                                  lognormal_sigma=0.5, reindex=True)),
     "decoder_1m": (decoder_workload, dict(B=8, T=1048576, kdtype="fp8", seed=6)),
 }
 

@@ -1,0 +1,145 @@
+"""The FP4 indexer QK path (DeepSeek-V4 essay §10.2): indexer keys stored as
+MXFP4 (CSA2_KDTYPE_MXFP4).  The keys dequantise exactly to bf16, so the scan
+and the pool re-scoring are compared with the oracle on the same stored
+bytes (parity, not recall); the recall of the FP4 path against unquantised
+keys is a property of the data and is reported by the benchmark.
+"""
+import numpy as np
+import pytest
+import torch
+
+from _helpers import check_selection, u16
+from oracle import indexer, pipeline
+import synth
+
+pytestmark = pytest.mark.gpu
+
+csa = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_lib():
+    global csa
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import compressed_sparse_attention_index_amd as m
+    m.lib()
+    csa = m
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _oracle_rows(buf, rows, first, n):
+    """Rows first .. first + n of an MXFP4 key buffer in the oracle's layout
+    ([n, 68]: 64 bytes of E2M1, then the 4 scales)."""
+    b = _np(buf)
+    e2m1 = b[:rows * 64].reshape(rows, 64)[first:first + n]
+    sc = b[rows * 64:].reshape(rows, 4)[first:first + n]
+    return np.concatenate([e2m1, sc], axis=1)
+
+
+def _keys(d):
+    B, T = d["B"], d["T"]
+    return csa.Mxfp4Keys(d["k_idx"].cuda(), B * T, T)
+
+
+@pytest.mark.parametrize("T", [2048, 4133])
+def test_scan_mxfp4_ragged(T):
+    vis = [0, 1, 7, 9, 33, 512, 513, T - 1, T]
+    B = len(vis)
+    d = synth.decode_workload(B=B, T=T, kdtype="mxfp4", seed=401, lognormal_sigma=0.5)
+    vis_t = torch.tensor(vis, dtype=torch.int32).reshape(B, 1).cuda()
+    sc = torch.full((B, 1, T), float("nan"), device="cuda")
+    bm = torch.full((B, 1, (T + 7) // 8), float("nan"), device="cuda")
+    print(f"scan mxfp4 T={T}", flush=True)
+    csa.index_score(d["q_idx"].cuda(), d["w_idx"].cuda(), _keys(d), vis_t, scores=sc, block_max=bm)
+    torch.cuda.synchronize()
+    sc, bm = _np(sc), _np(bm)
+    for b, v in enumerate(vis):
+        kr = _oracle_rows(d["k_idx"], B * T, b * T, T)
+        ref = pipeline.scores_prefix(u16(d["q_idx"][b, 0]), _np(d["w_idx"][b, 0]), kr, "mxfp4", v)
+        g = sc[b, 0, :v].astype(np.float64)
+        tol = 1e-5 * np.abs(ref) + 1e-6 * (np.abs(ref).max() if v else 0)
+        assert np.all(np.abs(g - ref) <= tol), f"row {b}: max err {np.abs(g - ref).max()}"
+        assert np.all(np.isnan(sc[b, 0, v:]))
+        nb = (v + 7) // 8
+        bref = indexer.block_max(ref, v)
+        assert np.all(np.abs(bm[b, 0, :nb] - bref) <= 1e-5 * np.abs(bref) +
+                      1e-6 * (np.abs(ref).max() if v else 0))
+
+
+@pytest.mark.parametrize("mode", ["full", "reindex"])
+def test_pool_topk_mxfp4(mode):
+    B, T = 2, 8192
+    d = synth.decode_workload(B=B, T=T, kdtype="mxfp4", seed=402, reindex=True)
+    keys = _keys(d)
+    vis = d["vis_len"].cuda()
+    bm = torch.empty(B, 1, T // 8, device="cuda")
+    csa.index_score(d["q_idx"].cuda(), d["w_idx"].cuda(), keys, vis, block_max=bm)
+    pool = torch.empty(B, 1, 512, dtype=torch.int32, device="cuda")
+    csa.block_topk(bm, vis, T, 512, pool)
+    q, w = (d["q_idx"], d["w_idx"]) if mode == "full" else (d["q_idx2"], d["w_idx2"])
+    idx = torch.empty(B, 1, 512, dtype=torch.int32, device="cuda")
+    print(f"pool top-k mxfp4 {mode}", flush=True)
+    csa.reindex_topk(csa.MODE_FULL if mode == "full" else csa.MODE_REINDEX, vis, T, 512, idx,
+                     q_idx=q.cuda(), w_idx=w.cuda(), k_idx=keys, pool_blocks=pool)
+    torch.cuda.synchronize()
+    for b in range(B):
+        kr = _oracle_rows(d["k_idx"], B * T, b * T, T)
+        qr, wr = u16(q[b, 0]), _np(w[b, 0])
+        if mode == "full":
+            ref = pipeline.full_layer(qr, wr, kr, "mxfp4", T, k_blocks=512)
+            check_selection(_np(pool[b, 0]), ref["pool"], lambda j: ref["block_max"][j],
+                            what=f"pool row {b}")
+            check_selection(_np(idx[b, 0]), ref["idx"], lambda t: ref["scores"][t],
+                            what=f"idx row {b}")
+        else:
+            ref = pipeline.reindex_layer(qr, wr, kr, "mxfp4", _np(pool[b, 0]), T)
+            check_selection(_np(idx[b, 0]), ref["idx"],
+                            lambda t: pipeline.scores_at(qr, wr, kr, "mxfp4", t),
+                            what=f"reindex row {b}")
+
+
+def test_scan_mxfp4_paged():
+    # The E2M1 rows and the scale rows of a page pool follow the same table.
+    B, T, P = 2, 2048, 128
+    d = synth.decode_workload(B=B, T=T, kdtype="mxfp4", seed=403)
+    rows = B * T
+    buf = d["k_idx"]
+    e2m1 = buf[:rows * 64].view(rows, 64)
+    sc = buf[rows * 64:].view(rows, 4)
+    rng = np.random.default_rng(403)
+    max_pages = T // P
+    num_pages = B * max_pages + 3
+    bt = rng.permutation(num_pages)[:B * max_pages].reshape(B, max_pages).astype(np.int32)
+    pool_rows = num_pages * P
+    pool = torch.zeros(pool_rows * 68, dtype=torch.uint8)
+    pe, ps = pool[:pool_rows * 64].view(pool_rows, 64), pool[pool_rows * 64:].view(pool_rows, 4)
+    for b in range(B):
+        for j in range(max_pages):
+            src = slice(b * T + j * P, b * T + (j + 1) * P)
+            dst = slice(int(bt[b, j]) * P, (int(bt[b, j]) + 1) * P)
+            pe[dst] = e2m1[src]
+            ps[dst] = sc[src]
+    paging = csa.Paging(torch.from_numpy(bt).cuda(), P, num_pages)
+    out = []
+    for keys, pg in ((_keys(d), None), (csa.Mxfp4Keys(pool.cuda(), pool_rows, T), paging)):
+        s = torch.full((B, 1, T), float("nan"), device="cuda")
+        print(f"scan mxfp4 paged={pg is not None}", flush=True)
+        csa.index_score(d["q_idx"].cuda(), d["w_idx"].cuda(), keys, d["vis_len"].cuda(), scores=s,
+                        paging=pg)
+        torch.cuda.synchronize()
+        out.append(_np(s))
+    assert np.array_equal(out[0], out[1], equal_nan=True)
+
+
+def test_mxfp4_keys_rejected_for_prefill_rows():
+    d = synth.decode_workload(B=1, T=1024, kdtype="mxfp4", seed=404)
+    q = torch.zeros(1, 16, 32, 128, dtype=torch.int16, device="cuda")
+    w = torch.zeros(1, 16, 32, device="cuda")
+    vis = torch.full((1, 16), 1024, dtype=torch.int32, device="cuda")
+    sc = torch.empty(1, 16, 1024, device="cuda")
+    with pytest.raises(csa.Csa2Error) as e:
+        csa.index_score(q, w, _keys(d), vis, scores=sc)
+    assert e.value.status == 3

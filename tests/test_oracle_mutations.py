@@ -257,6 +257,14 @@ def _layer_mode_variant():
     return layer_mode
 
 
+def _mxfp4_keys_scales_swapped(k_raw, kdtype):
+    # Mistake: the MXFP4 key row's scales read in reverse order.
+    if kdtype == "mxfp4":
+        k_raw = np.asarray(k_raw, dtype=np.uint8)
+        return formats.mxfp4_to_f64(k_raw[..., :64], k_raw[..., 64:68][..., ::-1])
+    return pipeline.decode_index_keys(k_raw, kdtype)
+
+
 def _unpage_variant():
     # Mistake: page j of a sequence read from pool row j * P instead of its
     # table entry's page (the table ignored).
@@ -324,6 +332,8 @@ MUTATIONS = [
      _attention_variant(slot_shift=-1)),
     ("attention empty slots kept", pp.pin_attention, pipeline.attention,
      _attention_variant(keep_empty=True)),
+    ("mxfp4 key scales reversed", pp.pin_decode_keys, pipeline.decode_index_keys,
+     _mxfp4_keys_scales_swapped),
     ("unpage with the page index as the row offset", pp.pin_unpage, pipeline.unpage,
      _unpage_variant()),
     ("schedule with decoder groups of five", pp.pin_layer_mode, pipeline.layer_mode,

@@ -19,10 +19,21 @@ import synth
 # ---------------------------------------------------------------------------
 # Independent helpers (no oracle arithmetic)
 
+_E2M1_LISTING = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+                 -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]   # OCP MX v1.0 E2M1 codes
+
+
 def _torch_keys(k_raw, kdtype):
     t = torch.from_numpy(np.ascontiguousarray(k_raw))
     if kdtype == "bf16":
         return t.view(torch.int16).view(torch.bfloat16).to(torch.float64).numpy()
+    if kdtype == "mxfp4":
+        # Nibbles (even element low) through the OCP listing, scales through
+        # torch's E8M0 cast, one per 32 dims.
+        nib = torch.stack([t[:, :64] & 15, t[:, :64] >> 4], dim=-1).reshape(-1, 128).long()
+        vals = torch.tensor(_E2M1_LISTING, dtype=torch.float64)[nib]
+        sc = t[:, 64:68].contiguous().view(torch.float8_e8m0fnu).to(torch.float64)
+        return (vals * sc.repeat_interleave(32, dim=1)).numpy()
     return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
 
 
@@ -61,6 +72,9 @@ def _inputs(seed, vis, kdtype, ties=False):
     q_raw = synth.to_bf16_bits(torch.from_numpy(q).float()).numpy().view(np.uint16)
     if kdtype == "bf16":
         k_raw = synth.to_bf16_bits(torch.from_numpy(kf).float()).numpy().view(np.uint16)
+    elif kdtype == "mxfp4":
+        p, sc = synth.to_mxfp4(torch.from_numpy(kf).float())
+        k_raw = np.concatenate([p.numpy(), sc.numpy()], axis=1)
     else:
         k_raw = synth.to_fp8_bytes(torch.from_numpy(kf).float()).numpy()
     return q_raw, w, k_raw
@@ -82,12 +96,24 @@ def pin_decode_keys(fn):
     f8 = rng.integers(0, 256, (9, 128), dtype=np.uint8)
     f8[(f8 & 0x7F) == 0x7F] = 0x38                       # no NaN codes
     ok &= np.array_equal(fn(f8, "fp8"), _torch_keys(f8, "fp8"))
+    f4 = rng.integers(0, 256, (9, 68), dtype=np.uint8)
+    f4[:, 64:] = rng.integers(100, 150, (9, 4))          # E8M0 codes away from NaN (255)
+    ok &= np.array_equal(fn(f4, "mxfp4"), _torch_keys(f4, "mxfp4"))
+    # A hand-made row: dims 0 and 1 in byte 0 (low nibble first), dims
+    # 32..63 under the second scale.
+    row = np.zeros((1, 68), np.uint8)
+    row[0, 0] = 0x2F            # dim 0: code 0xF = -6; dim 1: code 0x2 = 1.0
+    row[0, 16] = 0x07           # dim 32: 6.0
+    row[0, 64:68] = [127, 129, 0, 127]   # 2^0, 2^2, 2^-127, 2^0
+    want = np.zeros((1, 128))
+    want[0, 0], want[0, 1], want[0, 32] = -6.0, 1.0, 24.0
+    ok &= np.array_equal(fn(row, "mxfp4"), want)
     return bool(ok)
 
 
 def pin_scores_prefix(fn):
     # Chunks of 7 over 50 positions: 7 whole chunks and a partial one.
-    for kdtype in ("bf16", "fp8"):
+    for kdtype in ("bf16", "fp8", "mxfp4"):
         q_raw, w, k_raw = _inputs(2, 60, kdtype)
         want = _loop_scores(_qf(q_raw), w, _torch_keys(k_raw, kdtype))
         for vis, chunk in ((50, 7), (49, 7), (7, 7), (8, 7), (1, 3), (50, 64), (60, 1 << 16)):
@@ -117,6 +143,7 @@ def _brute_full(q_raw, w, k_raw, kdtype, vis, kb, k):
 
 FULL_CASES = [  # (seed, vis, kdtype, k_blocks, top_k, ties)
     (10, 200, "bf16", 12, 9, False),
+    (16, 180, "mxfp4", 10, 24, True),
     (11, 203, "fp8", 30, 16, True),
     (12, 64, "bf16", 2048, 512, False),     # every block kept, fewer than k positions
     (13, 97, "fp8", 6, 20, False),          # pool smaller than k: Top-k inside the pool only
