@@ -410,14 +410,15 @@ def cpu_baseline(name, d, budget_s):
 def traffic_from_profile(dominant, src_hash, workload):
     # Counters are per launch of one workload's dominant call: they apply only
     # to that workload and only while the kernel's sources are unchanged.
-    path = os.path.join(ROOT, "profiles", f"{dominant}_traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        rec = json.load(f)
-    if rec.get("source_hash") != src_hash or rec.get("workload") != workload:
-        return None
-    return rec.get("bytes_per_launch")
+    pdir = os.path.join(ROOT, "profiles")
+    for fname in sorted(os.listdir(pdir)):
+        if not (fname.startswith(dominant) and fname.endswith("_traffic.json")):
+            continue
+        with open(os.path.join(pdir, fname)) as f:
+            rec = json.load(f)
+        if rec.get("source_hash") == src_hash and rec.get("workload") == workload:
+            return rec.get("bytes_per_launch")
+    return None
 
 
 def cpu_model():
