@@ -156,12 +156,11 @@ class Step:
             self.bm = None
             self.scores = z(B, n_q, self.N, dt=torch.float32)
             return
+        # Full (and Reindex) decode layers through the layer driver; the
+        # block maxima of the dominant-kernel loop get their own buffer.
         self.bm = z(B, n_q, (self.N + 7) // 8, dt=torch.float32)
-        self.pool = z(B, n_q, 2048)
-        self.ws_bt = self._ws(csa.OP_BLOCK_TOPK, 512, 2048)
-        self.ws_re = self._ws(csa.OP_REINDEX_TOPK, 512, 2048)
+        self.state = csa.LayerState(B, n_q, self.N, k_blocks=2048, top_k=512)
         if "q_idx2" in d:
-            self.idx2 = z(B, n_q, 512)
             self.out2 = z(B, n_q, 64, 512, dt=torch.int16)
             self.lse2 = z(B, n_q, 64, dt=torch.float32)
 
@@ -199,7 +198,7 @@ class Step:
         fn(q, d["kv_fp4"], d["kv_scale"], idx, swa, d["swa_pos0"], d["q_pos"], d["sm_scale"], out,
            lse=lse, kv_fmt=fmt, ws=self.ws_attn)
 
-    def run(self):
+    def run(self, full_only=False):
         d, csa = self._next(), self.csa
         if self.name == "decoder_1m":
             self.state.struct.has_pool = self.state.struct.has_idx = 0
@@ -216,21 +215,20 @@ class Step:
         if self.name.startswith("reuse_128k"):
             self._attn(d, csa.reuse_attn, d["q"], d["swa"], d["idx"], self.out, self.lse)
             return
-        self._scan(d)
         if self.name == "prefill_128k":
+            self._scan(d)
             csa.reindex_topk(csa.MODE_FULL, d["vis_len"], self.N, 512, self.idx, scores=self.scores)
             self._attn(d, csa.sparse_attn_decode, d["q"], d["swa"], self.idx, self.out, self.lse)
             return
-        csa.block_topk(self.bm, d["vis_len"], self.N, 2048, self.pool, ws=self.ws_bt)
-        csa.reindex_topk(csa.MODE_FULL, d["vis_len"], self.N, 512, self.idx, q_idx=d["q_idx"],
-                         w_idx=d["w_idx"], k_idx=d["k_idx"], pool_blocks=self.pool, ws=self.ws_re)
-        self._attn(d, csa.sparse_attn_decode, d["q"], d["swa"], self.idx, self.out, self.lse)
-        if hasattr(self, "idx2"):
-            csa.reindex_topk(csa.MODE_REINDEX, d["vis_len"], self.N, 512, self.idx2,
-                             q_idx=d["q_idx2"], w_idx=d["w_idx2"], k_idx=d["k_idx"],
-                             pool_blocks=self.pool, ws=self.ws_re)
-            self._attn(d, csa.sparse_attn_decode, d["q2"], d["swa2"], self.idx2, self.out2,
-                       self.lse2)
+        fmt = csa.KV_FP4_E4M3_16 if d.get("kv_fmt") == "e4m3_16" else csa.KV_MXFP4_E8M0_32
+        layer = lambda mode, q_idx, w_idx, q, swa, out, lse: csa.run_layer(
+            mode, self.state, d["k_idx"], d["kv_fp4"], d["kv_scale"], d["vis_len"], q, swa,
+            d["swa_pos0"], d["q_pos"], d["sm_scale"], out, lse=lse, q_idx=q_idx, w_idx=w_idx,
+            kv_fmt=fmt)
+        layer(csa.MODE_FULL, d["q_idx"], d["w_idx"], d["q"], d["swa"], self.out, self.lse)
+        if "q_idx2" in d and not full_only:
+            layer(csa.MODE_REINDEX, d["q_idx2"], d["w_idx2"], d["q2"], d["swa2"], self.out2,
+                  self.lse2)
 
 
 def algorithmic(name, d):
@@ -286,7 +284,7 @@ def fp4_recall(d, step):
     per query row; the mean and the minimum over the rows."""
     import numpy as np
     from oracle import pipeline
-    step.run()
+    step.run(full_only=True)   # the Full layer's Top-512 stays in the layer state
     import torch
     torch.cuda.synchronize()
     rec = []
@@ -296,7 +294,7 @@ def fp4_recall(d, step):
                                   d["w_idx"][b, 0].cpu().numpy(),
                                   d["k_idx_ref"][b].cpu().numpy().view(np.uint16), "bf16", vis)
         want = ref["idx"][ref["idx"] >= 0]
-        got = step.idx[b, 0].cpu().numpy()
+        got = step.state.idx[b, 0].cpu().numpy()
         got = got[got >= 0]
         rec.append(len(np.intersect1d(want, got)) / max(len(want), 1))
     return {"mean": round(float(np.mean(rec)), 5), "min": round(float(np.min(rec)), 5),

@@ -35,6 +35,7 @@
 
 #include "csa2_launch.h"
 #include "index_core.h"
+#include "pool_select.h"
 #include "select_common.h"
 
 namespace csa2 {
@@ -48,6 +49,8 @@ constexpr int kBtItems = 4096;          // block maxima per filter workgroup
 constexpr int kBtMaxWgs = 128;          // filter workgroups per row (kBtMaxBlocks / kBtItems)
 constexpr int kBtFinalCap = 8192;       // final-bucket candidates held in LDS
 constexpr int kBtMaxBlocks = 1 << 19;   // LDS bitmap capacity (block ids)
+constexpr int kBtWaves = kBtThreads / 64;
+constexpr int kBtRankMax = 256;         // final buckets up to this size are resolved by ranks
 
 struct BtWs {
   uint32_t* hist;    // [rows][kHistBins] bins of key bits [31:20]
@@ -158,10 +161,11 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const float* __restrict
   __shared__ uint32_t fkey[kBtFinalCap];
   __shared__ int32_t fid[kBtFinalCap];
   __shared__ uint32_t bitmap[kBtMaxBlocks / 32];
-  __shared__ uint32_t off_s[kBtMaxWgs + 1], off_c[kBtMaxWgs + 1];
+  __shared__ uint32_t off_c[kBtMaxWgs + 1];
   __shared__ uint32_t hist256[256];
   __shared__ uint32_t wb[Wg<kBtThreads>::kScratch];
   __shared__ uint32_t fcount;
+  __shared__ uint32_t res[8];   // b1, above, n1, b2, above2, n2, totals of h1 and h2
   using W = Wg<kBtThreads>;
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
@@ -191,108 +195,139 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const float* __restrict
     return;
   }
   const uint32_t need = static_cast<uint32_t>(k);
-  uint32_t above, n1, tot1;
-  const int b1 = W::find_rank_bin_regs(h1, kHistBins, need, true, wb, &above, &n1, &tot1);
-  const uint32_t rem1 = need - above;
-  uint32_t above2, n2, tot2;
-  const int b2 = W::find_rank_bin_regs(h2, kHistBins, rem1, true, wb, &above2, &n2, &tot2);
-  const uint32_t rem2 = rem1 - above2;
-  // Both histograms are left zeroed for the next call: each thread clears
-  // the bins it read.
+  // Threshold bins b1 (rank need in h1) and b2 (rank need - above(b1) in
+  // h2), counting from the top bin down, with one prefix sum of both
+  // histograms' per-thread totals: three barriers.
+  uint32_t s1 = 0, s2 = 0;
 #pragma unroll
   for (int i = 0; i < kPerBin; ++i) {
-    gh[kHistBins - 1 - (tid * kPerBin + i)] = 0u;
-    gh2[kHistBins - 1 - (tid * kPerBin + i)] = 0u;
+    s1 += h1[i];
+    s2 += h2[i];
   }
-
-  // Prefix offsets of the filter workgroups' segments (nwg <= kBtMaxWgs).
-  const int nwg = (n + kBtItems - 1) / kBtItems;
-  if (tid < 64) {
-    uint32_t ps = 0, pc = 0;
+  const int wave = tid >> 6;
+  {
+    const uint32_t i1 = wave_incl_scan_u32(s1), i2 = wave_incl_scan_u32(s2);
+    if (wl == 63) {
+      wb[wave] = i1;
+      wb[kBtWaves + wave] = i2;
+    }
+    __syncthreads();
+    uint32_t p1 = i1 - s1, p2 = i2 - s2, t1 = 0, t2 = 0;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int w = 64 * half + tid;
-      const u32x2 c2 = half ? wcb : wca;
-      const uint32_t cs = w < nwg ? c2.x : 0u, cc = w < nwg ? c2.y : 0u;
-      const uint32_t is = wave_incl_scan_u32(cs), ic = wave_incl_scan_u32(cc);
-      // Past the last segment the offsets read as "infinite", so the segment
-      // search needs no bound test.
-      off_s[w + 1] = w < nwg ? ps + is : 0xffffffffu;
-      off_c[w + 1] = w < nwg ? pc + ic : 0xffffffffu;
-      ps += __shfl(is, 63, 64);
-      pc += __shfl(ic, 63, 64);
+    for (int w = 0; w < kBtWaves; ++w) {
+      const uint32_t a = wb[w], b = wb[kBtWaves + w];
+      p1 += w < wave ? a : 0u;
+      p2 += w < wave ? b : 0u;
+      t1 += a;
+      t2 += b;
+    }
+    if (p1 < need && need <= p1 + s1) {
+      uint32_t q = p1;
+#pragma unroll
+      for (int i = 0; i < kPerBin; ++i) {
+        if (need <= q + h1[i]) {
+          res[0] = static_cast<uint32_t>(kHistBins - 1 - (tid * kPerBin + i));
+          res[1] = q;
+          res[2] = h1[i];
+          break;
+        }
+        q += h1[i];
+      }
     }
     if (tid == 0) {
-      off_s[0] = 0;
-      off_c[0] = 0;
-      fcount = 0;
+      res[6] = t1;
+      res[7] = t2;
     }
+    __syncthreads();
+    const uint32_t rem = need - res[1];
+    if (p2 < rem && rem <= p2 + s2) {
+      uint32_t q = p2;
+#pragma unroll
+      for (int i = 0; i < kPerBin; ++i) {
+        if (rem <= q + h2[i]) {
+          res[3] = static_cast<uint32_t>(kHistBins - 1 - (tid * kPerBin + i));
+          res[4] = q;
+          res[5] = h2[i];
+          break;
+        }
+        q += h2[i];
+      }
+    }
+    __syncthreads();
   }
+  // With a dirty workspace the totals differ from the counts (checked below)
+  // and these values are not used.
+  const int b1 = static_cast<int>(res[0]);
+  const uint32_t above = res[1], tot1 = res[6], tot2 = res[7];
+  const uint32_t rem1 = need - above;
+  const int b2 = static_cast<int>(res[3]);
+  const uint32_t above2 = res[4], n2 = res[5];
+  const uint32_t rem2 = rem1 - above2;
+  const int nwg = (n + kBtItems - 1) / kBtItems;
+  if (tid == 0) fcount = 0;
   const int nwords = (n + 31) >> 5;
   for (int w = tid; w < nwords; w += kBtThreads) bitmap[w] = 0u;
+  // Candidate total over the segments: every wave holds every segment's
+  // counts (lane l: segments l and l + 64) and sums them itself.
+  uint32_t cc = (wl < nwg ? wca.y : 0u) + (wl + 64 < nwg ? wcb.y : 0u);
+  const uint32_t n_cand = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(wave_incl_scan_u32(cc)), 63));
   __syncthreads();
-  const uint32_t n_sure = off_s[nwg], n_cand = off_c[nwg];
   // The histograms were complete and started from zero exactly when their
   // totals are the visible block count and the candidate count.  Otherwise
   // (a workspace not left zeroed by a previous call) the threshold is
   // resolved exactly over the whole row instead.
   const bool clean = tot1 == static_cast<uint32_t>(n) && tot2 == n_cand;
   if (clean) {
-    // Flattened item g (< off[nwg]) -> (segment w, slot g - off[w]): the last
-    // w with off[w] <= g, by a fixed-step binary search without branches
-    // (independent searches interleave).
-    auto locate = [&](const uint32_t* off, uint32_t g) {
-      int lo = 0;
-#pragma unroll
-      for (int step = kBtMaxWgs / 2; step > 0; step >>= 1)
-        lo = off[lo + step] <= g ? lo + step : lo;
-      return static_cast<size_t>(r) * nb_cap + static_cast<size_t>(lo) * kBtItems + (g - off[lo]);
+    // Wave w takes the segments w, w + 16, ...: it marks their sure items
+    // and sorts their candidates by bits [19:8] against b2 (above: marked;
+    // equal: kept in LDS for the exact resolution).  Two segments' first 64
+    // items of each kind are loaded before either is worked on; loads past a
+    // segment's count read its first item and are ignored.
+    struct Chunk {
+      int sid;
+      uint32_t ck;
+      int ci;
     };
-    // The sure items (fewer than need <= 2048, i.e. at most two per thread) and
-    // the first batch of candidates are loaded together; items past the end
-    // read slot 0 of their row's first segment and are ignored.
-    static_assert(kMaxPoolBlocks <= 2 * kBtThreads, "two sure items per thread");
-    int sid_v[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t g = tid + u * kBtThreads;
-      sid_v[u] = ws.sure[locate(off_s, g < n_sure ? g : 0u)];
-    }
-    auto cand_batch = [&](uint32_t base, uint32_t key, int id) {
-      const uint32_t g = base + tid;
-      const bool in = g < n_cand;
-      const int mb = static_cast<int>(mid_bits(key));
-      if (in && mb > b2) atomicOr(&bitmap[id >> 5], 1u << (id & 31));
+    auto load = [&](int sg, uint32_t i0, uint32_t ns, uint32_t nc) {
+      const size_t base = static_cast<size_t>(r) * nb_cap + static_cast<size_t>(sg) * kBtItems;
+      const uint32_t i = i0 + static_cast<uint32_t>(wl);
+      Chunk c;
+      c.sid = ws.sure[base + (i < ns ? i : 0u)];
+      c.ck = ws.ckey[base + (i < nc ? i : 0u)];
+      c.ci = ws.cid[base + (i < nc ? i : 0u)];
+      return c;
+    };
+    auto work = [&](const Chunk& c, uint32_t i0, uint32_t ns, uint32_t nc) {
+      const uint32_t i = i0 + static_cast<uint32_t>(wl);
+      if (i < ns) atomicOr(&bitmap[c.sid >> 5], 1u << (c.sid & 31));
+      const bool in = i < nc;
+      const int mb = static_cast<int>(mid_bits(c.ck));
+      if (in && mb > b2) atomicOr(&bitmap[c.ci >> 5], 1u << (c.ci & 31));
       const bool fin = in && mb == b2;
       const uint32_t slot = wave_append(fin, &fcount);
       if (fin && slot < static_cast<uint32_t>(kBtFinalCap)) {
-        fkey[slot] = key;
-        fid[slot] = id;
+        fkey[slot] = c.ck;
+        fid[slot] = c.ci;
       }
     };
-    {
-      // The first kCandBatches batches of candidates are loaded in one go too.
-      constexpr int kCandBatches = 4;
-      uint32_t ck[kCandBatches];
-      int ci[kCandBatches];
-#pragma unroll
-      for (int u = 0; u < kCandBatches; ++u) {
-        const uint32_t g = u * kBtThreads + tid;
-        const size_t at = locate(off_c, g < n_cand ? g : 0u);
-        ck[u] = ws.ckey[at];
-        ci[u] = ws.cid[at];
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        if (tid + u * kBtThreads < n_sure) atomicOr(&bitmap[sid_v[u] >> 5], 1u << (sid_v[u] & 31));
-#pragma unroll
-      for (int u = 0; u < kCandBatches; ++u)
-        if (u * kBtThreads < static_cast<int>(n_cand)) cand_batch(u * kBtThreads, ck[u], ci[u]);
-    }
-    for (uint32_t base = 4 * kBtThreads; base < n_cand; base += kBtThreads) {
-      const uint32_t g = base + tid;
-      const size_t at = locate(off_c, g < n_cand ? g : 0u);
-      cand_batch(base, ws.ckey[at], ws.cid[at]);
+    // Counts of segment sg (wave-uniform).
+    auto counts = [&](int sg, uint32_t* ns, uint32_t* nc) {
+      const u32x2 c2 = sg < 64 ? wca : wcb;
+      *ns = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(c2.x), sg & 63));
+      *nc = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(c2.y), sg & 63));
+    };
+    for (int s0 = wave; s0 < nwg; s0 += 2 * kBtWaves) {
+      const int s1 = s0 + kBtWaves;
+      uint32_t ns0, nc0, ns1 = 0, nc1 = 0;
+      counts(s0, &ns0, &nc0);
+      if (s1 < nwg) counts(s1, &ns1, &nc1);
+      const Chunk a = load(s0, 0, ns0, nc0);
+      const Chunk b = load(s1 < nwg ? s1 : s0, 0, ns1, nc1);
+      work(a, 0, ns0, nc0);
+      work(b, 0, ns1, nc1);
+      for (uint32_t i0 = 64; i0 < max(ns0, nc0); i0 += 64) work(load(s0, i0, ns0, nc0), i0, ns0, nc0);
+      for (uint32_t i0 = 64; i0 < max(ns1, nc1); i0 += 64) work(load(s1, i0, ns1, nc1), i0, ns1, nc1);
     }
     __syncthreads();
     const uint32_t prefix =
@@ -300,13 +335,30 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const float* __restrict
     uint32_t kstar;
     int32_t istar;
     if (n2 <= static_cast<uint32_t>(kBtFinalCap)) {
-      W::resolve(ArrayCand{fkey, fid, n2}, prefix, 8, rem2, hist256, wb, &kstar, &istar);
+      if (n2 <= static_cast<uint32_t>(kBtRankMax))
+        resolve_by_rank<kBtThreads>(fkey, fid, n2, rem2, wb, &kstar, &istar);
+      else
+        W::resolve(ArrayCand{fkey, fid, n2}, prefix, 8, rem2, hist256, wb, &kstar, &istar);
       for (uint32_t c = tid; c < n2; c += kBtThreads)
         if (selected(fkey[c], fid[c], kstar, istar))
           atomicOr(&bitmap[fid[c] >> 5], 1u << (fid[c] & 31));
     } else {
       // Degenerate input (a huge bucket of equal high bits): resolve by
-      // re-reading the candidate segments.
+      // re-reading the candidate segments, located through their prefix
+      // offsets.
+      if (tid < 64) {
+        uint32_t pc = 0;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int w = 64 * half + tid;
+          const uint32_t c1 = w < nwg ? (half ? wcb.y : wca.y) : 0u;
+          const uint32_t ic = wave_incl_scan_u32(c1);
+          off_c[w + 1] = pc + ic;
+          pc += __shfl(ic, 63, 64);
+        }
+        if (tid == 0) off_c[0] = 0;
+      }
+      __syncthreads();
       struct SegCand {
         const uint32_t* ckey;
         const int32_t* cid;
@@ -348,22 +400,60 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const float* __restrict
         atomicOr(&bitmap[i >> 5], 1u << (i & 31));
   }
   __syncthreads();
-  const int wpt = (nwords + kBtThreads - 1) / kBtThreads;
-  const int w0 = tid * wpt;
-  uint32_t c = 0;
-  for (int w = w0; w < min(w0 + wpt, nwords); ++w) c += __popc(bitmap[w]);
-  uint32_t total;
-  uint32_t off = W::excl_scan_last(c, wb, &total);
-  for (int w = w0; w < min(w0 + wpt, nwords); ++w) {
-    uint32_t bits = bitmap[w];
-    while (bits) {
-      const int b = __ffs(static_cast<int>(bits)) - 1;
-      bits &= bits - 1u;
-      if (off < need) orow[off] = w * 32 + b;
-      ++off;
+  // Compaction in block-id order.  In each pass of 4 x 1024 bitmap words,
+  // thread t takes words t, t + 1024, t + 2048 and t + 3072, so a run of
+  // selected blocks is spread over many threads; the four columns' per-thread
+  // counts are prefix-summed together (two 16-bit counts per word).
+  uint32_t written = 0;
+  for (int base = 0; base < nwords; base += 4 * kBtThreads) {
+    uint32_t wv[4], c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int w = base + tid + j * kBtThreads;
+      wv[j] = w < nwords ? bitmap[w] : 0u;
+      c[j] = static_cast<uint32_t>(__popc(wv[j]));
     }
+    const uint32_t a = c[0] | (c[1] << 16), b = c[2] | (c[3] << 16);
+    const uint32_t ia = wave_incl_scan_u32(a), ib = wave_incl_scan_u32(b);
+    if (wl == 63) {
+      wb[wave] = ia;
+      wb[kBtWaves + wave] = ib;
+    }
+    __syncthreads();
+    uint32_t pa = ia - a, pb = ib - b, ta = 0, tb = 0;
+#pragma unroll
+    for (int w = 0; w < kBtWaves; ++w) {
+      const uint32_t x = wb[w], y = wb[kBtWaves + w];
+      pa += w < wave ? x : 0u;
+      pb += w < wave ? y : 0u;
+      ta += x;
+      tb += y;
+    }
+    if (base + 4 * kBtThreads < nwords) __syncthreads();   // wb is written again
+    const uint32_t col[4] = {ta & 0xffffu, ta >> 16, tb & 0xffffu, tb >> 16};
+    uint32_t off = written;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t o = off + ((j & 1) ? ((j < 2 ? pa : pb) >> 16) : ((j < 2 ? pa : pb) & 0xffffu));
+      uint32_t bits = wv[j];
+      const int w32 = (base + tid + j * kBtThreads) * 32;
+      while (bits) {
+        const int bb = __ffs(static_cast<int>(bits)) - 1;
+        bits &= bits - 1u;
+        if (o < need) orow[o] = w32 + bb;
+        ++o;
+      }
+      off += col[j];
+    }
+    written = off;
   }
-  for (int i = static_cast<int>(min(total, need)) + tid; i < k; i += kBtThreads) orow[i] = -1;
+  for (int i = static_cast<int>(min(written, need)) + tid; i < k; i += kBtThreads) orow[i] = -1;
+  // Both histograms are left zeroed for the next call: each thread clears
+  // the four bins of each that it read, with one 16-byte store, after the
+  // output (stores issued earlier would delay the loads behind them).
+  static_assert(kPerBin == 4, "one 16-byte store per histogram");
+  *reinterpret_cast<u32x4*>(gh + kHistBins - kPerBin * (tid + 1)) = u32x4{0u, 0u, 0u, 0u};
+  *reinterpret_cast<u32x4*>(gh2 + kHistBins - kPerBin * (tid + 1)) = u32x4{0u, 0u, 0u, 0u};
 }
 
 // ---------------------------------------------------------------------------
@@ -375,7 +465,6 @@ constexpr int kPscThreads = 256;                // scoring workgroup: 4 waves x 
 constexpr int kPscWaves = kPscThreads / 64;
 constexpr int kPsSlots = 2 * 32 * kPscWaves;    // slots per scoring workgroup
 constexpr int kPsBlocks = kPsSlots / kBlock;
-constexpr int kPsMaxSlots = kMaxPoolBlocks * kBlock;
 
 struct PoolArgs {
   const float* scores;       // stored scores [rows, N_cap], or null when re-scored
@@ -438,216 +527,33 @@ __global__ __launch_bounds__(kPscThreads) void k_pool_score(PoolArgs a) {
   }
 }
 
-// Slot 16 t + e of thread t is kept at LDS index e * 1024 + t (the accesses
-// of a wave fall in distinct banks); empty slots hold key 0, which no finite
-// score has.
-__device__ __forceinline__ int pf_lds(int slot) { return (slot & 15) * 1024 + (slot >> 4); }
-struct LdsKeys {
-  const uint32_t* k;
-  uint32_t n;   // LDS entries to walk (multiple of 1024 covering every slot)
-  __device__ uint32_t key(uint32_t c) const { return k[c]; }
-  __device__ int32_t id(uint32_t c) const { return static_cast<int32_t>((c & 1023) * 16 + (c >> 10)); }
-};
-constexpr int kPfBins = 2048;
-constexpr int kPfCap = 2048;
-constexpr int kRankMax = 256;   // threshold bins up to this size are resolved by counting ranks
-
-// One workgroup per row.  Thread t holds the scores of slots [16 t, 16 t +
-// 16) (two pool blocks) in registers, with a validity mask.  The threshold is
-// found as in the flat selection: 2048 bins linear in the score value between
-// the row's min and max, exact resolution of the threshold bin's items only
-// (from LDS copies), or of every slot when that bin is too large.  The
-// selection is VALU-bound on one compute unit, so each slot costs as few
-// instructions as possible: the bins are computed once from the float scores
-// and kept in registers, invalid slots go to a spare bin (no branch around
-// the LDS atomic), and exact keys are formed only for the threshold bin.
+// One workgroup per row: the selection of pool_select.h over the row's
+// slots (16 per thread), writing the positions (and scores) in slot order.
 __global__ __launch_bounds__(kPsThreads) void k_pool_final(PoolArgs a) {
-  __shared__ uint32_t keys[kPsMaxSlots];
-  __shared__ uint32_t hist[kPfBins + 1];   // + a spare bin for invalid slots
-  __shared__ uint32_t ckey_l[kPfCap];
-  __shared__ int32_t cid_l[kPfCap];
-  __shared__ uint32_t hist256[256];
-  __shared__ uint32_t wb[Wg<kPsThreads>::kScratch];
-  __shared__ uint32_t ccount;
-  using W = Wg<kPsThreads>;
+  using PS = PoolSel<kPsThreads>;
+  __shared__ typename PS::Scratch sm;
   const int r = blockIdx.x;
-  const int tid = threadIdx.x;
   const int vis = min(max(a.vis_len[r], 0), a.N_cap);
   const int nb_cap = (a.N_cap + 7) >> 3;
   const int nslots = a.kb * kBlock;
-  const int32_t* prow = a.pool + static_cast<size_t>(r) * a.kb;
-  const float* ps = a.ps + static_cast<size_t>(r) * nslots;
-  const float* srow = a.scores ? a.scores + static_cast<size_t>(r) * a.N_cap : nullptr;
-  constexpr int kPer = kPsMaxSlots / kPsThreads;
-  static_assert(kPer == 2 * kBlock, "two pool blocks per thread");
-  const int s0 = tid * kPer;
-  const bool mine = s0 < nslots;
-  // Clamped loads (no branch per load), then a select.
-  int blk[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int bi = min((s0 >> 3) + u, a.kb - 1);
-    const int v = prow[bi];
-    blk[u] = (mine && (s0 >> 3) + u < a.kb) ? v : -1;
-  }
-  // All of a thread's score loads are issued before any is used.
-  float sv[kPer];
-  if (srow) {
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int pos = blk[e >> 3] * kBlock + (e & 7);
-      sv[e] = srow[min(max(pos, 0), vis > 0 ? vis - 1 : 0)];
-    }
-  } else if (s0 + kPer <= nslots) {
-    const f32x4_t* p4 = reinterpret_cast<const f32x4_t*>(ps + s0);
-#pragma unroll
-    for (int e4 = 0; e4 < kPer / 4; ++e4) {
-      const f32x4_t v = p4[e4];
-      sv[4 * e4] = v[0]; sv[4 * e4 + 1] = v[1]; sv[4 * e4 + 2] = v[2]; sv[4 * e4 + 3] = v[3];
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) sv[e] = ps[min(s0 + e, nslots - 1)];
-  }
-  uint32_t vm = 0;   // bit e: slot s0 + e holds a visible position
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int bk = blk[u];
-    if (bk >= 0 && bk < nb_cap) {
-      const int m = min(max(vis - bk * kBlock, 0), kBlock);   // visible positions of the block
-      vm |= ((1u << m) - 1u) << (kBlock * u);
-    }
-  }
-  float vmax = -__builtin_inff(), vmin = __builtin_inff();
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const bool v = (vm >> e) & 1u;
-    vmax = fmaxf(vmax, v ? sv[e] : -__builtin_inff());
-    vmin = fminf(vmin, v ? sv[e] : __builtin_inff());
-  }
-  uint32_t nv = static_cast<uint32_t>(__popc(vm));
-  uint32_t mx = vm ? float_to_key(vmax) : 0u, mn_inv = vm ? ~float_to_key(vmin) : 0u;
-  for (int i = tid; i <= kPfBins; i += kPsThreads) hist[i] = 0;
-  W::reduce_sum_max_max(nv, mx, mn_inv, wb);   // includes the barrier after the clear
-  const uint32_t n_valid = nv;
-  const uint32_t need = min(static_cast<uint32_t>(a.top_k), n_valid);
-  // Selection among the valid slots, by mode: 0 every one (need == n_valid);
-  // 1 bin > b1, or bin == b1 and (key, id) selected by K*, I*; 2 (threshold
-  // bin too large) (key, id) selected by K*, I*.  Bin order is key order, so
-  // every key of a higher bin exceeds every key of bin b1.
-  int mode = 0, b1 = 0;
-  uint32_t kstar = 0;
-  int32_t istar = 0x7fffffff;
-  int bin[kPer];
-  if (need > 0 && need < n_valid) {
-    mode = 1;
-    const float vhi = key_to_float(mx);
-    const float vlo = key_to_float(~mn_inv);
-    // Bins linear in the value; subtraction, scaling and truncation never
-    // reverse an order, so bin order is key order.
-    const float range = vhi - vlo;
-    const float scale = (range > 0.0f && range < __builtin_inff())
-                            ? static_cast<float>(kPfBins) * 0.99999f / range : 0.0f;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int bv = min(kPfBins - 1, max(0, static_cast<int>((sv[e] - vlo) * scale)));
-      bin[e] = ((vm >> e) & 1u) ? bv : kPfBins;
-    }
-    // A wave without a valid slot (a pool of fewer than 2,048 blocks leaves
-    // whole waves empty) adds nothing: its 1,024 atomics would all hit the
-    // spare bin one after another.
-    if (__ballot(vm != 0u) != 0) {
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) atomicAdd(&hist[bin[e]], 1u);
-    }
-    __syncthreads();
-    uint32_t above;
-    b1 = W::find_rank_bin(hist, kPfBins, need, true, wb, &above);
-    const uint32_t ncand = hist[b1];
-    if (ncand <= static_cast<uint32_t>(kPfCap)) {
-      if (tid == 0) ccount = 0;
-      __syncthreads();
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) {
-        const bool c = bin[e] == b1;
-        if (__ballot(c) == 0) continue;   // wave-uniform
-        const uint32_t slot = wave_append(c, &ccount);
-        if (c) {
-          ckey_l[slot] = float_to_key(sv[e]);
-          cid_l[slot] = s0 + e;
-        }
-      }
-      __syncthreads();
-      if (ncand <= static_cast<uint32_t>(kRankMax))
-        resolve_by_rank<kPsThreads>(ckey_l, cid_l, ncand, need - above, wb, &kstar, &istar);
-      else
-        W::resolve(ArrayCand{ckey_l, cid_l, ncand}, 0u, 32, need - above, hist256, wb, &kstar,
-                   &istar);
-    } else {
-      // A huge threshold bin (scores barely spread): resolve over every slot.
-#pragma unroll
-      for (int e = 0; e < kPer; ++e)
-        keys[e * kPsThreads + tid] = ((vm >> e) & 1u) ? float_to_key(sv[e]) : 0u;
-      __syncthreads();
-      W::resolve(LdsKeys{keys, static_cast<uint32_t>(kPsMaxSlots)}, 0u, 32, need, hist256, wb,
-                 &kstar, &istar);
-      mode = 2;
-    }
-  }
-  // Selected slots: every valid one (mode 0); bin above b1, or the exact
-  // (key, id) test inside bin b1 (mode 1); the exact test (mode 2).  The exact
-  // test runs only where a wave holds a slot of bin b1.
-  uint32_t selmask = 0;
-  if (need > 0) {
-    if (mode == 0) {
-      selmask = vm;
-    } else if (mode == 1) {
-      uint32_t eq = 0;
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) {
-        selmask |= bin[e] > b1 && bin[e] < kPfBins ? (1u << e) : 0u;
-        eq |= bin[e] == b1 ? (1u << e) : 0u;
-      }
-      if (__ballot(eq != 0) != 0) {
-#pragma unroll
-        for (int e = 0; e < kPer; ++e)
-          if (((eq >> e) & 1u) && selected(float_to_key(sv[e]), s0 + e, kstar, istar))
-            selmask |= 1u << e;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < kPer; ++e)
-        if (((vm >> e) & 1u) && selected(float_to_key(sv[e]), s0 + e, kstar, istar))
-          selmask |= 1u << e;
-    }
-  }
-  const uint32_t cnt = static_cast<uint32_t>(__popc(selmask));
-  uint32_t total;
-  uint32_t off = W::excl_scan_last(cnt, wb, &total);
+  typename PS::Row row;
+  PS::load(row, a.pool + static_cast<size_t>(r) * a.kb, a.kb,
+           a.scores ? a.scores + static_cast<size_t>(r) * a.N_cap : nullptr,
+           a.ps + static_cast<size_t>(r) * nslots, vis);
   int32_t* orow = a.out + static_cast<size_t>(r) * a.top_k;
   float* krow = a.out_key ? a.out_key + static_cast<size_t>(r) * a.top_k : nullptr;
+  uint32_t need;
   if (krow == nullptr) {
-    // Positions only: walk the set bits (slot e of block blk[e / 8]).
-    uint32_t m = selmask;
-    while (m != 0u) {
-      const int e = __builtin_ctz(m);
-      m &= m - 1u;
-      if (off < need) orow[off] = (e < kBlock ? blk[0] : blk[1]) * kBlock + (e & 7);
-      ++off;
-    }
+    need = PS::template select<false>(row, nb_cap, vis, a.top_k, sm,
+                                      [&](uint32_t off, int pos, float) { orow[off] = pos; });
   } else {
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      if ((selmask >> e) & 1u) {
-        if (off < need) {
-          orow[off] = blk[e >> 3] * kBlock + (e & 7);
-          krow[off] = sv[e];
-        }
-        ++off;
-      }
-    }
+    need = PS::template select<true>(row, nb_cap, vis, a.top_k, sm,
+                                     [&](uint32_t off, int pos, float v) {
+                                       orow[off] = pos;
+                                       krow[off] = v;
+                                     });
   }
-  for (int i = static_cast<int>(min(total, need)) + tid; i < a.top_k; i += kPsThreads) {
+  for (int i = static_cast<int>(need) + threadIdx.x; i < a.top_k; i += kPsThreads) {
     orow[i] = -1;
     if (krow) krow[i] = -__builtin_inff();
   }
