@@ -397,6 +397,21 @@ __device__ __forceinline__ void softmax_pv(const AttnArgs& a, const Ctx& x, uint
   }
 }
 
+// The pair's S = (partial of wave d = 0) + (partial of wave d = 1), the same
+// sum in both waves, through one call site: the operands are selected by
+// the wave's half (two calls would be two copies of the code, and the
+// compiler would copy the whole O^T state between their register
+// assignments every tile).
+__device__ __forceinline__ void pair_softmax_pv(const AttnArgs& a, const Ctx& x, uint32_t vm0,
+                                                uint32_t vm1, const uint8_t* tile, int off_a,
+                                                int off_b, const f32x4_t (&mine)[2],
+                                                const f32x4_t (&other)[2], State& st) {
+  const bool lo = x.d == 0;
+  const f32x4_t s0[2] = {lo ? mine[0] : other[0], lo ? mine[1] : other[1]};
+  const f32x4_t s1[2] = {lo ? other[0] : mine[0], lo ? other[1] : mine[1]};
+  softmax_pv(a, x, vm0, vm1, tile, off_a, off_b, s0, s1, st);
+}
+
 // Waits (bounded) until the LDS counter reaches `want`.  The two waves of a
 // pair synchronise only with each other through these counters, so the four
 // pairs of a workgroup run independently and the two waves that share a SIMD
@@ -436,8 +451,7 @@ __device__ __forceinline__ void round_tile(const AttnArgs& a, const Ctx& x, Smem
   signal_counter(&sm.taken[x.wave], round);
   const uint32_t vm0 = static_cast<uint32_t>(__ballot(w.valid[0])) & 0xffffu;
   const uint32_t vm1 = static_cast<uint32_t>(__ballot(w.valid[1])) & 0xffffu;
-  if (x.d == 0) softmax_pv(a, x, vm0, vm1, tile, off_a, off_b, acc, other, st);
-  else softmax_pv(a, x, vm0, vm1, tile, off_a, off_b, other, acc, st);
+  pair_softmax_pv(a, x, vm0, vm1, tile, off_a, off_b, acc, other, st);
 }
 
 template <int FMT>
@@ -541,8 +555,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
       st.exchanged = round;
       const uint32_t vm0 = static_cast<uint32_t>(__ballot(wr.valid[0])) & 0xffffu;
       const uint32_t vm1 = static_cast<uint32_t>(__ballot(wr.valid[1])) & 0xffffu;
-      if (x.d == 0) softmax_pv(a, x, vm0, vm1, tile, off_a, off_b, acc, other, st);
-      else softmax_pv(a, x, vm0, vm1, tile, off_a, off_b, other, acc, st);
+      pair_softmax_pv(a, x, vm0, vm1, tile, off_a, off_b, acc, other, st);
     }
     const int rounds = (x.sel_tiles + kPairs - 1) / kPairs;
     int t = x.pair;

@@ -57,23 +57,24 @@ struct Wg {
   static constexpr int kWaves = NT / 64;
   static constexpr int kScratch = 3 * kWaves + 4;   // uint32 words of scratch
 
-  // Exclusive prefix sum in thread order; *total receives the sum.
+  // Exclusive prefix sum in thread order; *total receives the sum.  Every
+  // wave reads all wave totals and forms its own prefix (one barrier); the
+  // second barrier leaves wb free for the next writer.
   __device__ static uint32_t excl_scan(uint32_t v, uint32_t* wb, uint32_t* total) {
     const int wave = threadIdx.x >> 6, lane = lane_id();
     const uint32_t inc = wave_incl_scan_u32(v);
     if (lane == 63) wb[wave] = inc;
     __syncthreads();
-    if (wave == 0) {
-      const uint32_t t = lane < kWaves ? wb[lane] : 0u;
-      const uint32_t ti = wave_incl_scan_u32(t);
-      if (lane < kWaves) wb[kWaves + lane] = ti - t;
-      if (lane == kWaves - 1) wb[2 * kWaves] = ti;
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t t = wb[w];
+      before += w < wave ? t : 0u;
+      tot += t;
     }
+    *total = tot;
     __syncthreads();
-    const uint32_t r = wb[kWaves + wave] + inc - v;
-    *total = wb[2 * kWaves];
-    __syncthreads();
-    return r;
+    return before + inc - v;
   }
 
   // As excl_scan with one barrier: every wave reads all wave totals and
