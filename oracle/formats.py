@@ -33,6 +33,32 @@ def bf16_to_f64(u16):
         return u.view(np.float32).astype(np.float64)
 
 
+# bf16 keeps 8 significant bits (1 implicit + 7 stored) and binary32's
+# exponent range: normal magnitudes 2^-126 .. (2 - 2^-7) 2^127, subnormal
+# steps of 2^-133.
+_BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def f64_to_bf16(x):
+    """fp64 -> bf16 bit patterns, rounded once to the nearest bf16 value (a
+    tie goes to the even significand); magnitudes past the largest finite
+    value after rounding become infinities.  Inputs must not be NaN."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.isnan(x)):
+        raise FormatError("NaN to encode")
+    mag = np.abs(x)
+    # Quantum of the binade of |x| (the spacing of bf16 values there): 2^(e - 7)
+    # with e = floor(log2 |x|), never below the subnormal step 2^-133.
+    _, e = np.frexp(np.where(mag > 0, mag, 1.0))      # mag = f 2^e, 0.5 <= f < 1
+    quantum = np.ldexp(1.0, np.maximum(e - 1, -126) - 7)
+    r = np.round(mag / quantum) * quantum              # np.round: ties to even
+    r = np.where(r > _BF16_MAX, np.inf, r)
+    r = np.where(np.signbit(x), -r, r)
+    with np.errstate(over="ignore"):
+        bits = r.astype(np.float32).view(np.uint32)    # exact: <= 8 significant bits
+    return (bits >> 16).astype(np.uint16)
+
+
 def _e4m3_value(b):
     s, e, m = b >> 7, (b >> 3) & 15, b & 7
     if e == 15 and m == 7:

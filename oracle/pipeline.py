@@ -95,6 +95,18 @@ def prefill_topk(q_raw, w, k_raw, kdtype, vis, top_k=topk.TOP_K):
     return {"scores": s, "idx": topk.flat_topk(s, vis, top_k)}
 
 
+def prefill_topk_bf16(q_raw, w, k_raw, kdtype, vis, top_k=topk.TOP_K):
+    """The BF16-score variant ([V4 essay §10.2]: index scores kept in BF16
+    instead of FP32, for a faster selector at a small loss of recall): every
+    visible entry's score rounded to bf16, then the flat Top-k over those
+    values (ties by position, as everywhere).  Its set is measured by recall
+    against prefill_topk, not by parity."""
+    s = scores_prefix(q_raw, w, k_raw, kdtype, vis)
+    sb = formats.f64_to_bf16(s)
+    return {"scores": s, "scores_bf16": sb,
+            "idx": topk.flat_topk(formats.bf16_to_f64(sb), vis, top_k)}
+
+
 def decode_main_kv(kv_fp4, kv_scale, kv_fmt="e8m0_32"):
     """Main-KV entries -> fp64: E2M1 with an E8M0 scale per 32 elements
     ("e8m0_32", OCP MXFP4) or with an E4M3 scale per 16 channels ("e4m3_16",

@@ -235,3 +235,62 @@ def test_fp4e4_encode_error_bound():
     step = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
     bound = np.where(a <= 6, step / 2, a - 6) * scale
     assert np.all(np.abs(dec - x) <= bound + 1e-12)
+
+
+# ---------------------------------------------------------------- bf16 rounding
+
+def _bf16_rne_exact(x):
+    """Nearest bf16 value of a Python float by integer arithmetic on its
+    significand (ties to the even significand), as a float; independent of
+    the oracle's encoder."""
+    import math
+    if x == 0.0 or math.isinf(x):
+        return x
+    m, e = math.frexp(abs(x))                # |x| = m 2^e, 0.5 <= m < 1
+    mant = int(m * (1 << 53))                # exact 53-bit integer
+    # bf16 keeps 8 bits in the binade; subnormal below 2^-126 (e - 1 < -126).
+    keep = 8 - max(0, -126 - (e - 1))
+    drop = 53 - keep
+    if drop <= 0:
+        return x
+    q, rem = divmod(mant, 1 << drop)
+    half = 1 << (drop - 1)
+    if rem > half or (rem == half and (q & 1)):
+        q += 1
+    v = math.ldexp(q, e - 53 + drop)
+    if v > (2.0 - 2.0 ** -7) * 2.0 ** 127:
+        v = math.inf
+    return math.copysign(v, x)
+
+
+def pin_bf16_encode(encode):
+    """Worked values (ties, subnormals, overflow, a case where rounding
+    through binary32 first would differ), agreement with torch's binary32 ->
+    bf16 cast, and with the integer-arithmetic rounding on fp64 inputs."""
+    cases = [(1.0, 0x3F80), (1.0 + 2.0 ** -8, 0x3F80), (1.0 + 3 * 2.0 ** -8, 0x3F82),
+             (-(1.0 + 2.0 ** -8), 0xBF80), (1.0 + 2.0 ** -8 + 2.0 ** -30, 0x3F81),
+             (1.0 + 2.0 ** -8 + 2.0 ** -40, 0x3F81), (2.0 ** -133, 0x0001), (2.0 ** -134, 0x0000),
+             (3 * 2.0 ** -134, 0x0002), (2.0 ** 128, 0x7F80), ((2.0 - 2.0 ** -7) * 2.0 ** 127, 0x7F7F),
+             (-0.0, 0x8000), (0.0, 0x0000), (-3.0, 0xC040)]
+    for x, bits in cases:
+        if int(encode(np.array([x]))[0]) != bits:
+            return False
+    rng = np.random.default_rng(12)
+    f32 = (rng.standard_normal(4096) * np.exp2(rng.integers(-140, 120, 4096))).astype(np.float32)
+    lib = torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if not np.array_equal(encode(f32.astype(np.float64)), lib):
+        return False
+    f64 = rng.standard_normal(4096) * np.exp2(rng.integers(-130, 100, 4096).astype(np.float64))
+    got = formats.bf16_to_f64(encode(f64))
+    want = np.array([_bf16_rne_exact(float(v)) for v in f64])
+    return np.array_equal(got, want)
+
+
+def test_bf16_encode():
+    assert pin_bf16_encode(formats.f64_to_bf16)
+
+
+def test_bf16_encode_round_trips_every_finite_pattern():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = (bits & 0x7F80) != 0x7F80
+    assert np.array_equal(formats.f64_to_bf16(formats.bf16_to_f64(bits[finite])), bits[finite])

@@ -12,6 +12,7 @@ import pytest
 import torch
 
 from oracle import attention, formats, indexer, pipeline, topk
+import test_oracle_formats as tf
 import test_oracle_pipeline as pp
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
@@ -295,7 +296,40 @@ def _attention_variant(slot_shift=0, keep_empty=False):
     return fn
 
 
+def _bf16_truncated(x):
+    x = np.asarray(x, dtype=np.float64)
+    return (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _bf16_ties_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    mag = np.abs(x)
+    _, e = np.frexp(np.where(mag > 0, mag, 1.0))
+    quantum = np.ldexp(1.0, np.maximum(e - 1, -126) - 7)
+    r = np.floor(mag / quantum + 0.5) * quantum
+    r = np.where(r > (2.0 - 2.0 ** -7) * 2.0 ** 127, np.inf, r)
+    r = np.where(np.signbit(x), -r, r)
+    with np.errstate(over="ignore"):
+        return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _bf16_through_binary32(x):
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    return formats.f64_to_bf16(x32.astype(np.float64))
+
+
+def _prefill_bf16_selects_fp64(q_raw, w, k_raw, kdtype, vis, top_k=512):
+    r = pipeline.prefill_topk_bf16(q_raw, w, k_raw, kdtype, vis, top_k)
+    r["idx"] = topk.flat_topk(r["scores"], vis, top_k)
+    return r
+
+
 MUTATIONS = [
+    ("bf16 scores truncated", tf.pin_bf16_encode, formats.f64_to_bf16, _bf16_truncated),
+    ("bf16 scores ties away", tf.pin_bf16_encode, formats.f64_to_bf16, _bf16_ties_away),
+    ("bf16 scores rounded twice", tf.pin_bf16_encode, formats.f64_to_bf16, _bf16_through_binary32),
+    ("bf16 Top-k on fp64 scores", pp.pin_prefill_topk_bf16, pipeline.prefill_topk_bf16,
+     _prefill_bf16_selects_fp64),
     ("fp8 exponent bias", _pin_e4m3, formats.e4m3_to_f64, _e4m3_bias8),
     ("fp4 nibble order", _pin_mxfp4, formats.mxfp4_to_f64, _mxfp4_swapped_nibbles),
     ("ReLU dropped", _pin_scores, indexer.index_scores, _scores_no_relu),

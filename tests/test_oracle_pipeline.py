@@ -320,6 +320,49 @@ def test_prefill_topk_against_brute_force():
     assert pin_prefill_topk(pipeline.prefill_topk)
 
 
+def _bf16_nearest(x):
+    # The nearest bf16 value by search over torch's bf16 neighbours of the
+    # binary32 cast (ties to the even pattern): independent of the oracle.
+    c = torch.tensor([x], dtype=torch.float32).to(torch.bfloat16)
+    bits = int(c.view(torch.int16).item()) & 0xFFFF
+    cands = [b & 0xFFFF for b in (bits - 1, bits, bits + 1)]
+    vals = [float(torch.tensor([b], dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+                  .to(torch.float64)) for b in cands]
+    best = min(range(3), key=lambda i: (abs(vals[i] - x), cands[i] & 1))
+    return vals[best]
+
+
+def pin_prefill_topk_bf16(fn):
+    # Brute force on the scores rounded to bf16: random keys, tie-heavy keys,
+    # and a hand-made row whose fp64 order differs from its bf16 order.
+    for seed, vis, kdtype, ties, k in ((33, 90, "bf16", False, 16), (34, 41, "fp8", True, 16),
+                                       (35, 20, "bf16", False, 24)):
+        q_raw, w, k_raw = _inputs(seed, vis + 9, kdtype, ties)
+        s = _loop_scores(_qf(q_raw), w, _torch_keys(k_raw[:vis], kdtype))
+        sb = [_bf16_nearest(float(v)) for v in s]
+        want = _padded(_sorted_pick(sb, list(range(vis)), k), k)
+        r = fn(q_raw, w, k_raw, kdtype, vis, top_k=k)
+        if r["idx"].tolist() != want:
+            return False
+        if formats.bf16_to_f64(r["scores_bf16"]).tolist() != sb:
+            return False
+    # Head 0 (weight 1) reads dim 0, head 1 (weight 2^-10) dim 1: score =
+    # (1 + 2^-7) + c 2^-10.  c = 1, 2, 3 round down to 1 + 2^-7 (a three-way
+    # tie, so positions decide), c = 4 is a tie that goes up to 1 + 2^-6.
+    c = [1.0, 3.0, 2.0, 4.0, 0.0]   # fp64 order would take positions 1 and 3
+    q = np.zeros((32, 128)); q[0, 0] = 1.0; q[1, 1] = 1.0
+    w = np.zeros(32, np.float32); w[0] = 1.0; w[1] = 2.0 ** -10
+    kf = np.zeros((5, 128)); kf[:, 0] = 1.0 + 2.0 ** -7; kf[:, 1] = c
+    q_raw = synth.to_bf16_bits(torch.from_numpy(q).float()).numpy().view(np.uint16)
+    k_raw = synth.to_bf16_bits(torch.from_numpy(kf).float()).numpy().view(np.uint16)
+    r = fn(q_raw, w, k_raw, "bf16", 5, top_k=2)
+    return r["idx"].tolist() == [0, 3]    # bf16: 3 (up), then position 0 of the tie
+
+
+def test_prefill_topk_bf16_against_brute_force():
+    assert pin_prefill_topk_bf16(pipeline.prefill_topk_bf16)
+
+
 def test_kv_append_placement_and_skip_rules():
     assert pin_kv_append(pipeline.kv_append)
 
