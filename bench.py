@@ -302,6 +302,51 @@ def fp4_recall(d, step):
             "against": "oracle Top-512 over the same keys unquantised (bf16), fp64 scores"}
 
 
+def bf16_scores_report(d, csa, torch, steps):
+    """The BF16-score variant on the prefill chunk (V4 essay §10.2): the
+    scoring call and the flat Top-512 timed with fp32 and with bf16 scores
+    (HIP events, back-to-back launches), and the recall of the bf16 path's
+    Top-512 against the oracle's fp64 Top-512 on sampled query rows."""
+    import numpy as np
+    from oracle import pipeline
+    B, n_q, N = d["B"], d["n_q"], d["kv_fp4"].shape[1]
+    vis = d["vis_len"]
+    f32 = torch.empty(B, n_q, N, dtype=torch.float32, device="cuda")
+    b16 = torch.empty(B, n_q, N, dtype=torch.int16, device="cuda")
+    idx = torch.empty(B, n_q, 512, dtype=torch.int32, device="cuda")
+    calls = {
+        "scores_fp32": lambda: csa.index_score(d["q_idx"], d["w_idx"], d["k_idx"], vis, scores=f32),
+        "scores_bf16": lambda: csa.index_score_bf16(d["q_idx"], d["w_idx"], d["k_idx"], vis, b16),
+        "select_fp32": lambda: csa.reindex_topk(csa.MODE_FULL, vis, N, 512, idx, scores=f32),
+        "select_bf16": lambda: csa.flat_topk_bf16(b16, vis, 512, idx),
+    }
+    us = {}
+    for key, fn in calls.items():
+        fn()
+        us[key] = round(timed(torch, fn, max(3, steps // 4))[0] * 1e3, 1)
+    calls["scores_bf16"]()
+    calls["select_bf16"]()
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    rows = list(range(0, n_q, max(1, n_q // 8)))[:8]
+    kr = d["k_idx"][0].cpu().numpy()
+    kr = kr.view(np.uint16) if d["kdtype"] == "bf16" else kr
+    rec = []
+    for j in rows:
+        v = int(vis[0, j])
+        ref = pipeline.prefill_topk(d["q_idx"][0, j].cpu().numpy().view(np.uint16),
+                                    d["w_idx"][0, j].cpu().numpy(), kr, d["kdtype"], v)["idx"]
+        r = ref[ref >= 0]
+        g = got[0, j][got[0, j] >= 0]
+        rec.append(len(np.intersect1d(r, g)) / max(len(r), 1))
+    return {"us": us,
+            "select_speedup": round(us["select_fp32"] / us["select_bf16"], 3),
+            "scores_speedup": round(us["scores_fp32"] / us["scores_bf16"], 3),
+            "recall": {"mean": round(float(np.mean(rec)), 5), "min": round(float(np.min(rec)), 5),
+                       "rows": len(rec),
+                       "against": "oracle Top-512 over fp64 scores (the fp32 path's definition)"}}
+
+
 def cpu_baseline(name, d, budget_s):
     """The fp64 oracle as it stands, on a bounded sample of the same workload's rows."""
     import numpy as np
@@ -553,6 +598,10 @@ def measure(name, args, torch, synth, csa, cpu=True, graph=True):
     if graph_ms is not None:
         rec["graph_ms_per_step"] = round(graph_ms, 5)
         rec["graph_value"] = round(rows / (graph_ms / 1e3), 2)
+    if name == "prefill_128k":
+        t0 = time.time()
+        rec["bf16_scores"] = bf16_scores_report(d, csa, torch, args.steps)
+        log(f"[bench] BF16 scores {rec['bf16_scores']} ({time.time() - t0:.1f} s)")
     if d.get("kdtype") == "mxfp4":
         t0 = time.time()
         rec["recall_fp4_keys"] = fp4_recall(d, step)

@@ -34,6 +34,8 @@ _F = ctypes.c_float
 
 _SIGNATURES = {
     "csa2_index_score": [_P, _P, _P, _I, _P, _P, _I, _I, _I, _P, _P, _P, _S, _P],
+    "csa2_index_score_bf16": [_P, _P, _P, _I, _P, _P, _I, _I, _I, _P, _P],
+    "csa2_flat_topk_bf16": [_P, _P, _I, _I, _I, _I, _P, _P, _P],
     "csa2_block_topk": [_P, _P, _I, _I, _I, _I, _P, _P, _S, _P],
     "csa2_block_topk_noalloc": [_P, _P, _I, _I, _I, _I, _P, _P],
     "csa2_reindex_topk": [_I, _P, _P, _P, _P, _I, _P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _S,
@@ -199,6 +201,27 @@ def index_score(q_idx, w_idx, k_idx, vis_len, scores=None, block_max=None, pagin
           _ptr(vis_len, _I32, "vis_len"), B, n_q, N_cap,
           _ptr(scores, _F32, "scores"), _ptr(block_max, _F32, "block_max"), None, 0,
           _stream(stream))
+
+
+def index_score_bf16(q_idx, w_idx, k_idx, vis_len, scores, paging=None, stream=None):
+    """The scan with scores stored as bf16 bit patterns: scores [B, n_q, N_cap]
+    (int16 / uint16 / bfloat16 GPU tensor), each the fp32 score rounded to
+    nearest even."""
+    B, n_q = q_idx.shape[0], q_idx.shape[1]
+    kp, kd, kn = _keys(k_idx)
+    N_cap = paging.n_cap if paging is not None else kn
+    _call("csa2_index_score_bf16", _ptr(q_idx, _BITS16, "q_idx"), _ptr(w_idx, _F32, "w_idx"),
+          kp, kd, _paging(paging), _ptr(vis_len, _I32, "vis_len"), B, n_q, N_cap,
+          _ptr(scores, _BITS16, "scores"), _stream(stream))
+
+
+def flat_topk_bf16(scores, vis_len, top_k, idx_out, idx_score=None, stream=None):
+    """Flat Top-top_k over bf16 scores [B, n_q, N_cap] (ties by position),
+    ascending, -1 padded; idx_score (fp32) optional."""
+    B, n_q, N_cap = scores.shape[0], scores.shape[1], scores.shape[2]
+    _call("csa2_flat_topk_bf16", _ptr(scores, _BITS16, "scores"), _ptr(vis_len, _I32, "vis_len"),
+          B, n_q, N_cap, top_k, _ptr(idx_out, _I32, "idx_out"),
+          _ptr(idx_score, _F32, "idx_score"), _stream(stream))
 
 
 def block_topk(block_max, vis_len, N_cap, k_blocks, pool_blocks, ws=None, stream=None):

@@ -93,17 +93,12 @@ csa2_status attn_common(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t*
                                            kv_fmt, pg, B, n_q, out, lse, ws, stream));
 }
 
-}  // namespace
-
-extern "C" {
-
-csa2_status csa2_index_score(const uint16_t* q_idx, const float* w_idx, const void* k_idx,
+// Validation and launch of the scan; bf16: scores are bf16 bit patterns
+// (no block maxima).
+csa2_status index_score_impl(const uint16_t* q_idx, const float* w_idx, const void* k_idx,
                              csa2_kdtype k_dtype, const csa2_paging* paging,
                              const int32_t* vis_len, int32_t B, int32_t n_q, int32_t N_cap,
-                             float* scores, float* block_max, void* ws, size_t ws_bytes,
-                             hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
+                             float* scores, float* block_max, bool bf16, hipStream_t stream) {
   if (!q_idx || !w_idx || !k_idx || !vis_len) return CSA2_ERR_NULL;
   if (!scores && !block_max) return CSA2_ERR_NULL;
   if (k_dtype != CSA2_KDTYPE_BF16 && k_dtype != CSA2_KDTYPE_FP8_E4M3 &&
@@ -123,7 +118,48 @@ csa2_status csa2_index_score(const uint16_t* q_idx, const float* w_idx, const vo
   st = check_paging(paging, N_cap, &pg);
   if (st != CSA2_OK) return st;
   return from_hip(csa2::launch_index_score(q_idx, w_idx, k_idx, static_cast<int>(k_dtype), pg,
-                                           vis_len, B, n_q, N_cap, scores, block_max, stream));
+                                           vis_len, B, n_q, N_cap, scores, block_max, stream,
+                                           bf16));
+}
+
+}  // namespace
+
+extern "C" {
+
+csa2_status csa2_index_score(const uint16_t* q_idx, const float* w_idx, const void* k_idx,
+                             csa2_kdtype k_dtype, const csa2_paging* paging,
+                             const int32_t* vis_len, int32_t B, int32_t n_q, int32_t N_cap,
+                             float* scores, float* block_max, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return index_score_impl(q_idx, w_idx, k_idx, k_dtype, paging, vis_len, B, n_q, N_cap, scores,
+                          block_max, false, stream);
+}
+
+csa2_status csa2_index_score_bf16(const uint16_t* q_idx, const float* w_idx, const void* k_idx,
+                                  csa2_kdtype k_dtype, const csa2_paging* paging,
+                                  const int32_t* vis_len, int32_t B, int32_t n_q, int32_t N_cap,
+                                  uint16_t* scores, hipStream_t stream) {
+  if (!scores) return CSA2_ERR_NULL;
+  return index_score_impl(q_idx, w_idx, k_idx, k_dtype, paging, vis_len, B, n_q, N_cap,
+                          reinterpret_cast<float*>(scores), nullptr, true, stream);
+}
+
+csa2_status csa2_flat_topk_bf16(const uint16_t* scores, const int32_t* vis_len, int32_t B,
+                                int32_t n_q, int32_t N_cap, int32_t top_k, int32_t* idx_out,
+                                float* idx_score, hipStream_t stream) {
+  if (!scores || !vis_len || !idx_out) return CSA2_ERR_NULL;
+  csa2_status st = check_rows(B, n_q);
+  if (st != CSA2_OK) return st;
+  if (N_cap < 1 || N_cap > kMaxNcap || top_k < 1 || top_k > 512) return CSA2_ERR_SHAPE;
+  const int32_t rows = B * n_q;
+  if (rows > kMaxGridY) return CSA2_ERR_SHAPE;
+  const void* ptrs[] = {scores, vis_len, idx_out, idx_score};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return CSA2_ERR_ALIGN;
+  return from_hip(csa2::launch_flat_topk(scores, vis_len, rows, N_cap, top_k, idx_out, idx_score,
+                                         stream, true));
 }
 
 csa2_status csa2_block_topk(const float* block_max, const int32_t* vis_len, int32_t B,

@@ -50,6 +50,12 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16(uint32_t w) {
   return r;
 }
 
+// fp32 -> bf16 bits, rounded to the nearest bf16 value with ties to the even
+// pattern (the gfx950 conversion instruction).
+__device__ __forceinline__ uint16_t bf16_rne_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
 // Eight FP8 bytes (two words) -> eight bf16 as an MFMA operand.
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   u32x2 a = fp8x4_to_bf16(w0), b = fp8x4_to_bf16(w1);

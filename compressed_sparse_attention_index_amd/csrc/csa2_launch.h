@@ -17,15 +17,19 @@ struct Pages {
 };
 
 // kd: csa2_kdtype (0 bf16, 1 FP8, 2 MXFP4; MXFP4 only for n_q < 16).
+// scores_bf16: `scores` receives bf16 bit patterns (2 bytes per entry, the
+// fp32 score rounded to nearest even) and block_max must be null.
 hipError_t launch_index_score(const uint16_t* q_idx, const float* w_idx, const void* k_idx,
                               int kd, const Pages& pg, const int32_t* vis_len, int B, int n_q,
-                              int N_cap, float* scores, float* block_max, hipStream_t stream);
+                              int N_cap, float* scores, float* block_max, hipStream_t stream,
+                              bool scores_bf16 = false);
 
 // Prefill-chunk scoring on matrix cores (n_q >= 16 rows per sequence); see
 // index_gemm.hip.
 hipError_t launch_index_gemm(const uint16_t* q_idx, const float* w_idx, const uint8_t* k_idx,
                              bool fp8, const Pages& pg, const int32_t* vis_len, int B, int n_q,
-                             int N_cap, float* scores, float* block_max, hipStream_t stream);
+                             int N_cap, float* scores, float* block_max, hipStream_t stream,
+                             bool scores_bf16 = false);
 
 // Block Top-K (pool of blocks); see topk.hip.
 size_t block_topk_workspace_bytes(int rows, int N_cap);
@@ -49,8 +53,10 @@ hipError_t launch_pool_topk(int mode, const float* scores, const uint16_t* q_idx
                             hipStream_t stream);
 
 // Flat Top-K over [0, vis) of every row (prefill rows).
-hipError_t launch_flat_topk(const float* scores, const int32_t* vis_len, int rows, int N_cap,
-                            int k, int32_t* out, float* out_key, hipStream_t stream);
+// bf16: `scores` holds bf16 bit patterns (uint16) instead of fp32.
+hipError_t launch_flat_topk(const void* scores, const int32_t* vis_len, int rows, int N_cap,
+                            int k, int32_t* out, float* out_key, hipStream_t stream,
+                            bool bf16 = false);
 
 size_t attn_workspace_bytes(int rows, int top_k);
 

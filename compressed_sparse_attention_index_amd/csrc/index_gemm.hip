@@ -46,6 +46,7 @@ constexpr int kChunksPerRow = 8;    // key chunks per query group (one per XCD)
 
 constexpr int kOutScores = 1;
 constexpr int kOutBlockMax = 2;
+constexpr int kOutScoresBf16 = 4;   // scores stored as bf16 (rounded to nearest even)
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -222,7 +223,8 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_index_gemm(
           qa[i][hb][ks] = __builtin_bit_cast(bf16x8, to_agpr(qv[i][hb][ks]));
   }
   const size_t nb_cap = (N_cap + 7) >> 3;
-  constexpr int per_row = ((OUT & kOutScores) ? 1 : 0) + ((OUT & kOutBlockMax) ? 1 : 0);
+  constexpr int per_row =
+      ((OUT & (kOutScores | kOutScoresBf16)) ? 1 : 0) + ((OUT & kOutBlockMax) ? 1 : 0);
 
   // Keys are worked on in quarters of 16 (quarter qq: keys 16 qq .. + 15,
   // rows 16 (qq % 4) .. + 15 of tile qq / 4).  B operands of a quarter: lane
@@ -304,6 +306,8 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_index_gemm(
         const size_t row = row0 + jw + ir;
         if constexpr (OUT & kOutScores)
           if (valid) scores[row * N_cap + key] = sc;
+        if constexpr (OUT & kOutScoresBf16)
+          if (valid) reinterpret_cast<uint16_t*>(scores)[row * N_cap + key] = bf16_rne_bits(sc);
         if constexpr (OUT & kOutBlockMax) {
           float m = valid ? sc : -__builtin_inff();
           m = fmaxf(m, wave_xor(m, 1));
@@ -382,24 +386,28 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_index_gemm(
 
 hipError_t launch_index_gemm(const uint16_t* q_idx, const float* w_idx, const uint8_t* k_idx,
                              bool fp8, const Pages& pg, const int32_t* vis_len, int B, int n_q,
-                             int N_cap, float* scores, float* block_max, hipStream_t stream) {
+                             int N_cap, float* scores, float* block_max, hipStream_t stream,
+                             bool scores_bf16) {
   const int tiles = (N_cap + 63) / 64;
   int tpw = (tiles + kChunksPerRow - 1) / kChunksPerRow;
   if (pg.bt != nullptr) tpw = tpw < 32 ? tpw : 32;   // at most 33 pages per workgroup
   const int groups = (n_q + kRowsPerWg - 1) / kRowsPerWg;
   dim3 grid((tiles + tpw - 1) / tpw, groups, B);
-  const int out = (scores != nullptr ? kOutScores : 0) | (block_max != nullptr ? kOutBlockMax : 0);
+  const int out = (scores != nullptr ? (scores_bf16 ? kOutScoresBf16 : kOutScores) : 0) |
+                  (block_max != nullptr ? kOutBlockMax : 0);
 #define CSA2_GEMM_LAUNCH(F, O)                                                                 \
   hipLaunchKernelGGL((k_index_gemm<F, O>), grid, dim3(kThreads), 0, stream, q_idx, w_idx, k_idx, \
                      pg, vis_len, n_q, N_cap, tpw, scores, block_max)
-  switch ((fp8 ? 4 : 0) | out) {
+  switch ((fp8 ? 8 : 0) | out) {
     case 1: CSA2_GEMM_LAUNCH(false, 1); break;
     case 2: CSA2_GEMM_LAUNCH(false, 2); break;
     case 3: CSA2_GEMM_LAUNCH(false, 3); break;
-    case 5: CSA2_GEMM_LAUNCH(true, 1); break;
-    case 6: CSA2_GEMM_LAUNCH(true, 2); break;
-    case 7: CSA2_GEMM_LAUNCH(true, 3); break;
-    default: return hipErrorInvalidValue;   // no output requested
+    case 4: CSA2_GEMM_LAUNCH(false, 4); break;
+    case 9: CSA2_GEMM_LAUNCH(true, 1); break;
+    case 10: CSA2_GEMM_LAUNCH(true, 2); break;
+    case 11: CSA2_GEMM_LAUNCH(true, 3); break;
+    case 12: CSA2_GEMM_LAUNCH(true, 4); break;
+    default: return hipErrorInvalidValue;   // no output, or bf16 scores with block maxima
   }
 #undef CSA2_GEMM_LAUNCH
   return hipGetLastError();

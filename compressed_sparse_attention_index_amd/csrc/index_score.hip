@@ -17,6 +17,7 @@ constexpr int kThreads = 64 * kWaves;
 
 constexpr int kOutScores = 1;
 constexpr int kOutBlockMax = 2;
+constexpr int kOutScoresBf16 = 4;   // scores stored as bf16 (rounded to nearest even)
 
 // Stores of one position's score and of its block's maximum.  Lane 0 always
 // holds a visible position of a tile that is worked on, so each requested
@@ -27,6 +28,8 @@ __device__ __forceinline__ void emit(float s, int pos, int vis, int half, int co
   const bool valid = pos < vis;
   if constexpr (OUT & kOutScores)
     if (half == 0 && valid) scores[pos] = s;
+  if constexpr (OUT & kOutScoresBf16)
+    if (half == 0 && valid) reinterpret_cast<uint16_t*>(scores)[pos] = bf16_rne_bits(s);
   if constexpr (OUT & kOutBlockMax) {
     float m = valid ? s : -__builtin_inff();
     m = fmaxf(m, wave_xor(m, 1));
@@ -75,7 +78,8 @@ __global__ __launch_bounds__(kThreads) void k_index_scan(
     const uint8_t* __restrict__ k_idx, Pages pg, const int32_t* __restrict__ vis_len, int n_q,
     int N_cap, int tiles_per_wg, float* __restrict__ scores, float* __restrict__ block_max) {
   using TT = ScanTile<KD>;
-  constexpr int kStores = ((OUT & kOutScores) ? 1 : 0) + ((OUT & kOutBlockMax) ? 1 : 0);
+  constexpr int kStores = ((OUT & (kOutScores | kOutScoresBf16)) ? 1 : 0) +
+                          ((OUT & kOutBlockMax) ? 1 : 0);
   constexpr int kSteady = DEPTH * (TT::kLoads + kStores);
   static_assert(kSteady <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][DEPTH + 1][TT::kBytes];
@@ -104,7 +108,12 @@ __global__ __launch_bounds__(kThreads) void k_index_scan(
     bool mapped;
     my_page = page_id(pg, b, page0 + lane, mapped);
   }
-  float* srow = scores ? scores + static_cast<size_t>(r) * N_cap : nullptr;
+  // Row r of the scores (bf16 scores: 2 bytes per entry).
+  float* srow = scores == nullptr ? nullptr
+                : (OUT & kOutScoresBf16)
+                    ? reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(scores) +
+                                               static_cast<size_t>(r) * N_cap)
+                    : scores + static_cast<size_t>(r) * N_cap;
   float* brow = block_max ? block_max + static_cast<size_t>(r) * ((N_cap + 7) >> 3) : nullptr;
 
   // Source offset (within a tile) of this lane for each of the tile's
@@ -194,12 +203,14 @@ int pick_tiles_per_wg(long long total_tiles, int min_tiles, int target_wgs, int 
 
 hipError_t launch_index_score(const uint16_t* q_idx, const float* w_idx, const void* k_idx,
                               int kd, const Pages& pg, const int32_t* vis_len, int B, int n_q,
-                              int N_cap, float* scores, float* block_max, hipStream_t stream) {
+                              int N_cap, float* scores, float* block_max, hipStream_t stream,
+                              bool scores_bf16) {
   const int tiles = (N_cap + 31) / 32;
   const uint8_t* kb = static_cast<const uint8_t*>(k_idx);
   if (n_q < 16) {
     const int rows = B * n_q;
-    const int out = (scores != nullptr ? kOutScores : 0) | (block_max != nullptr ? kOutBlockMax : 0);
+    const int out = (scores != nullptr ? (scores_bf16 ? kOutScoresBf16 : kOutScores) : 0) |
+                    (block_max != nullptr ? kOutBlockMax : 0);
     const int tpw = pick_tiles_per_wg(static_cast<long long>(tiles) * rows, 8, 4096, 64);
 #define CSA2_SCAN_LAUNCH(F, D, O)                                                              \
   do {                                                                                         \
@@ -207,23 +218,26 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w_idx, const v
     hipLaunchKernelGGL((k_index_scan<F, D, O>), grid, dim3(kThreads), 0, stream, q_idx, w_idx, \
                        kb, pg, vis_len, n_q, N_cap, tpw, scores, block_max);                   \
   } while (0)
-    switch (4 * kd + out) {
+    switch (8 * kd + out) {
       case 1: CSA2_SCAN_LAUNCH(kKdBf16, 1, 1); break;
       case 2: CSA2_SCAN_LAUNCH(kKdBf16, 1, 2); break;
       case 3: CSA2_SCAN_LAUNCH(kKdBf16, 1, 3); break;
-      case 5: CSA2_SCAN_LAUNCH(kKdFp8, 1, 1); break;
-      case 6: CSA2_SCAN_LAUNCH(kKdFp8, 1, 2); break;
-      case 7: CSA2_SCAN_LAUNCH(kKdFp8, 1, 3); break;
-      case 9: CSA2_SCAN_LAUNCH(kKdFp4, 1, 1); break;
-      case 10: CSA2_SCAN_LAUNCH(kKdFp4, 1, 2); break;
-      case 11: CSA2_SCAN_LAUNCH(kKdFp4, 1, 3); break;
-      default: return hipErrorInvalidValue;   // no output requested
+      case 4: CSA2_SCAN_LAUNCH(kKdBf16, 1, 4); break;
+      case 9: CSA2_SCAN_LAUNCH(kKdFp8, 1, 1); break;
+      case 10: CSA2_SCAN_LAUNCH(kKdFp8, 1, 2); break;
+      case 11: CSA2_SCAN_LAUNCH(kKdFp8, 1, 3); break;
+      case 12: CSA2_SCAN_LAUNCH(kKdFp8, 1, 4); break;
+      case 17: CSA2_SCAN_LAUNCH(kKdFp4, 1, 1); break;
+      case 18: CSA2_SCAN_LAUNCH(kKdFp4, 1, 2); break;
+      case 19: CSA2_SCAN_LAUNCH(kKdFp4, 1, 3); break;
+      case 20: CSA2_SCAN_LAUNCH(kKdFp4, 1, 4); break;
+      default: return hipErrorInvalidValue;   // no output, or bf16 scores with block maxima
     }
 #undef CSA2_SCAN_LAUNCH
   } else {
     if (kd == kKdFp4) return hipErrorInvalidValue;   // rejected by the API layer first
     return launch_index_gemm(q_idx, w_idx, kb, kd == kKdFp8, pg, vis_len, B, n_q, N_cap, scores,
-                             block_max, stream);
+                             block_max, stream, scores_bf16);
   }
   return hipGetLastError();
 }

@@ -565,15 +565,35 @@ constexpr int kFsThreads = 1024;
 constexpr int kFsCandCap = 8192;
 constexpr int kFsPer = 8;
 
+// One row of scores, fp32 or bf16 bit patterns (BF16); at(i) is the score
+// as a float (a bf16 value converts exactly).
+template <bool BF16>
+struct ScoreRow {
+  const void* p;
+  __device__ float at(int i) const {
+    if constexpr (BF16)
+      return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+    else
+      return static_cast<const float*>(p)[i];
+  }
+};
+template <bool BF16>
+__device__ __forceinline__ ScoreRow<BF16> score_row(const void* scores, int r, int N_cap) {
+  const size_t off = static_cast<size_t>(r) * N_cap * (BF16 ? 2 : 4);
+  return ScoreRow<BF16>{static_cast<const uint8_t*>(scores) + off};
+}
+
+template <bool BF16>
 struct FlatCand {
-  const float* s;
+  ScoreRow<BF16> s;
   uint32_t n;
-  __device__ uint32_t key(uint32_t i) const { return float_to_key(s[i]); }
+  __device__ uint32_t key(uint32_t i) const { return float_to_key(s.at(static_cast<int>(i))); }
   __device__ int32_t id(uint32_t i) const { return static_cast<int32_t>(i); }
 };
 
 // Gathers the items of the row whose key has `prefix` above `shift` into LDS.
-__device__ void flat_gather(const float* row, int n, uint32_t prefix, int shift, uint32_t* ckey,
+template <bool BF16>
+__device__ void flat_gather(ScoreRow<BF16> row, int n, uint32_t prefix, int shift, uint32_t* ckey,
                             int32_t* cid, uint32_t* counter) {
   const uint32_t pmask = 0xffffffffu << shift;
   for (int base = 0; base < n; base += kFsThreads * kFsPer) {
@@ -581,7 +601,7 @@ __device__ void flat_gather(const float* row, int n, uint32_t prefix, int shift,
 #pragma unroll
     for (int e = 0; e < kFsPer; ++e) {
       const int i = base + e * kFsThreads + threadIdx.x;
-      v[e] = row[min(i, n - 1)];
+      v[e] = row.at(min(i, n - 1));
       if (i >= n) v[e] = 0.0f;
     }
 #pragma unroll
@@ -598,7 +618,8 @@ __device__ void flat_gather(const float* row, int n, uint32_t prefix, int shift,
   }
 }
 
-__global__ __launch_bounds__(kFsThreads) void k_flat_select(const float* __restrict__ scores,
+template <bool BF16>
+__global__ __launch_bounds__(kFsThreads) void k_flat_select(const void* __restrict__ scores,
                                                             const int32_t* __restrict__ vis_len,
                                                             int N_cap, int k,
                                                             int32_t* __restrict__ out,
@@ -613,7 +634,7 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select(const float* __restr
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int n = min(max(vis_len[r], 0), N_cap);
-  const float* row = scores + static_cast<size_t>(r) * N_cap;
+  const ScoreRow<BF16> row = score_row<BF16>(scores, r, N_cap);
   const uint32_t need = min(static_cast<uint32_t>(k), static_cast<uint32_t>(n));
   uint32_t kstar = 0;
   int32_t istar = 0x7fffffff;
@@ -626,7 +647,7 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select(const float* __restr
 #pragma unroll
       for (int e = 0; e < kFsPer; ++e) {
         const int i = base + e * kFsThreads + tid;
-        v[e] = row[min(i, n - 1)];
+        v[e] = row.at(min(i, n - 1));
         if (i >= n) v[e] = 0.0f;
       }
 #pragma unroll
@@ -650,7 +671,7 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select(const float* __restr
 #pragma unroll
         for (int e = 0; e < kFsPer; ++e) {
           const int i = base + e * kFsThreads + tid;
-          v[e] = row[min(i, n - 1)];
+          v[e] = row.at(min(i, n - 1));
           if (i >= n) v[e] = 0.0f;
         }
 #pragma unroll
@@ -675,8 +696,8 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select(const float* __restr
       __syncthreads();
       W::resolve(ArrayCand{ckey_l, cid_l, ncand}, prefix, shift, rem, hist256, wb, &kstar, &istar);
     } else {
-      W::resolve(FlatCand{row, static_cast<uint32_t>(n)}, prefix, shift, rem, hist256, wb, &kstar,
-                 &istar);
+      W::resolve(FlatCand<BF16>{row, static_cast<uint32_t>(n)}, prefix, shift, rem, hist256, wb,
+                 &kstar, &istar);
     }
   }
   // Ordered compaction: rounds of kFsThreads * kFsPer items, thread-contiguous.
@@ -689,7 +710,7 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select(const float* __restr
 #pragma unroll
     for (int e = 0; e < kFsPer; ++e) {
       const int i = base + tid * kFsPer + e;
-      v[e] = row[min(i, n - 1)];
+      v[e] = row.at(min(i, n - 1));
       if (i >= n) v[e] = -__builtin_inff();
       c += (i < n && selected(float_to_key(v[e]), i, kstar, istar)) ? 1u : 0u;
     }
@@ -730,8 +751,9 @@ constexpr int kFrBins = 2048;
 constexpr int kFrCap = 4096;
 constexpr int kFrWords = kFrPer * kFsThreads / 32;
 
+template <bool BF16>
 __global__ __launch_bounds__(kFsThreads) void k_flat_select_reg(
-    const float* __restrict__ scores, const int32_t* __restrict__ vis_len, int N_cap, int k,
+    const void* __restrict__ scores, const int32_t* __restrict__ vis_len, int N_cap, int k,
     int32_t* __restrict__ out, float* __restrict__ out_key) {
   __shared__ uint32_t hist[kFrBins];
   __shared__ uint32_t ckey_l[kFrCap];
@@ -744,20 +766,26 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select_reg(
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int n = min(max(vis_len[r], 0), N_cap);
-  const float* row = scores + static_cast<size_t>(r) * N_cap;
+  const ScoreRow<BF16> row = score_row<BF16>(scores, r, N_cap);
   const uint32_t need = min(static_cast<uint32_t>(k), static_cast<uint32_t>(n));
 
   // Raw buffer loads: block e of 1024 items gets a descriptor sized to the
   // items left in the row, so lanes past the end read 0 without a branch,
   // every lane shares one offset register and all loads are in flight
   // together.
+  // (bf16 scores: 2-byte loads, widened to the float's bit pattern.)
+  constexpr int kEl = BF16 ? 2 : 4;
   uint32_t key[kFrPer];
 #pragma unroll
   for (int e = 0; e < kFrPer; ++e) {
     const int left = min(max(n - e * kFsThreads, 0), kFsThreads);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(row) + e * kFsThreads, static_cast<short>(0), left * 4, kRawBufferFlags);
-    key[e] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * tid, 0, 0);
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(row.p)) + kEl * e * kFsThreads,
+        static_cast<short>(0), left * kEl, kRawBufferFlags);
+    if constexpr (BF16)
+      key[e] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, 2 * tid, 0, 0)) << 16;
+    else
+      key[e] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * tid, 0, 0);
   }
 #pragma unroll
   for (int e = 0; e < kFrPer; ++e)
@@ -826,7 +854,7 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select_reg(
         W::resolve(ArrayCand{ckey_l, cid_l, ncand}, 0u, 32, need - above, hist256, wb, &kstar,
                    &istar);
     } else {
-      W::resolve(FlatCand{row, static_cast<uint32_t>(n)}, 0u, 32, need, hist256, wb, &kstar,
+      W::resolve(FlatCand<BF16>{row, static_cast<uint32_t>(n)}, 0u, 32, need, hist256, wb, &kstar,
                  &istar);
     }
   }
@@ -862,7 +890,7 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select_reg(
       const int id = 32 * (3 * tid + u) + bit;
       if (off < need) {
         orow[off] = id;
-        if (krow) krow[off] = row[id];
+        if (krow) krow[off] = row.at(id);
       }
       ++off;
     }
@@ -1021,14 +1049,22 @@ hipError_t launch_pool_topk(int mode, const float* scores, const uint16_t* q_idx
   return hipGetLastError();
 }
 
-hipError_t launch_flat_topk(const float* scores, const int32_t* vis_len, int rows, int N_cap,
-                            int k, int32_t* out, float* out_key, hipStream_t stream) {
-  if (N_cap <= kFrPer * kFsThreads)
-    hipLaunchKernelGGL(k_flat_select_reg, dim3(rows), dim3(kFsThreads), 0, stream, scores,
-                       vis_len, N_cap, k, out, out_key);
+hipError_t launch_flat_topk(const void* scores, const int32_t* vis_len, int rows, int N_cap,
+                            int k, int32_t* out, float* out_key, hipStream_t stream, bool bf16) {
+  const bool reg = N_cap <= kFrPer * kFsThreads;
+  const dim3 grid(rows), block(kFsThreads);
+  if (reg && bf16)
+    hipLaunchKernelGGL(k_flat_select_reg<true>, grid, block, 0, stream, scores, vis_len, N_cap, k,
+                       out, out_key);
+  else if (reg)
+    hipLaunchKernelGGL(k_flat_select_reg<false>, grid, block, 0, stream, scores, vis_len, N_cap, k,
+                       out, out_key);
+  else if (bf16)
+    hipLaunchKernelGGL(k_flat_select<true>, grid, block, 0, stream, scores, vis_len, N_cap, k, out,
+                       out_key);
   else
-    hipLaunchKernelGGL(k_flat_select, dim3(rows), dim3(kFsThreads), 0, stream, scores, vis_len,
-                       N_cap, k, out, out_key);
+    hipLaunchKernelGGL(k_flat_select<false>, grid, block, 0, stream, scores, vis_len, N_cap, k, out,
+                       out_key);
   return hipGetLastError();
 }
 

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 5
+#define CSA2_ABI_VERSION 6
 
 /* Symbols of the C ABI; everything else in the library is hidden. */
 #define CSA2_API __attribute__((visibility("default")))
@@ -201,6 +201,51 @@ CSA2_API csa2_status csa2_index_score(const uint16_t* q_idx, const float* w_idx,
                              const int32_t* vis_len, int32_t B, int32_t n_q,
                              int32_t N_cap, float* scores, float* block_max, void* ws,
                              size_t ws_bytes, hipStream_t stream);
+
+/*
+ * csa2_index_score_bf16 -- the scan of csa2_index_score with the scores kept
+ *   in BF16: each score s[r][t] (computed exactly as above, fp32) is stored
+ *   rounded to the nearest bf16 value (ties to the even pattern).  The
+ *   BF16-score variant of the indexer (DeepSeek-V4 essay, mlqm.cn, §10.2:
+ *   FP32 index scores replaced by BF16 make the Top-k selector about twice as
+ *   fast at a KV-entry recall of 99.7%): half the score bytes written and
+ *   read.  Opt-in: a Top-k over bf16 scores is measured by its recall against
+ *   the fp32 selection, not by parity (bf16 rounding merges close scores
+ *   into ties, which the selection then breaks by position).
+ * Arguments as csa2_index_score, except
+ *   scores    [B, n_q, N_cap] uint16 (bf16 bit patterns) output, required;
+ *             entries t >= vis_len are not written.  No block maxima.
+ * Errors as csa2_index_score (CSA2_ERR_NULL for a missing scores).
+ */
+CSA2_API csa2_status csa2_index_score_bf16(const uint16_t* q_idx, const float* w_idx,
+                                           const void* k_idx, csa2_kdtype k_dtype,
+                                           const csa2_paging* paging, const int32_t* vis_len,
+                                           int32_t B, int32_t n_q, int32_t N_cap,
+                                           uint16_t* scores, hipStream_t stream);
+
+/*
+ * csa2_flat_topk_bf16 -- the flat Top-k of csa2_reindex_topk (no pool: every
+ *   visible entry of a query row is a candidate; the encoder prefill path,
+ *   "DeepSeek-V4.1-Flash 架构详解", §3.1/§3.2) over bf16 scores: the first
+ *   min(top_k, vis_len[r]) entries in (score descending, position
+ *   ascending) order, compared as the bf16 values, reported in ascending
+ *   position order and padded with -1.  (DeepSeek-V4 essay §10.2; see
+ *   csa2_index_score_bf16.)
+ * Arguments
+ *   scores    [B, n_q, N_cap] uint16 bf16 bit patterns (device memory), as
+ *             written by csa2_index_score_bf16; entries >= vis_len not read
+ *   vis_len   [B, n_q] int32
+ *   top_k     1 .. 512
+ *   idx_out   [B, n_q, top_k] int32 output
+ *   idx_score [B, n_q, top_k] fp32 output of the selected scores (the bf16
+ *             values; -inf for padding) or NULL
+ * Errors: CSA2_ERR_NULL (scores, vis_len or idx_out missing), CSA2_ERR_SHAPE
+ *   (sizes out of range), CSA2_ERR_ALIGN (a pointer not 16-byte aligned),
+ *   CSA2_ERR_HIP (launch failure).
+ */
+CSA2_API csa2_status csa2_flat_topk_bf16(const uint16_t* scores, const int32_t* vis_len,
+                                         int32_t B, int32_t n_q, int32_t N_cap, int32_t top_k,
+                                         int32_t* idx_out, float* idx_score, hipStream_t stream);
 
 /*
  * csa2_block_topk -- first level of the Top-K: the pool of blocks.

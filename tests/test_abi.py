@@ -21,13 +21,13 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     decls = re.findall(r"CSA2_API\s+[\w\s\*]+?\b(csa2_\w+)\s*\(", open(HEADER).read())
-    assert len(decls) == 13
+    assert len(decls) == 15
     for name in decls:
         assert hasattr(L, name), name
 
 
 def test_version_and_status_strings(L):
-    assert L.csa2_abi_version() == 5
+    assert L.csa2_abi_version() == 6
     for st in range(7):
         assert len(L.csa2_status_string(st)) > 0
     assert L.csa2_status_string(0) == b"ok"
@@ -52,6 +52,30 @@ MIS = A + 4      # misaligned
 
 def _score(L, q=A, w=A, k=A, kd=1, vis=A, B=1, n_q=1, N=64, sc=A, bm=A, pg=None):
     return L.csa2_index_score(q, w, k, kd, pg, vis, B, n_q, N, sc, bm, None, 0, None)
+
+
+def test_bf16_score_entry_points_validation(L):
+    f = L.csa2_index_score_bf16
+    ok = (A, A, A, 1, None, A, 1, 1, 64, A, None)
+    def call(**kw):
+        args = list(ok)
+        for i, v in kw.items():
+            args[int(i[1:])] = v
+        return f(*args)
+    assert call(a9=None) == 1                 # scores required
+    assert call(a0=None) == 1
+    assert call(a3=5) == 3                    # key dtype
+    assert call(a6=0) == 2
+    assert call(a9=MIS) == 5
+    assert f(A, A, A, 2, None, A, 1, 16, 64, A, None) == 3   # MXFP4 keys: decode rows only
+    g = L.csa2_flat_topk_bf16
+    assert g(None, A, 1, 1, 64, 16, A, None, None) == 1
+    assert g(A, A, 1, 1, 64, 16, None, None, None) == 1
+    assert g(A, A, 1, 1, 64, 0, A, None, None) == 2
+    assert g(A, A, 1, 1, 64, 513, A, None, None) == 2
+    assert g(A, A, 0, 1, 64, 16, A, None, None) == 2
+    assert g(A, A, 1, 1, 0, 16, A, None, None) == 2
+    assert g(A, A, 1, 1, 64, 16, A, MIS, None) == 5
 
 
 def _pg(bt=A, P=64, max_pages=1, num_pages=1):
