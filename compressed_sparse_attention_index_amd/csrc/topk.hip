@@ -735,8 +735,8 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select(const void* __restri
   }
 }
 
-// Flat Top-K of rows that fit in registers (n <= kFrPer * 1024): the row is
-// read from memory once into registers (item i = e * 1024 + tid), then
+// Flat Top-K of rows that fit in registers (n <= kFrItems = 73,728): the
+// row is read from memory once into registers, then
 //   1. the row's value range [vmin, vmax] is found and the items are
 //      counted into 2048 bins spread evenly over it (bin order is key order,
 //      and the bins spread the scores, so the LDS atomics rarely collide);
@@ -745,66 +745,110 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select(const void* __restri
 //   3. the selected items are marked in an LDS bitmap over ids and written
 //      in id order after one prefix sum over the bitmap words.
 // A threshold bin too large for LDS is resolved over the whole row instead.
-constexpr int kFrPer = 72;
+// fp32 scores: 1024 threads, item e * 1024 + t is thread t's key e (72
+// keys).  bf16 scores: the keys need only 16 bits, so two share a register
+// and a workgroup of 512 threads holds 144 per thread in half the registers
+// of the fp32 form, which lets two workgroups (two rows) share a compute
+// unit; thread t's keys 2 u and 2 u + 1 are items 2 (512 u + t) and
+// 2 (512 u + t) + 1, read with one 4-byte load.
+constexpr int kFrItems = 73728;
 constexpr int kRawBufferFlags = 0x00020000;   // dword 3 of a raw (untyped) buffer descriptor
 constexpr int kFrBins = 2048;
 constexpr int kFrCap = 4096;
-constexpr int kFrWords = kFrPer * kFsThreads / 32;
+constexpr int kFrWords = kFrItems / 32;
 
 template <bool BF16>
-__global__ __launch_bounds__(kFsThreads) void k_flat_select_reg(
+struct FrShape {
+  static constexpr int kThreads = BF16 ? 512 : 1024;
+  static constexpr int kPer = kFrItems / kThreads;     // keys per thread
+  static constexpr int kRegs = BF16 ? kPer / 2 : kPer; // registers holding them
+  static constexpr int kWordsPerThread = (kFrWords + kThreads - 1) / kThreads;
+  // Item held as key e by thread t.
+  __device__ static int item(int e, int t) {
+    return BF16 ? 2 * (kThreads * (e >> 1) + t) + (e & 1) : e * kThreads + t;
+  }
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(FrShape<BF16>::kThreads, 4) void k_flat_select_reg(
     const void* __restrict__ scores, const int32_t* __restrict__ vis_len, int N_cap, int k,
     int32_t* __restrict__ out, float* __restrict__ out_key) {
+  using S = FrShape<BF16>;
+  constexpr int NT = S::kThreads;
+  constexpr int PER = S::kPer;
   __shared__ uint32_t hist[kFrBins];
   __shared__ uint32_t ckey_l[kFrCap];
   __shared__ int32_t cid_l[kFrCap];
   __shared__ uint32_t bitmap[kFrWords];
   __shared__ uint32_t hist256[256];
-  __shared__ uint32_t wb[Wg<kFsThreads>::kScratch];
+  __shared__ uint32_t wb[Wg<NT>::kScratch];
   __shared__ uint32_t ccount;
-  using W = Wg<kFsThreads>;
+  using W = Wg<NT>;
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int n = min(max(vis_len[r], 0), N_cap);
   const ScoreRow<BF16> row = score_row<BF16>(scores, r, N_cap);
   const uint32_t need = min(static_cast<uint32_t>(k), static_cast<uint32_t>(n));
 
-  // Raw buffer loads: block e of 1024 items gets a descriptor sized to the
-  // items left in the row, so lanes past the end read 0 without a branch,
-  // every lane shares one offset register and all loads are in flight
-  // together.
-  // (bf16 scores: 2-byte loads, widened to the float's bit pattern.)
-  constexpr int kEl = BF16 ? 2 : 4;
-  uint32_t key[kFrPer];
-#pragma unroll
-  for (int e = 0; e < kFrPer; ++e) {
-    const int left = min(max(n - e * kFsThreads, 0), kFsThreads);
+  // Raw buffer loads through one descriptor sized to the row's visible
+  // bytes (bf16: whole 4-byte words only; an odd last item is read on its
+  // own below): lanes past the end read 0 without a branch, every load
+  // shares the lane's offset register (load u adds a constant offset) and
+  // all are in flight together.  Keys are the order-preserving images of
+  // the scores (bf16: of the 16-bit pattern, in the register's high or low
+  // half).
+  uint32_t kr[S::kRegs];
+  {
+    const int bytes = BF16 ? (n >> 1) * 4 : n * 4;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(static_cast<const uint8_t*>(row.p)) + kEl * e * kFsThreads,
-        static_cast<short>(0), left * kEl, kRawBufferFlags);
-    if constexpr (BF16)
-      key[e] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, 2 * tid, 0, 0)) << 16;
-    else
-      key[e] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * tid, 0, 0);
-  }
+        const_cast<void*>(row.p), static_cast<short>(0), bytes, kRawBufferFlags);
 #pragma unroll
-  for (int e = 0; e < kFrPer; ++e)
-    key[e] = e * kFsThreads + tid < n ? float_to_key(__builtin_bit_cast(float, key[e])) : 0u;
+    for (int u = 0; u < S::kRegs; ++u)
+      kr[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * tid, 4 * NT * u, 0);
+  }
+  if constexpr (BF16) {
+    if (n & 1) {
+      // Item n - 1 is the low half of word (n - 1) / 2, which the
+      // descriptor left out: its thread reads it alone (a select per
+      // register keeps the index constant).
+      const int w = (n - 1) >> 1;
+      if (tid == w % NT) {
+        const uint32_t v = static_cast<const uint16_t*>(row.p)[n - 1];
+#pragma unroll
+        for (int u = 0; u < S::kRegs; ++u) kr[u] = (u == w / NT) ? v : kr[u];
+      }
+    }
+  }
+  auto key = [&](int e) -> uint32_t {   // e: compile-time constant after unrolling
+    if constexpr (BF16) {
+      const uint32_t bits = (e & 1) ? (kr[e >> 1] & 0xffff0000u) : (kr[e >> 1] << 16);
+      return float_to_key(__builtin_bit_cast(float, bits));
+    } else {
+      return kr[e];
+    }
+  };
+  if constexpr (!BF16) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+      kr[e] = S::item(e, tid) < n ? float_to_key(__builtin_bit_cast(float, kr[e])) : 0u;
+  }
+  // Items past the row: key 0 (never selected: need <= n items rank above).
+  auto valid = [&](int e) { return S::item(e, tid) < n; };
 
   // Every item is taken when need == n: K* = 0, I* = max.
   uint32_t kstar = 0;
   int32_t istar = 0x7fffffff;
   if (need > 0 && need < static_cast<uint32_t>(n)) {
     uint32_t mx = 0, mn_inv = 0, unused = 0;
-    const int full = n / kFsThreads;   // blocks with every item inside the row
 #pragma unroll
-    for (int e = 0; e < kFrPer; ++e) {
-      if (e < full || e * kFsThreads + tid < n) {
-        mx = max(mx, key[e]);
-        mn_inv = max(mn_inv, ~key[e]);
+    for (int e = 0; e < PER; ++e) {
+      if (valid(e)) {
+        const uint32_t kk = key(e);
+        mx = max(mx, kk);
+        mn_inv = max(mn_inv, ~kk);
       }
     }
-    for (int i = tid; i < kFrBins; i += kFsThreads) hist[i] = 0;
+    for (int i = tid; i < kFrBins; i += NT) hist[i] = 0;
     W::reduce_sum_max_max(unused, mx, mn_inv, wb);
     const float vmax = key_to_float(mx);
     const float vmin = key_to_float(~mn_inv);
@@ -821,8 +865,8 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select_reg(
       return min(kFrBins - 1, max(0, static_cast<int>(x)));
     };
 #pragma unroll
-    for (int e = 0; e < kFrPer; ++e)
-      if (e * kFsThreads + tid < n) atomicAdd(&hist[bin_of(key[e])], 1u);
+    for (int e = 0; e < PER; ++e)
+      if (valid(e)) atomicAdd(&hist[bin_of(key(e))], 1u);
     __syncthreads();
     uint32_t above;
     const int b1 = W::find_rank_bin(hist, kFrBins, need, true, wb, &above);
@@ -837,19 +881,20 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select_reg(
                                ? float_to_key(vmin + (static_cast<float>(b1) - 1.0f) / scale)
                                : 0u;
 #pragma unroll
-      for (int e = 0; e < kFrPer; ++e) {
-        if (__ballot(key[e] >= klo) == 0) continue;   // wave-uniform
-        const int i = e * kFsThreads + tid;
-        const bool c = i < n && bin_of(key[e]) == b1;
+      for (int e = 0; e < PER; ++e) {
+        const uint32_t kk = key(e);
+        if (__ballot(kk >= klo) == 0) continue;   // wave-uniform
+        const int i = S::item(e, tid);
+        const bool c = i < n && bin_of(kk) == b1;
         const uint32_t slot = wave_append(c, &ccount);
         if (c) {
-          ckey_l[slot] = key[e];
+          ckey_l[slot] = kk;
           cid_l[slot] = i;
         }
       }
       __syncthreads();
       if (ncand <= static_cast<uint32_t>(kRankMax))
-        resolve_by_rank<kFsThreads>(ckey_l, cid_l, ncand, need - above, wb, &kstar, &istar);
+        resolve_by_rank<NT>(ckey_l, cid_l, ncand, need - above, wb, &kstar, &istar);
       else
         W::resolve(ArrayCand{ckey_l, cid_l, ncand}, 0u, 32, need - above, hist256, wb, &kstar,
                    &istar);
@@ -859,21 +904,24 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select_reg(
     }
   }
 
-  // Ordered output through a bitmap over ids: thread t owns words 3t .. 3t+2.
-  for (int w = tid; w < kFrWords; w += kFsThreads) bitmap[w] = 0;
+  // Ordered output through a bitmap over ids: thread t owns words
+  // kWordsPerThread t .. + kWordsPerThread - 1.
+  for (int w = tid; w < kFrWords; w += NT) bitmap[w] = 0;
   __syncthreads();
 #pragma unroll
-  for (int e = 0; e < kFrPer; ++e) {
-    if (__ballot(key[e] >= kstar) == 0) continue;   // selected items have key >= K*
-    const int i = e * kFsThreads + tid;
-    if (i < n && selected(key[e], i, kstar, istar)) atomicOr(&bitmap[i >> 5], 1u << (i & 31));
+  for (int e = 0; e < PER; ++e) {
+    const uint32_t kk = key(e);
+    if (__ballot(kk >= kstar) == 0) continue;   // selected items have key >= K*
+    const int i = S::item(e, tid);
+    if (i < n && selected(kk, i, kstar, istar)) atomicOr(&bitmap[i >> 5], 1u << (i & 31));
   }
   __syncthreads();
-  uint32_t words[3] = {0, 0, 0};
+  constexpr int WPT = S::kWordsPerThread;
+  uint32_t words[WPT];
   uint32_t cnt = 0;
 #pragma unroll
-  for (int u = 0; u < 3; ++u) {
-    const int w = 3 * tid + u;
+  for (int u = 0; u < WPT; ++u) {
+    const int w = WPT * tid + u;
     words[u] = w < kFrWords ? bitmap[w] : 0u;
     cnt += __popc(words[u]);
   }
@@ -882,12 +930,12 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select_reg(
   int32_t* orow = out + static_cast<size_t>(r) * k;
   float* krow = out_key ? out_key + static_cast<size_t>(r) * k : nullptr;
 #pragma unroll
-  for (int u = 0; u < 3; ++u) {
+  for (int u = 0; u < WPT; ++u) {
     uint32_t m = words[u];
     while (m != 0) {
       const int bit = __ffs(m) - 1;
       m &= m - 1;
-      const int id = 32 * (3 * tid + u) + bit;
+      const int id = 32 * (WPT * tid + u) + bit;
       if (off < need) {
         orow[off] = id;
         if (krow) krow[off] = row.at(id);
@@ -895,7 +943,7 @@ __global__ __launch_bounds__(kFsThreads) void k_flat_select_reg(
       ++off;
     }
   }
-  for (int i = static_cast<int>(min(total, need)) + tid; i < k; i += kFsThreads) {
+  for (int i = static_cast<int>(min(total, need)) + tid; i < k; i += NT) {
     orow[i] = -1;
     if (krow) krow[i] = -__builtin_inff();
   }
@@ -1051,14 +1099,14 @@ hipError_t launch_pool_topk(int mode, const float* scores, const uint16_t* q_idx
 
 hipError_t launch_flat_topk(const void* scores, const int32_t* vis_len, int rows, int N_cap,
                             int k, int32_t* out, float* out_key, hipStream_t stream, bool bf16) {
-  const bool reg = N_cap <= kFrPer * kFsThreads;
+  const bool reg = N_cap <= kFrItems;
   const dim3 grid(rows), block(kFsThreads);
   if (reg && bf16)
-    hipLaunchKernelGGL(k_flat_select_reg<true>, grid, block, 0, stream, scores, vis_len, N_cap, k,
-                       out, out_key);
+    hipLaunchKernelGGL(k_flat_select_reg<true>, grid, dim3(FrShape<true>::kThreads), 0, stream,
+                       scores, vis_len, N_cap, k, out, out_key);
   else if (reg)
-    hipLaunchKernelGGL(k_flat_select_reg<false>, grid, block, 0, stream, scores, vis_len, N_cap, k,
-                       out, out_key);
+    hipLaunchKernelGGL(k_flat_select_reg<false>, grid, dim3(FrShape<false>::kThreads), 0, stream,
+                       scores, vis_len, N_cap, k, out, out_key);
   else if (bf16)
     hipLaunchKernelGGL(k_flat_select<true>, grid, block, 0, stream, scores, vis_len, N_cap, k, out,
                        out_key);
