@@ -129,6 +129,7 @@ class Step:
         self.name, self.d, self.csa, self.torch = name, d, csa, torch
         self.sets = sets or [d]
         self.turn = 0
+        self._calls = {}
         dev = "cuda"
         B, n_q = d["B"], d["n_q"]
         self.B, self.n_q = B, n_q
@@ -201,12 +202,17 @@ class Step:
     def run(self, full_only=False):
         d, csa = self._next(), self.csa
         if self.name == "decoder_1m":
+            if id(d) not in self._calls:
+                self._calls[id(d)] = [
+                    (csa.layer_mode(e["layer"]),
+                     csa.layer_call(self.state, d["k_idx"], d["kv_fp4"], d["kv_scale"],
+                                    d["vis_len"], e["q"], e["swa"], d["swa_pos0"], d["q_pos"],
+                                    d["sm_scale"], self.out, lse=self.lse, q_idx=e.get("q_idx"),
+                                    w_idx=e.get("w_idx")))
+                    for e in d["layers"]]
             self.state.struct.has_pool = self.state.struct.has_idx = 0
-            for e in d["layers"]:
-                csa.run_layer(csa.layer_mode(e["layer"]), self.state, d["k_idx"], d["kv_fp4"],
-                              d["kv_scale"], d["vis_len"], e["q"], e["swa"], d["swa_pos0"],
-                              d["q_pos"], d["sm_scale"], self.out, lse=self.lse,
-                              q_idx=e.get("q_idx"), w_idx=e.get("w_idx"))
+            for mode, call in self._calls[id(d)]:
+                call.run(mode)
             return
         if self.name == "kv_append_64k":
             csa.kv_append(d["kv_new"], d["pos"], d["kv_fp4"], d["kv_scale"], swa_new=d["swa_new"],
@@ -220,15 +226,26 @@ class Step:
             csa.reindex_topk(csa.MODE_FULL, d["vis_len"], self.N, 512, self.idx, scores=self.scores)
             self._attn(d, csa.sparse_attn_decode, d["q"], d["swa"], self.idx, self.out, self.lse)
             return
-        fmt = csa.KV_FP4_E4M3_16 if d.get("kv_fmt") == "e4m3_16" else csa.KV_MXFP4_E8M0_32
-        layer = lambda mode, q_idx, w_idx, q, swa, out, lse: csa.run_layer(
-            mode, self.state, d["k_idx"], d["kv_fp4"], d["kv_scale"], d["vis_len"], q, swa,
-            d["swa_pos0"], d["q_pos"], d["sm_scale"], out, lse=lse, q_idx=q_idx, w_idx=w_idx,
-            kv_fmt=fmt)
-        layer(csa.MODE_FULL, d["q_idx"], d["w_idx"], d["q"], d["swa"], self.out, self.lse)
-        if "q_idx2" in d and not full_only:
-            layer(csa.MODE_REINDEX, d["q_idx2"], d["w_idx2"], d["q2"], d["swa2"], self.out2,
-                  self.lse2)
+        full, reindex = self._layer_calls(d)
+        full.run(csa.MODE_FULL)
+        if reindex is not None and not full_only:
+            reindex.run(csa.MODE_REINDEX)
+
+    def _layer_calls(self, d):
+        """The Full (and Reindex) layer calls of an input set, prepared once."""
+        key = id(d)
+        if key not in self._calls:
+            csa = self.csa
+            fmt = csa.KV_FP4_E4M3_16 if d.get("kv_fmt") == "e4m3_16" else csa.KV_MXFP4_E8M0_32
+            mk = lambda q_idx, w_idx, q, swa, out, lse: csa.layer_call(
+                self.state, d["k_idx"], d["kv_fp4"], d["kv_scale"], d["vis_len"], q, swa,
+                d["swa_pos0"], d["q_pos"], d["sm_scale"], out, lse=lse, q_idx=q_idx, w_idx=w_idx,
+                kv_fmt=fmt)
+            full = mk(d["q_idx"], d["w_idx"], d["q"], d["swa"], self.out, self.lse)
+            reindex = (mk(d["q_idx2"], d["w_idx2"], d["q2"], d["swa2"], self.out2, self.lse2)
+                       if "q_idx2" in d else None)
+            self._calls[key] = (full, reindex)
+        return self._calls[key]
 
 
 def algorithmic(name, d):

@@ -346,11 +346,12 @@ class LayerState:
             top_k, self.ws.data_ptr(), self.ws.numel(), 0, 0)
 
 
-def run_layer(mode, state, k_idx, kv_fp4, kv_scale, vis_len, q, swa_kv, swa_pos0, q_pos,
-              sm_scale, out, lse=None, q_idx=None, w_idx=None, kv_fmt=KV_MXFP4_E8M0_32,
-              window=128, replay_start=-1, sink=None, k_paging=None, kv_paging=None,
-              stream=None):
-    """One layer's CSA2 work by mode (include/csa2.h, csa2_run_layer)."""
+def layer_call(state, k_idx, kv_fp4, kv_scale, vis_len, q, swa_kv, swa_pos0, q_pos, sm_scale,
+               out, lse=None, q_idx=None, w_idx=None, kv_fmt=KV_MXFP4_E8M0_32, window=128,
+               replay_start=-1, sink=None, k_paging=None, kv_paging=None):
+    """A prepared csa2_run_layer call: the arguments are checked and packed
+    once; LayerCall.run(mode, stream) then makes only the C call (for loops
+    that issue the same layer's call on the same buffers many times)."""
     B, n_q = q.shape[0], q.shape[1]
     N_cap = kv_paging.n_cap if kv_paging is not None else kv_fp4.shape[1]
     kp, kd, _ = _keys(k_idx)
@@ -362,5 +363,32 @@ def run_layer(mode, state, k_idx, kv_fp4, kv_scale, vis_len, q, swa_kv, swa_pos0
                   _ptr(w_idx, _F32, "w_idx"), _ptr(q, _BITS16, "q"), _ptr(swa_kv, _U8, "swa_kv"),
                   swa_kv.shape[1], _ptr(swa_pos0, _I32, "swa_pos0"), _ptr(q_pos, _I32, "q_pos"),
                   float(sm_scale), window, replay_start, _ptr(sink, _F32, "sink"), B, n_q)
-    _call("csa2_run_layer", mode, ctypes.byref(a), ctypes.byref(state.struct),
-          _ptr(out, _BITS16, "out"), _ptr(lse, _F32, "lse"), _stream(stream))
+    return LayerCall(a, state, _ptr(out, _BITS16, "out"), _ptr(lse, _F32, "lse"),
+                     (k_idx, kv_fp4, kv_scale, vis_len, q, swa_kv, swa_pos0, q_pos, out, lse,
+                      q_idx, w_idx, sink, k_paging, kv_paging))
+
+
+class LayerCall:
+    """See layer_call; holds references to the tensors it points to."""
+
+    def __init__(self, args, state, out_ptr, lse_ptr, keep):
+        self.args, self.state, self.keep = args, state, keep
+        self._a, self._s = ctypes.byref(args), ctypes.byref(state.struct)
+        self._out, self._lse = out_ptr, lse_ptr
+        self._fn = lib().csa2_run_layer
+
+    def run(self, mode, stream=None):
+        st = self._fn(mode, self._a, self._s, self._out, self._lse, _stream(stream))
+        if st != 0:
+            raise Csa2Error("csa2_run_layer", st, lib().csa2_status_string(st).decode())
+
+
+def run_layer(mode, state, k_idx, kv_fp4, kv_scale, vis_len, q, swa_kv, swa_pos0, q_pos,
+              sm_scale, out, lse=None, q_idx=None, w_idx=None, kv_fmt=KV_MXFP4_E8M0_32,
+              window=128, replay_start=-1, sink=None, k_paging=None, kv_paging=None,
+              stream=None):
+    """One layer's CSA2 work by mode (include/csa2.h, csa2_run_layer)."""
+    layer_call(state, k_idx, kv_fp4, kv_scale, vis_len, q, swa_kv, swa_pos0, q_pos, sm_scale,
+               out, lse=lse, q_idx=q_idx, w_idx=w_idx, kv_fmt=kv_fmt, window=window,
+               replay_start=replay_start, sink=sink, k_paging=k_paging,
+               kv_paging=kv_paging).run(mode, stream)

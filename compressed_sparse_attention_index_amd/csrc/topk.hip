@@ -279,11 +279,14 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const float* __restrict
   // resolved exactly over the whole row instead.
   const bool clean = tot1 == static_cast<uint32_t>(n) && tot2 == n_cand;
   if (clean) {
-    // Wave w takes the segments w, w + 16, ...: it marks their sure items
-    // and sorts their candidates by bits [19:8] against b2 (above: marked;
-    // equal: kept in LDS for the exact resolution).  Two segments' first 64
-    // items of each kind are loaded before either is worked on; loads past a
-    // segment's count read its first item and are ignored.
+    // The segments' items are cut into chunks of 64 (a segment has
+    // ceil(max(sure, candidates) / 64) chunks); wave w takes chunks w, w + 16,
+    // ... and, per chunk, marks its sure items and sorts its candidates by
+    // bits [19:8] against b2 (above: marked; equal: kept in LDS for the exact
+    // resolution).  A chunk's segment is found from the chunk counts' prefix
+    // sums, which every wave forms itself (lane l: segments l and l + 64), by
+    // one ballot.  Two chunks are loaded before either is worked on; loads
+    // past a segment's count read its first item and are ignored.
     struct Chunk {
       int sid;
       uint32_t ck;
@@ -311,23 +314,46 @@ __global__ __launch_bounds__(kBtThreads) void k_bt_final(const float* __restrict
         fid[slot] = c.ci;
       }
     };
-    // Counts of segment sg (wave-uniform).
-    auto counts = [&](int sg, uint32_t* ns, uint32_t* nc) {
-      const u32x2 c2 = sg < 64 ? wca : wcb;
-      *ns = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(c2.x), sg & 63));
-      *nc = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(c2.y), sg & 63));
+    auto chunks = [](u32x2 c) { return (max(c.x, c.y) + 63u) >> 6; };
+    const uint32_t cha = wl < nwg ? chunks(wca) : 0u, chb = wl + 64 < nwg ? chunks(wcb) : 0u;
+    const uint32_t pa = wave_incl_scan_u32(cha);
+    const uint32_t tot_a = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(pa), 63));
+    const uint32_t pb = wave_incl_scan_u32(chb) + tot_a;
+    const uint32_t n_chunks =
+        static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(pb), 63));
+    // Chunk c (wave-uniform) -> its segment, first item and the segment's counts.
+    auto locate = [&](uint32_t c, int* sg, uint32_t* i0, uint32_t* ns, uint32_t* nc) {
+      const uint64_t ma = __ballot(pa > c);
+      uint32_t before;
+      u32x2 cnt;
+      if (ma != 0) {
+        const int s0 = __ffsll(static_cast<long long>(ma)) - 1;
+        before = s0 ? static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(pa), s0 - 1))
+                    : 0u;
+        *sg = s0;
+        cnt = wca;
+      } else {
+        const int s0 = __ffsll(static_cast<long long>(__ballot(pb > c))) - 1;
+        before = s0 ? static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(pb), s0 - 1))
+                    : tot_a;
+        *sg = 64 + s0;
+        cnt = wcb;
+      }
+      const int ln = *sg & 63;
+      *ns = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(cnt.x), ln));
+      *nc = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(cnt.y), ln));
+      *i0 = (c - before) * 64u;
     };
-    for (int s0 = wave; s0 < nwg; s0 += 2 * kBtWaves) {
-      const int s1 = s0 + kBtWaves;
-      uint32_t ns0, nc0, ns1 = 0, nc1 = 0;
-      counts(s0, &ns0, &nc0);
-      if (s1 < nwg) counts(s1, &ns1, &nc1);
-      const Chunk a = load(s0, 0, ns0, nc0);
-      const Chunk b = load(s1 < nwg ? s1 : s0, 0, ns1, nc1);
-      work(a, 0, ns0, nc0);
-      work(b, 0, ns1, nc1);
-      for (uint32_t i0 = 64; i0 < max(ns0, nc0); i0 += 64) work(load(s0, i0, ns0, nc0), i0, ns0, nc0);
-      for (uint32_t i0 = 64; i0 < max(ns1, nc1); i0 += 64) work(load(s1, i0, ns1, nc1), i0, ns1, nc1);
+    for (uint32_t c0 = static_cast<uint32_t>(wave); c0 < n_chunks; c0 += 2 * kBtWaves) {
+      const uint32_t c1 = c0 + kBtWaves;
+      int sg0, sg1 = 0;
+      uint32_t i00, ns0, nc0, i01 = 0, ns1 = 0, nc1 = 0;
+      locate(c0, &sg0, &i00, &ns0, &nc0);
+      if (c1 < n_chunks) locate(c1, &sg1, &i01, &ns1, &nc1);
+      const Chunk a = load(sg0, i00, ns0, nc0);
+      const Chunk b = load(c1 < n_chunks ? sg1 : sg0, i01, ns1, nc1);
+      work(a, i00, ns0, nc0);
+      work(b, i01, ns1, nc1);
     }
     __syncthreads();
     const uint32_t prefix =
