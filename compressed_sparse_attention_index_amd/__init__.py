@@ -203,6 +203,31 @@ def index_score(q_idx, w_idx, k_idx, vis_len, scores=None, block_max=None, pagin
           _stream(stream))
 
 
+class PreparedCall:
+    """A C call with its arguments checked and packed once; run() makes only
+    the call, on the current stream (or `stream`)."""
+
+    def __init__(self, name, args, keep):
+        self._fn, self._name, self._args, self.keep = getattr(lib(), name), name, args, keep
+
+    def run(self, stream=None):
+        st = self._fn(*self._args, _stream(stream))
+        if st != 0:
+            raise Csa2Error(self._name, st, lib().csa2_status_string(st).decode())
+
+
+def index_score_call(q_idx, w_idx, k_idx, vis_len, scores=None, block_max=None, paging=None):
+    """index_score prepared once (see PreparedCall)."""
+    B, n_q = q_idx.shape[0], q_idx.shape[1]
+    kp, kd, kn = _keys(k_idx)
+    N_cap = paging.n_cap if paging is not None else kn
+    args = (_ptr(q_idx, _BITS16, "q_idx"), _ptr(w_idx, _F32, "w_idx"), kp, kd, _paging(paging),
+            _ptr(vis_len, _I32, "vis_len"), B, n_q, N_cap, _ptr(scores, _F32, "scores"),
+            _ptr(block_max, _F32, "block_max"), None, 0)
+    return PreparedCall("csa2_index_score", args,
+                        (q_idx, w_idx, k_idx, vis_len, scores, block_max, paging))
+
+
 def index_score_bf16(q_idx, w_idx, k_idx, vis_len, scores, paging=None, stream=None):
     """The scan with scores stored as bf16 bit patterns: scores [B, n_q, N_cap]
     (int16 / uint16 / bfloat16 GPU tensor), each the fp32 score rounded to
