@@ -58,6 +58,9 @@ def parse():
                    help="skip the 128K points (Reuse decode, prefill chunk) of the default line")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a 1 GiB device copy (reference for the traffic counters)")
+    p.add_argument("--calibrate-mfma", action="store_true",
+                   help="also time library bf16 GEMMs (torch.matmul): a square one, the "
+                        "practical matrix-core rate, and the indexer contraction unfused")
     return p.parse_args()
 
 
@@ -571,6 +574,8 @@ def measure(name, args, torch, synth, csa, cpu=True, graph=True):
         torch.cuda.synchronize()
         del src, dst
 
+    mfma_cal = mfma_calibration(torch, args.steps) if args.calibrate_mfma else None
+
     append = name == "kv_append_64k"
     rows = step.rows
     unit = "tokens/s" if append else "query-tokens/s"
@@ -620,6 +625,8 @@ def measure(name, args, torch, synth, csa, cpu=True, graph=True):
     rec = {"value": round(rows / (ms / 1e3), 2), "unit": unit, "ms_per_step": round(ms, 5),
            "ms_per_step_p10": round(p10, 5), "ms_per_step_p90": round(p90, 5),
            "config": cfg, "roofline": roof, "cpu_baseline": cpu_rec}
+    if mfma_cal is not None:
+        rec["mfma_calibration"] = mfma_cal
     if graph_ms is not None:
         rec["graph_ms_per_step"] = round(graph_ms, 5)
         rec["graph_value"] = round(rows / (graph_ms / 1e3), 2)
@@ -635,6 +642,35 @@ def measure(name, args, torch, synth, csa, cpu=True, graph=True):
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return rec
+
+
+def mfma_calibration(torch, steps):
+    """Library bf16 GEMMs (torch.matmul, hipBLASLt) timed like the dominant
+    calls: an 8192^3 square product, the matrix-core rate a tuned dense GEMM
+    reaches here, and the prefill indexer's contraction without its fused
+    epilogue (4096 rows x 32 heads against 67,584 keys over 128 dims, bf16
+    head scores written out), the unfused alternative's first step."""
+    out = {"kernel": "torch.matmul bf16 (hipBLASLt)", "peak_tflops": BF16_PEAK_TFLOPS}
+    g = torch.Generator(device="cuda").manual_seed(7)
+    for tag, m, k, n in (("square_8192", 8192, 8192, 8192),
+                         ("indexer_heads_unfused", 4096 * 32, 128, 67584)):
+        a = torch.randn(m, k, device="cuda", generator=g).to(torch.bfloat16)
+        b = torch.randn(n, k, device="cuda", generator=g).to(torch.bfloat16)
+        bt = b.t().contiguous()   # (k, n)
+        c = torch.empty(m, n, device="cuda", dtype=torch.bfloat16)
+        fn = lambda: torch.matmul(a, bt, out=c)
+        for _ in range(3):
+            fn()
+        ms = timed(torch, fn, max(3, min(steps, 10)))[0]
+        flops = 2.0 * m * k * n
+        tf = flops / (ms / 1e3) / 1e12
+        out[tag] = {"m": m, "k": k, "n": n, "ms": round(ms, 4), "tflops": round(tf, 1),
+                    "frac": round(tf / BF16_PEAK_TFLOPS, 4), "out_bytes": m * n * 2}
+        log(f"[bench] calibration {tag}: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+        del a, b, bt, c
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
