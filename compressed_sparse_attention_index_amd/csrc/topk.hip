@@ -845,35 +845,43 @@ __global__ __launch_bounds__(FrShape<BF16>::kThreads, 4) void k_flat_select_reg(
       }
     }
   }
-  auto key = [&](int e) -> uint32_t {   // e: compile-time constant after unrolling
-    if constexpr (BF16) {
-      const uint32_t bits = (e & 1) ? (kr[e >> 1] & 0xffff0000u) : (kr[e >> 1] << 16);
-      return float_to_key(__builtin_bit_cast(float, bits));
-    } else {
-      return kr[e];
-    }
+  // Item e's score (e: a compile-time constant after unrolling); the bins
+  // and the range work on the scores, and order keys are formed only where
+  // items are compared.  Items past the row (read as 0) are never counted
+  // or selected.
+  auto val = [&](int e) -> float {
+    if constexpr (BF16)
+      return __builtin_bit_cast(float, (e & 1) ? (kr[e >> 1] & 0xffff0000u) : (kr[e >> 1] << 16));
+    else
+      return __builtin_bit_cast(float, kr[e]);
   };
-  if constexpr (!BF16) {
-#pragma unroll
-    for (int e = 0; e < PER; ++e)
-      kr[e] = S::item(e, tid) < n ? float_to_key(__builtin_bit_cast(float, kr[e])) : 0u;
-  }
-  // Items past the row: key 0 (never selected: need <= n items rank above).
+  auto key = [&](int e) -> uint32_t { return float_to_key(val(e)); };
   auto valid = [&](int e) { return S::item(e, tid) < n; };
 
   // Every item is taken when need == n: K* = 0, I* = max.
   uint32_t kstar = 0;
   int32_t istar = 0x7fffffff;
+  // The output is ordered through a bitmap over ids.  With fp32 scores the
+  // candidate pass marks the sure items (bins above the threshold bin) and
+  // the resolved threshold bin is marked from its LDS list, so no second
+  // pass over the registers is needed; `marked` says that happened.  (With
+  // bf16 scores a wave's items at one register index are not consecutive
+  // ids, and marking them there costs more registers than the second pass.)
+  bool marked = false;
+  for (int w = tid; w < kFrWords; w += NT) bitmap[w] = 0;
   if (need > 0 && need < static_cast<uint32_t>(n)) {
-    uint32_t mx = 0, mn_inv = 0, unused = 0;
+    float fmx = -__builtin_inff(), fmn = __builtin_inff();
+    bool any = false;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       if (valid(e)) {
-        const uint32_t kk = key(e);
-        mx = max(mx, kk);
-        mn_inv = max(mn_inv, ~kk);
+        const float v = val(e);
+        fmx = fmaxf(fmx, v);
+        fmn = fminf(fmn, v);
+        any = true;
       }
     }
+    uint32_t mx = any ? float_to_key(fmx) : 0u, mn_inv = any ? ~float_to_key(fmn) : 0u, unused = 0;
     for (int i = tid; i < kFrBins; i += NT) hist[i] = 0;
     W::reduce_sum_max_max(unused, mx, mn_inv, wb);
     const float vmax = key_to_float(mx);
@@ -886,13 +894,13 @@ __global__ __launch_bounds__(FrShape<BF16>::kThreads, 4) void k_flat_select_reg(
     const float range = vmax - vmin;
     const float scale = (range > 0.0f && range < __builtin_inff())
                             ? static_cast<float>(kFrBins) * 0.99999f / range : 0.0f;
-    auto bin_of = [&](uint32_t kk) {
-      const float x = (key_to_float(kk) - vmin) * scale;
+    auto bin_of = [&](float v) {
+      const float x = (v - vmin) * scale;
       return min(kFrBins - 1, max(0, static_cast<int>(x)));
     };
 #pragma unroll
     for (int e = 0; e < PER; ++e)
-      if (valid(e)) atomicAdd(&hist[bin_of(key(e))], 1u);
+      if (valid(e)) atomicAdd(&hist[bin_of(val(e))], 1u);
     __syncthreads();
     uint32_t above;
     const int b1 = W::find_rank_bin(hist, kFrBins, need, true, wb, &above);
@@ -900,22 +908,32 @@ __global__ __launch_bounds__(FrShape<BF16>::kThreads, 4) void k_flat_select_reg(
     if (ncand <= static_cast<uint32_t>(kFrCap)) {
       if (tid == 0) ccount = 0;
       __syncthreads();
-      // Items of bin b1 have keys >= klo, the key of the value one bin width
-      // below the bin's lower edge (a margin against rounding); only waves
-      // holding such keys evaluate the exact bin.
-      const uint32_t klo = scale > 0.0f
-                               ? float_to_key(vmin + (static_cast<float>(b1) - 1.0f) / scale)
-                               : 0u;
+      // Items of bin b1 and above score at least flo, one bin width below
+      // the bin's lower edge (a margin against rounding); only waves holding
+      // such scores evaluate the exact bin.  Items of a higher bin are
+      // selected whatever the threshold inside b1 (bin order is key order).
+      // fp32: a wave's 64 items at index e are the ids of two bitmap words,
+      // which its lanes 0 and 1 store from the wave's ballot of those items.
+      const float flo = scale > 0.0f ? vmin + (static_cast<float>(b1) - 1.0f) / scale
+                                     : -__builtin_inff();
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
-        const uint32_t kk = key(e);
-        if (__ballot(kk >= klo) == 0) continue;   // wave-uniform
+        const float v = val(e);
+        if (__ballot(v >= flo) == 0) continue;   // wave-uniform
         const int i = S::item(e, tid);
-        const bool c = i < n && bin_of(kk) == b1;
+        const int bk = i < n ? bin_of(v) : -1;
+        const bool c = bk == b1;
         const uint32_t slot = wave_append(c, &ccount);
         if (c) {
-          ckey_l[slot] = kk;
+          ckey_l[slot] = float_to_key(v);
           cid_l[slot] = i;
+        }
+        if constexpr (!BF16) {
+          const uint64_t sure = __ballot(bk > b1);
+          const int lane = tid & 63;
+          if (lane < 2)
+            bitmap[(S::item(e, tid - lane) >> 5) + lane] =
+                static_cast<uint32_t>(lane ? sure >> 32 : sure);
         }
       }
       __syncthreads();
@@ -924,24 +942,33 @@ __global__ __launch_bounds__(FrShape<BF16>::kThreads, 4) void k_flat_select_reg(
       else
         W::resolve(ArrayCand{ckey_l, cid_l, ncand}, 0u, 32, need - above, hist256, wb, &kstar,
                    &istar);
+      if constexpr (!BF16) {
+        for (uint32_t c = tid; c < ncand; c += NT) {
+          const int32_t i = cid_l[c];
+          if (selected(ckey_l[c], i, kstar, istar)) atomicOr(&bitmap[i >> 5], 1u << (i & 31));
+        }
+        marked = true;
+      }
     } else {
       W::resolve(FlatCand<BF16>{row, static_cast<uint32_t>(n)}, 0u, 32, need, hist256, wb, &kstar,
                  &istar);
     }
   }
 
-  // Ordered output through a bitmap over ids: thread t owns words
-  // kWordsPerThread t .. + kWordsPerThread - 1.
-  for (int w = tid; w < kFrWords; w += NT) bitmap[w] = 0;
+  // Ordered output: thread t owns bitmap words kWordsPerThread t .. +
+  // kWordsPerThread - 1.  Every item (need == n), or a threshold resolved
+  // over the whole row, is marked by a pass over the registers.
   __syncthreads();
+  if (!marked) {
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const uint32_t kk = key(e);
-    if (__ballot(kk >= kstar) == 0) continue;   // selected items have key >= K*
-    const int i = S::item(e, tid);
-    if (i < n && selected(kk, i, kstar, istar)) atomicOr(&bitmap[i >> 5], 1u << (i & 31));
+    for (int e = 0; e < PER; ++e) {
+      const uint32_t kk = key(e);
+      if (__ballot(kk >= kstar) == 0) continue;   // selected items have key >= K*
+      const int i = S::item(e, tid);
+      if (i < n && selected(kk, i, kstar, istar)) atomicOr(&bitmap[i >> 5], 1u << (i & 31));
+    }
+    __syncthreads();
   }
-  __syncthreads();
   constexpr int WPT = S::kWordsPerThread;
   uint32_t words[WPT];
   uint32_t cnt = 0;
