@@ -861,12 +861,10 @@ __global__ __launch_bounds__(FrShape<BF16>::kThreads, 4) void k_flat_select_reg(
   // Every item is taken when need == n: K* = 0, I* = max.
   uint32_t kstar = 0;
   int32_t istar = 0x7fffffff;
-  // The output is ordered through a bitmap over ids.  With fp32 scores the
-  // candidate pass marks the sure items (bins above the threshold bin) and
-  // the resolved threshold bin is marked from its LDS list, so no second
-  // pass over the registers is needed; `marked` says that happened.  (With
-  // bf16 scores a wave's items at one register index are not consecutive
-  // ids, and marking them there costs more registers than the second pass.)
+  // The output is ordered through a bitmap over ids.  The candidate pass
+  // marks the sure items (bins above the threshold bin) and the resolved
+  // threshold bin is marked from its LDS list, so no second pass over the
+  // registers is needed; `marked` says that happened.
   bool marked = false;
   for (int w = tid; w < kFrWords; w += NT) bitmap[w] = 0;
   if (need > 0 && need < static_cast<uint32_t>(n)) {
@@ -914,8 +912,13 @@ __global__ __launch_bounds__(FrShape<BF16>::kThreads, 4) void k_flat_select_reg(
       // selected whatever the threshold inside b1 (bin order is key order).
       // fp32: a wave's 64 items at index e are the ids of two bitmap words,
       // which its lanes 0 and 1 store from the wave's ballot of those items.
+      // bf16: item e of thread t is 2 (NT (e / 2) + t) + e % 2, i.e. bit
+      // 2 (t % 16) + e % 2 of word t / 16 + 32 (e / 2): one base word and two
+      // bit masks per thread, and a constant offset per e.
       const float flo = scale > 0.0f ? vmin + (static_cast<float>(b1) - 1.0f) / scale
                                      : -__builtin_inff();
+      const int mword = tid >> 4;
+      const uint32_t mbit0 = 1u << (2 * (tid & 15)), mbit1 = mbit0 << 1;
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
         const float v = val(e);
@@ -928,7 +931,9 @@ __global__ __launch_bounds__(FrShape<BF16>::kThreads, 4) void k_flat_select_reg(
           ckey_l[slot] = float_to_key(v);
           cid_l[slot] = i;
         }
-        if constexpr (!BF16) {
+        if constexpr (BF16) {
+          if (bk > b1) atomicOr(&bitmap[mword + 32 * (e >> 1)], (e & 1) ? mbit1 : mbit0);
+        } else {
           const uint64_t sure = __ballot(bk > b1);
           const int lane = tid & 63;
           if (lane < 2)
@@ -942,13 +947,11 @@ __global__ __launch_bounds__(FrShape<BF16>::kThreads, 4) void k_flat_select_reg(
       else
         W::resolve(ArrayCand{ckey_l, cid_l, ncand}, 0u, 32, need - above, hist256, wb, &kstar,
                    &istar);
-      if constexpr (!BF16) {
-        for (uint32_t c = tid; c < ncand; c += NT) {
-          const int32_t i = cid_l[c];
-          if (selected(ckey_l[c], i, kstar, istar)) atomicOr(&bitmap[i >> 5], 1u << (i & 31));
-        }
-        marked = true;
+      for (uint32_t c = tid; c < ncand; c += NT) {
+        const int32_t i = cid_l[c];
+        if (selected(ckey_l[c], i, kstar, istar)) atomicOr(&bitmap[i >> 5], 1u << (i & 31));
       }
+      marked = true;
     } else {
       W::resolve(FlatCand<BF16>{row, static_cast<uint32_t>(n)}, 0u, 32, need, hist256, wb, &kstar,
                  &istar);
