@@ -201,14 +201,21 @@ class Step:
             self.run()
         elif self.name.startswith("reuse_128k"):
             d = self._next()
-            self._attn(d, self.csa.reuse_attn, d["q"], d["swa"], d["idx"], self.out, self.lse)
+            self._attn(d, "reuse", d["q"], d["swa"], d["idx"], self.out, self.lse)
         else:
             self._scan(self._next())
 
-    def _attn(self, d, fn, q, swa, idx, out, lse):
-        fmt = self.csa.KV_FP4_E4M3_16 if d.get("kv_fmt") == "e4m3_16" else self.csa.KV_MXFP4_E8M0_32
-        fn(q, d["kv_fp4"], d["kv_scale"], idx, swa, d["swa_pos0"], d["q_pos"], d["sm_scale"], out,
-           lse=lse, kv_fmt=fmt, ws=self.ws_attn)
+    def _attn(self, d, kind, q, swa, idx, out, lse):
+        """An attention call of input set d (prepared once per set and kind)."""
+        key = (kind, id(d))
+        if key not in self._calls:
+            csa = self.csa
+            fmt = csa.KV_FP4_E4M3_16 if d.get("kv_fmt") == "e4m3_16" else csa.KV_MXFP4_E8M0_32
+            mk = csa.reuse_attn_call if kind == "reuse" else csa.sparse_attn_call
+            self._calls[key] = mk(q, d["kv_fp4"], d["kv_scale"], idx, swa, d["swa_pos0"],
+                                  d["q_pos"], d["sm_scale"], out, lse=lse, kv_fmt=fmt,
+                                  ws=self.ws_attn)
+        self._calls[key].run()
 
     def run(self, full_only=False):
         d, csa = self._next(), self.csa
@@ -230,12 +237,12 @@ class Step:
                           swa_kv=d["swa"], swa_pos0=d["swa_pos0"])
             return
         if self.name.startswith("reuse_128k"):
-            self._attn(d, csa.reuse_attn, d["q"], d["swa"], d["idx"], self.out, self.lse)
+            self._attn(d, "reuse", d["q"], d["swa"], d["idx"], self.out, self.lse)
             return
         if self.name == "prefill_128k":
             self._scan(d)
             csa.reindex_topk(csa.MODE_FULL, d["vis_len"], self.N, 512, self.idx, scores=self.scores)
-            self._attn(d, csa.sparse_attn_decode, d["q"], d["swa"], self.idx, self.out, self.lse)
+            self._attn(d, "decode", d["q"], d["swa"], self.idx, self.out, self.lse)
             return
         full, reindex = self._layer_calls(d)
         full.run(csa.MODE_FULL)

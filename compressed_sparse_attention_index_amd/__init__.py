@@ -284,9 +284,11 @@ def reindex_topk(mode, vis_len, N_cap, top_k, idx_out, scores=None, q_idx=None, 
           _stream(stream))
 
 
-def _attn(name, q, kv_fp4, kv_scale, idx, swa_kv, swa_pos0, q_pos, sm_scale, out, lse=None,
-          window=128, replay_start=-1, sink=None, kv_fmt=KV_MXFP4_E8M0_32, paging=None, ws=None,
-          stream=None):
+def _attn_args(q, kv_fp4, kv_scale, idx, swa_kv, swa_pos0, q_pos, sm_scale, out, lse=None,
+               window=128, replay_start=-1, sink=None, kv_fmt=KV_MXFP4_E8M0_32, paging=None,
+               ws=None):
+    """Checked and packed arguments of an attention call (all but the stream),
+    and the objects they point into."""
     B, n_q = q.shape[0], q.shape[1]
     N_cap = paging.n_cap if paging is not None else kv_fp4.shape[1]
     top_k = idx.shape[-1] if idx is not None else 0
@@ -297,12 +299,19 @@ def _attn(name, q, kv_fp4, kv_scale, idx, swa_kv, swa_pos0, q_pos, sm_scale, out
     flags = (ATTN_SINK if sp else 0) | (ATTN_PAGED if paging is not None else 0)
     opts = AttnOpts(window, replay_start, kv_fmt, flags, sp,
                     ctypes.pointer(paging.struct) if paging is not None else None)
-    _call(name, _ptr(q, _BITS16, "q"), _ptr(kv_fp4, _U8, "kv_fp4"),
-          _ptr(kv_scale, _U8, "kv_scale"), N_cap, _ptr(idx, _I32, "idx"), top_k,
-          _ptr(swa_kv, _U8, "swa_kv"), S_cap, _ptr(swa_pos0, _I32, "swa_pos0"),
-          _ptr(q_pos, _I32, "q_pos"), float(sm_scale), ctypes.byref(opts), B, n_q,
-          _ptr(out, _BITS16, "out"), _ptr(lse, _F32, "lse"), _ptr(ws, (torch.uint8,), "ws"),
-          nbytes, _stream(stream))
+    args = (_ptr(q, _BITS16, "q"), _ptr(kv_fp4, _U8, "kv_fp4"),
+            _ptr(kv_scale, _U8, "kv_scale"), N_cap, _ptr(idx, _I32, "idx"), top_k,
+            _ptr(swa_kv, _U8, "swa_kv"), S_cap, _ptr(swa_pos0, _I32, "swa_pos0"),
+            _ptr(q_pos, _I32, "q_pos"), float(sm_scale), ctypes.byref(opts), B, n_q,
+            _ptr(out, _BITS16, "out"), _ptr(lse, _F32, "lse"), _ptr(ws, (torch.uint8,), "ws"),
+            nbytes)
+    keep = (q, kv_fp4, kv_scale, idx, swa_kv, swa_pos0, q_pos, out, lse, sink, paging, ws, opts)
+    return args, keep
+
+
+def _attn(name, *args, stream=None, **kw):
+    a, _ = _attn_args(*args, **kw)
+    _call(name, *a, _stream(stream))
 
 
 def sparse_attn_decode(*args, **kw):
@@ -313,6 +322,16 @@ def sparse_attn_decode(*args, **kw):
 def reuse_attn(*args, **kw):
     """Attention of a Reuse layer (indices from an earlier layer, no indexer)."""
     _attn("csa2_reuse_attn", *args, **kw)
+
+
+def sparse_attn_call(*args, **kw):
+    """sparse_attn_decode prepared once (see PreparedCall)."""
+    return PreparedCall("csa2_sparse_attn_decode", *_attn_args(*args, **kw))
+
+
+def reuse_attn_call(*args, **kw):
+    """reuse_attn prepared once (see PreparedCall)."""
+    return PreparedCall("csa2_reuse_attn", *_attn_args(*args, **kw))
 
 
 def kv_append(kv_new, pos, kv_fp4, kv_scale, swa_new=None, swa_kv=None, swa_pos0=None,

@@ -163,6 +163,31 @@ def test_flat_select_long_rows(n):
         _select_case(rows, vis, k, "flat")
 
 
+def test_flat_select_many_rows():
+    # More rows than compute units: a workgroup takes every (grid)-th row and
+    # prefetches its next row while it works on the current one.  Row kinds
+    # cycle (distinct, heavy ties, all equal, short, empty, two clusters), so
+    # every marking path meets the loop and the prefetch of every other kind.
+    rng = np.random.default_rng(25)
+    n = 9000
+    kinds = [
+        lambda: rng.standard_normal(n),
+        lambda: np.round(rng.standard_normal(n) * 4) / 4,
+        lambda: np.full(n, -2.5),
+        lambda: rng.standard_normal(n),
+        lambda: rng.standard_normal(n),
+        lambda: np.concatenate([rng.standard_normal(5000) + 1e6, rng.standard_normal(4000)]),
+    ]
+    vis_of = [n, n - 5, n, 300, 0, 7001]
+    rows, vis = [], []
+    for i in range(600):
+        rows.append(kinds[i % 6]())
+        vis.append(vis_of[i % 6])
+    print("flat select 600 rows", flush=True)
+    for k in (100, 512):
+        _select_case(rows, vis, k, "flat")
+
+
 def test_block_topk_workspace_contents():
     # The block Top-K histograms live in the workspace and must start at
     # zero; every call leaves them zeroed.  A workspace that did not start at
@@ -553,6 +578,31 @@ def test_attention_running_max_moves_mid_row():
     # Head 0 of row 0 is dominated by the window: its lse is far above the
     # others'.
     assert lse[0, 0, 0] > 8.0 and np.median(lse[0, 0]) < 8.0
+
+
+def test_prepared_attention_calls_match_direct_calls():
+    # sparse_attn_call / reuse_attn_call pack the arguments once; every run
+    # makes the same C call, so the outputs are the direct call's bits.
+    T, B = 3000, 8
+    d = synth.decode_workload(B=B, T=T, kdtype="bf16", seed=92)
+    rng = np.random.default_rng(92)
+    idx = torch.from_numpy(np.stack([np.sort(rng.choice(T, size=512, replace=False))
+                                     for _ in range(B)]).astype(np.int32)).reshape(B, 1, 512)
+    print("prepared attention calls", flush=True)
+    for reuse in (False, True):
+        want, want_lse = _attn_gpu(d, idx, reuse=reuse)
+        out = torch.zeros(B, 1, 64, 512, dtype=torch.int16, device="cuda")
+        lse = torch.zeros(B, 1, 64, device="cuda")
+        mk = csa.reuse_attn_call if reuse else csa.sparse_attn_call
+        call = mk(d["q"].cuda(), d["kv_fp4"].cuda(), d["kv_scale"].cuda(), idx.cuda(),
+                  d["swa"].cuda(), d["swa_pos0"].cuda(), d["q_pos"].cuda(), d["sm_scale"], out,
+                  lse=lse)
+        for _ in range(2):
+            out.zero_()
+            lse.zero_()
+            call.run()
+            torch.cuda.synchronize()
+            assert np.array_equal(u16(out), want) and np.array_equal(_np(lse), want_lse), reuse
 
 
 def test_attention_batch_invariant():
