@@ -48,7 +48,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="full_reindex_1m",
                    choices=["tiny_2k", "full_64k", "reuse_128k", "reuse_128k_e4m3",
-                            "full_reindex_1m", "full_reindex_1m_fp4", "prefill_128k",
+                            "full_reindex_1m", "full_reindex_1m_fp4", "full_reindex_1m_fp4qk",
+                            "prefill_128k",
                             "kv_append_64k", "decoder_1m"])
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU time budget of the oracle baseline sample")
@@ -87,6 +88,7 @@ ROTATED = {
     "reuse_128k_e4m3": ("q", "swa", "idx"),
     "full_reindex_1m": (),
     "full_reindex_1m_fp4": (),
+    "full_reindex_1m_fp4qk": (),
     "prefill_128k": (),
     "kv_append_64k": ("kv_new", "swa_new"),
     "decoder_1m": (),
@@ -315,8 +317,9 @@ def mxfp4_rows(d, b):
 
 def fp4_recall(d, step):
     """Recall of the FP4 indexer path: the GPU Full layer's Top-512 on MXFP4
-    keys against the oracle's Top-512 on the same keys unquantised (bf16),
-    per query row; the mean and the minimum over the rows."""
+    keys (and, with the FP4 query, an MXFP4 query) against the oracle's
+    Top-512 on the same keys unquantised (bf16) with the bf16 query, per
+    query row; the mean and the minimum over the rows."""
     import numpy as np
     from oracle import pipeline
     step.run(full_only=True)   # the Full layer's Top-512 stays in the layer state
@@ -534,7 +537,8 @@ def measure(name, args, torch, synth, csa, cpu=True, graph=True):
         # The FP4 indexer keys go to the library as one buffer (E2M1 rows,
         # then their scales); the oracle reads them row by row.
         d["k_idx_buf"] = d["k_idx"]
-        d["k_idx"] = csa.Mxfp4Keys(d["k_idx"], d["B"] * d["T"], d["T"])
+        d["k_idx"] = csa.Mxfp4Keys(d["k_idx"], d["B"] * d["T"], d["T"],
+                                   fp4_query=name == "full_reindex_1m_fp4qk")
     dominant, per_launch, bound, step_bytes = algorithmic(name, d)
     sets = rotation_sets(name, d, step_bytes or per_launch, torch, synth)
     torch.cuda.synchronize()
@@ -615,11 +619,13 @@ def measure(name, args, torch, synth, csa, cpu=True, graph=True):
     else:
         reuse = name.startswith("reuse_128k")
         cfg = {"workload": name, "batch": d["B"], "query_rows": rows, "context": T,
-               "indexer_k": None if reuse else d.get("kdtype"), "top_k": 512,
+               "indexer_k": None if reuse else ("mxfp4 (query mxfp4)" if name == "full_reindex_1m_fp4qk"
+                                                else d.get("kdtype")), "top_k": 512,
                "pool_blocks": None if reuse or name == "prefill_128k" else 2048, "window": 128,
                "layers": {"full_64k": "Full", "tiny_2k": "Full", "reuse_128k": "Reuse",
                           "reuse_128k_e4m3": "Reuse", "full_reindex_1m": "Full+Reindex",
                           "full_reindex_1m_fp4": "Full+Reindex (FP4 indexer keys)",
+                          "full_reindex_1m_fp4qk": "Full+Reindex (FP4 indexer keys and query)",
                           "prefill_128k": "prefill (m=2)",
                           "decoder_1m": "decoder layers 20-39 (Full + 3 Reuse, "
                                         "4 x (Reindex + 3 Reuse))"}[name],
@@ -643,8 +649,9 @@ def measure(name, args, torch, synth, csa, cpu=True, graph=True):
         log(f"[bench] BF16 scores {rec['bf16_scores']} ({time.time() - t0:.1f} s)")
     if d.get("kdtype") == "mxfp4":
         t0 = time.time()
-        rec["recall_fp4_keys"] = fp4_recall(d, step)
-        log(f"[bench] FP4 indexer recall {rec['recall_fp4_keys']} ({time.time() - t0:.1f} s)")
+        key = "recall_fp4_qk" if name == "full_reindex_1m_fp4qk" else "recall_fp4_keys"
+        rec[key] = fp4_recall(d, step)
+        log(f"[bench] FP4 indexer recall {rec[key]} ({time.time() - t0:.1f} s)")
     del step, sets, d
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

@@ -12,7 +12,7 @@ import os
 import torch
 
 __all__ = [
-    "KDTYPE_BF16", "KDTYPE_FP8", "KDTYPE_MXFP4", "Mxfp4Keys", "KV_MXFP4_E8M0_32", "KV_FP4_E4M3_16", "MODE_FULL", "MODE_REINDEX", "MODE_REUSE",
+    "KDTYPE_BF16", "KDTYPE_FP8", "KDTYPE_MXFP4", "KDTYPE_MXFP4_QK", "Mxfp4Keys", "KV_MXFP4_E8M0_32", "KV_FP4_E4M3_16", "MODE_FULL", "MODE_REINDEX", "MODE_REUSE",
     "OP_INDEX_SCORE", "OP_BLOCK_TOPK", "OP_REINDEX_TOPK", "OP_SPARSE_ATTN",
     "Csa2Error", "Paging", "lib", "abi_version", "workspace_size", "index_score", "block_topk",
     "block_topk_noalloc",
@@ -20,7 +20,7 @@ __all__ = [
     "MODE_SWA", "layer_mode", "LayerState", "run_layer",
 ]
 
-KDTYPE_BF16, KDTYPE_FP8, KDTYPE_MXFP4 = 0, 1, 2
+KDTYPE_BF16, KDTYPE_FP8, KDTYPE_MXFP4, KDTYPE_MXFP4_QK = 0, 1, 2, 3
 KV_MXFP4_E8M0_32, KV_FP4_E4M3_16 = 0, 1   # main-KV scale formats (csa2_kvfmt)
 MODE_FULL, MODE_REINDEX, MODE_REUSE, MODE_SWA = 0, 1, 2, 3
 OP_INDEX_SCORE, OP_BLOCK_TOPK, OP_REINDEX_TOPK, OP_SPARSE_ATTN = 0, 1, 2, 3
@@ -95,11 +95,18 @@ def _paging(paging):
 class Mxfp4Keys:
     """Indexer keys in MXFP4 (CSA2_KDTYPE_MXFP4): `buf` is a uint8 GPU tensor
     of 68 * rows bytes (rows = B * N_cap, or the page pool's rows), the rows'
-    64 bytes of E2M1 first, then their 4 E8M0 scale bytes."""
+    64 bytes of E2M1 first, then their 4 E8M0 scale bytes.  fp4_query: the
+    query is quantised to MXFP4 too and QK runs on FP4 matrix instructions
+    (CSA2_KDTYPE_MXFP4_QK)."""
 
-    def __init__(self, buf, rows, n_cap):
+    def __init__(self, buf, rows, n_cap, fp4_query=False):
         assert buf.dtype == torch.uint8 and buf.numel() == 68 * rows
         self.buf, self.rows, self.n_cap = buf, int(rows), int(n_cap)
+        self.fp4_query = bool(fp4_query)
+
+    def with_fp4_query(self, on=True):
+        """The same key buffer, with or without the FP4 query."""
+        return Mxfp4Keys(self.buf, self.rows, self.n_cap, fp4_query=on)
 
 
 def _keys(k_idx):
@@ -107,7 +114,8 @@ def _keys(k_idx):
     if k_idx is None:
         return None, KDTYPE_BF16, None
     if isinstance(k_idx, Mxfp4Keys):
-        return _ptr(k_idx.buf, (torch.uint8,), "k_idx"), KDTYPE_MXFP4, k_idx.n_cap
+        kd = KDTYPE_MXFP4_QK if k_idx.fp4_query else KDTYPE_MXFP4
+        return _ptr(k_idx.buf, (torch.uint8,), "k_idx"), kd, k_idx.n_cap
     kd = KDTYPE_BF16 if k_idx.dtype in _BITS16 else KDTYPE_FP8
     return _ptr(k_idx, _BITS16 + _U8, "k_idx"), kd, k_idx.shape[1]
 

@@ -102,10 +102,11 @@ csa2_status index_score_impl(const uint16_t* q_idx, const float* w_idx, const vo
   if (!q_idx || !w_idx || !k_idx || !vis_len) return CSA2_ERR_NULL;
   if (!scores && !block_max) return CSA2_ERR_NULL;
   if (k_dtype != CSA2_KDTYPE_BF16 && k_dtype != CSA2_KDTYPE_FP8_E4M3 &&
-      k_dtype != CSA2_KDTYPE_MXFP4)
+      k_dtype != CSA2_KDTYPE_MXFP4 && k_dtype != CSA2_KDTYPE_MXFP4_QK)
     return CSA2_ERR_UNSUPPORTED;
   // MXFP4 keys: decode rows only (the prefill-shaped kernel reads bf16 / FP8).
-  if (k_dtype == CSA2_KDTYPE_MXFP4 && n_q >= 16) return CSA2_ERR_UNSUPPORTED;
+  if ((k_dtype == CSA2_KDTYPE_MXFP4 || k_dtype == CSA2_KDTYPE_MXFP4_QK) && n_q >= 16)
+    return CSA2_ERR_UNSUPPORTED;
   csa2_status st = check_rows(B, n_q);
   if (st != CSA2_OK) return st;
   if (N_cap < 1 || N_cap > kMaxNcap) return CSA2_ERR_SHAPE;
@@ -224,14 +225,15 @@ csa2_status csa2_reindex_topk(csa2_mode mode, const float* scores, const uint16_
   if (!stored) {
     if (!q_idx || !w_idx || !k_idx) return CSA2_ERR_NULL;
     if (k_dtype != CSA2_KDTYPE_BF16 && k_dtype != CSA2_KDTYPE_FP8_E4M3 &&
-        k_dtype != CSA2_KDTYPE_MXFP4)
+        k_dtype != CSA2_KDTYPE_MXFP4 && k_dtype != CSA2_KDTYPE_MXFP4_QK)
       return CSA2_ERR_UNSUPPORTED;
   }
   const size_t need = csa2::pool_topk_workspace_bytes(rows, k_blocks);
   if (!ws || ws_bytes < need) return CSA2_ERR_WORKSPACE;
   const int kmode = stored ? 0
                           : k_dtype == CSA2_KDTYPE_FP8_E4M3 ? 1
-                          : k_dtype == CSA2_KDTYPE_BF16 ? 2 : 3;
+                          : k_dtype == CSA2_KDTYPE_BF16 ? 2
+                          : k_dtype == CSA2_KDTYPE_MXFP4 ? 3 : 4;
   return from_hip(csa2::launch_pool_topk(kmode, scores, q_idx, w_idx, k_idx, pg, pool_blocks,
                                          k_blocks,
                                          vis_len, rows, n_q, N_cap, top_k, idx_out, idx_score, ws,

@@ -42,8 +42,9 @@ bool block_topk_noalloc_fits(int rows, int N_cap);
 hipError_t launch_block_topk_noalloc(const float* block_max, const int32_t* vis_len, int rows,
                                      int N_cap, int k, int32_t* out, hipStream_t stream);
 
-// Pool Top-K.  mode 0: keys are stored scores; 1 / 2 / 3: the pool
-// positions are re-scored with q_idx / w_idx on FP8 / bf16 / MXFP4 keys.
+// Pool Top-K.  mode 0: keys are stored scores; 1 / 2 / 3 / 4: the pool
+// positions are re-scored with q_idx / w_idx on FP8 / bf16 / MXFP4 keys /
+// MXFP4 keys with the query quantised to MXFP4.
 size_t pool_topk_workspace_bytes(int rows, int k_blocks);
 hipError_t launch_pool_topk(int mode, const float* scores, const uint16_t* q_idx,
                             const float* w_idx, const void* k_idx, const Pages& pg,

@@ -19,9 +19,15 @@ namespace csa2 {
 // Indexer-key storage types (csa2_kdtype): bf16 (256 B per entry), FP8
 // E4M3FN (128 B), MXFP4 (64 B of E2M1 plus 4 E8M0 scales, one per 32 dims;
 // the scales of all R rows of a buffer follow its R rows of E2M1).
+// kKdFp4Q: MXFP4 keys with the query quantised to MXFP4 as well, the
+// contraction on the scaled FP4 matrix instructions (products of two E2M1
+// values with power-of-two scales are exact in fp32, so the result is the
+// sum of the products of the dequantised values).
 constexpr int kKdBf16 = 0;
 constexpr int kKdFp8 = 1;
 constexpr int kKdFp4 = 2;
+constexpr int kKdFp4Q = 3;
+constexpr bool fp4_keys(int kd) { return kd == kKdFp4 || kd == kKdFp4Q; }
 template <int KD>
 struct KeyFmt {
   static constexpr int kRowBytes = KD == kKdBf16 ? 256 : KD == kKdFp8 ? 128 : 64;
@@ -42,16 +48,74 @@ __device__ __forceinline__ void load_key_half(KeyTile<KD>& t, const uint8_t* row
   const u32x4* p = reinterpret_cast<const u32x4*>(row + (KeyFmt<KD>::kRowBytes / 2) * half);
 #pragma unroll
   for (int i = 0; i < KeyTile<KD>::kWords; ++i) t.v[i] = p[i];
-  if constexpr (KD == kKdFp4)
+  if constexpr (fp4_keys(KD))
     t.sc = *reinterpret_cast<const uint16_t*>(scale_row + 2 * half);
 }
 
-// Query operand: the lane's head row (lane % 32), dims of its half.
-__device__ __forceinline__ void load_query(bf16x8 qa[8], const uint16_t* q_row_base, int col,
+// Query operand of the lane: its head row (lane % 32), dims of its half
+// (64 half .. + 63).  bf16 for the bf16 contraction; for kKdFp4Q the same
+// 64 dims as two MXFP4 blocks of 32 (16 bytes of E2M1 each, element 2j in
+// the low nibble of byte j) and their two E8M0 codes (low byte: the first
+// block).
+template <int KD>
+struct QueryOp {
+  bf16x8 qa[8];
+};
+template <>
+struct QueryOp<kKdFp4Q> {
+  u32x4 q4[2];
+  uint32_t sc;
+};
+
+// One OCP MXFP4 block of 32 bf16 values (p: four 16-byte words, exact in
+// fp32): shared exponent X = floor(log2(amax)) - 2, clamped to [-127, 127]
+// (-127 for an all-zero or subnormal amax); each v / 2^X rounded to the
+// nearest E2M1 value, ties to the even code, saturating at 6 (the gfx950
+// scaled conversion does this step).  A value that rounds to zero may keep
+// its sign; -0 and +0 multiply alike, so it is left as it is.  The block is
+// read twice (maximum, then conversion), so that only one word's values are
+// live at a time.  Returns the E8M0 code X + 127.
+__device__ __forceinline__ uint32_t mxfp4_block(const u32x4* p, u32x4& out) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 w = p[i];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[k] << 16)),
+                               fabsf(__uint_as_float(w[k] & 0xffff0000u))));
+  }
+  const int ef = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu);
+  const int X = ef == 0 ? -127 : max(ef - 127 - 2, -127);
+  const float scale = X > -127 ? __uint_as_float(static_cast<uint32_t>(X + 127) << 23)
+                               : __uint_as_float(0x00400000u);   // 2^X (2^-127 is subnormal)
+  asm volatile("" ::: "memory");   // read the words again rather than keep them
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 w = p[i];
+    auto lo = [](uint32_t u) { return __uint_as_float(u << 16); };
+    auto hi = [](uint32_t u) { return __uint_as_float(u & 0xffff0000u); };
+    uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, lo(w.x), hi(w.x), scale, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo(w.y), hi(w.y), scale, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo(w.z), hi(w.z), scale, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo(w.w), hi(w.w), scale, 3);
+    out[i] = r;
+  }
+  return static_cast<uint32_t>(X + 127);
+}
+
+template <int KD>
+__device__ __forceinline__ void load_query(QueryOp<KD>& q, const uint16_t* q_row_base, int col,
                                            int half) {
   const u32x4* p = reinterpret_cast<const u32x4*>(q_row_base + col * kIdxDim + 64 * half);
+  if constexpr (KD == kKdFp4Q) {
+    q.sc = mxfp4_block(p, q.q4[0]);
+    asm volatile("" ::: "memory");
+    q.sc |= mxfp4_block(p + 4, q.q4[1]) << 8;
+  } else {
 #pragma unroll
-  for (int s = 0; s < 8; ++s) qa[s] = __builtin_bit_cast(bf16x8, p[s]);
+    for (int s = 0; s < 8; ++s) q.qa[s] = __builtin_bit_cast(bf16x8, p[s]);
+  }
 }
 
 // Head weights of the 16 accumulator rows this lane holds.
@@ -61,24 +125,43 @@ __device__ __forceinline__ void load_weights(float wr[16], const float* w_row, i
 }
 
 template <int KD>
-__device__ __forceinline__ f32x16 key_tile_dot(const bf16x8 qa[8], const KeyTile<KD>& t) {
+__device__ __forceinline__ f32x16 key_tile_dot(const QueryOp<KD>& q, const KeyTile<KD>& t) {
   f32x16 acc = {};
+  if constexpr (KD == kKdFp4Q) {
+    // Two v_mfma_scale_f32_32x32x64_f8f6f4 steps with E2M1 operands: lane
+    // (c, half) gives 32 consecutive dims (one MX block) of head c (A) and of
+    // position c (B) and their block scales; step j covers dims
+    // 64 half + 32 j .. + 31 in both halves.
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    bf16x8 kb;
-    if constexpr (KD == kKdFp8) {
-      const u32x4 w = t.v[s / 2];
-      kb = (s & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
-    } else if constexpr (KD == kKdFp4) {
-      // Dims 64 half + 8 s .. + 7: word s % 4 of chunk s / 4, scale s / 4
-      // (the conversion reads the E8M0 code from the exponent field).
-      const u32x4 w = t.v[s / 4];
-      const uint32_t word = (s & 3) == 0 ? w.x : (s & 3) == 1 ? w.y : (s & 3) == 2 ? w.z : w.w;
-      kb = fp4x8_to_bf16x8(word, __uint_as_float(((t.sc >> (8 * (s / 4))) & 0xffu) << 23));
-    } else {
-      kb = __builtin_bit_cast(bf16x8, t.v[s]);
+    for (int j = 0; j < 2; ++j) {
+      const i32x8 a = {static_cast<int>(q.q4[j].x), static_cast<int>(q.q4[j].y),
+                       static_cast<int>(q.q4[j].z), static_cast<int>(q.q4[j].w), 0, 0, 0, 0};
+      const i32x8 b = {static_cast<int>(t.v[j].x), static_cast<int>(t.v[j].y),
+                       static_cast<int>(t.v[j].z), static_cast<int>(t.v[j].w), 0, 0, 0, 0};
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          a, b, acc, 4 /* A: E2M1 */, 4 /* B: E2M1 */, 0,
+          static_cast<int>((q.sc >> (8 * j)) & 0xffu), 0,
+          static_cast<int>((t.sc >> (8 * j)) & 0xffu));
     }
-    acc = mfma32(qa[s], kb, acc);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      bf16x8 kb;
+      if constexpr (KD == kKdFp8) {
+        const u32x4 w = t.v[s / 2];
+        kb = (s & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
+      } else if constexpr (KD == kKdFp4) {
+        // Dims 64 half + 8 s .. + 7: word s % 4 of chunk s / 4, scale s / 4
+        // (the conversion reads the E8M0 code from the exponent field).
+        const u32x4 w = t.v[s / 4];
+        const uint32_t word = (s & 3) == 0 ? w.x : (s & 3) == 1 ? w.y : (s & 3) == 2 ? w.z : w.w;
+        kb = fp4x8_to_bf16x8(word, __uint_as_float(((t.sc >> (8 * (s / 4))) & 0xffu) << 23));
+      } else {
+        kb = __builtin_bit_cast(bf16x8, t.v[s]);
+      }
+      acc = mfma32(q.qa[s], kb, acc);
+    }
   }
   return acc;
 }

@@ -62,8 +62,8 @@ struct ScanTile {
   static constexpr int kRowBytes = KeyFmt<KD>::kRowBytes;
   static constexpr int kChunks = kRowBytes / 16;            // 16-B chunks per row
   static constexpr int kDataBytes = 32 * kRowBytes;
-  static constexpr int kBytes = kDataBytes + (KD == kKdFp4 ? 256 : 0);   // one tile slot
-  static constexpr int kLoads = kDataBytes / 1024 + (KD == kKdFp4 ? 1 : 0);  // loads per tile
+  static constexpr int kBytes = kDataBytes + (fp4_keys(KD) ? 256 : 0);   // one tile slot
+  static constexpr int kLoads = kDataBytes / 1024 + (fp4_keys(KD) ? 1 : 0);  // loads per tile
   __device__ static int swz(int row) {
     return KD == kKdFp8 ? ((row >> 1) & 7) : KD == kKdBf16 ? (row & 15) : ((row >> 2) & 3);
   }
@@ -94,9 +94,9 @@ __global__ __launch_bounds__(kThreads) void k_index_scan(
   int t = t_begin + wave;
   if (t >= t_end) return;
 
-  bf16x8 qa[8];
+  QueryOp<KD> qa;
   float wr[16];
-  load_query(qa, q_idx + static_cast<size_t>(r) * kIdxHeads * kIdxDim, col, half);
+  load_query<KD>(qa, q_idx + static_cast<size_t>(r) * kIdxHeads * kIdxDim, col, half);
   load_weights(wr, w_idx + static_cast<size_t>(r) * kIdxHeads, half);
   // With paging, lane l holds the pool page of the workgroup's l-th logical
   // page (a workgroup spans at most 64 tiles of 32 entries, pages hold at
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void k_index_scan(
           (__attribute__((address_space(3))) void*)(&stage[wave][slot][i * 1024]), 16, 0,
           2 /* non-temporal */);
     }
-    if constexpr (KD == kKdFp4) {
+    if constexpr (fp4_keys(KD)) {
       const int r = lane & 31;
       const uint8_t* src = scales + (row0 + (r < rows ? r : 0)) * 4;
       __builtin_amdgcn_global_load_lds(
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void k_index_scan(
 #pragma unroll
     for (int j = 0; j < KeyTile<KD>::kWords; ++j)
       kt.v[j] = *reinterpret_cast<const u32x4*>(st + TT::pos(col, (TT::kChunks / 2) * half + j));
-    if constexpr (KD == kKdFp4)
+    if constexpr (fp4_keys(KD))
       kt.sc = *reinterpret_cast<const uint16_t*>(st + TT::kDataBytes + 4 * col + 2 * half);
     const float s = head_sum(key_tile_dot<KD>(qa, kt), wr);
     emit<OUT>(s, 32 * t + col, vis, half, col, srow, brow);
@@ -231,11 +231,15 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w_idx, const v
       case 18: CSA2_SCAN_LAUNCH(kKdFp4, 1, 2); break;
       case 19: CSA2_SCAN_LAUNCH(kKdFp4, 1, 3); break;
       case 20: CSA2_SCAN_LAUNCH(kKdFp4, 1, 4); break;
+      case 25: CSA2_SCAN_LAUNCH(kKdFp4Q, 1, 1); break;
+      case 26: CSA2_SCAN_LAUNCH(kKdFp4Q, 1, 2); break;
+      case 27: CSA2_SCAN_LAUNCH(kKdFp4Q, 1, 3); break;
+      case 28: CSA2_SCAN_LAUNCH(kKdFp4Q, 1, 4); break;
       default: return hipErrorInvalidValue;   // no output, or bf16 scores with block maxima
     }
 #undef CSA2_SCAN_LAUNCH
   } else {
-    if (kd == kKdFp4) return hipErrorInvalidValue;   // rejected by the API layer first
+    if (fp4_keys(kd)) return hipErrorInvalidValue;   // rejected by the API layer first
     return launch_index_gemm(q_idx, w_idx, kb, kd == kKdFp8, pg, vis_len, B, n_q, N_cap, scores,
                              block_max, stream, scores_bf16);
   }

@@ -521,9 +521,9 @@ __global__ __launch_bounds__(kPscThreads) void k_pool_score(PoolArgs a) {
   const int nslots = a.kb * kBlock;
   const int32_t* prow = a.pool + static_cast<size_t>(r) * a.kb;
   float* ps = a.ps + static_cast<size_t>(r) * nslots;
-  bf16x8 qa[8];
+  QueryOp<KD> qa;
   float wr[16];
-  load_query(qa, a.q_idx + static_cast<size_t>(r) * kIdxHeads * kIdxDim, col, half);
+  load_query<KD>(qa, a.q_idx + static_cast<size_t>(r) * kIdxHeads * kIdxDim, col, half);
   load_weights(wr, a.w_idx + static_cast<size_t>(r) * kIdxHeads, half);
   const int b = r / a.n_q;
   // Tiles of 32 slots (4 pool blocks each); wave w takes tiles w and w + 4.
@@ -1145,8 +1145,10 @@ hipError_t launch_pool_topk(int mode, const float* scores, const uint16_t* q_idx
       hipLaunchKernelGGL(k_pool_score<kKdFp8>, grid, dim3(kPscThreads), 0, stream, a);
     else if (mode == 2)
       hipLaunchKernelGGL(k_pool_score<kKdBf16>, grid, dim3(kPscThreads), 0, stream, a);
-    else
+    else if (mode == 3)
       hipLaunchKernelGGL(k_pool_score<kKdFp4>, grid, dim3(kPscThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(k_pool_score<kKdFp4Q>, grid, dim3(kPscThreads), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k_pool_final, dim3(rows), dim3(kPsThreads), 0, stream, a);

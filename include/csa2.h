@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 6
+#define CSA2_ABI_VERSION 7
 
 /* Symbols of the C ABI; everything else in the library is hidden. */
 #define CSA2_API __attribute__((visibility("default")))
@@ -91,7 +91,16 @@ typedef enum {
      page_entries with paging) holds the R rows of E2M1 first and then the R
      rows of 4 scale bytes: 68 * R bytes.  Decode rows only (n_q < 16);
      prefill-shaped calls return CSA2_ERR_UNSUPPORTED. */
-  CSA2_KDTYPE_MXFP4 = 2
+  CSA2_KDTYPE_MXFP4 = 2,
+  /* The same essay passage with the query on the FP4 path as well: keys
+     stored exactly as for CSA2_KDTYPE_MXFP4, and each query row quantised
+     to MXFP4 inside the kernel (OCP MX rules per 32 dims of each head:
+     shared exponent floor(log2(amax)) - 2 clamped to [-127, 127], elements
+     rounded to the nearest E2M1 value, ties to even, saturating at 6).  The
+     QK products run on the gfx950 scaled FP4 matrix instructions; each
+     product of two dequantised values is exact, the sums are fp32.  Decode
+     rows only, as above. */
+  CSA2_KDTYPE_MXFP4_QK = 3
 } csa2_kdtype;
 
 /* Storage format of main-KV entries (512 dims each).  Both store E2M1

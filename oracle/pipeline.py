@@ -28,24 +28,38 @@ def decode_index_keys(k_raw, kdtype):
     """Indexer keys -> fp64 [N, 128].  "bf16": uint16 [N, 128] bits; "fp8":
     uint8 [N, 128] E4M3FN; "mxfp4" (the FP4 indexer QK path of [V4 essay
     §10.2]): uint8 [N, 68] rows, 64 bytes of E2M1 (OCP MXFP4 nibble order)
-    then the 4 E8M0 scales of dims 32 q .. 32 q + 31."""
+    then the 4 E8M0 scales of dims 32 q .. 32 q + 31; "mxfp4_qk": the same
+    keys, with the query quantised too (see quantise_query)."""
     if kdtype == "bf16":
         return formats.bf16_to_f64(k_raw)
     if kdtype == "fp8":
         return formats.e4m3_to_f64(k_raw)
-    if kdtype == "mxfp4":
+    if kdtype in ("mxfp4", "mxfp4_qk"):
         k_raw = np.asarray(k_raw, dtype=np.uint8)
         return formats.mxfp4_to_f64(k_raw[..., :64], k_raw[..., 64:68])
     raise ValueError(f"unknown indexer K dtype {kdtype!r}")
 
 
-def _query(q_raw, w):
-    return formats.bf16_to_f64(q_raw), np.asarray(w, dtype=np.float64)
+def quantise_query(q):
+    """The query on the FP4 QK path as well ([V4 essay §10.2] puts the
+    indexer's QK path, not only its keys, under FP4; the training side
+    quantises to FP4 and computes with the dequantised values): each head's
+    128 dims as four OCP MXFP4 blocks of 32 (formats.f64_to_mxfp4), decoded
+    back to the values the products use.  fp64 [32, 128] -> fp64 [32, 128]."""
+    packed, scales = formats.f64_to_mxfp4(q)
+    return formats.mxfp4_to_f64(packed, scales)
+
+
+def _query(q_raw, w, kdtype=None):
+    q = formats.bf16_to_f64(q_raw)
+    if kdtype == "mxfp4_qk":
+        q = quantise_query(q)
+    return q, np.asarray(w, dtype=np.float64)
 
 
 def scores_prefix(q_raw, w, k_raw, kdtype, vis, chunk=CHUNK):
     """Scores of positions [0, vis), decoded and scored chunk by chunk."""
-    q, wf = _query(q_raw, w)
+    q, wf = _query(q_raw, w, kdtype)
     out = np.empty(int(vis), dtype=np.float64)
     for lo in range(0, int(vis), chunk):
         hi = min(int(vis), lo + chunk)
@@ -55,7 +69,7 @@ def scores_prefix(q_raw, w, k_raw, kdtype, vis, chunk=CHUNK):
 
 def scores_at(q_raw, w, k_raw, kdtype, positions):
     """Scores of the given positions only."""
-    q, wf = _query(q_raw, w)
+    q, wf = _query(q_raw, w, kdtype)
     positions = np.asarray(positions, dtype=np.int64)
     return indexer.index_scores(q, wf, decode_index_keys(k_raw[positions], kdtype))
 

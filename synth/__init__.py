@@ -294,6 +294,9 @@ WORKLOADS = {
     "kv_append_64k": (kv_append_workload, dict(B=4, n_new=65536, seed=5)),
     "full_reindex_1m_fp4": (decode_workload, dict(B=8, T=1048576, kdtype="mxfp4", seed=3,
                                                   lognormal_sigma=0.5, reindex=True)),
+    # The same inputs; the query goes on the FP4 path too (a library option).
+    "full_reindex_1m_fp4qk": (decode_workload, dict(B=8, T=1048576, kdtype="mxfp4", seed=3,
+                                                    lognormal_sigma=0.5, reindex=True)),
     "decoder_1m": (decoder_workload, dict(B=8, T=1048576, kdtype="fp8", seed=6)),
 }
 

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.csa2_abi_version() == 6
+    assert L.csa2_abi_version() == 7
     for st in range(7):
         assert len(L.csa2_status_string(st)) > 0
     assert L.csa2_status_string(0) == b"ok"
@@ -68,6 +68,7 @@ def test_bf16_score_entry_points_validation(L):
     assert call(a6=0) == 2
     assert call(a9=MIS) == 5
     assert f(A, A, A, 2, None, A, 1, 16, 64, A, None) == 3   # MXFP4 keys: decode rows only
+    assert f(A, A, A, 3, None, A, 1, 16, 64, A, None) == 3   # MXFP4 keys and query: likewise
     g = L.csa2_flat_topk_bf16
     assert g(None, A, 1, 1, 64, 16, A, None, None) == 1
     assert g(A, A, 1, 1, 64, 16, None, None, None) == 1
@@ -87,6 +88,8 @@ def test_index_score_validation(L):
     assert _score(L, q=None) == 1
     assert _score(L, sc=None, bm=None) == 1
     assert _score(L, kd=5) == 3
+    assert _score(L, kd=4) == 3
+    assert _score(L, kd=3, n_q=16) == 3    # MXFP4 keys and query: decode rows only
     assert _score(L, B=0) == 2
     assert _score(L, N=0) == 2
     assert _score(L, N=(1 << 22) + 1) == 2

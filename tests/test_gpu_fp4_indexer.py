@@ -1,8 +1,11 @@
 """The FP4 indexer QK path (DeepSeek-V4 essay §10.2): indexer keys stored as
-MXFP4 (CSA2_KDTYPE_MXFP4).  The keys dequantise exactly to bf16, so the scan
-and the pool re-scoring are compared with the oracle on the same stored
-bytes (parity, not recall); the recall of the FP4 path against unquantised
-keys is a property of the data and is reported by the benchmark.
+MXFP4 (CSA2_KDTYPE_MXFP4), and with the query quantised to MXFP4 as well
+(CSA2_KDTYPE_MXFP4_QK, the products on the scaled FP4 matrix instructions).
+The keys dequantise exactly to bf16 and every product of two dequantised
+values is exact, so the scan and the pool re-scoring are compared with the
+oracle on the same stored bytes (parity, not recall); the recall of the FP4
+path against unquantised keys is a property of the data and is reported by
+the benchmark.
 """
 import numpy as np
 import pytest
@@ -39,26 +42,29 @@ def _oracle_rows(buf, rows, first, n):
     return np.concatenate([e2m1, sc], axis=1)
 
 
-def _keys(d):
+def _keys(d, qk=False):
     B, T = d["B"], d["T"]
-    return csa.Mxfp4Keys(d["k_idx"].cuda(), B * T, T)
+    return csa.Mxfp4Keys(d["k_idx"].cuda(), B * T, T, fp4_query=qk)
 
 
+@pytest.mark.parametrize("qk", [False, True], ids=["keys", "qk"])
 @pytest.mark.parametrize("T", [2048, 4133])
-def test_scan_mxfp4_ragged(T):
+def test_scan_mxfp4_ragged(T, qk):
+    kd = "mxfp4_qk" if qk else "mxfp4"
     vis = [0, 1, 7, 9, 33, 512, 513, T - 1, T]
     B = len(vis)
     d = synth.decode_workload(B=B, T=T, kdtype="mxfp4", seed=401, lognormal_sigma=0.5)
     vis_t = torch.tensor(vis, dtype=torch.int32).reshape(B, 1).cuda()
     sc = torch.full((B, 1, T), float("nan"), device="cuda")
     bm = torch.full((B, 1, (T + 7) // 8), float("nan"), device="cuda")
-    print(f"scan mxfp4 T={T}", flush=True)
-    csa.index_score(d["q_idx"].cuda(), d["w_idx"].cuda(), _keys(d), vis_t, scores=sc, block_max=bm)
+    print(f"scan {kd} T={T}", flush=True)
+    csa.index_score(d["q_idx"].cuda(), d["w_idx"].cuda(), _keys(d, qk), vis_t, scores=sc,
+                    block_max=bm)
     torch.cuda.synchronize()
     sc, bm = _np(sc), _np(bm)
     for b, v in enumerate(vis):
         kr = _oracle_rows(d["k_idx"], B * T, b * T, T)
-        ref = pipeline.scores_prefix(u16(d["q_idx"][b, 0]), _np(d["w_idx"][b, 0]), kr, "mxfp4", v)
+        ref = pipeline.scores_prefix(u16(d["q_idx"][b, 0]), _np(d["w_idx"][b, 0]), kr, kd, v)
         g = sc[b, 0, :v].astype(np.float64)
         tol = 1e-5 * np.abs(ref) + 1e-6 * (np.abs(ref).max() if v else 0)
         assert np.all(np.abs(g - ref) <= tol), f"row {b}: max err {np.abs(g - ref).max()}"
@@ -69,11 +75,13 @@ def test_scan_mxfp4_ragged(T):
                       1e-6 * (np.abs(ref).max() if v else 0))
 
 
+@pytest.mark.parametrize("qk", [False, True], ids=["keys", "qk"])
 @pytest.mark.parametrize("mode", ["full", "reindex"])
-def test_pool_topk_mxfp4(mode):
+def test_pool_topk_mxfp4(mode, qk):
+    kd = "mxfp4_qk" if qk else "mxfp4"
     B, T = 2, 8192
     d = synth.decode_workload(B=B, T=T, kdtype="mxfp4", seed=402, reindex=True)
-    keys = _keys(d)
+    keys = _keys(d, qk)
     vis = d["vis_len"].cuda()
     bm = torch.empty(B, 1, T // 8, device="cuda")
     csa.index_score(d["q_idx"].cuda(), d["w_idx"].cuda(), keys, vis, block_max=bm)
@@ -81,7 +89,7 @@ def test_pool_topk_mxfp4(mode):
     csa.block_topk(bm, vis, T, 512, pool)
     q, w = (d["q_idx"], d["w_idx"]) if mode == "full" else (d["q_idx2"], d["w_idx2"])
     idx = torch.empty(B, 1, 512, dtype=torch.int32, device="cuda")
-    print(f"pool top-k mxfp4 {mode}", flush=True)
+    print(f"pool top-k {kd} {mode}", flush=True)
     csa.reindex_topk(csa.MODE_FULL if mode == "full" else csa.MODE_REINDEX, vis, T, 512, idx,
                      q_idx=q.cuda(), w_idx=w.cuda(), k_idx=keys, pool_blocks=pool)
     torch.cuda.synchronize()
@@ -89,19 +97,20 @@ def test_pool_topk_mxfp4(mode):
         kr = _oracle_rows(d["k_idx"], B * T, b * T, T)
         qr, wr = u16(q[b, 0]), _np(w[b, 0])
         if mode == "full":
-            ref = pipeline.full_layer(qr, wr, kr, "mxfp4", T, k_blocks=512)
+            ref = pipeline.full_layer(qr, wr, kr, kd, T, k_blocks=512)
             check_selection(_np(pool[b, 0]), ref["pool"], lambda j: ref["block_max"][j],
                             what=f"pool row {b}")
             check_selection(_np(idx[b, 0]), ref["idx"], lambda t: ref["scores"][t],
                             what=f"idx row {b}")
         else:
-            ref = pipeline.reindex_layer(qr, wr, kr, "mxfp4", _np(pool[b, 0]), T)
+            ref = pipeline.reindex_layer(qr, wr, kr, kd, _np(pool[b, 0]), T)
             check_selection(_np(idx[b, 0]), ref["idx"],
-                            lambda t: pipeline.scores_at(qr, wr, kr, "mxfp4", t),
+                            lambda t: pipeline.scores_at(qr, wr, kr, kd, t),
                             what=f"reindex row {b}")
 
 
-def test_scan_mxfp4_paged():
+@pytest.mark.parametrize("qk", [False, True], ids=["keys", "qk"])
+def test_scan_mxfp4_paged(qk):
     # The E2M1 rows and the scale rows of a page pool follow the same table.
     B, T, P = 2, 2048, 128
     d = synth.decode_workload(B=B, T=T, kdtype="mxfp4", seed=403)
@@ -124,7 +133,8 @@ def test_scan_mxfp4_paged():
             ps[dst] = sc[src]
     paging = csa.Paging(torch.from_numpy(bt).cuda(), P, num_pages)
     out = []
-    for keys, pg in ((_keys(d), None), (csa.Mxfp4Keys(pool.cuda(), pool_rows, T), paging)):
+    for keys, pg in ((_keys(d, qk), None),
+                     (csa.Mxfp4Keys(pool.cuda(), pool_rows, T, fp4_query=qk), paging)):
         s = torch.full((B, 1, T), float("nan"), device="cuda")
         print(f"scan mxfp4 paged={pg is not None}", flush=True)
         csa.index_score(d["q_idx"].cuda(), d["w_idx"].cuda(), keys, d["vis_len"].cuda(), scores=s,
@@ -140,6 +150,7 @@ def test_mxfp4_keys_rejected_for_prefill_rows():
     w = torch.zeros(1, 16, 32, device="cuda")
     vis = torch.full((1, 16), 1024, dtype=torch.int32, device="cuda")
     sc = torch.empty(1, 16, 1024, device="cuda")
-    with pytest.raises(csa.Csa2Error) as e:
-        csa.index_score(q, w, _keys(d), vis, scores=sc)
-    assert e.value.status == 3
+    for qk in (False, True):
+        with pytest.raises(csa.Csa2Error) as e:
+            csa.index_score(q, w, _keys(d, qk), vis, scores=sc)
+        assert e.value.status == 3

@@ -324,6 +324,28 @@ def _prefill_bf16_selects_fp64(q_raw, w, k_raw, kdtype, vis, top_k=512):
     return r
 
 
+def _scores_query_unquantised(q_raw, w, k_raw, kdtype, vis, chunk=pipeline.CHUNK):
+    # Mistake: the FP4 QK path quantises the keys only.
+    return pipeline.scores_prefix(q_raw, w, k_raw, "mxfp4" if kdtype == "mxfp4_qk" else kdtype,
+                                  vis, chunk)
+
+
+def _scores_query_blocks_of_16(q_raw, w, k_raw, kdtype, vis, chunk=pipeline.CHUNK):
+    # Mistake: the query quantised in blocks of 16 dims instead of 32.
+    if kdtype != "mxfp4_qk":
+        return pipeline.scores_prefix(q_raw, w, k_raw, kdtype, vis, chunk)
+    q = formats.bf16_to_f64(q_raw).reshape(32, 8, 16)
+    amax = np.abs(q).max(axis=-1)
+    _, e = np.frexp(amax)
+    X = np.where(amax > 0, np.clip(e - 3, -127, 127), -127)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    scaled = np.minimum(np.abs(q) / np.ldexp(1.0, X)[..., None], 6.0)
+    near = grid[np.abs(scaled[..., None] - grid).argmin(axis=-1)]
+    q4 = (np.sign(q) * near * np.ldexp(1.0, X)[..., None]).reshape(32, 128)
+    return indexer.index_scores(q4, np.asarray(w, np.float64),
+                                pipeline.decode_index_keys(k_raw[:vis], "mxfp4"))
+
+
 MUTATIONS = [
     ("bf16 scores truncated", tf.pin_bf16_encode, formats.f64_to_bf16, _bf16_truncated),
     ("bf16 scores ties away", tf.pin_bf16_encode, formats.f64_to_bf16, _bf16_ties_away),
@@ -372,6 +394,10 @@ MUTATIONS = [
      _unpage_variant()),
     ("schedule with decoder groups of five", pp.pin_layer_mode, pipeline.layer_mode,
      _layer_mode_variant()),
+    ("fp4 QK path with the query left in bf16", pp.pin_scores_fp4_query, pipeline.scores_prefix,
+     _scores_query_unquantised),
+    ("fp4 query in blocks of 16", pp.pin_scores_fp4_query, pipeline.scores_prefix,
+     _scores_query_blocks_of_16),
 ]
 
 

@@ -363,6 +363,58 @@ def test_prefill_topk_bf16_against_brute_force():
     assert pin_prefill_topk_bf16(pipeline.prefill_topk_bf16)
 
 
+def pin_scores_fp4_query(fn):
+    """The FP4 QK path with the query quantised ([V4 essay §10.2], R36), on a
+    hand-worked row: head 0's first 32-dim block is [1.25, 0.6875, 0.375,
+    -0.3125, 0 ..., 3.0 at dim 20, 0 ...], every other dim and head 0; the
+    key is [1, 2, 4, 8, 0, ...] in MXFP4 bytes written out by hand.
+
+    The block's amax 3.0 gives the shared exponent floor(log2 3) - 2 = -1, so
+    the elements are v / 0.5 rounded to E2M1 {0, .5, 1, 1.5, 2, 3, 4, 6}
+    (ties to the even code): 2.5 -> 2 (a tie), 1.375 -> 1.5, 0.75 -> 1 (a
+    tie), -0.625 -> -0.5, 6 -> 6; the query becomes [1, .75, .5, -.25, ...]
+    and the score with weight 1 is relu(1 + 1.5 + 2 - 2) = 2.5.  Without the
+    quantisation it is 1.25 + 1.375 + 1.5 - 2.5 = 1.625; with 16-element
+    blocks the first half-block's exponent is -2 and the score 2.0."""
+    q = np.zeros((32, 128))
+    q[0, :4] = [1.25, 0.6875, 0.375, -0.3125]
+    q[0, 20] = 3.0
+    q_raw = formats.f64_to_bf16(q)
+    w = np.zeros(32); w[0] = 1.0
+    # Key block 0: amax 8 -> exponent 1 (code 128); elements 0.5, 1, 2, 4 ->
+    # codes 1, 2, 4, 6, two per byte (low nibble first); blocks 1-3 are zero
+    # (exponent -127, code 0).
+    k = np.zeros((1, 68), dtype=np.uint8)
+    k[0, 0], k[0, 1] = 0x21, 0x64
+    k[0, 64] = 128
+    got_qk = fn(q_raw, w, k, "mxfp4_qk", 1)
+    got = fn(q_raw, w, k, "mxfp4", 1)
+    return np.array_equal(got_qk, [2.5]) and np.array_equal(got, [1.625])
+
+
+def test_scores_with_fp4_query_hand_worked():
+    assert pin_scores_fp4_query(pipeline.scores_prefix)
+
+
+def test_fp4_query_is_exact_for_representable_blocks():
+    # Blocks whose values lie on the E2M1 grid times the block's own 2^X
+    # (amax in [4, 8) 2^X) are left unchanged, so both key types score alike.
+    rng = np.random.default_rng(31)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    X = rng.integers(-6, 4, size=(32, 4))
+    vals = rng.choice(grid, size=(32, 4, 32)) * rng.choice([-1, 1], size=(32, 4, 32))
+    vals[..., 0] = 6.0
+    q = (vals * np.ldexp(1.0, X)[..., None]).reshape(32, 128)
+    q_raw = formats.f64_to_bf16(q)
+    assert np.array_equal(formats.bf16_to_f64(q_raw), q)
+    assert np.array_equal(pipeline.quantise_query(q), q)
+    w = rng.uniform(size=32)
+    k = rng.integers(0, 256, size=(40, 68), dtype=np.uint8)
+    k[:, 64:] = rng.integers(120, 134, size=(40, 4))
+    assert np.array_equal(pipeline.scores_prefix(q_raw, w, k, "mxfp4_qk", 40),
+                          pipeline.scores_prefix(q_raw, w, k, "mxfp4", 40))
+
+
 def test_kv_append_placement_and_skip_rules():
     assert pin_kv_append(pipeline.kv_append)
 
