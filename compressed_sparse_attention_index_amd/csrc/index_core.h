@@ -67,38 +67,31 @@ struct QueryOp<kKdFp4Q> {
   uint32_t sc;
 };
 
-// One OCP MXFP4 block of 32 bf16 values (p: four 16-byte words, exact in
+// One OCP MXFP4 block of 32 bf16 values (w: four 16-byte words, exact in
 // fp32): shared exponent X = floor(log2(amax)) - 2, clamped to [-127, 127]
 // (-127 for an all-zero or subnormal amax); each v / 2^X rounded to the
 // nearest E2M1 value, ties to the even code, saturating at 6 (the gfx950
 // scaled conversion does this step).  A value that rounds to zero may keep
-// its sign; -0 and +0 multiply alike, so it is left as it is.  The block is
-// read twice (maximum, then conversion), so that only one word's values are
-// live at a time.  Returns the E8M0 code X + 127.
-__device__ __forceinline__ uint32_t mxfp4_block(const u32x4* p, u32x4& out) {
+// its sign; -0 and +0 multiply alike, so it is left as it is.  Returns the
+// E8M0 code X + 127.
+__device__ __forceinline__ uint32_t mxfp4_block(const u32x4 (&w)[4], u32x4& out) {
+  auto lo = [](uint32_t u) { return __uint_as_float(u << 16); };
+  auto hi = [](uint32_t u) { return __uint_as_float(u & 0xffff0000u); };
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const u32x4 w = p[i];
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[k] << 16)),
-                               fabsf(__uint_as_float(w[k] & 0xffff0000u))));
-  }
+    for (int k = 0; k < 4; ++k) amax = fmaxf(amax, fmaxf(fabsf(lo(w[i][k])), fabsf(hi(w[i][k]))));
   const int ef = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu);
   const int X = ef == 0 ? -127 : max(ef - 127 - 2, -127);
   const float scale = X > -127 ? __uint_as_float(static_cast<uint32_t>(X + 127) << 23)
                                : __uint_as_float(0x00400000u);   // 2^X (2^-127 is subnormal)
-  asm volatile("" ::: "memory");   // read the words again rather than keep them
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const u32x4 w = p[i];
-    auto lo = [](uint32_t u) { return __uint_as_float(u << 16); };
-    auto hi = [](uint32_t u) { return __uint_as_float(u & 0xffff0000u); };
-    uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, lo(w.x), hi(w.x), scale, 0);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo(w.y), hi(w.y), scale, 1);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo(w.z), hi(w.z), scale, 2);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo(w.w), hi(w.w), scale, 3);
+    uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, lo(w[i].x), hi(w[i].x), scale, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo(w[i].y), hi(w[i].y), scale, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo(w[i].z), hi(w[i].z), scale, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo(w[i].w), hi(w[i].w), scale, 3);
     out[i] = r;
   }
   return static_cast<uint32_t>(X + 127);
@@ -109,9 +102,11 @@ __device__ __forceinline__ void load_query(QueryOp<KD>& q, const uint16_t* q_row
                                            int half) {
   const u32x4* p = reinterpret_cast<const u32x4*>(q_row_base + col * kIdxDim + 64 * half);
   if constexpr (KD == kKdFp4Q) {
-    q.sc = mxfp4_block(p, q.q4[0]);
-    asm volatile("" ::: "memory");
-    q.sc |= mxfp4_block(p + 4, q.q4[1]) << 8;
+    // All eight loads in flight together, then the two blocks.
+    u32x4 w[2][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i / 4][i % 4] = p[i];
+    q.sc = mxfp4_block(w[0], q.q4[0]) | (mxfp4_block(w[1], q.q4[1]) << 8);
   } else {
 #pragma unroll
     for (int s = 0; s < 8; ++s) q.qa[s] = __builtin_bit_cast(bf16x8, p[s]);

@@ -521,10 +521,16 @@ __global__ __launch_bounds__(kPscThreads) void k_pool_score(PoolArgs a) {
   const int nslots = a.kb * kBlock;
   const int32_t* prow = a.pool + static_cast<size_t>(r) * a.kb;
   float* ps = a.ps + static_cast<size_t>(r) * nslots;
+  // The query: for a bf16 query its loads go first; an FP4 query is loaded
+  // and quantised after the key loads are issued, so that the quantisation
+  // overlaps the dependent id -> key loads.
   QueryOp<KD> qa;
   float wr[16];
-  load_query<KD>(qa, a.q_idx + static_cast<size_t>(r) * kIdxHeads * kIdxDim, col, half);
-  load_weights(wr, a.w_idx + static_cast<size_t>(r) * kIdxHeads, half);
+  auto query = [&]() {
+    load_query<KD>(qa, a.q_idx + static_cast<size_t>(r) * kIdxHeads * kIdxDim, col, half);
+    load_weights(wr, a.w_idx + static_cast<size_t>(r) * kIdxHeads, half);
+  };
+  if constexpr (KD != kKdFp4Q) query();
   const int b = r / a.n_q;
   // Tiles of 32 slots (4 pool blocks each); wave w takes tiles w and w + 4.
   const int slot0 = blockIdx.x * kPsSlots;
@@ -546,6 +552,7 @@ __global__ __launch_bounds__(kPscThreads) void k_pool_score(PoolArgs a) {
     const size_t row = pool_row(a.pg, b, a.N_cap, pos, mapped);
     load_key_half<KD>(kt[u], a.k_idx + row * kRow, half, scales + row * 4);
   }
+  if constexpr (KD == kKdFp4Q) query();
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const float s = head_sum(key_tile_dot<KD>(qa, kt[u]), wr);
