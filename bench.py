@@ -337,7 +337,8 @@ def fp4_recall(d, step):
         rec.append(len(np.intersect1d(want, got)) / max(len(want), 1))
     return {"mean": round(float(np.mean(rec)), 5), "min": round(float(np.min(rec)), 5),
             "rows": len(rec),
-            "against": "oracle Top-512 over the same keys unquantised (bf16), fp64 scores"}
+            "against": "oracle Top-512 over the same keys unquantised (bf16) with the bf16 query, "
+                       "fp64 scores"}
 
 
 def bf16_scores_report(d, csa, torch, steps):
