@@ -144,6 +144,43 @@ def test_scan_mxfp4_paged(qk):
     assert np.array_equal(out[0], out[1], equal_nan=True)
 
 
+def test_fp4_query_special_blocks():
+    # The query's in-kernel MXFP4 quantisation on blocks that take every
+    # branch of the encoding: all zeros, subnormal bf16 values, values at the
+    # bottom of the exponent range (the clamp to -127), E2M1 ties both ways,
+    # very large values, a single nonzero element, signed zeros; the other
+    # heads are Gaussian.  Scores against the oracle on the same bytes.
+    from oracle import formats
+    B, T = 1, 320
+    d = synth.decode_workload(B=B, T=T, kdtype="mxfp4", seed=405)
+    rng = np.random.default_rng(405)
+    q = rng.standard_normal((32, 128))
+    q[0] = 0.0
+    q[1, :32] = rng.integers(-7, 8, 32) * 2.0 ** -133            # subnormal in bf16
+    q[2, :32] = rng.integers(-7, 8, 32) * 2.0 ** -126            # amax near 2^-123: X clamps
+    q[3, :8] = [1.25, 0.6875, 0.375, -0.3125, 0.875, -0.875, 2.5, -2.5]   # ties
+    q[3, 20] = 3.0
+    q[4] = rng.standard_normal(128) * 2.0 ** 100
+    q[5] = 0.0
+    q[5, [3, 40, 77, 127]] = [1.5, -3.0e-3, 7.0, -2.0e20]      # one element per block
+    q[6, ::2] = -0.0
+    q_raw = formats.f64_to_bf16(q)
+    w = rng.uniform(0.5, 1.5, 32)
+    w[4] = 2.0 ** -100
+    q_t = torch.from_numpy(q_raw.view(np.int16)).reshape(1, 1, 32, 128).cuda()
+    w_t = torch.from_numpy(w.astype(np.float32)).reshape(1, 1, 32).cuda()
+    vis_t = torch.tensor([[T]], dtype=torch.int32).cuda()
+    sc = torch.full((1, 1, T), float("nan"), device="cuda")
+    print("fp4 query special blocks", flush=True)
+    csa.index_score(q_t, w_t, _keys(d, True), vis_t, scores=sc)
+    torch.cuda.synchronize()
+    kr = _oracle_rows(d["k_idx"], T, 0, T)
+    ref = pipeline.scores_prefix(q_raw, w.astype(np.float32).astype(np.float64), kr, "mxfp4_qk", T)
+    g = _np(sc)[0, 0].astype(np.float64)
+    tol = 1e-5 * np.abs(ref) + 1e-6 * np.abs(ref).max()
+    assert np.all(np.abs(g - ref) <= tol), f"max err {np.abs(g - ref).max()}"
+
+
 def test_mxfp4_keys_rejected_for_prefill_rows():
     d = synth.decode_workload(B=1, T=1024, kdtype="mxfp4", seed=404)
     q = torch.zeros(1, 16, 32, 128, dtype=torch.int16, device="cuda")
