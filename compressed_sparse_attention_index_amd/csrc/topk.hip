@@ -941,6 +941,7 @@ __global__ __launch_bounds__(FrShape<BF16>::kThreads, 4) void k_flat_select_reg(
         if constexpr (BF16) {
           if (bk > b1) atomicOr(&bitmap[mword + 32 * (e >> 1)], (e & 1) ? mbit1 : mbit0);
         } else {
+          static_assert(NT % 64 == 0, "a wave's items at one index start a bitmap word");
           const uint64_t sure = __ballot(bk > b1);
           const int lane = tid & 63;
           if (lane < 2)
