@@ -723,9 +723,18 @@ def main():
         # The 128K points of the metric: the Reuse-layer decode (B=64) with
         # either main-KV scale format and the encoder prefill chunk, each with
         # its own dominant call's roofline.
-        rec["points_128k"] = [
-            measure(w, args, torch, synth, csa, cpu=False, graph=False)
-            for w in ("reuse_128k", "reuse_128k_e4m3", "prefill_128k")]
+        # A Reuse step is about 25 us, so those points time at least 200
+        # steps (5 ms): with 20, one slow host launch moved the mean by a
+        # third.
+        rec["points_128k"] = []
+        for w in ("reuse_128k", "reuse_128k_e4m3", "prefill_128k"):
+            pa = args
+            if w.startswith("reuse"):
+                pa = argparse.Namespace(**{**vars(args), "steps": max(args.steps, 200),
+                                           "warmup": max(args.warmup, 20)})
+            pt = measure(w, pa, torch, synth, csa, cpu=False, graph=False)
+            pt["steps"], pt["warmup"] = pa.steps, pa.warmup
+            rec["points_128k"].append(pt)
     for job in later:
         rec["cpu_baseline"] = job()
     print(json.dumps(rec), flush=True)
