@@ -117,6 +117,22 @@ def test_reuse_128k(name):
         check_attention(u16(out[b, 0]), _np(lse[b, 0]), o, l, what=f"{name} row {b}")
 
 
+def test_maximum_context():
+    # The largest context the boundary accepts: 2^22 entries per sequence,
+    # i.e. 524,288 block maxima per row for the block Top-K (whose selection
+    # bitmap in LDS is sized for that), and sequence 2's main KV starting
+    # 2 GiB into its buffer.  Row 2 is ragged (its last 5 entries not yet
+    # visible, the current token the last visible one).
+    T = 1 << 22
+    d = synth.make("full_reindex_1m", device="cuda", B=3, T=T)
+    d["vis_len"][2, 0] = T - 5
+    d["q_pos"][2, 0] = T - 6
+    print("workload full layer at 2^22 entries, B=3", flush=True)
+    pool, idx, out, lse = _full_layer(d)
+    for b in (0, 2):
+        _check_full(d, b, pool, idx, out, lse)
+
+
 def test_full_reindex_1m():
     d = synth.make("full_reindex_1m", device="cuda")
     print("workload full_reindex_1m", flush=True)
