@@ -127,10 +127,20 @@ def test_maximum_context():
     d = synth.make("full_reindex_1m", device="cuda", B=3, T=T)
     d["vis_len"][2, 0] = T - 5
     d["q_pos"][2, 0] = T - 6
-    print("workload full layer at 2^22 entries, B=3", flush=True)
+    print("workload full and reindex layers at 2^22 entries, B=3", flush=True)
     pool, idx, out, lse = _full_layer(d)
+    idx2 = torch.empty(d["B"], 1, 512, dtype=torch.int32, device="cuda")
+    csa.reindex_topk(csa.MODE_REINDEX, d["vis_len"], T, 512, idx2, q_idx=d["q_idx2"],
+                     w_idx=d["w_idx2"], k_idx=d["k_idx"], pool_blocks=pool)
+    torch.cuda.synchronize()
     for b in (0, 2):
-        _check_full(d, b, pool, idx, out, lse)
+        gp = _check_full(d, b, pool, idx, out, lse)
+        kr, kd = _kraw(d, b)
+        re = pipeline.reindex_layer(u16(d["q_idx2"][b, 0]), _np(d["w_idx2"][b, 0]), kr, kd, gp,
+                                    int(d["vis_len"][b, 0]))
+        key = dict(zip(re["positions"].tolist(), re["scores"].tolist()))
+        check_selection(_np(idx2[b, 0]), re["idx"], lambda t: np.array([key[int(x)] for x in t]),
+                        what=f"reindex row {b}")
 
 
 def test_full_reindex_1m():
