@@ -188,6 +188,35 @@ def test_prefill_128k():
         check_attention(u16(out[0, j]), _np(lse[0, j]), o, l, what=f"prefill attention row {j}")
 
 
+def test_prefill_past_2g_scores():
+    # A prefill call whose score matrix has more than 2^31 elements: 520
+    # query rows over the largest accepted context (4,194,304 entries), so
+    # the scoring GEMM stores, and the long-row flat Top-k reads, past the
+    # 32-bit element range.
+    n_q = 520
+    d = synth.make("prefill_128k", device="cuda", n_q=n_q, prefix_tokens=2 * ((1 << 22) - n_q // 2))
+    N = d["kv_fp4"].shape[1]
+    assert N == 1 << 22 and n_q * N > 2 ** 31
+    print(f"prefill {n_q} rows x {N} entries", flush=True)
+    scores = torch.empty(1, n_q, N, device="cuda")
+    csa.index_score(d["q_idx"], d["w_idx"], d["k_idx"], d["vis_len"], scores=scores)
+    idx = torch.empty(1, n_q, 512, dtype=torch.int32, device="cuda")
+    csa.reindex_topk(csa.MODE_FULL, d["vis_len"], N, 512, idx, scores=scores)
+    out, lse = _attention(d, d["q"], d["swa"], idx)
+    torch.cuda.synchronize()
+    kr, kd = _kraw(d, 0)
+    for j in (0, n_q - 1):
+        vis = int(d["vis_len"][0, j])
+        ref = pipeline.prefill_topk(u16(d["q_idx"][0, j]), _np(d["w_idx"][0, j]), kr, kd, vis)
+        g = _np(scores[0, j, :vis]).astype(np.float64)
+        s = ref["scores"]
+        assert np.all(np.abs(g - s) <= 1e-5 * np.abs(s) + 1e-6 * np.abs(s).max()), f"scores row {j}"
+        gi = _np(idx[0, j])
+        check_selection(gi, ref["idx"], lambda t: s[t], what=f"prefill idx row {j}")
+        o, l = _attn_ref(d, 0, j, gi, d["q"], d["swa"])
+        check_attention(u16(out[0, j]), _np(lse[0, j]), o, l, what=f"prefill attention row {j}")
+
+
 @pytest.mark.parametrize("kv_fmt", ["e8m0_32", "e4m3_16"])
 def test_kv_append_64k(kv_fmt):
     # The benchmark's append (4 x 65,536 tokens, window of the last 128), run
