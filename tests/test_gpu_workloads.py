@@ -217,6 +217,26 @@ def test_prefill_past_2g_scores():
         check_attention(u16(out[0, j]), _np(lse[0, j]), o, l, what=f"prefill attention row {j}")
 
 
+def test_kv_append_past_2g():
+    # Appends at the end of the largest accepted context (positions up to
+    # 2^22 - 1) in three sequences: the third one's rows sit past 2 GiB into
+    # the main-KV buffer.
+    N, n_new = 1 << 22, 8
+    d = synth.make("kv_append_64k", device="cuda", B=3, n_new=n_new)
+    kv_fp4 = torch.zeros(3, N, 256, dtype=torch.uint8, device="cuda")
+    kv_scale = torch.zeros(3, N, 16, dtype=torch.uint8, device="cuda")
+    pos = torch.full((3,), N - n_new, dtype=torch.int32, device="cuda")
+    print("kv append at 2^22 - 8, B=3", flush=True)
+    csa.kv_append(d["kv_new"], pos, kv_fp4, kv_scale)
+    torch.cuda.synchronize()
+    for b in range(3):
+        kv = formats.bf16_to_f64(_np(d["kv_new"][b]).view(np.uint16))
+        fp4, sc = formats.f64_to_mxfp4(kv)
+        assert np.array_equal(_np(kv_fp4[b, N - n_new:]), fp4), f"E2M1 rows of sequence {b}"
+        assert np.array_equal(_np(kv_scale[b, N - n_new:]), sc), f"scales of sequence {b}"
+        assert not bool(kv_fp4[b, :N - n_new].any()), f"rows outside the append, sequence {b}"
+
+
 @pytest.mark.parametrize("kv_fmt", ["e8m0_32", "e4m3_16"])
 def test_kv_append_64k(kv_fmt):
     # The benchmark's append (4 x 65,536 tokens, window of the last 128), run
