@@ -164,10 +164,10 @@ def test_flat_select_long_rows(n):
 
 
 def test_flat_select_many_rows():
-    # More rows than compute units: a workgroup takes every (grid)-th row and
-    # prefetches its next row while it works on the current one.  Row kinds
-    # cycle (distinct, heavy ties, all equal, short, empty, two clusters), so
-    # every marking path meets the loop and the prefetch of every other kind.
+    # More rows than compute units, so workgroups of every row kind run side
+    # by side over several rounds of the grid.  Row kinds cycle (distinct,
+    # heavy ties, all equal, short, empty, two clusters), so every marking
+    # path (ballot stores, list marks, the whole-row pass) is exercised.
     rng = np.random.default_rng(25)
     n = 9000
     kinds = [
