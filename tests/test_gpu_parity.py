@@ -343,12 +343,20 @@ def _attn_ref(d, b, j, idx_row, q=None, swa=None, window=128, replay_start=-1, s
                               window, replay_start, sink, kv_fmt=d.get("kv_fmt", "e8m0_32"))
 
 
+@pytest.mark.parametrize("n_q", [1, 16])
 @pytest.mark.parametrize("case", ["topk512", "ragged", "invalid", "dense", "window16", "replay",
                                   "seq_start", "no_main", "mixed_chunk"])
-def test_attention_cases(case):
+def test_attention_cases(case, n_q):
+    # n_q = 1: decode rows (head-group kernel); n_q = 16: prefill-shaped rows
+    # (one workgroup per row), the sequence's last 16 positions, each row with
+    # its own entries and its own (partly stored) window.
     T, B = 2048, 3
     d = synth.decode_workload(B=B, T=T, kdtype="bf16", seed=41)
     rng = np.random.default_rng(41)
+    if n_q > 1:
+        g = torch.Generator().manual_seed(42)
+        d["q"] = synth.to_bf16_bits(torch.randn(B, n_q, 64, 512, generator=g))
+        d["q_pos"] = (torch.arange(n_q, dtype=torch.int32) + (T - n_q)).repeat(B, 1)
     window, replay = 128, -1
     top_k = 512
     if case == "ragged":
@@ -361,12 +369,13 @@ def test_attention_cases(case):
         # 160 selected slots: one 64-entry chunk holds 32 selected and 32 window
         # entries, and the last chunk is half past the window.
         top_k = 160
-    idx = np.stack([np.sort(rng.choice(T, size=max(top_k, 1), replace=False))[:top_k] for _ in range(B)])
+    idx = np.stack([np.sort(rng.choice(T, size=max(top_k, 1), replace=False))[:top_k]
+                    for _ in range(B * n_q)]).reshape(B, n_q, top_k)
     if case == "dense":
-        idx = np.tile(np.arange(300), (B, 1))
+        idx = np.tile(np.arange(300), (B, n_q, 1))
     if case == "invalid":
-        idx[:, ::3] = -1
-        idx[0, :] = -1
+        idx[:, :, ::3] = -1
+        idx[0] = -1
     if case == "window16":
         window = 16
     if case == "replay":
@@ -374,13 +383,15 @@ def test_attention_cases(case):
     if case == "seq_start":
         # queries near the sequence start: the window holds positions 0..q_pos
         d["swa_pos0"][:] = 0
-        d["q_pos"][:, 0] = torch.tensor([0, 5, 127], dtype=torch.int32)
-    idx_t = torch.from_numpy(idx.astype(np.int32)).reshape(B, 1, top_k)
-    print(f"attention case={case}", flush=True)
+        d["q_pos"][:, :] = (torch.tensor([0, 5, 127], dtype=torch.int32)[:, None]
+                            + torch.arange(n_q, dtype=torch.int32)[None, :])
+    idx_t = torch.from_numpy(idx.astype(np.int32))
+    print(f"attention case={case} n_q={n_q}", flush=True)
     out, lse = _attn_gpu(d, idx_t, window=window, replay_start=replay)
     for b in range(B):
-        o, l = _attn_ref(d, b, 0, idx[b], window=window, replay_start=replay)
-        check_attention(out[b, 0], lse[b, 0], o, l, what=f"{case} row {b}")
+        for j in range(n_q):
+            o, l = _attn_ref(d, b, j, idx[b, j], window=window, replay_start=replay)
+            check_attention(out[b, j], lse[b, j], o, l, what=f"{case} row ({b}, {j})")
 
 
 def test_attention_dense_equals_sdpa_through_gpu():
