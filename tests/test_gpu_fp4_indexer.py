@@ -110,6 +110,38 @@ def test_pool_topk_mxfp4(mode, qk):
 
 
 @pytest.mark.parametrize("qk", [False, True], ids=["keys", "qk"])
+def test_mxfp4_full_layer_at_maximum_context(qk):
+    # 8 sequences of 2^22 entries (the largest accepted context): the key
+    # buffer is 2.28 GB, so the last sequence's E2M1 rows and its scales lie
+    # past 2^31 bytes.  Its row is ragged (vis = T - 3).
+    kd = "mxfp4_qk" if qk else "mxfp4"
+    B, T = 8, 1 << 22
+    d = synth.decode_workload(B=B, T=T, kdtype="mxfp4", seed=403, device="cuda")
+    d["vis_len"][B - 1, 0] = T - 3
+    assert B * T * 68 > 2 ** 31
+    keys = _keys(d, qk)
+    vis = d["vis_len"]
+    bm = torch.empty(B, 1, T // 8, device="cuda")
+    print(f"full layer {kd} at 2^22 entries, B={B}", flush=True)
+    csa.index_score(d["q_idx"], d["w_idx"], keys, vis, block_max=bm)
+    pool = torch.empty(B, 1, 2048, dtype=torch.int32, device="cuda")
+    csa.block_topk(bm, vis, T, 2048, pool)
+    idx = torch.empty(B, 1, 512, dtype=torch.int32, device="cuda")
+    csa.reindex_topk(csa.MODE_FULL, vis, T, 512, idx, q_idx=d["q_idx"], w_idx=d["w_idx"],
+                     k_idx=keys, pool_blocks=pool)
+    torch.cuda.synchronize()
+    buf = d["k_idx"].cpu()
+    for b in (0, B - 1):
+        v = int(vis[b, 0])
+        kr = _oracle_rows(buf, B * T, b * T, T)
+        ref = pipeline.full_layer(u16(d["q_idx"][b, 0]), _np(d["w_idx"][b, 0]), kr, kd, v)
+        check_selection(_np(pool[b, 0]), ref["pool"], lambda j: ref["block_max"][j],
+                        what=f"pool row {b}")
+        check_selection(_np(idx[b, 0]), ref["idx"], lambda t: ref["scores"][t],
+                        what=f"idx row {b}")
+
+
+@pytest.mark.parametrize("qk", [False, True], ids=["keys", "qk"])
 def test_scan_mxfp4_paged(qk):
     # The E2M1 rows and the scale rows of a page pool follow the same table.
     B, T, P = 2, 2048, 128
