@@ -220,3 +220,51 @@ def test_kv_append_paged(kv_fmt):
         # never written.
         for page in np.nonzero(~used)[0]:
             assert np.all(pool[page * P:(page + 1) * P] == 0x5A), page
+
+
+def test_paged_full_layer_past_2g():
+    # Two sequences of 2^22 entries (the largest accepted context) in
+    # 4,096-entry pages of one pool: the main-KV pool is 2.2 GB and sequence
+    # 1's last page is the pool's last, past 2^31 bytes.  The paged Full layer
+    # (scan, block Top-K, pool Top-512, attention) gives the bits of the
+    # contiguous one, which the workload tests check against the oracle.
+    B, T, P = 2, 1 << 22, 4096
+    d = synth.decode_workload(B=B, T=T, kdtype="fp8", seed=205, device="cuda")
+    bt, num_pages = _table(B, T // P, 5, 205)
+    hit = np.argwhere(bt == num_pages - 1)
+    if len(hit):
+        i, j = hit[0]
+        bt[i, j], bt[1, -1] = bt[1, -1], bt[i, j]
+    else:
+        bt[1, -1] = num_pages - 1
+    assert num_pages * P * 256 > 2 ** 31 and len(np.unique(bt)) == bt.size
+
+    def scatter(x):
+        pool = torch.zeros((num_pages * P,) + tuple(x.shape[2:]), dtype=x.dtype, device="cuda")
+        for b in range(B):
+            for j in range(T // P):
+                pool[int(bt[b, j]) * P:(int(bt[b, j]) + 1) * P] = x[b, j * P:(j + 1) * P]
+        return pool
+
+    def layer(k, fp4, sc, pg):
+        vis = d["vis_len"]
+        bm = torch.empty(B, 1, T // 8, device="cuda")
+        csa.index_score(d["q_idx"], d["w_idx"], k, vis, block_max=bm, paging=pg)
+        pool = torch.empty(B, 1, 2048, dtype=torch.int32, device="cuda")
+        csa.block_topk(bm, vis, T, 2048, pool)
+        idx = torch.empty(B, 1, 512, dtype=torch.int32, device="cuda")
+        csa.reindex_topk(csa.MODE_FULL, vis, T, 512, idx, q_idx=d["q_idx"], w_idx=d["w_idx"],
+                         k_idx=k, pool_blocks=pool, paging=pg)
+        out = torch.zeros(B, 1, 64, 512, dtype=torch.int16, device="cuda")
+        lse = torch.zeros(B, 1, 64, device="cuda")
+        csa.sparse_attn_decode(d["q"], fp4, sc, idx, d["swa"], d["swa_pos0"], d["q_pos"],
+                               d["sm_scale"], out, lse=lse, paging=pg)
+        torch.cuda.synchronize()
+        return [_np(t) for t in (bm, pool, idx, out, lse)]
+
+    print("paged full layer at 2^22 entries, pool past 2 GiB", flush=True)
+    flat = layer(d["k_idx"], d["kv_fp4"], d["kv_scale"], None)
+    paged = layer(scatter(d["k_idx"]), scatter(d["kv_fp4"]), scatter(d["kv_scale"]),
+                  _paging(bt, P, num_pages))
+    for a, b, name in zip(flat, paged, ("block max", "pool", "idx", "out", "lse")):
+        assert np.array_equal(a, b), name
