@@ -44,8 +44,8 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="full_reindex_1m",
                    choices=["tiny_2k", "full_64k", "reuse_128k", "reuse_128k_e4m3",
                             "full_reindex_1m", "full_reindex_1m_fp4", "full_reindex_1m_fp4qk",
